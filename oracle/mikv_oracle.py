@@ -1,0 +1,423 @@
+"""Plain CPU oracle of the MiKV mixed-precision KV-cache path.
+
+TEST INFRASTRUCTURE. This module is the checker: only tests, the smoke check
+and the benchmark's CPU-baseline leg may import it. It imports numpy only and
+shares no code, table or constant generator with the HIP library.
+
+Sources (cited by page title and section throughout):
+  [velog notes]      velog.io post "No Token Left Behind: Reliable KV Cache
+                     Compression via Importance-Aware Mixed Precision
+                     Quantization", a reader's notes on arXiv 2402.18096.
+  [paperlayer]       paperlayer.ai source-linked summary of arXiv 2402.18096v1,
+                     "No Token Left Behind ...".
+  [gist CriticalKV]  gist.science technical summary of arXiv 2502.03805
+                     (CriticalKV).
+
+Precision. Values that the parity tests compare bit for bit (the balancer b,
+balanced keys, quantization scale/zero and codes, selections) are discrete
+functions of fp16 inputs; they are computed here with one fixed float32
+operation sequence (IEEE round-to-nearest-even divide and square root, no
+fused multiply-add, no reciprocal multiply, round-half-to-even to integers)
+and that sequence is their definition. Everything compared to a tolerance
+(scores, softmax, attention output, accumulated scores, projected-value
+norms) is computed in float64.
+
+Readings where the pages are silent (each listed with its reason in the
+design notes of the repository):
+  * quantizer zero point is the group minimum, scale (max-min)/(2^bits-1)
+    rounded to fp16, codes are computed from the fp16-stored scale;
+  * groups are d/2 contiguous channels for keys and values alike;
+  * b = 1 where either channel maximum is zero; b is kept in fp32, q/b too;
+  * b is per sequence and per kv head, with the query maximum taken over the
+    query heads that share the kv head;
+  * every cached key is stored balanced (FP16 tier too); values are not;
+  * H2O score = running sum of softmax probabilities over the query heads of
+    the group; ties in the important-set ranking go to the lower position;
+  * the recent window is the R newest positions, the new token included;
+  * tokens in the low-bit tier are never promoted back;
+  * CriticalKV: b1 = floor(alpha*budget), b2 = budget-b1, stage-2 score
+    A_i * ||V_i W_O,h||_1 with W_O laid out [H*d, hidden].
+
+Parity unpinned (conventions of this repository, not fixed by the pages):
+  the bit layout of packed codes, the rounding of the budget split, and the
+  synthetic prefill scores acc0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "balance", "balance_keys", "quantize_rows", "pack_codes", "unpack_codes",
+    "dequantize_rows", "top_by_key", "prefill_build", "decode_attention",
+    "h2o_accumulate", "select_drop", "demote", "decode_step",
+    "projected_value_l1", "criticalkv_select", "empty_state",
+]
+
+F16, F32, F64 = np.float16, np.float32, np.float64
+
+
+# --------------------------------------------------------------------------
+# Channel balancer
+# --------------------------------------------------------------------------
+def balance(q: np.ndarray, k: np.ndarray):
+    """Channel balancer and balanced prompt keys.
+
+    [velog notes] Key contributions 2) "Outlier-aware": during prefill, for
+    layer l, head h, channel c, b_lhc is the square root of the ratio of the
+    channel's largest |query| to its largest |key| over the prompt tokens 0..t-1
+    (balancer equation); keys are multiplied by b before quantization
+    (equation for k-hat). [paperlayer] section 3.2: the balancer is computed
+    at prefill and applied to keys and queries.
+
+    q: [n, hq, T, d] fp16, k: [n, hkv, T, d] fp16 with hq a multiple of hkv.
+    Returns b [n, hkv, d] fp32 and kb [n, hkv, T, d] fp16.
+    """
+    n, hq, T, d = q.shape
+    _, hkv, Tk, dk = k.shape
+    assert Tk == T and dk == d and hq % hkv == 0
+    rep = hq // hkv
+    if T == 0:
+        mq = np.zeros((n, hkv, d), F32)
+        mk = np.zeros((n, hkv, d), F32)
+    else:
+        mq = np.abs(q.astype(F32)).reshape(n, hkv, rep, T, d).max(axis=(2, 3))
+        mk = np.abs(k.astype(F32)).max(axis=2)
+    zero = (mq == 0) | (mk == 0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = (mq / np.where(zero, F32(1), mk)).astype(F32)
+    b = np.sqrt(ratio).astype(F32)
+    b[zero] = F32(1)
+    return b, balance_keys(k, b[:, :, None, :])
+
+
+def balance_keys(k: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """k-hat before quantization: fp16(fp32(k) * b), per channel.
+
+    [velog notes] Key contributions 2), equation for k-hat: the key is
+    multiplied by b_lhc. k: [..., d] fp16 whose leading dims broadcast
+    against b's [n, hkv, d] once a token axis is inserted by the caller.
+    """
+    return (k.astype(F32) * b.astype(F32)).astype(F16)
+
+
+# --------------------------------------------------------------------------
+# Per-token asymmetric quantization
+# --------------------------------------------------------------------------
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack integer codes [rows, d] into bytes [rows, d*bits/8].
+
+    Little-endian within a byte: code of channel (8/bits)*j + m occupies
+    bits [bits*m, bits*m + bits) of byte j.
+    """
+    per = 8 // bits
+    rows, d = codes.shape
+    c = codes.astype(np.uint8).reshape(rows, d // per, per)
+    out = np.zeros((rows, d // per), np.uint8)
+    for m in range(per):
+        out |= (c[:, :, m] << (bits * m)).astype(np.uint8)
+    return out
+
+
+def unpack_codes(packed: np.ndarray, d: int, bits: int) -> np.ndarray:
+    per = 8 // bits
+    rows = packed.shape[0]
+    mask = (1 << bits) - 1
+    out = np.empty((rows, d // per, per), np.int64)
+    for m in range(per):
+        out[:, :, m] = (packed >> (bits * m)) & mask
+    return out.reshape(rows, d)
+
+
+def quantize_rows(x: np.ndarray, group: int, bits: int):
+    """Per-token asymmetric round-to-nearest quantization with groups.
+
+    [velog notes] Key contributions 1): the retained (evicted) tokens use
+    ordinary per-token asymmetric quantization (LLM-QAT style). [velog notes]
+    Key contributions 2), additional notes, and [paperlayer] section 3.2: the
+    group size is half of the head dimension, to soften RoPE artifacts.
+
+    Per row and group of `group` contiguous channels:
+      mn, mx = min, max (exact in fp16)
+      s = fp16( (f32(mx) - f32(mn)) / (2^bits - 1) ),  z = mn
+      code = clamp(round_half_even((f32(x) - f32(z)) / f32(s)), 0, 2^bits-1)
+      (all codes 0 when s == 0; a zero scale or zero point is stored as +0).
+    x: [rows, d] fp16. Returns packed codes [rows, d*bits/8] uint8 and
+    sz [rows, d/group, 2] fp16 holding (scale, zero) per group.
+    """
+    assert bits in (2, 4)
+    rows, d = x.shape
+    assert d % group == 0 and group % (8 // bits) == 0
+    qmax = F32((1 << bits) - 1)
+    ng = d // group
+    xs = x.reshape(rows, ng, group)
+    if rows == 0:
+        return (np.zeros((0, d * bits // 8), np.uint8), np.zeros((0, ng, 2), F16))
+    mn = xs.min(axis=2)
+    mx = xs.max(axis=2)
+    s32 = ((mx.astype(F32) - mn.astype(F32)) / qmax).astype(F32)
+    s16 = s32.astype(F16)
+    # signed zeros are stored as +0 so that (scale, zero) bits are unique
+    s16[s16 == 0] = F16(0)
+    z16 = np.where(mn == 0, F16(0), mn).astype(F16)
+    s_safe = np.where(s16 == 0, F32(1), s16.astype(F32)).astype(F32)
+    t = ((xs.astype(F32) - z16.astype(F32)[:, :, None]) / s_safe[:, :, None]).astype(F32)
+    codes = np.clip(np.rint(t), 0, qmax)
+    codes[s16 == 0] = 0
+    packed = pack_codes(codes.reshape(rows, d).astype(np.int64), bits)
+    sz = np.stack([s16, z16], axis=-1).astype(F16)
+    return packed, sz
+
+
+def dequantize_rows(packed: np.ndarray, sz: np.ndarray, group: int, bits: int) -> np.ndarray:
+    """code * scale + zero, in float64. Returns [rows, d]."""
+    rows = packed.shape[0]
+    d = packed.shape[1] * 8 // bits
+    c = unpack_codes(packed, d, bits).astype(F64).reshape(rows, d // group, group)
+    s = sz[:, :, 0].astype(F64)[:, :, None]
+    z = sz[:, :, 1].astype(F64)[:, :, None]
+    return (c * s + z).reshape(rows, d)
+
+
+# --------------------------------------------------------------------------
+# Importance ranking (H2O heavy hitters)
+# --------------------------------------------------------------------------
+def top_by_key(score: np.ndarray, pos: np.ndarray, m: int) -> np.ndarray:
+    """Indices of the m best entries by (score descending, position ascending).
+
+    The importance-based eviction the MiKV notes use is H2O ([velog notes]
+    Key contributions 1)); heavy hitters are the tokens with the largest
+    accumulated attention ([paperlayer] section 5, KV cache eviction). Equal
+    scores are ranked by lower token position.
+    """
+    order = np.lexsort((pos, -score.astype(F64)))
+    return order[:m]
+
+
+def empty_state(batch, hkv, d, cap16, capq, group, bits):
+    """Zeroed cache in the layout of the C interface (see include/mikv.h)."""
+    cb = d * bits // 8
+    return dict(
+        k16=np.zeros((batch, hkv, cap16, d), F16), v16=np.zeros((batch, hkv, cap16, d), F16),
+        pos16=np.full((batch, hkv, cap16), -1, np.int32),
+        acc16=np.zeros((batch, hkv, cap16), F32),
+        free16=np.zeros((batch, hkv), np.int32),
+        kq=np.zeros((batch, hkv, capq, cb), np.uint8), vq=np.zeros((batch, hkv, capq, cb), np.uint8),
+        ksz=np.zeros((batch, hkv, capq, d // group, 2), F16),
+        vsz=np.zeros((batch, hkv, capq, d // group, 2), F16),
+        posq=np.full((batch, hkv, capq), -1, np.int32),
+        group=group, bits=bits,
+    )
+
+
+def prefill_build(kb, v, acc0, B, R, group, bits, capq):
+    """Initial two-tier cache after the prompt.
+
+    [velog notes] one-line summary and Key contributions 1): tokens an
+    importance-based eviction would drop are kept at low precision; important
+    tokens stay at high precision. Important set = the R newest positions
+    plus the top-(B-R) older positions by accumulated attention (H2O heavy
+    hitters and local tokens, [paperlayer] section 5). The FP16 tier holds
+    the important set in ascending position (slots 0..B-1, slot B free); the
+    low-bit tier holds the others in ascending position. Grouping pairs by
+    precision is allowed because attention is permutation invariant
+    ([velog notes] section 3.4).
+
+    kb, v: [n, hkv, T, d] fp16 (balanced keys, values); acc0 [n, hkv, T] fp32.
+    """
+    n, hkv, T, d = kb.shape
+    H = B - R
+    assert 0 <= R <= B <= T and T - B <= capq
+    st = empty_state(n, hkv, d, B + 1, capq, group, bits)
+    pos_all = np.arange(T, dtype=np.int64)
+    for i in range(n):
+        for g in range(hkv):
+            cand = pos_all[:T - R]
+            heavy = cand[top_by_key(acc0[i, g, :T - R], cand, H)]
+            keep = np.zeros(T, bool)
+            keep[heavy] = True
+            keep[T - R:] = True
+            kp = pos_all[keep]
+            rp = pos_all[~keep]
+            st["k16"][i, g, :B] = kb[i, g, kp]
+            st["v16"][i, g, :B] = v[i, g, kp]
+            st["pos16"][i, g, :B] = kp
+            st["acc16"][i, g, :B] = acc0[i, g, kp]
+            st["free16"][i, g] = B
+            ck, sk = quantize_rows(kb[i, g, rp], group, bits)
+            cv, sv = quantize_rows(v[i, g, rp], group, bits)
+            m = len(rp)
+            st["kq"][i, g, :m], st["ksz"][i, g, :m] = ck, sk
+            st["vq"][i, g, :m], st["vsz"][i, g, :m] = cv, sv
+            st["posq"][i, g, :m] = rp
+    return st
+
+
+# --------------------------------------------------------------------------
+# Decode step
+# --------------------------------------------------------------------------
+def decode_attention(state, N, q, k_new, v_new, b):
+    """Append the new token, then attention over both precision tiers.
+
+    [velog notes] section 3.4 and [paperlayer] section 3.4: decode attention
+    is a batch matrix-vector product; keys and values are stored at reduced
+    precision while the query and the attention map stay floating point.
+    [velog notes] Key contributions 2): the query is divided by b (q-hat) and
+    the key was multiplied by b, so q-hat . k-hat reproduces q . k.
+    Scores use scale 1/sqrt(d); the new token attends to every cached token
+    and to itself.
+
+    state: cache dict (see empty_state) before the step; the low-bit tier
+    holds N - cap16 tokens and slot free16 of the FP16 tier is free.
+    q [n, hq, d], k_new/v_new [n, hkv, d] fp16; b [n, hkv, d] fp32.
+    Returns (o [n,hq,d] f64, p16 [n,hkv,cap16] f64 summed over the group's
+    query heads, pq [n,hkv,N-cap16] f64 likewise for the low-bit tier,
+    appended state).
+    """
+    st = {kk: (vv.copy() if isinstance(vv, np.ndarray) else vv) for kk, vv in state.items()}
+    group, bits = st["group"], st["bits"]
+    n, hkv, cap16, d = st["k16"].shape
+    hq = q.shape[1]
+    rep = hq // hkv
+    nq = N - cap16
+    assert nq >= 0
+    o = np.zeros((n, hq, d), F64)
+    p16 = np.zeros((n, hkv, cap16), F64)
+    pq = np.zeros((n, hkv, nq), F64)
+    for i in range(n):
+        for g in range(hkv):
+            s = int(st["free16"][i, g])
+            st["k16"][i, g, s] = balance_keys(k_new[i, g], b[i, g])
+            st["v16"][i, g, s] = v_new[i, g]
+            st["pos16"][i, g, s] = N - 1
+            st["acc16"][i, g, s] = 0.0
+            K = np.concatenate([st["k16"][i, g].astype(F64),
+                                dequantize_rows(st["kq"][i, g, :nq], st["ksz"][i, g, :nq], group, bits)])
+            V = np.concatenate([st["v16"][i, g].astype(F64),
+                                dequantize_rows(st["vq"][i, g, :nq], st["vsz"][i, g, :nq], group, bits)])
+            for r in range(rep):
+                h = g * rep + r
+                qh = q[i, h].astype(F64) / b[i, g].astype(F64)
+                sc = (K @ qh) / np.sqrt(F64(d))
+                e = np.exp(sc - sc.max())
+                p = e / e.sum()
+                o[i, h] = p @ V
+                p16[i, g] += p[:cap16]
+                pq[i, g] += p[cap16:]
+    return o, p16, pq, st
+
+
+def h2o_accumulate(acc16, p16):
+    """acc += probability mass of this step (float64). [paperlayer] section 5:
+    heavy hitters are ranked by accumulated attention."""
+    return acc16.astype(F64) + p16
+
+
+def select_drop(acc, pos16, N, R, H):
+    """Slot to demote per (n, g) after one decode step.
+
+    The FP16 tier holds the R newest positions (the window, new token
+    included) and H+1 older candidates. Re-selecting the top-H candidates by
+    (acc desc, position asc) leaves exactly one candidate out; that one is
+    demoted. Returns drop [n, hkv] int64 (slot index).
+    """
+    n, hkv, cap16 = pos16.shape
+    drop = np.empty((n, hkv), np.int64)
+    for i in range(n):
+        for g in range(hkv):
+            cand = np.nonzero(pos16[i, g] < N - R)[0]
+            assert len(cand) == H + 1, (len(cand), H)
+            keep = cand[top_by_key(acc[i, g, cand], pos16[i, g, cand], H)]
+            rest = np.setdiff1d(cand, keep)
+            assert len(rest) == 1
+            drop[i, g] = rest[0]
+    return drop
+
+
+def demote(state, N, drop):
+    """Quantize each dropped FP16-tier token into low-bit slot N - cap16.
+
+    [velog notes] Key contributions 1): tokens leaving the important set are
+    kept as low-bit codes instead of being discarded.
+    """
+    st = {kk: (vv.copy() if isinstance(vv, np.ndarray) else vv) for kk, vv in state.items()}
+    group, bits = st["group"], st["bits"]
+    n, hkv, cap16, d = st["k16"].shape
+    slot = N - cap16
+    for i in range(n):
+        for g in range(hkv):
+            s = int(drop[i, g])
+            ck, sk = quantize_rows(st["k16"][i, g, s:s + 1], group, bits)
+            cv, sv = quantize_rows(st["v16"][i, g, s:s + 1], group, bits)
+            st["kq"][i, g, slot], st["ksz"][i, g, slot] = ck[0], sk[0]
+            st["vq"][i, g, slot], st["vsz"][i, g, slot] = cv[0], sv[0]
+            st["posq"][i, g, slot] = st["pos16"][i, g, s]
+            st["free16"][i, g] = s
+    return st
+
+
+def decode_step(state, N, q, k_new, v_new, b, R, H):
+    """One full decode step: append, attention, accumulate, re-select, demote.
+    Returns (o, p16, new_state, drop)."""
+    o, p16, _, st = decode_attention(state, N, q, k_new, v_new, b)
+    acc = h2o_accumulate(st["acc16"], p16)
+    st["acc16"] = acc.astype(F32)
+    drop = select_drop(acc, st["pos16"], N, R, H)
+    return o, p16, demote(st, N, drop), drop
+
+
+# --------------------------------------------------------------------------
+# CriticalKV two-stage selection
+# --------------------------------------------------------------------------
+def projected_value_l1(V, W_O, rows=None, chunk=2048):
+    """n_i = || V_h[i,:] @ W_O[h*d:(h+1)*d, :] ||_1 per head (float64).
+
+    [gist CriticalKV] theoretical framework: the output-perturbation bound
+    depends on the attention weights and on the value states projected by the
+    output matrix W_O. V: [H, T, d] fp16; W_O: [H*d, hidden] fp16.
+    Returns [H, T] float64 (rows outside `rows[h]`, if given, are left 0).
+    """
+    H, T, d = V.shape
+    out = np.zeros((H, T), F64)
+    for h in range(H):
+        Wh = W_O[h * d:(h + 1) * d].astype(F64)
+        idx = np.arange(T) if rows is None else np.asarray(rows[h])
+        for c0 in range(0, len(idx), chunk):
+            sl = idx[c0:c0 + chunk]
+            out[h, sl] = np.abs(V[h, sl].astype(F64) @ Wh).sum(axis=1)
+    return out
+
+
+def criticalkv_select(A, V, W_O, budget, alpha, norms=None, score2=None):
+    """CriticalKV perturbation-constrained two-stage selection per head.
+
+    [gist CriticalKV] Algorithm 1: stage 1 spends b' = alpha * b of the
+    budget on the entries with the largest attention weight A_i; stage 2
+    spends the remaining b'' on the entries maximising A_i times the L1 norm
+    of the projected value state (V_i W_O). Ties go to the lower index.
+
+    A [H, T] fp32, V [H, T, d] fp16, W_O [H*d, hidden] fp16.
+    Returns idx [H, budget] (ascending), score2 [H, T] float64 (A_i * n_i for
+    entries outside stage 1, -1 for stage-1 entries) and s1 mask [H, T].
+    `norms` may pass precomputed n [H, T] (rows outside stage 1 are used);
+    `score2` may pass a stage-2 score array to rank instead (its stage-1
+    entries are ignored), which is how a device result is re-ranked.
+    """
+    H, T = A.shape
+    assert 1 <= budget <= T and 0.0 <= alpha <= 1.0
+    b1 = int(np.floor(F64(alpha) * budget))
+    b2 = budget - b1
+    pos = np.arange(T)
+    s1 = np.zeros((H, T), bool)
+    for h in range(H):
+        s1[h, top_by_key(A[h], pos, b1)] = True
+    if score2 is None:
+        if norms is None:
+            norms = projected_value_l1(V, W_O, rows=[pos[~s1[h]] for h in range(H)])
+        score2 = A.astype(F64) * norms
+    score2 = np.where(s1, -1.0, np.asarray(score2, F64))
+    idx = np.empty((H, budget), np.int64)
+    for h in range(H):
+        rest = pos[~s1[h]]
+        sel2 = rest[top_by_key(score2[h, rest], rest, b2)]
+        idx[h] = np.sort(np.concatenate([pos[s1[h]], sel2]))
+    return idx, score2, s1

@@ -1,0 +1,441 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values
+derived by hand (tests/golden), closed forms on planted inputs, invariants
+(balancer identity, permutation invariance, probability conservation),
+library routines for special cases (scaled-dot-product attention in float64)
+and brute force over all subsets on tiny inputs.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixed_precision_decode_amd import synth as S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F16, F32, F64 = np.float16, np.float32, np.float64
+
+
+# ---------------------------------------------------------------- balancer
+def _small_qk(rng, n, hq, hkv, T, d):
+    q = (rng.uniform(-0.5, 0.5, (n, hq, T, d))).astype(F16)
+    k = (rng.uniform(-0.5, 0.5, (n, hkv, T, d))).astype(F16)
+    return q, k
+
+
+def test_balancer_planted_maxima_closed_form():
+    """b = sqrt(max|q| / max|k|): plant the channel maxima so b is known exactly.
+
+    The q maximum is planted in a random query head of the group (often the
+    last one) and a random token, so a wrong head-to-group mapping or a
+    missing token range changes b."""
+    rng = np.random.default_rng(7)
+    n, hq, hkv, T, d = 2, 8, 2, 6, 8
+    rep = hq // hkv
+    q, k = _small_qk(rng, n, hq, hkv, T, d)
+    ratios = [(4.0, 1.0, 2.0), (1.0, 4.0, 0.5), (2.0, 2.0, 1.0), (16.0, 1.0, 4.0),
+              (9.0, 1.0, 3.0), (1.0, 16.0, 0.25), (8.0, 2.0, 2.0), (3.0, 12.0, 0.5)]
+    expect = np.empty((n, hkv, d), F32)
+    for i in range(n):
+        for g in range(hkv):
+            for c in range(d):
+                mq, mk, bb = ratios[(i * 3 + g * 5 + c) % len(ratios)]
+                h = g * rep + (rep - 1 if c % 2 == 0 else int(rng.integers(rep)))
+                t = int(rng.integers(T))
+                q[i, h, t, c] = F16(-mq if c % 3 == 0 else mq)
+                k[i, g, int(rng.integers(T)), c] = F16(mk if c % 2 else -mk)
+                expect[i, g, c] = bb
+    b, kb = O.balance(q, k)
+    assert b.dtype == F32 and np.array_equal(b, expect)
+    # keys are multiplied (not divided) by b; these products are exact in fp16
+    exact = np.isin(expect, [0.25, 0.5, 1.0, 2.0, 4.0])
+    prod = (k.astype(F64) * expect[:, :, None, :].astype(F64))
+    m = np.broadcast_to(exact[:, :, None, :], prod.shape)
+    assert np.array_equal(kb.astype(F64)[m], prod[m])
+
+
+def test_balancer_zero_guard_and_empty_prompt():
+    rng = np.random.default_rng(1)
+    q, k = _small_qk(rng, 1, 2, 1, 5, 4)
+    k[0, 0, :, 1] = 0          # key channel identically zero
+    q[0, :, :, 2] = 0          # query channel identically zero
+    b, _ = O.balance(q, k)
+    assert b[0, 0, 1] == 1.0 and b[0, 0, 2] == 1.0
+    b0, kb0 = O.balance(q[:, :, :0], k[:, :, :0])
+    assert np.all(b0 == 1.0) and kb0.shape == (1, 1, 0, 4)
+
+
+def test_balancer_q_equals_k_gives_one():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((2, 3, 17, 8)).astype(F16)
+    b, kb = O.balance(x, x.copy())
+    assert np.all(b == 1.0) and np.array_equal(kb, x)
+
+
+def test_balancer_equalises_channel_ranges():
+    """After balancing, the largest |k*b| and the largest |q/b| of a channel
+    both equal sqrt(max|q| * max|k|) (the geometric mean): the purpose stated
+    for b on the velog notes page (K side range shrinks, Q absorbs it)."""
+    cfg = S.CONFIGS["tiny"].scaled(hq=4, hkv=2, d=64, T=64)
+    q, k, _, _ = S.prefill_tensors(cfg, 11)
+    b, _ = O.balance(q, k)
+    mq = np.abs(q.astype(F64)).reshape(1, 2, 2, 64, 64).max(axis=(2, 3))
+    mk = np.abs(k.astype(F64)).max(axis=2)
+    gm = np.sqrt(mq * mk)
+    np.testing.assert_allclose(mk * b, gm, rtol=1e-6)
+    np.testing.assert_allclose(mq / b, gm, rtol=1e-6)
+
+
+def test_balancer_identity_before_quantization():
+    """(q / b) . (k * b) == q . k in float64 (velog notes, k-hat / q-hat equations)."""
+    cfg = S.CONFIGS["tiny"].scaled(hq=2, hkv=1, T=48)
+    q, k, _, _ = S.prefill_tensors(cfg, 3)
+    b, _ = O.balance(q, k)
+    bb = b.astype(F64)[0, 0]
+    qq = q.astype(F64)[0, 0]
+    kk = k.astype(F64)[0, 0]
+    lhs = (qq / bb) @ (kk * bb).T
+    rhs = qq @ kk.T
+    assert np.max(np.abs(lhs - rhs)) <= 1e-12 * np.max(np.abs(rhs))
+    assert not np.all(b == 1.0)
+
+
+# ---------------------------------------------------------------- quantizer
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "quantizer_hand_vectors.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_quantizer_hand_vectors(case):
+    x = np.array(case["x"], F16)[None, :]
+    packed, sz = O.quantize_rows(x, case["group"], case["bits"])
+    assert sz[0, :, 0].astype(F64).tolist() == case["scale"]
+    assert sz[0, :, 1].astype(F64).tolist() == case["zero"]
+    assert packed[0].tobytes().hex() == case["packed_hex"].replace(" ", "")
+    d = x.shape[1]
+    assert O.unpack_codes(packed, d, case["bits"])[0].tolist() == case["codes"]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("group", [32, 64])
+def test_quantizer_roundtrip_bound(bits, group):
+    """|x - dequant(quant(x))| <= scale/2 for every element (round to nearest
+    with the stored fp16 scale), codes in [0, 2^bits - 1], min -> code 0."""
+    rng = np.random.default_rng(5)
+    rows, d = 2000, 64
+    x = rng.standard_normal((rows, d)).astype(F32)
+    x[:, [3, 35]] *= 20
+    x[::7] *= 1e-3
+    x[::11] *= 500
+    x = x.astype(F16)
+    x[5, :] = F16(0.75)                      # constant row
+    packed, sz = O.quantize_rows(x, group, bits)
+    xr = O.dequantize_rows(packed, sz, group, bits)
+    s = np.repeat(sz[:, :, 0].astype(F64), group, axis=1)
+    err = np.abs(xr - x.astype(F64))
+    slack = 1e-6 * (np.abs(x.astype(F64)) + s)
+    assert np.all(err <= 0.5 * s + slack)
+    codes = O.unpack_codes(packed, d, bits)
+    assert codes.min() >= 0 and codes.max() <= (1 << bits) - 1
+    xs = x.reshape(rows, d // group, group)
+    cs = codes.reshape(rows, d // group, group)
+    am = xs.argmin(axis=2)
+    assert np.all(np.take_along_axis(cs, am[:, :, None], 2) == 0)
+    assert np.array_equal(xr[5], np.full(d, 0.75))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_pack_unpack_roundtrip(bits):
+    rng = np.random.default_rng(9)
+    c = rng.integers(0, 1 << bits, (13, 128))
+    assert np.array_equal(O.unpack_codes(O.pack_codes(c, bits), 128, bits), c)
+
+
+def test_quantizer_empty():
+    p, sz = O.quantize_rows(np.zeros((0, 64), F16), 32, 4)
+    assert p.shape == (0, 32) and sz.shape == (0, 2, 2)
+
+
+# ---------------------------------------------------------------- selection
+def _dominates(a1, p1, a2, p2):
+    return a1 > a2 or (a1 == a2 and p1 < p2)
+
+
+def _brute_top(score, pos, m):
+    """Unique subset of size m whose members all outrank every non-member."""
+    idx = range(len(score))
+    found = []
+    for S_ in itertools.combinations(idx, m):
+        rest = [j for j in idx if j not in S_]
+        if all(_dominates(score[i], pos[i], score[j], pos[j]) for i in S_ for j in rest):
+            found.append(sorted(S_))
+    assert len(found) == 1
+    return found[0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_top_by_key_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    T = int(rng.integers(1, 11))
+    score = rng.integers(0, 4, T).astype(F32) * F32(0.25)    # many ties
+    pos = rng.permutation(50)[:T]
+    for m in range(T + 1):
+        got = sorted(O.top_by_key(score, pos, m).tolist())
+        assert got == _brute_top(score, pos, m)
+
+
+def test_prefill_build_brute_force_tiny():
+    rng = np.random.default_rng(4)
+    T, d, B, R = 11, 8, 6, 2
+    kb = rng.standard_normal((1, 1, T, d)).astype(F16)
+    v = rng.standard_normal((1, 1, T, d)).astype(F16)
+    acc0 = (rng.integers(0, 3, (1, 1, T)) * 0.5).astype(F32)
+    st = O.prefill_build(kb, v, acc0, B, R, 4, 4, T)
+    heavy = _brute_top(acc0[0, 0, :T - R], np.arange(T - R), B - R)
+    keep = sorted(heavy + list(range(T - R, T)))
+    assert st["pos16"][0, 0, :B].tolist() == keep and st["free16"][0, 0] == B
+    rest = [p for p in range(T) if p not in keep]
+    assert st["posq"][0, 0, :T - B].tolist() == rest
+    assert np.array_equal(st["k16"][0, 0, :B], kb[0, 0, keep])
+    assert np.array_equal(st["acc16"][0, 0, :B], acc0[0, 0, keep])
+
+
+def test_decode_drop_is_minimum_key():
+    """Re-selecting top-H of H+1 candidates == dropping the candidate with the
+    smallest accumulated score (latest position among equal scores)."""
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        cap16, R, N = 9, 3, 40
+        H = cap16 - 1 - R
+        pos = rng.permutation(N - R)[:H + 1].tolist() + list(range(N - R, N))
+        pos = np.array(pos, np.int32)[rng.permutation(cap16)][None, None]
+        acc = rng.integers(0, 3, (1, 1, cap16)).astype(F64)
+        drop = O.select_drop(acc, pos, N, R, H)[0, 0]
+        cand = [s for s in range(cap16) if pos[0, 0, s] < N - R]
+        worst = min(cand, key=lambda s: (acc[0, 0, s], -pos[0, 0, s]))
+        assert drop == worst
+
+
+# ---------------------------------------------------------------- attention
+def _sdpa(q, K, V):
+    """Textbook softmax attention in float64 via the library routine."""
+    qt = torch.from_numpy(np.ascontiguousarray(q, F64))[None, None, None]
+    Kt = torch.from_numpy(np.ascontiguousarray(K, F64))[None, None]
+    Vt = torch.from_numpy(np.ascontiguousarray(V, F64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt)[0, 0, 0].numpy()
+
+
+def _build(cfg, seed, balanced=True):
+    q, k, v, acc0 = S.prefill_tensors(cfg, seed)
+    if balanced:
+        b, kb = O.balance(q, k)
+    else:
+        b = np.ones((cfg.batch, cfg.hkv, cfg.d), F32)
+        kb = k
+    st = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq())
+    return st, b, (q, k, v)
+
+
+def test_all_fp16_attention_equals_full_attention():
+    """Importance share 100% (empty low-bit tier), b = 1: the mixed attention
+    is plain softmax attention over prompt + new token."""
+    cfg = S.CONFIGS["tiny"].scaled(hq=2, hkv=1, T=40, pct=100, recent=8, factor=3.0)
+    st, b, (_, k, v) = _build(cfg, 21, balanced=False)
+    qd, kd, vd = S.decode_tensors(cfg, 21, 0)
+    N = cfg.T + 1
+    o, p16, pq, _ = O.decode_attention(st, N, qd, kd, vd, b)
+    assert pq.shape[-1] == 0
+    K = np.concatenate([k[0, 0], kd[0, :1]]).astype(F64)
+    V = np.concatenate([v[0, 0], vd[0, :1]]).astype(F64)
+    for h in range(2):
+        ref = _sdpa(qd[0, h].astype(F64), K, V)
+        assert np.max(np.abs(o[0, h] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_balanced_attention_matches_unbalanced_within_fp16_key_rounding():
+    cfg = S.CONFIGS["tiny"].scaled(hq=2, hkv=1, T=40, pct=100, recent=8, factor=3.0)
+    st, b, (_, k, v) = _build(cfg, 22, balanced=True)
+    assert not np.all(b == 1)
+    qd, kd, vd = S.decode_tensors(cfg, 22, 0)
+    o, _, _, _ = O.decode_attention(st, cfg.T + 1, qd, kd, vd, b)
+    K = np.concatenate([k[0, 0], kd[0, :1]]).astype(F64)
+    V = np.concatenate([v[0, 0], vd[0, :1]]).astype(F64)
+    for h in range(2):
+        ref = _sdpa(qd[0, h].astype(F64), K, V)
+        assert np.max(np.abs(o[0, h] - ref)) <= 1e-2 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_mixed_attention_equals_sdpa_over_both_tiers(bits):
+    cfg = S.CONFIGS["tiny"].scaled(hq=4, hkv=2, T=64, bits=bits, pct=25, recent=4)
+    st, b, _ = _build(cfg, 23)
+    qd, kd, vd = S.decode_tensors(cfg, 23, 0)
+    N = cfg.T + 1
+    o, p16, pq, st2 = O.decode_attention(st, N, qd, kd, vd, b)
+    nq = N - cfg.cap16
+    for g in range(2):
+        Kq = O.dequantize_rows(st2["kq"][0, g, :nq], st2["ksz"][0, g, :nq], cfg.G, bits)
+        Vq = O.dequantize_rows(st2["vq"][0, g, :nq], st2["vsz"][0, g, :nq], cfg.G, bits)
+        K = np.concatenate([st2["k16"][0, g].astype(F64), Kq])
+        V = np.concatenate([st2["v16"][0, g].astype(F64), Vq])
+        for r in range(2):
+            h = 2 * g + r
+            ref = _sdpa(qd[0, h].astype(F64) / b[0, g].astype(F64), K, V)
+            assert np.max(np.abs(o[0, h] - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+        # the new key is stored balanced, in the free slot
+        s = st["free16"][0, g]
+        assert np.array_equal(st2["k16"][0, g, s], (kd[0, g].astype(F32) * b[0, g]).astype(F16))
+        # probability conservation: each query head distributes mass 1
+        assert abs(p16[0, g].sum() + pq[0, g].sum() - 2.0) <= 1e-12
+
+
+def test_permutation_invariance():
+    """Attention is invariant under jointly permuting KV pairs (velog notes,
+    section 3.4); the selection is by position, so it is invariant too."""
+    cfg = S.CONFIGS["tiny"].scaled(hq=2, hkv=1, T=64, pct=25, recent=4)
+    st, b, _ = _build(cfg, 31)
+    qd, kd, vd = S.decode_tensors(cfg, 31, 0)
+    N = cfg.T + 1
+    o1, p1, st1, d1 = O.decode_step(st, N, qd, kd, vd, b, cfg.recent, cfg.H)
+    rng = np.random.default_rng(0)
+    p16 = rng.permutation(cfg.cap16)
+    nq = N - cfg.cap16
+    pq = rng.permutation(nq)
+    sp = {kk: (vv.copy() if isinstance(vv, np.ndarray) else vv) for kk, vv in st.items()}
+    for name in ("k16", "v16", "pos16", "acc16"):
+        sp[name][0, 0] = st[name][0, 0][p16]
+    sp["free16"][0, 0] = int(np.nonzero(p16 == st["free16"][0, 0])[0][0])
+    for name in ("kq", "vq", "ksz", "vsz", "posq"):
+        sp[name][0, 0, :nq] = st[name][0, 0, :nq][pq]
+    o2, p2, st2, d2 = O.decode_step(sp, N, qd, kd, vd, b, cfg.recent, cfg.H)
+    assert np.max(np.abs(o1 - o2)) <= 1e-12
+    np.testing.assert_allclose(p2[0, 0], p1[0, 0][p16], atol=1e-15)
+    assert st1["pos16"][0, 0, d1[0, 0]] == st2["pos16"][0, 0, d2[0, 0]]
+
+
+def test_uniform_low_bit_case():
+    """Importance budget 0: every cached token is low-bit; the new token is
+    the only FP16 entry and is demoted right after its step."""
+    cfg = S.CONFIGS["tiny"].scaled(T=32, pct=0, recent=0)
+    st, b, _ = _build(cfg, 41)
+    assert cfg.cap16 == 1
+    N = cfg.T + 1
+    qd, kd, vd = S.decode_tensors(cfg, 41, 0)
+    o, p16, st2, drop = O.decode_step(st, N, qd, kd, vd, b, 0, 0)
+    assert drop[0, 0] == 0 and st2["posq"][0, 0, N - 1] == N - 1
+    Kq = O.dequantize_rows(st["kq"][0, 0, :N - 1], st["ksz"][0, 0, :N - 1], cfg.G, cfg.bits)
+    Vq = O.dequantize_rows(st["vq"][0, 0, :N - 1], st["vsz"][0, 0, :N - 1], cfg.G, cfg.bits)
+    kb_new = (kd[0, 0].astype(F32) * b[0, 0]).astype(F16).astype(F64)
+    K = np.concatenate([kb_new[None], Kq])
+    V = np.concatenate([vd[0, 0].astype(F64)[None], Vq])
+    ref = _sdpa(qd[0, 0].astype(F64) / b[0, 0].astype(F64), K, V)
+    assert np.max(np.abs(o[0, 0] - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_multi_step_bookkeeping():
+    cfg = S.CONFIGS["tiny"]
+    st, b, _ = _build(cfg, 1000)
+    N = cfg.T
+    for step in range(8):
+        N += 1
+        qd, kd, vd = S.decode_tensors(cfg, 1000, step)
+        _, _, st, drop = O.decode_step(st, N, qd, kd, vd, b, cfg.recent, cfg.H)
+        live16 = np.delete(st["pos16"][0, 0], st["free16"][0, 0])
+        live = np.concatenate([live16, st["posq"][0, 0, :N - cfg.B]])
+        assert sorted(live.tolist()) == list(range(N))
+        assert set(range(N - cfg.recent, N)) <= set(live16.tolist())
+
+
+# ---------------------------------------------------------------- CriticalKV
+def test_projected_l1_closed_forms():
+    rng = np.random.default_rng(3)
+    H, T, d = 3, 5, 4
+    # W_O = identity: V_i W_O,h puts V_i in columns h*d..h*d+d-1 -> ||V_i||_1
+    V = rng.standard_normal((H, T, d)).astype(F16)
+    n1 = O.projected_value_l1(V, np.eye(H * d, dtype=F16))
+    np.testing.assert_array_equal(n1, np.abs(V.astype(F64)).sum(axis=2))
+    # V rows = unit vectors e_c: n_i = L1 norm of row h*d + c of W_O
+    W = rng.standard_normal((H * d, 7)).astype(F16)
+    c = rng.integers(0, d, (H, T))
+    Ve = np.zeros((H, T, d), F16)
+    for h in range(H):
+        Ve[h, np.arange(T), c[h]] = 1
+    n2 = O.projected_value_l1(Ve, W)
+    for h in range(H):
+        np.testing.assert_array_equal(n2[h], np.abs(W.astype(F64)[h * d + c[h]]).sum(axis=1))
+
+
+def test_criticalkv_alpha_one_is_top_attention():
+    rng = np.random.default_rng(8)
+    H, T, d = 2, 30, 4
+    A = (rng.integers(0, 6, (H, T)) / 8).astype(F32)
+    V = rng.standard_normal((H, T, d)).astype(F16)
+    W = rng.standard_normal((H * d, 5)).astype(F16)
+    idx, score2, s1 = O.criticalkv_select(A, V, W, 9, 1.0)
+    for h in range(H):
+        assert idx[h].tolist() == sorted(O.top_by_key(A[h], np.arange(T), 9).tolist())
+        assert s1[h].sum() == 9
+
+
+def test_criticalkv_constant_norm_reduces_to_attention():
+    """Equal ||V_i W_O||_1 for all i: stage 2 ranks by A alone, so the whole
+    selection is the top-budget by attention weight."""
+    rng = np.random.default_rng(9)
+    H, T, d = 2, 40, 4
+    A = rng.random((H, T)).astype(F32)
+    V = np.zeros((H, T, d), F16)
+    V[:, :, 0] = np.where(rng.random((H, T)) < 0.5, -2.0, 2.0)
+    W = rng.standard_normal((H * d, 6)).astype(F16)
+    for alpha in (0.0, 0.3, 0.5, 1.0):
+        idx, _, _ = O.criticalkv_select(A, V, W, 11, alpha)
+        for h in range(H):
+            assert idx[h].tolist() == sorted(np.argsort(-A[h].astype(F64), kind="stable")[:11].tolist())
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_criticalkv_brute_force_tiny(seed):
+    rng = np.random.default_rng(seed)
+    H, T, d = 1, int(rng.integers(3, 9)), 4
+    A = (rng.integers(0, 4, (H, T)) / 4).astype(F32)
+    V = np.zeros((H, T, d), F16)
+    V[0, np.arange(T), rng.integers(0, d, T)] = rng.integers(1, 3, T)   # n_i closed form
+    W = rng.integers(-2, 3, (H * d, 3)).astype(F16)
+    n = np.array([np.abs(W.astype(F64)[np.nonzero(V[0, i])[0][0]]).sum() * float(V[0, i].max())
+                  for i in range(T)])
+    budget = int(rng.integers(1, T + 1))
+    alpha = float(rng.choice([0.0, 0.5, 1.0]))
+    b1 = int(math.floor(alpha * budget))
+    idx, _, s1 = O.criticalkv_select(A, V, W, budget, alpha)
+    S1 = _brute_top(A[0].astype(F64), np.arange(T), b1)
+    rest = [i for i in range(T) if i not in S1]
+    sc = (A[0].astype(F64) * n)[rest]
+    S2 = [rest[j] for j in _brute_top(sc, np.array(rest), budget - b1)]
+    assert idx[0].tolist() == sorted(S1 + S2)
+    assert sorted(np.nonzero(s1[0])[0].tolist()) == S1
+
+
+def test_criticalkv_stage1_mass_closed_form():
+    """For softmax of N(0, s^2) logits, the top fraction f of entries carries
+    mass ~ Phi(s - Phi^-1(1 - f)); with s = 3, f = 0.1 this is ~0.957 > 0.5,
+    the stage-1 condition stated for CriticalKV (gist CriticalKV, Algorithm 1)."""
+    from scipy.stats import norm
+    cfg = S.CKV_CONFIGS["criticalkv_32k"]
+    A, _, _ = S.criticalkv_inputs(dataclass_replace(cfg, H=2, hidden=8), 5)
+    b1 = int(math.floor(cfg.alpha * cfg.budget))
+    expect = norm.cdf(cfg.sigma - norm.ppf(1 - b1 / cfg.T))
+    for h in range(2):
+        top = O.top_by_key(A[h], np.arange(cfg.T), b1)
+        mass = float(A[h].astype(F64)[top].sum())
+        assert mass > 0.5 and abs(mass - expect) < 0.03
+
+
+def dataclass_replace(cfg, **kw):
+    import dataclasses
+    return dataclasses.replace(cfg, **kw)
