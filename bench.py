@@ -1,0 +1,241 @@
+"""Benchmark of the MiKV mixed-precision decode path on one MI355X.
+
+A step is one decode step of the whole batch: mixed-precision attention over
+both cache tiers (append + scores + softmax + value sum, one kernel) followed
+by the H2O accumulate / re-select / demote kernel. The cache is built once
+before timing (balancer + prefill build on the GPU) from seeded synthetic
+inputs; every step consumes a new seeded (q, k, v) token per sequence and
+kv head, so the low-bit tier grows by one token per step.
+
+Before each timed step an untimed 1 GiB device write evicts the caches
+(MI355X has a 256 MB Infinity Cache, larger than the per-step working set of
+the configs), so each step streams its cache from HBM. Step and kernel times
+come from HIP events recorded on the stream the kernels run on.
+
+Prints one JSON line (rank 0). --gpus N > 1 is refused: this build targets
+one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "mixed-precision decode attn KV-tokens/s + achieved HBM GB/s (% of peak)"
+HBM_PEAK_GBPS = 8000.0
+
+
+def attn_bytes(cfg, N):
+    """Algorithmic bytes of one decode-attention launch at length N (new
+    token included): FP16 tier rows read (cap16-1) plus the new row read and
+    appended, low-bit rows (codes + fp16 scale/zero per group, K and V), q, b,
+    o and p16."""
+    d, G = cfg.d, cfg.G
+    nq = N - cfg.cap16
+    per_unit = ((cfg.cap16 - 1) * 4 * d + 4 * d + 4 * d
+                + nq * 2 * (d * cfg.bits // 8 + 4 * (d // G))
+                + cfg.rep * d * 2 + d * 4 + cfg.rep * d * 4 + cfg.cap16 * 4)
+    return per_unit * cfg.batch * cfg.hkv
+
+
+def h2o_bytes(cfg):
+    """acc16 read+write, p16 and pos16 read per FP16 slot; the demoted K/V
+    rows read and written as codes."""
+    d = cfg.d
+    per_unit = cfg.cap16 * 16 + 4 * d + 2 * (d * cfg.bits // 8 + 4 * (d // cfg.G)) + 16
+    return per_unit * cfg.batch * cfg.hkv
+
+
+def cpu_baseline(cfg, cache_np, b_np, N, seed, step, budget_s):
+    """The CPU oracle (as it stands) on a bounded sample of the same workload:
+    one sequence's decode step (all its kv heads), repeated until budget_s."""
+    import oracle as O
+    from mixed_precision_decode_amd import synth as S
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    sub = {k: (v[:1].copy() if isinstance(v, np.ndarray) else v) for k, v in cache_np.items()}
+    qd, kd, vd = S.decode_tensors(cfg.scaled(batch=1), seed, step)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.decode_step(sub, N, qd, kd, vd, b_np[:1], cfg.recent, cfg.H)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": reps * N / el, "unit": "KV-tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{reps} oracle decode steps of 1 of {cfg.batch} sequences "
+                       f"({cfg.hkv} kv heads, N={N}), fp64 numpy, {el:.1f} s; "
+                       f"host os.cpu_count()={os.cpu_count()}")}
+
+
+def calibrate_copy(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size: the reference kernel
+    whose FETCH_SIZE / WRITE_SIZE readings scale the counters of the MiKV
+    kernels."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ts = []
+    for _ in range(reps):
+        ev[0].record()
+        dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ts.append(ev[0].elapsed_time(ev[1]))
+    t = float(np.median(ts)) * 1e-3
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
+                      "copy_GBps": 2 * nbytes / t / 1e9}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2_7b_layer")
+    ap.add_argument("--seed", type=int, default=1001)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference kernel for HBM counters)")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs the MiKV path on one GPU only; --gpus must be 1 "
+              "(the path shards by (sequence, kv head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixed_precision_decode_amd import _lib as L
+    from mixed_precision_decode_amd import synth as S
+
+    cfg = S.CONFIGS[args.workload]
+    K, W = args.steps, args.warmup
+    total = K + W
+    assert total <= cfg.steps, f"the workload defines {cfg.steps} decode steps"
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    t0 = time.perf_counter()
+    q, k, v, acc0 = S.prefill_tensors(cfg, args.seed)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
+    dims = L.Dims(batch=cfg.batch, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, group=cfg.G, bits=cfg.bits,
+                  cap16=cfg.cap16, capq=cfg.T - cfg.B + total)
+    cache = L.Cache(dims)
+    b = torch.empty((cfg.batch, cfg.hkv, cfg.d), dtype=torch.float32, device="cuda")
+    qg, kg = dev(q), dev(k)
+    ws_b = torch.empty(L.mikv_balance_workspace(dims, cfg.T), dtype=torch.uint8, device="cuda")
+    L.mikv_balance_prefill(dims, cfg.T, qg, kg, b, None, ws_b)
+    del qg, q
+    ws_h = torch.empty(L.mikv_h2o_workspace(dims, cfg.T), dtype=torch.uint8, device="cuda")
+    L.mikv_h2o_update_select(dims, cache, cfg.T, cfg.recent, cfg.H,
+                             src=dict(k=kg, v=dev(v), acc0=dev(acc0), b=b), ws=ws_h)
+    torch.cuda.synchronize()
+    del kg, ws_h, ws_b
+    steps_in = [tuple(dev(x) for x in S.decode_tensors(cfg, args.seed, s)) for s in range(total)]
+    o = torch.empty((cfg.batch, cfg.hq, cfg.d), dtype=torch.float32, device="cuda")
+    p16 = torch.empty((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + total), dtype=torch.uint8,
+                     device="cuda")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    log(f"[bench] cache built ({time.perf_counter() - t0:.1f}s); warmup {W}, timed {K}")
+
+    N = cfg.T
+    cpu_state = None
+
+    def one_step(s, ev=None):
+        nonlocal N
+        N += 1
+        qd, kd, vd = steps_in[s]
+        if ev is not None:
+            ev[0].record()
+        L.mikv_decode_attn(dims, cache, N, qd, kd, vd, b, o, p16, ws)
+        if ev is not None:
+            ev[1].record()
+        L.mikv_h2o_update_select(dims, cache, N, cfg.recent, cfg.H, p16=p16)
+        if ev is not None:
+            ev[2].record()
+
+    for s in range(W):
+        if not args.no_flush:
+            flush.fill_(float(s))
+        one_step(s)
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        cpu_state = (cache.to_numpy(), b.cpu().numpy(), N + 1, W)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    lens = []
+    torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    for i in range(K):
+        if not args.no_flush:
+            flush.fill_(float(i))
+        one_step(W + i, evs[i])
+        lens.append(N)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - tw0
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    lens = np.array(lens)
+    ms_per_step = float(step_ms.mean())
+    value = float(cfg.batch * lens.mean() / (ms_per_step * 1e-3))
+    abytes = np.array([attn_bytes(cfg, n) for n in lens], dtype=np.float64)
+    a_gbps = float((abytes / (attn_ms * 1e-3)).mean() / 1e9)
+    s_gbps = float(((abytes + h2o_bytes(cfg)) / (step_ms * 1e-3)).mean() / 1e9)
+    log(f"[bench] attn {attn_ms.mean() * 1e3:.1f} us ({a_gbps:.0f} GB/s), step "
+        f"{ms_per_step * 1e3:.1f} us ({s_gbps:.0f} GB/s), wall incl. flush {wall / K * 1e3:.3f} ms/step")
+
+    cpu = None
+    if cpu_state is not None:
+        cache_np, b_np, Nc, st = cpu_state
+        cpu = cpu_baseline(cfg, cache_np, b_np, Nc, args.seed, st, args.cpu_seconds)
+        log(f"[bench] cpu oracle {cpu['value']:.3g} KV-tokens/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "q_heads": cfg.hq, "kv_heads": cfg.hkv,
+                   "head_dim": cfg.d, "context": cfg.T, "low_bits": cfg.bits,
+                   "important_pct": cfg.pct, "recent": cfg.recent, "group": cfg.G,
+                   "cache_flush_per_step": not args.no_flush},
+        "roofline": {"bound": "hbm", "achieved": a_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": a_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "decode_split_kernel + decode_merge_kernel (one mikv_decode_attn call)", "kernel_us": float(attn_ms.mean() * 1e3),
+                     "bytes_per_launch": float(abytes.mean())},
+        "step_hbm_gbps": s_gbps,
+        "wall_ms_per_step_incl_flush": wall / K * 1e3,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

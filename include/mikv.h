@@ -1,0 +1,250 @@
+/*
+ * mikv.h - C interface of the MiKV mixed-precision KV-cache path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method sources (cited by page title and section):
+ *   [velog notes]      velog.io post "No Token Left Behind: Reliable KV Cache
+ *                      Compression via Importance-Aware Mixed Precision
+ *                      Quantization" (reader's notes on arXiv 2402.18096).
+ *   [paperlayer]       paperlayer.ai source-linked summary of arXiv
+ *                      2402.18096v1, "No Token Left Behind ...".
+ *   [gist CriticalKV]  gist.science technical summary of arXiv 2502.03805
+ *                      (CriticalKV).
+ *
+ * Conventions for every entry point
+ *   - fp16 tensors are passed as uint16_t bit patterns (IEEE binary16).
+ *   - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *     never allocates, frees or synchronises, and keeps no mutable global
+ *     state. Tensors are dense row-major in the index order written next to
+ *     them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls validate their arguments on the host, enqueue kernels on
+ *     `stream` and return at once. On a validation failure nothing is
+ *     enqueued and the status says why. A failed launch returns
+ *     MIKV_ERR_HIP. Faults inside kernels surface at the caller's next
+ *     synchronisation. No C++ exception crosses this interface.
+ *   - Supported shapes: head dim d in {64, 128}; bits in {2, 4}; group in
+ *     {d/2, d} (d/2 is the method's setting); hq a multiple of hkv.
+ *   - Inputs must be finite; non-finite values give unspecified results.
+ *
+ * Two-tier cache (mikv_cache), per sequence n and kv head g:
+ *   FP16 "importance" tier, cap16 slots:
+ *     k16, v16 [batch][hkv][cap16][d] fp16   balanced keys k*b, values
+ *     pos16    [batch][hkv][cap16]    int32  token position of the slot
+ *     acc16    [batch][hkv][cap16]    fp32   H2O accumulated attention
+ *     free16   [batch][hkv]           int32  the one free slot
+ *   Low-bit "retention" tier, capq slots, filled in order 0,1,2,...:
+ *     kq, vq   [batch][hkv][capq][d*bits/8] uint8  packed codes
+ *     ksz, vsz [batch][hkv][capq][d/group][2] fp16 (scale, zero) per group
+ *     posq     [batch][hkv][capq]     int32  token position of the slot
+ *   Code packing: code of channel (8/bits)*j + m sits in bits
+ *   [bits*m, bits*m+bits) of byte j. Dequantized value = code*scale + zero.
+ *   Grouping pairs by precision is allowed because attention is invariant
+ *   under jointly permuting KV pairs ([velog notes] section 3.4).
+ *   With B = cap16 - 1 important tokens and a current length N (new token
+ *   included), the low-bit tier holds N - 1 - B tokens when a decode step
+ *   starts and N - B after it.
+ */
+#ifndef MIKV_H
+#define MIKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MIKV_ABI_VERSION 1
+
+typedef enum {
+  MIKV_OK = 0,
+  MIKV_ERR_NULL = 1,        /* a required pointer is NULL                   */
+  MIKV_ERR_SHAPE = 2,       /* sizes inconsistent with each other           */
+  MIKV_ERR_UNSUPPORTED = 3, /* d, bits or group outside the supported set   */
+  MIKV_ERR_CAPACITY = 4,    /* the low-bit tier would exceed capq slots     */
+  MIKV_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required      */
+  MIKV_ERR_HIP = 6          /* a HIP call or kernel launch failed           */
+} mikv_status;
+
+/* Static English text for a status value (never NULL). */
+const char* mikv_status_str(int status);
+
+/* MIKV_ABI_VERSION of the built library. */
+int mikv_abi_version(void);
+
+typedef struct {
+  int32_t batch; /* sequences n                                            */
+  int32_t hq;    /* query heads                                            */
+  int32_t hkv;   /* kv heads; query head h uses kv head h / (hq/hkv)       */
+  int32_t d;     /* head dim, 64 or 128                                    */
+  int32_t group; /* channels per quantization group: d/2 or d              */
+  int32_t bits;  /* low-bit code width, 4 or 2                             */
+  int32_t cap16; /* FP16-tier slots per (n, g) = B + 1                     */
+  int32_t capq;  /* low-bit-tier slots per (n, g)                          */
+} mikv_dims;
+
+typedef struct {
+  uint16_t* k16;
+  uint16_t* v16;
+  int32_t* pos16;
+  float* acc16;
+  int32_t* free16;
+  uint8_t* kq;
+  uint8_t* vq;
+  uint16_t* ksz;
+  uint16_t* vsz;
+  int32_t* posq;
+} mikv_cache;
+
+/*
+ * Channel balancer ([velog notes] Key contributions 2), balancer equation
+ * and k-hat equation; [paperlayer] section 3.2).
+ *   b[n][g][c] = sqrt( max_{h in group g, t < T} |q[n][h][t][c]|
+ *                      / max_{t < T} |k[n][g][t][c]| )      (fp32 IEEE ops)
+ *   b = 1 where either maximum is 0 (also when T == 0).
+ *   kb[n][g][t][c] = fp16_rne( fp32(k) * b[n][g][c] ), written if kb != NULL.
+ * q  [batch][hq][T][d] fp16, k [batch][hkv][T][d] fp16 (inputs).
+ * b  [batch][hkv][d] fp32 (output), kb [batch][hkv][T][d] fp16 (output).
+ * ws: workspace of mikv_balance_workspace(dims, T) bytes (any contents).
+ * dims->group, bits, cap16, capq are not used.
+ */
+size_t mikv_balance_workspace(const mikv_dims* dims, int32_t T);
+mikv_status mikv_balance_prefill(const mikv_dims* dims, int32_t T,
+                                 const uint16_t* q, const uint16_t* k,
+                                 float* b, uint16_t* kb,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Per-token asymmetric quantization with groups ([velog notes] Key
+ * contributions 1): per-token asymmetric (LLM-QAT style); Key contributions
+ * 2), additional notes: group = half the head dim; [paperlayer] section 3.2).
+ * For output row r, source row x[rows ? rows[r] : r] and each group of
+ * `group` contiguous channels:
+ *   scale = fp16_rne((fp32(max) - fp32(min)) / (2^bits - 1)), zero = min;
+ *   code  = clamp(rint_half_even((fp32(x) - fp32(zero)) / fp32(scale)),
+ *                 0, 2^bits - 1), all codes 0 when scale == 0;
+ *   a zero scale or zero point is stored as +0.
+ * x [*][d] fp16; rows [n_rows] int32 or NULL; codes [n_rows][d*bits/8] uint8
+ * and sz [n_rows][d/group][2] fp16 (outputs). n_rows == 0 enqueues nothing.
+ * The caller guarantees 0 <= rows[r] < (rows of x).
+ */
+mikv_status mikv_quantize_tokens(const uint16_t* x, const int32_t* rows,
+                                 int64_t n_rows, int32_t d, int32_t group,
+                                 int32_t bits, uint8_t* codes, uint16_t* sz,
+                                 void* stream);
+
+/*
+ * One decode step of mixed-precision attention ([velog notes] section 3.4
+ * and [paperlayer] section 3.4: decode attention is a memory-bound batched
+ * matrix-vector product over a precision-grouped cache whose keys and values
+ * are low precision while the query and the attention map stay floating
+ * point; [velog notes] Key contributions 2): q-hat = q / b).
+ *   1. Append: the new token (position len-1) goes into FP16 slot
+ *      free16[n][g]: k16 = fp16_rne(fp32(k_new) * b), v16 = v_new,
+ *      pos16 = len-1 (acc16 and free16 are left to mikv_h2o_update_select).
+ *   2. For each query head h of kv head g, q-hat = fp32(q) / b and
+ *      s_i = q-hat . k~_i / sqrt(d) over the cap16 FP16-tier tokens
+ *      (k~ = k16) and the len - cap16 low-bit tokens (k~ = code*scale+zero);
+ *      p = softmax(s) over both tiers; o[n][h] = sum_i p_i v~_i.
+ *   3. p16[n][g][slot] = sum over the query heads of group g of p at that
+ *      FP16 slot (input of the H2O accumulation).
+ * Precondition: the low-bit tier holds len - cap16 tokens (slots
+ * 0..len-cap16-1); every FP16 slot other than free16 is occupied.
+ * q [batch][hq][d] fp16, k_new/v_new [batch][hkv][d] fp16, b [batch][hkv][d]
+ * fp32 (inputs); o [batch][hq][d] fp32, p16 [batch][hkv][cap16] fp32
+ * (outputs). Accumulation is fp32.
+ * ws: mikv_decode_attn_workspace(dims, max_len) bytes (any contents), valid
+ * for any len <= max_len; it holds the per-split partial results between the
+ * two kernels of the call. One workspace serves one call at a time.
+ * Errors: len - cap16 < 0 -> MIKV_ERR_SHAPE; len - cap16 > capq ->
+ * MIKV_ERR_CAPACITY.
+ */
+size_t mikv_decode_attn_workspace(const mikv_dims* dims, int32_t max_len);
+mikv_status mikv_decode_attn(const mikv_dims* dims, const mikv_cache* cache,
+                             int32_t len, const uint16_t* q,
+                             const uint16_t* k_new, const uint16_t* v_new,
+                             const float* b, float* o, float* p16,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Source of the prefill build of mikv_h2o_update_select.
+ *   k    [batch][hkv][T][d] fp16  prompt keys (multiplied by b when b != NULL,
+ *                                 exactly as mikv_balance_prefill's kb)
+ *   v    [batch][hkv][T][d] fp16  prompt values
+ *   acc0 [batch][hkv][T]    fp32  accumulated attention of the prompt (>= 0)
+ *   b    [batch][hkv][d]    fp32  balancer or NULL (keys used as given)
+ */
+typedef struct {
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* acc0;
+  const float* b;
+  int32_t T;
+} mikv_prefill_src;
+
+/*
+ * Heavy-hitter bookkeeping, important-set re-selection and demotion
+ * ([velog notes] one-line summary and Key contributions 1): tokens an
+ * importance-based (H2O) eviction would drop are kept as low-bit codes;
+ * [paperlayer] section 5: heavy hitters plus local tokens). The ranking key
+ * is (accumulated attention descending, token position ascending). The
+ * recent window is the `recent` newest positions. Requires
+ * heavy + recent == cap16 - 1 (= B).
+ *
+ * Decode mode (p16 != NULL, src == NULL), after mikv_decode_attn at the
+ * same len:
+ *   acc16[slot] = (slot == free16 ? 0 : acc16[slot]) + p16[slot];
+ *   candidates = FP16 slots with pos16 < len - recent (heavy + 1 of them);
+ *   the candidate outside the top-`heavy` is quantized (as in
+ *   mikv_quantize_tokens, keys and values) into low-bit slot len - cap16,
+ *   its position copied to posq, and free16 set to its slot.
+ *   demoted_pos[n][g] (optional) receives its position.
+ * Prefill mode (p16 == NULL, src != NULL, len == src->T):
+ *   important = positions >= T - recent plus the top-`heavy` positions of
+ *   [0, T - recent) by (acc0 desc, position asc); they fill FP16 slots
+ *   0..B-1 in ascending position with acc16 = acc0, free16 = B; the other
+ *   T - B positions are quantized into low-bit slots 0..T-B-1 in ascending
+ *   position. demoted_pos is ignored.
+ * ws: mikv_h2o_workspace(dims, max_T) bytes (any contents; decode mode
+ * needs none and accepts ws == NULL).
+ * Errors: T < B -> MIKV_ERR_SHAPE; low-bit tier overflow -> MIKV_ERR_CAPACITY.
+ */
+size_t mikv_h2o_workspace(const mikv_dims* dims, int32_t max_T);
+mikv_status mikv_h2o_update_select(const mikv_dims* dims,
+                                   const mikv_cache* cache, int32_t len,
+                                   int32_t recent, int32_t heavy,
+                                   const float* p16,
+                                   const mikv_prefill_src* src,
+                                   int32_t* demoted_pos, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/*
+ * CriticalKV two-stage selection per head ([gist CriticalKV] Algorithm 1;
+ * theoretical framework: the output perturbation bound depends on the
+ * attention weights and the value states projected by W_O).
+ *   b1 = floor(alpha * budget), b2 = budget - b1;
+ *   S1 = top-b1 of A[h] by (A desc, index asc);
+ *   n_i = sum_j | sum_c V[h][i][c] * W_O[h*d + c][j] |  for i not in S1
+ *         (fp16 products, fp32 accumulation);
+ *   score2[h][i] = A[h][i] * n_i (fp32) for i not in S1, -1 for i in S1;
+ *   S2 = top-b2 of the rest by (score2 desc, index asc);
+ *   idx[h] = S1 u S2 in ascending order.
+ * A [H][T] fp32 (>= 0), V [H][T][d] fp16, W_O [H*d][hidden] fp16 (inputs);
+ * idx [H][budget] int32, score2 [H][T] fp32 or NULL (outputs).
+ * ws: mikv_criticalkv_workspace(H, T, d, hidden) bytes (any contents).
+ * Requires d == 128, hidden % 128 == 0, 1 <= budget <= T, 0 <= alpha <= 1.
+ */
+size_t mikv_criticalkv_workspace(int32_t H, int32_t T, int32_t d,
+                                 int32_t hidden);
+mikv_status mikv_criticalkv_select(const float* A, const uint16_t* V,
+                                   const uint16_t* W_O, int32_t H, int32_t T,
+                                   int32_t d, int32_t hidden, int32_t budget,
+                                   float alpha, int32_t* idx, float* score2,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIKV_H */

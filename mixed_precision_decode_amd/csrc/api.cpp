@@ -1,0 +1,205 @@
+// C interface of the MiKV library: host-side validation and launches.
+// Every function validates its arguments before anything is enqueued; see
+// include/mikv.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.hpp"
+#include "mikv.h"
+
+using namespace mikv;
+
+namespace {
+
+bool supported_dims(int d, int group, int bits) {
+  if (d != 64 && d != 128) return false;
+  if (bits != 2 && bits != 4) return false;
+  return group == d / 2 || group == d;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mikv_status check_dims(const mikv_dims* m, bool need_tiers) {
+  if (!m) return MIKV_ERR_NULL;
+  if (m->batch < 1 || m->hq < 1 || m->hkv < 1 || m->d < 1) return MIKV_ERR_SHAPE;
+  if (m->hq % m->hkv != 0) return MIKV_ERR_SHAPE;
+  if (m->d != 64 && m->d != 128) return MIKV_ERR_UNSUPPORTED;
+  if (need_tiers) {
+    if (m->group < 1 || m->d % m->group != 0) return MIKV_ERR_SHAPE;
+    if (m->bits != 2 && m->bits != 4) return MIKV_ERR_UNSUPPORTED;
+    if (!supported_dims(m->d, m->group, m->bits)) return MIKV_ERR_UNSUPPORTED;
+    if (m->cap16 < 1 || m->capq < 0) return MIKV_ERR_SHAPE;
+  }
+  return MIKV_OK;
+}
+
+mikv_status check_cache(const mikv_cache* c) {
+  if (!c) return MIKV_ERR_NULL;
+  if (!c->k16 || !c->v16 || !c->pos16 || !c->acc16 || !c->free16 || !c->kq || !c->vq ||
+      !c->ksz || !c->vsz || !c->posq)
+    return MIKV_ERR_NULL;
+  if (!aligned16(c->k16) || !aligned16(c->v16) || !aligned16(c->kq) || !aligned16(c->vq))
+    return MIKV_ERR_SHAPE;
+  return MIKV_OK;
+}
+
+mikv_status from_hip(hipError_t e) { return e == hipSuccess ? MIKV_OK : MIKV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mikv_status_str(int s) {
+  switch (s) {
+    case MIKV_OK: return "ok";
+    case MIKV_ERR_NULL: return "a required pointer is NULL";
+    case MIKV_ERR_SHAPE: return "inconsistent sizes";
+    case MIKV_ERR_UNSUPPORTED: return "unsupported head dim, bit width or group size";
+    case MIKV_ERR_CAPACITY: return "low-bit tier capacity exceeded";
+    case MIKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case MIKV_ERR_HIP: return "HIP call or kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mikv_abi_version(void) { return MIKV_ABI_VERSION; }
+
+// ---------------------------------------------------------------- balancer
+size_t mikv_balance_workspace(const mikv_dims* m, int32_t T) {
+  if (check_dims(m, false) != MIKV_OK || T < 0) return 0;
+  return balance_ws_bytes(m->batch, m->hkv, m->hq / m->hkv, m->d, T);
+}
+
+mikv_status mikv_balance_prefill(const mikv_dims* m, int32_t T, const uint16_t* q,
+                                 const uint16_t* k, float* b, uint16_t* kb, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  mikv_status st = check_dims(m, false);
+  if (st != MIKV_OK) return st;
+  if (T < 0) return MIKV_ERR_SHAPE;
+  if (!b) return MIKV_ERR_NULL;
+  if (T > 0 && (!q || !k)) return MIKV_ERR_NULL;
+  if (T > 0 && (!aligned16(q) || !aligned16(k) || (kb && !aligned16(kb)))) return MIKV_ERR_SHAPE;
+  const size_t need = balance_ws_bytes(m->batch, m->hkv, m->hq / m->hkv, m->d, T);
+  if (need > 0 && (!ws || ws_bytes < need)) return MIKV_ERR_WORKSPACE;
+  return from_hip(launch_balance(m->batch, m->hq, m->hkv, m->d, T, q, k, b, kb, ws,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- quantize
+mikv_status mikv_quantize_tokens(const uint16_t* x, const int32_t* rows, int64_t n_rows,
+                                 int32_t d, int32_t group, int32_t bits, uint8_t* codes,
+                                 uint16_t* sz, void* stream) {
+  if (n_rows < 0 || d < 1 || group < 1) return MIKV_ERR_SHAPE;
+  if (d % group != 0 || group % (8 / (bits == 2 ? 2 : 4)) != 0) return MIKV_ERR_SHAPE;
+  if (!supported_dims(d, group, bits)) return MIKV_ERR_UNSUPPORTED;
+  if (n_rows == 0) return MIKV_OK;
+  if (!x || !codes || !sz) return MIKV_ERR_NULL;
+  if (!aligned16(x)) return MIKV_ERR_SHAPE;
+  return from_hip(launch_quantize_rows(x, rows, n_rows, d, group, bits, codes, sz,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- decode attention
+size_t mikv_decode_attn_workspace(const mikv_dims* m, int32_t max_len) {
+  if (check_dims(m, true) != MIKV_OK) return 0;
+  const int nq = max_len - m->cap16;
+  if (nq < 0) return 0;
+  const DecodePlan pl = decode_plan(m->d, m->bits, m->hq / m->hkv, m->cap16, nq);
+  return decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, pl);
+}
+
+mikv_status mikv_decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t len,
+                             const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                             const float* b, float* o, float* p16, void* ws, size_t ws_bytes,
+                             void* stream) {
+  mikv_status st = check_dims(m, true);
+  if (st != MIKV_OK) return st;
+  st = check_cache(c);
+  if (st != MIKV_OK) return st;
+  if (!q || !k_new || !v_new || !b || !o || !p16) return MIKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new)) return MIKV_ERR_SHAPE;
+  const int nq = len - m->cap16;
+  if (nq < 0) return MIKV_ERR_SHAPE;
+  if (nq > m->capq) return MIKV_ERR_CAPACITY;
+  const DecodePlan pl = decode_plan(m->d, m->bits, m->hq / m->hkv, m->cap16, nq);
+  const size_t need = decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, pl);
+  if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
+  DecodeArgs a;
+  a.batch = m->batch; a.hq = m->hq; a.hkv = m->hkv; a.d = m->d; a.group = m->group;
+  a.bits = m->bits; a.cap16 = m->cap16; a.capq = m->capq; a.len = len;
+  a.q = q; a.k_new = k_new; a.v_new = v_new; a.b = b;
+  a.k16 = c->k16; a.v16 = c->v16; a.pos16 = c->pos16; a.free16 = c->free16;
+  a.kq = c->kq; a.vq = c->vq; a.ksz = c->ksz; a.vsz = c->vsz;
+  a.o = o; a.p16 = p16; a.ws = ws;
+  return from_hip(launch_decode_attn(a, pl, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- H2O
+size_t mikv_h2o_workspace(const mikv_dims* m, int32_t max_T) {
+  if (check_dims(m, true) != MIKV_OK || max_T < 0) return 0;
+  return h2o_ws_bytes(m->batch, m->hkv, max_T);
+}
+
+mikv_status mikv_h2o_update_select(const mikv_dims* m, const mikv_cache* c, int32_t len,
+                                   int32_t recent, int32_t heavy, const float* p16,
+                                   const mikv_prefill_src* src, int32_t* demoted_pos, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  mikv_status st = check_dims(m, true);
+  if (st != MIKV_OK) return st;
+  st = check_cache(c);
+  if (st != MIKV_OK) return st;
+  if ((p16 == nullptr) == (src == nullptr)) return MIKV_ERR_NULL;
+  if (recent < 0 || heavy < 0 || heavy + recent != m->cap16 - 1) return MIKV_ERR_SHAPE;
+  H2OArgs a = {};
+  a.batch = m->batch; a.hkv = m->hkv; a.d = m->d; a.group = m->group; a.bits = m->bits;
+  a.cap16 = m->cap16; a.capq = m->capq; a.len = len; a.recent = recent; a.heavy = heavy;
+  a.k16 = c->k16; a.v16 = c->v16; a.pos16 = c->pos16; a.acc16 = c->acc16; a.free16 = c->free16;
+  a.kq = c->kq; a.vq = c->vq; a.ksz = c->ksz; a.vsz = c->vsz; a.posq = c->posq;
+  const int B = m->cap16 - 1;
+  if (p16) {
+    // decode: the low-bit tier grows to len - B tokens
+    if (len - m->cap16 < 0) return MIKV_ERR_SHAPE;
+    if (len - B > m->capq) return MIKV_ERR_CAPACITY;
+    a.p16 = p16;
+    a.demoted_pos = demoted_pos;
+    return from_hip(launch_h2o_decode(a, static_cast<hipStream_t>(stream)));
+  }
+  if (src->T != len || len < B) return MIKV_ERR_SHAPE;
+  if (len > 0 && (!src->k || !src->v || !src->acc0)) return MIKV_ERR_NULL;
+  if (len > 0 && (!aligned16(src->k) || !aligned16(src->v))) return MIKV_ERR_SHAPE;
+  if (len - B > m->capq) return MIKV_ERR_CAPACITY;
+  const size_t need = h2o_ws_bytes(m->batch, m->hkv, len);
+  if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
+  a.src_k = src->k; a.src_v = src->v; a.src_acc0 = src->acc0; a.src_b = src->b;
+  a.ws = ws;
+  return from_hip(launch_h2o_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- CriticalKV
+size_t mikv_criticalkv_workspace(int32_t H, int32_t T, int32_t d, int32_t hidden) {
+  if (H < 1 || T < 1 || d != 128 || hidden < 128 || hidden % 128 != 0) return 0;
+  return criticalkv_ws_bytes(H, T, d, hidden);
+}
+
+mikv_status mikv_criticalkv_select(const float* A, const uint16_t* V, const uint16_t* W_O,
+                                   int32_t H, int32_t T, int32_t d, int32_t hidden,
+                                   int32_t budget, float alpha, int32_t* idx, float* score2,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  if (!A || !V || !W_O || !idx) return MIKV_ERR_NULL;
+  if (H < 1 || T < 1 || hidden < 1) return MIKV_ERR_SHAPE;
+  if (d != 128) return MIKV_ERR_UNSUPPORTED;
+  if (hidden % 128 != 0) return MIKV_ERR_UNSUPPORTED;
+  if (budget < 1 || budget > T) return MIKV_ERR_SHAPE;
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return MIKV_ERR_SHAPE;
+  if (!aligned16(V) || !aligned16(W_O)) return MIKV_ERR_SHAPE;
+  const size_t need = criticalkv_ws_bytes(H, T, d, hidden);
+  if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
+  const int b1 = static_cast<int>(std::floor(static_cast<double>(alpha) * budget));
+  const int b2 = budget - b1;
+  return from_hip(launch_criticalkv(A, V, W_O, H, T, d, hidden, b1, b2, idx, score2, ws,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// Shared device helpers of the MiKV HIP library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mikv {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float h2f(uint16_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, bits));
+}
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default mode).
+__device__ __forceinline__ uint16_t f2h(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+// fp32 product rounded to fp32 before anything else: the empty asm keeps the
+// compiler from fusing the multiply with a following fp16 conversion
+// (v_fma_mixlo_f16 rounds once), so fp16(mul_rn(a, b)) is the two-step
+// rounding fp16(fp32(a*b)).
+__device__ __forceinline__ float mul_rn(float a, float b) {
+  float p = a * b;
+  asm volatile("" : "+v"(p));
+  return p;
+}
+__device__ __forceinline__ float lo_h(uint32_t w) { return h2f(static_cast<uint16_t>(w & 0xFFFFu)); }
+__device__ __forceinline__ float hi_h(uint32_t w) { return h2f(static_cast<uint16_t>(w >> 16)); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane data movement inside a row of 16 lanes (DPP) and across rows.
+// DPP controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_half_mirror = 0x141, row_mirror = 0x140, row_ror:n = 0x120 + n.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+
+// Sum / max over aligned groups of N lanes (N in {1,2,4,8,16}); every lane of
+// the group ends with the result.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<0xB1>(v);
+  if constexpr (N >= 4) v += dpp<0x4E>(v);
+  if constexpr (N >= 8) v += dpp<0x141>(v);
+  if constexpr (N >= 16) v += dpp<0x140>(v);
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (N >= 2) v = fmaxf(v, dpp<0xB1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp<0x4E>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp<0x141>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp<0x140>(v));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_min(float v) {
+  if constexpr (N >= 2) v = fminf(v, dpp<0xB1>(v));
+  if constexpr (N >= 4) v = fminf(v, dpp<0x4E>(v));
+  if constexpr (N >= 8) v = fminf(v, dpp<0x141>(v));
+  if constexpr (N >= 16) v = fminf(v, dpp<0x140>(v));
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) {
+  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, v), m));
+}
+
+// Sum over lanes that share (lane % S) within the wave, S a power of two <= 16.
+template <int S>
+__device__ __forceinline__ float sum_over_stride(float v) {
+  if constexpr (S <= 1) v += shfl_xor_f(v, 1);
+  if constexpr (S <= 2) v += shfl_xor_f(v, 2);
+  if constexpr (S <= 4) v += shfl_xor_f(v, 4);
+  if constexpr (S <= 8) v += shfl_xor_f(v, 8);
+  if constexpr (S <= 16) v += shfl_xor_f(v, 16);
+  v += shfl_xor_f(v, 32);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Per-token asymmetric quantization of one group held by NL lanes, 8
+// channels per lane (velog notes "No Token Left Behind ...", Key
+// contributions 1) and 2): per-token asymmetric codes, groups of d/2).
+// Fixed fp32 sequence: scale = fp16((max - min) / qmax), zero = min,
+// code = clamp(rint((x - zero) / scale), 0, qmax); zeros stored as +0.
+// Returns the packed codes of the lane's 8 channels in the low 8*BITS bits
+// and writes (scale | zero << 16) to *sz_word.
+// ---------------------------------------------------------------------------
+template <int BITS, int NL>
+__device__ __forceinline__ uint32_t quantize8(const float (&x)[8], uint32_t* sz_word) {
+  constexpr float qmax = static_cast<float>((1 << BITS) - 1);
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    mn = fminf(mn, x[i]);
+    mx = fmaxf(mx, x[i]);
+  }
+  mn = group_min<NL>(mn);
+  mx = group_max<NL>(mx);
+  const float s32 = (mx - mn) / qmax;
+  uint16_t s16 = f2h(s32);
+  if ((s16 & 0x7FFFu) == 0) s16 = 0;
+  uint16_t z16 = f2h(mn);  // exact: mn is an fp16 value
+  if ((z16 & 0x7FFFu) == 0) z16 = 0;
+  *sz_word = static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16);
+  uint32_t packed = 0;
+  if (s16 != 0) {
+    const float s = h2f(s16);
+    const float z = h2f(z16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float t = rintf((x[i] - z) / s);
+      t = fminf(fmaxf(t, 0.0f), qmax);
+      packed |= static_cast<uint32_t>(t) << (BITS * i);
+    }
+  }
+  return packed;
+}
+
+// Load 8 fp16 values (16 bytes) and widen to fp32.
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  x[0] = lo_h(w.x); x[1] = hi_h(w.x);
+  x[2] = lo_h(w.y); x[3] = hi_h(w.y);
+  x[4] = lo_h(w.z); x[5] = hi_h(w.z);
+  x[6] = lo_h(w.w); x[7] = hi_h(w.w);
+}
+
+// Store packed codes of 8 channels: INT4 -> one 32-bit word, INT2 -> 16 bits.
+template <int BITS>
+__device__ __forceinline__ void store_codes8(uint8_t* row_codes, int lane_in_row, uint32_t packed) {
+  if constexpr (BITS == 4) {
+    reinterpret_cast<uint32_t*>(row_codes)[lane_in_row] = packed;
+  } else {
+    reinterpret_cast<uint16_t*>(row_codes)[lane_in_row] = static_cast<uint16_t>(packed);
+  }
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger key);
+// -0 is treated as +0.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace mikv

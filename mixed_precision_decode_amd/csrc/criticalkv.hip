@@ -1,0 +1,290 @@
+// CriticalKV two-stage selection (gist.science summary of arXiv 2502.03805,
+// "Algorithm 1": stage 1 takes alpha*budget entries with the largest
+// attention weight; stage 2 takes the rest by attention weight times the L1
+// norm of the value state projected by the output matrix W_O, the quantity
+// the perturbation bound of the theoretical framework depends on).
+//
+// Kernels (one launch each, all on the caller's stream):
+//   stage1  per head: radix top-b1 of A; marks stage-1 entries, writes -1 to
+//           their score2 and the ascending list of the other rows.
+//   project MFMA GEMM (v_mfma_f32_32x32x16_f16, fp32 accumulation) of the
+//           listed V rows with the head's W_O slice, with the |.| row sum
+//           fused into the epilogue so the [rows x hidden] product is never
+//           stored: score2[i] = A[i] * sum_j |(V_i W_O,h)_j|.
+//   stage2  per head: radix top-b2 of score2 outside stage 1, then the
+//           ascending union of both stages.
+// The projection is the only dense contraction of the method; it is the
+// kernel bound by the matrix cores.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "topk.hpp"
+
+namespace mikv {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kCkvD = 128;     // head dim (contraction length)
+constexpr int kBM = 256;       // rows per block (4 waves x 64)
+constexpr int kBN = 64;        // hidden columns per step
+constexpr int kLdw = kCkvD + 8;  // padded LDS row (halves) of the transposed W tile
+
+struct CkvWs {
+  uint8_t* s1;      // [H][T] stage-1 membership
+  int32_t* rows2;   // [H][T - b1] rows outside stage 1, ascending
+  float* score2;    // [H][T] used when the caller passes no score2
+};
+
+static inline size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+static CkvWs carve(void* ws, int H, int T) {
+  char* w = static_cast<char*>(ws);
+  CkvWs r;
+  r.s1 = reinterpret_cast<uint8_t*>(w);
+  w += al256(static_cast<size_t>(H) * T);
+  r.rows2 = reinterpret_cast<int32_t*>(w);
+  w += al256(static_cast<size_t>(H) * T * sizeof(int32_t));
+  r.score2 = reinterpret_cast<float*>(w);
+  return r;
+}
+
+size_t criticalkv_ws_bytes(int H, int T, int d, int hidden) {
+  (void)d; (void)hidden;
+  return al256(static_cast<size_t>(H) * T) + al256(static_cast<size_t>(H) * T * sizeof(int32_t)) +
+         al256(static_cast<size_t>(H) * T * sizeof(float));
+}
+
+// ------------------------------------------------------------------ stage 1
+__global__ __launch_bounds__(256) void ckv_stage1_kernel(const float* __restrict__ A, int T, int b1,
+                                                         CkvWs w, float* __restrict__ score2) {
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* a = A + static_cast<int64_t>(h) * T;
+  uint32_t tau = 0xFFFFFFFFu;
+  int need = 0;
+  if (b1 > 0) {
+    block_radix_topm(T, b1, [&](int i, uint32_t* key) {
+      *key = float_key(a[i]);
+      return true;
+    }, &tau, &need);
+  }
+  int eq_seen = 0, nrest = 0;
+  uint8_t* s1 = w.s1 + static_cast<int64_t>(h) * T;
+  int32_t* rows2 = w.rows2 + static_cast<int64_t>(h) * (T - b1);
+  float* sc = score2 + static_cast<int64_t>(h) * T;
+  for (int p0 = 0; p0 < T; p0 += 256) {
+    const int p = p0 + tid;
+    const bool valid = p < T;
+    uint32_t key = 0;
+    if (valid) key = float_key(a[p]);
+    const int eq = (b1 > 0 && valid && key == tau) ? 1 : 0;
+    int eq_tot;
+    const int eq_rank = eq_seen + block_prefix(eq, &eq_tot);
+    eq_seen += eq_tot;
+    const bool sel = valid && b1 > 0 && (key > tau || (eq && eq_rank < need));
+    int r_tot;
+    const int rrank = block_prefix((valid && !sel) ? 1 : 0, &r_tot);
+    if (valid) {
+      s1[p] = sel ? 1 : 0;
+      if (sel) sc[p] = -1.0f;
+      else if (nrest + rrank < T - b1) rows2[nrest + rrank] = p;
+    }
+    nrest += r_tot;
+  }
+}
+
+// ------------------------------------------------------------------ projection
+// Block: 256 threads = 4 waves; rows [blk*256, blk*256+256) of the head's
+// row list; wave w owns 64 rows = two 32-row MFMA tiles. Hidden columns are
+// walked in steps of 64: the W_O,h tile [128 x 64] is read from global
+// (coalesced), transposed in registers and stored [n][k] in LDS so that every
+// MFMA B operand is one 16-byte LDS read.
+// MFMA 32x32x16 operand layout (lane l): A[l%32][8*(l/32) + 0..7],
+// B[8*(l/32) + 0..7][l%32], D register r: row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32.
+__global__ __launch_bounds__(256) void ckv_project_kernel(const float* __restrict__ A,
+                                                              const uint16_t* __restrict__ V,
+                                                              const uint16_t* __restrict__ W, int H,
+                                                              int T, int hidden, int nrows, int mt,
+                                                              CkvWs w, float* __restrict__ score2) {
+  __shared__ __attribute__((aligned(16))) uint16_t wt[kBN * kLdw];
+  int head, tile;
+  if (H % 8 == 0) {
+    // keep every block of a head on one XCD (blocks go round-robin over 8)
+    const int xcd = blockIdx.x % 8, local = blockIdx.x / 8;
+    head = xcd + 8 * (local / mt);
+    tile = local % mt;
+  } else {
+    head = blockIdx.x / mt;
+    tile = blockIdx.x % mt;
+  }
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int32_t* rows2 = w.rows2 + static_cast<int64_t>(head) * nrows;
+  const uint16_t* Vh = V + static_cast<int64_t>(head) * T * kCkvD;
+  const uint16_t* Wh = W + static_cast<int64_t>(head) * kCkvD * hidden;
+
+  // A operands: two 32-row tiles x 8 k-steps, held for the whole kernel
+  half8 afrag[2][8];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int j = tile * kBM + wave * 64 + mi * 32 + lane % 32;
+    const bool ok = j < nrows;
+    const int src = ok ? min(max(rows2[j], 0), T - 1) : 0;  // clamp: rows2 comes from stage 1
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ok) {
+        const uint4 t = *reinterpret_cast<const uint4*>(Vh + static_cast<int64_t>(src) * kCkvD + ks * 16 + (lane / 32) * 8);
+        afrag[mi][ks] = __builtin_bit_cast(half8, t);
+      } else {
+        afrag[mi][ks] = half8{};
+      }
+    }
+  }
+  float rsum[2][16];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rsum[mi][r] = 0.0f;
+
+  // W tile loader: thread covers k rows k0..k0+3 and columns n0..n0+7
+  const int lk0 = (tid / 8) * 4;
+  const int ln0 = (tid % 8) * 8;
+  uint4 wreg[4];
+  auto load_w = [&](int nb) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      wreg[kk] = *reinterpret_cast<const uint4*>(Wh + static_cast<int64_t>(lk0 + kk) * hidden + nb + ln0);
+  };
+  const int nsteps = hidden / kBN;
+  load_w(0);
+  for (int step = 0; step < nsteps; ++step) {
+    __syncthreads();  // previous tile fully consumed
+    {
+      // transpose 4(k) x 8(n) halves -> for each n, 4 consecutive k (8 bytes)
+      const uint32_t* r32 = reinterpret_cast<const uint32_t*>(wreg);
+#pragma unroll
+      for (int nn = 0; nn < 8; ++nn) {
+        uint32_t h[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t word = r32[kk * 4 + nn / 2];
+          h[kk] = (nn & 1) ? (word >> 16) : (word & 0xFFFFu);
+        }
+        uint2 v;
+        v.x = h[0] | (h[1] << 16);
+        v.y = h[2] | (h[3] << 16);
+        *reinterpret_cast<uint2*>(&wt[(ln0 + nn) * kLdw + lk0]) = v;
+      }
+    }
+    __syncthreads();
+    if (step + 1 < nsteps) load_w((step + 1) * kBN);
+    // four independent accumulator chains: 2 row tiles x 2 column tiles
+    floatx16 c00 = {}, c10 = {}, c01 = {}, c11 = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int kofs = ks * 16 + (lane / 32) * 8;
+      const half8 b0 = *reinterpret_cast<const half8*>(&wt[(lane % 32) * kLdw + kofs]);
+      const half8 b1 = *reinterpret_cast<const half8*>(&wt[(32 + lane % 32) * kLdw + kofs]);
+      c00 = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[0][ks], b0, c00, 0, 0, 0);
+      c10 = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[1][ks], b0, c10, 0, 0, 0);
+      c01 = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[0][ks], b1, c01, 0, 0, 0);
+      c11 = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[1][ks], b1, c11, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      rsum[0][r] += fabsf(c00[r]) + fabsf(c01[r]);
+      rsum[1][r] += fabsf(c10[r]) + fabsf(c11[r]);
+    }
+  }
+  // reduce over the 32 columns held by lanes with equal lane/32
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = rsum[mi][r];
+      v += shfl_xor_f(v, 1);
+      v += shfl_xor_f(v, 2);
+      v += shfl_xor_f(v, 4);
+      v += shfl_xor_f(v, 8);
+      v += shfl_xor_f(v, 16);
+      rsum[mi][r] = v;
+    }
+  if (lane % 32 == 0) {
+    const float* a = A + static_cast<int64_t>(head) * T;
+    float* sc = score2 + static_cast<int64_t>(head) * T;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row_in_tile = 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+        const int j = tile * kBM + wave * 64 + mi * 32 + row_in_tile;
+        if (j < nrows) {
+          const int i = rows2[j];
+          if (i >= 0 && i < T) sc[i] = a[i] * rsum[mi][r];
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------ stage 2
+__global__ __launch_bounds__(256) void ckv_stage2_kernel(int T, int b1, int b2, CkvWs w,
+                                                         const float* __restrict__ score2,
+                                                         int32_t* __restrict__ idx) {
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint8_t* s1 = w.s1 + static_cast<int64_t>(h) * T;
+  const float* sc = score2 + static_cast<int64_t>(h) * T;
+  uint32_t tau = 0xFFFFFFFFu;
+  int need = 0;
+  if (b2 > 0) {
+    block_radix_topm(T, b2, [&](int i, uint32_t* key) {
+      if (s1[i]) return false;
+      *key = float_key(sc[i]);
+      return true;
+    }, &tau, &need);
+  }
+  int eq_seen = 0, nsel = 0;
+  int32_t* out = idx + static_cast<int64_t>(h) * (b1 + b2);
+  for (int p0 = 0; p0 < T; p0 += 256) {
+    const int p = p0 + tid;
+    const bool valid = p < T;
+    bool in1 = false;
+    uint32_t key = 0;
+    if (valid) {
+      in1 = s1[p] != 0;
+      if (!in1) key = float_key(sc[p]);
+    }
+    const int eq = (b2 > 0 && valid && !in1 && key == tau) ? 1 : 0;
+    int eq_tot;
+    const int eq_rank = eq_seen + block_prefix(eq, &eq_tot);
+    eq_seen += eq_tot;
+    const bool sel = valid && (in1 || (b2 > 0 && (key > tau || (eq && eq_rank < need))));
+    int s_tot;
+    const int rank = block_prefix(sel ? 1 : 0, &s_tot);
+    if (sel && nsel + rank < b1 + b2) out[nsel + rank] = p;
+    nsel += s_tot;
+  }
+}
+
+hipError_t launch_criticalkv(const float* A, const uint16_t* V, const uint16_t* W, int H, int T,
+                             int d, int hidden, int b1, int b2, int32_t* idx, float* score2,
+                             void* ws, hipStream_t stream) {
+  if (d != kCkvD || hidden % kBN != 0) return hipErrorInvalidValue;
+  CkvWs w = carve(ws, H, T);
+  float* sc = score2 ? score2 : w.score2;
+  ckv_stage1_kernel<<<H, 256, 0, stream>>>(A, T, b1, w, sc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nrows = T - b1;
+  if (nrows > 0) {
+    const int mt = (nrows + kBM - 1) / kBM;
+    ckv_project_kernel<<<H * mt, 256, 0, stream>>>(A, V, W, H, T, hidden, nrows, mt, w, sc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ckv_stage2_kernel<<<H, 256, 0, stream>>>(T, b1, b2, w, sc, idx);
+  return hipGetLastError();
+}
+
+}  // namespace mikv

@@ -1,0 +1,248 @@
+// Heavy-hitter bookkeeping, important-set re-selection and demotion.
+//
+// velog notes "No Token Left Behind ...", one-line summary and Key
+// contributions 1): the importance-based eviction (H2O) decides which tokens
+// stay at high precision; the tokens it would evict are kept as low-bit
+// codes instead. paperlayer summary of arXiv 2402.18096, section 5:
+// heavy hitters (largest accumulated attention) plus local (recent) tokens.
+// Ranking key: accumulated attention descending, token position ascending.
+//
+// Decode: one block per (sequence, kv head) adds this step's probabilities,
+// finds the one candidate that falls out of the top-`heavy` (an argmin over
+// heavy+1 candidates) and quantizes its key and value rows into the next
+// low-bit slot.
+// Prefill: a radix select over 32-bit order-preserving keys finds the
+// top-`heavy` threshold of [0, T-recent), ties are taken by ascending
+// position, and block-wide prefix sums assign ascending-position slots in
+// both tiers; a second, token-parallel kernel moves the rows (fp16 copy or
+// quantization) - the HBM-bound part.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "topk.hpp"
+
+#include <climits>
+
+namespace mikv {
+
+// ------------------------------------------------------------------ decode
+template <int D, int BITS, int NL>
+__global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
+  __shared__ float s_acc[4];
+  __shared__ int s_pos[4];
+  __shared__ int s_slot[4];
+  __shared__ int s_drop;
+  const int unit = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t base16 = static_cast<int64_t>(unit) * a.cap16;
+  const int fr = a.free16[unit];
+  const int limit = a.len - a.recent;  // candidates: pos < limit
+  // worst candidate = smallest acc, latest position among equal acc
+  float wa = INFINITY;
+  int wp = -1, ws = -1;
+  for (int s = tid; s < a.cap16; s += 256) {
+    const float prev = (s == fr) ? 0.0f : a.acc16[base16 + s];
+    const float v = prev + a.p16[base16 + s];
+    a.acc16[base16 + s] = v;
+    const int pos = (s == fr) ? a.len - 1 : a.pos16[base16 + s];
+    if (pos < limit && (v < wa || (v == wa && pos > wp))) { wa = v; wp = pos; ws = s; }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float oa = shfl_xor_f(wa, m);
+    const int op = __shfl_xor(wp, m);
+    const int os = __shfl_xor(ws, m);
+    if (os >= 0 && (ws < 0 || oa < wa || (oa == wa && op > wp))) { wa = oa; wp = op; ws = os; }
+  }
+  if (tid % kWave == 0) { s_acc[tid / kWave] = wa; s_pos[tid / kWave] = wp; s_slot[tid / kWave] = ws; }
+  __syncthreads();
+  if (tid == 0) {
+    float ba = s_acc[0]; int bp = s_pos[0], bs = s_slot[0];
+    for (int w = 1; w < 4; ++w) {
+      const int os = s_slot[w];
+      if (os >= 0 && (bs < 0 || s_acc[w] < ba || (s_acc[w] == ba && s_pos[w] > bp))) {
+        ba = s_acc[w]; bp = s_pos[w]; bs = os;
+      }
+    }
+    s_drop = bs;
+  }
+  __syncthreads();
+  const int drop = s_drop;
+  if (drop < 0) return;  // unreachable when heavy + recent == cap16 - 1
+  constexpr int LPR = D / 8;
+  constexpr int CB = D * BITS / 8;
+  constexpr int GPT = D / (8 * NL);
+  const int64_t qslot = static_cast<int64_t>(unit) * a.capq + (a.len - a.cap16);
+  // rows: threads [0, LPR) quantize the key, [LPR, 2*LPR) the value
+  if (tid < 2 * LPR) {
+    const int lane = tid % LPR;
+    const bool is_v = tid >= LPR;
+    const uint16_t* src = (is_v ? a.v16 : a.k16) + (base16 + drop) * D + lane * 8;
+    float x[8];
+    load8(src, x);
+    uint32_t szw;
+    const uint32_t packed = quantize8<BITS, NL>(x, &szw);
+    store_codes8<BITS>((is_v ? a.vq : a.kq) + qslot * CB, lane, packed);
+    if (lane % NL == 0)
+      reinterpret_cast<uint32_t*>(is_v ? a.vsz : a.ksz)[qslot * GPT + lane / NL] = szw;
+  }
+  if (tid == 0) {
+    const int pos = (drop == fr) ? a.len - 1 : a.pos16[base16 + drop];
+    a.posq[qslot] = pos;
+    a.free16[unit] = drop;
+    if (a.demoted_pos) a.demoted_pos[unit] = pos;
+  }
+}
+
+// ------------------------------------------------------------------ prefill
+__global__ __launch_bounds__(256) void h2o_prefill_select_kernel(H2OArgs a, int T, int32_t* map) {
+  const int unit = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* acc0 = a.src_acc0 + static_cast<int64_t>(unit) * T;
+  const int ncand = T - a.recent;
+  const int H = a.heavy;
+  // threshold key of the H-th best candidate; `need` of its ties are kept
+  uint32_t tau = 0xFFFFFFFFu;
+  int need = 0;
+  if (H > 0) {
+    block_radix_topm(ncand, H, [&](int i, uint32_t* key) {
+      *key = float_key(acc0[i]);
+      return true;
+    }, &tau, &need);
+  }
+  // ascending-position slot assignment in both tiers
+  int eq_seen = 0, kept = 0, dropped = 0;
+  const int64_t base16 = static_cast<int64_t>(unit) * a.cap16;
+  const int64_t baseq = static_cast<int64_t>(unit) * a.capq;
+  for (int p0 = 0; p0 < T; p0 += 256) {
+    const int p = p0 + tid;
+    const bool valid = p < T;
+    const bool cand = valid && p < ncand;
+    uint32_t key = 0;
+    float av = 0.0f;
+    if (valid) { av = acc0[p]; key = float_key(av); }
+    const int eq = (H > 0 && cand && key == tau) ? 1 : 0;
+    int eq_tot;
+    const int eq_rank = eq_seen + block_prefix(eq, &eq_tot);
+    eq_seen += eq_tot;
+    bool keep = false;
+    if (valid) {
+      if (!cand) keep = true;
+      else if (H > 0 && (key > tau || (eq && eq_rank < need))) keep = true;
+    }
+    int k_tot;
+    const int krank = block_prefix(keep ? 1 : 0, &k_tot);
+    // slots are bounds-checked so that a selection error can only show up
+    // as a wrong result (map entry INT_MIN = not stored)
+    if (valid) {
+      if (keep) {
+        const int slot = kept + krank;
+        const bool ok = slot < a.cap16 - 1;
+        if (ok) {
+          a.pos16[base16 + slot] = p;
+          a.acc16[base16 + slot] = av;
+        }
+        map[static_cast<int64_t>(unit) * T + p] = ok ? slot : INT_MIN;
+      } else {
+        const int slot = dropped + (p - p0 - krank);
+        const bool ok = slot < a.capq;
+        if (ok) a.posq[baseq + slot] = p;
+        map[static_cast<int64_t>(unit) * T + p] = ok ? -1 - slot : INT_MIN;
+      }
+    }
+    const int nvalid = min(256, T - p0);
+    kept += k_tot;
+    dropped += nvalid - k_tot;
+  }
+  if (tid == 0) {
+    a.free16[unit] = a.cap16 - 1;
+    a.pos16[base16 + a.cap16 - 1] = -1;
+    a.acc16[base16 + a.cap16 - 1] = 0.0f;
+  }
+}
+
+template <int D, int BITS, int NL>
+__global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int T,
+                                                                  const int32_t* map) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  constexpr int CB = D * BITS / 8;
+  constexpr int GPT = D / (8 * NL);
+  const int lane = threadIdx.x % LPR;
+  const int64_t n_rows = static_cast<int64_t>(a.batch) * a.hkv * T;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * RPB;
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR; r < n_rows; r += step) {
+    const int64_t unit = r / T;
+    const int slot = map[r];
+    float kx[8], vx[8];
+    load8(a.src_k + r * D + lane * 8, kx);
+    load8(a.src_v + r * D + lane * 8, vx);
+    uint32_t kw[4];
+    if (a.src_b) {
+      const float* bb = a.src_b + unit * D + lane * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kx[i] = h2f(f2h(mul_rn(kx[i], bb[i])));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      kw[i] = static_cast<uint32_t>(f2h(kx[2 * i])) | (static_cast<uint32_t>(f2h(kx[2 * i + 1])) << 16);
+    // quantize both rows unconditionally (row-uniform control flow for DPP)
+    uint32_t kszw, vszw;
+    const uint32_t kp = quantize8<BITS, NL>(kx, &kszw);
+    const uint32_t vp = quantize8<BITS, NL>(vx, &vszw);
+    if (slot == INT_MIN) continue;
+    if (slot >= 0) {
+      const int64_t o16 = (unit * a.cap16 + slot) * D + lane * 8;
+      *reinterpret_cast<uint4*>(a.k16 + o16) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+      *reinterpret_cast<uint4*>(a.v16 + o16) = *reinterpret_cast<const uint4*>(a.src_v + r * D + lane * 8);
+    } else {
+      const int64_t qs = unit * a.capq + (-1 - slot);
+      store_codes8<BITS>(a.kq + qs * CB, lane, kp);
+      store_codes8<BITS>(a.vq + qs * CB, lane, vp);
+      if (lane % NL == 0) {
+        reinterpret_cast<uint32_t*>(a.ksz)[qs * GPT + lane / NL] = kszw;
+        reinterpret_cast<uint32_t*>(a.vsz)[qs * GPT + lane / NL] = vszw;
+      }
+    }
+  }
+}
+
+size_t h2o_ws_bytes(int batch, int hkv, int T) {
+  return static_cast<size_t>(batch) * hkv * (T > 0 ? T : 1) * sizeof(int32_t);
+}
+
+template <int D, int BITS, int NL>
+static hipError_t launch_dec(const H2OArgs& a, hipStream_t stream) {
+  h2o_decode_kernel<D, BITS, NL><<<a.batch * a.hkv, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int D, int BITS, int NL>
+static hipError_t launch_pre(const H2OArgs& a, hipStream_t stream) {
+  const int T = a.len;
+  int32_t* map = static_cast<int32_t*>(a.ws);
+  h2o_prefill_select_kernel<<<a.batch * a.hkv, 256, 0, stream>>>(a, T, map);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || T == 0) return e;
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t n_rows = static_cast<int64_t>(a.batch) * a.hkv * T;
+  int64_t blocks = (n_rows + RPB - 1) / RPB;
+  if (blocks > 65536) blocks = 65536;
+  h2o_prefill_scatter_kernel<D, BITS, NL><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(a, T, map);
+  return hipGetLastError();
+}
+
+#define MIKV_H2O_DISPATCH(FN)                                                \
+  if (a.d == 128 && a.bits == 4 && a.group == 64) return FN<128, 4, 8>(a, stream);  \
+  if (a.d == 128 && a.bits == 4 && a.group == 128) return FN<128, 4, 16>(a, stream); \
+  if (a.d == 128 && a.bits == 2 && a.group == 64) return FN<128, 2, 8>(a, stream);  \
+  if (a.d == 128 && a.bits == 2 && a.group == 128) return FN<128, 2, 16>(a, stream); \
+  if (a.d == 64 && a.bits == 4 && a.group == 32) return FN<64, 4, 4>(a, stream);    \
+  if (a.d == 64 && a.bits == 4 && a.group == 64) return FN<64, 4, 8>(a, stream);    \
+  if (a.d == 64 && a.bits == 2 && a.group == 32) return FN<64, 2, 4>(a, stream);    \
+  if (a.d == 64 && a.bits == 2 && a.group == 64) return FN<64, 2, 8>(a, stream);    \
+  return hipErrorInvalidValue;
+
+hipError_t launch_h2o_decode(const H2OArgs& a, hipStream_t stream) { MIKV_H2O_DISPATCH(launch_dec) }
+hipError_t launch_h2o_prefill(const H2OArgs& a, hipStream_t stream) { MIKV_H2O_DISPATCH(launch_pre) }
+
+}  // namespace mikv

@@ -1,0 +1,79 @@
+// Host-side launchers of the MiKV kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mikv {
+
+hipError_t launch_quantize_rows(const uint16_t* x, const int32_t* rows, int64_t n_rows, int d,
+                                int group, int bits, uint8_t* codes, uint16_t* sz,
+                                hipStream_t stream);
+
+// Channel balancer: partial maxima per token chunk, then finalize; optional kb.
+size_t balance_ws_bytes(int batch, int hkv, int rep, int d, int T);
+hipError_t launch_balance(int batch, int hq, int hkv, int d, int T, const uint16_t* q,
+                          const uint16_t* k, float* b, uint16_t* kb, void* ws,
+                          hipStream_t stream);
+
+struct DecodePlan {
+  int C16, Cq;     // tokens per split in the FP16 / low-bit tier
+  int S16, Sq;     // splits per tier
+  int RT;          // query heads per block
+  int tiles;       // rep / RT
+};
+DecodePlan decode_plan(int d, int bits, int rep, int cap16, int nq);
+size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int cap16, const DecodePlan& plan);
+
+struct DecodeArgs {
+  int batch, hq, hkv, d, group, bits, cap16, capq, len;
+  const uint16_t* q;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const float* b;
+  uint16_t* k16;
+  uint16_t* v16;
+  int32_t* pos16;
+  const int32_t* free16;
+  const uint8_t* kq;
+  const uint8_t* vq;
+  const uint16_t* ksz;
+  const uint16_t* vsz;
+  float* o;
+  float* p16;
+  void* ws;
+};
+hipError_t launch_decode_attn(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+struct H2OArgs {
+  int batch, hkv, d, group, bits, cap16, capq, len, recent, heavy;
+  uint16_t* k16;
+  uint16_t* v16;
+  int32_t* pos16;
+  float* acc16;
+  int32_t* free16;
+  uint8_t* kq;
+  uint8_t* vq;
+  uint16_t* ksz;
+  uint16_t* vsz;
+  int32_t* posq;
+  const float* p16;
+  int32_t* demoted_pos;
+  // prefill
+  const uint16_t* src_k;
+  const uint16_t* src_v;
+  const float* src_acc0;
+  const float* src_b;
+  void* ws;
+};
+size_t h2o_ws_bytes(int batch, int hkv, int T);
+hipError_t launch_h2o_decode(const H2OArgs& a, hipStream_t stream);
+hipError_t launch_h2o_prefill(const H2OArgs& a, hipStream_t stream);
+
+size_t criticalkv_ws_bytes(int H, int T, int d, int hidden);
+hipError_t launch_criticalkv(const float* A, const uint16_t* V, const uint16_t* W, int H, int T,
+                             int d, int hidden, int b1, int b2, int32_t* idx, float* score2,
+                             void* ws, hipStream_t stream);
+
+}  // namespace mikv

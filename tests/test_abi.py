@@ -1,0 +1,141 @@
+"""C interface checks that need no GPU: the library loads, exports every
+function include/mikv.h declares, and rejects invalid arguments on the host
+with the documented status before anything is enqueued."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from mixed_precision_decode_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20   # never dereferenced: validation fails before any launch
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from mixed_precision_decode_amd import build_lib
+        build_lib.build()
+    return L.lib()
+
+
+def _header_functions():
+    txt = open(os.path.join(ROOT, "include", "mikv.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mikv_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _header_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L._SIGS)
+
+
+def test_abi_version_and_status_text(lib):
+    assert lib.mikv_abi_version() == 1
+    for s in range(7):
+        assert len(L.mikv_status_str(s)) > 0
+    assert L.mikv_status_str(99) == "unknown status"
+
+
+def _dims(**kw):
+    d = dict(batch=2, hq=8, hkv=2, d=128, group=64, bits=4, cap16=11, capq=100)
+    d.update(kw)
+    return L.Dims(**d)
+
+
+def _cache():
+    return L.MikvCache(*([FAKE] * 10))
+
+
+def test_decode_attn_validation(lib):
+    c = _cache()
+    good = _dims()
+    ws_need = lib.mikv_decode_attn_workspace(C.byref(good.c()), 80)
+    assert ws_need > 0
+    call = lambda dims, length=50, ws_bytes=ws_need, cache=c, q=FAKE: lib.mikv_decode_attn(
+        C.byref(dims.c()), C.byref(cache), length, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        ws_bytes, None)
+    assert call(_dims(hq=7)) == L.MIKV_ERR_SHAPE
+    assert call(_dims(d=96)) == L.MIKV_ERR_UNSUPPORTED
+    assert call(_dims(bits=3)) == L.MIKV_ERR_UNSUPPORTED
+    assert call(_dims(group=32)) == L.MIKV_ERR_UNSUPPORTED
+    assert call(good, q=None) == L.MIKV_ERR_NULL
+    assert call(good, length=10) == L.MIKV_ERR_SHAPE            # len < cap16
+    assert call(good, length=112) == L.MIKV_ERR_CAPACITY        # len - cap16 > capq
+    assert call(good, ws_bytes=ws_need - 1) == L.MIKV_ERR_WORKSPACE
+    bad = _cache()
+    bad.kq = None
+    assert call(good, cache=bad) == L.MIKV_ERR_NULL
+    mis = _cache()
+    mis.k16 = FAKE + 2
+    assert call(good, cache=mis) == L.MIKV_ERR_SHAPE            # 16-byte alignment
+
+
+def test_h2o_validation(lib):
+    c = _cache()
+    dims = _dims()
+    dec = lambda recent, heavy, length=50, p16=FAKE: lib.mikv_h2o_update_select(
+        C.byref(dims.c()), C.byref(c), length, recent, heavy, p16, None, None, None, 0, None)
+    assert dec(4, 7) == L.MIKV_ERR_SHAPE        # heavy + recent != cap16 - 1
+    assert dec(-1, 11) == L.MIKV_ERR_SHAPE
+    assert dec(4, 6, length=112) == L.MIKV_ERR_CAPACITY
+    assert dec(4, 6, p16=None) == L.MIKV_ERR_NULL  # neither mode
+    src = L.MikvPrefillSrc(FAKE, FAKE, FAKE, None, 40)
+    pre = lambda length, ws_bytes, s=src: lib.mikv_h2o_update_select(
+        C.byref(dims.c()), C.byref(c), length, 4, 6, None, C.byref(s), None, FAKE, ws_bytes, None)
+    need = lib.mikv_h2o_workspace(C.byref(dims.c()), 40)
+    assert pre(39, need) == L.MIKV_ERR_SHAPE      # len != src.T
+    assert pre(40, need - 1) == L.MIKV_ERR_WORKSPACE
+    small = L.MikvPrefillSrc(FAKE, FAKE, FAKE, None, 9)
+    assert pre(9, need, small) == L.MIKV_ERR_SHAPE  # T < B
+    tight = _dims(capq=20)
+    assert lib.mikv_h2o_update_select(C.byref(tight.c()), C.byref(c), 40, 4, 6, None,
+                                      C.byref(src), None, FAKE, need, None) == L.MIKV_ERR_CAPACITY
+
+
+def test_balance_quantize_validation(lib):
+    dims = _dims()
+    need = lib.mikv_balance_workspace(C.byref(dims.c()), 64)
+    assert need > 0
+    bal = lambda T, q=FAKE, b=FAKE, ws_bytes=need: lib.mikv_balance_prefill(
+        C.byref(dims.c()), T, q, FAKE, b, None, FAKE, ws_bytes, None)
+    assert bal(-1) == L.MIKV_ERR_SHAPE
+    assert bal(64, q=None) == L.MIKV_ERR_NULL
+    assert bal(64, b=None) == L.MIKV_ERR_NULL
+    assert bal(64, ws_bytes=need - 1) == L.MIKV_ERR_WORKSPACE
+    q = lambda n, d, g, bits, x=FAKE: lib.mikv_quantize_tokens(x, None, n, d, g, bits, FAKE, FAKE, None)
+    assert q(-1, 128, 64, 4) == L.MIKV_ERR_SHAPE
+    assert q(5, 128, 48, 4) == L.MIKV_ERR_SHAPE
+    assert q(5, 96, 48, 4) == L.MIKV_ERR_UNSUPPORTED
+    assert q(5, 128, 64, 8) == L.MIKV_ERR_UNSUPPORTED
+    assert q(5, 128, 64, 4, x=None) == L.MIKV_ERR_NULL
+    assert q(0, 128, 64, 4, x=None) == L.MIKV_OK      # empty input enqueues nothing
+
+
+def test_criticalkv_validation(lib):
+    need = lib.mikv_criticalkv_workspace(4, 100, 128, 256)
+    assert need > 0
+    ck = lambda H=4, T=100, d=128, hidden=256, budget=20, alpha=0.5, ws_bytes=need, A=FAKE: \
+        lib.mikv_criticalkv_select(A, FAKE, FAKE, H, T, d, hidden, budget, alpha, FAKE, None,
+                                   FAKE, ws_bytes, None)
+    assert ck(A=None) == L.MIKV_ERR_NULL
+    assert ck(d=64) == L.MIKV_ERR_UNSUPPORTED
+    assert ck(hidden=200) == L.MIKV_ERR_UNSUPPORTED
+    assert ck(budget=0) == L.MIKV_ERR_SHAPE
+    assert ck(budget=101) == L.MIKV_ERR_SHAPE
+    assert ck(alpha=1.5) == L.MIKV_ERR_SHAPE
+    assert ck(alpha=float("nan")) == L.MIKV_ERR_SHAPE
+    assert ck(ws_bytes=need - 1) == L.MIKV_ERR_WORKSPACE
+
+
+def test_workspace_queries(lib):
+    dims = _dims()
+    a = lib.mikv_decode_attn_workspace(C.byref(dims.c()), 1000)
+    b = lib.mikv_decode_attn_workspace(C.byref(dims.c()), 4000)
+    assert 0 < a <= b
+    assert lib.mikv_decode_attn_workspace(C.byref(dims.c()), 5) == 0   # max_len < cap16

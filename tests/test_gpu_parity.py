@@ -1,0 +1,287 @@
+"""Parity of the HIP path (through the C interface) with the CPU oracle.
+
+Bit-exact: balancer b and balanced keys, quantization codes and (scale,
+zero), important-set positions, demoted rows, top-k selections.
+Tolerance (fp32 accumulation vs fp64 oracle): attention outputs and
+accumulated scores, max|gpu - oracle| <= 2e-3 * max|oracle|.
+Multi-step decode is checked in lockstep: each step starts the oracle from
+the device state, so fp32 probabilities that underflow to exactly 0 (which
+fp64 keeps distinct) cannot make the two selections drift apart.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from mixed_precision_decode_amd import _lib as L
+from mixed_precision_decode_amd import synth as S
+
+pytestmark = pytest.mark.gpu
+F16, F32, F64 = np.float16, np.float32, np.float64
+TOL = 2e-3
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bits16(a):
+    return np.ascontiguousarray(a).view(np.uint16)
+
+
+def assert_close(gpu, ref, what, floor=0.0):
+    """max|gpu - ref| <= TOL * max|ref| + floor. `floor` covers only values
+    fp32 cannot hold: probabilities below 2^-126 flush to 0 on the device
+    while fp64 keeps them."""
+    ref = np.asarray(ref, F64)
+    err = np.max(np.abs(np.asarray(gpu, F64) - ref)) if ref.size else 0.0
+    scale = np.max(np.abs(ref)) if ref.size else 0.0
+    assert err <= TOL * scale + floor, f"{what}: max err {err:.3e} > {TOL} * {scale:.3e} + {floor:.1e}"
+
+
+def dims_of(cfg, capq=None):
+    return L.Dims(batch=cfg.batch, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, group=cfg.G, bits=cfg.bits,
+                  cap16=cfg.cap16, capq=cfg.capq() if capq is None else capq)
+
+
+# ---------------------------------------------------------------- quantize
+@pytest.mark.parametrize("d,group,bits", [(128, 64, 4), (128, 64, 2), (128, 128, 4),
+                                          (64, 32, 4), (64, 32, 2), (64, 64, 2)])
+@pytest.mark.parametrize("n_rows", [1, 37, 4099])
+def test_quantize_parity(d, group, bits, n_rows):
+    print(f"quantize d={d} G={group} bits={bits} rows={n_rows}", flush=True)
+    rng = np.random.default_rng(n_rows * 7 + d + bits)
+    x = rng.standard_normal((n_rows + 5, d)).astype(F32)
+    x[:, rng.integers(0, d, 4)] *= 20
+    x[::5] *= 1e-4            # fp16 subnormal territory
+    x[::9] *= 300
+    x = x.astype(F16)
+    x[3 % len(x)] = F16(1.5)  # constant row
+    x[4 % len(x), :group] = F16(-0.0)
+    rows = rng.permutation(n_rows + 5)[:n_rows].astype(np.int32)
+    for use_rows in (False, True):
+        src = x[rows] if use_rows else x[:n_rows]
+        codes = torch.zeros((n_rows, d * bits // 8), dtype=torch.uint8, device="cuda")
+        sz = torch.zeros((n_rows, d // group, 2), dtype=torch.float16, device="cuda")
+        L.mikv_quantize_tokens(dev(x), dev(rows) if use_rows else None, codes, sz, group, bits)
+        ref_c, ref_sz = O.quantize_rows(src, group, bits)
+        assert np.array_equal(host(codes), ref_c)
+        assert np.array_equal(bits16(host(sz)), bits16(ref_sz))
+
+
+def test_quantize_empty():
+    codes = torch.zeros((0, 64), dtype=torch.uint8, device="cuda")
+    sz = torch.zeros((0, 2, 2), dtype=torch.float16, device="cuda")
+    x = torch.zeros((4, 128), dtype=torch.float16, device="cuda")
+    L.mikv_quantize_tokens(x, None, codes, sz, 64, 4)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- balancer
+def _balance_gpu(cfg, q, k, want_kb=True):
+    dims = dims_of(cfg)
+    T = q.shape[2]
+    b = torch.empty((cfg.batch, cfg.hkv, cfg.d), dtype=torch.float32, device="cuda")
+    kb = torch.empty(k.shape, dtype=torch.float16, device="cuda") if want_kb else None
+    ws = torch.empty(max(1, L.mikv_balance_workspace(dims, T)), dtype=torch.uint8, device="cuda")
+    L.mikv_balance_prefill(dims, T, dev(q), dev(k), b, kb, ws)
+    return b, kb
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny", {}), ("tiny", dict(T=1)), ("tiny", dict(T=0)),
+    ("gqa_throughput", dict(batch=2, T=300)),
+    ("llama2_7b_layer", dict(batch=1, hq=4, hkv=4, T=777)),
+    ("llama3_8b_32k", dict(hq=8, hkv=2, T=5000)),
+])
+def test_balance_parity(name, over):
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"balance {name} {over}", flush=True)
+    q, k, _, _ = S.prefill_tensors(cfg, 77)
+    b, kb = _balance_gpu(cfg, q, k)
+    rb, rkb = O.balance(q, k)
+    assert np.array_equal(host(b).view(np.uint32), rb.view(np.uint32))
+    if cfg.T > 0:
+        assert np.array_equal(bits16(host(kb)), bits16(rkb))
+
+
+# ---------------------------------------------------------------- prefill build
+def _prefill_gpu(cfg, seed, balanced=True, capq=None):
+    q, k, v, acc0 = S.prefill_tensors(cfg, seed)
+    dims = dims_of(cfg, capq)
+    cache = L.Cache(dims)
+    if balanced:
+        b, _ = _balance_gpu(cfg, q, k, want_kb=False)
+    else:
+        b = torch.ones((cfg.batch, cfg.hkv, cfg.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, L.mikv_h2o_workspace(dims, cfg.T)), dtype=torch.uint8, device="cuda")
+    src = dict(k=dev(k), v=dev(v), acc0=dev(acc0), b=b if balanced else None)
+    L.mikv_h2o_update_select(dims, cache, cfg.T, cfg.recent, cfg.H, src=src, ws=ws)
+    return dims, cache, b, (q, k, v, acc0)
+
+
+def _state_equal(gpu, ref, n16=None, nq=None):
+    for key in ("pos16", "free16", "posq"):
+        assert np.array_equal(gpu[key], ref[key]), key
+    assert np.array_equal(gpu["acc16"].view(np.uint32), ref["acc16"].view(np.uint32))
+    for key in ("k16", "v16", "ksz", "vsz"):
+        assert np.array_equal(bits16(gpu[key]), bits16(ref[key])), key
+    for key in ("kq", "vq"):
+        assert np.array_equal(gpu[key], ref[key]), key
+
+
+@pytest.mark.parametrize("name,over,balanced", [
+    ("tiny", {}, True), ("tiny", {}, False),
+    ("tiny", dict(pct=0, recent=0), True),          # uniform low-bit (B = 0)
+    ("tiny", dict(pct=100, recent=16), True),       # everything important
+    ("tiny", dict(recent=0), True),
+    ("tiny", dict(recent=51), True),                # heavy = 0
+    ("gqa_throughput", dict(batch=2, T=700), True),
+    ("llama3_8b_32k", dict(hq=8, hkv=2, T=3000), True),
+])
+def test_prefill_build_parity(name, over, balanced):
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"prefill {name} {over} balanced={balanced}", flush=True)
+    dims, cache, b, (q, k, v, acc0) = _prefill_gpu(cfg, 5, balanced)
+    if balanced:
+        _, kb = O.balance(q, k)
+    else:
+        kb = k
+    ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq())
+    _state_equal(cache.to_numpy(), ref)
+
+
+# ---------------------------------------------------------------- decode lockstep
+def _lockstep(cfg, seed, steps, balanced=True, check_every=1):
+    dims, cache, b, _ = _prefill_gpu(cfg, seed, balanced)
+    bh = host(b)
+    o = torch.empty((cfg.batch, cfg.hq, cfg.d), dtype=torch.float32, device="cuda")
+    p16 = torch.empty((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
+    dpos = torch.empty((cfg.batch, cfg.hkv), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + steps), dtype=torch.uint8,
+                     device="cuda")
+    N = cfg.T
+    for step in range(steps):
+        N += 1
+        qd, kd, vd = S.decode_tensors(cfg, seed, step)
+        check = step % check_every == 0 or step == steps - 1
+        if check:
+            before = cache.to_numpy()
+        L.mikv_decode_attn(dims, cache, N, dev(qd), dev(kd), dev(vd), b, o, p16, ws)
+        if check:
+            mid = cache.to_numpy()
+        L.mikv_h2o_update_select(dims, cache, N, cfg.recent, cfg.H, p16=p16, demoted_pos=dpos)
+        if not check:
+            continue
+        after = cache.to_numpy()
+        ro, rp16, _, rst = O.decode_attention(before, N, qd, kd, vd, bh)
+        # append: balanced key, value and position in the free slot
+        for key in ("k16", "v16"):
+            assert np.array_equal(bits16(mid[key]), bits16(rst[key])), key
+        assert np.array_equal(mid["pos16"], rst["pos16"])
+        assert_close(host(o), ro, f"o step {step}")
+        # p16 holds probabilities: scale = the group's total mass (rep)
+        underflow = N * cfg.rep * 2.0 ** -126
+        err = np.max(np.abs(host(p16).astype(F64) - rp16))
+        assert err <= TOL * cfg.rep, f"p16 step {step}: max err {err:.3e}"
+        acc_prev = before["acc16"].astype(F64)
+        fr = before["free16"]
+        for i in range(cfg.batch):
+            for g in range(cfg.hkv):
+                acc_prev[i, g, fr[i, g]] = 0.0
+        assert_close(after["acc16"], acc_prev + rp16, f"acc step {step}", floor=underflow)
+        # selection on the device's own fp32 scores must match exactly
+        drop = O.select_drop(after["acc16"].astype(F64), mid["pos16"], N, cfg.recent, cfg.H)
+        assert np.array_equal(after["free16"], drop), f"selection step {step}"
+        mid2 = dict(mid)
+        mid2["acc16"] = after["acc16"]
+        rdem = O.demote(mid2, N, drop)
+        _state_equal(after, rdem)
+        assert np.array_equal(host(dpos), np.take_along_axis(mid["pos16"], drop[..., None], 2)[..., 0])
+    return cache
+
+
+@pytest.mark.parametrize("name,over,balanced,steps", [
+    ("tiny", {}, True, 32),
+    ("tiny", {}, False, 32),
+    ("tiny", dict(bits=2), True, 12),
+    ("tiny", dict(pct=0, recent=0), True, 6),
+    ("tiny", dict(pct=100, recent=16), True, 6),
+    ("tiny", dict(recent=0), True, 6),
+    ("tiny", dict(hq=4, hkv=1), True, 6),            # MQA-style group of 4
+    ("tiny", dict(hq=8, hkv=1), True, 4),            # group of 8: two head tiles
+    ("gqa_throughput", dict(batch=3, T=600), True, 5),
+    ("llama3_8b_32k", dict(hq=8, hkv=2, T=4100), True, 4),
+    ("llama2_7b_layer", dict(batch=2, hq=3, hkv=3, T=1500), True, 4),
+])
+def test_decode_lockstep(name, over, balanced, steps):
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"lockstep {name} {over} balanced={balanced} steps={steps}", flush=True)
+    _lockstep(cfg, 11, steps, balanced)
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_layer", "llama3_8b_32k", "gqa_throughput"])
+def test_decode_full_size(name):
+    """The configs' full shapes, two lockstep steps, in the launch
+    configuration the benchmark times."""
+    cfg = S.CONFIGS[name]
+    print(f"full-size lockstep {name}", flush=True)
+    _lockstep(cfg, 1000 + list(S.CONFIGS).index(name), 2)
+
+
+# ---------------------------------------------------------------- CriticalKV
+def _ckv_gpu(A, V, W, budget, alpha):
+    H, T = A.shape
+    idx = torch.empty((H, budget), dtype=torch.int32, device="cuda")
+    sc = torch.empty((H, T), dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.mikv_criticalkv_workspace(H, T, V.shape[-1], W.shape[1]), dtype=torch.uint8,
+                     device="cuda")
+    L.mikv_criticalkv_select(dev(A), dev(V), dev(W), budget, alpha, idx, sc, ws)
+    return host(idx), host(sc)
+
+
+def _ckv_check(A, V, W, budget, alpha, sample=None):
+    H, T = A.shape
+    idx, sc = _ckv_gpu(A, V, W, budget, alpha)
+    b1 = int(np.floor(F64(np.float32(alpha)) * budget))
+    pos = np.arange(T)
+    s1 = np.zeros((H, T), bool)
+    for h in range(H):
+        s1[h, O.top_by_key(A[h], pos, b1)] = True
+    assert np.array_equal(sc < 0, s1), "stage-1 membership"
+    rng = np.random.default_rng(0)
+    rows = []
+    for h in range(H):
+        rest = pos[~s1[h]]
+        rows.append(rest if sample is None or len(rest) <= sample else np.sort(rng.choice(rest, sample, replace=False)))
+    norms = O.projected_value_l1(V, W, rows=rows)
+    for h in range(H):
+        r = rows[h]
+        assert_close(sc[h, r], A[h, r].astype(F64) * norms[h, r], f"score2 head {h}")
+    ridx, _, _ = O.criticalkv_select(A, V, W, budget, alpha, score2=sc.astype(F64))
+    assert np.array_equal(idx, ridx)
+
+
+@pytest.mark.parametrize("H,T,hidden,budget,alpha", [
+    (8, 1000, 256, 200, 0.5), (8, 1000, 256, 200, 0.0), (8, 1000, 256, 200, 1.0),
+    (3, 257, 128, 1, 0.5), (3, 257, 128, 257, 0.5), (16, 4099, 512, 811, 0.3),
+])
+def test_criticalkv_parity(H, T, hidden, budget, alpha):
+    print(f"criticalkv H={H} T={T} hidden={hidden} budget={budget} alpha={alpha}", flush=True)
+    cfg = dataclasses.replace(S.CKV_CONFIGS["criticalkv_32k"], H=H, T=T, hidden=hidden)
+    A, V, W = S.criticalkv_inputs(cfg, 3)
+    _ckv_check(A, V, W, budget, alpha)
+
+
+def test_criticalkv_full_size():
+    cfg = S.CKV_CONFIGS["criticalkv_32k"]
+    print("criticalkv full size", flush=True)
+    A, V, W = S.criticalkv_inputs(cfg, 1004)
+    _ckv_check(A, V, W, cfg.budget, cfg.alpha, sample=192)
