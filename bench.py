@@ -7,10 +7,13 @@ before timing (balancer + prefill build on the GPU) from seeded synthetic
 inputs; every step consumes a new seeded (q, k, v) token per sequence and
 kv head, so the low-bit tier grows by one token per step.
 
-Before each timed step an untimed 1 GiB device write evicts the caches
-(MI355X has a 256 MB Infinity Cache, larger than the per-step working set of
-the configs), so each step streams its cache from HBM. Step and kernel times
-come from HIP events recorded on the stream the kernels run on.
+Before each timed step an untimed read of a 1 GiB device buffer evicts the
+caches (MI355X has a 256 MB Infinity Cache, larger than the per-step working
+set of the configs), so each step streams its cache from HBM. The flush
+reads rather than writes: a written flush leaves the Infinity Cache full of
+dirty lines whose write-back would then compete with the measured kernel
+(--flush write shows that case, --flush none the warm-cache case). Step and
+kernel times come from HIP events recorded on the stream the kernels run on.
 
 Prints one JSON line (rank 0). --gpus N > 1 is refused: this build targets
 one GPU.
@@ -106,11 +109,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--attn-steps", type=int, default=20,
+                    help="extra decode steps timed around the attention call alone")
     ap.add_argument("--workload", default="llama2_7b_layer")
     ap.add_argument("--seed", type=int, default=1001)
+    ap.add_argument("--set", action="append", default=[], metavar="FIELD=INT",
+                    help="override an integer field of the workload (e.g. pct=100)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--flush", choices=("read", "write", "none"), default="read")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -128,8 +135,10 @@ def main():
     from mixed_precision_decode_amd import synth as S
 
     cfg = S.CONFIGS[args.workload]
-    K, W = args.steps, args.warmup
-    total = K + W
+    if args.set:
+        cfg = cfg.scaled(**{kv.split("=")[0]: int(kv.split("=")[1]) for kv in args.set})
+    K, W, KA = args.steps, args.warmup, args.attn_steps
+    total = K + W + KA
     assert total <= cfg.steps, f"the workload defines {cfg.steps} decode steps"
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
@@ -155,51 +164,68 @@ def main():
     p16 = torch.empty((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
     ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + total), dtype=torch.uint8,
                      device="cuda")
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def do_flush(i):
+        if args.flush == "read":
+            torch.sum(flush, dim=0, out=flush_out)
+        elif args.flush == "write":
+            flush.fill_(float(i))
     log(f"[bench] cache built ({time.perf_counter() - t0:.1f}s); warmup {W}, timed {K}")
 
     N = cfg.T
     cpu_state = None
 
-    def one_step(s, ev=None):
+    def one_step(s, ev_start=None, ev_attn=None, ev_end=None):
         nonlocal N
         N += 1
         qd, kd, vd = steps_in[s]
-        if ev is not None:
-            ev[0].record()
+        if ev_start is not None:
+            ev_start.record()
         L.mikv_decode_attn(dims, cache, N, qd, kd, vd, b, o, p16, ws)
-        if ev is not None:
-            ev[1].record()
+        if ev_attn is not None:
+            ev_attn.record()
         L.mikv_h2o_update_select(dims, cache, N, cfg.recent, cfg.H, p16=p16)
-        if ev is not None:
-            ev[2].record()
+        if ev_end is not None:
+            ev_end.record()
 
     for s in range(W):
-        if not args.no_flush:
-            flush.fill_(float(s))
+        do_flush(s)
         one_step(s)
     torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         cpu_state = (cache.to_numpy(), b.cpu().numpy(), N + 1, W)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # timed steps: events only at the step boundaries (an event between two
+    # kernels costs a few microseconds of its own)
+    Ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(Ev(), Ev()) for _ in range(K)]
     lens = []
     torch.cuda.synchronize()
     tw0 = time.perf_counter()
     for i in range(K):
-        if not args.no_flush:
-            flush.fill_(float(i))
-        one_step(W + i, evs[i])
+        do_flush(i)
+        one_step(W + i, ev_start=evs[i][0], ev_end=evs[i][1])
         lens.append(N)
     torch.cuda.synchronize()
     wall = time.perf_counter() - tw0
-    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    # attention kernels alone (split + merge of one mikv_decode_attn call)
+    eva = [(Ev(), Ev()) for _ in range(KA)]
+    alens = []
+    for i in range(KA):
+        do_flush(i)
+        one_step(W + K + i, ev_start=eva[i][0], ev_attn=eva[i][1])
+        alens.append(N)
+    torch.cuda.synchronize()
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in eva])
     lens = np.array(lens)
     ms_per_step = float(step_ms.mean())
     value = float(cfg.batch * lens.mean() / (ms_per_step * 1e-3))
-    abytes = np.array([attn_bytes(cfg, n) for n in lens], dtype=np.float64)
+    abytes = np.array([attn_bytes(cfg, n) for n in alens], dtype=np.float64)
     a_gbps = float((abytes / (attn_ms * 1e-3)).mean() / 1e9)
-    s_gbps = float(((abytes + h2o_bytes(cfg)) / (step_ms * 1e-3)).mean() / 1e9)
+    sbytes = np.array([attn_bytes(cfg, n) + h2o_bytes(cfg) for n in lens], dtype=np.float64)
+    s_gbps = float((sbytes / (step_ms * 1e-3)).mean() / 1e9)
     log(f"[bench] attn {attn_ms.mean() * 1e3:.1f} us ({a_gbps:.0f} GB/s), step "
         f"{ms_per_step * 1e3:.1f} us ({s_gbps:.0f} GB/s), wall incl. flush {wall / K * 1e3:.3f} ms/step")
 
@@ -225,9 +251,10 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "q_heads": cfg.hq, "kv_heads": cfg.hkv,
                    "head_dim": cfg.d, "context": cfg.T, "low_bits": cfg.bits,
                    "important_pct": cfg.pct, "recent": cfg.recent, "group": cfg.G,
-                   "cache_flush_per_step": not args.no_flush},
+                   "cache_flush_per_step": args.flush},
         "roofline": {"bound": "hbm", "achieved": a_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": a_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "launches_timed": KA,
                      "kernel": "decode_split_kernel + decode_merge_kernel (one mikv_decode_attn call)", "kernel_us": float(attn_ms.mean() * 1e3),
                      "bytes_per_launch": float(abytes.mean())},
         "step_hbm_gbps": s_gbps,

@@ -106,8 +106,7 @@ size_t mikv_decode_attn_workspace(const mikv_dims* m, int32_t max_len) {
   if (check_dims(m, true) != MIKV_OK) return 0;
   const int nq = max_len - m->cap16;
   if (nq < 0) return 0;
-  const DecodePlan pl = decode_plan(m->d, m->bits, m->hq / m->hkv, m->cap16, nq);
-  return decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, pl);
+  return decode_ws_bound(m->batch, m->hq, m->hkv, m->d, m->bits, m->group, m->cap16, nq);
 }
 
 mikv_status mikv_decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t len,
@@ -123,7 +122,8 @@ mikv_status mikv_decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t le
   const int nq = len - m->cap16;
   if (nq < 0) return MIKV_ERR_SHAPE;
   if (nq > m->capq) return MIKV_ERR_CAPACITY;
-  const DecodePlan pl = decode_plan(m->d, m->bits, m->hq / m->hkv, m->cap16, nq);
+  const DecodePlan pl = decode_plan(m->batch, m->hkv, m->d, m->bits, m->group, m->hq / m->hkv,
+                                    m->cap16, nq);
   const size_t need = decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, pl);
   if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
   DecodeArgs a;

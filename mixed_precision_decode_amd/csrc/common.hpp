@@ -125,6 +125,22 @@ __device__ __forceinline__ uint32_t quantize8(const float (&x)[8], uint32_t* sz_
   return packed;
 }
 
+// Streaming loads with the nontemporal hint (the cache rows of a decode
+// step are read once; the hint keeps them from displacing reused lines).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_nt16(const void* p) {
+  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ uint2 ld_nt8(const void* p) {
+  const u32x2_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(t.x, t.y);
+}
+__device__ __forceinline__ uint32_t ld_nt4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
 // Load 8 fp16 values (16 bytes) and widen to fp32.
 __device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
   const uint4 w = *reinterpret_cast<const uint4*>(p);

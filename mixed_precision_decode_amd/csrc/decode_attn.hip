@@ -10,31 +10,45 @@
 //
 // Split-K ("flash-decoding") in two launches:
 //   split kernel  one block per (sequence, kv head, query-head tile, split);
-//                 a split is a slot range of ONE tier. Every thread first
-//                 issues all of its key and value loads (TPT tokens), then
-//                 computes scores (kept in registers), the split maximum,
-//                 p = exp2(s - max) and sum p*v. Rows are streamed once:
-//                   FP16 tier: d/8 lanes per token, 16-byte fp16 loads;
-//                   low-bit tier: LPTQ lanes per token, packed-code loads,
+//                 a split is a contiguous slot range of ONE tier, sized so
+//                 that every block streams about the same number of bytes.
+//                 The block walks its range in batches; each thread keeps an
+//                 online softmax (running max, sum, p*v) for its tokens and
+//                 prefetches the next batch while it computes the current
+//                 one, so loads stay in flight without block barriers.
+//                   FP16 tier: d/8 lanes per token, 16-byte fp16 row loads.
+//                   low-bit tier: LPTQ lanes per token, packed-code loads;
 //                   score = scale*sum(q*code) + zero*sum(q) per group,
-//                   o += (p*scale)*code + p*zero per group.
+//                   o += (p*scale)*code + p*zero per group (rows are never
+//                   widened in memory).
 //                 The block owning FP16 slot free16 appends the new token.
 //   merge kernel  one block per (sequence, kv head): combines the split
-//                 partials (max, sum, o) of every query head of the group and
-//                 turns the FP16-tier scores into p16 (summed over the group).
-// Scores are kept in the log2 domain (q-hat is pre-multiplied by
-// log2(e)/sqrt(d)).
+//                 partials of every query head of the group and turns the
+//                 FP16-tier scores into p16 (summed over the group).
+// Scores are in the log2 domain (q-hat is pre-multiplied by log2(e)/sqrt(d)).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace mikv {
 
 constexpr int kThreads = 256;
-#ifndef MIKV_TPT
-#define MIKV_TPT 8
+#ifndef MIKV_TPT16
+#define MIKV_TPT16 4
 #endif
-constexpr int kTPT = MIKV_TPT;  // tokens per thread in a split
+#ifndef MIKV_TPTQ
+#define MIKV_TPTQ 4
+#endif
+#ifndef MIKV_BLOCKS_PER_CU
+#define MIKV_BLOCKS_PER_CU 4
+#endif
+constexpr int kTPT16 = MIKV_TPT16;  // FP16 tokens per thread per batch
+constexpr int kTPTQ = MIKV_TPTQ;    // low-bit tokens per thread per batch
+constexpr int kCUs = 256;
 constexpr float kLog2e = 1.4426950408889634f;
+
+// lanes per low-bit token: 8 (16 or 8 channels per lane), never fewer than
+// 4 bytes of codes per lane
+constexpr int lptq_for(int d, int bits) { return (d * bits / 32) < 8 ? (d * bits / 32) : 8; }
 
 struct DecodeK {
   int hq, hkv, rep, cap16, capq, nq, len, group;
@@ -60,13 +74,20 @@ struct DecodeK {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The empty asm keeps the masked word opaque so that each byte converts with
+// one v_cvt_f32_ubyteN instead of a bit-field extract plus a conversion.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 template <int BITS, int CPL>
 __device__ __forceinline__ void unpack_codes(const uint32_t* w, float (&c)[CPL]) {
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int i = 0; i < CPL / 8; ++i) {
-      const uint32_t lo = w[i] & 0x0F0F0F0Fu;
-      const uint32_t hi = (w[i] >> 4) & 0x0F0F0F0Fu;
+      const uint32_t lo = opaque(w[i] & 0x0F0F0F0Fu);
+      const uint32_t hi = opaque((w[i] >> 4) & 0x0F0F0F0Fu);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         c[8 * i + 2 * k] = static_cast<float>((lo >> (8 * k)) & 0xFFu);
@@ -78,7 +99,7 @@ __device__ __forceinline__ void unpack_codes(const uint32_t* w, float (&c)[CPL])
     for (int i = 0; i < CPL / 16; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t m = (w[i] >> (2 * j)) & 0x03030303u;
+        const uint32_t m = opaque((w[i] >> (2 * j)) & 0x03030303u);
 #pragma unroll
         for (int k = 0; k < 4; ++k) c[16 * i + 4 * k + j] = static_cast<float>((m >> (8 * k)) & 0xFFu);
       }
@@ -93,13 +114,13 @@ template <int NW>
 __device__ __forceinline__ Words<NW> load_words(const uint8_t* p) {
   Words<NW> r;
   if constexpr (NW == 4) {
-    const uint4 t = *reinterpret_cast<const uint4*>(p);
+    const uint4 t = ld_nt16(p);
     r.w[0] = t.x; r.w[1] = t.y; r.w[2] = t.z; r.w[3] = t.w;
   } else if constexpr (NW == 2) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    const uint2 t = ld_nt8(p);
     r.w[0] = t.x; r.w[1] = t.y;
   } else {
-    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    r.w[0] = ld_nt4(p);
   }
   return r;
 }
@@ -122,60 +143,97 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Block-wide: per-head maximum of the per-thread maxima (4 waves).
-template <int RT>
-__device__ __forceinline__ void block_max(float (&m)[RT], float (*sm)[RT], float* out) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+// Online-softmax state of one thread for RT heads and CPL channels.
+template <int RT, int CPL>
+struct Acc {
+  float m[RT], l[RT], z[RT];
+  float a[RT][CPL];
+  __device__ __forceinline__ void init() {
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const float w = wave_max(m[r]);
-    if (lane == 0) sm[wave][r] = w;
+    for (int r = 0; r < RT; ++r) {
+      m[r] = -INFINITY; l[r] = 0.0f; z[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) a[r][i] = 0.0f;
+    }
   }
-  __syncthreads();
-  if (threadIdx.x < RT) {
-    const int r = threadIdx.x;
-    out[r] = fmaxf(fmaxf(sm[0][r], sm[1][r]), fmaxf(sm[2][r], sm[3][r]));
+  // raise the running max of head r to at least mb, rescaling the sums
+  __device__ __forceinline__ void rebase(int r, float mb) {
+    const float mn = fmaxf(m[r], mb);
+    if (mn > m[r]) {
+      const float f = fast_exp2(m[r] - mn);  // 0 when m was -inf
+      l[r] *= f;
+      z[r] *= f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) a[r][i] *= f;
+      m[r] = mn;
+    }
   }
-  __syncthreads();
-}
+};
 
-// Write the split partial: per-thread acc[RT][CPL] over channel slice
-// c0 = lane*CPL (lane = tid % LPT) and per-thread lsum[RT].
+// Combine the block's per-thread states into one partial (max, sum, o).
 template <int D, int RT, int LPT, int CPL>
-__device__ __forceinline__ void write_partial(float (&acc)[RT][CPL], float (&lsum)[RT], const float* M,
-                                              float* red, float* po, float2* pml) {
+__device__ __forceinline__ void write_partial(Acc<RT, CPL>& s, float* red, float (*sm)[RT],
+                                              float* sM, float* po, float2* pml) {
   const int tid = threadIdx.x, wave = tid / kWave, lane64 = tid % kWave;
   const int lane = tid % LPT;
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
+    const float w = wave_max(s.m[r]);
+    if (lane64 == 0) sm[wave][r] = w;
+  }
+  __syncthreads();
+  if (tid < RT) sM[tid] = fmaxf(fmaxf(sm[0][tid], sm[1][tid]), fmaxf(sm[2][tid], sm[3][tid]));
+  __syncthreads();
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) acc[r][i] = fold_slots<LPT>(acc[r][i]);
-    lsum[r] = fold_slots<LPT>(lsum[r]);
+  for (int r = 0; r < RT; ++r) {
+    const float f = (s.m[r] == -INFINITY) ? 0.0f : fast_exp2(s.m[r] - sM[r]);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) s.a[r][i] = fold_slots<LPT>((s.a[r][i] + s.z[r]) * f);
+    s.l[r] = fold_slots<LPT>(s.l[r] * f);
   }
   if (lane64 < LPT) {
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) red[(wave * RT + r) * D + lane * CPL + i] = acc[r][i];
-    }
+      for (int i = 0; i < CPL; ++i) red[(wave * RT + r) * D + lane * CPL + i] = s.a[r][i];
     if (lane64 == 0) {
 #pragma unroll
-      for (int r = 0; r < RT; ++r) red[4 * RT * D + wave * RT + r] = lsum[r];
+      for (int r = 0; r < RT; ++r) red[4 * RT * D + wave * RT + r] = s.l[r];
     }
   }
   __syncthreads();
   for (int i = tid; i < RT * D; i += kThreads) {
-    const int r = i / D;
-    po[i] = red[(0 * RT + r) * D + i % D] + red[(1 * RT + r) * D + i % D] +
-            red[(2 * RT + r) * D + i % D] + red[(3 * RT + r) * D + i % D];
+    const int r = i / D, c = i % D;
+    po[i] = red[(0 * RT + r) * D + c] + red[(1 * RT + r) * D + c] + red[(2 * RT + r) * D + c] +
+            red[(3 * RT + r) * D + c];
   }
   if (tid < RT) {
     const float* l = red + 4 * RT * D;
-    pml[tid] = make_float2(M[tid], l[tid] + l[RT + tid] + l[2 * RT + tid] + l[3 * RT + tid]);
+    pml[tid] = make_float2(sM[tid], l[tid] + l[RT + tid] + l[2 * RT + tid] + l[3 * RT + tid]);
   }
 }
 
-template <int D, int BITS, int RT, int LPTQ>
+// q-hat for the lane's CPL channels of the block's RT heads (fp32; the
+// reciprocal is the hardware approximation, q-hat only feeds scores).
+template <int D, int RT, int CPL>
+__device__ __forceinline__ void load_qhat(const DecodeK& p, int n, int g, int tile, int c0,
+                                          const float* bvec, float (&qh)[RT][CPL]) {
+  const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int h = g * p.rep + tile * RT + r;
+    const uint16_t* qp = p.q + (static_cast<int64_t>(n) * p.hq + h) * D + c0;
+#pragma unroll
+    for (int i = 0; i < CPL; i += 8) {
+      float qv[8];
+      load8(qp + i, qv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qh[r][i + e] = qv[e] * __builtin_amdgcn_rcpf(bvec[c0 + i + e]) * qscale;
+    }
+  }
+}
+
+template <int D, int BITS, int RT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p) {
   const int S = p.S16 + p.Sq;
   const int split = blockIdx.x % S;
@@ -185,7 +243,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
   const int n = unit / p.hkv;
   const int g = unit % p.hkv;
   const int tid = threadIdx.x;
-  const float qscale = kLog2e / sqrtf(static_cast<float>(D));
   const float* bvec = p.b + static_cast<int64_t>(unit) * D;
   const int part = (unit * p.tiles + tile) * S + split;
   float* po = p.part_o + static_cast<int64_t>(part) * RT * D;
@@ -197,258 +254,380 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
 
   if (split < p.S16) {
     // ---------------- FP16 tier ----------------
-    constexpr int LPT = D / 8, CPL = 8, SLOTS = kThreads / LPT;
+    constexpr int LPT = D / 8, CPL = 8, SLOTS = kThreads / LPT, TPT = kTPT16;
+    constexpr int BATCH = SLOTS * TPT;
     const int lane = tid % LPT, tslot = tid / LPT, c0 = lane * CPL;
     const int s0 = split * p.C16;
     const int s1 = min(p.cap16, s0 + p.C16);
     const int fr = p.free16[unit];
     const int64_t rb = static_cast<int64_t>(unit) * p.cap16;
-    uint4 kr[kTPT] = {}, vr[kTPT] = {};
+    struct Regs { uint4 k[TPT], v[TPT]; };
+    auto load = [&](int base, Regs& R) {
 #pragma unroll
-    for (int j = 0; j < kTPT; ++j) {
-      const int t = s0 + j * SLOTS + tslot;
-      if (t < s1) {
-        kr[j] = *reinterpret_cast<const uint4*>(p.k16 + (rb + t) * D + c0);
-        vr[j] = *reinterpret_cast<const uint4*>(p.v16 + (rb + t) * D + c0);
-      }
-    }
-    float qh[RT][CPL];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int h = g * p.rep + tile * RT + r;
-      float qv[8];
-      load8(p.q + (static_cast<int64_t>(n) * p.hq + h) * D + c0, qv);
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) qh[r][i] = qv[i] * __builtin_amdgcn_rcpf(bvec[c0 + i]) * qscale;
-    }
-    // the new token replaces the free slot's stale row (and is appended)
-    if (fr >= s0 && fr < s1 && (fr - s0) % SLOTS == tslot) {
-      const int j = (fr - s0) / SLOTS;
-      const int64_t nb = static_cast<int64_t>(unit) * D + c0;
-      float kn[8];
-      load8(p.k_new + nb, kn);
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = f2h(mul_rn(kn[2 * i], bvec[c0 + 2 * i]));
-        const uint32_t hi = f2h(mul_rn(kn[2 * i + 1], bvec[c0 + 2 * i + 1]));
-        w[i] = lo | (hi << 16);
-      }
-      const uint4 kv = make_uint4(w[0], w[1], w[2], w[3]);
-      const uint4 vv = *reinterpret_cast<const uint4*>(p.v_new + nb);
-#pragma unroll
-      for (int jj = 0; jj < kTPT; ++jj)
-        if (jj == j) { kr[jj] = kv; vr[jj] = vv; }
-      if (tile == 0) {
-        *reinterpret_cast<uint4*>(p.k16 + (rb + fr) * D + c0) = kv;
-        *reinterpret_cast<uint4*>(p.v16 + (rb + fr) * D + c0) = vv;
-        if (lane == 0) p.pos16[rb + fr] = p.len - 1;
-      }
-    }
-    float sc[kTPT][RT];
-    float mloc[RT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) mloc[r] = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kTPT; ++j) {
-      const int t = s0 + j * SLOTS + tslot;
-      const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kr[j]);
-      float kx[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { kx[2 * i] = lo_h(kw[i]); kx[2 * i + 1] = hi_h(kw[i]); }
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        float dot = 0.0f;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) dot += qh[r][i] * kx[i];
-        dot = group_sum<LPT>(dot);
-        sc[j][r] = (t < s1) ? dot : -INFINITY;
-        mloc[r] = fmaxf(mloc[r], sc[j][r]);
-        if (lane == 0 && t < s1)
-          p.sc16[(static_cast<int64_t>(unit) * p.rep + tile * RT + r) * p.cap16 + t] = dot;
-      }
-    }
-    block_max<RT>(mloc, sm_max, sm_M);
-    float acc[RT][CPL], lsum[RT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      lsum[r] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[r][i] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < kTPT; ++j) {
-      const int t = s0 + j * SLOTS + tslot;
-      if (t < s1) {
-        const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vr[j]);
-        float vx[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { vx[2 * i] = lo_h(vw[i]); vx[2 * i + 1] = hi_h(vw[i]); }
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const float pr = fast_exp2(sc[j][r] - sm_M[r]);
-          lsum[r] += pr;
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) acc[r][i] += pr * vx[i];
+      for (int j = 0; j < TPT; ++j) {
+        const int t = base + j * SLOTS + tslot;
+        if (t < s1) {
+          R.k[j] = ld_nt16(p.k16 + (rb + t) * D + c0);
+          R.v[j] = ld_nt16(p.v16 + (rb + t) * D + c0);
         }
       }
+    };
+    float qh[RT][CPL];
+    Acc<RT, CPL> st;
+    st.init();
+    Regs cur = {}, nxt = {};
+    load(s0, cur);
+    load_qhat<D, RT, CPL>(p, n, g, tile, c0, bvec, qh);
+    for (int base = s0; base < s1; base += BATCH) {
+      if (base + BATCH < s1) load(base + BATCH, nxt);
+      // the new token replaces the free slot's stale row (and is appended)
+      if (fr >= base && fr < base + BATCH && fr < s1 && (fr - base) % SLOTS == tslot) {
+        const int j = (fr - base) / SLOTS;
+        const int64_t nb = static_cast<int64_t>(unit) * D + c0;
+        float kn[8];
+        load8(p.k_new + nb, kn);
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = f2h(mul_rn(kn[2 * i], bvec[c0 + 2 * i]));
+          const uint32_t hi = f2h(mul_rn(kn[2 * i + 1], bvec[c0 + 2 * i + 1]));
+          w[i] = lo | (hi << 16);
+        }
+        const uint4 kv = make_uint4(w[0], w[1], w[2], w[3]);
+        const uint4 vv = *reinterpret_cast<const uint4*>(p.v_new + nb);
+#pragma unroll
+        for (int jj = 0; jj < TPT; ++jj)
+          if (jj == j) { cur.k[jj] = kv; cur.v[jj] = vv; }
+        if (tile == 0) {
+          *reinterpret_cast<uint4*>(p.k16 + (rb + fr) * D + c0) = kv;
+          *reinterpret_cast<uint4*>(p.v16 + (rb + fr) * D + c0) = vv;
+          if (lane == 0) p.pos16[rb + fr] = p.len - 1;
+        }
+      }
+      float sc[TPT][RT];
+#pragma unroll
+      for (int j = 0; j < TPT; ++j) {
+        const int t = base + j * SLOTS + tslot;
+        const uint32_t* kw = reinterpret_cast<const uint32_t*>(&cur.k[j]);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          float dot = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dot += qh[r][2 * i] * lo_h(kw[i]);
+            dot += qh[r][2 * i + 1] * hi_h(kw[i]);
+          }
+          dot = group_sum<LPT>(dot);
+          sc[j][r] = (t < s1) ? dot : -INFINITY;
+          if (lane == 0 && t < s1)
+            p.sc16[(static_cast<int64_t>(unit) * p.rep + tile * RT + r) * p.cap16 + t] = dot;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        float bm = sc[0][r];
+#pragma unroll
+        for (int j = 1; j < TPT; ++j) bm = fmaxf(bm, sc[j][r]);
+        st.rebase(r, bm);
+      }
+#pragma unroll
+      for (int j = 0; j < TPT; ++j) {
+        const int t = base + j * SLOTS + tslot;
+        if (t < s1) {
+          const uint32_t* vw = reinterpret_cast<const uint32_t*>(&cur.v[j]);
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            const float pr = fast_exp2(sc[j][r] - st.m[r]);
+            st.l[r] += pr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              st.a[r][2 * i] += pr * lo_h(vw[i]);
+              st.a[r][2 * i + 1] += pr * hi_h(vw[i]);
+            }
+          }
+        }
+      }
+      cur = nxt;
     }
-    write_partial<D, RT, LPT, CPL>(acc, lsum, sm_M, red, po, pml);
+    write_partial<D, RT, LPT, CPL>(st, red, sm_max, sm_M, po, pml);
   } else {
     // ---------------- low-bit tier ----------------
-    constexpr int LPT = LPTQ, CPL = D / LPTQ, SLOTS = kThreads / LPT;
+    constexpr int LPT = lptq_for(D, BITS), CPL = D / LPT, SLOTS = kThreads / LPT, TPT = kTPTQ;
+    constexpr int BATCH = SLOTS * TPT;
     constexpr int NB = CPL * BITS / 8, NW = NB / 4;
     constexpr int CB = D * BITS / 8;
+    // single-head tiles score keys with integer dot products on the packed
+    // codes (no per-code conversion); head tiles share converted codes
+    constexpr bool kIntDot = (RT == 1);
     const int lane = tid % LPT, tslot = tid / LPT, c0 = lane * CPL;
     const int gpt = D / p.group;
     const int gi = c0 / p.group;
     const int t0 = (split - p.S16) * p.Cq;
     const int t1 = min(p.nq, t0 + p.Cq);
     const int64_t rb = static_cast<int64_t>(unit) * p.capq;
-    Words<NW> kc[kTPT] = {}, vc[kTPT] = {};
-    uint32_t ks[kTPT] = {}, vs[kTPT] = {};
+    // per-thread stream pointers; token j of a batch is j*SLOTS rows further
+    const uint8_t* pkq = p.kq + (rb + t0 + tslot) * CB + lane * NB;
+    const uint8_t* pvq = p.vq + (rb + t0 + tslot) * CB + lane * NB;
+    const uint32_t* pks = p.ksz + (rb + t0 + tslot) * gpt + gi;
+    const uint32_t* pvs = p.vsz + (rb + t0 + tslot) * gpt + gi;
+    const int sz_step = SLOTS * gpt;
+    struct Regs { Words<NW> k[TPT], v[TPT]; uint32_t ks[TPT], vs[TPT]; };
+    auto load = [&](int base, int boff, Regs& R) {
 #pragma unroll
-    for (int j = 0; j < kTPT; ++j) {
-      const int t = t0 + j * SLOTS + tslot;
-      if (t < t1) {
-        kc[j] = load_words<NW>(p.kq + (rb + t) * CB + lane * NB);
-        ks[j] = p.ksz[(rb + t) * gpt + gi];
-        vc[j] = load_words<NW>(p.vq + (rb + t) * CB + lane * NB);
-        vs[j] = p.vsz[(rb + t) * gpt + gi];
+      for (int j = 0; j < TPT; ++j) {
+        const int t = base + j * SLOTS + tslot;
+        if (t < t1) {
+          R.k[j] = load_words<NW>(pkq + static_cast<int64_t>(boff + j * SLOTS) * CB);
+          R.ks[j] = ld_nt4(pks + static_cast<int64_t>(boff / SLOTS + j) * sz_step);
+          R.v[j] = load_words<NW>(pvq + static_cast<int64_t>(boff + j * SLOTS) * CB);
+          R.vs[j] = ld_nt4(pvs + static_cast<int64_t>(boff / SLOTS + j) * sz_step);
+        }
+      }
+    };
+    float qsum[RT];
+    Acc<RT, CPL> st;
+    st.init();
+    Regs cur = {}, nxt = {};
+    load(t0, 0, cur);
+    float qh[RT][CPL];
+    load_qhat<D, RT, CPL>(p, n, g, tile, c0, bvec, qh);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      qsum[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) qsum[r] += qh[r][i];
+    }
+    // Integer form of q-hat (single head): q_int = rint(q-hat * 2^F) with F
+    // chosen per lane so |q_int| < 2^22, biased by 2^23 into [0, 2^24) and
+    // cut into six 4-bit digits laid out like the code nibbles. Then
+    //   sum_c q_int[c]*code[c] = sum_d 16^d dot8(codes, digit_d)
+    //                            - 2^23 * dot8(codes, 0x11111111),
+    // exact in 32-bit integers (two's-complement wraparound cancels the bias).
+    constexpr int NQW = CPL / 8;  // nibble words (8 channels each) per lane
+    uint32_t qd[6][NQW];
+    float qunit = 1.0f;
+    if constexpr (kIntDot) {
+      static_assert(static_cast<unsigned long long>(CPL) * ((1 << BITS) - 1) * 15ull * 1118481ull <
+                        4294967296ull, "digit sums must fit 32 bits");
+      float mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) mx = fmaxf(mx, fabsf(qh[0][i]));
+      int e = 0;
+      if (mx > 0.0f) (void)frexpf(mx, &e);
+      const int F = 22 - e;
+      qunit = ldexpf(1.0f, -F);
+#pragma unroll
+      for (int d = 0; d < 6; ++d)
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) qd[d][i] = 0;
+#pragma unroll
+      for (int i = 0; i < NQW; ++i) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          // channel of nibble k in nibble word i
+          int ch;
+          if constexpr (BITS == 4) ch = 8 * i + k;
+          else ch = 16 * (i / 2) + 4 * (k / 2) + 2 * (k % 2) + (i % 2);
+          const int qi = static_cast<int>(rintf(ldexpf(qh[0][ch], F)));
+          const uint32_t qb = static_cast<uint32_t>(qi + (1 << 23));
+#pragma unroll
+          for (int d = 0; d < 6; ++d) qd[d][i] |= ((qb >> (4 * d)) & 0xFu) << (4 * k);
+        }
       }
     }
-    float sc[kTPT][RT];
-    float mloc[RT];
+    for (int base = t0, boff = 0; base < t1; base += BATCH, boff += BATCH) {
+      if (base + BATCH < t1) load(base + BATCH, boff + BATCH, nxt);
+      float sc[TPT][RT];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) mloc[r] = -INFINITY;
-    {
-      float qh[RT][CPL], qsum[RT];
+      for (int j = 0; j < TPT; ++j) {
+        const int t = base + j * SLOTS + tslot;
+        const float s = lo_h(cur.ks[j]), z = hi_h(cur.ks[j]);
+        if constexpr (kIntDot) {
+          uint32_t acc[6] = {0u, 0u, 0u, 0u, 0u, 0u}, csum = 0u;
 #pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const int h = g * p.rep + tile * RT + r;
-        const uint16_t* qp = p.q + (static_cast<int64_t>(n) * p.hq + h) * D + c0;
-        qsum[r] = 0.0f;
+          for (int i = 0; i < NQW; ++i) {
+            uint32_t x;
+            if constexpr (BITS == 4) x = cur.k[j].w[i];
+            else x = (i % 2 == 0) ? (cur.k[j].w[i / 2] & 0x33333333u)
+                                  : ((cur.k[j].w[i / 2] >> 2) & 0x33333333u);
 #pragma unroll
-        for (int i = 0; i < CPL; i += 8) {
-          float qv[8];
-          load8(qp + i, qv);
+            for (int d = 0; d < 6; ++d) acc[d] = __builtin_amdgcn_udot8(x, qd[d][i], acc[d], false);
+            csum = __builtin_amdgcn_udot8(x, 0x11111111u, csum, false);
+          }
+          const uint32_t u = acc[0] + (acc[1] << 4) + (acc[2] << 8) + (acc[3] << 12) +
+                             (acc[4] << 16) + (acc[5] << 20);
+          const int32_t rdot = static_cast<int32_t>(u - (csum << 23));
+          const float dot = static_cast<float>(rdot) * qunit;
+          const float v = group_sum<LPT>(s * dot + z * qsum[0]);
+          sc[j][0] = (t < t1) ? v : -INFINITY;
+        } else {
+          float cf[CPL];
+          unpack_codes<BITS, CPL>(cur.k[j].w, cf);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            qh[r][i + e] = qv[e] * __builtin_amdgcn_rcpf(bvec[c0 + i + e]) * qscale;
-            qsum[r] += qh[r][i + e];
+          for (int r = 0; r < RT; ++r) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) dot += qh[r][i] * cf[i];
+            const float v = group_sum<LPT>(s * dot + z * qsum[r]);
+            sc[j][r] = (t < t1) ? v : -INFINITY;
           }
         }
       }
 #pragma unroll
-      for (int j = 0; j < kTPT; ++j) {
-        const int t = t0 + j * SLOTS + tslot;
-        float cf[CPL];
-        unpack_codes<BITS, CPL>(kc[j].w, cf);
-        const float s = lo_h(ks[j]), z = hi_h(ks[j]);
+      for (int r = 0; r < RT; ++r) {
+        float bm = sc[0][r];
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          float dot = 0.0f;
+        for (int j = 1; j < TPT; ++j) bm = fmaxf(bm, sc[j][r]);
+        st.rebase(r, bm);
+      }
 #pragma unroll
-          for (int i = 0; i < CPL; ++i) dot += qh[r][i] * cf[i];
-          float v = s * dot + z * qsum[r];
-          v = group_sum<LPT>(v);
-          sc[j][r] = (t < t1) ? v : -INFINITY;
-          mloc[r] = fmaxf(mloc[r], sc[j][r]);
+      for (int j = 0; j < TPT; ++j) {
+        const int t = base + j * SLOTS + tslot;
+        if (t < t1) {
+          float cf[CPL];
+          unpack_codes<BITS, CPL>(cur.v[j].w, cf);
+          const float s = lo_h(cur.vs[j]), z = hi_h(cur.vs[j]);
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            const float pr = fast_exp2(sc[j][r] - st.m[r]);
+            st.l[r] += pr;
+            st.z[r] += pr * z;
+            const float w = pr * s;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) st.a[r][i] += w * cf[i];
+          }
         }
       }
+      cur = nxt;
     }
-    block_max<RT>(mloc, sm_max, sm_M);
-    float acc[RT][CPL], lsum[RT], accz[RT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      lsum[r] = 0.0f;
-      accz[r] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[r][i] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < kTPT; ++j) {
-      const int t = t0 + j * SLOTS + tslot;
-      if (t < t1) {
-        float cf[CPL];
-        unpack_codes<BITS, CPL>(vc[j].w, cf);
-        const float s = lo_h(vs[j]), z = hi_h(vs[j]);
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const float pr = fast_exp2(sc[j][r] - sm_M[r]);
-          lsum[r] += pr;
-          const float w = pr * s;
-          accz[r] += pr * z;
-#pragma unroll
-          for (int i = 0; i < CPL; ++i) acc[r][i] += w * cf[i];
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < RT; ++r)
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[r][i] += accz[r];
-    write_partial<D, RT, LPT, CPL>(acc, lsum, sm_M, red, po, pml);
+    write_partial<D, RT, LPT, CPL>(st, red, sm_max, sm_M, po, pml);
   }
 }
 
+// One block per (sequence, kv head). All global loads of the block (split
+// statistics, the first kMergePF partial vectors of each output, the
+// FP16-tier scores) are issued before the first barrier so the kernel costs
+// about one memory round trip. Dynamic LDS: [rep][S] (max, sum) pairs, then
+// [rep] maxima and [rep] reciprocal sums.
+constexpr int kMergePF = 8;
+constexpr int kMergeSlots = 4;  // FP16-tier slots per thread held in registers
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p, int RT) {
-  extern __shared__ float sML[];  // [rep][2]
+  extern __shared__ float2 sml[];
   const int unit = blockIdx.x;
   const int n = unit / p.hkv, g = unit % p.hkv;
   const int tid = threadIdx.x;
   const int S = p.S16 + p.Sq;
-  for (int hl = tid; hl < p.rep; hl += kThreads) {
-    const int tl = hl / RT, r = hl % RT;
-    const float2* ml = p.part_ml + static_cast<int64_t>((unit * p.tiles + tl) * S) * RT + r;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s * RT].x);
-    float L = 0.0f;
-    for (int s = 0; s < S; ++s) L += ml[s * RT].y * fast_exp2(ml[s * RT].x - M);
-    sML[2 * hl] = M;
-    sML[2 * hl + 1] = 1.0f / L;
+  const int rep = p.rep;
+  float* sM = reinterpret_cast<float*>(sml + rep * S);
+  float* sIL = sM + rep;
+  const float2* __restrict__ pml = p.part_ml;
+  const float* __restrict__ pov = p.part_o;
+  const float* __restrict__ sc = p.sc16 + static_cast<int64_t>(unit) * rep * p.cap16;
+  // (1) issue every load
+  for (int i = tid; i < rep * S; i += kThreads) {
+    const int hl = i / S, s = i % S;
+    sml[i] = pml[(static_cast<int64_t>((unit * p.tiles + hl / RT) * S) + s) * RT + hl % RT];
+  }
+  const int i0 = tid;  // first output (head hl0, channel c0) of this thread
+  const bool has0 = i0 < rep * D;
+  const int hl0 = i0 / D, c0 = i0 % D;
+  const float* po0 = pov + (static_cast<int64_t>((unit * p.tiles + hl0 / RT) * S) * RT + hl0 % RT) * D + c0;
+  float pf[kMergePF];
+#pragma unroll
+  for (int s = 0; s < kMergePF; ++s) pf[s] = (has0 && s < S) ? po0[static_cast<int64_t>(s) * RT * D] : 0.0f;
+  float sv[kMergeSlots];
+  const bool slots_in_regs = (rep == 1) && (p.cap16 <= kMergeSlots * kThreads);
+  if (slots_in_regs) {
+#pragma unroll
+    for (int k = 0; k < kMergeSlots; ++k) {
+      const int sl = tid + k * kThreads;
+      sv[k] = (sl < p.cap16) ? sc[sl] : 0.0f;
+    }
   }
   __syncthreads();
-  for (int i = tid; i < p.rep * D; i += kThreads) {
-    const int hl = i / D, c = i % D;
-    const int tl = hl / RT, r = hl % RT;
-    const int64_t pb = static_cast<int64_t>((unit * p.tiles + tl) * S);
-    const float M = sML[2 * hl];
-    float v = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float2 ml = p.part_ml[(pb + s) * RT + r];
-      v += p.part_o[((pb + s) * RT + r) * D + c] * fast_exp2(ml.x - M);
-    }
-    p.o[(static_cast<int64_t>(n) * p.hq + g * p.rep + hl) * D + c] = v * sML[2 * hl + 1];
+  // (2) per head: maximum and reciprocal normaliser
+  for (int hl = tid; hl < rep; hl += kThreads) {
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, sml[hl * S + s].x);
+    float L = 0.0f;
+    for (int s = 0; s < S; ++s) L += sml[hl * S + s].y * fast_exp2(sml[hl * S + s].x - M);
+    sM[hl] = M;
+    sIL[hl] = 1.0f / L;
   }
-  for (int sl = tid; sl < p.cap16; sl += kThreads) {
-    float a = 0.0f;
-    for (int hl = 0; hl < p.rep; ++hl) {
-      const float s = p.sc16[(static_cast<int64_t>(unit) * p.rep + hl) * p.cap16 + sl];
-      a += fast_exp2(s - sML[2 * hl]) * sML[2 * hl + 1];
+  __syncthreads();
+  // (3) outputs
+  for (int i = tid; i < rep * D; i += kThreads) {
+    const int hl = i / D, c = i % D;
+    const float M = sM[hl];
+    const float2* ml = sml + hl * S;
+    float v = 0.0f;
+    int s = 0;
+    if (i == i0) {
+#pragma unroll
+      for (int k = 0; k < kMergePF; ++k)
+        if (k < S) v += pf[k] * fast_exp2(ml[k].x - M);
+      s = kMergePF;
     }
-    p.p16[static_cast<int64_t>(unit) * p.cap16 + sl] = a;
+    const float* po = pov + (static_cast<int64_t>((unit * p.tiles + hl / RT) * S) * RT + hl % RT) * D + c;
+#pragma unroll 4
+    for (; s < S; ++s) v += po[static_cast<int64_t>(s) * RT * D] * fast_exp2(ml[s].x - M);
+    p.o[(static_cast<int64_t>(n) * p.hq + g * rep + hl) * D + c] = v * sIL[hl];
+  }
+  // (4) p16 = sum over the group's heads of the FP16-tier probabilities
+  float* __restrict__ p16 = p.p16 + static_cast<int64_t>(unit) * p.cap16;
+  if (slots_in_regs) {
+#pragma unroll
+    for (int k = 0; k < kMergeSlots; ++k) {
+      const int sl = tid + k * kThreads;
+      if (sl < p.cap16) p16[sl] = fast_exp2(sv[k] - sM[0]) * sIL[0];
+    }
+  } else {
+    for (int sl = tid; sl < p.cap16; sl += kThreads) {
+      float a = 0.0f;
+      for (int hl = 0; hl < rep; ++hl) a += fast_exp2(sc[hl * p.cap16 + sl] - sM[hl]) * sIL[hl];
+      p16[sl] = a;
+    }
   }
 }
 
 static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// lanes per low-bit token: 4 for a single head (32 channels per lane at
-// d = 128), 8 for head tiles (fewer registers per lane), never below 4 bytes
-// of codes per lane
-constexpr int lptq_for(int d, int bits, int RT) {
-  return (RT == 1) ? 4 : ((d * bits / 32) < 8 ? (d * bits / 32) : 8);
-}
-
-DecodePlan decode_plan(int d, int bits, int rep, int cap16, int nq) {
+// Split sizes. The grid is sized to one resident wave of blocks
+// (MIKV_BLOCKS_PER_CU per compute unit, which the split kernel's register
+// use allows), so no block starts after the others have drained. The
+// splits of a (sequence, kv head) are shared between the tiers in
+// proportion to their bytes, so every block streams about the same amount;
+// each tier gets at least one split when it has tokens.
+DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq) {
   DecodePlan pl;
   pl.RT = (rep % 4 == 0) ? 4 : (rep % 2 == 0 ? 2 : 1);
   pl.tiles = rep / pl.RT;
-  pl.C16 = (kThreads / (d / 8)) * kTPT;
-  pl.Cq = (kThreads / lptq_for(d, bits, pl.RT)) * kTPT;
+  const double b16 = static_cast<double>(cap16) * 4.0 * d;
+  const double bq = static_cast<double>(nq) * 2.0 * (d * bits / 8 + 4 * (d / group));
+  const long units = static_cast<long>(batch) * hkv * pl.tiles;
+  long per_unit = (static_cast<long>(kCUs) * MIKV_BLOCKS_PER_CU) / units;
+  // no split below ~16 KB of rows
+  const long cap_splits = static_cast<long>((b16 + bq) / 16384.0) + 1;
+  if (per_unit > cap_splits) per_unit = cap_splits;
+  if (nq > 0) {
+    if (per_unit < 2) per_unit = 2;
+    long s16 = static_cast<long>(per_unit * b16 / (b16 + bq) + 0.5);
+    if (s16 < 1) s16 = 1;
+    if (s16 > per_unit - 1) s16 = per_unit - 1;
+    if (s16 > cap16) s16 = cap16;
+    long sq = per_unit - s16;
+    if (sq > nq) sq = nq;
+    pl.S16 = static_cast<int>(s16);
+    pl.Sq = static_cast<int>(sq);
+  } else {
+    pl.S16 = static_cast<int>(per_unit < 1 ? 1 : (per_unit > cap16 ? cap16 : per_unit));
+    pl.Sq = 0;
+  }
+  pl.C16 = cdiv(cap16, pl.S16);
   pl.S16 = cdiv(cap16, pl.C16);
-  pl.Sq = nq > 0 ? cdiv(nq, pl.Cq) : 0;
+  pl.Cq = nq > 0 ? cdiv(nq, pl.Sq) : 0;
+  if (nq > 0) pl.Sq = cdiv(nq, pl.Cq);
   return pl;
 }
 
@@ -460,6 +639,19 @@ size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int cap16, const Decod
   const size_t nparts = units * pl.tiles * (pl.S16 + pl.Sq);
   return al256(nparts * pl.RT * sizeof(float2)) + al256(nparts * pl.RT * d * sizeof(float)) +
          al256(units * rep * cap16 * sizeof(float));
+}
+
+// Workspace for every length up to nq_max: the partial count of any plan is
+// at most max(2, blocks-per-unit) + 1 splits per (sequence, kv head, tile).
+size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nq_max) {
+  const int rep = hq / hkv;
+  DecodePlan pl = decode_plan(batch, hkv, d, bits, group, rep, cap16, nq_max);
+  const long units = static_cast<long>(batch) * hkv * pl.tiles;
+  long per_unit = (static_cast<long>(kCUs) * MIKV_BLOCKS_PER_CU) / units;
+  if (per_unit < 2) per_unit = 2;
+  pl.S16 = static_cast<int>(per_unit + 1);
+  pl.Sq = 0;
+  return decode_ws_bytes(batch, hq, hkv, d, cap16, pl);
 }
 
 template <int D, int BITS, int RT>
@@ -475,18 +667,19 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   k.vsz = reinterpret_cast<const uint32_t*>(a.vsz);
   k.o = a.o; k.p16 = a.p16;
   const size_t units = static_cast<size_t>(a.batch) * a.hkv;
-  const size_t nparts = units * pl.tiles * (pl.S16 + pl.Sq);
+  const int S = pl.S16 + pl.Sq;
+  const size_t nparts = units * pl.tiles * S;
   char* w = static_cast<char*>(a.ws);
   k.part_ml = reinterpret_cast<float2*>(w);
   w += al256(nparts * pl.RT * sizeof(float2));
   k.part_o = reinterpret_cast<float*>(w);
   w += al256(nparts * pl.RT * D * sizeof(float));
   k.sc16 = reinterpret_cast<float*>(w);
-  constexpr int LPTQ = lptq_for(D, BITS, RT);
-  decode_split_kernel<D, BITS, RT, LPTQ><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
+  decode_split_kernel<D, BITS, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_merge_kernel<D><<<static_cast<unsigned>(units), kThreads, 2 * k.rep * sizeof(float), stream>>>(k, RT);
+  const size_t lds = static_cast<size_t>(k.rep) * S * sizeof(float2) + 2 * k.rep * sizeof(float);
+  decode_merge_kernel<D><<<static_cast<unsigned>(units), kThreads, lds, stream>>>(k, RT);
   return hipGetLastError();
 }
 

@@ -25,6 +25,10 @@
 namespace mikv {
 
 // ------------------------------------------------------------------ decode
+// All slot loads of the block are issued at once (up to kH2OSlots per
+// thread, the common case), so the select costs one memory round trip and the
+// demotion a second one.
+constexpr int kH2OSlots = 16;
 template <int D, int BITS, int NL>
 __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
   __shared__ float s_acc[4];
@@ -34,17 +38,35 @@ __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
   const int unit = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t base16 = static_cast<int64_t>(unit) * a.cap16;
+  const float* accin = a.acc16 + base16;  // rewritten below, so not restrict
+  const float* __restrict__ p16 = a.p16 + base16;
+  const int32_t* __restrict__ pos16 = a.pos16 + base16;
   const int fr = a.free16[unit];
   const int limit = a.len - a.recent;  // candidates: pos < limit
   // worst candidate = smallest acc, latest position among equal acc
   float wa = INFINITY;
   int wp = -1, ws = -1;
-  for (int s = tid; s < a.cap16; s += 256) {
-    const float prev = (s == fr) ? 0.0f : a.acc16[base16 + s];
-    const float v = prev + a.p16[base16 + s];
+  auto consider = [&](int s, float prev, float pp, int pos) {
+    if (s == fr) { prev = 0.0f; pos = a.len - 1; }
+    const float v = prev + pp;
     a.acc16[base16 + s] = v;
-    const int pos = (s == fr) ? a.len - 1 : a.pos16[base16 + s];
     if (pos < limit && (v < wa || (v == wa && pos > wp))) { wa = v; wp = pos; ws = s; }
+  };
+  if (a.cap16 <= kH2OSlots * 256) {
+    float av[kH2OSlots], pv[kH2OSlots];
+    int qv[kH2OSlots];
+#pragma unroll
+    for (int k = 0; k < kH2OSlots; ++k) {
+      const int s = tid + k * 256;
+      if (s < a.cap16) { av[k] = accin[s]; pv[k] = p16[s]; qv[k] = pos16[s]; }
+    }
+#pragma unroll
+    for (int k = 0; k < kH2OSlots; ++k) {
+      const int s = tid + k * 256;
+      if (s < a.cap16) consider(s, av[k], pv[k], qv[k]);
+    }
+  } else {
+    for (int s = tid; s < a.cap16; s += 256) consider(s, accin[s], p16[s], pos16[s]);
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {

@@ -23,8 +23,10 @@ struct DecodePlan {
   int RT;          // query heads per block
   int tiles;       // rep / RT
 };
-DecodePlan decode_plan(int d, int bits, int rep, int cap16, int nq);
+DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq);
 size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int cap16, const DecodePlan& plan);
+// workspace that serves every length up to nq_max low-bit tokens
+size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nq_max);
 
 struct DecodeArgs {
   int batch, hq, hkv, d, group, bits, cap16, capq, len;

@@ -67,7 +67,7 @@ def test_decode_attn_validation(lib):
     assert call(good, q=None) == L.MIKV_ERR_NULL
     assert call(good, length=10) == L.MIKV_ERR_SHAPE            # len < cap16
     assert call(good, length=112) == L.MIKV_ERR_CAPACITY        # len - cap16 > capq
-    assert call(good, ws_bytes=ws_need - 1) == L.MIKV_ERR_WORKSPACE
+    assert call(good, ws_bytes=16) == L.MIKV_ERR_WORKSPACE
     bad = _cache()
     bad.kq = None
     assert call(good, cache=bad) == L.MIKV_ERR_NULL
