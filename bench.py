@@ -1,8 +1,9 @@
 """Benchmark of the MiKV mixed-precision decode path on one MI355X.
 
-A step is one decode step of the whole batch: mixed-precision attention over
-both cache tiers (append + scores + softmax + value sum, one kernel) followed
-by the H2O accumulate / re-select / demote kernel. The cache is built once
+A step is one decode step of the whole batch (mikv_decode_step):
+mixed-precision attention over both cache tiers (append + scores + softmax +
+value sum) and the H2O accumulate / re-select / demote, in two launches (the
+attention's merge kernel also runs the H2O update). The cache is built once
 before timing (balancer + prefill build on the GPU) from seeded synthetic
 inputs; every step consumes a new seeded (q, k, v) token per sequence and
 kv head, so the low-bit tier grows by one token per step.
@@ -118,6 +119,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", choices=("read", "write", "none"), default="read")
+    ap.add_argument("--graph", type=int, default=0,
+                    help="1: replay each timed step as one HIP graph; 0 (default): eager "
+                         "launches, measured faster on MI355X for this step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -177,16 +181,45 @@ def main():
     N = cfg.T
     cpu_state = None
 
+    def attn_call(s, n_len):
+        qd, kd, vd = steps_in[s]
+        L.mikv_decode_attn(dims, cache, n_len, qd, kd, vd, b, o, p16, ws)
+
+    def step_call(s, n_len):
+        qd, kd, vd = steps_in[s]
+        L.mikv_decode_step(dims, cache, n_len, cfg.recent, cfg.H, qd, kd, vd, b, o, p16, ws)
+
+    def h2o_call(n_len):
+        L.mikv_h2o_update_select(dims, cache, n_len, cfg.recent, cfg.H, p16=p16)
+
+    # Optionally replay each timed step (decode attention + H2O) as one HIP
+    # graph, as a decode loop could.
+    graphs = {}
+    if args.graph:
+        for s in range(W, W + K):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_call(s, cfg.T + s + 1)
+            graphs[s] = g
+        torch.cuda.synchronize()
+
     def one_step(s, ev_start=None, ev_attn=None, ev_end=None):
         nonlocal N
         N += 1
-        qd, kd, vd = steps_in[s]
+        assert N == cfg.T + s + 1
         if ev_start is not None:
             ev_start.record()
-        L.mikv_decode_attn(dims, cache, N, qd, kd, vd, b, o, p16, ws)
-        if ev_attn is not None:
+        if ev_attn is None:
+            # one decode step: mikv_decode_step (attention + H2O, two launches)
+            if s in graphs:
+                graphs[s].replay()
+            else:
+                step_call(s, N)
+        else:
+            # attention-only timing: mikv_decode_attn, then the H2O call
+            attn_call(s, N)
             ev_attn.record()
-        L.mikv_h2o_update_select(dims, cache, N, cfg.recent, cfg.H, p16=p16)
+            h2o_call(N)
         if ev_end is not None:
             ev_end.record()
 
@@ -251,7 +284,7 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "q_heads": cfg.hq, "kv_heads": cfg.hkv,
                    "head_dim": cfg.d, "context": cfg.T, "low_bits": cfg.bits,
                    "important_pct": cfg.pct, "recent": cfg.recent, "group": cfg.G,
-                   "cache_flush_per_step": args.flush},
+                   "cache_flush_per_step": args.flush, "step_launch": "hip_graph" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": a_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": a_gbps / HBM_PEAK_GBPS, "traffic": None,
                      "launches_timed": KA,

@@ -220,6 +220,25 @@ mikv_status mikv_h2o_update_select(const mikv_dims* dims,
                                    size_t ws_bytes, void* stream);
 
 /*
+ * One full decode step: mikv_decode_attn followed by the decode mode of
+ * mikv_h2o_update_select at the same len (append, attention over both
+ * tiers, H2O accumulate, re-select, demote; see those two entry points for
+ * the definitions). Results are bit-identical to the two calls; the H2O work
+ * runs inside the attention's merge launch when cap16 <= 4096, so the step
+ * takes two kernel launches instead of three.
+ * q, k_new, v_new, b, o, p16 as in mikv_decode_attn; recent, heavy and
+ * demoted_pos (optional) as in mikv_h2o_update_select.
+ * ws: mikv_decode_attn_workspace(dims, max_len) bytes.
+ * Errors: the union of both entry points' errors.
+ */
+mikv_status mikv_decode_step(const mikv_dims* dims, const mikv_cache* cache,
+                             int32_t len, int32_t recent, int32_t heavy,
+                             const uint16_t* q, const uint16_t* k_new,
+                             const uint16_t* v_new, const float* b, float* o,
+                             float* p16, int32_t* demoted_pos, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
  * CriticalKV two-stage selection per head ([gist CriticalKV] Algorithm 1;
  * theoretical framework: the output perturbation bound depends on the
  * attention weights and the value states projected by W_O).

@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     mikv_abi_version, mikv_status_str,
     mikv_balance_workspace, mikv_balance_prefill,
     mikv_quantize_tokens,
-    mikv_decode_attn_workspace, mikv_decode_attn,
+    mikv_decode_attn_workspace, mikv_decode_attn, mikv_decode_step,
     mikv_h2o_workspace, mikv_h2o_update_select,
     mikv_criticalkv_workspace, mikv_criticalkv_select,
 )

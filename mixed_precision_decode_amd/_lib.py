@@ -51,6 +51,8 @@ _SIGS = {
     "mikv_decode_attn_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
     "mikv_decode_attn": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mikv_decode_step": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _i32, _i32, _vp,
+                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mikv_h2o_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
     "mikv_h2o_update_select": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _i32, _i32,
                                          _vp, C.POINTER(MikvPrefillSrc), _vp, _vp, _sz, _vp]),
@@ -94,7 +96,12 @@ class Dims:
     capq: int
 
     def c(self) -> MikvDims:
-        return MikvDims(*(int(getattr(self, f.name)) for f in dataclasses.fields(self)))
+        key = tuple(int(getattr(self, f.name)) for f in dataclasses.fields(self))
+        cached = self.__dict__.get("_c")
+        if cached is None or cached[0] != key:
+            cached = (key, MikvDims(*key))
+            self.__dict__["_c"] = cached
+        return cached[1]
 
 
 def _ptr(t, dtype=None, shape=None, name="tensor", optional=False):
@@ -196,7 +203,9 @@ class Cache:
         self.posq = torch.full((n, g, cq), -1, dtype=torch.int32, device=device)
 
     def c(self) -> MikvCache:
-        return MikvCache(*(getattr(self, f).data_ptr() for f, _ in MikvCache._fields_))
+        if getattr(self, "_c", None) is None:
+            self._c = MikvCache(*(getattr(self, f).data_ptr() for f, _ in MikvCache._fields_))
+        return self._c
 
     NAMES = ("k16", "v16", "pos16", "acc16", "free16", "kq", "vq", "ksz", "vsz", "posq")
 
@@ -214,6 +223,18 @@ def mikv_decode_attn(dims: Dims, cache: Cache, length: int, q, k_new, v_new, b, 
         _ptr(q, "f16", (n, hq, d), "q"), _ptr(k_new, "f16", (n, hkv, d), "k_new"),
         _ptr(v_new, "f16", (n, hkv, d), "v_new"), _ptr(b, _f32t(), (n, hkv, d), "b"),
         _ptr(o, _f32t(), (n, hq, d), "o"), _ptr(p16, _f32t(), (n, hkv, dims.cap16), "p16"),
+        _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mikv_decode_step(dims: Dims, cache: Cache, length: int, recent: int, heavy: int, q, k_new, v_new,
+                     b, o, p16, ws, demoted_pos=None, stream=None):
+    n, hq, hkv, d = dims.batch, dims.hq, dims.hkv, dims.d
+    _check(lib().mikv_decode_step(
+        C.byref(dims.c()), C.byref(cache.c()), length, recent, heavy,
+        _ptr(q, "f16", (n, hq, d), "q"), _ptr(k_new, "f16", (n, hkv, d), "k_new"),
+        _ptr(v_new, "f16", (n, hkv, d), "v_new"), _ptr(b, _f32t(), (n, hkv, d), "b"),
+        _ptr(o, _f32t(), (n, hq, d), "o"), _ptr(p16, _f32t(), (n, hkv, dims.cap16), "p16"),
+        _ptr(demoted_pos, _i32t(), (n, hkv), "demoted_pos", optional=True),
         _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))
 
 

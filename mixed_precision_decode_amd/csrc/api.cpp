@@ -133,7 +133,54 @@ mikv_status mikv_decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t le
   a.k16 = c->k16; a.v16 = c->v16; a.pos16 = c->pos16; a.free16 = c->free16;
   a.kq = c->kq; a.vq = c->vq; a.ksz = c->ksz; a.vsz = c->vsz;
   a.o = o; a.p16 = p16; a.ws = ws;
+  a.fuse_h2o = false;
+  a.h2o = H2OView{};
   return from_hip(launch_decode_attn(a, pl, static_cast<hipStream_t>(stream)));
+}
+
+mikv_status mikv_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t len, int32_t recent,
+                             int32_t heavy, const uint16_t* q, const uint16_t* k_new,
+                             const uint16_t* v_new, const float* b, float* o, float* p16,
+                             int32_t* demoted_pos, void* ws, size_t ws_bytes, void* stream) {
+  mikv_status st = check_dims(m, true);
+  if (st != MIKV_OK) return st;
+  st = check_cache(c);
+  if (st != MIKV_OK) return st;
+  if (!q || !k_new || !v_new || !b || !o || !p16) return MIKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new)) return MIKV_ERR_SHAPE;
+  if (recent < 0 || heavy < 0 || heavy + recent != m->cap16 - 1) return MIKV_ERR_SHAPE;
+  const int nq = len - m->cap16;
+  if (nq < 0) return MIKV_ERR_SHAPE;
+  if (nq + 1 > m->capq) return MIKV_ERR_CAPACITY;  // the demotion adds one low-bit token
+  const DecodePlan pl = decode_plan(m->batch, m->hkv, m->d, m->bits, m->group, m->hq / m->hkv,
+                                    m->cap16, nq);
+  const size_t need = decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, pl);
+  if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
+  DecodeArgs a;
+  a.batch = m->batch; a.hq = m->hq; a.hkv = m->hkv; a.d = m->d; a.group = m->group;
+  a.bits = m->bits; a.cap16 = m->cap16; a.capq = m->capq; a.len = len;
+  a.q = q; a.k_new = k_new; a.v_new = v_new; a.b = b;
+  a.k16 = c->k16; a.v16 = c->v16; a.pos16 = c->pos16; a.free16 = c->free16;
+  a.kq = c->kq; a.vq = c->vq; a.ksz = c->ksz; a.vsz = c->vsz;
+  a.o = o; a.p16 = p16; a.ws = ws;
+  a.fuse_h2o = m->cap16 <= kFusedMaxCap16;
+  H2OView& v = a.h2o;
+  v.cap16 = m->cap16; v.capq = m->capq; v.len = len; v.recent = recent;
+  v.k16 = c->k16; v.v16 = c->v16; v.pos16 = c->pos16; v.acc16 = c->acc16; v.free16 = c->free16;
+  v.kq = c->kq; v.vq = c->vq;
+  v.ksz = reinterpret_cast<uint32_t*>(c->ksz);
+  v.vsz = reinterpret_cast<uint32_t*>(c->vsz);
+  v.posq = c->posq; v.demoted_pos = demoted_pos;
+  hipError_t e = launch_decode_attn(a, pl, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess || a.fuse_h2o) return from_hip(e);
+  // large FP16 tiers: the H2O step runs as its own launch
+  H2OArgs h = {};
+  h.batch = m->batch; h.hkv = m->hkv; h.d = m->d; h.group = m->group; h.bits = m->bits;
+  h.cap16 = m->cap16; h.capq = m->capq; h.len = len; h.recent = recent; h.heavy = heavy;
+  h.k16 = c->k16; h.v16 = c->v16; h.pos16 = c->pos16; h.acc16 = c->acc16; h.free16 = c->free16;
+  h.kq = c->kq; h.vq = c->vq; h.ksz = c->ksz; h.vsz = c->vsz; h.posq = c->posq;
+  h.p16 = p16; h.demoted_pos = demoted_pos;
+  return from_hip(launch_h2o_decode(h, static_cast<hipStream_t>(stream)));
 }
 
 // ---------------------------------------------------------------- H2O

@@ -28,6 +28,7 @@
 // Scores are in the log2 domain (q-hat is pre-multiplied by log2(e)/sqrt(d)).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "h2o_common.hpp"
 
 namespace mikv {
 
@@ -506,24 +507,29 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
 
 // One block per (sequence, kv head). All global loads of the block (split
 // statistics, the first kMergePF partial vectors of each output, the
-// FP16-tier scores) are issued before the first barrier so the kernel costs
-// about one memory round trip. Dynamic LDS: [rep][S] (max, sum) pairs, then
-// [rep] maxima and [rep] reciprocal sums.
+// FP16-tier scores and, when fused, the H2O state) are issued before the
+// first barrier, so the kernel costs about one memory round trip. Dynamic
+// LDS: [rep][S] (max, sum) pairs, then [rep] maxima and [rep] reciprocal sums.
+// FUSE: the block then applies the decode-step H2O update to its unit
+// (acc += p16, drop the worst candidate, demote it), which the stand-alone
+// H2O kernel would otherwise do in a third launch.
 constexpr int kMergePF = 8;
-constexpr int kMergeSlots = 4;  // FP16-tier slots per thread held in registers
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p, int RT) {
+constexpr int kMergeSlots = 16;  // FP16-tier slots per thread held in registers
+template <int D, int BITS, int NL, bool FUSE>
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p, int RT, H2OView hv) {
   extern __shared__ float2 sml[];
   const int unit = blockIdx.x;
   const int n = unit / p.hkv, g = unit % p.hkv;
   const int tid = threadIdx.x;
   const int S = p.S16 + p.Sq;
   const int rep = p.rep;
+  const int cap16 = p.cap16;
   float* sM = reinterpret_cast<float*>(sml + rep * S);
   float* sIL = sM + rep;
   const float2* __restrict__ pml = p.part_ml;
   const float* __restrict__ pov = p.part_o;
-  const float* __restrict__ sc = p.sc16 + static_cast<int64_t>(unit) * rep * p.cap16;
+  const float* __restrict__ sc = p.sc16 + static_cast<int64_t>(unit) * rep * cap16;
+  const int64_t base16 = static_cast<int64_t>(unit) * cap16;
   // (1) issue every load
   for (int i = tid; i < rep * S; i += kThreads) {
     const int hl = i / S, s = i % S;
@@ -536,13 +542,23 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   float pf[kMergePF];
 #pragma unroll
   for (int s = 0; s < kMergePF; ++s) pf[s] = (has0 && s < S) ? po0[static_cast<int64_t>(s) * RT * D] : 0.0f;
-  float sv[kMergeSlots];
-  const bool slots_in_regs = (rep == 1) && (p.cap16 <= kMergeSlots * kThreads);
-  if (slots_in_regs) {
+  const bool slots_in_regs = cap16 <= kMergeSlots * kThreads;
+  float sv[kMergeSlots], accv[kMergeSlots];
+  int posv[kMergeSlots];
+  if (slots_in_regs && rep == 1) {
 #pragma unroll
     for (int k = 0; k < kMergeSlots; ++k) {
       const int sl = tid + k * kThreads;
-      sv[k] = (sl < p.cap16) ? sc[sl] : 0.0f;
+      sv[k] = (sl < cap16) ? sc[sl] : 0.0f;
+    }
+  }
+  int fr = 0;
+  if constexpr (FUSE) {
+    fr = hv.free16[unit];
+#pragma unroll
+    for (int k = 0; k < kMergeSlots; ++k) {
+      const int sl = tid + k * kThreads;
+      if (sl < cap16) { accv[k] = hv.acc16[base16 + sl]; posv[k] = hv.pos16[base16 + sl]; }
     }
   }
   __syncthreads();
@@ -575,19 +591,33 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
     p.o[(static_cast<int64_t>(n) * p.hq + g * rep + hl) * D + c] = v * sIL[hl];
   }
   // (4) p16 = sum over the group's heads of the FP16-tier probabilities
-  float* __restrict__ p16 = p.p16 + static_cast<int64_t>(unit) * p.cap16;
+  float* __restrict__ p16 = p.p16 + base16;
+  auto prob = [&](int sl) {
+    float a = 0.0f;
+    for (int hl = 0; hl < rep; ++hl) a += fast_exp2(sc[hl * cap16 + sl] - sM[hl]) * sIL[hl];
+    return a;
+  };
   if (slots_in_regs) {
+    Worst w;
+    const int limit = hv.len - hv.recent;
 #pragma unroll
     for (int k = 0; k < kMergeSlots; ++k) {
       const int sl = tid + k * kThreads;
-      if (sl < p.cap16) p16[sl] = fast_exp2(sv[k] - sM[0]) * sIL[0];
+      if (sl < cap16) {
+        const float a = (rep == 1) ? fast_exp2(sv[k] - sM[0]) * sIL[0] : prob(sl);
+        p16[sl] = a;
+        if constexpr (FUSE) {
+          const float prev = (sl == fr) ? 0.0f : accv[k];
+          const int pos = (sl == fr) ? hv.len - 1 : posv[k];
+          const float v = prev + a;
+          hv.acc16[base16 + sl] = v;
+          if (pos < limit) w.consider(v, pos, sl);
+        }
+      }
     }
+    if constexpr (FUSE) h2o_select_demote<D, BITS, NL>(w, hv, unit, fr);
   } else {
-    for (int sl = tid; sl < p.cap16; sl += kThreads) {
-      float a = 0.0f;
-      for (int hl = 0; hl < rep; ++hl) a += fast_exp2(sc[hl * p.cap16 + sl] - sM[hl]) * sIL[hl];
-      p16[sl] = a;
-    }
+    for (int sl = tid; sl < cap16; sl += kThreads) p16[sl] = prob(sl);
   }
 }
 
@@ -679,7 +709,15 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = static_cast<size_t>(k.rep) * S * sizeof(float2) + 2 * k.rep * sizeof(float);
-  decode_merge_kernel<D><<<static_cast<unsigned>(units), kThreads, lds, stream>>>(k, RT);
+  const bool fuse = a.fuse_h2o && a.cap16 <= kFusedMaxCap16;
+  H2OView hv = a.h2o;
+  if (!a.fuse_h2o) hv.len = a.len, hv.recent = 0;
+#define MIKV_MERGE(NL_, F_) \
+  decode_merge_kernel<D, BITS, NL_, F_><<<static_cast<unsigned>(units), kThreads, lds, stream>>>(k, RT, hv)
+  if (!fuse) MIKV_MERGE(D / 16, false);
+  else if (a.group == D / 2) MIKV_MERGE(D / 16, true);
+  else MIKV_MERGE(D / 8, true);
+#undef MIKV_MERGE
   return hipGetLastError();
 }
 

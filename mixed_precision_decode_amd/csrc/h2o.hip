@@ -19,6 +19,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "topk.hpp"
+#include "h2o_common.hpp"
 
 #include <climits>
 
@@ -31,10 +32,6 @@ namespace mikv {
 constexpr int kH2OSlots = 16;
 template <int D, int BITS, int NL>
 __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
-  __shared__ float s_acc[4];
-  __shared__ int s_pos[4];
-  __shared__ int s_slot[4];
-  __shared__ int s_drop;
   const int unit = blockIdx.x;
   const int tid = threadIdx.x;
   const int64_t base16 = static_cast<int64_t>(unit) * a.cap16;
@@ -43,14 +40,12 @@ __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
   const int32_t* __restrict__ pos16 = a.pos16 + base16;
   const int fr = a.free16[unit];
   const int limit = a.len - a.recent;  // candidates: pos < limit
-  // worst candidate = smallest acc, latest position among equal acc
-  float wa = INFINITY;
-  int wp = -1, ws = -1;
+  Worst w;
   auto consider = [&](int s, float prev, float pp, int pos) {
     if (s == fr) { prev = 0.0f; pos = a.len - 1; }
     const float v = prev + pp;
     a.acc16[base16 + s] = v;
-    if (pos < limit && (v < wa || (v == wa && pos > wp))) { wa = v; wp = pos; ws = s; }
+    if (pos < limit) w.consider(v, pos, s);
   };
   if (a.cap16 <= kH2OSlots * 256) {
     float av[kH2OSlots], pv[kH2OSlots];
@@ -68,51 +63,14 @@ __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
   } else {
     for (int s = tid; s < a.cap16; s += 256) consider(s, accin[s], p16[s], pos16[s]);
   }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float oa = shfl_xor_f(wa, m);
-    const int op = __shfl_xor(wp, m);
-    const int os = __shfl_xor(ws, m);
-    if (os >= 0 && (ws < 0 || oa < wa || (oa == wa && op > wp))) { wa = oa; wp = op; ws = os; }
-  }
-  if (tid % kWave == 0) { s_acc[tid / kWave] = wa; s_pos[tid / kWave] = wp; s_slot[tid / kWave] = ws; }
-  __syncthreads();
-  if (tid == 0) {
-    float ba = s_acc[0]; int bp = s_pos[0], bs = s_slot[0];
-    for (int w = 1; w < 4; ++w) {
-      const int os = s_slot[w];
-      if (os >= 0 && (bs < 0 || s_acc[w] < ba || (s_acc[w] == ba && s_pos[w] > bp))) {
-        ba = s_acc[w]; bp = s_pos[w]; bs = os;
-      }
-    }
-    s_drop = bs;
-  }
-  __syncthreads();
-  const int drop = s_drop;
-  if (drop < 0) return;  // unreachable when heavy + recent == cap16 - 1
-  constexpr int LPR = D / 8;
-  constexpr int CB = D * BITS / 8;
-  constexpr int GPT = D / (8 * NL);
-  const int64_t qslot = static_cast<int64_t>(unit) * a.capq + (a.len - a.cap16);
-  // rows: threads [0, LPR) quantize the key, [LPR, 2*LPR) the value
-  if (tid < 2 * LPR) {
-    const int lane = tid % LPR;
-    const bool is_v = tid >= LPR;
-    const uint16_t* src = (is_v ? a.v16 : a.k16) + (base16 + drop) * D + lane * 8;
-    float x[8];
-    load8(src, x);
-    uint32_t szw;
-    const uint32_t packed = quantize8<BITS, NL>(x, &szw);
-    store_codes8<BITS>((is_v ? a.vq : a.kq) + qslot * CB, lane, packed);
-    if (lane % NL == 0)
-      reinterpret_cast<uint32_t*>(is_v ? a.vsz : a.ksz)[qslot * GPT + lane / NL] = szw;
-  }
-  if (tid == 0) {
-    const int pos = (drop == fr) ? a.len - 1 : a.pos16[base16 + drop];
-    a.posq[qslot] = pos;
-    a.free16[unit] = drop;
-    if (a.demoted_pos) a.demoted_pos[unit] = pos;
-  }
+  H2OView v;
+  v.cap16 = a.cap16; v.capq = a.capq; v.len = a.len; v.recent = a.recent;
+  v.k16 = a.k16; v.v16 = a.v16; v.pos16 = a.pos16; v.acc16 = a.acc16; v.free16 = a.free16;
+  v.kq = a.kq; v.vq = a.vq;
+  v.ksz = reinterpret_cast<uint32_t*>(a.ksz);
+  v.vsz = reinterpret_cast<uint32_t*>(a.vsz);
+  v.posq = a.posq; v.demoted_pos = a.demoted_pos;
+  h2o_select_demote<D, BITS, NL>(w, v, unit, fr);
 }
 
 // ------------------------------------------------------------------ prefill

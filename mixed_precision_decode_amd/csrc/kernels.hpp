@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "h2o_common.hpp"
+
 namespace mikv {
 
 hipError_t launch_quantize_rows(const uint16_t* x, const int32_t* rows, int64_t n_rows, int d,
@@ -45,8 +47,14 @@ struct DecodeArgs {
   float* o;
   float* p16;
   void* ws;
+  // fused decode step: the merge kernel also runs the H2O update, re-select
+  // and demotion (fuse_h2o = true; h2o holds the cache views it writes)
+  bool fuse_h2o;
+  H2OView h2o;
 };
 hipError_t launch_decode_attn(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+// largest FP16 tier the fused merge handles (slots held in registers)
+constexpr int kFusedMaxCap16 = 16 * 256;
 
 struct H2OArgs {
   int batch, hkv, d, group, bits, cap16, capq, len, recent, heavy;

@@ -29,7 +29,7 @@ def _header_functions():
 
 def test_exports_every_declared_function(lib):
     names = _header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L._SIGS)
@@ -74,6 +74,21 @@ def test_decode_attn_validation(lib):
     mis = _cache()
     mis.k16 = FAKE + 2
     assert call(good, cache=mis) == L.MIKV_ERR_SHAPE            # 16-byte alignment
+
+
+def test_decode_step_validation(lib):
+    c = _cache()
+    good = _dims()
+    need = lib.mikv_decode_attn_workspace(C.byref(good.c()), 80)
+    call = lambda dims=good, length=50, recent=4, heavy=6, ws_bytes=need, q=FAKE: lib.mikv_decode_step(
+        C.byref(dims.c()), C.byref(c), length, recent, heavy, q, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+        FAKE, ws_bytes, None)
+    assert call(q=None) == L.MIKV_ERR_NULL
+    assert call(recent=5) == L.MIKV_ERR_SHAPE
+    assert call(length=10) == L.MIKV_ERR_SHAPE
+    assert call(length=111) == L.MIKV_ERR_CAPACITY     # demotion would need slot 100
+    assert call(ws_bytes=16) == L.MIKV_ERR_WORKSPACE
+    assert call(_dims(bits=8)) == L.MIKV_ERR_UNSUPPORTED
 
 
 def test_h2o_validation(lib):

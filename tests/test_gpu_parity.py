@@ -285,3 +285,81 @@ def test_criticalkv_full_size():
     print("criticalkv full size", flush=True)
     A, V, W = S.criticalkv_inputs(cfg, 1004)
     _ckv_check(A, V, W, cfg.budget, cfg.alpha, sample=192)
+
+
+# ---------------------------------------------------------------- graph replay
+def test_graph_replay_matches_eager():
+    """Decode steps captured as HIP graphs (one graph per step, as the
+    benchmark replays them) give bit-identical caches and outputs to eager
+    launches, with eager work and synchronisations between the replays."""
+    cfg = S.CONFIGS["tiny"].scaled(hq=4, hkv=2)
+    outs = []
+    for use_graph in (False, True):
+        dims, cache, b, _ = _prefill_gpu(cfg, 21, True)
+        o = torch.zeros((cfg.batch, cfg.hq, cfg.d), dtype=torch.float32, device="cuda")
+        p16 = torch.zeros((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + 6), dtype=torch.uint8, device="cuda")
+        inputs = [tuple(dev(x) for x in S.decode_tensors(cfg, 21, s)) for s in range(6)]
+        graphs = []
+        if use_graph:
+            for s in range(6):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    L.mikv_decode_attn(dims, cache, cfg.T + s + 1, *inputs[s], b, o, p16, ws)
+                    L.mikv_h2o_update_select(dims, cache, cfg.T + s + 1, cfg.recent, cfg.H, p16=p16)
+                graphs.append(g)
+        trace = []
+        for s in range(6):
+            if use_graph:
+                graphs[s].replay()
+                torch.ones(1 << 20, device="cuda").sum()   # eager work between replays
+            else:
+                L.mikv_decode_attn(dims, cache, cfg.T + s + 1, *inputs[s], b, o, p16, ws)
+                L.mikv_h2o_update_select(dims, cache, cfg.T + s + 1, cfg.recent, cfg.H, p16=p16)
+            torch.cuda.synchronize()
+            trace.append((host(o).copy(), host(p16).copy(), cache.to_numpy()))
+        outs.append(trace)
+    for (o1, p1, c1), (o2, p2, c2) in zip(*outs):
+        assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+        assert np.array_equal(p1.view(np.uint32), p2.view(np.uint32))
+        for key in L.Cache.NAMES:
+            assert np.array_equal(np.asarray(c1[key]).view(np.uint8), np.asarray(c2[key]).view(np.uint8)), key
+
+
+# ---------------------------------------------------------------- fused decode step
+@pytest.mark.parametrize("name,over,steps", [
+    ("tiny", {}, 8), ("tiny", dict(hq=8, hkv=2, bits=2), 6), ("tiny", dict(recent=0), 4),
+    ("tiny", dict(pct=0, recent=0), 4), ("tiny", dict(group=64), 4),
+    ("gqa_throughput", dict(batch=2, T=900), 3),
+    ("llama3_8b_32k", dict(hq=8, hkv=2, T=20000, pct=25), 2),    # FP16 tier > 4096 slots: unfused path
+])
+def test_decode_step_matches_separate_calls(name, over, steps):
+    """mikv_decode_step is bit-identical to mikv_decode_attn followed by
+    mikv_h2o_update_select (decode mode)."""
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"decode_step {name} {over}", flush=True)
+    runs = []
+    for fused in (False, True):
+        dims, cache, b, _ = _prefill_gpu(cfg, 31, True)
+        o = torch.zeros((cfg.batch, cfg.hq, cfg.d), dtype=torch.float32, device="cuda")
+        p16 = torch.zeros((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
+        dpos = torch.zeros((cfg.batch, cfg.hkv), dtype=torch.int32, device="cuda")
+        ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + steps), dtype=torch.uint8, device="cuda")
+        trace = []
+        for s in range(steps):
+            N = cfg.T + s + 1
+            qd, kd, vd = (dev(x) for x in S.decode_tensors(cfg, 31, s))
+            if fused:
+                L.mikv_decode_step(dims, cache, N, cfg.recent, cfg.H, qd, kd, vd, b, o, p16, ws,
+                                   demoted_pos=dpos)
+            else:
+                L.mikv_decode_attn(dims, cache, N, qd, kd, vd, b, o, p16, ws)
+                L.mikv_h2o_update_select(dims, cache, N, cfg.recent, cfg.H, p16=p16, demoted_pos=dpos)
+            trace.append((host(o).copy(), host(p16).copy(), host(dpos).copy(), cache.to_numpy()))
+        runs.append(trace)
+    for (o1, p1, d1, c1), (o2, p2, d2, c2) in zip(*runs):
+        assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+        assert np.array_equal(p1.view(np.uint32), p2.view(np.uint32))
+        assert np.array_equal(d1, d2)
+        for key in L.Cache.NAMES:
+            assert np.array_equal(np.asarray(c1[key]).view(np.uint8), np.asarray(c2[key]).view(np.uint8)), key
