@@ -505,20 +505,24 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
   }
 }
 
-// One block per (sequence, kv head). All global loads of the block (split
-// statistics, the first kMergePF partial vectors of each output, the
-// FP16-tier scores and, when fused, the H2O state) are issued before the
-// first barrier, so the kernel costs about one memory round trip. Dynamic
-// LDS: [rep][S] (max, sum) pairs, then [rep] maxima and [rep] reciprocal sums.
-// FUSE: the block then applies the decode-step H2O update to its unit
-// (acc += p16, drop the worst candidate, demote it), which the stand-alone
-// H2O kernel would otherwise do in a third launch.
-constexpr int kMergePF = 8;
+// Grid: (unit, output chunk). Block y of unit x combines the split
+// partials of kMergeOut outputs (head, channel) of the unit, kMergeTPO threads
+// per output, each summing a strided subset of the splits, so a unit with
+// many splits spreads its partials over many blocks and loads. Block 0 of
+// the unit also turns the FP16-tier scores into p16 and, when FUSE, applies
+// the decode-step H2O update (acc += p16, drop the worst candidate, demote
+// it), which the stand-alone H2O kernel would otherwise do in a third launch.
+// Dynamic LDS: [rep][S] (max, sum) pairs, then [rep] maxima and [rep]
+// reciprocal sums.
+constexpr int kMergeOut = 64;
+constexpr int kMergeTPO = kThreads / kMergeOut;
 constexpr int kMergeSlots = 16;  // FP16-tier slots per thread held in registers
 template <int D, int BITS, int NL, bool FUSE>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p, int RT, H2OView hv) {
   extern __shared__ float2 sml[];
+  __shared__ float red[kThreads];
   const int unit = blockIdx.x;
+  const int chunk = blockIdx.y;
   const int n = unit / p.hkv, g = unit % p.hkv;
   const int tid = threadIdx.x;
   const int S = p.S16 + p.Sq;
@@ -530,40 +534,51 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   const float* __restrict__ pov = p.part_o;
   const float* __restrict__ sc = p.sc16 + static_cast<int64_t>(unit) * rep * cap16;
   const int64_t base16 = static_cast<int64_t>(unit) * cap16;
+  // heads this block needs (statistics): its outputs' heads, or all for p16
+  const int out0 = chunk * kMergeOut;
+  const int h_lo = (chunk == 0) ? 0 : out0 / D;
+  const int h_hi = (chunk == 0) ? rep : min(rep, (out0 + kMergeOut - 1) / D + 1);
   // (1) issue every load
-  for (int i = tid; i < rep * S; i += kThreads) {
+  for (int i = h_lo * S + tid; i < h_hi * S; i += kThreads) {
     const int hl = i / S, s = i % S;
     sml[i] = pml[(static_cast<int64_t>((unit * p.tiles + hl / RT) * S) + s) * RT + hl % RT];
   }
-  const int i0 = tid;  // first output (head hl0, channel c0) of this thread
-  const bool has0 = i0 < rep * D;
-  const int hl0 = i0 / D, c0 = i0 % D;
-  const float* po0 = pov + (static_cast<int64_t>((unit * p.tiles + hl0 / RT) * S) * RT + hl0 % RT) * D + c0;
-  float pf[kMergePF];
+  const int oi = out0 + tid % kMergeOut;  // this thread's output
+  const int sub = tid / kMergeOut;        // its subset of splits: s = sub, sub + TPO, ...
+  const bool has_out = oi < rep * D;
+  const int ohl = oi / D, oc = oi % D;
+  const float* po = pov + (static_cast<int64_t>((unit * p.tiles + ohl / RT) * S) * RT + ohl % RT) * D + oc;
+  constexpr int PF = 8;
+  float pf[PF];
 #pragma unroll
-  for (int s = 0; s < kMergePF; ++s) pf[s] = (has0 && s < S) ? po0[static_cast<int64_t>(s) * RT * D] : 0.0f;
+  for (int k = 0; k < PF; ++k) {
+    const int s = sub + k * kMergeTPO;
+    pf[k] = (has_out && s < S) ? po[static_cast<int64_t>(s) * RT * D] : 0.0f;
+  }
   const bool slots_in_regs = cap16 <= kMergeSlots * kThreads;
   float sv[kMergeSlots], accv[kMergeSlots];
   int posv[kMergeSlots];
-  if (slots_in_regs && rep == 1) {
-#pragma unroll
-    for (int k = 0; k < kMergeSlots; ++k) {
-      const int sl = tid + k * kThreads;
-      sv[k] = (sl < cap16) ? sc[sl] : 0.0f;
-    }
-  }
   int fr = 0;
-  if constexpr (FUSE) {
-    fr = hv.free16[unit];
+  if (chunk == 0) {
+    if (slots_in_regs && rep == 1) {
 #pragma unroll
-    for (int k = 0; k < kMergeSlots; ++k) {
-      const int sl = tid + k * kThreads;
-      if (sl < cap16) { accv[k] = hv.acc16[base16 + sl]; posv[k] = hv.pos16[base16 + sl]; }
+      for (int k = 0; k < kMergeSlots; ++k) {
+        const int sl = tid + k * kThreads;
+        sv[k] = (sl < cap16) ? sc[sl] : 0.0f;
+      }
+    }
+    if constexpr (FUSE) {
+      fr = hv.free16[unit];
+#pragma unroll
+      for (int k = 0; k < kMergeSlots; ++k) {
+        const int sl = tid + k * kThreads;
+        if (sl < cap16) { accv[k] = hv.acc16[base16 + sl]; posv[k] = hv.pos16[base16 + sl]; }
+      }
     }
   }
   __syncthreads();
   // (2) per head: maximum and reciprocal normaliser
-  for (int hl = tid; hl < rep; hl += kThreads) {
+  for (int hl = h_lo + tid; hl < h_hi; hl += kThreads) {
     float M = -INFINITY;
     for (int s = 0; s < S; ++s) M = fmaxf(M, sml[hl * S + s].x);
     float L = 0.0f;
@@ -572,24 +587,32 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
     sIL[hl] = 1.0f / L;
   }
   __syncthreads();
-  // (3) outputs
-  for (int i = tid; i < rep * D; i += kThreads) {
-    const int hl = i / D, c = i % D;
-    const float M = sM[hl];
-    const float2* ml = sml + hl * S;
+  // (3) outputs: each thread sums its subset of splits, then the kMergeTPO
+  // threads of an output combine through LDS
+  {
     float v = 0.0f;
-    int s = 0;
-    if (i == i0) {
+    if (has_out) {
+      const float M = sM[ohl];
+      const float2* ml = sml + ohl * S;
 #pragma unroll
-      for (int k = 0; k < kMergePF; ++k)
-        if (k < S) v += pf[k] * fast_exp2(ml[k].x - M);
-      s = kMergePF;
-    }
-    const float* po = pov + (static_cast<int64_t>((unit * p.tiles + hl / RT) * S) * RT + hl % RT) * D + c;
+      for (int k = 0; k < PF; ++k) {
+        const int s = sub + k * kMergeTPO;
+        if (s < S) v += pf[k] * fast_exp2(ml[s].x - M);
+      }
 #pragma unroll 4
-    for (; s < S; ++s) v += po[static_cast<int64_t>(s) * RT * D] * fast_exp2(ml[s].x - M);
-    p.o[(static_cast<int64_t>(n) * p.hq + g * rep + hl) * D + c] = v * sIL[hl];
+      for (int s = sub + PF * kMergeTPO; s < S; s += kMergeTPO)
+        v += po[static_cast<int64_t>(s) * RT * D] * fast_exp2(ml[s].x - M);
+    }
+    red[tid] = v;
+    __syncthreads();
+    if (tid < kMergeOut && has_out) {
+      float t = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kMergeTPO; ++k) t += red[tid + k * kMergeOut];
+      p.o[(static_cast<int64_t>(n) * p.hq + g * rep + ohl) * D + oc] = t * sIL[ohl];
+    }
   }
+  if (chunk != 0) return;
   // (4) p16 = sum over the group's heads of the FP16-tier probabilities
   float* __restrict__ p16 = p.p16 + base16;
   auto prob = [&](int sl) {
@@ -712,8 +735,9 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   const bool fuse = a.fuse_h2o && a.cap16 <= kFusedMaxCap16;
   H2OView hv = a.h2o;
   if (!a.fuse_h2o) hv.len = a.len, hv.recent = 0;
+  const dim3 mgrid(static_cast<unsigned>(units), static_cast<unsigned>((k.rep * D + kMergeOut - 1) / kMergeOut));
 #define MIKV_MERGE(NL_, F_) \
-  decode_merge_kernel<D, BITS, NL_, F_><<<static_cast<unsigned>(units), kThreads, lds, stream>>>(k, RT, hv)
+  decode_merge_kernel<D, BITS, NL_, F_><<<mgrid, kThreads, lds, stream>>>(k, RT, hv)
   if (!fuse) MIKV_MERGE(D / 16, false);
   else if (a.group == D / 2) MIKV_MERGE(D / 16, true);
   else MIKV_MERGE(D / 8, true);
