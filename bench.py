@@ -35,6 +35,38 @@ if ROOT not in sys.path:
 
 METRIC = "mixed-precision decode attn KV-tokens/s + achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBPS = 8000.0
+# sources compiled into the decode-attention kernels; the HBM traffic recorded
+# under profiles/ is reported only while their hash matches the recorded one
+KERNEL_SOURCES = ("mixed_precision_decode_amd/csrc/decode_attn.hip",
+                  "mixed_precision_decode_amd/csrc/common.hpp",
+                  "mixed_precision_decode_amd/csrc/kernels.hpp",
+                  "mixed_precision_decode_amd/csrc/h2o_common.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attn_hbm_traffic.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per decode-attention call (split + merge kernels) from the
+    FETCH_SIZE / WRITE_SIZE counter runs recorded under profiles/, each
+    scaled by the reading of a plain 1 GiB copy; None when the kernels
+    changed since the counters were taken or the workload was not profiled."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else float(w["traffic_bytes_per_call"])
 
 
 def attn_bytes(cfg, N):
@@ -286,7 +318,8 @@ def main():
                    "important_pct": cfg.pct, "recent": cfg.recent, "group": cfg.G,
                    "cache_flush_per_step": args.flush, "step_launch": "hip_graph" if args.graph else "eager"},
         "roofline": {"bound": "hbm", "achieved": a_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": a_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": a_gbps / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic(cfg.name) if not args.set else None,
                      "launches_timed": KA,
                      "kernel": "decode_split_kernel + decode_merge_kernel (one mikv_decode_attn call)", "kernel_us": float(attn_ms.mean() * 1e3),
                      "bytes_per_launch": float(abytes.mean())},
