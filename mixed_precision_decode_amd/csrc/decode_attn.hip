@@ -560,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   int posv[kMergeSlots];
   int fr = 0;
   if (chunk == 0) {
-    if (slots_in_regs && rep == 1) {
+    if (slots_in_regs) {  // head 0's scores (the only head when rep == 1)
 #pragma unroll
       for (int k = 0; k < kMergeSlots; ++k) {
         const int sl = tid + k * kThreads;
@@ -621,13 +621,27 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
     return a;
   };
   if (slots_in_regs) {
+    // all loads of a head are issued together, before any store
+    float pa[kMergeSlots];
+#pragma unroll
+    for (int k = 0; k < kMergeSlots; ++k) pa[k] = fast_exp2(sv[k] - sM[0]) * sIL[0];
+    for (int hl = 1; hl < rep; ++hl) {
+#pragma unroll
+      for (int k = 0; k < kMergeSlots; ++k) {
+        const int sl = tid + k * kThreads;
+        sv[k] = (sl < cap16) ? sc[hl * cap16 + sl] : 0.0f;
+      }
+      const float M = sM[hl], IL = sIL[hl];
+#pragma unroll
+      for (int k = 0; k < kMergeSlots; ++k) pa[k] += fast_exp2(sv[k] - M) * IL;
+    }
     Worst w;
     const int limit = hv.len - hv.recent;
 #pragma unroll
     for (int k = 0; k < kMergeSlots; ++k) {
       const int sl = tid + k * kThreads;
       if (sl < cap16) {
-        const float a = (rep == 1) ? fast_exp2(sv[k] - sM[0]) * sIL[0] : prob(sl);
+        const float a = pa[k];
         p16[sl] = a;
         if constexpr (FUSE) {
           const float prev = (sl == fr) ? 0.0f : accv[k];
