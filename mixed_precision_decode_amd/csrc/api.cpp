@@ -31,6 +31,10 @@ mikv_status check_dims(const mikv_dims* m, bool need_tiers) {
     if (m->bits != 2 && m->bits != 4) return MIKV_ERR_UNSUPPORTED;
     if (!supported_dims(m->d, m->group, m->bits)) return MIKV_ERR_UNSUPPORTED;
     if (m->cap16 < 1 || m->capq < 0) return MIKV_ERR_SHAPE;
+    // the decode kernels address one (sequence, kv head) tier with 32-bit byte offsets
+    if (static_cast<int64_t>(m->capq) * m->d * m->bits / 8 >= (int64_t{1} << 31) ||
+        static_cast<int64_t>(m->cap16) * m->d * 2 >= (int64_t{1} << 31))
+      return MIKV_ERR_SHAPE;
   }
   return MIKV_OK;
 }

@@ -26,6 +26,8 @@
 //                 partials of every query head of the group and turns the
 //                 FP16-tier scores into p16 (summed over the group).
 // Scores are in the log2 domain (q-hat is pre-multiplied by log2(e)/sqrt(d)).
+#include <cfloat>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "h2o_common.hpp"
@@ -37,7 +39,7 @@ constexpr int kThreads = 256;
 #define MIKV_TPT16 4
 #endif
 #ifndef MIKV_TPTQ
-#define MIKV_TPTQ 4
+#define MIKV_TPTQ 2
 #endif
 #ifndef MIKV_BLOCKS_PER_CU
 #define MIKV_BLOCKS_PER_CU 4
@@ -47,9 +49,6 @@ constexpr int kTPTQ = MIKV_TPTQ;    // low-bit tokens per thread per batch
 constexpr int kCUs = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// lanes per low-bit token: 8 (16 or 8 channels per lane), never fewer than
-// 4 bytes of codes per lane
-constexpr int lptq_for(int d, int bits) { return (d * bits / 32) < 8 ? (d * bits / 32) : 8; }
 
 struct DecodeK {
   int hq, hkv, rep, cap16, capq, nq, len, group;
@@ -234,6 +233,263 @@ __device__ __forceinline__ void load_qhat(const DecodeK& p, int n, int g, int ti
   }
 }
 
+// ---------------------------------------------------------------------------
+// Low-bit tier.
+//
+// Buffer loads through a per-block resource that spans exactly the block's
+// token range [t0, t1): the lane offset of a token is a 32-bit byte offset
+// from t0, so no 64-bit address arithmetic runs per load, and a load past t1
+// returns zeros without touching memory (scale 0 and zero 0, so such a token
+// adds nothing once its score is masked). The prefetch of the batch after the
+// last one is therefore issued unconditionally, which keeps the loop free of
+// branches around loads.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kBufNT = 2;  // cache policy bit: nontemporal
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  // dword 3 of a raw (stride 0) gfx9 buffer resource: 32-bit data format
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+template <int NW>
+__device__ __forceinline__ Words<NW> bload(Rsrc r, uint32_t off) {
+  Words<NW> o;
+  if constexpr (NW == 4) {
+    const auto t = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kBufNT);
+    o.w[0] = t[0]; o.w[1] = t[1]; o.w[2] = t[2]; o.w[3] = t[3];
+  } else if constexpr (NW == 2) {
+    const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, kBufNT);
+    o.w[0] = t[0]; o.w[1] = t[1];
+  } else {
+    o.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, kBufNT);
+  }
+  return o;
+}
+__device__ __forceinline__ uint32_t bload1(Rsrc r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, kBufNT);
+}
+
+// fp16 pairs (1024 + code_a, 1024 + code_b) from one word of packed codes:
+// each code is isolated in a byte, and v_perm puts it under a 0x64 byte, the
+// fp16 1024 + code exactly. Pair k of the word's CPW channels covers:
+//   INT4 (channels at bits 4c): k = 0,1 even channels (4k, 4k+2), k = 2,3 odd
+//        channels (4(k-2)+1, 4(k-2)+3);
+//   INT2 (channels at bits 2c): pair 2m+q holds (8q+m, 8q+4+m).
+template <int BITS>
+struct MagicPairs {
+  static constexpr int kPairs = (BITS == 4) ? 4 : 8;
+  uint32_t h[kPairs];
+  // word channel of half e (0 = low) of pair k
+  static constexpr int chan(int k, int e) {
+    return (BITS == 4) ? ((k < 2) ? 4 * k + 2 * e : 4 * (k - 2) + 2 * e + 1) : 8 * ((k % 2)) + 4 * e + k / 2;
+  }
+  __device__ __forceinline__ MagicPairs(uint32_t w, uint32_t magic) {
+    constexpr uint32_t kLo = 0x04010400u, kHi = 0x04030402u;  // bytes (0, 1) / (2, 3) under 0x64
+    if constexpr (BITS == 4) {
+      const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+      h[0] = __builtin_amdgcn_perm(magic, lo, kLo);
+      h[1] = __builtin_amdgcn_perm(magic, lo, kHi);
+      h[2] = __builtin_amdgcn_perm(magic, hi, kLo);
+      h[3] = __builtin_amdgcn_perm(magic, hi, kHi);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t b = (w >> (2 * m)) & 0x03030303u;  // byte j = channel 4j + m
+        h[2 * m] = __builtin_amdgcn_perm(magic, b, kLo);
+        h[2 * m + 1] = __builtin_amdgcn_perm(magic, b, kHi);
+      }
+    }
+  }
+};
+
+// channels per lane on the low-bit tier: 32 for single-head tiles (keys by
+// integer dot products, so only the accumulators scale with it), 16 when the
+// float q-hat of 2-4 heads is held too
+constexpr int lowbit_cpl(int d, int rt) { return (rt == 1 ? 32 : 16) < d ? (rt == 1 ? 32 : 16) : d; }
+
+template <int D, int BITS, int RT>
+__device__ __forceinline__ void lowbit_split(const DecodeK& p, int unit, int n, int g, int tile, int split,
+                                             const float* bvec, float* red, float (*sm)[RT], float* sM,
+                                             float* po, float2* pml) {
+  constexpr int CPL = lowbit_cpl(D, RT), LPT = D / CPL, SLOTS = kThreads / LPT, TPT = kTPTQ;
+  constexpr int BATCH = SLOTS * TPT;
+  constexpr int NB = CPL * BITS / 8, NW = NB / 4;  // code bytes / words per lane and token
+  constexpr int CB = D * BITS / 8;                 // code bytes per token
+  constexpr int CPW = 32 / BITS;                   // channels per code word
+  constexpr bool kIntDot = (RT == 1);
+  static_assert(NB % 4 == 0 && NW >= 1 && NW <= 4, "lane code slice must be 1, 2 or 4 words");
+  const int tid = threadIdx.x;
+  const int lane = tid % LPT, tslot = tid / LPT, c0 = lane * CPL;
+  const int gpt = D / p.group;
+  const int gi = c0 / p.group;
+  const int t0 = (split - p.S16) * p.Cq;
+  const int t1 = min(p.nq, t0 + p.Cq);
+  const int nt = max(t1 - t0, 0);  // tokens of this block (>= 1 for every planned split)
+  const int64_t ub = static_cast<int64_t>(unit) * p.capq + t0;
+  const uint32_t rbytes = static_cast<uint32_t>(nt) * CB;
+  const uint32_t sbytes = static_cast<uint32_t>(nt) * gpt * 4;
+  const Rsrc rk = make_rsrc(p.kq + ub * CB, rbytes);
+  const Rsrc rv = make_rsrc(p.vq + ub * CB, rbytes);
+  const Rsrc rks = make_rsrc(p.ksz + ub * gpt, sbytes);
+  const Rsrc rvs = make_rsrc(p.vsz + ub * gpt, sbytes);
+  // byte offsets of this lane's slice of token 0 of its slot
+  const uint32_t cof = static_cast<uint32_t>(tslot * CB + lane * NB);
+  const uint32_t sof = static_cast<uint32_t>((tslot * gpt + gi) * 4);
+  struct Regs { Words<NW> k[TPT], v[TPT]; uint32_t ks[TPT], vs[TPT]; };
+  // base: first token of the batch, relative to t0
+  auto load = [&](int base, Regs& R) {
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const uint32_t t = static_cast<uint32_t>(base + j * SLOTS);
+      R.k[j] = bload<NW>(rk, cof + t * CB);
+      R.ks[j] = bload1(rks, sof + t * gpt * 4);
+      R.v[j] = bload<NW>(rv, cof + t * CB);
+      R.vs[j] = bload1(rvs, sof + t * gpt * 4);
+    }
+  };
+  Regs A, B;
+  load(0, A);
+  float qh[RT][CPL];
+  load_qhat<D, RT, CPL>(p, n, g, tile, c0, bvec, qh);
+  float qsum[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    qsum[r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) qsum[r] += qh[r][i];
+  }
+  // Integer form of q-hat (single head): q_int = rint(q-hat * 2^F) with F
+  // chosen per lane so |q_int| < 2^22, biased by 2^23 into [0, 2^24) and
+  // cut into six 4-bit digits laid out like the code nibbles. Then
+  //   sum_c q_int[c]*code[c] = sum_d 16^d dot8(codes, digit_d)
+  //                            - 2^23 * dot8(codes, 0x11111111),
+  // exact in 32-bit integers (two's-complement wraparound cancels the bias).
+  constexpr int NQW = CPL / 8;  // nibble words (8 channels each) per lane
+  uint32_t qd[6][kIntDot ? NQW : 1];
+  float qunit = 1.0f;
+  if constexpr (kIntDot) {
+    // |sum_c q_int*code| <= CPL * (2^BITS - 1) * 2^22 must fit a signed 32-bit
+    // integer; the digit sums themselves may wrap, the result is taken mod 2^32
+    static_assert(static_cast<long long>(CPL) * ((1 << BITS) - 1) * (1ll << 22) < (1ll << 31),
+                  "the lane's dot product must fit 32 bits");
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) mx = fmaxf(mx, fabsf(qh[0][i]));
+    int e = 0;
+    if (mx > 0.0f) (void)frexpf(mx, &e);
+    const int F = 22 - e;
+    qunit = ldexpf(1.0f, -F);
+#pragma unroll
+    for (int d = 0; d < 6; ++d)
+#pragma unroll
+      for (int i = 0; i < NQW; ++i) qd[d][i] = 0;
+#pragma unroll
+    for (int i = 0; i < NQW; ++i) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        // channel of nibble k in nibble word i
+        int ch;
+        if constexpr (BITS == 4) ch = 8 * i + k;
+        else ch = 16 * (i / 2) + 2 * k + (i % 2);
+        const int qi = static_cast<int>(rintf(ldexpf(qh[0][ch], F)));
+        const uint32_t qb = static_cast<uint32_t>(qi + (1 << 23));
+#pragma unroll
+        for (int d = 0; d < 6; ++d) qd[d][i] |= ((qb >> (4 * d)) & 0xFu) << (4 * k);
+      }
+    }
+  }
+  Acc<RT, CPL> st;
+  st.init();
+  const uint32_t magic = opaque(0x64646464u);  // kept in a register for v_perm
+  // one batch: TPT tokens per thread, token j of the slot at base + j*SLOTS
+  auto step = [&](const Regs& R, int base) {
+    float sc[TPT][RT];
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const bool valid = base + j * SLOTS + tslot < nt;
+      const float s = lo_h(R.ks[j]), z = hi_h(R.ks[j]);
+      if constexpr (kIntDot) {
+        uint32_t acc[6] = {0u, 0u, 0u, 0u, 0u, 0u}, csum = 0u;
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) {
+          uint32_t x;
+          if constexpr (BITS == 4) x = R.k[j].w[i];
+          else x = (i % 2 == 0) ? (R.k[j].w[i / 2] & 0x33333333u) : ((R.k[j].w[i / 2] >> 2) & 0x33333333u);
+#pragma unroll
+          for (int d = 0; d < 6; ++d) acc[d] = __builtin_amdgcn_udot8(x, qd[d][i], acc[d], false);
+          csum = __builtin_amdgcn_udot8(x, 0x11111111u, csum, false);
+        }
+        const uint32_t u = acc[0] + (acc[1] << 4) + (acc[2] << 8) + (acc[3] << 12) +
+                           (acc[4] << 16) + (acc[5] << 20);
+        const int32_t rdot = static_cast<int32_t>(u - (csum << 23));
+        const float dot = static_cast<float>(rdot) * qunit;
+        const float v = group_sum<LPT>(s * dot + z * qsum[0]);
+        sc[j][0] = valid ? v : -INFINITY;
+      } else {
+        float cf[CPL];
+        unpack_codes<BITS, CPL>(R.k[j].w, cf);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          float dot = 0.0f;
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) dot += qh[r][i] * cf[i];
+          const float v = group_sum<LPT>(s * dot + z * qsum[r]);
+          sc[j][r] = valid ? v : -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      float bm = sc[0][r];
+#pragma unroll
+      for (int j = 1; j < TPT; ++j) bm = fmaxf(bm, sc[j][r]);
+      st.rebase(r, bm);
+    }
+    float mref[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) mref[r] = fmaxf(st.m[r], -FLT_MAX);  // exp2(-inf - mref) = 0
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const float s = lo_h(R.vs[j]), z = hi_h(R.vs[j]);
+      // value codes as fp16 1024 + code: a += w * (1024 + code), and the
+      // 1024 * w it adds is taken back out of the zero-point sum z
+      float w[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float pr = fast_exp2(sc[j][r] - mref[r]);
+        st.l[r] += pr;
+        w[r] = pr * s;
+        st.z[r] += pr * z;
+        st.z[r] -= 1024.0f * w[r];
+      }
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const MagicPairs<BITS> mp(R.v[j].w[i], magic);
+#pragma unroll
+        for (int k = 0; k < MagicPairs<BITS>::kPairs; ++k) {
+          const float lo = lo_h(mp.h[k]), hi = hi_h(mp.h[k]);
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            st.a[r][CPW * i + MagicPairs<BITS>::chan(k, 0)] += w[r] * lo;
+            st.a[r][CPW * i + MagicPairs<BITS>::chan(k, 1)] += w[r] * hi;
+          }
+        }
+      }
+    }
+  };
+  // two register sets in turn: the loads of one batch are in flight while
+  // the other is computed
+  for (int base = 0;;) {
+    load(base + BATCH, B);
+    step(A, base);
+    base += BATCH;
+    if (base >= nt) break;
+    load(base + BATCH, A);
+    step(B, base);
+    base += BATCH;
+    if (base >= nt) break;
+  }
+  write_partial<D, RT, LPT, CPL>(st, red, sm, sM, po, pml);
+}
+
 template <int D, int BITS, int RT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p) {
   const int S = p.S16 + p.Sq;
@@ -352,156 +608,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
     }
     write_partial<D, RT, LPT, CPL>(st, red, sm_max, sm_M, po, pml);
   } else {
-    // ---------------- low-bit tier ----------------
-    constexpr int LPT = lptq_for(D, BITS), CPL = D / LPT, SLOTS = kThreads / LPT, TPT = kTPTQ;
-    constexpr int BATCH = SLOTS * TPT;
-    constexpr int NB = CPL * BITS / 8, NW = NB / 4;
-    constexpr int CB = D * BITS / 8;
-    // single-head tiles score keys with integer dot products on the packed
-    // codes (no per-code conversion); head tiles share converted codes
-    constexpr bool kIntDot = (RT == 1);
-    const int lane = tid % LPT, tslot = tid / LPT, c0 = lane * CPL;
-    const int gpt = D / p.group;
-    const int gi = c0 / p.group;
-    const int t0 = (split - p.S16) * p.Cq;
-    const int t1 = min(p.nq, t0 + p.Cq);
-    const int64_t rb = static_cast<int64_t>(unit) * p.capq;
-    // per-thread stream pointers; token j of a batch is j*SLOTS rows further
-    const uint8_t* pkq = p.kq + (rb + t0 + tslot) * CB + lane * NB;
-    const uint8_t* pvq = p.vq + (rb + t0 + tslot) * CB + lane * NB;
-    const uint32_t* pks = p.ksz + (rb + t0 + tslot) * gpt + gi;
-    const uint32_t* pvs = p.vsz + (rb + t0 + tslot) * gpt + gi;
-    const int sz_step = SLOTS * gpt;
-    struct Regs { Words<NW> k[TPT], v[TPT]; uint32_t ks[TPT], vs[TPT]; };
-    auto load = [&](int base, int boff, Regs& R) {
-#pragma unroll
-      for (int j = 0; j < TPT; ++j) {
-        const int t = base + j * SLOTS + tslot;
-        if (t < t1) {
-          R.k[j] = load_words<NW>(pkq + static_cast<int64_t>(boff + j * SLOTS) * CB);
-          R.ks[j] = ld_nt4(pks + static_cast<int64_t>(boff / SLOTS + j) * sz_step);
-          R.v[j] = load_words<NW>(pvq + static_cast<int64_t>(boff + j * SLOTS) * CB);
-          R.vs[j] = ld_nt4(pvs + static_cast<int64_t>(boff / SLOTS + j) * sz_step);
-        }
-      }
-    };
-    float qsum[RT];
-    Acc<RT, CPL> st;
-    st.init();
-    Regs cur = {}, nxt = {};
-    load(t0, 0, cur);
-    float qh[RT][CPL];
-    load_qhat<D, RT, CPL>(p, n, g, tile, c0, bvec, qh);
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      qsum[r] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) qsum[r] += qh[r][i];
-    }
-    // Integer form of q-hat (single head): q_int = rint(q-hat * 2^F) with F
-    // chosen per lane so |q_int| < 2^22, biased by 2^23 into [0, 2^24) and
-    // cut into six 4-bit digits laid out like the code nibbles. Then
-    //   sum_c q_int[c]*code[c] = sum_d 16^d dot8(codes, digit_d)
-    //                            - 2^23 * dot8(codes, 0x11111111),
-    // exact in 32-bit integers (two's-complement wraparound cancels the bias).
-    constexpr int NQW = CPL / 8;  // nibble words (8 channels each) per lane
-    uint32_t qd[6][NQW];
-    float qunit = 1.0f;
-    if constexpr (kIntDot) {
-      static_assert(static_cast<unsigned long long>(CPL) * ((1 << BITS) - 1) * 15ull * 1118481ull <
-                        4294967296ull, "digit sums must fit 32 bits");
-      float mx = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) mx = fmaxf(mx, fabsf(qh[0][i]));
-      int e = 0;
-      if (mx > 0.0f) (void)frexpf(mx, &e);
-      const int F = 22 - e;
-      qunit = ldexpf(1.0f, -F);
-#pragma unroll
-      for (int d = 0; d < 6; ++d)
-#pragma unroll
-        for (int i = 0; i < NQW; ++i) qd[d][i] = 0;
-#pragma unroll
-      for (int i = 0; i < NQW; ++i) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          // channel of nibble k in nibble word i
-          int ch;
-          if constexpr (BITS == 4) ch = 8 * i + k;
-          else ch = 16 * (i / 2) + 4 * (k / 2) + 2 * (k % 2) + (i % 2);
-          const int qi = static_cast<int>(rintf(ldexpf(qh[0][ch], F)));
-          const uint32_t qb = static_cast<uint32_t>(qi + (1 << 23));
-#pragma unroll
-          for (int d = 0; d < 6; ++d) qd[d][i] |= ((qb >> (4 * d)) & 0xFu) << (4 * k);
-        }
-      }
-    }
-    for (int base = t0, boff = 0; base < t1; base += BATCH, boff += BATCH) {
-      if (base + BATCH < t1) load(base + BATCH, boff + BATCH, nxt);
-      float sc[TPT][RT];
-#pragma unroll
-      for (int j = 0; j < TPT; ++j) {
-        const int t = base + j * SLOTS + tslot;
-        const float s = lo_h(cur.ks[j]), z = hi_h(cur.ks[j]);
-        if constexpr (kIntDot) {
-          uint32_t acc[6] = {0u, 0u, 0u, 0u, 0u, 0u}, csum = 0u;
-#pragma unroll
-          for (int i = 0; i < NQW; ++i) {
-            uint32_t x;
-            if constexpr (BITS == 4) x = cur.k[j].w[i];
-            else x = (i % 2 == 0) ? (cur.k[j].w[i / 2] & 0x33333333u)
-                                  : ((cur.k[j].w[i / 2] >> 2) & 0x33333333u);
-#pragma unroll
-            for (int d = 0; d < 6; ++d) acc[d] = __builtin_amdgcn_udot8(x, qd[d][i], acc[d], false);
-            csum = __builtin_amdgcn_udot8(x, 0x11111111u, csum, false);
-          }
-          const uint32_t u = acc[0] + (acc[1] << 4) + (acc[2] << 8) + (acc[3] << 12) +
-                             (acc[4] << 16) + (acc[5] << 20);
-          const int32_t rdot = static_cast<int32_t>(u - (csum << 23));
-          const float dot = static_cast<float>(rdot) * qunit;
-          const float v = group_sum<LPT>(s * dot + z * qsum[0]);
-          sc[j][0] = (t < t1) ? v : -INFINITY;
-        } else {
-          float cf[CPL];
-          unpack_codes<BITS, CPL>(cur.k[j].w, cf);
-#pragma unroll
-          for (int r = 0; r < RT; ++r) {
-            float dot = 0.0f;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) dot += qh[r][i] * cf[i];
-            const float v = group_sum<LPT>(s * dot + z * qsum[r]);
-            sc[j][r] = (t < t1) ? v : -INFINITY;
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        float bm = sc[0][r];
-#pragma unroll
-        for (int j = 1; j < TPT; ++j) bm = fmaxf(bm, sc[j][r]);
-        st.rebase(r, bm);
-      }
-#pragma unroll
-      for (int j = 0; j < TPT; ++j) {
-        const int t = base + j * SLOTS + tslot;
-        if (t < t1) {
-          float cf[CPL];
-          unpack_codes<BITS, CPL>(cur.v[j].w, cf);
-          const float s = lo_h(cur.vs[j]), z = hi_h(cur.vs[j]);
-#pragma unroll
-          for (int r = 0; r < RT; ++r) {
-            const float pr = fast_exp2(sc[j][r] - st.m[r]);
-            st.l[r] += pr;
-            st.z[r] += pr * z;
-            const float w = pr * s;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) st.a[r][i] += w * cf[i];
-          }
-        }
-      }
-      cur = nxt;
-    }
-    write_partial<D, RT, LPT, CPL>(st, red, sm_max, sm_M, po, pml);
+    lowbit_split<D, BITS, RT>(p, unit, n, g, tile, split, bvec, red, sm_max, sm_M, po, pml);
   }
 }
 
