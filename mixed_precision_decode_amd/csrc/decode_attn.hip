@@ -490,6 +490,183 @@ __device__ __forceinline__ void lowbit_split(const DecodeK& p, int unit, int n, 
   write_partial<D, RT, LPT, CPL>(st, red, sm, sM, po, pml);
 }
 
+// ---------------------------------------------------------------------------
+// FP16 tier: LPT lanes per token, CPL channels (2*CPL bytes) of the key and
+// value rows per lane. Rows are read through a buffer resource spanning the
+// block's slot range [s0, s1), as on the low-bit tier. The new token enters
+// the state of the block that owns the free slot directly (the tile-0 block
+// also writes its balanced key and value into that slot).
+#ifndef MIKV_FP16_CPL1
+#define MIKV_FP16_CPL1 8
+#endif
+#ifndef MIKV_FP16_TPT1
+#define MIKV_FP16_TPT1 2
+#endif
+constexpr int fp16_cpl(int rt) { return rt == 1 ? MIKV_FP16_CPL1 : 8; }
+
+template <int D, int RT>
+__device__ __forceinline__ void fp16_split(const DecodeK& p, int unit, int n, int g, int tile, int split,
+                                           const float* bvec, float* red, float (*sm)[RT], float* sM,
+                                           float* po, float2* pml) {
+  constexpr int CPL = fp16_cpl(RT), LPT = D / CPL, SLOTS = kThreads / LPT;
+  constexpr int TPT = (RT == 1) ? MIKV_FP16_TPT1 : kTPT16;
+  constexpr int BATCH = SLOTS * TPT;
+  constexpr int NV = CPL / 8;  // 16-byte loads per row and lane
+  const int tid = threadIdx.x;
+  const int lane = tid % LPT, tslot = tid / LPT, c0 = lane * CPL;
+  const int s0 = split * p.C16;
+  const int s1 = min(p.cap16, s0 + p.C16);
+  const int ns = max(s1 - s0, 0);
+  const int fr = p.free16[unit];
+  const int64_t rb = static_cast<int64_t>(unit) * p.cap16;
+  const uint32_t rbytes = static_cast<uint32_t>(ns) * D * 2;
+  const Rsrc rk = make_rsrc(p.k16 + (rb + s0) * D, rbytes);
+  const Rsrc rv = make_rsrc(p.v16 + (rb + s0) * D, rbytes);
+  // scores of this tile's heads for the block's slots, [RT][cap16] rows
+  const int64_t scb = (static_cast<int64_t>(unit) * p.rep + tile * RT) * p.cap16 + s0;
+  const uint32_t cof = static_cast<uint32_t>((tslot * D + c0) * 2);
+  struct Regs { Words<4> k[TPT][NV], v[TPT][NV]; };
+  auto load = [&](int base, Regs& R) {
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const uint32_t off = cof + static_cast<uint32_t>(base + j * SLOTS) * (D * 2);
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        R.k[j][e] = bload<4>(rk, off + 16 * e);
+        R.v[j][e] = bload<4>(rv, off + 16 * e);
+      }
+    }
+  };
+  Regs A, B;
+  load(0, A);
+  float qh[RT][CPL];
+  load_qhat<D, RT, CPL>(p, n, g, tile, c0, bvec, qh);
+  Acc<RT, CPL> st;
+  st.init();
+  // The new token: balanced key (fp32 product rounded once to fp16) and
+  // value. In the block owning the free slot it seeds the state of slot
+  // group 0 (max = its score, sum = 1, o = its value); the free slot's stale
+  // row is masked in the stream (it holds finite values: zeros after the
+  // prefill build, the demoted token's row after a decode step).
+  const int frel = fr - s0;
+  const bool owns_fr = frel >= 0 && frel < ns;
+  if (owns_fr) {  // uniform
+    const int64_t nb = static_cast<int64_t>(unit) * D + c0;
+    uint4 kn[NV], vn[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      float kx[8];
+      load8(p.k_new + nb + 8 * e, kx);
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = f2h(mul_rn(kx[2 * i], bvec[c0 + 8 * e + 2 * i]));
+        const uint32_t hi = f2h(mul_rn(kx[2 * i + 1], bvec[c0 + 8 * e + 2 * i + 1]));
+        w[i] = lo | (hi << 16);
+      }
+      kn[e] = make_uint4(w[0], w[1], w[2], w[3]);
+      vn[e] = *reinterpret_cast<const uint4*>(p.v_new + nb + 8 * e);
+      if (tile == 0 && tslot == 0) {
+        *reinterpret_cast<uint4*>(p.k16 + (rb + fr) * D + c0 + 8 * e) = kn[e];
+        *reinterpret_cast<uint4*>(p.v16 + (rb + fr) * D + c0 + 8 * e) = vn[e];
+      }
+    }
+    if (tile == 0 && tid == 0) p.pos16[rb + fr] = p.len - 1;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < NV; ++e) {
+        const uint32_t* kw = reinterpret_cast<const uint32_t*>(&kn[e]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dot += qh[r][8 * e + 2 * i] * lo_h(kw[i]);
+          dot += qh[r][8 * e + 2 * i + 1] * hi_h(kw[i]);
+        }
+      }
+      dot = group_sum<LPT>(dot);
+      if (tslot == 0) {
+        st.m[r] = dot;
+        st.l[r] = 1.0f;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          const uint32_t* vw = reinterpret_cast<const uint32_t*>(&vn[e]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            st.a[r][8 * e + 2 * i] = lo_h(vw[i]);
+            st.a[r][8 * e + 2 * i + 1] = hi_h(vw[i]);
+          }
+        }
+        if (lane == 0) p.sc16[scb + static_cast<int64_t>(r) * p.cap16 + frel] = dot;
+      }
+    }
+  }
+  auto step = [&](const Regs& R, int base) {
+    float sc[TPT][RT];
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const int t = base + j * SLOTS + tslot;
+      const bool valid = t < ns && t != frel;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          const uint32_t* kw = R.k[j][e].w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dot += qh[r][8 * e + 2 * i] * lo_h(kw[i]);
+            dot += qh[r][8 * e + 2 * i + 1] * hi_h(kw[i]);
+          }
+        }
+        dot = group_sum<LPT>(dot);
+        sc[j][r] = valid ? dot : -INFINITY;
+        if (lane == 0 && valid) p.sc16[scb + static_cast<int64_t>(r) * p.cap16 + t] = dot;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      float bm = sc[0][r];
+#pragma unroll
+      for (int j = 1; j < TPT; ++j) bm = fmaxf(bm, sc[j][r]);
+      st.rebase(r, bm);
+    }
+    float mref[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) mref[r] = fmaxf(st.m[r], -FLT_MAX);
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      // masked rows (past the range: loaded as zeros; the stale free row:
+      // finite) get probability 0 and add nothing
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const float pr = fast_exp2(sc[j][r] - mref[r]);
+        st.l[r] += pr;
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+          const uint32_t* vw = R.v[j][e].w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            st.a[r][8 * e + 2 * i] += pr * lo_h(vw[i]);
+            st.a[r][8 * e + 2 * i + 1] += pr * hi_h(vw[i]);
+          }
+        }
+      }
+    }
+  };
+  for (int base = 0;;) {
+    load(base + BATCH, B);
+    step(A, base);
+    base += BATCH;
+    if (base >= ns) break;
+    load(base + BATCH, A);
+    step(B, base);
+    base += BATCH;
+    if (base >= ns) break;
+  }
+  write_partial<D, RT, LPT, CPL>(st, red, sm, sM, po, pml);
+}
+
 template <int D, int BITS, int RT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p) {
   const int S = p.S16 + p.Sq;
@@ -510,103 +687,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
   __shared__ float sm_M[RT];
 
   if (split < p.S16) {
-    // ---------------- FP16 tier ----------------
-    constexpr int LPT = D / 8, CPL = 8, SLOTS = kThreads / LPT, TPT = kTPT16;
-    constexpr int BATCH = SLOTS * TPT;
-    const int lane = tid % LPT, tslot = tid / LPT, c0 = lane * CPL;
-    const int s0 = split * p.C16;
-    const int s1 = min(p.cap16, s0 + p.C16);
-    const int fr = p.free16[unit];
-    const int64_t rb = static_cast<int64_t>(unit) * p.cap16;
-    struct Regs { uint4 k[TPT], v[TPT]; };
-    auto load = [&](int base, Regs& R) {
-#pragma unroll
-      for (int j = 0; j < TPT; ++j) {
-        const int t = base + j * SLOTS + tslot;
-        if (t < s1) {
-          R.k[j] = ld_nt16(p.k16 + (rb + t) * D + c0);
-          R.v[j] = ld_nt16(p.v16 + (rb + t) * D + c0);
-        }
-      }
-    };
-    float qh[RT][CPL];
-    Acc<RT, CPL> st;
-    st.init();
-    Regs cur = {}, nxt = {};
-    load(s0, cur);
-    load_qhat<D, RT, CPL>(p, n, g, tile, c0, bvec, qh);
-    for (int base = s0; base < s1; base += BATCH) {
-      if (base + BATCH < s1) load(base + BATCH, nxt);
-      // the new token replaces the free slot's stale row (and is appended)
-      if (fr >= base && fr < base + BATCH && fr < s1 && (fr - base) % SLOTS == tslot) {
-        const int j = (fr - base) / SLOTS;
-        const int64_t nb = static_cast<int64_t>(unit) * D + c0;
-        float kn[8];
-        load8(p.k_new + nb, kn);
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = f2h(mul_rn(kn[2 * i], bvec[c0 + 2 * i]));
-          const uint32_t hi = f2h(mul_rn(kn[2 * i + 1], bvec[c0 + 2 * i + 1]));
-          w[i] = lo | (hi << 16);
-        }
-        const uint4 kv = make_uint4(w[0], w[1], w[2], w[3]);
-        const uint4 vv = *reinterpret_cast<const uint4*>(p.v_new + nb);
-#pragma unroll
-        for (int jj = 0; jj < TPT; ++jj)
-          if (jj == j) { cur.k[jj] = kv; cur.v[jj] = vv; }
-        if (tile == 0) {
-          *reinterpret_cast<uint4*>(p.k16 + (rb + fr) * D + c0) = kv;
-          *reinterpret_cast<uint4*>(p.v16 + (rb + fr) * D + c0) = vv;
-          if (lane == 0) p.pos16[rb + fr] = p.len - 1;
-        }
-      }
-      float sc[TPT][RT];
-#pragma unroll
-      for (int j = 0; j < TPT; ++j) {
-        const int t = base + j * SLOTS + tslot;
-        const uint32_t* kw = reinterpret_cast<const uint32_t*>(&cur.k[j]);
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          float dot = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            dot += qh[r][2 * i] * lo_h(kw[i]);
-            dot += qh[r][2 * i + 1] * hi_h(kw[i]);
-          }
-          dot = group_sum<LPT>(dot);
-          sc[j][r] = (t < s1) ? dot : -INFINITY;
-          if (lane == 0 && t < s1)
-            p.sc16[(static_cast<int64_t>(unit) * p.rep + tile * RT + r) * p.cap16 + t] = dot;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        float bm = sc[0][r];
-#pragma unroll
-        for (int j = 1; j < TPT; ++j) bm = fmaxf(bm, sc[j][r]);
-        st.rebase(r, bm);
-      }
-#pragma unroll
-      for (int j = 0; j < TPT; ++j) {
-        const int t = base + j * SLOTS + tslot;
-        if (t < s1) {
-          const uint32_t* vw = reinterpret_cast<const uint32_t*>(&cur.v[j]);
-#pragma unroll
-          for (int r = 0; r < RT; ++r) {
-            const float pr = fast_exp2(sc[j][r] - st.m[r]);
-            st.l[r] += pr;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              st.a[r][2 * i] += pr * lo_h(vw[i]);
-              st.a[r][2 * i + 1] += pr * hi_h(vw[i]);
-            }
-          }
-        }
-      }
-      cur = nxt;
-    }
-    write_partial<D, RT, LPT, CPL>(st, red, sm_max, sm_M, po, pml);
+    fp16_split<D, RT>(p, unit, n, g, tile, split, bvec, red, sm_max, sm_M, po, pml);
   } else {
     lowbit_split<D, BITS, RT>(p, unit, n, g, tile, split, bvec, red, sm_max, sm_M, po, pml);
   }

@@ -138,6 +138,13 @@ __global__ __launch_bounds__(256) void h2o_prefill_select_kernel(H2OArgs a, int 
     a.pos16[base16 + a.cap16 - 1] = -1;
     a.acc16[base16 + a.cap16 - 1] = 0.0f;
   }
+  // the free slot's rows start as zeros: decode reads them (masked), so they
+  // must hold finite values
+  for (int i = tid; i < a.d / 8; i += 256) {
+    const int64_t o = (base16 + a.cap16 - 1) * a.d + 8 * i;
+    *reinterpret_cast<uint4*>(a.k16 + o) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(a.v16 + o) = make_uint4(0u, 0u, 0u, 0u);
+  }
 }
 
 template <int D, int BITS, int NL>
