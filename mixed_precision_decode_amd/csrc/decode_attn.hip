@@ -51,7 +51,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 
 struct DecodeK {
-  int hq, hkv, rep, cap16, capq, nq, len, group;
+  int hq, hkv, rep, cap16, capq, nq, len, group, units;
   int S16, Sq, C16, Cq, tiles;
   const uint16_t* q;
   const uint16_t* k_new;
@@ -669,9 +669,15 @@ __device__ __forceinline__ void fp16_split(const DecodeK& p, int unit, int n, in
 
 template <int D, int BITS, int RT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p) {
+  // Split-major block order. Blocks are dispatched to the 8 XCDs in turn
+  // (block i to XCD i mod 8), so with the split index outermost every XCD
+  // sees consecutive (unit, tile) pairs of every split: the same mix of
+  // FP16 and low-bit splits, instead of XCDs that hold only one tier's
+  // splits and finish at different times.
   const int S = p.S16 + p.Sq;
-  const int split = blockIdx.x % S;
-  const int rest = blockIdx.x / S;
+  const int ut = p.units * p.tiles;
+  const int split = blockIdx.x / ut;
+  const int rest = blockIdx.x % ut;
   const int tile = rest % p.tiles;
   const int unit = rest / p.tiles;
   const int n = unit / p.hkv;
@@ -705,6 +711,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
 constexpr int kMergeOut = 64;
 constexpr int kMergeTPO = kThreads / kMergeOut;
 constexpr int kMergeSlots = 16;  // FP16-tier slots per thread held in registers
+constexpr int kMergeHeads = 4;   // heads whose FP16-tier scores are loaded up front
 template <int D, int BITS, int NL, bool FUSE>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p, int RT, H2OView hv) {
   extern __shared__ float2 sml[];
@@ -726,11 +733,10 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   const int out0 = chunk * kMergeOut;
   const int h_lo = (chunk == 0) ? 0 : out0 / D;
   const int h_hi = (chunk == 0) ? rep : min(rep, (out0 + kMergeOut - 1) / D + 1);
-  // (1) issue every load
-  for (int i = h_lo * S + tid; i < h_hi * S; i += kThreads) {
-    const int hl = i / S, s = i % S;
-    sml[i] = pml[(static_cast<int64_t>((unit * p.tiles + hl / RT) * S) + s) * RT + hl % RT];
-  }
+  // (1) issue every load before the first wait: the thread's partial
+  // outputs, the FP16-tier scores of up to kMergeHeads heads and the H2O
+  // state (chunk 0), then the split statistics, whose LDS stores wait for
+  // all of them at once
   const int oi = out0 + tid % kMergeOut;  // this thread's output
   const int sub = tid / kMergeOut;        // its subset of splits: s = sub, sub + TPO, ...
   const bool has_out = oi < rep * D;
@@ -744,16 +750,18 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
     pf[k] = (has_out && s < S) ? po[static_cast<int64_t>(s) * RT * D] : 0.0f;
   }
   const bool slots_in_regs = cap16 <= kMergeSlots * kThreads;
-  float sv[kMergeSlots], accv[kMergeSlots];
+  float sv[kMergeHeads][kMergeSlots], accv[kMergeSlots];
   int posv[kMergeSlots];
   int fr = 0;
   if (chunk == 0) {
-    if (slots_in_regs) {  // head 0's scores (the only head when rep == 1)
+    if (slots_in_regs) {
 #pragma unroll
-      for (int k = 0; k < kMergeSlots; ++k) {
-        const int sl = tid + k * kThreads;
-        sv[k] = (sl < cap16) ? sc[sl] : 0.0f;
-      }
+      for (int h = 0; h < kMergeHeads; ++h)
+#pragma unroll
+        for (int k = 0; k < kMergeSlots; ++k) {
+          const int sl = tid + k * kThreads;
+          sv[h][k] = (h < rep && sl < cap16) ? sc[h * cap16 + sl] : 0.0f;
+        }
     }
     if constexpr (FUSE) {
       fr = hv.free16[unit];
@@ -763,6 +771,10 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
         if (sl < cap16) { accv[k] = hv.acc16[base16 + sl]; posv[k] = hv.pos16[base16 + sl]; }
       }
     }
+  }
+  for (int i = h_lo * S + tid; i < h_hi * S; i += kThreads) {
+    const int hl = i / S, s = i % S;
+    sml[i] = pml[(static_cast<int64_t>((unit * p.tiles + hl / RT) * S) + s) * RT + hl % RT];
   }
   __syncthreads();
   // (2) per head: maximum and reciprocal normaliser
@@ -812,16 +824,25 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
     // all loads of a head are issued together, before any store
     float pa[kMergeSlots];
 #pragma unroll
-    for (int k = 0; k < kMergeSlots; ++k) pa[k] = fast_exp2(sv[k] - sM[0]) * sIL[0];
-    for (int hl = 1; hl < rep; ++hl) {
+    for (int k = 0; k < kMergeSlots; ++k) pa[k] = fast_exp2(sv[0][k] - sM[0]) * sIL[0];
+#pragma unroll
+    for (int hl = 1; hl < kMergeHeads; ++hl) {
+      if (hl < rep) {
+        const float M = sM[hl], IL = sIL[hl];
+#pragma unroll
+        for (int k = 0; k < kMergeSlots; ++k) pa[k] += fast_exp2(sv[hl][k] - M) * IL;
+      }
+    }
+    for (int hl = kMergeHeads; hl < rep; ++hl) {
+      float x[kMergeSlots];
 #pragma unroll
       for (int k = 0; k < kMergeSlots; ++k) {
         const int sl = tid + k * kThreads;
-        sv[k] = (sl < cap16) ? sc[hl * cap16 + sl] : 0.0f;
+        x[k] = (sl < cap16) ? sc[hl * cap16 + sl] : 0.0f;
       }
       const float M = sM[hl], IL = sIL[hl];
 #pragma unroll
-      for (int k = 0; k < kMergeSlots; ++k) pa[k] += fast_exp2(sv[k] - M) * IL;
+      for (int k = 0; k < kMergeSlots; ++k) pa[k] += fast_exp2(x[k] - M) * IL;
     }
     Worst w;
     const int limit = hv.len - hv.recent;
@@ -913,7 +934,7 @@ template <int D, int BITS, int RT>
 static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
   DecodeK k;
   k.hq = a.hq; k.hkv = a.hkv; k.rep = a.hq / a.hkv; k.cap16 = a.cap16; k.capq = a.capq;
-  k.nq = a.len - a.cap16; k.len = a.len; k.group = a.group;
+  k.nq = a.len - a.cap16; k.len = a.len; k.group = a.group; k.units = a.batch * a.hkv;
   k.S16 = pl.S16; k.Sq = pl.Sq; k.C16 = pl.C16; k.Cq = pl.Cq; k.tiles = pl.tiles;
   k.q = a.q; k.k_new = a.k_new; k.v_new = a.v_new; k.b = a.b;
   k.k16 = a.k16; k.v16 = a.v16; k.pos16 = a.pos16; k.free16 = a.free16;
