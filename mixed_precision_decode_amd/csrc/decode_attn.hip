@@ -712,7 +712,11 @@ constexpr int kMergeOut = 64;
 constexpr int kMergeTPO = kThreads / kMergeOut;
 constexpr int kMergeSlots = 16;  // FP16-tier slots per thread held in registers
 constexpr int kMergeHeads = 4;   // heads whose FP16-tier scores are loaded up front
-template <int D, int BITS, int NL, bool FUSE>
+#ifndef MIKV_MERGE_MAX_BLOCKS
+#define MIKV_MERGE_MAX_BLOCKS 1024
+#endif
+constexpr long kMergeMaxBlocks = MIKV_MERGE_MAX_BLOCKS;  // above this, one block takes several output groups
+template <int D, int BITS, int NL, bool FUSE, int G>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p, int RT, H2OView hv) {
   extern __shared__ float2 sml[];
   __shared__ float red[kThreads];
@@ -730,45 +734,60 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   const float* __restrict__ sc = p.sc16 + static_cast<int64_t>(unit) * rep * cap16;
   const int64_t base16 = static_cast<int64_t>(unit) * cap16;
   // heads this block needs (statistics): its outputs' heads, or all for p16
-  const int out0 = chunk * kMergeOut;
+  const int out0 = chunk * kMergeOut * G;
   const int h_lo = (chunk == 0) ? 0 : out0 / D;
-  const int h_hi = (chunk == 0) ? rep : min(rep, (out0 + kMergeOut - 1) / D + 1);
+  const int h_hi = (chunk == 0) ? rep : min(rep, (out0 + kMergeOut * G - 1) / D + 1);
   // (1) issue every load before the first wait: the thread's partial
   // outputs, the FP16-tier scores of up to kMergeHeads heads and the H2O
   // state (chunk 0), then the split statistics, whose LDS stores wait for
   // all of them at once
-  const int oi = out0 + tid % kMergeOut;  // this thread's output
-  const int sub = tid / kMergeOut;        // its subset of splits: s = sub, sub + TPO, ...
-  const bool has_out = oi < rep * D;
-  const int ohl = oi / D, oc = oi % D;
-  const float* po = pov + (static_cast<int64_t>((unit * p.tiles + ohl / RT) * S) * RT + ohl % RT) * D + oc;
-  constexpr int PF = 8;
-  float pf[PF];
+  // group gi of the block: outputs out0 + 64*gi + (tid % 64)
+  const int sub = tid / kMergeOut;  // the thread's subset of splits: s = sub, sub + TPO, ...
+  auto out_of = [&](int gi) { return out0 + gi * kMergeOut + tid % kMergeOut; };
+  auto part_of = [&](int oi) {
+    const int hl = oi / D;
+    return pov + (static_cast<int64_t>((unit * p.tiles + hl / RT) * S) * RT + hl % RT) * D + oi % D;
+  };
+  constexpr int PF = (G == 1) ? 8 : 2;  // splits per thread loaded up front, per group
+  float pf[G][PF];
 #pragma unroll
-  for (int k = 0; k < PF; ++k) {
-    const int s = sub + k * kMergeTPO;
-    pf[k] = (has_out && s < S) ? po[static_cast<int64_t>(s) * RT * D] : 0.0f;
+  for (int gi = 0; gi < G; ++gi) {
+    const int oi = out_of(gi);
+    const float* po = part_of(oi < rep * D ? oi : 0);
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      const int s = sub + k * kMergeTPO;
+      pf[gi][k] = (oi < rep * D && s < S) ? po[static_cast<int64_t>(s) * RT * D] : 0.0f;
+    }
   }
   const bool slots_in_regs = cap16 <= kMergeSlots * kThreads;
   float sv[kMergeHeads][kMergeSlots], accv[kMergeSlots];
   int posv[kMergeSlots];
   int fr = 0;
+  // slot rounds actually used; heads and rounds are uniform branches, and
+  // slot indices past the tier are clamped (their values are never used),
+  // so the loads issue back to back without per-lane branches
+  const int nslot = (cap16 + kThreads - 1) / kThreads;
   if (chunk == 0) {
     if (slots_in_regs) {
 #pragma unroll
-      for (int h = 0; h < kMergeHeads; ++h)
+      for (int h = 0; h < kMergeHeads; ++h) {
+        if (h < rep) {
 #pragma unroll
-        for (int k = 0; k < kMergeSlots; ++k) {
-          const int sl = tid + k * kThreads;
-          sv[h][k] = (h < rep && sl < cap16) ? sc[h * cap16 + sl] : 0.0f;
+          for (int k = 0; k < kMergeSlots; ++k)
+            if (k < nslot) sv[h][k] = sc[h * cap16 + min(tid + k * kThreads, cap16 - 1)];
         }
+      }
     }
     if constexpr (FUSE) {
       fr = hv.free16[unit];
 #pragma unroll
       for (int k = 0; k < kMergeSlots; ++k) {
-        const int sl = tid + k * kThreads;
-        if (sl < cap16) { accv[k] = hv.acc16[base16 + sl]; posv[k] = hv.pos16[base16 + sl]; }
+        if (k < nslot) {
+          const int sl = min(tid + k * kThreads, cap16 - 1);
+          accv[k] = hv.acc16[base16 + sl];
+          posv[k] = hv.pos16[base16 + sl];
+        }
       }
     }
   }
@@ -789,7 +808,11 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   __syncthreads();
   // (3) outputs: each thread sums its subset of splits, then the kMergeTPO
   // threads of an output combine through LDS
-  {
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const int oi = out_of(gi);
+    const bool has_out = oi < rep * D;
+    const int ohl = oi / D, oc = oi % D;
     float v = 0.0f;
     if (has_out) {
       const float M = sM[ohl];
@@ -797,12 +820,14 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
 #pragma unroll
       for (int k = 0; k < PF; ++k) {
         const int s = sub + k * kMergeTPO;
-        if (s < S) v += pf[k] * fast_exp2(ml[s].x - M);
+        if (s < S) v += pf[gi][k] * fast_exp2(ml[s].x - M);
       }
+      const float* po = part_of(oi);
 #pragma unroll 4
       for (int s = sub + PF * kMergeTPO; s < S; s += kMergeTPO)
         v += po[static_cast<int64_t>(s) * RT * D] * fast_exp2(ml[s].x - M);
     }
+    if (gi > 0) __syncthreads();  // the previous group's reads of red are done
     red[tid] = v;
     __syncthreads();
     if (tid < kMergeOut && has_out) {
@@ -824,32 +849,33 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
     // all loads of a head are issued together, before any store
     float pa[kMergeSlots];
 #pragma unroll
-    for (int k = 0; k < kMergeSlots; ++k) pa[k] = fast_exp2(sv[0][k] - sM[0]) * sIL[0];
+    for (int k = 0; k < kMergeSlots; ++k)
+      if (k < nslot) pa[k] = fast_exp2(sv[0][k] - sM[0]) * sIL[0];
 #pragma unroll
     for (int hl = 1; hl < kMergeHeads; ++hl) {
       if (hl < rep) {
         const float M = sM[hl], IL = sIL[hl];
 #pragma unroll
-        for (int k = 0; k < kMergeSlots; ++k) pa[k] += fast_exp2(sv[hl][k] - M) * IL;
+        for (int k = 0; k < kMergeSlots; ++k)
+          if (k < nslot) pa[k] += fast_exp2(sv[hl][k] - M) * IL;
       }
     }
     for (int hl = kMergeHeads; hl < rep; ++hl) {
       float x[kMergeSlots];
 #pragma unroll
-      for (int k = 0; k < kMergeSlots; ++k) {
-        const int sl = tid + k * kThreads;
-        x[k] = (sl < cap16) ? sc[hl * cap16 + sl] : 0.0f;
-      }
+      for (int k = 0; k < kMergeSlots; ++k)
+        if (k < nslot) x[k] = sc[hl * cap16 + min(tid + k * kThreads, cap16 - 1)];
       const float M = sM[hl], IL = sIL[hl];
 #pragma unroll
-      for (int k = 0; k < kMergeSlots; ++k) pa[k] += fast_exp2(x[k] - M) * IL;
+      for (int k = 0; k < kMergeSlots; ++k)
+        if (k < nslot) pa[k] += fast_exp2(x[k] - M) * IL;
     }
     Worst w;
     const int limit = hv.len - hv.recent;
 #pragma unroll
     for (int k = 0; k < kMergeSlots; ++k) {
       const int sl = tid + k * kThreads;
-      if (sl < cap16) {
+      if (k < nslot && sl < cap16) {
         const float a = pa[k];
         p16[sl] = a;
         if constexpr (FUSE) {
@@ -958,13 +984,28 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   const bool fuse = a.fuse_h2o && a.cap16 <= kFusedMaxCap16;
   H2OView hv = a.h2o;
   if (!a.fuse_h2o) hv.len = a.len, hv.recent = 0;
-  const dim3 mgrid(static_cast<unsigned>(units), static_cast<unsigned>((k.rep * D + kMergeOut - 1) / kMergeOut));
-#define MIKV_MERGE(NL_, F_) \
-  decode_merge_kernel<D, BITS, NL_, F_><<<mgrid, kThreads, lds, stream>>>(k, RT, hv)
+  // Output groups of 64 per merge block: with few splits one block takes all
+  // of a unit's outputs (fewer, fuller blocks); with many splits the outputs
+  // spread over a 2-D grid so each block reads a bounded number of partials.
+  const int groups = (k.rep * D + kMergeOut - 1) / kMergeOut;
+  int G = 1;
+  if (S <= 2 * kMergeTPO)
+    while (G < 8 && G < groups && units * ((groups + G - 1) / G) > kMergeMaxBlocks) G *= 2;
+  const dim3 mgrid(static_cast<unsigned>(units), static_cast<unsigned>((groups + G - 1) / G));
+#define MIKV_MERGE_G(NL_, F_, G_) \
+  decode_merge_kernel<D, BITS, NL_, F_, G_><<<mgrid, kThreads, lds, stream>>>(k, RT, hv)
+#define MIKV_MERGE(NL_, F_)                   \
+  do {                                        \
+    if (G == 1) MIKV_MERGE_G(NL_, F_, 1);     \
+    else if (G == 2) MIKV_MERGE_G(NL_, F_, 2); \
+    else if (G == 4) MIKV_MERGE_G(NL_, F_, 4); \
+    else MIKV_MERGE_G(NL_, F_, 8);            \
+  } while (0)
   if (!fuse) MIKV_MERGE(D / 16, false);
   else if (a.group == D / 2) MIKV_MERGE(D / 16, true);
   else MIKV_MERGE(D / 8, true);
 #undef MIKV_MERGE
+#undef MIKV_MERGE_G
   return hipGetLastError();
 }
 
