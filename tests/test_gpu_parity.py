@@ -220,6 +220,11 @@ def _lockstep(cfg, seed, steps, balanced=True, check_every=1):
     ("gqa_throughput", dict(batch=3, T=600), True, 5),
     ("llama3_8b_32k", dict(hq=8, hkv=2, T=4100), True, 4),
     ("llama2_7b_layer", dict(batch=2, hq=3, hkv=3, T=1500), True, 4),
+    # one (sequence, head) unit per 1024-thread block, whole units per block
+    ("tiny", dict(batch=256), True, 6),
+    ("tiny", dict(batch=512, bits=2), True, 4),                 # two units per block
+    ("tiny", dict(batch=256, group=64, pct=0, recent=0), True, 3),
+    ("llama2_7b_layer", dict(T=700), True, 3),
 ])
 def test_decode_lockstep(name, over, balanced, steps):
     cfg = S.CONFIGS[name].scaled(**over)
@@ -332,6 +337,8 @@ def test_graph_replay_matches_eager():
     ("tiny", dict(pct=0, recent=0), 4), ("tiny", dict(group=64), 4),
     ("gqa_throughput", dict(batch=2, T=900), 3),
     ("llama3_8b_32k", dict(hq=8, hkv=2, T=20000, pct=25), 2),    # FP16 tier > 4096 slots: unfused path
+    ("tiny", dict(batch=256), 4), ("tiny", dict(batch=512, bits=2, group=64), 3),  # one-pass kernel
+    ("llama2_7b_layer", dict(T=700), 2),
 ])
 def test_decode_step_matches_separate_calls(name, over, steps):
     """mikv_decode_step is bit-identical to mikv_decode_attn followed by
