@@ -26,6 +26,7 @@
 //                 partials of every query head of the group and turns the
 //                 FP16-tier scores into p16 (summed over the group).
 // Scores are in the log2 domain (q-hat is pre-multiplied by log2(e)/sqrt(d)).
+#include <atomic>
 #include <cfloat>
 
 #include "common.hpp"
@@ -895,9 +896,41 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
 
 static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Resident split-kernel blocks per compute unit for this instantiation, from
+// the runtime's occupancy calculator (cached per instantiation); the
+// default when it cannot answer (no device).
+template <int D, int BITS, int RT>
+static int occupancy_of() {
+  int n = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &n, reinterpret_cast<const void*>(decode_split_kernel<D, BITS, RT>), kThreads, 0);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+static int split_blocks_per_cu(int d, int bits, int rt) {
+  static std::atomic<int> cache[2][2][3];
+  std::atomic<int>& c = cache[d == 128][bits == 4][rt == 1 ? 0 : (rt == 2 ? 1 : 2)];
+  int n = c.load(std::memory_order_relaxed);
+  if (n == 0) {
+#define MIKV_OCC(D_, B_, RT_) \
+  if (d == D_ && bits == B_ && rt == RT_) n = occupancy_of<D_, B_, RT_>();
+    MIKV_OCC(128, 4, 1) MIKV_OCC(128, 4, 2) MIKV_OCC(128, 4, 4)
+    MIKV_OCC(128, 2, 1) MIKV_OCC(128, 2, 2) MIKV_OCC(128, 2, 4)
+    MIKV_OCC(64, 4, 1) MIKV_OCC(64, 4, 2) MIKV_OCC(64, 4, 4)
+    MIKV_OCC(64, 2, 1) MIKV_OCC(64, 2, 2) MIKV_OCC(64, 2, 4)
+#undef MIKV_OCC
+    if (n <= 0) return MIKV_BLOCKS_PER_CU;
+    c.store(n, std::memory_order_relaxed);
+  }
+  return n < MIKV_BLOCKS_PER_CU ? n : MIKV_BLOCKS_PER_CU;
+}
+
 // Split sizes. The grid is sized to one resident wave of blocks
-// (MIKV_BLOCKS_PER_CU per compute unit, which the split kernel's register
-// use allows), so no block starts after the others have drained. The
+// (the instantiation's occupancy, at most MIKV_BLOCKS_PER_CU per compute
+// unit), so no block starts after the others have drained. The
 // splits of a (sequence, kv head) are shared between the tiers in
 // proportion to their bytes, so every block streams about the same amount;
 // each tier gets at least one split when it has tokens.
@@ -908,7 +941,7 @@ DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, 
   const double b16 = static_cast<double>(cap16) * 4.0 * d;
   const double bq = static_cast<double>(nq) * 2.0 * (d * bits / 8 + 4 * (d / group));
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
-  long per_unit = (static_cast<long>(kCUs) * MIKV_BLOCKS_PER_CU) / units;
+  long per_unit = (static_cast<long>(kCUs) * split_blocks_per_cu(d, bits, pl.RT)) / units;
   // no split below ~16 KB of rows
   const long cap_splits = static_cast<long>((b16 + bq) / 16384.0) + 1;
   if (per_unit > cap_splits) per_unit = cap_splits;
