@@ -154,3 +154,44 @@ def test_workspace_queries(lib):
     b = lib.mikv_decode_attn_workspace(C.byref(dims.c()), 4000)
     assert 0 < a <= b
     assert lib.mikv_decode_attn_workspace(C.byref(dims.c()), 5) == 0   # max_len < cap16
+
+
+def _no_device():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+@pytest.mark.skipif(not _no_device(), reason="launches with fake pointers: only where no GPU is visible")
+@pytest.mark.parametrize("batch,hq,hkv,d,bits,group,cap16", [
+    (8, 32, 32, 128, 4, 64, 820), (1, 32, 8, 128, 2, 64, 3277), (64, 32, 8, 128, 4, 64, 410),
+    (1, 1, 1, 64, 4, 32, 52), (3, 9, 3, 64, 2, 64, 17), (2, 16, 2, 128, 4, 128, 1),
+    (256, 1, 1, 64, 4, 32, 52), (1, 64, 1, 128, 4, 64, 5000),
+])
+def test_workspace_bound_covers_every_length(lib, batch, hq, hkv, d, bits, group, cap16):
+    """The workspace bound for max_len serves every length up to max_len: a
+    call with exactly that many bytes passes the workspace check and fails
+    only at the launch (no device here)."""
+    max_len = cap16 + 40000
+    dims = L.Dims(batch=batch, hq=hq, hkv=hkv, d=d, group=group, bits=bits, cap16=cap16, capq=max_len)
+    need = lib.mikv_decode_attn_workspace(C.byref(dims.c()), max_len)
+    assert need > 0
+    c = _cache()
+    for length in sorted({cap16, cap16 + 1, cap16 + 7, cap16 + 600, cap16 + 4097, max_len - 1, max_len}):
+        st = lib.mikv_decode_attn(C.byref(dims.c()), C.byref(c), length, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, need, None)
+        assert st == L.MIKV_ERR_HIP, (length, st)
+        st = lib.mikv_decode_step(C.byref(dims.c()), C.byref(c), length, 0, cap16 - 1, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, None, FAKE, need, None)
+        assert st in (L.MIKV_ERR_HIP, L.MIKV_ERR_CAPACITY), (length, st)
+
+
+def test_tier_offsets_limit(lib):
+    """The decode kernels address one (sequence, kv head) tier with 32-bit
+    byte offsets: larger per-unit tiers are rejected before any launch."""
+    c = _cache()
+    big = _dims(capq=1 << 27)            # 2^27 slots * 64 B = 2^33 B of INT4 codes
+    assert lib.mikv_decode_attn(C.byref(big.c()), C.byref(c), 50, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, 1 << 40, None) == L.MIKV_ERR_SHAPE
+    big16 = _dims(cap16=1 << 23, capq=100)   # 2^23 slots * 256 B = 2^31 B of fp16 rows
+    assert lib.mikv_decode_attn(C.byref(big16.c()), C.byref(c), (1 << 23) + 5, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, FAKE, 1 << 40, None) == L.MIKV_ERR_SHAPE
