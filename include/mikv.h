@@ -150,7 +150,10 @@ mikv_status mikv_quantize_tokens(const uint16_t* x, const int32_t* rows,
  *   3. p16[n][g][slot] = sum over the query heads of group g of p at that
  *      FP16 slot (input of the H2O accumulation).
  * Precondition: the low-bit tier holds len - cap16 tokens (slots
- * 0..len-cap16-1); every FP16 slot other than free16 is occupied.
+ * 0..len-cap16-1); every FP16 slot other than free16 is occupied. The free
+ * slot's stale K/V rows are read and masked, so they must hold finite fp16
+ * values (the prefill build zeroes them; afterwards they hold the token the
+ * last step demoted).
  * q [batch][hq][d] fp16, k_new/v_new [batch][hkv][d] fp16, b [batch][hkv][d]
  * fp32 (inputs); o [batch][hq][d] fp32, p16 [batch][hkv][cap16] fp32
  * (outputs). Accumulation is fp32.
@@ -158,7 +161,9 @@ mikv_status mikv_quantize_tokens(const uint16_t* x, const int32_t* rows,
  * for any len <= max_len; it holds the per-split partial results between the
  * two kernels of the call. One workspace serves one call at a time.
  * Errors: len - cap16 < 0 -> MIKV_ERR_SHAPE; len - cap16 > capq ->
- * MIKV_ERR_CAPACITY.
+ * MIKV_ERR_CAPACITY; a per-(sequence, kv head) tier of 2^31 bytes or more
+ * (capq*d*bits/8 or cap16*2*d) -> MIKV_ERR_SHAPE (the kernels address a tier
+ * with 32-bit offsets).
  */
 size_t mikv_decode_attn_workspace(const mikv_dims* dims, int32_t max_len);
 mikv_status mikv_decode_attn(const mikv_dims* dims, const mikv_cache* cache,
@@ -203,9 +208,10 @@ typedef struct {
  * Prefill mode (p16 == NULL, src != NULL, len == src->T):
  *   important = positions >= T - recent plus the top-`heavy` positions of
  *   [0, T - recent) by (acc0 desc, position asc); they fill FP16 slots
- *   0..B-1 in ascending position with acc16 = acc0, free16 = B; the other
- *   T - B positions are quantized into low-bit slots 0..T-B-1 in ascending
- *   position. demoted_pos is ignored.
+ *   0..B-1 in ascending position with acc16 = acc0, free16 = B (its K/V
+ *   rows zeroed, pos16 = -1, acc16 = 0); the other T - B positions are
+ *   quantized into low-bit slots 0..T-B-1 in ascending position.
+ *   demoted_pos is ignored.
  * ws: mikv_h2o_workspace(dims, max_T) bytes (any contents; decode mode
  * needs none and accepts ws == NULL).
  * Errors: T < B -> MIKV_ERR_SHAPE; low-bit tier overflow -> MIKV_ERR_CAPACITY.
