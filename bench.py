@@ -137,6 +137,109 @@ def calibrate_copy(nbytes=1 << 30, reps=5):
                       "copy_GBps": 2 * nbytes / t / 1e9}), flush=True)
 
 
+def _events(n):
+    import torch
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+
+def bench_criticalkv(args, log):
+    """CriticalKV prefill select at 32 heads x 32K tokens (hidden 4096): the
+    two-stage selection with the ||V_h W_O,h||_1 projection on MFMA. Flops
+    are the projection's algorithmic 2 (T - b1) d hidden per head."""
+    import torch
+    from mixed_precision_decode_amd import _lib as L
+    from mixed_precision_decode_amd import synth as S
+    cfg = S.CKV_CONFIGS["criticalkv_32k"]
+    A, V, W = S.criticalkv_inputs(cfg, args.seed)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    Ag, Vg, Wg = dev(A), dev(V), dev(W)
+    budget = cfg.budget
+    b1 = int(np.floor(np.float64(np.float32(cfg.alpha)) * budget))
+    idx = torch.empty((cfg.H, budget), dtype=torch.int32, device="cuda")
+    ws = torch.empty(L.mikv_criticalkv_workspace(cfg.H, cfg.T, cfg.d, cfg.hidden), dtype=torch.uint8,
+                     device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    fo = torch.empty((), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        L.mikv_criticalkv_select(Ag, Vg, Wg, budget, cfg.alpha, idx, ws=ws)
+    evs = _events(args.steps)
+    for e0, e1 in evs:
+        torch.sum(flush, dim=0, out=fo)
+        e0.record()
+        L.mikv_criticalkv_select(Ag, Vg, Wg, budget, cfg.alpha, idx, ws=ws)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flops = 2.0 * (cfg.T - b1) * cfg.d * cfg.hidden * cfg.H
+    log(f"[bench] criticalkv select {ms:.3f} ms, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s over the call")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        h = 0
+        t0 = time.perf_counter()
+        O.criticalkv_select(A[h:h + 1], V[h:h + 1], W[h * cfg.d:(h + 1) * cfg.d], budget, cfg.alpha)
+        el = time.perf_counter() - t0
+        cpu = {"value": el * cfg.H * 1e3, "unit": "ms per select (32 heads, extrapolated)", "kind": "oracle",
+               "sample": f"1 of {cfg.H} heads, fp64 numpy, {el:.1f} s"}
+    return {"metric": "CriticalKV prefill select ms (MFMA projection TFLOP/s)", "value": ms, "unit": "ms",
+            "higher_is_better": False, "steps": args.steps, "warmup": args.warmup, "dtype": "f16 MFMA, f32 accumulate",
+            "data": "synthetic",
+            "config": {"workload": cfg.name, "heads": cfg.H, "head_dim": cfg.d, "hidden": cfg.hidden,
+                       "context": cfg.T, "budget": budget, "alpha": cfg.alpha},
+            "roofline": {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12, "peak": 2500.0,
+                         "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / 2500.0,
+                         "flops_per_call": flops, "kernel": "mikv_criticalkv_select (stage 1 + projection + stage 2)"},
+            "context": "the pages report about 0.06 s added TTFT at 32K, batch 1 (hardware not given)",
+            "cpu_baseline": cpu}
+
+
+def bench_prefill(args, log):
+    """Prefill-time kernels of the workload: the channel balancer (q and k
+    max-abs scan, b) and the prefill build (top-H selection, FP16 rows and
+    quantized low-bit rows). HBM-bound; GB/s from their algorithmic bytes."""
+    import torch
+    from mixed_precision_decode_amd import _lib as L
+    from mixed_precision_decode_amd import synth as S
+    cfg = S.CONFIGS[args.workload]
+    q, k, v, acc0 = S.prefill_tensors(cfg, args.seed)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    dims = L.Dims(batch=cfg.batch, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, group=cfg.G, bits=cfg.bits,
+                  cap16=cfg.cap16, capq=cfg.T - cfg.B + 1)
+    cache = L.Cache(dims)
+    qg, kg, vg, ag = dev(q), dev(k), dev(v), dev(acc0)
+    b = torch.empty((cfg.batch, cfg.hkv, cfg.d), dtype=torch.float32, device="cuda")
+    ws_b = torch.empty(L.mikv_balance_workspace(dims, cfg.T), dtype=torch.uint8, device="cuda")
+    ws_h = torch.empty(L.mikv_h2o_workspace(dims, cfg.T), dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    fo = torch.empty((), dtype=torch.float32, device="cuda")
+    n_u = cfg.batch * cfg.hkv
+    bal_bytes = 2.0 * cfg.d * cfg.T * (cfg.batch * cfg.hq + n_u) + 4.0 * cfg.d * n_u
+    build_bytes = n_u * (cfg.T * (4.0 * cfg.d + 4 + 4)          # k, v, acc0 read; slot map
+                         + cfg.B * (4.0 * cfg.d + 8)             # FP16 rows + pos/acc written
+                         + (cfg.T - cfg.B) * (2 * (cfg.d * cfg.bits / 8 + 4 * cfg.d / cfg.G) + 4))
+    res = {}
+    for name, fn, nbytes in (
+            ("balance", lambda: L.mikv_balance_prefill(dims, cfg.T, qg, kg, b, None, ws_b), bal_bytes),
+            ("build", lambda: L.mikv_h2o_update_select(dims, cache, cfg.T, cfg.recent, cfg.H,
+                                                       src=dict(k=kg, v=vg, acc0=ag, b=b), ws=ws_h), build_bytes)):
+        for _ in range(args.warmup):
+            fn()
+        evs = _events(args.steps)
+        for e0, e1 in evs:
+            torch.sum(flush, dim=0, out=fo)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(e) for a, e in evs])) * 1e3
+        res[name] = {"us": us, "bytes": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
+                     "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
+        log(f"[bench] prefill {name} {us:.1f} us, {res[name]['GBps']:.0f} GB/s")
+    return {"metric": "prefill balancer and build GB/s", "value": res["balance"]["GBps"], "unit": "GB/s",
+            "higher_is_better": True, "steps": args.steps, "warmup": args.warmup, "dtype": "f32",
+            "data": "synthetic", "config": {"workload": cfg.name}, "kernels": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,9 +259,17 @@ def main():
                          "launches, measured faster on MI355X for this step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference kernel for HBM counters)")
+    ap.add_argument("--criticalkv", action="store_true",
+                    help="only time the CriticalKV prefill select (32 heads, 32K tokens); one JSON line")
+    ap.add_argument("--prefill", action="store_true",
+                    help="only time the workload's prefill balancer and build; one JSON line")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.criticalkv or args.prefill:
+        log = lambda *a: print(*a, file=sys.stderr, flush=True)
+        print(json.dumps(bench_criticalkv(args, log) if args.criticalkv else bench_prefill(args, log)), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs the MiKV path on one GPU only; --gpus must be 1 "
