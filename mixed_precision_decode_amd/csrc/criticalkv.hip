@@ -55,15 +55,22 @@ size_t criticalkv_ws_bytes(int H, int T, int d, int hidden) {
 }
 
 // ------------------------------------------------------------------ stage 1
-__global__ __launch_bounds__(256) void ckv_stage1_kernel(const float* __restrict__ A, int T, int b1,
-                                                         CkvWs w, float* __restrict__ score2) {
+// Stage kernels: one block of kStageThreads per head. After the radix
+// select, positions are visited in chunks of kStageThreads * kRun; each thread
+// takes kRun consecutive positions, so a chunk needs two block scans (ties,
+// then the kept or rest positions) instead of two per kStageThreads positions.
+constexpr int kStageThreads = 1024;
+constexpr int kRun = 8;
+
+__global__ __launch_bounds__(kStageThreads) void ckv_stage1_kernel(const float* __restrict__ A, int T, int b1,
+                                                                   CkvWs w, float* __restrict__ score2) {
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
   const float* a = A + static_cast<int64_t>(h) * T;
   uint32_t tau = 0xFFFFFFFFu;
   int need = 0;
   if (b1 > 0) {
-    block_radix_topm(T, b1, [&](int i, uint32_t* key) {
+    block_radix_topm<kStageThreads>(T, b1, [&](int i, uint32_t* key) {
       *key = float_key(a[i]);
       return true;
     }, &tau, &need);
@@ -72,22 +79,41 @@ __global__ __launch_bounds__(256) void ckv_stage1_kernel(const float* __restrict
   uint8_t* s1 = w.s1 + static_cast<int64_t>(h) * T;
   int32_t* rows2 = w.rows2 + static_cast<int64_t>(h) * (T - b1);
   float* sc = score2 + static_cast<int64_t>(h) * T;
-  for (int p0 = 0; p0 < T; p0 += 256) {
-    const int p = p0 + tid;
-    const bool valid = p < T;
-    uint32_t key = 0;
-    if (valid) key = float_key(a[p]);
-    const int eq = (b1 > 0 && valid && key == tau) ? 1 : 0;
+  for (int p0 = 0; p0 < T; p0 += kStageThreads * kRun) {
+    const int base = p0 + tid * kRun;
+    uint32_t key[kRun];
+    int neq = 0;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      key[j] = (base + j < T) ? float_key(a[base + j]) : 0u;
+      neq += (b1 > 0 && base + j < T && key[j] == tau) ? 1 : 0;
+    }
     int eq_tot;
-    const int eq_rank = eq_seen + block_prefix(eq, &eq_tot);
+    int eq_rank = eq_seen + block_scan_add<kStageThreads>(neq, &eq_tot);
     eq_seen += eq_tot;
-    const bool sel = valid && b1 > 0 && (key > tau || (eq && eq_rank < need));
+    bool sel[kRun];
+    int nr = 0;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const bool valid = base + j < T;
+      const bool eq = b1 > 0 && valid && key[j] == tau;
+      sel[j] = valid && b1 > 0 && (key[j] > tau || (eq && eq_rank < need));
+      eq_rank += eq ? 1 : 0;
+      nr += (valid && !sel[j]) ? 1 : 0;
+    }
     int r_tot;
-    const int rrank = block_prefix((valid && !sel) ? 1 : 0, &r_tot);
-    if (valid) {
-      s1[p] = sel ? 1 : 0;
-      if (sel) sc[p] = -1.0f;
-      else if (nrest + rrank < T - b1) rows2[nrest + rrank] = p;
+    int rrank = nrest + block_scan_add<kStageThreads>(nr, &r_tot);
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const int p = base + j;
+      if (p < T) {
+        s1[p] = sel[j] ? 1 : 0;
+        if (sel[j]) sc[p] = -1.0f;
+        else {
+          if (rrank < T - b1) rows2[rrank] = p;
+          ++rrank;
+        }
+      }
     }
     nrest += r_tot;
   }
@@ -228,9 +254,9 @@ __global__ __launch_bounds__(256) void ckv_project_kernel(const float* __restric
 }
 
 // ------------------------------------------------------------------ stage 2
-__global__ __launch_bounds__(256) void ckv_stage2_kernel(int T, int b1, int b2, CkvWs w,
-                                                         const float* __restrict__ score2,
-                                                         int32_t* __restrict__ idx) {
+__global__ __launch_bounds__(kStageThreads) void ckv_stage2_kernel(int T, int b1, int b2, CkvWs w,
+                                                                   const float* __restrict__ score2,
+                                                                   int32_t* __restrict__ idx) {
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
   const uint8_t* s1 = w.s1 + static_cast<int64_t>(h) * T;
@@ -238,7 +264,7 @@ __global__ __launch_bounds__(256) void ckv_stage2_kernel(int T, int b1, int b2, 
   uint32_t tau = 0xFFFFFFFFu;
   int need = 0;
   if (b2 > 0) {
-    block_radix_topm(T, b2, [&](int i, uint32_t* key) {
+    block_radix_topm<kStageThreads>(T, b2, [&](int i, uint32_t* key) {
       if (s1[i]) return false;
       *key = float_key(sc[i]);
       return true;
@@ -246,23 +272,40 @@ __global__ __launch_bounds__(256) void ckv_stage2_kernel(int T, int b1, int b2, 
   }
   int eq_seen = 0, nsel = 0;
   int32_t* out = idx + static_cast<int64_t>(h) * (b1 + b2);
-  for (int p0 = 0; p0 < T; p0 += 256) {
-    const int p = p0 + tid;
-    const bool valid = p < T;
-    bool in1 = false;
-    uint32_t key = 0;
-    if (valid) {
-      in1 = s1[p] != 0;
-      if (!in1) key = float_key(sc[p]);
+  for (int p0 = 0; p0 < T; p0 += kStageThreads * kRun) {
+    const int base = p0 + tid * kRun;
+    uint32_t key[kRun];
+    bool in1[kRun];
+    int neq = 0;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const bool valid = base + j < T;
+      in1[j] = valid && s1[base + j] != 0;
+      key[j] = (valid && !in1[j]) ? float_key(sc[base + j]) : 0u;
+      neq += (b2 > 0 && valid && !in1[j] && key[j] == tau) ? 1 : 0;
     }
-    const int eq = (b2 > 0 && valid && !in1 && key == tau) ? 1 : 0;
     int eq_tot;
-    const int eq_rank = eq_seen + block_prefix(eq, &eq_tot);
+    int eq_rank = eq_seen + block_scan_add<kStageThreads>(neq, &eq_tot);
     eq_seen += eq_tot;
-    const bool sel = valid && (in1 || (b2 > 0 && (key > tau || (eq && eq_rank < need))));
+    bool sel[kRun];
+    int ns = 0;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const bool valid = base + j < T;
+      const bool eq = b2 > 0 && valid && !in1[j] && key[j] == tau;
+      sel[j] = valid && (in1[j] || (b2 > 0 && (key[j] > tau || (eq && eq_rank < need))));
+      eq_rank += eq ? 1 : 0;
+      ns += sel[j] ? 1 : 0;
+    }
     int s_tot;
-    const int rank = block_prefix(sel ? 1 : 0, &s_tot);
-    if (sel && nsel + rank < b1 + b2) out[nsel + rank] = p;
+    int rank = nsel + block_scan_add<kStageThreads>(ns, &s_tot);
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      if (sel[j]) {
+        if (rank < b1 + b2) out[rank] = base + j;
+        ++rank;
+      }
+    }
     nsel += s_tot;
   }
 }
@@ -273,7 +316,7 @@ hipError_t launch_criticalkv(const float* A, const uint16_t* V, const uint16_t* 
   if (d != kCkvD || hidden % kBN != 0) return hipErrorInvalidValue;
   CkvWs w = carve(ws, H, T);
   float* sc = score2 ? score2 : w.score2;
-  ckv_stage1_kernel<<<H, 256, 0, stream>>>(A, T, b1, w, sc);
+  ckv_stage1_kernel<<<H, kStageThreads, 0, stream>>>(A, T, b1, w, sc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nrows = T - b1;
@@ -283,7 +326,7 @@ hipError_t launch_criticalkv(const float* A, const uint16_t* V, const uint16_t* 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  ckv_stage2_kernel<<<H, 256, 0, stream>>>(T, b1, b2, w, sc, idx);
+  ckv_stage2_kernel<<<H, kStageThreads, 0, stream>>>(T, b1, b2, w, sc, idx);
   return hipGetLastError();
 }
 

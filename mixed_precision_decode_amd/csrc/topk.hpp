@@ -1,5 +1,5 @@
-// Block-wide (256 threads) top-m selection by (key descending, index
-// ascending) with 32-bit order-preserving keys, and block prefix sums.
+// Block-wide top-m selection by (key descending, index ascending) with
+// 32-bit order-preserving keys, and block prefix sums.
 #pragma once
 
 #include "common.hpp"
@@ -22,34 +22,73 @@ __device__ __forceinline__ int block_prefix(int flag, int* total) {
   return off + in_wave;
 }
 
+// Exclusive prefix sum of an int over the block (NT threads), in thread
+// order. Every thread must call it; *total receives the block sum.
+template <int NT>
+__device__ __forceinline__ int block_scan_add(int v, int* total) {
+  constexpr int NWV = NT / kWave;
+  __shared__ int s_w[NWV];
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) s_w[w] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) {
+    off += (i < w) ? s_w[i] : 0;
+    tot += s_w[i];
+  }
+  *total = tot;
+  __syncthreads();
+  return off + incl - v;
+}
+
 // Radix select (4 passes of 8 bits, most significant first) of the m-th
 // largest key among the elements i in [0, n) for which keyfn(i, &key) is
-// true. On return, on every thread: *tau is that key and *need the number of
-// elements equal to *tau that belong to the top m (the lowest-index ones);
-// elements with key > *tau all belong to it. Requires 1 <= m <= count.
-template <class KeyFn>
+// true, by a block of NT threads. On return, on every thread: *tau is that
+// key and *need the number of elements equal to *tau that belong to the top
+// m (the lowest-index ones); elements with key > *tau all belong to it.
+// Requires 1 <= m <= count. Each wave counts into its own histogram (keys
+// such as probabilities share few top bytes, so one shared histogram
+// serialises the atomics); the histograms are summed before the digit search.
+template <int NT = 256, class KeyFn>
 __device__ void block_radix_topm(int n, int m, KeyFn keyfn, uint32_t* tau, int* need) {
-  __shared__ uint32_t hist[256];
+  constexpr int NWV = NT / kWave;
+  __shared__ uint32_t hist[NWV][256];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wv = tid / kWave;
   uint32_t prefix = 0, mask = 0;
   int nd = m;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    for (int i = tid; i < NWV * 256; i += NT) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += 256) {
+    for (int i = tid; i < n; i += NT) {
       uint32_t key;
-      if (keyfn(i, &key) && (key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xFFu], 1u);
+      if (keyfn(i, &key) && (key & mask) == prefix) atomicAdd(&hist[wv][(key >> shift) & 0xFFu], 1u);
     }
     __syncthreads();
+    if (NWV > 1) {
+      for (int dg = tid; dg < 256; dg += NT) {
+        uint32_t t = hist[0][dg];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) t += hist[w][dg];
+        hist[0][dg] = t;
+      }
+      __syncthreads();
+    }
     if (tid < kWave) {
       // lane owns digits 255-4*lane .. 252-4*lane (descending); find the
       // first digit (from the top) where the running count reaches nd.
       int c[4];
       int sum = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { c[j] = static_cast<int>(hist[255 - 4 * tid - j]); sum += c[j]; }
+      for (int j = 0; j < 4; ++j) { c[j] = static_cast<int>(hist[0][255 - 4 * tid - j]); sum += c[j]; }
       // inclusive scan of lane sums across the wave
       int incl = sum;
 #pragma unroll
