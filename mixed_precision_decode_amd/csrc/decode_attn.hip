@@ -674,10 +674,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
   // (block i to XCD i mod 8), so with the split index outermost every XCD
   // sees consecutive (unit, tile) pairs of every split: the same mix of
   // FP16 and low-bit splits, instead of XCDs that hold only one tier's
-  // splits and finish at different times.
+  // splits and finish at different times. The low-bit splits, which take
+  // longer, are dispatched first: the wave scheduler favours older waves.
   const int S = p.S16 + p.Sq;
   const int ut = p.units * p.tiles;
-  const int split = blockIdx.x / ut;
+  const int sd = blockIdx.x / ut;
+  const int split = (sd < p.Sq) ? p.S16 + sd : sd - p.Sq;
   const int rest = blockIdx.x % ut;
   const int tile = rest % p.tiles;
   const int unit = rest / p.tiles;
