@@ -655,15 +655,36 @@ __device__ __forceinline__ void fp16_split(const DecodeK& p, int unit, int n, in
       }
     }
   };
-  for (int base = 0;;) {
-    load(base + BATCH, B);
-    step(A, base);
-    base += BATCH;
-    if (base >= ns) break;
-    load(base + BATCH, A);
-    step(B, base);
-    base += BATCH;
-    if (base >= ns) break;
+  if constexpr (RT == 1) {
+    // three register sets in turn: two batches in flight while one is computed
+    Regs C;
+    load(BATCH, B);
+    for (int base = 0;;) {
+      load(base + 2 * BATCH, C);
+      step(A, base);
+      base += BATCH;
+      if (base >= ns) break;
+      load(base + 2 * BATCH, A);
+      step(B, base);
+      base += BATCH;
+      if (base >= ns) break;
+      load(base + 2 * BATCH, B);
+      step(C, base);
+      base += BATCH;
+      if (base >= ns) break;
+    }
+  } else {
+    // head tiles hold more state: two register sets
+    for (int base = 0;;) {
+      load(base + BATCH, B);
+      step(A, base);
+      base += BATCH;
+      if (base >= ns) break;
+      load(base + BATCH, A);
+      step(B, base);
+      base += BATCH;
+      if (base >= ns) break;
+    }
   }
   write_partial<D, RT, LPT, CPL>(st, red, sm, sM, po, pml);
 }
