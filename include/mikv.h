@@ -214,7 +214,9 @@ typedef struct {
  *   demoted_pos is ignored.
  * ws: mikv_h2o_workspace(dims, max_T) bytes (any contents; decode mode
  * needs none and accepts ws == NULL).
- * Errors: T < B -> MIKV_ERR_SHAPE; low-bit tier overflow -> MIKV_ERR_CAPACITY.
+ * Errors: T < B -> MIKV_ERR_SHAPE; src->k, src->v or a non-NULL src->b not
+ * 16-byte aligned -> MIKV_ERR_SHAPE; low-bit tier overflow ->
+ * MIKV_ERR_CAPACITY.
  */
 size_t mikv_h2o_workspace(const mikv_dims* dims, int32_t max_T);
 mikv_status mikv_h2o_update_select(const mikv_dims* dims,

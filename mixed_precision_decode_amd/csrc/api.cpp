@@ -219,7 +219,8 @@ mikv_status mikv_h2o_update_select(const mikv_dims* m, const mikv_cache* c, int3
   }
   if (src->T != len || len < B) return MIKV_ERR_SHAPE;
   if (len > 0 && (!src->k || !src->v || !src->acc0)) return MIKV_ERR_NULL;
-  if (len > 0 && (!aligned16(src->k) || !aligned16(src->v))) return MIKV_ERR_SHAPE;
+  if (len > 0 && (!aligned16(src->k) || !aligned16(src->v) || (src->b && !aligned16(src->b))))
+    return MIKV_ERR_SHAPE;
   if (len - B > m->capq) return MIKV_ERR_CAPACITY;
   const size_t need = h2o_ws_bytes(m->batch, m->hkv, len);
   if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;

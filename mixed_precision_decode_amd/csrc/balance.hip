@@ -63,19 +63,45 @@ __global__ __launch_bounds__(256) void balance_partial_kernel(const uint16_t* __
   }
 }
 
+// One block per (sequence, kv head): 1024 / D groups of threads take
+// interleaved chunk subsets, with several loads in flight per thread, and
+// combine through LDS (a long prompt has hundreds of chunks).
+constexpr int kFinThreads = 1024;
 template <int D>
-__global__ void balance_finalize_kernel(const float* __restrict__ part, int units, int nqc,
-                                        int nkc, float* __restrict__ b) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= units * D) return;
-  const int unit = i / D, c = i % D;
+__global__ __launch_bounds__(kFinThreads) void balance_finalize_kernel(const float* __restrict__ part,
+                                                                      int units, int nqc, int nkc,
+                                                                      float* __restrict__ b) {
+  constexpr int NG = kFinThreads / D;
+  __shared__ float red[2][NG][D];
+  const int unit = blockIdx.x;
+  const int c = threadIdx.x % D, grp = threadIdx.x / D;
   const float* p = part + static_cast<int64_t>(unit) * (nqc + nkc) * D + c;
-  float mq = 0.0f, mk = 0.0f;
-  for (int j = 0; j < nqc; ++j) mq = fmaxf(mq, p[static_cast<int64_t>(j) * D]);
-  for (int j = 0; j < nkc; ++j) mk = fmaxf(mk, p[static_cast<int64_t>(nqc + j) * D]);
-  float r = 1.0f;
-  if (mq != 0.0f && mk != 0.0f) r = sqrtf(mq / mk);
-  b[i] = r;
+  auto chunk_max = [&](int j0, int j1) {
+    float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f, m3 = 0.0f;
+    int j = j0 + grp;
+    for (; j + 3 * NG < j1; j += 4 * NG) {
+      m0 = fmaxf(m0, p[static_cast<int64_t>(j) * D]);
+      m1 = fmaxf(m1, p[static_cast<int64_t>(j + NG) * D]);
+      m2 = fmaxf(m2, p[static_cast<int64_t>(j + 2 * NG) * D]);
+      m3 = fmaxf(m3, p[static_cast<int64_t>(j + 3 * NG) * D]);
+    }
+    for (; j < j1; j += NG) m0 = fmaxf(m0, p[static_cast<int64_t>(j) * D]);
+    return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  };
+  red[0][grp][c] = chunk_max(0, nqc);
+  red[1][grp][c] = chunk_max(nqc, nqc + nkc);
+  __syncthreads();
+  if (grp == 0) {
+    float mq = 0.0f, mk = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      mq = fmaxf(mq, red[0][i][c]);
+      mk = fmaxf(mk, red[1][i][c]);
+    }
+    float r = 1.0f;
+    if (mq != 0.0f && mk != 0.0f) r = sqrtf(mq / mk);
+    b[static_cast<int64_t>(unit) * D + c] = r;
+  }
 }
 
 template <int D>
@@ -123,7 +149,7 @@ static hipError_t launch_bal(int batch, int hq, int hkv, int T, const uint16_t* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  balance_finalize_kernel<D><<<ceil_div(units * D, 256), 256, 0, stream>>>(part, units, nqc, nkc, b);
+  balance_finalize_kernel<D><<<units, kFinThreads, 0, stream>>>(part, units, nqc, nkc, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (kb && T > 0) {

@@ -74,7 +74,14 @@ __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
 }
 
 // ------------------------------------------------------------------ prefill
-__global__ __launch_bounds__(256) void h2o_prefill_select_kernel(H2OArgs a, int T, int32_t* map) {
+// One block of kSelThreads per (sequence, kv head). After the radix select,
+// positions are visited in chunks of kSelThreads * kSelRun; each thread takes
+// kSelRun consecutive positions, so a chunk costs two block scans (ties, then
+// the kept positions).
+constexpr int kSelThreads = 1024;
+constexpr int kSelRun = 8;
+
+__global__ __launch_bounds__(kSelThreads) void h2o_prefill_select_kernel(H2OArgs a, int T, int32_t* map) {
   const int unit = blockIdx.x;
   const int tid = threadIdx.x;
   const float* acc0 = a.src_acc0 + static_cast<int64_t>(unit) * T;
@@ -84,54 +91,68 @@ __global__ __launch_bounds__(256) void h2o_prefill_select_kernel(H2OArgs a, int 
   uint32_t tau = 0xFFFFFFFFu;
   int need = 0;
   if (H > 0) {
-    block_radix_topm(ncand, H, [&](int i, uint32_t* key) {
+    block_radix_topm<kSelThreads>(ncand, H, [&](int i, uint32_t* key) {
       *key = float_key(acc0[i]);
       return true;
     }, &tau, &need);
   }
   // ascending-position slot assignment in both tiers
-  int eq_seen = 0, kept = 0, dropped = 0;
+  int eq_seen = 0, kept = 0;
   const int64_t base16 = static_cast<int64_t>(unit) * a.cap16;
   const int64_t baseq = static_cast<int64_t>(unit) * a.capq;
-  for (int p0 = 0; p0 < T; p0 += 256) {
-    const int p = p0 + tid;
-    const bool valid = p < T;
-    const bool cand = valid && p < ncand;
-    uint32_t key = 0;
-    float av = 0.0f;
-    if (valid) { av = acc0[p]; key = float_key(av); }
-    const int eq = (H > 0 && cand && key == tau) ? 1 : 0;
+  int32_t* umap = map + static_cast<int64_t>(unit) * T;
+  for (int p0 = 0; p0 < T; p0 += kSelThreads * kSelRun) {
+    const int base = p0 + tid * kSelRun;
+    float av[kSelRun];
+    uint32_t key[kSelRun];
+    int neq = 0;
+#pragma unroll
+    for (int j = 0; j < kSelRun; ++j) {
+      const int p = base + j;
+      av[j] = (p < T) ? acc0[p] : 0.0f;
+      key[j] = float_key(av[j]);
+      neq += (H > 0 && p < ncand && key[j] == tau) ? 1 : 0;
+    }
     int eq_tot;
-    const int eq_rank = eq_seen + block_prefix(eq, &eq_tot);
+    int eq_rank = eq_seen + block_scan_add<kSelThreads>(neq, &eq_tot);
     eq_seen += eq_tot;
-    bool keep = false;
-    if (valid) {
-      if (!cand) keep = true;
-      else if (H > 0 && (key > tau || (eq && eq_rank < need))) keep = true;
+    bool keep[kSelRun];
+    int nk = 0;
+#pragma unroll
+    for (int j = 0; j < kSelRun; ++j) {
+      const int p = base + j;
+      const bool cand = p < ncand;
+      const bool eq = H > 0 && cand && key[j] == tau;
+      keep[j] = p < T && (!cand || (H > 0 && (key[j] > tau || (eq && eq_rank < need))));
+      eq_rank += eq ? 1 : 0;
+      nk += keep[j] ? 1 : 0;
     }
     int k_tot;
-    const int krank = block_prefix(keep ? 1 : 0, &k_tot);
+    int krank = kept + block_scan_add<kSelThreads>(nk, &k_tot);
     // slots are bounds-checked so that a selection error can only show up
     // as a wrong result (map entry INT_MIN = not stored)
-    if (valid) {
-      if (keep) {
-        const int slot = kept + krank;
-        const bool ok = slot < a.cap16 - 1;
-        if (ok) {
-          a.pos16[base16 + slot] = p;
-          a.acc16[base16 + slot] = av;
+#pragma unroll
+    for (int j = 0; j < kSelRun; ++j) {
+      const int p = base + j;
+      if (p < T) {
+        if (keep[j]) {
+          const int slot = krank++;
+          const bool ok = slot < a.cap16 - 1;
+          if (ok) {
+            a.pos16[base16 + slot] = p;
+            a.acc16[base16 + slot] = av[j];
+          }
+          umap[p] = ok ? slot : INT_MIN;
+        } else {
+          // positions before p that were not kept
+          const int slot = p - krank;
+          const bool ok = slot < a.capq;
+          if (ok) a.posq[baseq + slot] = p;
+          umap[p] = ok ? -1 - slot : INT_MIN;
         }
-        map[static_cast<int64_t>(unit) * T + p] = ok ? slot : INT_MIN;
-      } else {
-        const int slot = dropped + (p - p0 - krank);
-        const bool ok = slot < a.capq;
-        if (ok) a.posq[baseq + slot] = p;
-        map[static_cast<int64_t>(unit) * T + p] = ok ? -1 - slot : INT_MIN;
       }
     }
-    const int nvalid = min(256, T - p0);
     kept += k_tot;
-    dropped += nvalid - k_tot;
   }
   if (tid == 0) {
     a.free16[unit] = a.cap16 - 1;
@@ -140,12 +161,18 @@ __global__ __launch_bounds__(256) void h2o_prefill_select_kernel(H2OArgs a, int 
   }
   // the free slot's rows start as zeros: decode reads them (masked), so they
   // must hold finite values
-  for (int i = tid; i < a.d / 8; i += 256) {
+  for (int i = tid; i < a.d / 8; i += kSelThreads) {
     const int64_t o = (base16 + a.cap16 - 1) * a.d + 8 * i;
     *reinterpret_cast<uint4*>(a.k16 + o) = make_uint4(0u, 0u, 0u, 0u);
     *reinterpret_cast<uint4*>(a.v16 + o) = make_uint4(0u, 0u, 0u, 0u);
   }
 }
+
+#ifndef MIKV_SCATTER_BLOCKS
+#define MIKV_SCATTER_BLOCKS 2048
+#endif
+// resident-sized grid: 8 blocks of 256 threads on each of the 256 compute units
+constexpr int64_t kScatterBlocks = MIKV_SCATTER_BLOCKS;
 
 template <int D, int BITS, int NL>
 __global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int T,
@@ -157,32 +184,62 @@ __global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int
   const int lane = threadIdx.x % LPR;
   const int64_t n_rows = static_cast<int64_t>(a.batch) * a.hkv * T;
   const int64_t step = static_cast<int64_t>(gridDim.x) * RPB;
-  for (int64_t r = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR; r < n_rows; r += step) {
+  int64_t r = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR;
+  if (r >= n_rows) return;
+  // grid-stride over rows with the next row's loads issued before the
+  // current row is quantized and stored
+  // the balancer slice of a row's unit (8 channels of the lane), or ones
+  const bool bal = a.src_b != nullptr;
+  auto load_b = [&](int64_t row, float4& b0, float4& b1) {
+    if (bal) {
+      const float4* bb = reinterpret_cast<const float4*>(a.src_b + (row / T) * D + lane * 8);
+      b0 = bb[0];
+      b1 = bb[1];
+    }
+  };
+  float4 bc0 = make_float4(1.f, 1.f, 1.f, 1.f), bc1 = bc0;
+  uint4 kc = *reinterpret_cast<const uint4*>(a.src_k + r * D + lane * 8);
+  uint4 vc = *reinterpret_cast<const uint4*>(a.src_v + r * D + lane * 8);
+  int sc = map[r];
+  load_b(r, bc0, bc1);
+  for (;;) {
+    const int64_t rn = r + step;
+    const bool more = rn < n_rows;  // the same for every lane of a row
+    uint4 kn = kc, vn = vc;
+    int sn = sc;
+    float4 bn0 = bc0, bn1 = bc1;
+    if (more) {
+      kn = *reinterpret_cast<const uint4*>(a.src_k + rn * D + lane * 8);
+      vn = *reinterpret_cast<const uint4*>(a.src_v + rn * D + lane * 8);
+      sn = map[rn];
+      load_b(rn, bn0, bn1);
+    }
     const int64_t unit = r / T;
-    const int slot = map[r];
     float kx[8], vx[8];
-    load8(a.src_k + r * D + lane * 8, kx);
-    load8(a.src_v + r * D + lane * 8, vx);
-    uint32_t kw[4];
-    if (a.src_b) {
-      const float* bb = a.src_b + unit * D + lane * 8;
+    kx[0] = lo_h(kc.x); kx[1] = hi_h(kc.x); kx[2] = lo_h(kc.y); kx[3] = hi_h(kc.y);
+    kx[4] = lo_h(kc.z); kx[5] = hi_h(kc.z); kx[6] = lo_h(kc.w); kx[7] = hi_h(kc.w);
+    vx[0] = lo_h(vc.x); vx[1] = hi_h(vc.x); vx[2] = lo_h(vc.y); vx[3] = hi_h(vc.y);
+    vx[4] = lo_h(vc.z); vx[5] = hi_h(vc.z); vx[6] = lo_h(vc.w); vx[7] = hi_h(vc.w);
+    uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+    if (bal) {
+      const float bb[8] = {bc0.x, bc0.y, bc0.z, bc0.w, bc1.x, bc1.y, bc1.z, bc1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) kx[i] = h2f(f2h(mul_rn(kx[i], bb[i])));
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      kw[i] = static_cast<uint32_t>(f2h(kx[2 * i])) | (static_cast<uint32_t>(f2h(kx[2 * i + 1])) << 16);
-    // quantize both rows unconditionally (row-uniform control flow for DPP)
-    uint32_t kszw, vszw;
-    const uint32_t kp = quantize8<BITS, NL>(kx, &kszw);
-    const uint32_t vp = quantize8<BITS, NL>(vx, &vszw);
-    if (slot == INT_MIN) continue;
-    if (slot >= 0) {
-      const int64_t o16 = (unit * a.cap16 + slot) * D + lane * 8;
+      for (int i = 0; i < 4; ++i)
+        kw[i] = static_cast<uint32_t>(f2h(kx[2 * i])) | (static_cast<uint32_t>(f2h(kx[2 * i + 1])) << 16);
+    }
+    // sc is the same on every lane of a row and the group reductions of
+    // quantize8 stay inside a row, so the branches keep rows whole
+    if (sc >= 0) {
+      const int64_t o16 = (unit * a.cap16 + sc) * D + lane * 8;
       *reinterpret_cast<uint4*>(a.k16 + o16) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-      *reinterpret_cast<uint4*>(a.v16 + o16) = *reinterpret_cast<const uint4*>(a.src_v + r * D + lane * 8);
-    } else {
-      const int64_t qs = unit * a.capq + (-1 - slot);
+      *reinterpret_cast<uint4*>(a.v16 + o16) = vc;
+    } else if (sc != INT_MIN) {
+      uint32_t kszw, vszw;
+      const uint32_t kp = quantize8<BITS, NL>(kx, &kszw);
+      const uint32_t vp = quantize8<BITS, NL>(vx, &vszw);
+      const int64_t qs = unit * a.capq + (-1 - sc);
       store_codes8<BITS>(a.kq + qs * CB, lane, kp);
       store_codes8<BITS>(a.vq + qs * CB, lane, vp);
       if (lane % NL == 0) {
@@ -190,6 +247,13 @@ __global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int
         reinterpret_cast<uint32_t*>(a.vsz)[qs * GPT + lane / NL] = vszw;
       }
     }
+    if (!more) break;
+    r = rn;
+    kc = kn;
+    vc = vn;
+    sc = sn;
+    bc0 = bn0;
+    bc1 = bn1;
   }
 }
 
@@ -207,13 +271,13 @@ template <int D, int BITS, int NL>
 static hipError_t launch_pre(const H2OArgs& a, hipStream_t stream) {
   const int T = a.len;
   int32_t* map = static_cast<int32_t*>(a.ws);
-  h2o_prefill_select_kernel<<<a.batch * a.hkv, 256, 0, stream>>>(a, T, map);
+  h2o_prefill_select_kernel<<<a.batch * a.hkv, kSelThreads, 0, stream>>>(a, T, map);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || T == 0) return e;
   constexpr int RPB = 256 / (D / 8);
   const int64_t n_rows = static_cast<int64_t>(a.batch) * a.hkv * T;
   int64_t blocks = (n_rows + RPB - 1) / RPB;
-  if (blocks > 65536) blocks = 65536;
+  if (blocks > kScatterBlocks) blocks = kScatterBlocks;
   h2o_prefill_scatter_kernel<D, BITS, NL><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(a, T, map);
   return hipGetLastError();
 }

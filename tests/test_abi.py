@@ -108,6 +108,8 @@ def test_h2o_validation(lib):
     assert pre(40, need - 1) == L.MIKV_ERR_WORKSPACE
     small = L.MikvPrefillSrc(FAKE, FAKE, FAKE, None, 9)
     assert pre(9, need, small) == L.MIKV_ERR_SHAPE  # T < B
+    mis_b = L.MikvPrefillSrc(FAKE, FAKE, FAKE, FAKE + 4, 40)
+    assert pre(40, need, mis_b) == L.MIKV_ERR_SHAPE  # balancer not 16-byte aligned
     tight = _dims(capq=20)
     assert lib.mikv_h2o_update_select(C.byref(tight.c()), C.byref(c), 40, 4, 6, None,
                                       C.byref(src), None, FAKE, need, None) == L.MIKV_ERR_CAPACITY

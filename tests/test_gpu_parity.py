@@ -145,6 +145,9 @@ def _state_equal(gpu, ref, n16=None, nq=None):
     ("tiny", dict(recent=51), True),                # heavy = 0
     ("gqa_throughput", dict(batch=2, T=700), True),
     ("llama3_8b_32k", dict(hq=8, hkv=2, T=3000), True),
+    # more rows than the scatter grid holds threads: rows loop with prefetch
+    ("gqa_throughput", dict(batch=8, T=700), True),
+    ("tiny", dict(batch=64, T=2500), True),
 ])
 def test_prefill_build_parity(name, over, balanced):
     cfg = S.CONFIGS[name].scaled(**over)
