@@ -169,9 +169,9 @@ __global__ __launch_bounds__(kSelThreads) void h2o_prefill_select_kernel(H2OArgs
 }
 
 #ifndef MIKV_SCATTER_BLOCKS
-#define MIKV_SCATTER_BLOCKS 2048
+#define MIKV_SCATTER_BLOCKS 4096
 #endif
-// resident-sized grid: 8 blocks of 256 threads on each of the 256 compute units
+// 16 blocks of 256 threads per compute unit (measured best among 1024-65536)
 constexpr int64_t kScatterBlocks = MIKV_SCATTER_BLOCKS;
 
 template <int D, int BITS, int NL>
@@ -184,62 +184,63 @@ __global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int
   const int lane = threadIdx.x % LPR;
   const int64_t n_rows = static_cast<int64_t>(a.batch) * a.hkv * T;
   const int64_t step = static_cast<int64_t>(gridDim.x) * RPB;
-  int64_t r = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR;
-  if (r >= n_rows) return;
-  // grid-stride over rows with the next row's loads issued before the
-  // current row is quantized and stored
-  // the balancer slice of a row's unit (8 channels of the lane), or ones
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / LPR;
+  if (r0 >= n_rows) return;
   const bool bal = a.src_b != nullptr;
-  auto load_b = [&](int64_t row, float4& b0, float4& b1) {
-    if (bal) {
-      const float4* bb = reinterpret_cast<const float4*>(a.src_b + (row / T) * D + lane * 8);
-      b0 = bb[0];
-      b1 = bb[1];
+  // a row is tracked as (row, unit, position); the grid stride advances all
+  // three without a division per row
+  const int64_t su = step / T;
+  const int sr = static_cast<int>(step % T);
+  auto advance = [&](int64_t& r, int64_t& u, int& t) {
+    r += step;
+    u += su;
+    t += sr;
+    if (t >= T) {
+      t -= T;
+      ++u;
     }
   };
-  float4 bc0 = make_float4(1.f, 1.f, 1.f, 1.f), bc1 = bc0;
-  uint4 kc = *reinterpret_cast<const uint4*>(a.src_k + r * D + lane * 8);
-  uint4 vc = *reinterpret_cast<const uint4*>(a.src_v + r * D + lane * 8);
-  int sc = map[r];
-  load_b(r, bc0, bc1);
-  for (;;) {
-    const int64_t rn = r + step;
-    const bool more = rn < n_rows;  // the same for every lane of a row
-    uint4 kn = kc, vn = vc;
-    int sn = sc;
-    float4 bn0 = bc0, bn1 = bc1;
-    if (more) {
-      kn = *reinterpret_cast<const uint4*>(a.src_k + rn * D + lane * 8);
-      vn = *reinterpret_cast<const uint4*>(a.src_v + rn * D + lane * 8);
-      sn = map[rn];
-      load_b(rn, bn0, bn1);
-    }
-    const int64_t unit = r / T;
-    float kx[8], vx[8];
-    kx[0] = lo_h(kc.x); kx[1] = hi_h(kc.x); kx[2] = lo_h(kc.y); kx[3] = hi_h(kc.y);
-    kx[4] = lo_h(kc.z); kx[5] = hi_h(kc.z); kx[6] = lo_h(kc.w); kx[7] = hi_h(kc.w);
-    vx[0] = lo_h(vc.x); vx[1] = hi_h(vc.x); vx[2] = lo_h(vc.y); vx[3] = hi_h(vc.y);
-    vx[4] = lo_h(vc.z); vx[5] = hi_h(vc.z); vx[6] = lo_h(vc.w); vx[7] = hi_h(vc.w);
-    uint32_t kw[4] = {kc.x, kc.y, kc.z, kc.w};
+  struct Row {
+    uint4 k, v;
+    float4 b0, b1;
+    int s;
+  };
+  auto load = [&](int64_t r, int64_t u, Row& R) {
+    R.k = *reinterpret_cast<const uint4*>(a.src_k + r * D + lane * 8);
+    R.v = *reinterpret_cast<const uint4*>(a.src_v + r * D + lane * 8);
+    R.s = map[r];
     if (bal) {
-      const float bb[8] = {bc0.x, bc0.y, bc0.z, bc0.w, bc1.x, bc1.y, bc1.z, bc1.w};
+      const float4* bb = reinterpret_cast<const float4*>(a.src_b + u * D + lane * 8);
+      R.b0 = bb[0];
+      R.b1 = bb[1];
+    }
+  };
+  auto process = [&](int64_t unit, const Row& R) {
+    float kx[8], vx[8];
+    kx[0] = lo_h(R.k.x); kx[1] = hi_h(R.k.x); kx[2] = lo_h(R.k.y); kx[3] = hi_h(R.k.y);
+    kx[4] = lo_h(R.k.z); kx[5] = hi_h(R.k.z); kx[6] = lo_h(R.k.w); kx[7] = hi_h(R.k.w);
+    vx[0] = lo_h(R.v.x); vx[1] = hi_h(R.v.x); vx[2] = lo_h(R.v.y); vx[3] = hi_h(R.v.y);
+    vx[4] = lo_h(R.v.z); vx[5] = hi_h(R.v.z); vx[6] = lo_h(R.v.w); vx[7] = hi_h(R.v.w);
+    uint32_t kw[4] = {R.k.x, R.k.y, R.k.z, R.k.w};
+    if (bal) {
+      const float bb[8] = {R.b0.x, R.b0.y, R.b0.z, R.b0.w, R.b1.x, R.b1.y, R.b1.z, R.b1.w};
 #pragma unroll
       for (int i = 0; i < 8; ++i) kx[i] = h2f(f2h(mul_rn(kx[i], bb[i])));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         kw[i] = static_cast<uint32_t>(f2h(kx[2 * i])) | (static_cast<uint32_t>(f2h(kx[2 * i + 1])) << 16);
     }
-    // sc is the same on every lane of a row and the group reductions of
+    // R.s is the same on every lane of a row and the group reductions of
     // quantize8 stay inside a row, so the branches keep rows whole
-    if (sc >= 0) {
-      const int64_t o16 = (unit * a.cap16 + sc) * D + lane * 8;
+    if (R.s >= 0) {
+      const int64_t o16 = (unit * a.cap16 + R.s) * D + lane * 8;
       *reinterpret_cast<uint4*>(a.k16 + o16) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-      *reinterpret_cast<uint4*>(a.v16 + o16) = vc;
-    } else if (sc != INT_MIN) {
+      *reinterpret_cast<uint4*>(a.v16 + o16) = R.v;
+    } else if (R.s != INT_MIN) {
       uint32_t kszw, vszw;
       const uint32_t kp = quantize8<BITS, NL>(kx, &kszw);
       const uint32_t vp = quantize8<BITS, NL>(vx, &vszw);
-      const int64_t qs = unit * a.capq + (-1 - sc);
+      const int64_t qs = unit * a.capq + (-1 - R.s);
       store_codes8<BITS>(a.kq + qs * CB, lane, kp);
       store_codes8<BITS>(a.vq + qs * CB, lane, vp);
       if (lane % NL == 0) {
@@ -247,13 +248,30 @@ __global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int
         reinterpret_cast<uint32_t*>(a.vsz)[qs * GPT + lane / NL] = vszw;
       }
     }
-    if (!more) break;
-    r = rn;
-    kc = kn;
-    vc = vn;
-    sc = sn;
-    bc0 = bn0;
-    bc1 = bn1;
+  };
+  // two register sets in turn: the loads of the next row are in flight
+  // while the current one is processed; past the end a load repeats the
+  // current row (a valid address) and its result is not used
+  int64_t ra = r0, ua = r0 / T;
+  int ta = static_cast<int>(r0 % T);
+  Row A, B;
+  load(ra, ua, A);
+  for (;;) {
+    int64_t rb = ra, ub = ua;
+    int tb = ta;
+    advance(rb, ub, tb);
+    const bool hb = rb < n_rows;  // the same for every lane of a row
+    load(hb ? rb : ra, hb ? ub : ua, B);
+    process(ua, A);
+    if (!hb) break;
+    ra = rb;
+    ua = ub;
+    ta = tb;
+    advance(ra, ua, ta);
+    const bool ha = ra < n_rows;
+    load(ha ? ra : rb, ha ? ua : ub, A);
+    process(ub, B);
+    if (!ha) break;
   }
 }
 
