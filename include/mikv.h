@@ -259,7 +259,9 @@ mikv_status mikv_decode_step(const mikv_dims* dims, const mikv_cache* cache,
  *   idx[h] = S1 u S2 in ascending order.
  * A [H][T] fp32 (>= 0), V [H][T][d] fp16, W_O [H*d][hidden] fp16 (inputs);
  * idx [H][budget] int32, score2 [H][T] fp32 or NULL (outputs).
- * ws: mikv_criticalkv_workspace(H, T, d, hidden) bytes (any contents).
+ * ws: mikv_criticalkv_workspace(H, T, d, hidden) bytes (any contents): the
+ * stage-1 marks and row list, score2 when the caller passes NULL, and a
+ * copy of W_O laid out [H][hidden][d] (H*d*hidden*2 bytes).
  * Requires d == 128, hidden % 128 == 0, 1 <= budget <= T, 0 <= alpha <= 1.
  */
 size_t mikv_criticalkv_workspace(int32_t H, int32_t T, int32_t d,

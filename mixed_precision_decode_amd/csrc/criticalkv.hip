@@ -7,6 +7,8 @@
 // Kernels (one launch each, all on the caller's stream):
 //   stage1  per head: radix top-b1 of A; marks stage-1 entries, writes -1 to
 //           their score2 and the ascending list of the other rows.
+//   wt      W_O rearranged per head as [hidden][d] (d contiguous), so that
+//           every MFMA B operand is a run of 8 consecutive k.
 //   project MFMA GEMM (v_mfma_f32_32x32x16_f16, fp32 accumulation) of the
 //           listed V rows with the head's W_O slice, with the |.| row sum
 //           fused into the epilogue so the [rows x hidden] product is never
@@ -33,6 +35,7 @@ struct CkvWs {
   uint8_t* s1;      // [H][T] stage-1 membership
   int32_t* rows2;   // [H][T - b1] rows outside stage 1, ascending
   float* score2;    // [H][T] used when the caller passes no score2
+  uint16_t* wt;     // [H][hidden][d] W_O,h with the head dim contiguous
 };
 
 static inline size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -45,13 +48,15 @@ static CkvWs carve(void* ws, int H, int T) {
   r.rows2 = reinterpret_cast<int32_t*>(w);
   w += al256(static_cast<size_t>(H) * T * sizeof(int32_t));
   r.score2 = reinterpret_cast<float*>(w);
+  w += al256(static_cast<size_t>(H) * T * sizeof(float));
+  r.wt = reinterpret_cast<uint16_t*>(w);
   return r;
 }
 
 size_t criticalkv_ws_bytes(int H, int T, int d, int hidden) {
-  (void)d; (void)hidden;
   return al256(static_cast<size_t>(H) * T) + al256(static_cast<size_t>(H) * T * sizeof(int32_t)) +
-         al256(static_cast<size_t>(H) * T * sizeof(float));
+         al256(static_cast<size_t>(H) * T * sizeof(float)) +
+         al256(static_cast<size_t>(H) * d * hidden * sizeof(uint16_t));
 }
 
 // ------------------------------------------------------------------ stage 1
@@ -119,21 +124,51 @@ __global__ __launch_bounds__(kStageThreads) void ckv_stage1_kernel(const float* 
   }
 }
 
+// ------------------------------------------------------------------ W_O layout
+// wt[h][n][k] = W_O[h*d + k][n]: one block per (64 columns, head) through an
+// LDS tile [n][k] (row pitch kLdw halves, 16-byte aligned rows).
+__global__ __launch_bounds__(256) void ckv_wt_kernel(const uint16_t* __restrict__ W, int hidden,
+                                                     uint16_t* __restrict__ wt) {
+  __shared__ __attribute__((aligned(16))) uint16_t t[kBN * kLdw];
+  const int h = blockIdx.y, nb = blockIdx.x * kBN;
+  const int tid = threadIdx.x;
+  const uint16_t* src = W + static_cast<int64_t>(h) * kCkvD * hidden + nb;
+#pragma unroll
+  for (int i = 0; i < kCkvD * kBN / (8 * 256); ++i) {
+    const int idx = tid + i * 256;
+    const int k = idx / (kBN / 8), c = (idx % (kBN / 8)) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(k) * hidden + c);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      t[(c + j) * kLdw + k] = static_cast<uint16_t>((j & 1) ? (w4[j / 2] >> 16) : (w4[j / 2] & 0xFFFFu));
+  }
+  __syncthreads();
+  uint16_t* dst = wt + (static_cast<int64_t>(h) * hidden + nb) * kCkvD;
+#pragma unroll
+  for (int i = 0; i < kCkvD * kBN / (8 * 256); ++i) {
+    const int idx = tid + i * 256;
+    const int n = idx / (kCkvD / 8), kc = (idx % (kCkvD / 8)) * 8;
+    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(n) * kCkvD + kc) =
+        *reinterpret_cast<const uint4*>(&t[n * kLdw + kc]);
+  }
+}
+
 // ------------------------------------------------------------------ projection
 // Block: 256 threads = 4 waves; rows [blk*256, blk*256+256) of the head's
 // row list; wave w owns 64 rows = two 32-row MFMA tiles. Hidden columns are
-// walked in steps of 64: the W_O,h tile [128 x 64] is read from global
-// (coalesced), transposed in registers and stored [n][k] in LDS so that every
-// MFMA B operand is one 16-byte LDS read.
+// walked in steps of 64: the wt tile [64 n][128 k] (16 KB, contiguous) is
+// copied into one of two LDS buffers while the other one feeds the MFMAs, so
+// each step needs a single barrier; every MFMA B operand is one 16-byte LDS
+// read.
 // MFMA 32x32x16 operand layout (lane l): A[l%32][8*(l/32) + 0..7],
 // B[8*(l/32) + 0..7][l%32], D register r: row 8*(r/4) + 4*(l/32) + r%4,
 // column l%32.
 __global__ __launch_bounds__(256) void ckv_project_kernel(const float* __restrict__ A,
-                                                              const uint16_t* __restrict__ V,
-                                                              const uint16_t* __restrict__ W, int H,
+                                                              const uint16_t* __restrict__ V, int H,
                                                               int T, int hidden, int nrows, int mt,
                                                               CkvWs w, float* __restrict__ score2) {
-  __shared__ __attribute__((aligned(16))) uint16_t wt[kBN * kLdw];
+  __shared__ __attribute__((aligned(16))) uint16_t wbuf[2][kBN * kLdw];
   int head, tile;
   if (H % 8 == 0) {
     // keep every block of a head on one XCD (blocks go round-robin over 8)
@@ -148,7 +183,27 @@ __global__ __launch_bounds__(256) void ckv_project_kernel(const float* __restric
   const int wave = tid / kWave, lane = tid % kWave;
   const int32_t* rows2 = w.rows2 + static_cast<int64_t>(head) * nrows;
   const uint16_t* Vh = V + static_cast<int64_t>(head) * T * kCkvD;
-  const uint16_t* Wh = W + static_cast<int64_t>(head) * kCkvD * hidden;
+  const uint16_t* Wh = w.wt + static_cast<int64_t>(head) * hidden * kCkvD;
+
+  // wt tile copy: thread covers row n = tid / 4, k = 32 * (tid % 4) .. +31
+  const int ln = tid / 4, lk = (tid % 4) * 32;
+  uint4 w0, w1, w2, w3;
+  auto load_w = [&](int nb) {
+    const uint4* src = reinterpret_cast<const uint4*>(Wh + static_cast<int64_t>(nb + ln) * kCkvD + lk);
+    w0 = src[0];
+    w1 = src[1];
+    w2 = src[2];
+    w3 = src[3];
+  };
+  auto store_w = [&](int buf) {
+    uint4* dst = reinterpret_cast<uint4*>(&wbuf[buf][ln * kLdw + lk]);
+    dst[0] = w0;
+    dst[1] = w1;
+    dst[2] = w2;
+    dst[3] = w3;
+  };
+  const int nsteps = hidden / kBN;
+  load_w(0);
 
   // A operands: two 32-row tiles x 8 k-steps, held for the whole kernel
   half8 afrag[2][8];
@@ -173,38 +228,11 @@ __global__ __launch_bounds__(256) void ckv_project_kernel(const float* __restric
 #pragma unroll
     for (int r = 0; r < 16; ++r) rsum[mi][r] = 0.0f;
 
-  // W tile loader: thread covers k rows k0..k0+3 and columns n0..n0+7
-  const int lk0 = (tid / 8) * 4;
-  const int ln0 = (tid % 8) * 8;
-  uint4 wreg[4];
-  auto load_w = [&](int nb) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      wreg[kk] = *reinterpret_cast<const uint4*>(Wh + static_cast<int64_t>(lk0 + kk) * hidden + nb + ln0);
-  };
-  const int nsteps = hidden / kBN;
-  load_w(0);
+  store_w(0);
+  if (nsteps > 1) load_w(kBN);
+  __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
-    __syncthreads();  // previous tile fully consumed
-    {
-      // transpose 4(k) x 8(n) halves -> for each n, 4 consecutive k (8 bytes)
-      const uint32_t* r32 = reinterpret_cast<const uint32_t*>(wreg);
-#pragma unroll
-      for (int nn = 0; nn < 8; ++nn) {
-        uint32_t h[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t word = r32[kk * 4 + nn / 2];
-          h[kk] = (nn & 1) ? (word >> 16) : (word & 0xFFFFu);
-        }
-        uint2 v;
-        v.x = h[0] | (h[1] << 16);
-        v.y = h[2] | (h[3] << 16);
-        *reinterpret_cast<uint2*>(&wt[(ln0 + nn) * kLdw + lk0]) = v;
-      }
-    }
-    __syncthreads();
-    if (step + 1 < nsteps) load_w((step + 1) * kBN);
+    const uint16_t* wt = wbuf[step & 1];
     // four independent accumulator chains: 2 row tiles x 2 column tiles
     floatx16 c00 = {}, c10 = {}, c01 = {}, c11 = {};
 #pragma unroll
@@ -222,6 +250,13 @@ __global__ __launch_bounds__(256) void ckv_project_kernel(const float* __restric
       rsum[0][r] += fabsf(c00[r]) + fabsf(c01[r]);
       rsum[1][r] += fabsf(c10[r]) + fabsf(c11[r]);
     }
+    // the next tile goes into the other buffer, which every wave finished
+    // reading before the previous barrier
+    if (step + 1 < nsteps) {
+      store_w((step + 1) & 1);
+      if (step + 2 < nsteps) load_w((step + 2) * kBN);
+    }
+    __syncthreads();
   }
   // reduce over the 32 columns held by lanes with equal lane/32
 #pragma unroll
@@ -321,8 +356,11 @@ hipError_t launch_criticalkv(const float* A, const uint16_t* V, const uint16_t* 
   if (e != hipSuccess) return e;
   const int nrows = T - b1;
   if (nrows > 0) {
+    ckv_wt_kernel<<<dim3(hidden / kBN, H), 256, 0, stream>>>(W, hidden, w.wt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const int mt = (nrows + kBM - 1) / kBM;
-    ckv_project_kernel<<<H * mt, 256, 0, stream>>>(A, V, W, H, T, hidden, nrows, mt, w, sc);
+    ckv_project_kernel<<<H * mt, 256, 0, stream>>>(A, V, H, T, hidden, nrows, mt, w, sc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
