@@ -188,7 +188,7 @@ def bench_criticalkv(args, log):
                        "context": cfg.T, "budget": budget, "alpha": cfg.alpha},
             "roofline": {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12, "peak": 2500.0,
                          "unit": "TFLOP/s", "frac": flops / (ms * 1e-3) / 1e12 / 2500.0,
-                         "flops_per_call": flops, "kernel": "mikv_criticalkv_select (stage 1 + projection + stage 2)"},
+                         "flops_per_call": flops, "kernel": "mikv_criticalkv_select (stage 1 + W_O layout pass + projection + stage 2)"},
             "context": "the pages report about 0.06 s added TTFT at 32K, batch 1 (hardware not given)",
             "cpu_baseline": cpu}
 

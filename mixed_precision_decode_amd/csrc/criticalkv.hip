@@ -233,6 +233,9 @@ __global__ __launch_bounds__(256) void ckv_project_kernel(const float* __restric
   __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
     const uint16_t* wt = wbuf[step & 1];
+    // the MFMA phase runs at raised wave priority: the SIMD's arbiter issues
+    // it ahead of the other resident wave's epilogue and tile copy
+    __builtin_amdgcn_s_setprio(1);
     // four independent accumulator chains: 2 row tiles x 2 column tiles
     floatx16 c00 = {}, c10 = {}, c01 = {}, c11 = {};
 #pragma unroll
@@ -245,6 +248,7 @@ __global__ __launch_bounds__(256) void ckv_project_kernel(const float* __restric
       c01 = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[0][ks], b1, c01, 0, 0, 0);
       c11 = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag[1][ks], b1, c11, 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       rsum[0][r] += fabsf(c00[r]) + fabsf(c01[r]);
