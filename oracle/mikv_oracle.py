@@ -40,7 +40,8 @@ design notes of the repository):
 
 Parity unpinned (conventions of this repository, not fixed by the pages):
   the bit layout of packed codes, the rounding of the budget split, and the
-  synthetic prefill scores acc0.
+  synthetic prefill scores acc0 that the decode parity cases start from
+  (prefill_scores computes acc0 from q and k; it is pinned by its tests).
 """
 from __future__ import annotations
 
@@ -50,7 +51,7 @@ __all__ = [
     "balance", "balance_keys", "quantize_rows", "pack_codes", "unpack_codes",
     "dequantize_rows", "top_by_key", "prefill_build", "decode_attention",
     "h2o_accumulate", "select_drop", "demote", "decode_step",
-    "projected_value_l1", "criticalkv_select", "empty_state",
+    "projected_value_l1", "criticalkv_select", "empty_state", "prefill_scores",
 ]
 
 F16, F32, F64 = np.float16, np.float32, np.float64
@@ -304,6 +305,34 @@ def decode_attention(state, N, q, k_new, v_new, b):
                 p16[i, g] += p[:cap16]
                 pq[i, g] += p[cap16:]
     return o, p16, pq, st
+
+
+def prefill_scores(q, k):
+    """Heavy-hitter scores of the prompt tokens (acc0), float64.
+
+    [paperlayer] section 5: a token's importance is the attention it has
+    accumulated. Over the prompt this is taken as: for every query head h of
+    the group and every query position i, the causal softmax of
+    q_i . k_t / sqrt(d) over t <= i; acc0[t] sums those weights over the
+    group's heads and over the queries i >= t. The plain reading of
+    "accumulated attention" at prefill (the pages give no separate formula):
+    the same sum the decode steps keep adding to, started from the prompt.
+
+    q [n, hq, T, d], k [n, hkv, T, d] (fp16 values) -> acc0 [n, hkv, T].
+    """
+    n, hq, T, d = q.shape
+    hkv = k.shape[1]
+    rep = hq // hkv
+    acc = np.zeros((n, hkv, T), F64)
+    later = np.triu(np.ones((T, T), bool), 1)   # key t > query i
+    for i in range(n):
+        for h in range(hq):
+            g = h // rep
+            s = (q[i, h].astype(F64) @ k[i, g].astype(F64).T) / np.sqrt(F64(d))
+            s[later] = -np.inf
+            e = np.exp(s - s.max(axis=1, keepdims=True))
+            acc[i, g] += (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+    return acc
 
 
 def h2o_accumulate(acc16, p16):

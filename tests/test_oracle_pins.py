@@ -439,3 +439,46 @@ def test_criticalkv_stage1_mass_closed_form():
 def dataclass_replace(cfg, **kw):
     import dataclasses
     return dataclasses.replace(cfg, **kw)
+
+
+# ---------------------------------------------------------------- prefill scores (acc0)
+def test_prefill_scores_conservation_and_single_token():
+    """Every query row of a causal softmax sums to 1, so the scores of a
+    group sum to rep * T; with one token each head gives it weight 1."""
+    rng = np.random.default_rng(31)
+    n, hq, hkv, T, d = 2, 6, 2, 37, 16
+    q = rng.normal(0, 2, (n, hq, T, d)).astype(F16)
+    k = rng.normal(0, 2, (n, hkv, T, d)).astype(F16)
+    acc = O.prefill_scores(q, k)
+    assert acc.shape == (n, hkv, T)
+    assert np.allclose(acc.sum(axis=-1), hq // hkv * T, rtol=0, atol=1e-9)
+    one = O.prefill_scores(q[:, :, :1], k[:, :, :1])
+    assert np.allclose(one, hq // hkv, rtol=0, atol=1e-12)
+
+
+def test_prefill_scores_zero_query_harmonic_tail():
+    """q = 0 makes every causal row uniform: query i gives 1/(i+1) to each
+    t <= i, so acc0[t] = rep * sum_{i=t}^{T-1} 1/(i+1)."""
+    n, hq, hkv, T, d = 1, 4, 1, 50, 8
+    q = np.zeros((n, hq, T, d), F16)
+    k = np.random.default_rng(2).normal(size=(n, hkv, T, d)).astype(F16)
+    acc = O.prefill_scores(q, k)
+    tail = np.array([sum(1.0 / (i + 1) for i in range(t, T)) for t in range(T)])
+    assert np.allclose(acc[0, 0], 4 * tail, rtol=1e-12, atol=0)
+
+
+def test_prefill_scores_match_causal_sdpa_weights():
+    """With the identity matrix as values, causal scaled-dot-product
+    attention (torch, float64) returns the weight matrix itself; its column
+    sums over the group's heads are acc0."""
+    rng = np.random.default_rng(5)
+    n, hq, hkv, T, d = 2, 8, 2, 29, 32
+    q = rng.normal(0, 1.5, (n, hq, T, d)).astype(F16)
+    k = rng.normal(0, 1.5, (n, hkv, T, d)).astype(F16)
+    rep = hq // hkv
+    qt = torch.from_numpy(q.astype(F64))
+    kt = torch.from_numpy(np.repeat(k.astype(F64), rep, axis=1))
+    eye = torch.eye(T, dtype=torch.float64).expand(n, hq, T, T)
+    w = torch.nn.functional.scaled_dot_product_attention(qt, kt, eye, is_causal=True).numpy()
+    ref = w.sum(axis=2).reshape(n, hkv, rep, T).sum(axis=2)
+    assert np.allclose(O.prefill_scores(q, k), ref, rtol=1e-10, atol=1e-12)
