@@ -53,11 +53,13 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def recorded_traffic(workload):
-    """HBM bytes per decode-attention call (split + merge kernels) from the
-    FETCH_SIZE / WRITE_SIZE counter runs recorded under profiles/, each
-    scaled by the reading of a plain 1 GiB copy; None when the kernels
-    changed since the counters were taken or the workload was not profiled."""
+def recorded_traffic(workload, key="split_traffic_bytes_per_launch"):
+    """HBM bytes per launch of the split kernel (key
+    split_traffic_bytes_per_launch) or per decode-attention call, split +
+    merge (call_traffic_bytes), from the FETCH_SIZE / WRITE_SIZE counter runs
+    recorded under profiles/, each scaled by the reading of a plain 1 GiB
+    copy; None when the kernels changed since the counters were taken or the
+    workload was not profiled."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
@@ -66,7 +68,7 @@ def recorded_traffic(workload):
     if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
     w = rec.get("workloads", {}).get(workload)
-    return None if w is None else float(w["traffic_bytes_per_call"])
+    return None if w is None or key not in w else float(w[key])
 
 
 def attn_bytes(cfg, N):
@@ -80,6 +82,12 @@ def attn_bytes(cfg, N):
                 + nq * 2 * (d * cfg.bits // 8 + 4 * (d // G))
                 + cfg.rep * d * 2 + d * 4 + cfg.rep * d * 4 + cfg.cap16 * 4)
     return per_unit * cfg.batch * cfg.hkv
+
+
+def split_bytes(cfg, N):
+    """Algorithmic bytes of one split-kernel launch at length N: everything
+    attn_bytes counts except o and p16, which the merge kernel writes."""
+    return attn_bytes(cfg, N) - (cfg.rep * cfg.d * 4 + cfg.cap16 * 4) * cfg.batch * cfg.hkv
 
 
 def h2o_bytes(cfg):
@@ -246,7 +254,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--attn-steps", type=int, default=20,
-                    help="extra decode steps timed around the attention call alone")
+                    help="decode steps timed around the attention call alone, and as many "
+                         "timed at the split kernel's own start and end")
     ap.add_argument("--workload", default="llama2_7b_layer")
     ap.add_argument("--seed", type=int, default=1001)
     ap.add_argument("--set", action="append", default=[], metavar="FIELD=INT",
@@ -285,7 +294,7 @@ def main():
     if args.set:
         cfg = cfg.scaled(**{kv.split("=")[0]: int(kv.split("=")[1]) for kv in args.set})
     K, W, KA = args.steps, args.warmup, args.attn_steps
-    total = K + W + KA
+    total = K + W + 2 * KA
     assert total <= cfg.steps, f"the workload defines {cfg.steps} decode steps"
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
@@ -324,9 +333,13 @@ def main():
     N = cfg.T
     cpu_state = None
 
-    def attn_call(s, n_len):
+    def attn_call(s, n_len, split_ev=None):
         qd, kd, vd = steps_in[s]
-        L.mikv_decode_attn(dims, cache, n_len, qd, kd, vd, b, o, p16, ws)
+        if split_ev is None:
+            L.mikv_decode_attn(dims, cache, n_len, qd, kd, vd, b, o, p16, ws)
+        else:
+            # the events take the split kernel's own start and end
+            L.mikv_decode_attn_timed(dims, cache, n_len, qd, kd, vd, b, o, p16, ws, *split_ev)
 
     def step_call(s, n_len):
         qd, kd, vd = steps_in[s]
@@ -346,7 +359,7 @@ def main():
             graphs[s] = g
         torch.cuda.synchronize()
 
-    def one_step(s, ev_start=None, ev_attn=None, ev_end=None):
+    def one_step(s, ev_start=None, ev_attn=None, ev_end=None, split_ev=None):
         nonlocal N
         N += 1
         assert N == cfg.T + s + 1
@@ -360,8 +373,9 @@ def main():
                 step_call(s, N)
         else:
             # attention-only timing: mikv_decode_attn, then the H2O call
-            attn_call(s, N)
-            ev_attn.record()
+            attn_call(s, N, split_ev)
+            if ev_attn is not None:
+                ev_attn.record()
             h2o_call(N)
         if ev_end is not None:
             ev_end.record()
@@ -385,24 +399,39 @@ def main():
         lens.append(N)
     torch.cuda.synchronize()
     wall = time.perf_counter() - tw0
-    # attention kernels alone (split + merge of one mikv_decode_attn call)
+    # attention alone, two passes of KA decode steps each:
+    #  - events on the stream around each mikv_decode_attn call (split + merge);
+    #  - mikv_decode_attn_timed, whose events take the start and end of the
+    #    split kernel itself, the dominant kernel (hipExtLaunchKernel; such a
+    #    launch leaves a gap of a few microseconds before the next kernel, so
+    #    these calls are not the ones the call-level time comes from)
     eva = [(Ev(), Ev()) for _ in range(KA)]
     alens = []
     for i in range(KA):
         do_flush(i)
         one_step(W + K + i, ev_start=eva[i][0], ev_attn=eva[i][1])
         alens.append(N)
+    evk = [(Ev(), Ev()) for _ in range(KA)]
+    klens = []
+    for i in range(KA):
+        do_flush(i)
+        one_step(W + K + KA + i, ev_attn=Ev(), split_ev=evk[i])
+        klens.append(N)
     torch.cuda.synchronize()
     step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     attn_ms = np.array([e[0].elapsed_time(e[1]) for e in eva])
+    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evk])
     lens = np.array(lens)
     ms_per_step = float(step_ms.mean())
     value = float(cfg.batch * lens.mean() / (ms_per_step * 1e-3))
     abytes = np.array([attn_bytes(cfg, n) for n in alens], dtype=np.float64)
     a_gbps = float((abytes / (attn_ms * 1e-3)).mean() / 1e9)
+    kbytes = np.array([split_bytes(cfg, n) for n in klens], dtype=np.float64)
+    k_gbps = float(kbytes.mean() / (split_ms.mean() * 1e-3) / 1e9)
     sbytes = np.array([attn_bytes(cfg, n) + h2o_bytes(cfg) for n in lens], dtype=np.float64)
     s_gbps = float((sbytes / (step_ms * 1e-3)).mean() / 1e9)
-    log(f"[bench] attn {attn_ms.mean() * 1e3:.1f} us ({a_gbps:.0f} GB/s), step "
+    log(f"[bench] split kernel {split_ms.mean() * 1e3:.1f} us ({k_gbps:.0f} GB/s), attn call "
+        f"{attn_ms.mean() * 1e3:.1f} us ({a_gbps:.0f} GB/s), step "
         f"{ms_per_step * 1e3:.1f} us ({s_gbps:.0f} GB/s), wall incl. flush {wall / K * 1e3:.3f} ms/step")
 
     cpu = None
@@ -428,12 +457,18 @@ def main():
                    "head_dim": cfg.d, "context": cfg.T, "low_bits": cfg.bits,
                    "important_pct": cfg.pct, "recent": cfg.recent, "group": cfg.G,
                    "cache_flush_per_step": args.flush, "step_launch": "hip_graph" if args.graph else "eager"},
-        "roofline": {"bound": "hbm", "achieved": a_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": a_gbps / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": k_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": k_gbps / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic(cfg.name) if not args.set else None,
-                     "launches_timed": KA,
-                     "kernel": "decode_split_kernel + decode_merge_kernel (one mikv_decode_attn call)", "kernel_us": float(attn_ms.mean() * 1e3),
-                     "bytes_per_launch": float(abytes.mean())},
+                     "launches_timed": KA, "kernel": "decode_split_kernel",
+                     "kernel_us": float(split_ms.mean() * 1e3),
+                     "bytes_per_launch": float(kbytes.mean()),
+                     "timing": "hipExtLaunchKernel start/stop events of the kernel itself"},
+        "attn_call": {"kernels": "decode_split_kernel + decode_merge_kernel (one mikv_decode_attn call)",
+                      "us": float(attn_ms.mean() * 1e3), "bytes": float(abytes.mean()),
+                      "GBps": a_gbps, "frac": a_gbps / HBM_PEAK_GBPS,
+                      "traffic": recorded_traffic(cfg.name, "call_traffic_bytes") if not args.set else None,
+                      "timing": "HIP events recorded on the stream before and after the call"},
         "step_hbm_gbps": s_gbps,
         "wall_ms_per_step_incl_flush": wall / K * 1e3,
         "cpu_baseline": cpu,

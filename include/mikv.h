@@ -173,6 +173,24 @@ mikv_status mikv_decode_attn(const mikv_dims* dims, const mikv_cache* cache,
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * mikv_decode_attn with the duration of its first kernel measured: the
+ * same computation, arguments, outputs and errors, and in addition the
+ * caller's events split_start and split_stop (hipEvent_t passed as void*,
+ * created with timing enabled, owned by the caller) receive the start and
+ * end timestamps of the split kernel, which streams both cache tiers and
+ * moves nearly all of the call's bytes. hipEventElapsedTime(split_start,
+ * split_stop) is then that kernel's duration alone, without launch gaps.
+ * The events are recorded through hipExtLaunchKernel on `stream`.
+ * Errors: as mikv_decode_attn; a NULL event -> MIKV_ERR_NULL.
+ */
+mikv_status mikv_decode_attn_timed(const mikv_dims* dims, const mikv_cache* cache,
+                                   int32_t len, const uint16_t* q,
+                                   const uint16_t* k_new, const uint16_t* v_new,
+                                   const float* b, float* o, float* p16,
+                                   void* ws, size_t ws_bytes, void* stream,
+                                   void* split_start, void* split_stop);
+
+/*
  * Source of the prefill build of mikv_h2o_update_select.
  *   k    [batch][hkv][T][d] fp16  prompt keys (multiplied by b when b != NULL,
  *                                 exactly as mikv_balance_prefill's kb)

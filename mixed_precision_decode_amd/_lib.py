@@ -51,6 +51,8 @@ _SIGS = {
     "mikv_decode_attn_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
     "mikv_decode_attn": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _vp, _vp, _vp,
                                    _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mikv_decode_attn_timed": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _vp, _vp, _vp,
+                                         _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
     "mikv_decode_step": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _i32, _i32, _vp,
                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mikv_h2o_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
@@ -224,6 +226,31 @@ def mikv_decode_attn(dims: Dims, cache: Cache, length: int, q, k_new, v_new, b, 
         _ptr(v_new, "f16", (n, hkv, d), "v_new"), _ptr(b, _f32t(), (n, hkv, d), "b"),
         _ptr(o, _f32t(), (n, hq, d), "o"), _ptr(p16, _f32t(), (n, hkv, dims.cap16), "p16"),
         _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def _event(ev):
+    """Raw hipEvent_t of a torch.cuda.Event created with enable_timing=True
+    (torch creates the event at its first record)."""
+    import torch
+    if not isinstance(ev, torch.cuda.Event):
+        raise ValueError("expected a torch.cuda.Event")
+    if not ev.cuda_event:
+        ev.record()
+    return ev.cuda_event
+
+
+def mikv_decode_attn_timed(dims: Dims, cache: Cache, length: int, q, k_new, v_new, b, o, p16, ws,
+                           split_start, split_stop, stream=None):
+    """mikv_decode_attn; split_start / split_stop (torch.cuda.Event, timing
+    enabled) receive the start and end of the split kernel itself."""
+    n, hq, hkv, d = dims.batch, dims.hq, dims.hkv, dims.d
+    _check(lib().mikv_decode_attn_timed(
+        C.byref(dims.c()), C.byref(cache.c()), length,
+        _ptr(q, "f16", (n, hq, d), "q"), _ptr(k_new, "f16", (n, hkv, d), "k_new"),
+        _ptr(v_new, "f16", (n, hkv, d), "v_new"), _ptr(b, _f32t(), (n, hkv, d), "b"),
+        _ptr(o, _f32t(), (n, hq, d), "o"), _ptr(p16, _f32t(), (n, hkv, dims.cap16), "p16"),
+        _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream),
+        _event(split_start), _event(split_stop)))
 
 
 def mikv_decode_step(dims: Dims, cache: Cache, length: int, recent: int, heavy: int, q, k_new, v_new,

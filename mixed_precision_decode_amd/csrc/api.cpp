@@ -113,10 +113,10 @@ size_t mikv_decode_attn_workspace(const mikv_dims* m, int32_t max_len) {
   return decode_ws_bound(m->batch, m->hq, m->hkv, m->d, m->bits, m->group, m->cap16, nq);
 }
 
-mikv_status mikv_decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t len,
-                             const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
-                             const float* b, float* o, float* p16, void* ws, size_t ws_bytes,
-                             void* stream) {
+static mikv_status decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t len,
+                               const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                               const float* b, float* o, float* p16, void* ws, size_t ws_bytes,
+                               void* stream, void* ev_start, void* ev_stop) {
   mikv_status st = check_dims(m, true);
   if (st != MIKV_OK) return st;
   st = check_cache(c);
@@ -139,7 +139,25 @@ mikv_status mikv_decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t le
   a.o = o; a.p16 = p16; a.ws = ws;
   a.fuse_h2o = false;
   a.h2o = H2OView{};
+  a.ev_split_start = static_cast<hipEvent_t>(ev_start);
+  a.ev_split_stop = static_cast<hipEvent_t>(ev_stop);
   return from_hip(launch_decode_attn(a, pl, static_cast<hipStream_t>(stream)));
+}
+
+mikv_status mikv_decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t len,
+                             const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                             const float* b, float* o, float* p16, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return decode_attn(m, c, len, q, k_new, v_new, b, o, p16, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+mikv_status mikv_decode_attn_timed(const mikv_dims* m, const mikv_cache* c, int32_t len,
+                                   const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                                   const float* b, float* o, float* p16, void* ws, size_t ws_bytes,
+                                   void* stream, void* split_start, void* split_stop) {
+  if (!split_start || !split_stop) return MIKV_ERR_NULL;
+  return decode_attn(m, c, len, q, k_new, v_new, b, o, p16, ws, ws_bytes, stream, split_start,
+                     split_stop);
 }
 
 mikv_status mikv_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t len, int32_t recent,
@@ -168,6 +186,8 @@ mikv_status mikv_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t le
   a.kq = c->kq; a.vq = c->vq; a.ksz = c->ksz; a.vsz = c->vsz;
   a.o = o; a.p16 = p16; a.ws = ws;
   a.fuse_h2o = m->cap16 <= kFusedMaxCap16;
+  a.ev_split_start = nullptr;
+  a.ev_split_stop = nullptr;
   H2OView& v = a.h2o;
   v.cap16 = m->cap16; v.capq = m->capq; v.len = len; v.recent = recent;
   v.k16 = c->k16; v.v16 = c->v16; v.pos16 = c->pos16; v.acc16 = c->acc16; v.free16 = c->free16;

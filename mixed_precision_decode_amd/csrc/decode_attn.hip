@@ -27,6 +27,7 @@
 //                 FP16-tier scores into p16 (summed over the group).
 // Scores are in the log2 domain (q-hat is pre-multiplied by log2(e)/sqrt(d)).
 #include <atomic>
+#include <hip/hip_ext.h>
 #include <cfloat>
 
 #include "common.hpp"
@@ -1033,8 +1034,17 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   k.part_o = reinterpret_cast<float*>(w);
   w += al256(nparts * pl.RT * D * sizeof(float));
   k.sc16 = reinterpret_cast<float*>(w);
-  decode_split_kernel<D, BITS, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (a.ev_split_start || a.ev_split_stop) {
+    // the events take the kernel's own start and end timestamps
+    void* args[] = {&k};
+    e = hipExtLaunchKernel(reinterpret_cast<const void*>(decode_split_kernel<D, BITS, RT>),
+                           dim3(static_cast<unsigned>(nparts)), dim3(kThreads), args, 0, stream,
+                           a.ev_split_start, a.ev_split_stop, 0);
+  } else {
+    decode_split_kernel<D, BITS, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   const size_t lds = static_cast<size_t>(k.rep) * S * sizeof(float2) + 2 * k.rep * sizeof(float);
   const bool fuse = a.fuse_h2o && a.cap16 <= kFusedMaxCap16;

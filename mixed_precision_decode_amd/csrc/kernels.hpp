@@ -51,6 +51,9 @@ struct DecodeArgs {
   // and demotion (fuse_h2o = true; h2o holds the cache views it writes)
   bool fuse_h2o;
   H2OView h2o;
+  // optional hipEvent_t pair that records the split kernel's own start and
+  // end (hipExtLaunchKernel); both null for an ordinary launch
+  hipEvent_t ev_split_start, ev_split_stop;
 };
 hipError_t launch_decode_attn(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 // largest FP16 tier the fused merge handles (slots held in registers)

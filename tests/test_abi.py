@@ -29,7 +29,7 @@ def _header_functions():
 
 def test_exports_every_declared_function(lib):
     names = _header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L._SIGS)
@@ -74,6 +74,20 @@ def test_decode_attn_validation(lib):
     mis = _cache()
     mis.k16 = FAKE + 2
     assert call(good, cache=mis) == L.MIKV_ERR_SHAPE            # 16-byte alignment
+
+
+def test_decode_attn_timed_validation(lib):
+    c = _cache()
+    good = _dims()
+    ws_need = lib.mikv_decode_attn_workspace(C.byref(good.c()), 80)
+    call = lambda dims=good, length=50, ws_bytes=ws_need, ev0=FAKE, ev1=FAKE: lib.mikv_decode_attn_timed(
+        C.byref(dims.c()), C.byref(c), length, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        ws_bytes, None, ev0, ev1)
+    assert call(ev0=None) == L.MIKV_ERR_NULL
+    assert call(ev1=None) == L.MIKV_ERR_NULL
+    assert call(_dims(hq=7)) == L.MIKV_ERR_SHAPE
+    assert call(length=112) == L.MIKV_ERR_CAPACITY
+    assert call(ws_bytes=16) == L.MIKV_ERR_WORKSPACE
 
 
 def test_decode_step_validation(lib):

@@ -373,3 +373,36 @@ def test_decode_step_matches_separate_calls(name, over, steps):
         assert np.array_equal(d1, d2)
         for key in L.Cache.NAMES:
             assert np.array_equal(np.asarray(c1[key]).view(np.uint8), np.asarray(c2[key]).view(np.uint8)), key
+
+
+# ---------------------------------------------------------------- timed launch
+@pytest.mark.parametrize("name,over", [("llama2_7b_layer", dict(T=700)), ("tiny", dict(hq=8, hkv=2))])
+def test_decode_attn_timed_matches_plain(name, over):
+    """mikv_decode_attn_timed computes exactly what mikv_decode_attn does
+    and its events bracket the split kernel (a positive duration no longer
+    than the whole call's)."""
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"decode_attn_timed {name} {over}", flush=True)
+    res = []
+    for timed in (False, True):
+        dims, cache, b, _ = _prefill_gpu(cfg, 41, True)
+        o = torch.zeros((cfg.batch, cfg.hq, cfg.d), dtype=torch.float32, device="cuda")
+        p16 = torch.zeros((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
+        ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + 1), dtype=torch.uint8, device="cuda")
+        qd, kd, vd = (dev(x) for x in S.decode_tensors(cfg, 41, 0))
+        if timed:
+            e0, e1, c0, c1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+            c0.record()
+            L.mikv_decode_attn_timed(dims, cache, cfg.T + 1, qd, kd, vd, b, o, p16, ws, e0, e1)
+            c1.record()
+            torch.cuda.synchronize()
+            t_split, t_call = e0.elapsed_time(e1), c0.elapsed_time(c1)
+            assert 0.0 < t_split <= t_call, (t_split, t_call)
+        else:
+            L.mikv_decode_attn(dims, cache, cfg.T + 1, qd, kd, vd, b, o, p16, ws)
+        res.append((host(o).copy(), host(p16).copy(), cache.to_numpy()))
+    (o1, p1, c1), (o2, p2, c2) = res
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(p1.view(np.uint32), p2.view(np.uint32))
+    for key in L.Cache.NAMES:
+        assert np.array_equal(np.asarray(c1[key]).view(np.uint8), np.asarray(c2[key]).view(np.uint8)), key
