@@ -145,6 +145,12 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
+  return v;
+}
+
 // Online-softmax state of one thread for RT heads and CPL channels.
 template <int RT, int CPL>
 struct Acc {
@@ -821,14 +827,22 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
     sml[i] = pml[(static_cast<int64_t>((unit * p.tiles + hl / RT) * S) + s) * RT + hl % RT];
   }
   __syncthreads();
-  // (2) per head: maximum and reciprocal normaliser
-  for (int hl = h_lo + tid; hl < h_hi; hl += kThreads) {
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, sml[hl * S + s].x);
-    float L = 0.0f;
-    for (int s = 0; s < S; ++s) L += sml[hl * S + s].y * fast_exp2(sml[hl * S + s].x - M);
-    sM[hl] = M;
-    sIL[hl] = 1.0f / L;
+  // (2) per head: maximum and reciprocal normaliser, one wave per head, its
+  // lanes taking the splits in turn (a unit of a long sequence has ~64)
+  {
+    const int wave = tid / kWave, lane = tid % kWave;
+    for (int hl = h_lo + wave; hl < h_hi; hl += kThreads / kWave) {
+      float M = -INFINITY;
+      for (int s = lane; s < S; s += kWave) M = fmaxf(M, sml[hl * S + s].x);
+      M = wave_max(M);
+      float L = 0.0f;
+      for (int s = lane; s < S; s += kWave) L += sml[hl * S + s].y * fast_exp2(sml[hl * S + s].x - M);
+      L = wave_sum(L);
+      if (lane == 0) {
+        sM[hl] = M;
+        sIL[hl] = 1.0f / L;
+      }
+    }
   }
   __syncthreads();
   // (3) outputs: each thread sums its subset of splits, then the kMergeTPO
@@ -956,14 +970,21 @@ static int split_blocks_per_cu(int d, int bits, int rt) {
 // (the instantiation's occupancy, at most MIKV_BLOCKS_PER_CU per compute
 // unit), so no block starts after the others have drained. The
 // splits of a (sequence, kv head) are shared between the tiers in
-// proportion to their bytes, so every block streams about the same amount;
-// each tier gets at least one split when it has tokens.
+// proportion to the time their tokens take, so blocks end together; each
+// tier gets at least one split when it has tokens. Single-head tiles are
+// bound by HBM: the time of a tier is its bytes. Tiles of 2-4 heads are
+// bound by VALU issue, and a token costs about the same instructions in
+// both tiers (4 heads x d multiply-adds for the score and as many for the
+// value sum; the low-bit unpacking roughly matches the FP16 tier's wider
+// lane groups): the time of a tier is its token count.
 DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq) {
   DecodePlan pl;
   pl.RT = (rep % 4 == 0) ? 4 : (rep % 2 == 0 ? 2 : 1);
   pl.tiles = rep / pl.RT;
   const double b16 = static_cast<double>(cap16) * 4.0 * d;
   const double bq = static_cast<double>(nq) * 2.0 * (d * bits / 8 + 4 * (d / group));
+  const double t16 = pl.RT == 1 ? b16 : static_cast<double>(cap16);
+  const double tq = pl.RT == 1 ? bq : static_cast<double>(nq);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
   long per_unit = (static_cast<long>(kCUs) * split_blocks_per_cu(d, bits, pl.RT)) / units;
   // no split below ~16 KB of rows
@@ -971,7 +992,7 @@ DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, 
   if (per_unit > cap_splits) per_unit = cap_splits;
   if (nq > 0) {
     if (per_unit < 2) per_unit = 2;
-    long s16 = static_cast<long>(per_unit * b16 / (b16 + bq) + 0.5);
+    long s16 = static_cast<long>(per_unit * t16 / (t16 + tq) + 0.5);
     if (s16 < 1) s16 = 1;
     if (s16 > per_unit - 1) s16 = per_unit - 1;
     if (s16 > cap16) s16 = cap16;
