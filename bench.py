@@ -204,7 +204,9 @@ def bench_criticalkv(args, log):
 def bench_prefill(args, log):
     """Prefill-time kernels of the workload: the channel balancer (q and k
     max-abs scan, b) and the prefill build (top-H selection, FP16 rows and
-    quantized low-bit rows). HBM-bound; GB/s from their algorithmic bytes."""
+    quantized low-bit rows), HBM-bound, GB/s from their algorithmic bytes;
+    and the prompt heavy-hitter scores (causal attention column sums),
+    MFMA-bound, TFLOP/s."""
     import torch
     from mixed_precision_decode_amd import _lib as L
     from mixed_precision_decode_amd import synth as S
@@ -225,11 +227,20 @@ def bench_prefill(args, log):
     build_bytes = n_u * (cfg.T * (4.0 * cfg.d + 4 + 4)          # k, v, acc0 read; slot map
                          + cfg.B * (4.0 * cfg.d + 8)             # FP16 rows + pos/acc written
                          + (cfg.T - cfg.B) * (2 * (cfg.d * cfg.bits / 8 + 4 * cfg.d / cfg.G) + 4))
+    acc_s = torch.empty((cfg.batch, cfg.hkv, cfg.T), dtype=torch.float32, device="cuda")
+    ws_s = torch.empty(L.mikv_prefill_scores_workspace(dims, cfg.T), dtype=torch.uint8, device="cuda")
+    # prompt heavy-hitter scores: the causal score matrix of every query head,
+    # T (T + 1) / 2 dot products of d, is the algorithmic work; the kernels
+    # form it twice (softmax statistics, then column sums) in 32 x 32 tiles
+    score_flops = 2.0 * cfg.d * cfg.T * (cfg.T + 1) / 2 * cfg.batch * cfg.hq
+    nt = (cfg.T + 31) // 32
+    exec_flops = 2 * 2.0 * cfg.d * 32 * 32 * nt * (nt + 1) / 2 * cfg.batch * cfg.hq
     res = {}
     for name, fn, nbytes in (
             ("balance", lambda: L.mikv_balance_prefill(dims, cfg.T, qg, kg, b, None, ws_b), bal_bytes),
             ("build", lambda: L.mikv_h2o_update_select(dims, cache, cfg.T, cfg.recent, cfg.H,
-                                                       src=dict(k=kg, v=vg, acc0=ag, b=b), ws=ws_h), build_bytes)):
+                                                       src=dict(k=kg, v=vg, acc0=ag, b=b), ws=ws_h), build_bytes),
+            ("scores", lambda: L.mikv_prefill_scores(dims, cfg.T, qg, kg, acc_s, ws_s), None)):
         for _ in range(args.warmup):
             fn()
         evs = _events(args.steps)
@@ -240,6 +251,14 @@ def bench_prefill(args, log):
             e1.record()
         torch.cuda.synchronize()
         us = float(np.mean([a.elapsed_time(e) for a, e in evs])) * 1e3
+        if nbytes is None:
+            tf = score_flops / (us * 1e-6) / 1e12
+            res[name] = {"us": us, "algorithmic_flops": score_flops, "executed_flops": exec_flops,
+                         "TFLOPs": tf, "executed_TFLOPs": exec_flops / (us * 1e-6) / 1e12,
+                         "bound": "mfma", "peak_TFLOPs": 2500.0, "frac": tf / 2500.0}
+            log(f"[bench] prefill {name} {us:.1f} us, {tf:.0f} TFLOP/s algorithmic, "
+                f"{res[name]['executed_TFLOPs']:.0f} executed (fp16 MFMA)")
+            continue
         res[name] = {"us": us, "bytes": nbytes, "GBps": nbytes / (us * 1e-6) / 1e9,
                      "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS}
         log(f"[bench] prefill {name} {us:.1f} us, {res[name]['GBps']:.0f} GB/s")
@@ -271,7 +290,8 @@ def main():
     ap.add_argument("--criticalkv", action="store_true",
                     help="only time the CriticalKV prefill select (32 heads, 32K tokens); one JSON line")
     ap.add_argument("--prefill", action="store_true",
-                    help="only time the workload's prefill balancer and build; one JSON line")
+                    help="only time the workload's prefill kernels (balancer, build, heavy-hitter "
+                         "scores); one JSON line")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()

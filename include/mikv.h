@@ -191,6 +191,33 @@ mikv_status mikv_decode_attn_timed(const mikv_dims* dims, const mikv_cache* cach
                                    void* split_start, void* split_stop);
 
 /*
+ * Prompt heavy-hitter scores acc0 (input of the prefill build of
+ * mikv_h2o_update_select): the attention each prompt token has accumulated
+ * during the prompt ([paperlayer] section 5 and [velog notes] Key
+ * contributions 1): important tokens are the heavy hitters of accumulated
+ * attention, H2O). For query head h of kv head g and query position i,
+ * P[i][t] = softmax over t <= i of q[n][h][i] . k[n][g][t] / sqrt(d)
+ * (causal); acc0[n][g][t] = sum over the group's query heads h and the
+ * queries i >= t of P[i][t]. Each row of P sums to 1, so the scores of a
+ * (sequence, kv head) sum to (hq/hkv) * T.
+ * q [batch][hq][T][d], k [batch][hkv][T][d] fp16 as given to the model's
+ * attention (not balanced: the balancer leaves q . k unchanged);
+ * acc0 [batch][hkv][T] fp32 (output). Scores on matrix cores (fp16 inputs,
+ * fp32 accumulation), softmax and sums in fp32.
+ * ws: mikv_prefill_scores_workspace(dims, T) bytes (any contents): the
+ * per-query softmax maximum and normaliser between the two kernels.
+ * Only batch, hq, hkv and d of dims are used. T == 0 enqueues nothing.
+ * Errors: NULL pointer -> MIKV_ERR_NULL; q or k not 16-byte aligned, T < 0
+ * -> MIKV_ERR_SHAPE; d not in {64, 128} -> MIKV_ERR_UNSUPPORTED; workspace
+ * too small -> MIKV_ERR_WORKSPACE.
+ */
+size_t mikv_prefill_scores_workspace(const mikv_dims* dims, int32_t T);
+mikv_status mikv_prefill_scores(const mikv_dims* dims, int32_t T,
+                                const uint16_t* q, const uint16_t* k,
+                                float* acc0, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
  * Source of the prefill build of mikv_h2o_update_select.
  *   k    [batch][hkv][T][d] fp16  prompt keys (multiplied by b when b != NULL,
  *                                 exactly as mikv_balance_prefill's kb)

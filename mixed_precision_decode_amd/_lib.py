@@ -47,6 +47,8 @@ _SIGS = {
     "mikv_abi_version": (C.c_int, []),
     "mikv_balance_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
     "mikv_balance_prefill": (C.c_int, [C.POINTER(MikvDims), _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mikv_prefill_scores_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
+    "mikv_prefill_scores": (C.c_int, [C.POINTER(MikvDims), _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mikv_quantize_tokens": (C.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "mikv_decode_attn_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
     "mikv_decode_attn": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _vp, _vp, _vp,
@@ -173,6 +175,19 @@ def mikv_balance_prefill(dims: Dims, T: int, q, k, b, kb=None, ws=None, stream=N
         _ptr(b, _f32t(), (n, hkv, d), "b"), _ptr(kb, "f16", (n, hkv, T, d), "kb", optional=True),
         _ptr(ws, name="ws", optional=True), 0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def mikv_prefill_scores_workspace(dims: Dims, T: int) -> int:
+    return lib().mikv_prefill_scores_workspace(C.byref(dims.c()), T)
+
+
+def mikv_prefill_scores(dims: Dims, T: int, q, k, acc0, ws, stream=None):
+    n, hq, hkv, d = dims.batch, dims.hq, dims.hkv, dims.d
+    _check(lib().mikv_prefill_scores(
+        C.byref(dims.c()), T,
+        _ptr(q, "f16", (n, hq, T, d), "q"), _ptr(k, "f16", (n, hkv, T, d), "k"),
+        _ptr(acc0, _f32t(), (n, hkv, T), "acc0"),
+        _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def mikv_quantize_tokens(x, rows, codes, sz, group: int, bits: int, stream=None):

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmikv.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "balance.hip", "decode_attn.hip", "h2o.hip", "criticalkv.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "balance.hip", "decode_attn.hip", "h2o.hip", "criticalkv.hip",
+           "prefill_scores.hip"]
 
 
 def hipcc() -> str:

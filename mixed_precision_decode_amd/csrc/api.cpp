@@ -91,6 +91,28 @@ mikv_status mikv_balance_prefill(const mikv_dims* m, int32_t T, const uint16_t* 
                                  static_cast<hipStream_t>(stream)));
 }
 
+// ---------------------------------------------------------------- prompt heavy-hitter scores
+size_t mikv_prefill_scores_workspace(const mikv_dims* m, int32_t T) {
+  if (check_dims(m, false) != MIKV_OK || T < 0) return 0;
+  return prefill_scores_ws_bytes(m->batch, m->hq, T);
+}
+
+mikv_status mikv_prefill_scores(const mikv_dims* m, int32_t T, const uint16_t* q, const uint16_t* k,
+                                float* acc0, void* ws, size_t ws_bytes, void* stream) {
+  mikv_status st = check_dims(m, false);
+  if (st != MIKV_OK) return st;
+  if (T < 0) return MIKV_ERR_SHAPE;
+  if (T == 0) return MIKV_OK;
+  if (!q || !k || !acc0) return MIKV_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k)) return MIKV_ERR_SHAPE;
+  // blocks of 128 rows per (sequence, head) must fit a 32-bit grid index
+  if (static_cast<int64_t>(m->batch) * m->hq * ((T + 127) / 128) >= (int64_t{1} << 31)) return MIKV_ERR_SHAPE;
+  const size_t need = prefill_scores_ws_bytes(m->batch, m->hq, T);
+  if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
+  return from_hip(launch_prefill_scores(m->batch, m->hq, m->hkv, m->d, T, q, k, acc0, ws,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------- quantize
 mikv_status mikv_quantize_tokens(const uint16_t* x, const int32_t* rows, int64_t n_rows,
                                  int32_t d, int32_t group, int32_t bits, uint8_t* codes,

@@ -84,6 +84,11 @@ size_t h2o_ws_bytes(int batch, int hkv, int T);
 hipError_t launch_h2o_decode(const H2OArgs& a, hipStream_t stream);
 hipError_t launch_h2o_prefill(const H2OArgs& a, hipStream_t stream);
 
+// Prompt heavy-hitter scores: per-query softmax statistics, then column sums.
+size_t prefill_scores_ws_bytes(int batch, int hq, int T);
+hipError_t launch_prefill_scores(int batch, int hq, int hkv, int d, int T, const uint16_t* q,
+                                 const uint16_t* k, float* acc0, void* ws, hipStream_t stream);
+
 size_t criticalkv_ws_bytes(int H, int T, int d, int hidden);
 hipError_t launch_criticalkv(const float* A, const uint16_t* V, const uint16_t* W, int H, int T,
                              int d, int hidden, int b1, int b2, int32_t* idx, float* score2,

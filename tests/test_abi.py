@@ -29,7 +29,7 @@ def _header_functions():
 
 def test_exports_every_declared_function(lib):
     names = _header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L._SIGS)
@@ -88,6 +88,24 @@ def test_decode_attn_timed_validation(lib):
     assert call(_dims(hq=7)) == L.MIKV_ERR_SHAPE
     assert call(length=112) == L.MIKV_ERR_CAPACITY
     assert call(ws_bytes=16) == L.MIKV_ERR_WORKSPACE
+
+
+def test_prefill_scores_validation(lib):
+    good = _dims()
+    T = 300
+    need = lib.mikv_prefill_scores_workspace(C.byref(good.c()), T)
+    assert need == 2 * 8 * T * 8                      # (max, 1/sum) per query row and head
+    call = lambda dims=good, T=T, q=FAKE, k=FAKE, acc=FAKE, ws_bytes=need: lib.mikv_prefill_scores(
+        C.byref(dims.c()), T, q, k, acc, FAKE, ws_bytes, None)
+    assert call(_dims(hq=7)) == L.MIKV_ERR_SHAPE
+    assert call(_dims(d=96)) == L.MIKV_ERR_UNSUPPORTED
+    assert call(q=None) == L.MIKV_ERR_NULL
+    assert call(k=None) == L.MIKV_ERR_NULL
+    assert call(acc=None) == L.MIKV_ERR_NULL
+    assert call(q=FAKE + 2) == L.MIKV_ERR_SHAPE           # 16-byte alignment
+    assert call(T=-1) == L.MIKV_ERR_SHAPE
+    assert call(ws_bytes=need - 1) == L.MIKV_ERR_WORKSPACE
+    assert call(T=0, q=None, k=None, acc=None) == L.MIKV_OK    # nothing to do, nothing enqueued
 
 
 def test_decode_step_validation(lib):
