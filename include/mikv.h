@@ -205,7 +205,7 @@ mikv_status mikv_decode_attn_timed(const mikv_dims* dims, const mikv_cache* cach
  * acc0 [batch][hkv][T] fp32 (output). Scores on matrix cores (fp16 inputs,
  * fp32 accumulation), softmax and sums in fp32.
  * ws: mikv_prefill_scores_workspace(dims, T) bytes (any contents): the
- * per-query softmax maximum and normaliser between the two kernels.
+ * log-sum-exp of every query row between the two kernels.
  * Only batch, hq, hkv and d of dims are used. T == 0 enqueues nothing.
  * Errors: NULL pointer -> MIKV_ERR_NULL; q or k not 16-byte aligned, T < 0
  * -> MIKV_ERR_SHAPE; d not in {64, 128} -> MIKV_ERR_UNSUPPORTED; workspace

@@ -16,16 +16,19 @@
 //                     queries' rows are the held B operand, the causal key
 //                     tiles stream through the A operand; each lane keeps an
 //                     online (max, sum) of its column; the two lanes of a
-//                     column combine at the end -> (M_i, 1/L_i) in log2 units.
+//                     column combine at the end -> lse_i = M_i + log2(L_i),
+//                     the row's log-sum-exp in log2 units.
 //   pass 2 (colsum)   one wave per (sequence, kv head, 32 keys); the keys'
 //                     rows are the held A operand; every query tile at or
 //                     after the diagonal of every head of the group streams
-//                     through the B operand; p = exp2(s - M_i) / L_i is
-//                     summed per key row in registers, then across the 32
-//                     lanes that share the rows -> acc0.
+//                     through the B operand; p = exp2(s - lse_i) is summed
+//                     per key row in registers, then across the 32 lanes
+//                     that share the rows -> acc0.
 // The two passes compute bit-identical scores (same operands, same MFMA
-// sequence), so every p <= 1. No LDS, no atomics, no barriers: each wave
-// owns its outputs. Blocks with the most tiles are dispatched first.
+// sequence), so every p <= 1. Only the diagonal tile of a wave is masked.
+// The streamed operand tile (keys in pass 1, queries in pass 2) is shared by
+// the block's four waves through LDS. No atomics: each wave owns its
+// outputs. Blocks with the most tiles are dispatched first.
 #include <cfloat>
 
 #include "common.hpp"
@@ -37,6 +40,7 @@ namespace {
 
 typedef _Float16 ps_half8 __attribute__((ext_vector_type(8)));
 typedef float ps_floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned ps_u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPsWaves = 4;                 // waves per block
 constexpr int kPsThreads = kPsWaves * kWave;
@@ -68,11 +72,53 @@ __device__ __forceinline__ ps_floatx16 scores(const ps_half8 (&a)[D / 16], const
 // key row of accumulator register r within a 32-row tile
 __device__ __forceinline__ int row_of(int r, int lane) { return 8 * (r / 4) + 4 * (lane / 32) + (r % 4); }
 
+__device__ __forceinline__ float ps_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// LDS staging of the streamed 32-row tile, shared by the block's four waves.
+// The block copies a tile with coalesced 16-byte loads (consecutive threads,
+// consecutive bytes of consecutive rows) into one of two buffers while the
+// waves read MFMA operands from the other; rows are padded by 16 bytes so
+// that the operand reads of the 32 rows spread over the LDS banks.
+template <int D>
+struct PsStage {
+  static constexpr int kStride = D + 8;                  // halves per LDS row
+  static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
+  static constexpr int kRowsPerPass = kPsThreads / kChunks;
+  static constexpr int kPasses = kPsTile / kRowsPerPass;  // loads per thread and tile
+  static_assert(kPasses == 1 || kPasses == 2, "a 32-row tile is one or two passes of the block");
+  ps_u32x4 r0, r1;  // native vectors (HIP's uint4 struct here was left in scratch memory)
+  // rows row0 .. row0 + 31 of base (clamped to the last row)
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int row0, int T) {
+    const int tid = threadIdx.x;
+    const uint16_t* p = base + 8 * (tid % kChunks);
+    r0 = *reinterpret_cast<const ps_u32x4*>(p + static_cast<int64_t>(min(row0 + tid / kChunks, T - 1)) * D);
+    if constexpr (kPasses == 2)
+      r1 = *reinterpret_cast<const ps_u32x4*>(
+          p + static_cast<int64_t>(min(row0 + kRowsPerPass + tid / kChunks, T - 1)) * D);
+  }
+  __device__ __forceinline__ void store(uint16_t* buf) const {
+    const int tid = threadIdx.x;
+    uint16_t* p = buf + (tid / kChunks) * kStride + 8 * (tid % kChunks);
+    *reinterpret_cast<ps_u32x4*>(p) = r0;
+    if constexpr (kPasses == 2) *reinterpret_cast<ps_u32x4*>(p + kRowsPerPass * kStride) = r1;
+  }
+  // the lane's MFMA operand slices of the staged tile (row l % 32)
+  static __device__ __forceinline__ void operand(const uint16_t* buf, ps_half8 (&f)[D / 16]) {
+    const int lane = threadIdx.x % kWave;
+    const uint16_t* p = buf + (lane % 32) * kStride + 8 * (lane / 32);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) f[ks] = *reinterpret_cast<const ps_half8*>(p + 16 * ks);
+  }
+};
+
 template <int D>
 __global__ __launch_bounds__(kPsThreads) void ps_rowstat_kernel(const uint16_t* __restrict__ q,
                                                                   const uint16_t* __restrict__ k, int hq,
                                                                   int hkv, int T, int nh, int nib,
-                                                                  float2* __restrict__ stat) {
+                                                                  float* __restrict__ lse) {
+  constexpr int KS = D / 16;
+  using Stage = PsStage<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][kPsTile * Stage::kStride];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   // the last query blocks (most key tiles) first
   const int ib = nib - 1 - static_cast<int>(blockIdx.x) / nh;
@@ -80,119 +126,126 @@ __global__ __launch_bounds__(kPsThreads) void ps_rowstat_kernel(const uint16_t* 
   const int n = nhi / hq, h = nhi % hq;
   const int g = h / (hq / hkv);
   const int i0 = ib * kPsBlockRows + wave * kPsTile;
-  if (i0 >= T) return;
+  const bool active = i0 < T;  // every wave takes part in the copies and barriers
   const int i = i0 + lane % 32;  // this lane's query column
-  const uint16_t* qb = q + static_cast<int64_t>(nhi) * T * D;
   const uint16_t* kb = k + (static_cast<int64_t>(n) * hkv + g) * T * D;
-  ps_half8 bq[D / 16];
-  load_rows<D>(qb, min(i, T - 1), bq);
+  ps_half8 bq[KS];
+  load_rows<D>(q + static_cast<int64_t>(nhi) * T * D, min(i, T - 1), bq);
   const float c = kPsLog2e / sqrtf(static_cast<float>(D));
-  const int last = min(i0 + kPsTile - 1, T - 1);  // last key any lane of the wave needs
-  const int ntiles = last / kPsTile + 1;
-  float m = -INFINITY, l = 0.0f;
-  ps_half8 ka[D / 16], kn[D / 16] = {};
-  load_rows<D>(kb, min(lane % 32, T - 1), ka);
-  for (int tt = 0; tt < ntiles; ++tt) {
-    const int t0 = tt * kPsTile;
-    if (tt + 1 < ntiles) load_rows<D>(kb, min(t0 + kPsTile + lane % 32, T - 1), kn);
-    const ps_floatx16 s = scores<D>(ka, bq);
-    float sv[16];
-    float mt = -INFINITY;
+  // key tiles 0 .. diag of this wave (the diagonal tile holds t = i and is
+  // the only one with keys after some of the wave's queries); the block
+  // walks the tiles of its last active wave
+  const int diag = i0 / kPsTile;
+  const int last = min(ib * kPsBlockRows + kPsBlockRows - 1, T - 1) / kPsTile;
+  float m = -INFINITY, l = 0.0f;  // log2-domain running max and sum of the lane's keys
+  Stage st;
+  st.load(kb, 0, T);
+  st.store(kt[0]);
+  __syncthreads();
+  for (int tt = 0; tt <= last; ++tt) {
+    if (tt < last) st.load(kb, (tt + 1) * kPsTile, T);
+    if (active && tt <= diag) {
+      ps_half8 ka[KS];
+      Stage::operand(kt[tt & 1], ka);
+      ps_floatx16 s = scores<D>(ka, bq);
+      if (tt == diag) {
+        const int t0 = tt * kPsTile;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = t0 + row_of(r, lane);
-      sv[r] = (t <= i) ? s[r] * c : -INFINITY;  // causal; t <= i < T keeps t in range
-      mt = fmaxf(mt, sv[r]);
+        for (int r = 0; r < 16; ++r)
+          if (t0 + row_of(r, lane) > i) s[r] = -INFINITY;  // causal
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      const float mn = fmaxf(m, mx * c);
+      const float mref = fmaxf(mn, -FLT_MAX);  // exp2(-inf - mref) = 0 while nothing is seen
+      l *= ps_exp2(m - mref);
+      m = mn;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) l += ps_exp2(fmaf(s[r], c, -mref));
     }
-    if (mt > m) {
-      l *= exp2f(m - mt);  // 0 while m is -inf
-      m = mt;
-    }
-    const float mref = fmaxf(m, -FLT_MAX);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) l += exp2f(sv[r] - mref);
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) ka[ks] = kn[ks];
+    // the other buffer was last read before the previous barrier
+    if (tt < last) st.store(kt[(tt + 1) & 1]);
+    __syncthreads();
   }
+  if (!active) return;
   // lanes l and l + 32 hold the two halves of column i's key rows
   const float mo = shfl_xor_f(m, 32), lo = shfl_xor_f(l, 32);
   const float M = fmaxf(m, mo);  // finite: key t = i is in lane l or l + 32
-  const float L = l * exp2f(m - M) + lo * exp2f(mo - M);
-  if (lane < 32 && i < T) stat[static_cast<int64_t>(nhi) * T + i] = make_float2(M, 1.0f / L);
+  const float L = l * ps_exp2(m - M) + lo * ps_exp2(mo - M);  // >= 1
+  // log2-sum-exp of the row: p[i][t] = exp2(s[i][t] * c - lse[i])
+  if (lane < 32 && i < T) lse[static_cast<int64_t>(nhi) * T + i] = M + __builtin_amdgcn_logf(L);
 }
 
 template <int D>
 __global__ __launch_bounds__(kPsThreads) void ps_colsum_kernel(const uint16_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ k, int hq,
                                                                  int hkv, int T, int ng,
-                                                                 const float2* __restrict__ stat,
+                                                                 const float* __restrict__ lse,
                                                                  float* __restrict__ acc0) {
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  constexpr int KS = D / 16;
+  using Stage = PsStage<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t qt[2][kPsTile * Stage::kStride];
+  __shared__ float qlse[2][kPsTile];
+  const int tid = threadIdx.x;
+  const int lane = tid % kWave, wave = tid / kWave;
   // the first key blocks (most query tiles) first
   const int tb = static_cast<int>(blockIdx.x) / ng;
   const int ngi = static_cast<int>(blockIdx.x) % ng;  // n * hkv + g
   const int n = ngi / hkv, g = ngi % hkv;
   const int rep = hq / hkv;
   const int t0 = tb * kPsBlockRows + wave * kPsTile;
-  if (t0 >= T) return;
-  const uint16_t* kb = k + static_cast<int64_t>(ngi) * T * D;
-  ps_half8 ka[D / 16];
-  load_rows<D>(kb, min(t0 + lane % 32, T - 1), ka);
+  const bool active = t0 < T;  // every wave takes part in the copies and barriers
+  ps_half8 ka[KS];
+  load_rows<D>(k + static_cast<int64_t>(ngi) * T * D, min(t0 + lane % 32, T - 1), ka);
   const float c = kPsLog2e / sqrtf(static_cast<float>(D));
   float col[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) col[r] = 0.0f;
-  const int first = t0 / kPsTile, ntiles = (T - 1) / kPsTile + 1;
+  // the block walks query tiles first .. ntiles-1 of every head of the
+  // group; wave w starts at its diagonal tile first + w
+  const int first = tb * kPsWaves, ntiles = (T - 1) / kPsTile + 1;
   const int per_head = ntiles - first;
   const int total = rep * per_head;
-  // iteration j: head h = g*rep + j / per_head, query tile first + j % per_head
-  auto src = [&](int j, const uint16_t*& qb, const float2*& st, int& i) {
-    const int h = g * rep + j / per_head;
-    const int nhi = n * hq + h;
-    i = (first + j % per_head) * kPsTile + lane % 32;
-    qb = q + static_cast<int64_t>(nhi) * T * D;
-    st = stat + static_cast<int64_t>(nhi) * T;
+  const int diag = t0 / kPsTile;
+  Stage st;
+  float ls = 0.0f;
+  // iteration j: head g*rep + j / per_head, query tile first + j % per_head
+  auto fetch = [&](int j) {
+    const int nhi = n * hq + g * rep + j / per_head;
+    const int i0 = (first + j % per_head) * kPsTile;
+    st.load(q + static_cast<int64_t>(nhi) * T * D, i0, T);
+    // a query past the prompt contributes nothing: exp2(-inf)
+    if (tid < kPsTile) ls = (i0 + tid < T) ? lse[static_cast<int64_t>(nhi) * T + i0 + tid] : INFINITY;
   };
-  ps_half8 bq[D / 16], bn[D / 16] = {};
-  float2 ms, mn = make_float2(0.0f, 0.0f);
-  {
-    const uint16_t* qb;
-    const float2* st;
-    int i;
-    src(0, qb, st, i);
-    load_rows<D>(qb, min(i, T - 1), bq);
-    ms = st[min(i, T - 1)];
-  }
+  auto stage = [&](int buf) {
+    st.store(qt[buf]);
+    if (tid < kPsTile) qlse[buf][tid] = ls;
+  };
+  fetch(0);
+  stage(0);
+  __syncthreads();
   for (int j = 0; j < total; ++j) {
-    const uint16_t* qb;
-    const float2* st;
-    int i, in;
-    src(j, qb, st, i);
-    if (j + 1 < total) {
-      const uint16_t* qn;
-      const float2* sn;
-      src(j + 1, qn, sn, in);
-      load_rows<D>(qn, min(in, T - 1), bn);
-      mn = sn[min(in, T - 1)];
-    }
-    const ps_floatx16 s = scores<D>(ka, bq);
-    // a query past the prompt contributes nothing: exp2(-inf) * 0
-    const float M = (i < T) ? ms.x : INFINITY;
-    const float IL = (i < T) ? ms.y : 0.0f;
-    if ((i & ~(kPsTile - 1)) == t0) {  // diagonal tile: causal mask
+    if (j + 1 < total) fetch(j + 1);
+    const int it = first + j % per_head;
+    if (active && it >= diag) {
+      ps_half8 bq[KS];
+      Stage::operand(qt[j & 1], bq);
+      const float li = qlse[j & 1][lane % 32];
+      ps_floatx16 s = scores<D>(ka, bq);
+      if (it == diag) {  // diagonal tile: causal mask
+        const int i = it * kPsTile + lane % 32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = t0 + row_of(r, lane);
-        col[r] += (t <= i) ? exp2f(s[r] * c - M) * IL : 0.0f;
+        for (int r = 0; r < 16; ++r)
+          if (t0 + row_of(r, lane) > i) s[r] = -INFINITY;
       }
-    } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) col[r] += exp2f(s[r] * c - M) * IL;
+      for (int r = 0; r < 16; ++r) col[r] += ps_exp2(fmaf(s[r], c, -li));
     }
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) bq[ks] = bn[ks];
-    ms = mn;
+    if (j + 1 < total) stage((j + 1) & 1);
+    __syncthreads();
   }
+  if (!active) return;
   // sum over the 32 query columns of the lanes that share l / 32
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -217,12 +270,12 @@ __global__ __launch_bounds__(kPsThreads) void ps_colsum_kernel(const uint16_t* _
 }  // namespace
 
 size_t prefill_scores_ws_bytes(int batch, int hq, int T) {
-  return static_cast<size_t>(batch) * hq * T * sizeof(float2);
+  return static_cast<size_t>(batch) * hq * T * sizeof(float);
 }
 
 hipError_t launch_prefill_scores(int batch, int hq, int hkv, int d, int T, const uint16_t* q,
                                  const uint16_t* k, float* acc0, void* ws, hipStream_t stream) {
-  float2* stat = static_cast<float2*>(ws);
+  float* stat = static_cast<float*>(ws);
   const int nb = (T + kPsBlockRows - 1) / kPsBlockRows;
   const int nh = batch * hq, ng = batch * hkv;
   const dim3 g1(static_cast<unsigned>(nh) * nb), g2(static_cast<unsigned>(ng) * nb);

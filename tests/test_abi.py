@@ -94,7 +94,7 @@ def test_prefill_scores_validation(lib):
     good = _dims()
     T = 300
     need = lib.mikv_prefill_scores_workspace(C.byref(good.c()), T)
-    assert need == 2 * 8 * T * 8                      # (max, 1/sum) per query row and head
+    assert need == 2 * 8 * T * 4                      # log-sum-exp per query row and head
     call = lambda dims=good, T=T, q=FAKE, k=FAKE, acc=FAKE, ws_bytes=need: lib.mikv_prefill_scores(
         C.byref(dims.c()), T, q, k, acc, FAKE, ws_bytes, None)
     assert call(_dims(hq=7)) == L.MIKV_ERR_SHAPE
