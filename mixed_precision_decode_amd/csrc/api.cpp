@@ -105,8 +105,8 @@ mikv_status mikv_prefill_scores(const mikv_dims* m, int32_t T, const uint16_t* q
   if (T == 0) return MIKV_OK;
   if (!q || !k || !acc0) return MIKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k)) return MIKV_ERR_SHAPE;
-  // blocks of 128 rows per (sequence, head) must fit a 32-bit grid index
-  if (static_cast<int64_t>(m->batch) * m->hq * ((T + 127) / 128) >= (int64_t{1} << 31)) return MIKV_ERR_SHAPE;
+  // blocks of 256 rows per (sequence, head) must fit a 32-bit grid index
+  if (static_cast<int64_t>(m->batch) * m->hq * ((T + 255) / 256) >= (int64_t{1} << 31)) return MIKV_ERR_SHAPE;
   const size_t need = prefill_scores_ws_bytes(m->batch, m->hq, T);
   if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
   return from_hip(launch_prefill_scores(m->batch, m->hq, m->hkv, m->d, T, q, k, acc0, ws,

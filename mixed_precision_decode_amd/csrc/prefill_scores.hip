@@ -12,18 +12,20 @@
 // v_mfma_f32_32x32x16_f16 (fp16 in, fp32 accumulation). In that orientation
 // a lane's 16 accumulator registers are 16 key rows of ONE query column, so
 // the softmax statistics of a query need no cross-lane work per tile.
-//   pass 1 (rowstat)  one wave per (sequence, query head, 32 queries); the
+//   pass 1 (rowstat)  one wave per (sequence, query head, 64 queries); the
 //                     queries' rows are the held B operand, the causal key
 //                     tiles stream through the A operand; each lane keeps an
 //                     online (max, sum) of its column; the two lanes of a
 //                     column combine at the end -> lse_i = M_i + log2(L_i),
 //                     the row's log-sum-exp in log2 units.
-//   pass 2 (colsum)   one wave per (sequence, kv head, 32 keys); the keys'
+//   pass 2 (colsum)   one wave per (sequence, kv head, 64 keys); the keys'
 //                     rows are the held A operand; every query tile at or
 //                     after the diagonal of every head of the group streams
 //                     through the B operand; p = exp2(s - lse_i) is summed
 //                     per key row in registers, then across the 32 lanes
 //                     that share the rows -> acc0.
+// A wave holds two 32-row tiles, so every streamed tile feeds two
+// independent MFMA chains.
 // The two passes compute bit-identical scores (same operands, same MFMA
 // sequence), so every p <= 1. Only the diagonal tile of a wave is masked.
 // The streamed operand tile (keys in pass 1, queries in pass 2) is shared by
@@ -44,8 +46,10 @@ typedef unsigned ps_u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPsWaves = 4;                 // waves per block
 constexpr int kPsThreads = kPsWaves * kWave;
-constexpr int kPsTile = 32;                 // rows (keys or queries) per wave
-constexpr int kPsBlockRows = kPsWaves * kPsTile;
+constexpr int kPsTile = 32;                 // rows of one MFMA operand tile
+constexpr int kPsTilesPerWave = 2;          // operand tiles a wave holds
+constexpr int kPsWaveRows = kPsTilesPerWave * kPsTile;
+constexpr int kPsBlockRows = kPsWaves * kPsWaveRows;
 constexpr float kPsLog2e = 1.4426950408889634f;
 
 // MFMA 32x32x16 operand layout (lane l): A[l%32][8*(l/32) + 0..7],
@@ -112,7 +116,7 @@ struct PsStage {
 };
 
 template <int D>
-__global__ __launch_bounds__(kPsThreads) void ps_rowstat_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kPsThreads, 3) void ps_rowstat_kernel(const uint16_t* __restrict__ q,
                                                                   const uint16_t* __restrict__ k, int hq,
                                                                   int hkv, int T, int nh, int nib,
                                                                   float* __restrict__ lse) {
@@ -125,60 +129,84 @@ __global__ __launch_bounds__(kPsThreads) void ps_rowstat_kernel(const uint16_t* 
   const int nhi = static_cast<int>(blockIdx.x) % nh;  // n * hq + h
   const int n = nhi / hq, h = nhi % hq;
   const int g = h / (hq / hkv);
-  const int i0 = ib * kPsBlockRows + wave * kPsTile;
+  // the wave's queries: two tiles of 32, i0 .. i0 + 63
+  const int i0 = ib * kPsBlockRows + wave * kPsWaveRows;
   const bool active = i0 < T;  // every wave takes part in the copies and barriers
-  const int i = i0 + lane % 32;  // this lane's query column
   const uint16_t* kb = k + (static_cast<int64_t>(n) * hkv + g) * T * D;
-  ps_half8 bq[KS];
-  load_rows<D>(q + static_cast<int64_t>(nhi) * T * D, min(i, T - 1), bq);
+  const uint16_t* qb = q + static_cast<int64_t>(nhi) * T * D;
+  int iq[kPsTilesPerWave];
+  ps_half8 bq[kPsTilesPerWave][KS];
+#pragma unroll
+  for (int u = 0; u < kPsTilesPerWave; ++u) {
+    iq[u] = i0 + u * kPsTile + lane % 32;  // this lane's query column in tile u
+    load_rows<D>(qb, min(iq[u], T - 1), bq[u]);
+  }
   const float c = kPsLog2e / sqrtf(static_cast<float>(D));
-  // key tiles 0 .. diag of this wave (the diagonal tile holds t = i and is
-  // the only one with keys after some of the wave's queries); the block
+  // key tiles 0 .. diag + u for query tile u (its diagonal tile holds t = i
+  // and is the only one with keys after some of its queries); the block
   // walks the tiles of its last active wave
   const int diag = i0 / kPsTile;
   const int last = min(ib * kPsBlockRows + kPsBlockRows - 1, T - 1) / kPsTile;
-  float m = -INFINITY, l = 0.0f;  // log2-domain running max and sum of the lane's keys
+  float m[kPsTilesPerWave], l[kPsTilesPerWave];  // log2-domain running max and sum per column
+#pragma unroll
+  for (int u = 0; u < kPsTilesPerWave; ++u) m[u] = -INFINITY, l[u] = 0.0f;
   Stage st;
   st.load(kb, 0, T);
   st.store(kt[0]);
   __syncthreads();
   for (int tt = 0; tt <= last; ++tt) {
     if (tt < last) st.load(kb, (tt + 1) * kPsTile, T);
-    if (active && tt <= diag) {
+    if (active && tt <= diag + kPsTilesPerWave - 1) {
       ps_half8 ka[KS];
       Stage::operand(kt[tt & 1], ka);
-      ps_floatx16 s = scores<D>(ka, bq);
-      if (tt == diag) {
-        const int t0 = tt * kPsTile;
+      ps_floatx16 s[kPsTilesPerWave];
+      // independent accumulator chains for the query tiles
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (t0 + row_of(r, lane) > i) s[r] = -INFINITY;  // causal
+      for (int u = 0; u < kPsTilesPerWave; ++u) s[u] = ps_floatx16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int u = 0; u < kPsTilesPerWave; ++u)
+          s[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks], bq[u][ks], s[u], 0, 0, 0);
+      const int t0 = tt * kPsTile;
+#pragma unroll
+      for (int u = 0; u < kPsTilesPerWave; ++u) {
+        if (tt > diag + u) continue;  // keys all after tile u's queries
+        if (tt == diag + u) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (t0 + row_of(r, lane) > iq[u]) s[u][r] = -INFINITY;  // causal
+        }
+        float mx = s[u][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[u][r]);
+        const float mn = fmaxf(m[u], mx * c);
+        const float mref = fmaxf(mn, -FLT_MAX);  // exp2(-inf - mref) = 0 while nothing is seen
+        float lu = l[u] * ps_exp2(m[u] - mref);
+        m[u] = mn;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lu += ps_exp2(fmaf(s[u][r], c, -mref));
+        l[u] = lu;
       }
-      float mx = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      const float mn = fmaxf(m, mx * c);
-      const float mref = fmaxf(mn, -FLT_MAX);  // exp2(-inf - mref) = 0 while nothing is seen
-      l *= ps_exp2(m - mref);
-      m = mn;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) l += ps_exp2(fmaf(s[r], c, -mref));
     }
     // the other buffer was last read before the previous barrier
     if (tt < last) st.store(kt[(tt + 1) & 1]);
     __syncthreads();
   }
   if (!active) return;
-  // lanes l and l + 32 hold the two halves of column i's key rows
-  const float mo = shfl_xor_f(m, 32), lo = shfl_xor_f(l, 32);
-  const float M = fmaxf(m, mo);  // finite: key t = i is in lane l or l + 32
-  const float L = l * ps_exp2(m - M) + lo * ps_exp2(mo - M);  // >= 1
-  // log2-sum-exp of the row: p[i][t] = exp2(s[i][t] * c - lse[i])
-  if (lane < 32 && i < T) lse[static_cast<int64_t>(nhi) * T + i] = M + __builtin_amdgcn_logf(L);
+#pragma unroll
+  for (int u = 0; u < kPsTilesPerWave; ++u) {
+    // lanes l and l + 32 hold the two halves of column i's key rows
+    const float mo = shfl_xor_f(m[u], 32), lo = shfl_xor_f(l[u], 32);
+    const float M = fmaxf(m[u], mo);  // finite: key t = i is in lane l or l + 32
+    const float L = l[u] * ps_exp2(m[u] - M) + lo * ps_exp2(mo - M);  // >= 1
+    // log2-sum-exp of the row: p[i][t] = exp2(s[i][t] * c - lse[i])
+    if (lane < 32 && iq[u] < T) lse[static_cast<int64_t>(nhi) * T + iq[u]] = M + __builtin_amdgcn_logf(L);
+  }
 }
 
 template <int D>
-__global__ __launch_bounds__(kPsThreads) void ps_colsum_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kPsThreads, 3) void ps_colsum_kernel(const uint16_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ k, int hq,
                                                                  int hkv, int T, int ng,
                                                                  const float* __restrict__ lse,
@@ -194,17 +222,22 @@ __global__ __launch_bounds__(kPsThreads) void ps_colsum_kernel(const uint16_t* _
   const int ngi = static_cast<int>(blockIdx.x) % ng;  // n * hkv + g
   const int n = ngi / hkv, g = ngi % hkv;
   const int rep = hq / hkv;
-  const int t0 = tb * kPsBlockRows + wave * kPsTile;
+  // the wave's keys: two tiles of 32, t0 .. t0 + 63
+  const int t0 = tb * kPsBlockRows + wave * kPsWaveRows;
   const bool active = t0 < T;  // every wave takes part in the copies and barriers
-  ps_half8 ka[KS];
-  load_rows<D>(k + static_cast<int64_t>(ngi) * T * D, min(t0 + lane % 32, T - 1), ka);
-  const float c = kPsLog2e / sqrtf(static_cast<float>(D));
-  float col[16];
+  ps_half8 ka[kPsTilesPerWave][KS];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) col[r] = 0.0f;
+  for (int u = 0; u < kPsTilesPerWave; ++u)
+    load_rows<D>(k + static_cast<int64_t>(ngi) * T * D, min(t0 + u * kPsTile + lane % 32, T - 1), ka[u]);
+  const float c = kPsLog2e / sqrtf(static_cast<float>(D));
+  float col[kPsTilesPerWave][16];
+#pragma unroll
+  for (int u = 0; u < kPsTilesPerWave; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) col[u][r] = 0.0f;
   // the block walks query tiles first .. ntiles-1 of every head of the
-  // group; wave w starts at its diagonal tile first + w
-  const int first = tb * kPsWaves, ntiles = (T - 1) / kPsTile + 1;
+  // group; key tile u of the wave starts at its diagonal query tile diag + u
+  const int first = tb * (kPsBlockRows / kPsTile), ntiles = (T - 1) / kPsTile + 1;
   const int per_head = ntiles - first;
   const int total = rep * per_head;
   const int diag = t0 / kPsTile;
@@ -232,15 +265,26 @@ __global__ __launch_bounds__(kPsThreads) void ps_colsum_kernel(const uint16_t* _
       ps_half8 bq[KS];
       Stage::operand(qt[j & 1], bq);
       const float li = qlse[j & 1][lane % 32];
-      ps_floatx16 s = scores<D>(ka, bq);
-      if (it == diag) {  // diagonal tile: causal mask
-        const int i = it * kPsTile + lane % 32;
+      const int i = it * kPsTile + lane % 32;
+      ps_floatx16 s[kPsTilesPerWave];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (t0 + row_of(r, lane) > i) s[r] = -INFINITY;
+      for (int u = 0; u < kPsTilesPerWave; ++u) s[u] = ps_floatx16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int u = 0; u < kPsTilesPerWave; ++u)
+          s[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[u][ks], bq[ks], s[u], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < kPsTilesPerWave; ++u) {
+        if (it < diag + u) continue;  // queries all before tile u's keys
+        if (it == diag + u) {         // diagonal tile: causal mask
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (t0 + u * kPsTile + row_of(r, lane) > i) s[u][r] = -INFINITY;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) col[u][r] += ps_exp2(fmaf(s[u][r], c, -li));
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) col[r] += ps_exp2(fmaf(s[r], c, -li));
     }
     if (j + 1 < total) stage((j + 1) & 1);
     __syncthreads();
@@ -248,22 +292,26 @@ __global__ __launch_bounds__(kPsThreads) void ps_colsum_kernel(const uint16_t* _
   if (!active) return;
   // sum over the 32 query columns of the lanes that share l / 32
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float v = col[r];
-    v += shfl_xor_f(v, 1);
-    v += shfl_xor_f(v, 2);
-    v += shfl_xor_f(v, 4);
-    v += shfl_xor_f(v, 8);
-    v += shfl_xor_f(v, 16);
-    col[r] = v;
-  }
+  for (int u = 0; u < kPsTilesPerWave; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = col[u][r];
+      v += shfl_xor_f(v, 1);
+      v += shfl_xor_f(v, 2);
+      v += shfl_xor_f(v, 4);
+      v += shfl_xor_f(v, 8);
+      v += shfl_xor_f(v, 16);
+      col[u][r] = v;
+    }
   if (lane % 32 == 0) {
     float* out = acc0 + static_cast<int64_t>(ngi) * T;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = t0 + row_of(r, lane);
-      if (t < T) out[t] = col[r];
-    }
+    for (int u = 0; u < kPsTilesPerWave; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = t0 + u * kPsTile + row_of(r, lane);
+        if (t < T) out[t] = col[u][r];
+      }
   }
 }
 
