@@ -976,14 +976,16 @@ static int split_blocks_per_cu(int d, int bits, int rt) {
 // bound by VALU issue, and a token costs about the same instructions in
 // both tiers (4 heads x d multiply-adds for the score and as many for the
 // value sum; the low-bit unpacking roughly matches the FP16 tier's wider
-// lane groups): the time of a tier is its token count.
+// lane groups): the time of a tier is its token count, an FP16 token
+// weighted 1.3 (on the 32K GQA shape, token shares of 1:1 and 1.3:1 gave a
+// split kernel of 29.6 and 28.7 us, byte shares 34.2 us).
 DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq) {
   DecodePlan pl;
   pl.RT = (rep % 4 == 0) ? 4 : (rep % 2 == 0 ? 2 : 1);
   pl.tiles = rep / pl.RT;
   const double b16 = static_cast<double>(cap16) * 4.0 * d;
   const double bq = static_cast<double>(nq) * 2.0 * (d * bits / 8 + 4 * (d / group));
-  const double t16 = pl.RT == 1 ? b16 : static_cast<double>(cap16);
+  const double t16 = pl.RT == 1 ? b16 : 1.3 * cap16;
   const double tq = pl.RT == 1 ? bq : static_cast<double>(nq);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
   long per_unit = (static_cast<long>(kCUs) * split_blocks_per_cu(d, bits, pl.RT)) / units;
