@@ -145,6 +145,45 @@ def calibrate_copy(nbytes=1 << 30, reps=5):
                       "copy_GBps": 2 * nbytes / t / 1e9}), flush=True)
 
 
+def read_ceiling(args, log):
+    """A plain streaming read (mikv_read_probe: 16-byte nontemporal loads,
+    one contiguous chunk per block) of as many bytes as one split-kernel
+    launch of the workload, timed like the decode kernels: 1 GiB read flush
+    before each launch, HIP events on the stream. Grids of 1024 to 8192
+    blocks are tried; the fastest is the practical HBM read ceiling the
+    decode kernels are compared against, next to the 8 TB/s vendor peak."""
+    import torch
+    from mixed_precision_decode_amd import _lib as L
+    from mixed_precision_decode_amd import synth as S
+    cfg = S.CONFIGS[args.workload]
+    nbytes = int(split_bytes(cfg, cfg.T + 1)) // 16 * 16
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    fo = torch.empty((), dtype=torch.float32, device="cuda")
+    res = {}
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        for _ in range(args.warmup):
+            L.mikv_read_probe(buf, blocks, sink)
+        evs = _events(args.steps)
+        for e0, e1 in evs:
+            torch.sum(flush, dim=0, out=fo)
+            e0.record()
+            L.mikv_read_probe(buf, blocks, sink)
+            e1.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        res[blocks] = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9}
+        log(f"[bench] streaming read of {nbytes / 1e6:.1f} MB, {blocks} blocks: {us:.1f} us, "
+            f"{res[blocks]['GBps']:.0f} GB/s")
+    best = max(res, key=lambda b: res[b]["GBps"])
+    gbps = res[best]["GBps"]
+    return {"metric": "streaming-read ceiling GB/s", "value": gbps, "unit": "GB/s", "higher_is_better": True,
+            "steps": args.steps, "warmup": args.warmup, "bytes": nbytes, "best_blocks": best,
+            "frac_of_peak": gbps / HBM_PEAK_GBPS, "kernel": "mikv_read_probe (plain 16-byte nontemporal reads)",
+            "by_blocks": res, "config": {"workload": cfg.name}}
+
+
 def _events(n):
     import torch
     return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
@@ -289,6 +328,8 @@ def main():
                     help="only run a plain 1 GiB device copy (reference kernel for HBM counters)")
     ap.add_argument("--criticalkv", action="store_true",
                     help="only time the CriticalKV prefill select (32 heads, 32K tokens); one JSON line")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only time a plain streaming read of one split-kernel launch's bytes; one JSON line")
     ap.add_argument("--prefill", action="store_true",
                     help="only time the workload's prefill kernels (balancer, build, heavy-hitter "
                          "scores); one JSON line")
@@ -296,9 +337,10 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    if args.criticalkv or args.prefill:
+    if args.criticalkv or args.prefill or args.read_ceiling:
         log = lambda *a: print(*a, file=sys.stderr, flush=True)
-        print(json.dumps(bench_criticalkv(args, log) if args.criticalkv else bench_prefill(args, log)), flush=True)
+        fn = bench_criticalkv if args.criticalkv else (bench_prefill if args.prefill else read_ceiling)
+        print(json.dumps(fn(args, log)), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs the MiKV path on one GPU only; --gpus must be 1 "

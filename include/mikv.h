@@ -218,6 +218,20 @@ mikv_status mikv_prefill_scores(const mikv_dims* dims, int32_t T,
                                 void* stream);
 
 /*
+ * Measurement helper, not a step of the method: a plain streaming read of
+ * `bytes` of device memory at p (16-byte nontemporal loads, `blocks`
+ * workgroups of 256 threads, each reading one contiguous chunk), so that the
+ * HBM bandwidth of the decode kernels can be compared with what a kernel
+ * that only reads reaches on the same device. sink [blocks] uint32 receives
+ * one word per block (an XOR of the data, which keeps the loads live).
+ * bytes == 0 enqueues nothing.
+ * Errors: NULL p or sink -> MIKV_ERR_NULL; p not 16-byte aligned, bytes not
+ * a multiple of 16, blocks < 1 -> MIKV_ERR_SHAPE.
+ */
+mikv_status mikv_read_probe(const void* p, size_t bytes, int32_t blocks,
+                            uint32_t* sink, void* stream);
+
+/*
  * Source of the prefill build of mikv_h2o_update_select.
  *   k    [batch][hkv][T][d] fp16  prompt keys (multiplied by b when b != NULL,
  *                                 exactly as mikv_balance_prefill's kb)

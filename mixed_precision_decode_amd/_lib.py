@@ -49,6 +49,7 @@ _SIGS = {
     "mikv_balance_prefill": (C.c_int, [C.POINTER(MikvDims), _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mikv_prefill_scores_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
     "mikv_prefill_scores": (C.c_int, [C.POINTER(MikvDims), _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mikv_read_probe": (C.c_int, [_vp, _sz, _i32, _vp, _vp]),
     "mikv_quantize_tokens": (C.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp]),
     "mikv_decode_attn_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
     "mikv_decode_attn": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _vp, _vp, _vp,
@@ -188,6 +189,12 @@ def mikv_prefill_scores(dims: Dims, T: int, q, k, acc0, ws, stream=None):
         _ptr(q, "f16", (n, hq, T, d), "q"), _ptr(k, "f16", (n, hkv, T, d), "k"),
         _ptr(acc0, _f32t(), (n, hkv, T), "acc0"),
         _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mikv_read_probe(buf, blocks: int, sink, stream=None):
+    """Streaming read of the whole of `buf` (measurement helper)."""
+    _check(lib().mikv_read_probe(_ptr(buf, name="buf"), buf.numel() * buf.element_size(), blocks,
+                                 _ptr(sink, None, (blocks,), "sink"), _stream(stream)))
 
 
 def mikv_quantize_tokens(x, rows, codes, sz, group: int, bits: int, stream=None):

@@ -113,6 +113,14 @@ mikv_status mikv_prefill_scores(const mikv_dims* m, int32_t T, const uint16_t* q
                                         static_cast<hipStream_t>(stream)));
 }
 
+// ---------------------------------------------------------------- streaming-read probe
+mikv_status mikv_read_probe(const void* p, size_t bytes, int32_t blocks, uint32_t* sink, void* stream) {
+  if (bytes == 0) return MIKV_OK;
+  if (!p || !sink) return MIKV_ERR_NULL;
+  if (!aligned16(p) || bytes % 16 != 0 || blocks < 1) return MIKV_ERR_SHAPE;
+  return from_hip(launch_read_probe(p, bytes, blocks, sink, static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------- quantize
 mikv_status mikv_quantize_tokens(const uint16_t* x, const int32_t* rows, int64_t n_rows,
                                  int32_t d, int32_t group, int32_t bits, uint8_t* codes,

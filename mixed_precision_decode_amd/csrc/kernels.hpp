@@ -89,6 +89,9 @@ size_t prefill_scores_ws_bytes(int batch, int hq, int T);
 hipError_t launch_prefill_scores(int batch, int hq, int hkv, int d, int T, const uint16_t* q,
                                  const uint16_t* k, float* acc0, void* ws, hipStream_t stream);
 
+// Streaming-read probe (measurement): reads `bytes` (a multiple of 16) of p.
+hipError_t launch_read_probe(const void* p, size_t bytes, int blocks, uint32_t* sink, hipStream_t stream);
+
 size_t criticalkv_ws_bytes(int H, int T, int d, int hidden);
 hipError_t launch_criticalkv(const float* A, const uint16_t* V, const uint16_t* W, int H, int T,
                              int d, int hidden, int b1, int b2, int32_t* idx, float* score2,

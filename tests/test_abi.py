@@ -29,7 +29,7 @@ def _header_functions():
 
 def test_exports_every_declared_function(lib):
     names = _header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L._SIGS)
@@ -106,6 +106,16 @@ def test_prefill_scores_validation(lib):
     assert call(T=-1) == L.MIKV_ERR_SHAPE
     assert call(ws_bytes=need - 1) == L.MIKV_ERR_WORKSPACE
     assert call(T=0, q=None, k=None, acc=None) == L.MIKV_OK    # nothing to do, nothing enqueued
+
+
+def test_read_probe_validation(lib):
+    call = lambda p=FAKE, nbytes=1 << 20, blocks=8, sink=FAKE: lib.mikv_read_probe(p, nbytes, blocks, sink, None)
+    assert call(p=None) == L.MIKV_ERR_NULL
+    assert call(sink=None) == L.MIKV_ERR_NULL
+    assert call(p=FAKE + 4) == L.MIKV_ERR_SHAPE
+    assert call(nbytes=(1 << 20) + 8) == L.MIKV_ERR_SHAPE
+    assert call(blocks=0) == L.MIKV_ERR_SHAPE
+    assert call(nbytes=0, p=None, sink=None) == L.MIKV_OK
 
 
 def test_decode_step_validation(lib):

@@ -406,3 +406,17 @@ def test_decode_attn_timed_matches_plain(name, over):
     assert np.array_equal(p1.view(np.uint32), p2.view(np.uint32))
     for key in L.Cache.NAMES:
         assert np.array_equal(np.asarray(c1[key]).view(np.uint8), np.asarray(c2[key]).view(np.uint8)), key
+
+
+# ---------------------------------------------------------------- read probe
+@pytest.mark.parametrize("nbytes,blocks", [(16, 1), (4096 + 48, 7), (1 << 22, 1024), ((1 << 20) + 16 * 5, 4096)])
+def test_read_probe_reads_every_word(nbytes, blocks):
+    """The streaming-read probe (measurement helper) touches the whole
+    buffer: the XOR of its per-block words equals the XOR of all words."""
+    rng = np.random.default_rng(nbytes + blocks)
+    words = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32).copy()).cuda()
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    L.mikv_read_probe(buf, blocks, sink)
+    got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)
