@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kStageThreads) void ckv_stage1_kernel(const float* 
   uint32_t tau = 0xFFFFFFFFu;
   int need = 0;
   if (b1 > 0) {
-    block_radix_topm<kStageThreads>(T, b1, [&](int i, uint32_t* key) {
+    block_radix_topm<kStageThreads, 32>(T, b1, [&](int i, uint32_t* key) {
       *key = float_key(a[i]);
       return true;
     }, &tau, &need);
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kStageThreads) void ckv_stage2_kernel(int T, int b1
   uint32_t tau = 0xFFFFFFFFu;
   int need = 0;
   if (b2 > 0) {
-    block_radix_topm<kStageThreads>(T, b2, [&](int i, uint32_t* key) {
+    block_radix_topm<kStageThreads, 32>(T, b2, [&](int i, uint32_t* key) {
       if (s1[i]) return false;
       *key = float_key(sc[i]);
       return true;

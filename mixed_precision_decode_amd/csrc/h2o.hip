@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kSelThreads) void h2o_prefill_select_kernel(H2OArgs
   uint32_t tau = 0xFFFFFFFFu;
   int need = 0;
   if (H > 0) {
-    block_radix_topm<kSelThreads>(ncand, H, [&](int i, uint32_t* key) {
+    block_radix_topm<kSelThreads, 32>(ncand, H, [&](int i, uint32_t* key) {
       *key = float_key(acc0[i]);
       return true;
     }, &tau, &need);

@@ -56,7 +56,11 @@ __device__ __forceinline__ int block_scan_add(int v, int* total) {
 // Requires 1 <= m <= count. Each wave counts into its own histogram (keys
 // such as probabilities share few top bytes, so one shared histogram
 // serialises the atomics); the histograms are summed before the digit search.
-template <int NT = 256, class KeyFn>
+//
+// When n <= NT * KPT, each thread first loads its keys (elements tid,
+// tid + NT, ...) into registers with every load in flight, and the four
+// passes count from registers; otherwise each pass reads the keys again.
+template <int NT = 256, int KPT = 0, class KeyFn>
 __device__ void block_radix_topm(int n, int m, KeyFn keyfn, uint32_t* tau, int* need) {
   constexpr int NWV = NT / kWave;
   __shared__ uint32_t hist[NWV][256];
@@ -65,12 +69,31 @@ __device__ void block_radix_topm(int n, int m, KeyFn keyfn, uint32_t* tau, int* 
   const int tid = threadIdx.x, wv = tid / kWave;
   uint32_t prefix = 0, mask = 0;
   int nd = m;
+  constexpr int KC = KPT > 0 ? KPT : 1;
+  static_assert(KC <= 32, "validity of the cached keys is one 32-bit mask");
+  const bool cached = KPT > 0 && n <= NT * KPT;
+  uint32_t kc[KC];
+  uint32_t kvalid = 0;
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const int i = tid + j * NT;
+      kc[j] = 0;
+      if (i < n && keyfn(i, &kc[j])) kvalid |= 1u << j;
+    }
+  }
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < NWV * 256; i += NT) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      uint32_t key;
-      if (keyfn(i, &key) && (key & mask) == prefix) atomicAdd(&hist[wv][(key >> shift) & 0xFFu], 1u);
+    if (cached) {
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        if (((kvalid >> j) & 1u) && (kc[j] & mask) == prefix) atomicAdd(&hist[wv][(kc[j] >> shift) & 0xFFu], 1u);
+    } else {
+      for (int i = tid; i < n; i += NT) {
+        uint32_t key;
+        if (keyfn(i, &key) && (key & mask) == prefix) atomicAdd(&hist[wv][(key >> shift) & 0xFFu], 1u);
+      }
     }
     __syncthreads();
     if (NWV > 1) {
