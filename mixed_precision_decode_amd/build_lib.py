@@ -37,9 +37,15 @@ FLAGS = [
 ]
 
 
+# Per-source options. The CriticalKV projection keeps its MFMA accumulators in
+# ordinary VGPRs (202 of them, still two waves per SIMD), so the |.| row-sum
+# epilogue reads them directly instead of copying each one out of an AGPR.
+EXTRA_FLAGS = {"criticalkv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
