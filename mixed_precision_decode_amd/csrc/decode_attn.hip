@@ -730,13 +730,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
   }
 }
 
-// Grid: (unit, output chunk). Block y of unit x combines the split
-// partials of kMergeOut outputs (head, channel) of the unit, kMergeTPO threads
-// per output, each summing a strided subset of the splits, so a unit with
-// many splits spreads its partials over many blocks and loads. Block 0 of
-// the unit also turns the FP16-tier scores into p16 and, when FUSE, applies
-// the decode-step H2O update (acc += p16, drop the worst candidate, demote
-// it), which the stand-alone H2O kernel would otherwise do in a third launch.
+// Grid: (unit, output chunk [+ 1]). An output block of unit x combines the
+// split partials of kMergeOut * G outputs (head, channel) of the unit,
+// kMergeTPO threads per output, each summing a strided subset of the splits,
+// so a unit with many splits spreads its partials over many blocks and
+// loads. One block per unit turns the FP16-tier scores into p16 and, when
+// FUSE, applies the decode-step H2O update (acc += p16, drop the worst
+// candidate, demote it), which the stand-alone H2O kernel would otherwise do
+// in a third launch. That is an extra block beside the output blocks when
+// the grid stays within one wave of blocks (32K GQA: step 43.4 -> 40.9 us),
+// else output block 0 after its outputs (a 1536-block grid cost the GQA
+// batch about 1 us).
 // Dynamic LDS: [rep][S] (max, sum) pairs, then [rep] maxima and [rep]
 // reciprocal sums.
 constexpr int kMergeOut = 64;
@@ -748,7 +752,7 @@ constexpr int kMergeHeads = 4;   // heads whose FP16-tier scores are loaded up f
 #endif
 constexpr long kMergeMaxBlocks = MIKV_MERGE_MAX_BLOCKS;  // above this, one block takes several output groups
 template <int D, int BITS, int NL, bool FUSE, int G>
-__global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p, int RT, H2OView hv) {
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p, int RT, H2OView hv, bool sep) {
   extern __shared__ float2 sml[];
   __shared__ float red[kThreads];
   const int unit = blockIdx.x;
@@ -764,10 +768,16 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   const float* __restrict__ pov = p.part_o;
   const float* __restrict__ sc = p.sc16 + static_cast<int64_t>(unit) * rep * cap16;
   const int64_t base16 = static_cast<int64_t>(unit) * cap16;
+  // With sep, the unit's last block (chunk gridDim.y - 1) turns the FP16-tier
+  // scores into p16 and applies the H2O update while the others combine the
+  // outputs, side by side; without it, block 0 does both, one after the other.
+  const bool last = chunk == static_cast<int>(gridDim.y) - 1;
+  const bool do_out = !(sep && last);
+  const bool pblk = sep ? last : chunk == 0;
   // heads this block needs (statistics): its outputs' heads, or all for p16
   const int out0 = chunk * kMergeOut * G;
-  const int h_lo = (chunk == 0) ? 0 : out0 / D;
-  const int h_hi = (chunk == 0) ? rep : min(rep, (out0 + kMergeOut * G - 1) / D + 1);
+  const int h_lo = pblk ? 0 : out0 / D;
+  const int h_hi = pblk ? rep : min(rep, (out0 + kMergeOut * G - 1) / D + 1);
   // (1) issue every load before the first wait: the thread's partial
   // outputs, the FP16-tier scores of up to kMergeHeads heads and the H2O
   // state (chunk 0), then the split statistics, whose LDS stores wait for
@@ -781,14 +791,16 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   };
   constexpr int PF = (G == 1) ? 8 : 2;  // splits per thread loaded up front, per group
   float pf[G][PF];
+  if (do_out) {
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    const int oi = out_of(gi);
-    const float* po = part_of(oi < rep * D ? oi : 0);
+    for (int gi = 0; gi < G; ++gi) {
+      const int oi = out_of(gi);
+      const float* po = part_of(oi < rep * D ? oi : 0);
 #pragma unroll
-    for (int k = 0; k < PF; ++k) {
-      const int s = sub + k * kMergeTPO;
-      pf[gi][k] = (oi < rep * D && s < S) ? po[static_cast<int64_t>(s) * RT * D] : 0.0f;
+      for (int k = 0; k < PF; ++k) {
+        const int s = sub + k * kMergeTPO;
+        pf[gi][k] = (oi < rep * D && s < S) ? po[static_cast<int64_t>(s) * RT * D] : 0.0f;
+      }
     }
   }
   const bool slots_in_regs = cap16 <= kMergeSlots * kThreads;
@@ -799,7 +811,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   // slot indices past the tier are clamped (their values are never used),
   // so the loads issue back to back without per-lane branches
   const int nslot = (cap16 + kThreads - 1) / kThreads;
-  if (chunk == 0) {
+  if (pblk) {
     if (slots_in_regs) {
 #pragma unroll
       for (int h = 0; h < kMergeHeads; ++h) {
@@ -847,36 +859,38 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   __syncthreads();
   // (3) outputs: each thread sums its subset of splits, then the kMergeTPO
   // threads of an output combine through LDS
+  if (do_out) {
 #pragma unroll
-  for (int gi = 0; gi < G; ++gi) {
-    const int oi = out_of(gi);
-    const bool has_out = oi < rep * D;
-    const int ohl = oi / D, oc = oi % D;
-    float v = 0.0f;
-    if (has_out) {
-      const float M = sM[ohl];
-      const float2* ml = sml + ohl * S;
+    for (int gi = 0; gi < G; ++gi) {
+      const int oi = out_of(gi);
+      const bool has_out = oi < rep * D;
+      const int ohl = oi / D, oc = oi % D;
+      float v = 0.0f;
+      if (has_out) {
+        const float M = sM[ohl];
+        const float2* ml = sml + ohl * S;
 #pragma unroll
-      for (int k = 0; k < PF; ++k) {
-        const int s = sub + k * kMergeTPO;
-        if (s < S) v += pf[gi][k] * fast_exp2(ml[s].x - M);
-      }
-      const float* po = part_of(oi);
+        for (int k = 0; k < PF; ++k) {
+          const int s = sub + k * kMergeTPO;
+          if (s < S) v += pf[gi][k] * fast_exp2(ml[s].x - M);
+        }
+        const float* po = part_of(oi);
 #pragma unroll 4
-      for (int s = sub + PF * kMergeTPO; s < S; s += kMergeTPO)
-        v += po[static_cast<int64_t>(s) * RT * D] * fast_exp2(ml[s].x - M);
-    }
-    if (gi > 0) __syncthreads();  // the previous group's reads of red are done
-    red[tid] = v;
-    __syncthreads();
-    if (tid < kMergeOut && has_out) {
-      float t = 0.0f;
+        for (int s = sub + PF * kMergeTPO; s < S; s += kMergeTPO)
+          v += po[static_cast<int64_t>(s) * RT * D] * fast_exp2(ml[s].x - M);
+      }
+      if (gi > 0) __syncthreads();  // the previous group's reads of red are done
+      red[tid] = v;
+      __syncthreads();
+      if (tid < kMergeOut && has_out) {
+        float t = 0.0f;
 #pragma unroll
-      for (int k = 0; k < kMergeTPO; ++k) t += red[tid + k * kMergeOut];
-      p.o[(static_cast<int64_t>(n) * p.hq + g * rep + ohl) * D + oc] = t * sIL[ohl];
+        for (int k = 0; k < kMergeTPO; ++k) t += red[tid + k * kMergeOut];
+        p.o[(static_cast<int64_t>(n) * p.hq + g * rep + ohl) * D + oc] = t * sIL[ohl];
+      }
     }
   }
-  if (chunk != 0) return;
+  if (!pblk) return;
   // (4) p16 = sum over the group's heads of the FP16-tier probabilities
   float* __restrict__ p16 = p.p16 + base16;
   auto prob = [&](int sl) {
@@ -1080,9 +1094,13 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   int G = 1;
   if (S <= 2 * kMergeTPO)
     while (G < 8 && G < groups && units * ((groups + G - 1) / G) > kMergeMaxBlocks) G *= 2;
-  const dim3 mgrid(static_cast<unsigned>(units), static_cast<unsigned>((groups + G - 1) / G));
+  // Output chunks, plus one block per unit for p16 and the H2O update while
+  // that still fits one wave of blocks; otherwise chunk 0 does that work too.
+  const int chunks = (groups + G - 1) / G;
+  const bool sep = units * (chunks + 1) <= kMergeMaxBlocks;
+  const dim3 mgrid(static_cast<unsigned>(units), static_cast<unsigned>(chunks + (sep ? 1 : 0)));
 #define MIKV_MERGE_G(NL_, F_, G_) \
-  decode_merge_kernel<D, BITS, NL_, F_, G_><<<mgrid, kThreads, lds, stream>>>(k, RT, hv)
+  decode_merge_kernel<D, BITS, NL_, F_, G_><<<mgrid, kThreads, lds, stream>>>(k, RT, hv, sep)
 #define MIKV_MERGE(NL_, F_)                   \
   do {                                        \
     if (G == 1) MIKV_MERGE_G(NL_, F_, 1);     \

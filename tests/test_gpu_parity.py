@@ -342,6 +342,9 @@ def test_graph_replay_matches_eager():
     ("llama3_8b_32k", dict(hq=8, hkv=2, T=20000, pct=25), 2),    # FP16 tier > 4096 slots: unfused path
     ("tiny", dict(batch=256), 4), ("tiny", dict(batch=512, bits=2, group=64), 3),  # one-pass kernel
     ("llama2_7b_layer", dict(T=700), 2),
+    # 1024 units: the merge grid is too large for a separate p16 / H2O block,
+    # so output block 0 of each unit does that work after its outputs
+    ("tiny", dict(batch=1024), 2),
 ])
 def test_decode_step_matches_separate_calls(name, over, steps):
     """mikv_decode_step is bit-identical to mikv_decode_attn followed by
