@@ -51,6 +51,10 @@ constexpr int kPsTilesPerWave = 2;          // operand tiles a wave holds
 constexpr int kPsWaveRows = kPsTilesPerWave * kPsTile;
 constexpr int kPsBlockRows = kPsWaves * kPsWaveRows;
 constexpr float kPsLog2e = 1.4426950408889634f;
+// Both kernels are compiled for at least three waves per SIMD (168 VGPRs):
+// left to itself the compiler took 170-190 registers, two waves per SIMD,
+// and the passes ran 15% slower.
+constexpr int kPsMinWaves = 3;
 
 // MFMA 32x32x16 operand layout (lane l): A[l%32][8*(l/32) + 0..7],
 // B[8*(l/32) + 0..7][l%32], D register r: row 8*(r/4) + 4*(l/32) + r%4,
@@ -63,14 +67,6 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ base, int
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
     f[ks] = __builtin_bit_cast(ps_half8, *reinterpret_cast<const uint4*>(p + 16 * ks));
-}
-
-template <int D>
-__device__ __forceinline__ ps_floatx16 scores(const ps_half8 (&a)[D / 16], const ps_half8 (&b)[D / 16]) {
-  ps_floatx16 c = {};
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) c = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], b[ks], c, 0, 0, 0);
-  return c;
 }
 
 // key row of accumulator register r within a 32-row tile
@@ -116,7 +112,7 @@ struct PsStage {
 };
 
 template <int D>
-__global__ __launch_bounds__(kPsThreads, 3) void ps_rowstat_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kPsThreads, kPsMinWaves) void ps_rowstat_kernel(const uint16_t* __restrict__ q,
                                                                   const uint16_t* __restrict__ k, int hq,
                                                                   int hkv, int T, int nh, int nib,
                                                                   float* __restrict__ lse) {
@@ -206,7 +202,7 @@ __global__ __launch_bounds__(kPsThreads, 3) void ps_rowstat_kernel(const uint16_
 }
 
 template <int D>
-__global__ __launch_bounds__(kPsThreads, 3) void ps_colsum_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kPsThreads, kPsMinWaves) void ps_colsum_kernel(const uint16_t* __restrict__ q,
                                                                  const uint16_t* __restrict__ k, int hq,
                                                                  int hkv, int T, int ng,
                                                                  const float* __restrict__ lse,
