@@ -28,7 +28,8 @@ are a seeded stand-in: log-normal draws scaled so that the total mass equals
 ``rep * T`` (every prefill query row of every query head in the group carries
 probability mass 1), rounded to a 2^-10 grid so that exact ties occur, with
 about 5% exact zeros. The pages do not describe how H2O initialises its scores,
-so this input is drawn, not computed.
+so for the decode workloads this input is drawn, with exact ties on purpose;
+the library's mikv_prefill_scores computes acc0 from a prompt's q and k.
 
 Every array of one (sequence, kv head) unit comes from its own generator
 seeded by ``(seed, stream, n, g[, step])`` so that any unit can be drawn on
