@@ -239,3 +239,42 @@ def test_tier_offsets_limit(lib):
     big16 = _dims(cap16=1 << 23, capq=100)   # 2^23 slots * 256 B = 2^31 B of fp16 rows
     assert lib.mikv_decode_attn(C.byref(big16.c()), C.byref(c), (1 << 23) + 5, FAKE, FAKE, FAKE, FAKE,
                                 FAKE, FAKE, FAKE, 1 << 40, None) == L.MIKV_ERR_SHAPE
+
+
+def test_header_is_plain_c(lib, tmp_path):
+    """include/mikv.h compiles as C99 on its own (no HIP or C++ headers), and
+    a C program linked against the library gets the documented statuses
+    from host-side validation."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "abi_check.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "mikv.h"
+int main(void) {
+  mikv_dims d = {2, 8, 2, 128, 64, 4, 11, 100};
+  mikv_dims bad = d;
+  bad.hq = 7;
+  int fails = 0;
+  if (mikv_abi_version() != MIKV_ABI_VERSION) fails++;
+  if (mikv_decode_attn_workspace(&d, 80) == 0) fails++;
+  if (mikv_decode_attn(&bad, NULL, 50, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) != MIKV_ERR_SHAPE) fails++;
+  if (mikv_decode_attn(&d, NULL, 50, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) != MIKV_ERR_NULL) fails++;
+  if (mikv_prefill_scores(&d, 0, NULL, NULL, NULL, NULL, 0, NULL) != MIKV_OK) fails++;
+  if (mikv_read_probe(NULL, 16, 1, NULL, NULL) != MIKV_ERR_NULL) fails++;
+  printf("%s %d\n", mikv_status_str(MIKV_ERR_CAPACITY), fails);
+  return fails;
+}
+''')
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(L.LIB_PATH)
+    cmd = [gcc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"), str(src),
+           "-o", str(exe), "-L", libdir, "-lmikv", "-Wl,-rpath," + libdir]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.stdout, r.stderr)
+    assert r.stdout.strip().endswith(" 0")
