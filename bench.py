@@ -145,6 +145,44 @@ def calibrate_copy(nbytes=1 << 30, reps=5):
                       "copy_GBps": 2 * nbytes / t / 1e9}), flush=True)
 
 
+def bench_quantize(args, log):
+    """mikv_quantize_tokens on every prompt row of the workload, keys and
+    values (2 * batch * hkv * T rows of d fp16). HBM-bound: per row it reads
+    2d bytes and writes d*bits/8 code bytes plus an fp16 (scale, zero) pair
+    per group."""
+    import torch
+    from mixed_precision_decode_amd import _lib as L
+    from mixed_precision_decode_amd import synth as S
+    cfg = S.CONFIGS[args.workload]
+    _, k, v, _ = S.prefill_tensors(cfg, args.seed)
+    x = torch.from_numpy(np.ascontiguousarray(np.stack([k, v]).reshape(-1, cfg.d))).cuda()
+    n_rows = x.shape[0]
+    codes = torch.empty((n_rows, cfg.d * cfg.bits // 8), dtype=torch.uint8, device="cuda")
+    sz = torch.empty((n_rows, cfg.d // cfg.G, 2), dtype=torch.float16, device="cuda")
+    nbytes = n_rows * (2.0 * cfg.d + cfg.d * cfg.bits / 8 + 4.0 * cfg.d / cfg.G)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    fo = torch.empty((), dtype=torch.float32, device="cuda")
+    for _ in range(args.warmup):
+        L.mikv_quantize_tokens(x, None, codes, sz, cfg.G, cfg.bits)
+    evs = _events(args.steps)
+    for e0, e1 in evs:
+        torch.sum(flush, dim=0, out=fo)
+        e0.record()
+        L.mikv_quantize_tokens(x, None, codes, sz, cfg.G, cfg.bits)
+        e1.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    gbps = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] quantize {n_rows} rows: {us:.1f} us, {gbps:.0f} GB/s")
+    return {"metric": "quantize GB/s", "value": gbps, "unit": "GB/s", "higher_is_better": True,
+            "steps": args.steps, "warmup": args.warmup, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": cfg.name, "rows": n_rows, "head_dim": cfg.d, "bits": cfg.bits,
+                       "group": cfg.G},
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gbps / HBM_PEAK_GBPS, "bytes_per_launch": nbytes, "kernel_us": us,
+                         "kernel": "quantize_rows_kernel"}}
+
+
 def read_ceiling(args, log):
     """A plain streaming read (mikv_read_probe: 16-byte nontemporal loads,
     one contiguous chunk per block) of as many bytes as one split-kernel
@@ -328,6 +366,8 @@ def main():
                     help="only run a plain 1 GiB device copy (reference kernel for HBM counters)")
     ap.add_argument("--criticalkv", action="store_true",
                     help="only time the CriticalKV prefill select (32 heads, 32K tokens); one JSON line")
+    ap.add_argument("--quantize", action="store_true",
+                    help="only time mikv_quantize_tokens on the workload's prompt rows; one JSON line")
     ap.add_argument("--read-ceiling", action="store_true",
                     help="only time a plain streaming read of one split-kernel launch's bytes; one JSON line")
     ap.add_argument("--prefill", action="store_true",
@@ -337,9 +377,10 @@ def main():
     if args.calibrate_copy:
         calibrate_copy()
         return
-    if args.criticalkv or args.prefill or args.read_ceiling:
+    if args.criticalkv or args.prefill or args.read_ceiling or args.quantize:
         log = lambda *a: print(*a, file=sys.stderr, flush=True)
-        fn = bench_criticalkv if args.criticalkv else (bench_prefill if args.prefill else read_ceiling)
+        fn = (bench_criticalkv if args.criticalkv else bench_prefill if args.prefill
+              else bench_quantize if args.quantize else read_ceiling)
         print(json.dumps(fn(args, log)), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

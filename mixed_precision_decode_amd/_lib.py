@@ -198,8 +198,12 @@ def mikv_read_probe(buf, blocks: int, sink, stream=None):
 
 
 def mikv_quantize_tokens(x, rows, codes, sz, group: int, bits: int, stream=None):
+    """Row r of codes/sz quantizes row rows[r] of x (rows given) or row r
+    (rows None); x holds whole rows of d channels."""
     n_rows, cb = codes.shape
     d = x.shape[-1]
+    if x.numel() % d != 0 or (rows is None and x.numel() < n_rows * d):
+        raise ValueError(f"x: {x.numel()} elements do not hold {n_rows} rows of {d}")
     _check(lib().mikv_quantize_tokens(
         _ptr(x, "f16", None, "x"), _ptr(rows, _i32t(), (n_rows,), "rows", optional=True),
         n_rows, d, group, bits,

@@ -115,11 +115,31 @@ __device__ __forceinline__ uint32_t quantize8(const float (&x)[8], uint32_t* sz_
   if (s16 != 0) {
     const float s = h2f(s16);
     const float z = h2f(z16);
+    // code = rint of the IEEE quotient fl((x - z) / s), found without the
+    // divide: y = (x - z) * rcp(s) is within 1.6 * 2^-23 |Q| of the exact
+    // quotient Q (rcp within 1 ulp, one rounded multiply) and fl(Q) within
+    // 2^-24 |Q|, so |y - fl(Q)| <= 2^-18 for the codes' range |Q| <= 16.
+    // When y is more than 2^-16 away from its nearest half-integer, y and
+    // fl(Q) lie in the same rounding interval and rint(y) = rint(fl(Q)); a
+    // lane with any value closer than that (about 1e-5 of values) takes the
+    // IEEE divide for all of its values.
+    const float r = __builtin_amdgcn_rcpf(s);
+    float t[8];
+    bool near_half = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float t = rintf((x[i] - z) / s);
-      t = fminf(fmaxf(t, 0.0f), qmax);
-      packed |= static_cast<uint32_t>(t) << (BITS * i);
+      const float y = (x[i] - z) * r;
+      near_half |= fabsf((y - floorf(y)) - 0.5f) <= 0x1p-16f;
+      t[i] = rintf(y);
+    }
+    if (near_half) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = rintf((x[i] - z) / s);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float c = fminf(fmaxf(t[i], 0.0f), qmax);
+      packed |= static_cast<uint32_t>(c) << (BITS * i);
     }
   }
   return packed;
