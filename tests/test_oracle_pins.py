@@ -482,3 +482,4 @@ def test_prefill_scores_match_causal_sdpa_weights():
     w = torch.nn.functional.scaled_dot_product_attention(qt, kt, eye, is_causal=True).numpy()
     ref = w.sum(axis=2).reshape(n, hkv, rep, T).sum(axis=2)
     assert np.allclose(O.prefill_scores(q, k), ref, rtol=1e-10, atol=1e-12)
+
