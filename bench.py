@@ -112,14 +112,18 @@ def cpu_baseline(cfg, cache_np, b_np, N, seed, step, budget_s):
     qd, kd, vd = S.decode_tensors(cfg.scaled(batch=1), seed, step)
     reps = 0
     t0 = time.perf_counter()
+    c0 = time.process_time()
     while True:
         O.decode_step(sub, N, qd, kd, vd, b_np[:1], cfg.recent, cfg.H)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return {"value": reps * N / el, "unit": "KV-tokens/s", "cores": int(threads),
-            "kind": "oracle",
+    # cores actually used: the process's CPU time over the wall time (numpy's
+    # elementwise work is single-threaded; only its BLAS calls use the pool)
+    busy = (time.process_time() - c0) / el
+    return {"value": reps * N / el, "unit": "KV-tokens/s", "cores": max(1, int(round(busy))),
+            "cores_busy": busy, "blas_threads": int(threads), "kind": "oracle",
             "sample": (f"{reps} oracle decode steps of 1 of {cfg.batch} sequences "
                        f"({cfg.hkv} kv heads, N={N}), fp64 numpy, {el:.1f} s; "
                        f"host os.cpu_count()={os.cpu_count()}")}
@@ -262,9 +266,12 @@ def bench_criticalkv(args, log):
         import oracle as O
         h = 0
         t0 = time.perf_counter()
+        c0 = time.process_time()
         O.criticalkv_select(A[h:h + 1], V[h:h + 1], W[h * cfg.d:(h + 1) * cfg.d], budget, cfg.alpha)
         el = time.perf_counter() - t0
+        busy = (time.process_time() - c0) / el
         cpu = {"value": el * cfg.H * 1e3, "unit": "ms per select (32 heads, extrapolated)", "kind": "oracle",
+               "cores": max(1, int(round(busy))), "cores_busy": busy,
                "sample": f"1 of {cfg.H} heads, fp64 numpy, {el:.1f} s"}
     return {"metric": "CriticalKV prefill select ms (MFMA projection TFLOP/s)", "value": ms, "unit": "ms",
             "higher_is_better": False, "steps": args.steps, "warmup": args.warmup, "dtype": "f16 MFMA, f32 accumulate",
