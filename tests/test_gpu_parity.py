@@ -423,3 +423,31 @@ def test_read_probe_reads_every_word(nbytes, blocks):
     L.mikv_read_probe(buf, blocks, sink)
     got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
     assert got == np.bitwise_xor.reduce(words)
+
+
+def test_quantize_golden_ties_on_device():
+    """The hand-derived quantizer vectors (tests/golden), including exact
+    half-integer quotients that round half to even, through the device
+    quantizer. Each golden group's values are tiled over a 32-channel group
+    of a d = 64 row (tiling keeps the group's min, max, scale and codes); the
+    device codes and (scale, zero) must equal the golden ones."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "quantizer_hand_vectors.json")))
+    d, group = 64, 32
+    for case in gold["cases"]:
+        g, bits = case["group"], case["bits"]
+        x = np.asarray(case["x"], F64).astype(F16).reshape(-1, g)
+        codes = np.asarray(case["codes"], np.int64).reshape(-1, g)
+        rows_x, rows_c, rows_sz = [], [], []
+        for i in range(x.shape[0]):            # one device row per golden group: both halves hold it
+            rows_x.append(np.tile(x[i], 2 * group // g))
+            rows_c.append(np.tile(codes[i], 2 * group // g))
+            rows_sz.append([[case["scale"][i], case["zero"][i]]] * 2)
+        xr = np.stack(rows_x).astype(F16)
+        out = torch.zeros((len(xr), d * bits // 8), dtype=torch.uint8, device="cuda")
+        sz = torch.zeros((len(xr), d // group, 2), dtype=torch.float16, device="cuda")
+        print(f"golden {case['name']}", flush=True)
+        L.mikv_quantize_tokens(dev(xr), None, out, sz, group, bits)
+        assert np.array_equal(O.unpack_codes(host(out), d, bits), np.stack(rows_c)), case["name"]
+        assert np.array_equal(host(sz).astype(F64), np.asarray(rows_sz, F64)), case["name"]
