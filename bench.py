@@ -16,8 +16,17 @@ dirty lines whose write-back would then compete with the measured kernel
 (--flush write shows that case, --flush none the warm-cache case). Step and
 kernel times come from HIP events recorded on the stream the kernels run on.
 
-Prints one JSON line (rank 0). --gpus N > 1 is refused: this build targets
-one GPU.
+The JSON line's roofline is the dominant kernel's: the split kernel, timed
+by start/stop events of its own launch (mikv_decode_attn_timed); the call
+(split + merge) is reported beside it. Other modes, one JSON line each:
+--prefill (balancer, prefill build, prompt heavy-hitter scores), --quantize
+(mikv_quantize_tokens on every prompt row), --criticalkv (the CriticalKV
+select, 32 heads x 32K tokens), --read-ceiling (a plain streaming read of
+one split launch's bytes), --calibrate-copy (the 1 GiB copy that scales the
+HBM counters).
+
+Prints one JSON line (rank 0). --gpus N > 1 is refused: the path runs on one
+GPU.
 """
 from __future__ import annotations
 
