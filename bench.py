@@ -400,7 +400,7 @@ def main():
         print(json.dumps(fn(args, log)), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs the MiKV path on one GPU only; --gpus must be 1 "
+        print("bench.py: the MiKV path runs on one GPU only; --gpus must be 1 "
               "(the path shards by (sequence, kv head) with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
