@@ -451,3 +451,59 @@ def test_quantize_golden_ties_on_device():
         L.mikv_quantize_tokens(dev(xr), None, out, sz, group, bits)
         assert np.array_equal(O.unpack_codes(host(out), d, bits), np.stack(rows_c)), case["name"]
         assert np.array_equal(host(sz).astype(F64), np.asarray(rows_sz, F64)), case["name"]
+
+
+# ---------------------------------------------------------------- free-running
+@pytest.mark.parametrize("name,over,steps", [
+    ("tiny", {}, 32),
+    ("tiny", dict(batch=64, hq=4, hkv=2), 16),
+    ("llama2_7b_layer", dict(batch=1, T=700), 8),
+    ("gqa_throughput", dict(batch=2, T=600), 8),
+])
+def test_decode_free_running(name, over, steps):
+    """Device decode steps (mikv_decode_step) and the oracle's, each from its
+    own state after the same prefill. Per (sequence, kv head) unit, outputs
+    match to tolerance and the demoted positions agree until the unit's first
+    divergence; a divergence must be a near-tie (the two candidates' fp64
+    scores within the tolerance of the accumulated scores), after which the
+    unit's states differ and it is no longer compared."""
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"free-running {name} {over} steps={steps}", flush=True)
+    dims, cache, b, _ = _prefill_gpu(cfg, 77, True)
+    st = cache.to_numpy()
+    bh = host(b)
+    o = torch.empty((cfg.batch, cfg.hq, cfg.d), dtype=torch.float32, device="cuda")
+    p16 = torch.empty((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
+    dpos = torch.empty((cfg.batch, cfg.hkv), dtype=torch.int32, device="cuda")
+    ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + steps), dtype=torch.uint8, device="cuda")
+    live = np.ones((cfg.batch, cfg.hkv), bool)
+    diverged = 0
+    for step in range(steps):
+        N = cfg.T + step + 1
+        qd, kd, vd = S.decode_tensors(cfg, 77, step)
+        L.mikv_decode_step(dims, cache, N, cfg.recent, cfg.H, dev(qd), dev(kd), dev(vd), b, o, p16, ws,
+                           demoted_pos=dpos)
+        ro, rp16, _, rst = O.decode_attention(st, N, qd, kd, vd, bh)
+        acc = O.h2o_accumulate(rst["acc16"], rp16)
+        rst["acc16"] = acc.astype(F32)
+        drop = O.select_drop(acc, rst["pos16"], N, cfg.recent, cfg.H)
+        og, dp = host(o), host(dpos)
+        rpos = np.take_along_axis(rst["pos16"], drop[..., None], 2)[..., 0]
+        floor = N * cfg.rep * 2.0 ** -126
+        for i in range(cfg.batch):
+            for g in range(cfg.hkv):
+                if not live[i, g]:
+                    continue
+                hs = slice(g * cfg.rep, (g + 1) * cfg.rep)
+                assert_close(og[i, hs], ro[i, hs], f"o step {step} unit ({i},{g})")
+                if dp[i, g] != rpos[i, g]:
+                    slot = np.nonzero(rst["pos16"][i, g] == dp[i, g])[0]
+                    assert len(slot) == 1, f"step {step} unit ({i},{g}): demoted position {dp[i, g]} not resident"
+                    gap = abs(acc[i, g, slot[0]] - acc[i, g, drop[i, g]])
+                    assert gap <= TOL * np.max(acc[i, g]) + floor, \
+                        f"step {step} unit ({i},{g}): selections differ by {gap:.3e}, not a near-tie"
+                    live[i, g] = False
+                    diverged += 1
+        st = O.demote(rst, N, drop)
+    print(f"free-running {name}: {diverged} of {live.size} units diverged over {steps} steps, "
+          f"all at near-ties", flush=True)
