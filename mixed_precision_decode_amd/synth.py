@@ -164,7 +164,8 @@ def unit_acc0(cfg: DecodeConfig, seed: int, n: int, g: int) -> np.ndarray:
     """Stand-in prefill heavy-hitter scores [T] fp32 (see module docstring)."""
     rng = _rng(seed, _S_ACC0, n, g)
     a = rng.lognormal(mean=0.0, sigma=2.0, size=cfg.T)
-    a *= cfg.rep * cfg.T / a.sum()
+    if cfg.T > 0:
+        a *= cfg.rep * cfg.T / a.sum()
     a = np.round(a * 1024.0) / 1024.0
     a[rng.random(cfg.T) < 0.05] = 0.0
     return a.astype(np.float32)
