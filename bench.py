@@ -414,7 +414,9 @@ def main():
         cfg = cfg.scaled(**{kv.split("=")[0]: int(kv.split("=")[1]) for kv in args.set})
     K, W, KA = args.steps, args.warmup, args.attn_steps
     total = K + W + 2 * KA
-    assert total <= cfg.steps, f"the workload defines {cfg.steps} decode steps"
+    if total > cfg.steps:
+        ap.error(f"workload {cfg.name} defines {cfg.steps} decode steps: --warmup + --steps + "
+                 f"2 * --attn-steps must not exceed it (got {total})")
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
 
