@@ -24,6 +24,7 @@ struct DecodePlan {
   int S16, Sq;     // splits per tier
   int RT;          // query heads per block
   int tiles;       // rep / RT
+  int f16_first;   // 1: FP16-tier splits take the first block indices (else the low-bit splits do)
 };
 DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq);
 size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int cap16, const DecodePlan& plan);
