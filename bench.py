@@ -8,25 +8,32 @@ before timing (balancer + prefill build on the GPU) from seeded synthetic
 inputs; every step consumes a new seeded (q, k, v) token per sequence and
 kv head, so the low-bit tier grows by one token per step.
 
-Before each timed step an untimed read of a 1 GiB device buffer evicts the
+Per decode workload: --steps timed steps after --warmup steps (mean and
+median step time; `value` = KV-tokens/s over the timed steps), then
+--attn-steps replays of one attention call (split + merge, events around the
+call) and as many of the split kernel alone (events of its own launch,
+mikv_decode_attn_timed); medians are reported. The headline line is the
+Llama-2-7B-shaped layer; the 32K GQA layer and the GQA throughput batch
+follow in the same run under "configs". The CPU baseline leg replays one
+more step of sequence 0 on the oracle, timed on the host cores, and compares
+its result with the device's ("parity").
+
+Before each timed launch an untimed read of a 1 GiB device buffer evicts the
 caches (MI355X has a 256 MB Infinity Cache, larger than the per-step working
-set of the configs), so each step streams its cache from HBM. The flush
+set of the workloads), so each launch streams its cache from HBM. The flush
 reads rather than writes: a written flush leaves the Infinity Cache full of
 dirty lines whose write-back would then compete with the measured kernel
-(--flush write shows that case, --flush none the warm-cache case). Step and
-kernel times come from HIP events recorded on the stream the kernels run on.
+(--flush write shows that case, --flush none the warm-cache case). Times
+come from HIP events recorded on the stream the kernels run on.
 
-The JSON line's roofline is the dominant kernel's: the split kernel, timed
-by start/stop events of its own launch (mikv_decode_attn_timed); the call
-(split + merge) is reported beside it. Other modes, one JSON line each:
---prefill (balancer, prefill build, prompt heavy-hitter scores), --quantize
-(mikv_quantize_tokens on every prompt row), --criticalkv (the CriticalKV
-select, 32 heads x 32K tokens), --read-ceiling (a plain streaming read of
-one split launch's bytes), --calibrate-copy (the 1 GiB copy that scales the
-HBM counters).
+The JSON line's roofline is the dominant kernel's: the split kernel. Other
+modes, one JSON line each: --prefill (balancer, prefill build, prompt
+heavy-hitter scores), --quantize (mikv_quantize_tokens on every prompt row),
+--criticalkv (the CriticalKV select, 32 heads x 32K tokens), --read-ceiling
+(a plain streaming read of one split launch's bytes), --calibrate-copy (the
+1 GiB copy that scales the HBM counters).
 
-Prints one JSON line (rank 0). --gpus N > 1 is refused: the path runs on one
-GPU.
+Prints one JSON line. --gpus N > 1 is refused: the path runs on one GPU.
 """
 from __future__ import annotations
 
@@ -107,23 +114,29 @@ def h2o_bytes(cfg):
     return per_unit * cfg.batch * cfg.hkv
 
 
-def cpu_baseline(cfg, cache_np, b_np, N, seed, step, budget_s):
+def cpu_baseline(cfg, before, b_np, N, q_np, k_np, v_np, gpu, budget_s):
     """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    one sequence's decode step (all its kv heads), repeated until budget_s."""
+    the decode step of sequence 0 (all its kv heads) from the device's state
+    before that step, repeated until budget_s. The first repetition's result
+    is also compared with what the device computed for the same step
+    (returned under "parity"): o and the accumulated scores to the stated
+    tolerance, the demoted token chosen from the device's own fp32 scores and
+    its codes exactly, and whether the oracle's fp64 scores pick the same
+    token."""
     import oracle as O
-    from mixed_precision_decode_amd import synth as S
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    sub = {k: (v[:1].copy() if isinstance(v, np.ndarray) else v) for k, v in cache_np.items()}
-    qd, kd, vd = S.decode_tensors(cfg.scaled(batch=1), seed, step)
     reps = 0
     t0 = time.perf_counter()
     c0 = time.process_time()
+    first = None
     while True:
-        O.decode_step(sub, N, qd, kd, vd, b_np[:1], cfg.recent, cfg.H)
+        res = O.decode_step(before, N, q_np, k_np, v_np, b_np, cfg.recent, cfg.H)
+        if first is None:
+            first = res
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -131,11 +144,37 @@ def cpu_baseline(cfg, cache_np, b_np, N, seed, step, budget_s):
     # cores actually used: the process's CPU time over the wall time (numpy's
     # elementwise work is single-threaded; only its BLAS calls use the pool)
     busy = (time.process_time() - c0) / el
+    # parity of the device's step with the oracle's, on this sample
+    o_ref, p16_ref, st_ref, drop_ref = first
+    tol = 2e-3
+    o_err = float(np.max(np.abs(gpu["o"].astype(np.float64) - o_ref)) / np.max(np.abs(o_ref)))
+    acc_prev = before["acc16"].astype(np.float64).copy()
+    for g in range(cfg.hkv):
+        acc_prev[0, g, before["free16"][0, g]] = 0.0
+    acc_ref = acc_prev + p16_ref
+    acc_gpu = gpu["after"]["acc16"].astype(np.float64)
+    acc_err = float(np.max(np.abs(acc_gpu - acc_ref)) / np.max(np.abs(acc_ref)))
+    _, _, _, appended = O.decode_attention(before, N, q_np, k_np, v_np, b_np)
+    drop_dev = O.select_drop(acc_gpu, appended["pos16"], N, cfg.recent, cfg.H)
+    sel_ok = bool(np.array_equal(gpu["after"]["free16"], drop_dev))
+    mid = dict(appended)
+    mid["acc16"] = gpu["after"]["acc16"]
+    dem = O.demote(mid, N, drop_dev)
+    slot = N - cfg.cap16
+    raw = lambda a: np.ascontiguousarray(np.asarray(a)[:, :, slot]).view(np.uint8)
+    codes_ok = all(np.array_equal(raw(gpu["after"][key]), raw(dem[key]))
+                   for key in ("kq", "vq", "ksz", "vsz", "posq"))
+    parity = {"units": f"sequence 0, {cfg.hkv} kv heads, step N={N}",
+              "o_max_err_rel": o_err, "acc_max_err_rel": acc_err, "tolerance": tol,
+              "selection_on_device_scores_exact": sel_ok, "demoted_codes_exact": bool(codes_ok),
+              "oracle_fp64_selection_agrees": bool(np.array_equal(drop_ref, drop_dev)),
+              "ok": bool(o_err <= tol and acc_err <= tol and sel_ok and codes_ok)}
     return {"value": reps * N / el, "unit": "KV-tokens/s", "cores": max(1, int(round(busy))),
             "cores_busy": busy, "blas_threads": int(threads), "kind": "oracle",
             "sample": (f"{reps} oracle decode steps of 1 of {cfg.batch} sequences "
                        f"({cfg.hkv} kv heads, N={N}), fp64 numpy, {el:.1f} s; "
-                       f"host os.cpu_count()={os.cpu_count()}")}
+                       f"host os.cpu_count()={os.cpu_count()}"),
+            "parity": parity}
 
 
 def calibrate_copy(nbytes=1 << 30, reps=5):
@@ -184,7 +223,7 @@ def bench_quantize(args, log):
         L.mikv_quantize_tokens(x, None, codes, sz, cfg.G, cfg.bits)
         e1.record()
     torch.cuda.synchronize()
-    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
     gbps = nbytes / (us * 1e-6) / 1e9
     log(f"[bench] quantize {n_rows} rows: {us:.1f} us, {gbps:.0f} GB/s")
     return {"metric": "quantize GB/s", "value": gbps, "unit": "GB/s", "higher_is_better": True,
@@ -223,7 +262,7 @@ def read_ceiling(args, log):
             L.mikv_read_probe(buf, blocks, sink)
             e1.record()
         torch.cuda.synchronize()
-        us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+        us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
         res[blocks] = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9}
         log(f"[bench] streaming read of {nbytes / 1e6:.1f} MB, {blocks} blocks: {us:.1f} us, "
             f"{res[blocks]['GBps']:.0f} GB/s")
@@ -252,7 +291,7 @@ def bench_criticalkv(args, log):
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
     Ag, Vg, Wg = dev(A), dev(V), dev(W)
     budget = cfg.budget
-    b1 = int(np.floor(np.float64(np.float32(cfg.alpha)) * budget))
+    b1 = int(np.floor(np.float64(cfg.alpha) * budget))
     idx = torch.empty((cfg.H, budget), dtype=torch.int32, device="cuda")
     ws = torch.empty(L.mikv_criticalkv_workspace(cfg.H, cfg.T, cfg.d, cfg.hidden), dtype=torch.uint8,
                      device="cuda")
@@ -267,7 +306,7 @@ def bench_criticalkv(args, log):
         L.mikv_criticalkv_select(Ag, Vg, Wg, budget, cfg.alpha, idx, ws=ws)
         e1.record()
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
     flops = 2.0 * (cfg.T - b1) * cfg.d * cfg.hidden * cfg.H
     log(f"[bench] criticalkv select {ms:.3f} ms, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s over the call")
     cpu = None
@@ -343,7 +382,7 @@ def bench_prefill(args, log):
             fn()
             e1.record()
         torch.cuda.synchronize()
-        us = float(np.mean([a.elapsed_time(e) for a, e in evs])) * 1e3
+        us = float(np.median([a.elapsed_time(e) for a, e in evs])) * 1e3
         if nbytes is None:
             tf = score_flops / (us * 1e-6) / 1e12
             res[name] = {"us": us, "algorithmic_flops": score_flops, "executed_flops": exec_flops,
@@ -360,19 +399,181 @@ def bench_prefill(args, log):
             "data": "synthetic", "config": {"workload": cfg.name}, "kernels": res}
 
 
+def decode_run(cfg, args, log, K, W, KA, cpu_seconds):
+    """Build the workload's cache on the device, then time it:
+      - K decode steps (mikv_decode_step: attention + H2O update, two
+        launches), HIP events at the step boundaries, after W warmup steps;
+      - KA replays of one mikv_decode_attn call (split + merge) at a fixed
+        length, events around the call: the call appends the same token and
+        overwrites the same outputs each time, so replays leave the state as
+        one call does;
+      - KA replays of mikv_decode_attn_timed, whose events take the split
+        kernel's own start and end (hipExtLaunchKernel);
+    with an untimed read of 1 GiB before each timed launch. Then one more
+    step runs untimed for the CPU baseline leg, which replays it on the
+    oracle and compares. Returns the workload's entry of the JSON line."""
+    import torch
+    from mixed_precision_decode_amd import _lib as L
+    from mixed_precision_decode_amd import synth as S
+    total = W + K + 1
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    t0 = time.perf_counter()
+    q, k, v, acc0 = S.prefill_tensors(cfg, args.seed)
+    dims = L.Dims(batch=cfg.batch, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, group=cfg.G, bits=cfg.bits,
+                  cap16=cfg.cap16, capq=cfg.T - cfg.B + total)
+    cache = L.Cache(dims)
+    b = torch.empty((cfg.batch, cfg.hkv, cfg.d), dtype=torch.float32, device="cuda")
+    qg, kg = dev(q), dev(k)
+    ws_b = torch.empty(L.mikv_balance_workspace(dims, cfg.T), dtype=torch.uint8, device="cuda")
+    L.mikv_balance_prefill(dims, cfg.T, qg, kg, b, None, ws_b)
+    del qg, q
+    ws_h = torch.empty(L.mikv_h2o_workspace(dims, cfg.T), dtype=torch.uint8, device="cuda")
+    L.mikv_h2o_update_select(dims, cache, cfg.T, cfg.recent, cfg.H,
+                             src=dict(k=kg, v=dev(v), acc0=dev(acc0), b=b), ws=ws_h)
+    torch.cuda.synchronize()
+    del kg, ws_h, ws_b, k, v, acc0
+    steps_np = [S.decode_tensors(cfg, args.seed, s) for s in range(total)]
+    steps_in = [tuple(dev(x) for x in t) for t in steps_np]
+    o = torch.empty((cfg.batch, cfg.hq, cfg.d), dtype=torch.float32, device="cuda")
+    p16 = torch.empty((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + total), dtype=torch.uint8, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def do_flush(i):
+        if args.flush == "read":
+            torch.sum(flush, dim=0, out=flush_out)
+        elif args.flush == "write":
+            flush.fill_(float(i))
+    log(f"[bench] {cfg.name}: cache built ({time.perf_counter() - t0:.1f}s); warmup {W}, timed {K}, "
+        f"replays {KA}")
+
+    def step_call(s, n_len):
+        qd, kd, vd = steps_in[s]
+        L.mikv_decode_step(dims, cache, n_len, cfg.recent, cfg.H, qd, kd, vd, b, o, p16, ws)
+
+    graphs = {}
+    if args.graph:
+        # replay each timed step as one HIP graph, as a decode loop could
+        for s in range(W, W + K):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_call(s, cfg.T + s + 1)
+            graphs[s] = g
+        torch.cuda.synchronize()
+    N = cfg.T
+    for s in range(W):
+        N += 1
+        do_flush(s)
+        step_call(s, N)
+    torch.cuda.synchronize()
+    Ev = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [(Ev(), Ev()) for _ in range(K)]
+    lens = []
+    tw0 = time.perf_counter()
+    for i in range(K):
+        N += 1
+        do_flush(i)
+        evs[i][0].record()
+        if W + i in graphs:
+            graphs[W + i].replay()
+        else:
+            step_call(W + i, N)
+        evs[i][1].record()
+        lens.append(N)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - tw0
+    # replays of the next step's attention call at length N + 1
+    s_next = W + K
+    qd, kd, vd = steps_in[s_next]
+    eva = [(Ev(), Ev()) for _ in range(KA)]
+    for i in range(KA):
+        do_flush(i)
+        eva[i][0].record()
+        L.mikv_decode_attn(dims, cache, N + 1, qd, kd, vd, b, o, p16, ws)
+        eva[i][1].record()
+    evk = [(Ev(), Ev()) for _ in range(KA)]
+    for i in range(KA):
+        do_flush(i)
+        L.mikv_decode_attn_timed(dims, cache, N + 1, qd, kd, vd, b, o, p16, ws, *evk[i])
+    torch.cuda.synchronize()
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in eva])
+    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evk])
+    lens = np.array(lens)
+    ms_per_step = float(step_ms.mean())
+    value = float(cfg.batch * lens.mean() / (ms_per_step * 1e-3))
+    kbytes = float(split_bytes(cfg, N + 1))
+    abytes = float(attn_bytes(cfg, N + 1))
+    split_us = float(np.median(split_ms)) * 1e3
+    call_us = float(np.median(attn_ms)) * 1e3
+    k_gbps = kbytes / (split_us * 1e-6) / 1e9
+    a_gbps = abytes / (call_us * 1e-6) / 1e9
+    sbytes = np.array([attn_bytes(cfg, n) + h2o_bytes(cfg) for n in lens], dtype=np.float64)
+    s_gbps = float((sbytes / (step_ms * 1e-3)).mean() / 1e9)
+    log(f"[bench] {cfg.name}: split kernel {split_us:.1f} us median ({k_gbps:.0f} GB/s, "
+        f"{k_gbps / HBM_PEAK_GBPS:.3f}), attn call {call_us:.1f} us median ({a_gbps:.0f} GB/s, "
+        f"{a_gbps / HBM_PEAK_GBPS:.3f}), step {ms_per_step * 1e3:.1f} us mean "
+        f"({np.median(step_ms) * 1e3:.1f} median), {value:.3g} KV-tokens/s")
+    cpu = None
+    if cpu_seconds > 0:
+        # one more decode step, untimed: the oracle replays it from the same
+        # state (sequence 0) and compares
+        before = {kk: getattr(cache, kk)[:1].cpu().numpy() for kk in L.Cache.NAMES}
+        before["group"], before["bits"] = cfg.G, cfg.bits
+        N += 1
+        step_call(s_next, N)
+        after = {kk: getattr(cache, kk)[:1].cpu().numpy() for kk in L.Cache.NAMES}
+        gpu = {"o": o[:1].cpu().numpy(), "after": after}
+        qn, kn, vn = (x[:1] for x in steps_np[s_next])
+        cpu = cpu_baseline(cfg, before, b[:1].cpu().numpy(), N, qn, kn, vn, gpu, cpu_seconds)
+        log(f"[bench] {cfg.name}: cpu oracle {cpu['value']:.3g} KV-tokens/s ({cpu['sample']}); "
+            f"parity {cpu['parity']}")
+    del cache, steps_in, ws, flush
+    torch.cuda.empty_cache()
+    traffic_ok = not args.set
+    return {
+        "workload": cfg.name, "value": value, "unit": "KV-tokens/s", "ms_per_step": ms_per_step,
+        "ms_per_step_median": float(np.median(step_ms)), "steps": K, "warmup": W,
+        "config": {"workload": cfg.name, "batch": cfg.batch, "q_heads": cfg.hq, "kv_heads": cfg.hkv,
+                   "head_dim": cfg.d, "context": cfg.T, "low_bits": cfg.bits,
+                   "important_pct": cfg.pct, "recent": cfg.recent, "group": cfg.G,
+                   "cache_flush_per_step": args.flush,
+                   "step_launch": "hip_graph" if args.graph else "eager"},
+        "roofline": {"bound": "hbm", "achieved": k_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": k_gbps / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic(cfg.name) if traffic_ok else None,
+                     "launches_timed": KA, "statistic": "median", "kernel": "decode_split_kernel",
+                     "kernel_us": split_us, "bytes_per_launch": kbytes,
+                     "timing": "hipExtLaunchKernel start/stop events of the kernel itself"},
+        "attn_call": {"kernels": "decode_split_kernel + decode_merge_kernel (one mikv_decode_attn call)",
+                      "us": call_us, "bytes": abytes, "GBps": a_gbps, "frac": a_gbps / HBM_PEAK_GBPS,
+                      "launches_timed": KA, "statistic": "median",
+                      "traffic": recorded_traffic(cfg.name, "call_traffic_bytes") if traffic_ok else None,
+                      "timing": "HIP events recorded on the stream before and after the call"},
+        "step_hbm_gbps": s_gbps,
+        "wall_ms_per_step_incl_flush": wall / K * 1e3,
+        "cpu_baseline": cpu,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--attn-steps", type=int, default=20,
-                    help="decode steps timed around the attention call alone, and as many "
-                         "timed at the split kernel's own start and end")
+    ap.add_argument("--attn-steps", type=int, default=60,
+                    help="replays of the attention call, and as many of the split kernel with its "
+                         "own start/stop events (medians reported)")
     ap.add_argument("--workload", default="llama2_7b_layer")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only --workload (by default the other decode workloads follow it in "
+                         "the same run, under \"configs\")")
     ap.add_argument("--seed", type=int, default=1001)
     ap.add_argument("--set", action="append", default=[], metavar="FIELD=INT",
                     help="override an integer field of the workload (e.g. pct=100)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--extra-cpu-seconds", type=float, default=4.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", choices=("read", "write", "none"), default="read")
     ap.add_argument("--graph", type=int, default=0,
@@ -401,198 +602,58 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: the MiKV path runs on one GPU only; --gpus must be 1 "
-              "(the path shards by (sequence, kv head) with no exchange; see the design notes)",
+              "(every (sequence, kv head) unit is independent, so the path would shard by unit "
+              "with no exchange; no multi-GPU figure is measured here)",
               file=sys.stderr)
         sys.exit(2)
 
-    import torch
-    from mixed_precision_decode_amd import _lib as L
     from mixed_precision_decode_amd import synth as S
 
     cfg = S.CONFIGS[args.workload]
     if args.set:
         cfg = cfg.scaled(**{kv.split("=")[0]: int(kv.split("=")[1]) for kv in args.set})
     K, W, KA = args.steps, args.warmup, args.attn_steps
-    total = K + W + 2 * KA
-    if total > cfg.steps:
-        ap.error(f"workload {cfg.name} defines {cfg.steps} decode steps: --warmup + --steps + "
-                 f"2 * --attn-steps must not exceed it (got {total})")
-    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    if W + K + 1 > cfg.steps:
+        ap.error(f"workload {cfg.name} defines {cfg.steps} decode steps: --warmup + --steps + 1 "
+                 f"must not exceed it (got {W + K + 1})")
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
-
-    t0 = time.perf_counter()
-    q, k, v, acc0 = S.prefill_tensors(cfg, args.seed)
-    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
-    dims = L.Dims(batch=cfg.batch, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, group=cfg.G, bits=cfg.bits,
-                  cap16=cfg.cap16, capq=cfg.T - cfg.B + total)
-    cache = L.Cache(dims)
-    b = torch.empty((cfg.batch, cfg.hkv, cfg.d), dtype=torch.float32, device="cuda")
-    qg, kg = dev(q), dev(k)
-    ws_b = torch.empty(L.mikv_balance_workspace(dims, cfg.T), dtype=torch.uint8, device="cuda")
-    L.mikv_balance_prefill(dims, cfg.T, qg, kg, b, None, ws_b)
-    del qg, q
-    ws_h = torch.empty(L.mikv_h2o_workspace(dims, cfg.T), dtype=torch.uint8, device="cuda")
-    L.mikv_h2o_update_select(dims, cache, cfg.T, cfg.recent, cfg.H,
-                             src=dict(k=kg, v=dev(v), acc0=dev(acc0), b=b), ws=ws_h)
-    torch.cuda.synchronize()
-    del kg, ws_h, ws_b
-    steps_in = [tuple(dev(x) for x in S.decode_tensors(cfg, args.seed, s)) for s in range(total)]
-    o = torch.empty((cfg.batch, cfg.hq, cfg.d), dtype=torch.float32, device="cuda")
-    p16 = torch.empty((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + total), dtype=torch.uint8,
-                     device="cuda")
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
-    flush_out = torch.empty((), dtype=torch.float32, device="cuda")
-
-    def do_flush(i):
-        if args.flush == "read":
-            torch.sum(flush, dim=0, out=flush_out)
-        elif args.flush == "write":
-            flush.fill_(float(i))
-    log(f"[bench] cache built ({time.perf_counter() - t0:.1f}s); warmup {W}, timed {K}")
-
-    N = cfg.T
-    cpu_state = None
-
-    def attn_call(s, n_len, split_ev=None):
-        qd, kd, vd = steps_in[s]
-        if split_ev is None:
-            L.mikv_decode_attn(dims, cache, n_len, qd, kd, vd, b, o, p16, ws)
-        else:
-            # the events take the split kernel's own start and end
-            L.mikv_decode_attn_timed(dims, cache, n_len, qd, kd, vd, b, o, p16, ws, *split_ev)
-
-    def step_call(s, n_len):
-        qd, kd, vd = steps_in[s]
-        L.mikv_decode_step(dims, cache, n_len, cfg.recent, cfg.H, qd, kd, vd, b, o, p16, ws)
-
-    def h2o_call(n_len):
-        L.mikv_h2o_update_select(dims, cache, n_len, cfg.recent, cfg.H, p16=p16)
-
-    # Optionally replay each timed step (decode attention + H2O) as one HIP
-    # graph, as a decode loop could.
-    graphs = {}
-    if args.graph:
-        for s in range(W, W + K):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step_call(s, cfg.T + s + 1)
-            graphs[s] = g
-        torch.cuda.synchronize()
-
-    def one_step(s, ev_start=None, ev_attn=None, ev_end=None, split_ev=None):
-        nonlocal N
-        N += 1
-        assert N == cfg.T + s + 1
-        if ev_start is not None:
-            ev_start.record()
-        if ev_attn is None:
-            # one decode step: mikv_decode_step (attention + H2O, two launches)
-            if s in graphs:
-                graphs[s].replay()
-            else:
-                step_call(s, N)
-        else:
-            # attention-only timing: mikv_decode_attn, then the H2O call
-            attn_call(s, N, split_ev)
-            if ev_attn is not None:
-                ev_attn.record()
-            h2o_call(N)
-        if ev_end is not None:
-            ev_end.record()
-
-    for s in range(W):
-        do_flush(s)
-        one_step(s)
-    torch.cuda.synchronize()
-    if not args.no_cpu_baseline:
-        cpu_state = (cache.to_numpy(), b.cpu().numpy(), N + 1, W)
-    # timed steps: events only at the step boundaries (an event between two
-    # kernels costs a few microseconds of its own)
-    Ev = lambda: torch.cuda.Event(enable_timing=True)
-    evs = [(Ev(), Ev()) for _ in range(K)]
-    lens = []
-    torch.cuda.synchronize()
-    tw0 = time.perf_counter()
-    for i in range(K):
-        do_flush(i)
-        one_step(W + i, ev_start=evs[i][0], ev_end=evs[i][1])
-        lens.append(N)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - tw0
-    # attention alone, two passes of KA decode steps each:
-    #  - events on the stream around each mikv_decode_attn call (split + merge);
-    #  - mikv_decode_attn_timed, whose events take the start and end of the
-    #    split kernel itself, the dominant kernel (hipExtLaunchKernel; such a
-    #    launch leaves a gap of a few microseconds before the next kernel, so
-    #    these calls are not the ones the call-level time comes from)
-    eva = [(Ev(), Ev()) for _ in range(KA)]
-    alens = []
-    for i in range(KA):
-        do_flush(i)
-        one_step(W + K + i, ev_start=eva[i][0], ev_attn=eva[i][1])
-        alens.append(N)
-    evk = [(Ev(), Ev()) for _ in range(KA)]
-    klens = []
-    for i in range(KA):
-        do_flush(i)
-        one_step(W + K + KA + i, ev_attn=Ev(), split_ev=evk[i])
-        klens.append(N)
-    torch.cuda.synchronize()
-    step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in eva])
-    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evk])
-    lens = np.array(lens)
-    ms_per_step = float(step_ms.mean())
-    value = float(cfg.batch * lens.mean() / (ms_per_step * 1e-3))
-    abytes = np.array([attn_bytes(cfg, n) for n in alens], dtype=np.float64)
-    a_gbps = float((abytes / (attn_ms * 1e-3)).mean() / 1e9)
-    kbytes = np.array([split_bytes(cfg, n) for n in klens], dtype=np.float64)
-    k_gbps = float(kbytes.mean() / (split_ms.mean() * 1e-3) / 1e9)
-    sbytes = np.array([attn_bytes(cfg, n) + h2o_bytes(cfg) for n in lens], dtype=np.float64)
-    s_gbps = float((sbytes / (step_ms * 1e-3)).mean() / 1e9)
-    log(f"[bench] split kernel {split_ms.mean() * 1e3:.1f} us ({k_gbps:.0f} GB/s), attn call "
-        f"{attn_ms.mean() * 1e3:.1f} us ({a_gbps:.0f} GB/s), step "
-        f"{ms_per_step * 1e3:.1f} us ({s_gbps:.0f} GB/s), wall incl. flush {wall / K * 1e3:.3f} ms/step")
-
-    cpu = None
-    if cpu_state is not None:
-        cache_np, b_np, Nc, st = cpu_state
-        cpu = cpu_baseline(cfg, cache_np, b_np, Nc, args.seed, st, args.cpu_seconds)
-        log(f"[bench] cpu oracle {cpu['value']:.3g} KV-tokens/s ({cpu['sample']})")
-
+    cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    head = decode_run(cfg, args, log, K, W, KA, cpu_s)
+    extra = []
+    if not args.no_extra and not args.set:
+        for name in ("llama3_8b_32k", "gqa_throughput"):
+            if name == cfg.name:
+                continue
+            c2 = S.CONFIGS[name]
+            w2 = min(W, c2.steps - 2)
+            k2 = min(K, c2.steps - w2 - 1)
+            extra.append(decode_run(c2, args, log, k2, w2, KA,
+                                    0.0 if args.no_cpu_baseline else args.extra_cpu_seconds))
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": head["value"],
         "unit": "KV-tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": cfg.batch, "q_heads": cfg.hq, "kv_heads": cfg.hkv,
-                   "head_dim": cfg.d, "context": cfg.T, "low_bits": cfg.bits,
-                   "important_pct": cfg.pct, "recent": cfg.recent, "group": cfg.G,
-                   "cache_flush_per_step": args.flush, "step_launch": "hip_graph" if args.graph else "eager"},
-        "roofline": {"bound": "hbm", "achieved": k_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": k_gbps / HBM_PEAK_GBPS,
-                     "traffic": recorded_traffic(cfg.name) if not args.set else None,
-                     "launches_timed": KA, "kernel": "decode_split_kernel",
-                     "kernel_us": float(split_ms.mean() * 1e3),
-                     "bytes_per_launch": float(kbytes.mean()),
-                     "timing": "hipExtLaunchKernel start/stop events of the kernel itself"},
-        "attn_call": {"kernels": "decode_split_kernel + decode_merge_kernel (one mikv_decode_attn call)",
-                      "us": float(attn_ms.mean() * 1e3), "bytes": float(abytes.mean()),
-                      "GBps": a_gbps, "frac": a_gbps / HBM_PEAK_GBPS,
-                      "traffic": recorded_traffic(cfg.name, "call_traffic_bytes") if not args.set else None,
-                      "timing": "HIP events recorded on the stream before and after the call"},
-        "step_hbm_gbps": s_gbps,
-        "wall_ms_per_step_incl_flush": wall / K * 1e3,
-        "cpu_baseline": cpu,
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "attn_call": head["attn_call"],
+        "ms_per_step_median": head["ms_per_step_median"],
+        "step_hbm_gbps": head["step_hbm_gbps"],
+        "wall_ms_per_step_incl_flush": head["wall_ms_per_step_incl_flush"],
+        "parity": None if head["cpu_baseline"] is None else head["cpu_baseline"]["parity"],
+        "cpu_baseline": head["cpu_baseline"],
+        "configs": [{kk: e[kk] for kk in ("workload", "value", "unit", "ms_per_step", "ms_per_step_median",
+                                           "steps", "warmup", "config", "roofline", "attn_call",
+                                           "cpu_baseline")}
+                    for e in extra],
     }
     print(json.dumps(out), flush=True)
 

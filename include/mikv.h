@@ -14,9 +14,12 @@
  * Conventions for every entry point
  *   - fp16 tensors are passed as uint16_t bit patterns (IEEE binary16).
  *   - Every tensor pointer is DEVICE memory owned by the caller; the library
- *     never allocates, frees or synchronises, and keeps no mutable global
- *     state. Tensors are dense row-major in the index order written next to
- *     them.
+ *     never allocates, frees or synchronises. Its only global state is a
+ *     per-process cache of launch facts (each device's compute-unit count
+ *     and the kernels' occupancy), filled on first use with relaxed atomics
+ *     and never changed afterwards, so concurrent calls from several host
+ *     threads are safe. Tensors are dense row-major in the index order
+ *     written next to them.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls validate their arguments on the host, enqueue kernels on
  *     `stream` and return at once. On a validation failure nothing is
@@ -55,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MIKV_ABI_VERSION 1
+#define MIKV_ABI_VERSION 2
 
 typedef enum {
   MIKV_OK = 0,
@@ -147,6 +150,9 @@ mikv_status mikv_quantize_tokens(const uint16_t* x, const int32_t* rows,
  *      s_i = q-hat . k~_i / sqrt(d) over the cap16 FP16-tier tokens
  *      (k~ = k16) and the len - cap16 low-bit tokens (k~ = code*scale+zero);
  *      p = softmax(s) over both tiers; o[n][h] = sum_i p_i v~_i.
+ *      The kernels form q-hat as fp32(q) times the hardware reciprocal of b
+ *      (within 1 ulp of the quotient) with 1/sqrt(d) folded in; scores only
+ *      enter outputs that are specified to a tolerance.
  *   3. p16[n][g][slot] = sum over the query heads of group g of p at that
  *      FP16 slot (input of the H2O accumulation).
  * Precondition: the low-bit tier holds len - cap16 tokens (slots
@@ -309,7 +315,9 @@ mikv_status mikv_decode_step(const mikv_dims* dims, const mikv_cache* cache,
  * CriticalKV two-stage selection per head ([gist CriticalKV] Algorithm 1;
  * theoretical framework: the output perturbation bound depends on the
  * attention weights and the value states projected by W_O).
- *   b1 = floor(alpha * budget), b2 = budget - b1;
+ *   b1 = floor(alpha * budget) evaluated in double precision (alpha is a
+ *   double so that a decimal such as 0.7 is not first rounded to float),
+ *   b2 = budget - b1;
  *   S1 = top-b1 of A[h] by (A desc, index asc);
  *   n_i = sum_j | sum_c V[h][i][c] * W_O[h*d + c][j] |  for i not in S1
  *         (fp16 products, fp32 accumulation);
@@ -328,7 +336,7 @@ size_t mikv_criticalkv_workspace(int32_t H, int32_t T, int32_t d,
 mikv_status mikv_criticalkv_select(const float* A, const uint16_t* V,
                                    const uint16_t* W_O, int32_t H, int32_t T,
                                    int32_t d, int32_t hidden, int32_t budget,
-                                   float alpha, int32_t* idx, float* score2,
+                                   double alpha, int32_t* idx, float* score2,
                                    void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmikv.so")
 MIKV_OK, MIKV_ERR_NULL, MIKV_ERR_SHAPE, MIKV_ERR_UNSUPPORTED = 0, 1, 2, 3
 MIKV_ERR_CAPACITY, MIKV_ERR_WORKSPACE, MIKV_ERR_HIP = 4, 5, 6
 
-_vp, _sz, _i32, _i64, _f32 = C.c_void_p, C.c_size_t, C.c_int32, C.c_int64, C.c_float
+_vp, _sz, _i32, _i64, _f64 = C.c_void_p, C.c_size_t, C.c_int32, C.c_int64, C.c_double
 
 
 class MikvDims(C.Structure):
@@ -62,7 +62,7 @@ _SIGS = {
     "mikv_h2o_update_select": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _i32, _i32,
                                          _vp, C.POINTER(MikvPrefillSrc), _vp, _vp, _sz, _vp]),
     "mikv_criticalkv_workspace": (_sz, [_i32, _i32, _i32, _i32]),
-    "mikv_criticalkv_select": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp,
+    "mikv_criticalkv_select": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f64, _vp, _vp,
                                          _vp, _sz, _vp]),
 }
 

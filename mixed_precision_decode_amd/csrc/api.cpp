@@ -287,18 +287,18 @@ size_t mikv_criticalkv_workspace(int32_t H, int32_t T, int32_t d, int32_t hidden
 
 mikv_status mikv_criticalkv_select(const float* A, const uint16_t* V, const uint16_t* W_O,
                                    int32_t H, int32_t T, int32_t d, int32_t hidden,
-                                   int32_t budget, float alpha, int32_t* idx, float* score2,
+                                   int32_t budget, double alpha, int32_t* idx, float* score2,
                                    void* ws, size_t ws_bytes, void* stream) {
   if (!A || !V || !W_O || !idx) return MIKV_ERR_NULL;
   if (H < 1 || T < 1 || hidden < 1) return MIKV_ERR_SHAPE;
   if (d != 128) return MIKV_ERR_UNSUPPORTED;
   if (hidden % 128 != 0) return MIKV_ERR_UNSUPPORTED;
   if (budget < 1 || budget > T) return MIKV_ERR_SHAPE;
-  if (!(alpha >= 0.0f && alpha <= 1.0f)) return MIKV_ERR_SHAPE;
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return MIKV_ERR_SHAPE;
   if (!aligned16(V) || !aligned16(W_O)) return MIKV_ERR_SHAPE;
   const size_t need = criticalkv_ws_bytes(H, T, d, hidden);
   if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
-  const int b1 = static_cast<int>(std::floor(static_cast<double>(alpha) * budget));
+  const int b1 = static_cast<int>(std::floor(alpha * budget));
   const int b2 = budget - b1;
   return from_hip(launch_criticalkv(A, V, W_O, H, T, d, hidden, b1, b2, idx, score2, ws,
                                     static_cast<hipStream_t>(stream)));

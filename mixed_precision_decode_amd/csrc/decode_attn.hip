@@ -48,7 +48,6 @@ constexpr int kThreads = 256;
 #endif
 constexpr int kTPT16 = MIKV_TPT16;  // FP16 tokens per thread per batch
 constexpr int kTPTQ = MIKV_TPTQ;    // low-bit tokens per thread per batch
-constexpr int kCUs = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 
@@ -221,8 +220,10 @@ __device__ __forceinline__ void write_partial(Acc<RT, CPL>& s, float* red, float
   }
 }
 
-// q-hat for the lane's CPL channels of the block's RT heads (fp32; the
-// reciprocal is the hardware approximation, q-hat only feeds scores).
+// q-hat for the lane's CPL channels of the block's RT heads: fp32(q) times
+// the hardware reciprocal of b (v_rcp_f32, within 1 ulp of 1/b) times
+// log2(e)/sqrt(d); q-hat only feeds scores, which are compared to a
+// tolerance.
 template <int D, int RT, int CPL>
 __device__ __forceinline__ void load_qhat(const DecodeK& p, int n, int g, int tile, int c0,
                                           const float* bvec, float (&qh)[RT][CPL]) {
@@ -948,6 +949,28 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
 
 static inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Compute units of the current device (the grid is sized to one resident
+// round of blocks over all of them), read once per device and cached; 256
+// (MI355X) when no device answers.
+static int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      return 256;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // Resident split-kernel blocks per compute unit for this instantiation, from
 // the runtime's occupancy calculator (cached per instantiation); the
 // default when it cannot answer (no device).
@@ -1002,7 +1025,7 @@ DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, 
   const double t16 = pl.RT == 1 ? b16 : 1.3 * cap16;
   const double tq = pl.RT == 1 ? bq : static_cast<double>(nq);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
-  long per_unit = (static_cast<long>(kCUs) * split_blocks_per_cu(d, bits, pl.RT)) / units;
+  long per_unit = (static_cast<long>(device_cus()) * split_blocks_per_cu(d, bits, pl.RT)) / units;
   // no split below ~16 KB of rows
   const long cap_splits = static_cast<long>((b16 + bq) / 16384.0) + 1;
   if (per_unit > cap_splits) per_unit = cap_splits;
@@ -1052,7 +1075,7 @@ size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, i
   const int rep = hq / hkv;
   DecodePlan pl = decode_plan(batch, hkv, d, bits, group, rep, cap16, nq_max);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
-  long per_unit = (static_cast<long>(kCUs) * MIKV_BLOCKS_PER_CU) / units;
+  long per_unit = (static_cast<long>(device_cus()) * MIKV_BLOCKS_PER_CU) / units;
   if (per_unit < 2) per_unit = 2;
   pl.S16 = static_cast<int>(per_unit + 1);
   pl.Sq = 0;

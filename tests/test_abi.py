@@ -36,7 +36,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.mikv_abi_version() == 1
+    assert lib.mikv_abi_version() == 2
     for s in range(7):
         assert len(L.mikv_status_str(s)) > 0
     assert L.mikv_status_str(99) == "unknown status"

@@ -113,7 +113,11 @@ def test_balance_parity(name, over):
 
 
 # ---------------------------------------------------------------- prefill build
-def _prefill_gpu(cfg, seed, balanced=True, capq=None):
+def _prefill_gpu(cfg, seed, balanced=True, capq=None, gpu_scores=False):
+    """Balancer and prefill build on the device. gpu_scores: the heavy-hitter
+    scores acc0 come from the prompt through mikv_prefill_scores (the method's
+    own chain) instead of the drawn stand-in; the returned acc0 is then the
+    device's, which both sides consume."""
     q, k, v, acc0 = S.prefill_tensors(cfg, seed)
     dims = dims_of(cfg, capq)
     cache = L.Cache(dims)
@@ -121,13 +125,21 @@ def _prefill_gpu(cfg, seed, balanced=True, capq=None):
         b, _ = _balance_gpu(cfg, q, k, want_kb=False)
     else:
         b = torch.ones((cfg.batch, cfg.hkv, cfg.d), dtype=torch.float32, device="cuda")
+    if gpu_scores:
+        acc_d = torch.empty((cfg.batch, cfg.hkv, cfg.T), dtype=torch.float32, device="cuda")
+        ws_s = torch.empty(max(1, L.mikv_prefill_scores_workspace(dims, cfg.T)), dtype=torch.uint8,
+                           device="cuda")
+        L.mikv_prefill_scores(dims, cfg.T, dev(q), dev(k), acc_d, ws_s)
+        acc0 = host(acc_d)
+    else:
+        acc_d = dev(acc0)
     ws = torch.empty(max(1, L.mikv_h2o_workspace(dims, cfg.T)), dtype=torch.uint8, device="cuda")
-    src = dict(k=dev(k), v=dev(v), acc0=dev(acc0), b=b if balanced else None)
+    src = dict(k=dev(k), v=dev(v), acc0=acc_d, b=b if balanced else None)
     L.mikv_h2o_update_select(dims, cache, cfg.T, cfg.recent, cfg.H, src=src, ws=ws)
     return dims, cache, b, (q, k, v, acc0)
 
 
-def _state_equal(gpu, ref, n16=None, nq=None):
+def _state_equal(gpu, ref):
     for key in ("pos16", "free16", "posq"):
         assert np.array_equal(gpu[key], ref[key]), key
     assert np.array_equal(gpu["acc16"].view(np.uint32), ref["acc16"].view(np.uint32))
@@ -162,53 +174,121 @@ def test_prefill_build_parity(name, over, balanced):
 
 
 # ---------------------------------------------------------------- decode lockstep
-def _lockstep(cfg, seed, steps, balanced=True, check_every=1):
-    dims, cache, b, _ = _prefill_gpu(cfg, seed, balanced)
+def _units_state(cache, units):
+    """The cache of the listed (sequence, kv head) units, gathered on the
+    device and copied to the host, laid out as a batch of units with one kv
+    head each (the oracle treats every unit independently)."""
+    ns = torch.tensor([u[0] for u in units], device="cuda")
+    gs = torch.tensor([u[1] for u in units], device="cuda")
+    out = {k: getattr(cache, k)[ns, gs].unsqueeze(1).cpu().numpy() for k in L.Cache.NAMES}
+    out["group"], out["bits"] = cache.dims.group, cache.dims.bits
+    return out
+
+
+def _units_inputs(cfg, units, qd, kd, vd, bh, o, p16, dpos):
+    """Step inputs and device outputs of the listed units, in the same
+    one-kv-head-per-unit layout."""
+    r = cfg.rep
+    q = np.stack([qd[n, g * r:(g + 1) * r] for n, g in units])
+    k = np.stack([kd[n, g:g + 1] for n, g in units])
+    v = np.stack([vd[n, g:g + 1] for n, g in units])
+    b = np.stack([bh[n, g:g + 1] for n, g in units])
+    oo = np.stack([o[n, g * r:(g + 1) * r] for n, g in units])
+    pp = np.stack([p16[n, g:g + 1] for n, g in units])
+    dp = np.stack([dpos[n, g:g + 1] for n, g in units])
+    return q, k, v, b, oo, pp, dp
+
+
+def _check_step(cfg, N, step, before, after, qd, kd, vd, bh, og, gp16, gdpos, mid=None):
+    """One decode step of the device against the oracle started from the
+    device's own state before the step (lockstep). All arrays are host
+    arrays laid out [units or sequences][kv heads][...]."""
+    ro, rp16, _, rst = O.decode_attention(before, N, qd, kd, vd, bh)
+    if mid is not None:
+        # separate calls: the attention call alone appends the new token
+        for key in ("k16", "v16"):
+            assert np.array_equal(bits16(mid[key]), bits16(rst[key])), key
+        assert np.array_equal(mid["pos16"], rst["pos16"])
+    assert_close(og, ro, f"o step {step}")
+    # probabilities below 2^-126 flush to 0 in fp32, fp64 keeps them
+    underflow = N * cfg.rep * 2.0 ** -126
+    assert_close(gp16.astype(F64), rp16, f"p16 step {step}", floor=underflow)
+    acc_prev = before["acc16"].astype(F64)
+    fr = before["free16"]
+    for i in range(acc_prev.shape[0]):
+        for g in range(acc_prev.shape[1]):
+            acc_prev[i, g, fr[i, g]] = 0.0
+    acc = after["acc16"].astype(F64)
+    assert_close(acc, acc_prev + rp16, f"acc step {step}", floor=underflow)
+    # the step's increment on its own, to the p16 rule; the stored fp32 sum
+    # is rounded once (half an ulp of the new score)
+    inc_err = np.abs(acc - acc_prev - rp16) - 2.0 ** -24 * np.abs(acc)
+    lim = TOL * np.max(np.abs(rp16)) + underflow
+    assert np.max(inc_err) <= lim, f"acc increment step {step}: {np.max(inc_err):.3e} > {lim:.3e}"
+    # selection on the device's own fp32 scores must match exactly
+    drop = O.select_drop(acc, rst["pos16"], N, cfg.recent, cfg.H)
+    assert np.array_equal(after["free16"], drop), f"selection step {step}"
+    ref_mid = dict(rst)
+    ref_mid["acc16"] = after["acc16"]
+    rdem = O.demote(ref_mid, N, drop)
+    _state_equal(after, rdem)
+    assert np.array_equal(gdpos, np.take_along_axis(rst["pos16"], drop[..., None], 2)[..., 0])
+
+
+def _lockstep(cfg, seed, steps, balanced=True, check_every=1, fused=False, sample=0, gpu_scores=False):
+    """steps decode steps on the device; every check_every-th step (and the
+    last) is compared with the oracle over all units, and with sample > 0
+    every other step is compared over `sample` units (a different set each
+    step). fused: one mikv_decode_step call per step (the benchmark's launch
+    configuration); else mikv_decode_attn then mikv_h2o_update_select.
+    gpu_scores: the prompt's heavy-hitter scores come from
+    mikv_prefill_scores, and the prefill build on them is checked first."""
+    dims, cache, b, (q, k, v, acc0) = _prefill_gpu(cfg, seed, balanced, gpu_scores=gpu_scores)
     bh = host(b)
+    if gpu_scores:
+        kb = O.balance(q, k)[1] if balanced else k
+        ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq())
+        _state_equal(cache.to_numpy(), ref)
+        print(f"  prefill build on the device's prompt scores matches the oracle", flush=True)
+    del q, k, v
     o = torch.empty((cfg.batch, cfg.hq, cfg.d), dtype=torch.float32, device="cuda")
     p16 = torch.empty((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
     dpos = torch.empty((cfg.batch, cfg.hkv), dtype=torch.int32, device="cuda")
     ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + steps), dtype=torch.uint8,
                      device="cuda")
+    n_units = cfg.batch * cfg.hkv
     N = cfg.T
+    checked = sampled = 0
     for step in range(steps):
         N += 1
         qd, kd, vd = S.decode_tensors(cfg, seed, step)
-        check = step % check_every == 0 or step == steps - 1
-        if check:
-            before = cache.to_numpy()
-        L.mikv_decode_attn(dims, cache, N, dev(qd), dev(kd), dev(vd), b, o, p16, ws)
-        if check:
-            mid = cache.to_numpy()
-        L.mikv_h2o_update_select(dims, cache, N, cfg.recent, cfg.H, p16=p16, demoted_pos=dpos)
-        if not check:
-            continue
-        after = cache.to_numpy()
-        ro, rp16, _, rst = O.decode_attention(before, N, qd, kd, vd, bh)
-        # append: balanced key, value and position in the free slot
-        for key in ("k16", "v16"):
-            assert np.array_equal(bits16(mid[key]), bits16(rst[key])), key
-        assert np.array_equal(mid["pos16"], rst["pos16"])
-        assert_close(host(o), ro, f"o step {step}")
-        # p16 holds probabilities: scale = the group's total mass (rep)
-        underflow = N * cfg.rep * 2.0 ** -126
-        err = np.max(np.abs(host(p16).astype(F64) - rp16))
-        assert err <= TOL * cfg.rep, f"p16 step {step}: max err {err:.3e}"
-        acc_prev = before["acc16"].astype(F64)
-        fr = before["free16"]
-        for i in range(cfg.batch):
-            for g in range(cfg.hkv):
-                acc_prev[i, g, fr[i, g]] = 0.0
-        assert_close(after["acc16"], acc_prev + rp16, f"acc step {step}", floor=underflow)
-        # selection on the device's own fp32 scores must match exactly
-        drop = O.select_drop(after["acc16"].astype(F64), mid["pos16"], N, cfg.recent, cfg.H)
-        assert np.array_equal(after["free16"], drop), f"selection step {step}"
-        mid2 = dict(mid)
-        mid2["acc16"] = after["acc16"]
-        rdem = O.demote(mid2, N, drop)
-        _state_equal(after, rdem)
-        assert np.array_equal(host(dpos), np.take_along_axis(mid["pos16"], drop[..., None], 2)[..., 0])
-    return cache
+        full = step % check_every == 0 or step == steps - 1
+        units = None
+        if not full and sample > 0:
+            stride = max(1, n_units // sample)
+            units = sorted({((step * 7 + j * stride) % n_units) for j in range(min(sample, n_units))})
+            units = [(u // cfg.hkv, u % cfg.hkv) for u in units]
+        before = cache.to_numpy() if full else (_units_state(cache, units) if units else None)
+        mid = None
+        if fused:
+            L.mikv_decode_step(dims, cache, N, cfg.recent, cfg.H, dev(qd), dev(kd), dev(vd), b, o, p16,
+                               ws, demoted_pos=dpos)
+        else:
+            L.mikv_decode_attn(dims, cache, N, dev(qd), dev(kd), dev(vd), b, o, p16, ws)
+            if full:
+                mid = cache.to_numpy()
+            L.mikv_h2o_update_select(dims, cache, N, cfg.recent, cfg.H, p16=p16, demoted_pos=dpos)
+        if full:
+            _check_step(cfg, N, step, before, cache.to_numpy(), qd, kd, vd, bh, host(o), host(p16),
+                        host(dpos), mid)
+            checked += 1
+            if check_every > 1:
+                print(f"  step {step} (N={N}): all {n_units} units match the oracle", flush=True)
+        elif units:
+            ins = _units_inputs(cfg, units, qd, kd, vd, bh, host(o), host(p16), host(dpos))
+            _check_step(cfg, N, step, before, _units_state(cache, units), *ins)
+            sampled += 1
+    return cache, checked, sampled
 
 
 @pytest.mark.parametrize("name,over,balanced,steps", [
@@ -235,13 +315,57 @@ def test_decode_lockstep(name, over, balanced, steps):
     _lockstep(cfg, 11, steps, balanced)
 
 
-@pytest.mark.parametrize("name", ["llama2_7b_layer", "llama3_8b_32k", "gqa_throughput"])
-def test_decode_full_size(name):
-    """The configs' full shapes, two lockstep steps, in the launch
-    configuration the benchmark times."""
+@pytest.mark.parametrize("name,over,steps", [
+    ("tiny", {}, 16),
+    ("tiny", dict(hq=8, hkv=2, bits=2), 8),
+    # 1 sequence x 8 kv heads, groups of 4, INT2: the fused merge with a
+    # separate p16/H2O block, decode_merge_kernel<128, 2, 8, true, 1>
+    ("llama3_8b_32k", dict(T=6000), 4),
+    # 43 x 8 units of 4 heads: 4 output groups per merge block and no room for
+    # a separate H2O block (output block 0 runs it), <128, 4, 8, true, 4>
+    ("gqa_throughput", dict(batch=43, T=300), 4),
+    ("llama2_7b_layer", dict(T=700), 3),
+])
+def test_decode_lockstep_fused(name, over, steps):
+    """mikv_decode_step (attention with the H2O update fused into its merge
+    launch) against the oracle, every step."""
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"fused lockstep {name} {over} steps={steps}", flush=True)
+    _lockstep(cfg, 13, steps, fused=True)
+
+
+@pytest.mark.parametrize("name,over,steps", [
+    ("tiny", dict(hq=4, hkv=2), 12),
+    ("gqa_throughput", dict(batch=4, T=900), 6),
+    ("llama2_7b_layer", {}, 12),
+])
+def test_prompt_scores_to_decode(name, over, steps):
+    """The method's own chain: prompt heavy-hitter scores on the device
+    (mikv_prefill_scores), the balancer and prefill build on those scores
+    (exact against the oracle given the same scores), then decode steps
+    through mikv_decode_step in lockstep with the oracle. The Llama-2-7B
+    layer runs at full size (sampled units per step, all units at the last)."""
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"prompt scores -> prefill build -> decode: {name} {over} steps={steps}", flush=True)
+    full = name == "llama2_7b_layer" and not over
+    _lockstep(cfg, 1000 + list(S.CONFIGS).index(name), steps, fused=True, gpu_scores=True,
+              check_every=steps if full else 1, sample=8 if full else 0)
+
+
+@pytest.mark.parametrize("name,check_every", [("llama2_7b_layer", 16), ("llama3_8b_32k", 8),
+                                              ("gqa_throughput", 20)])
+def test_decode_full_size(name, check_every):
+    """The configs' full shapes over every decode step they define, through
+    mikv_decode_step as the benchmark launches it (seed 1000 + config index).
+    Every step is compared with the oracle, started from the device state
+    before that step: over all units every check_every-th step and at the
+    last, over 8 units (a different set each step) at the others."""
     cfg = S.CONFIGS[name]
-    print(f"full-size lockstep {name}", flush=True)
-    _lockstep(cfg, 1000 + list(S.CONFIGS).index(name), 2)
+    print(f"full-size lockstep {name}: {cfg.steps} steps, all units every {check_every}", flush=True)
+    _, checked, sampled = _lockstep(cfg, 1000 + list(S.CONFIGS).index(name), cfg.steps,
+                                    check_every=check_every, fused=True, sample=8)
+    assert checked + sampled == cfg.steps
+    print(f"full-size lockstep {name}: {checked} full checks, {sampled} sampled", flush=True)
 
 
 # ---------------------------------------------------------------- CriticalKV
@@ -258,7 +382,7 @@ def _ckv_gpu(A, V, W, budget, alpha):
 def _ckv_check(A, V, W, budget, alpha, sample=None):
     H, T = A.shape
     idx, sc = _ckv_gpu(A, V, W, budget, alpha)
-    b1 = int(np.floor(F64(np.float32(alpha)) * budget))
+    b1 = int(np.floor(F64(alpha) * budget))
     pos = np.arange(T)
     s1 = np.zeros((H, T), bool)
     for h in range(H):
@@ -297,6 +421,9 @@ def _ckv_check(A, V, W, budget, alpha, sample=None):
 @pytest.mark.parametrize("H,T,hidden,budget,alpha", [
     (8, 1000, 256, 200, 0.5), (8, 1000, 256, 200, 0.0), (8, 1000, 256, 200, 1.0),
     (3, 257, 128, 1, 0.5), (3, 257, 128, 257, 0.5), (16, 4099, 512, 811, 0.3),
+    # decimals whose float32 rounding lies below the decimal: floor(0.7f * 10) = 6,
+    # floor(0.7 * 10) = 7 in double
+    (4, 300, 128, 10, 0.7), (4, 300, 128, 10, 0.9), (4, 1000, 128, 100, 0.29),
 ])
 def test_criticalkv_parity(H, T, hidden, budget, alpha):
     print(f"criticalkv H={H} T={T} hidden={hidden} budget={budget} alpha={alpha}", flush=True)

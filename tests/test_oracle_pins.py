@@ -483,3 +483,111 @@ def test_prefill_scores_match_causal_sdpa_weights():
     ref = w.sum(axis=2).reshape(n, hkv, rep, T).sum(axis=2)
     assert np.allclose(O.prefill_scores(q, k), ref, rtol=1e-10, atol=1e-12)
 
+
+
+# ---------------------------------------------------------------- multi-step H2O bookkeeping
+def _grid_history(seed, T, steps, d, G, rep):
+    """Keys whose per-token groups quantize losslessly at INT4: every group is
+    z + 0.25*c with integer c in [0, 15] and both c = 0 and c = 15 present, so
+    scale = 0.25 and zero = z exactly and dequant(quant(k)) == k. The mixed
+    attention then equals plain softmax attention over the full history,
+    whichever tokens sit in which tier, so the probabilities each step hands
+    out can be recomputed from the history alone."""
+    rng = np.random.default_rng(seed)
+    n_tok = T + steps
+    c = rng.integers(0, 16, (n_tok, d // G, G))
+    c[:, :, 0] = 0
+    c[:, :, 1] = 15
+    for t in range(n_tok):
+        for j in range(d // G):
+            c[t, j] = c[t, j][rng.permutation(G)]
+    z = rng.integers(-8, 9, (n_tok, d // G, 1)) * 0.25
+    k_all = (z + 0.25 * c).reshape(n_tok, d).astype(F16)
+    v_all = rng.standard_normal((n_tok, d)).astype(F16)
+    q_all = (rng.standard_normal((steps, rep, d)) * 0.6).astype(F16)
+    return k_all, v_all, q_all
+
+
+def _brute_probs(q_all, k_all, T, j):
+    """Softmax weights of decode step j (length T + j + 1) summed over the
+    group's query heads, float64, from the full history (no tiers)."""
+    N = T + j + 1
+    d = k_all.shape[1]
+    s = q_all[j].astype(F64) @ k_all[:N].astype(F64).T / math.sqrt(d)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+
+
+def test_h2o_scores_carry_over_steps_and_restart_for_new_tokens():
+    """acc after k decode steps = acc0 (prompt tokens) + the sum of every
+    step's probability since the token arrived, recomputed from the history;
+    a token appended during decode starts from 0, not from the score of the
+    token it replaced in its slot (heavy hitters = accumulated attention,
+    paperlayer section 5; the new token's score starts with its first step).
+    Also re-runs the one-way selection from those brute-force scores: each
+    step demotes the FP16 candidate outside the window with the smallest
+    (score, -position), and its key and value rows land in the low-bit tier
+    within scale/2 of the original rows."""
+    T, steps, d, G, rep, B, R = 24, 7, 16, 8, 2, 10, 3
+    H = B - R
+    k_all, v_all, q_all = _grid_history(77, T, steps, d, G, rep)
+    rng = np.random.default_rng(5)
+    acc0 = (rng.integers(1, 6, T) * 0.125).astype(F32)[None, None]   # positive, with ties
+    st = O.prefill_build(k_all[None, None, :T], v_all[None, None, :T], acc0, B, R, G, 4, T - B + steps)
+    b = np.ones((1, 1, d), F32)
+    bf = {int(p): F64(acc0[0, 0, p]) for p in st["pos16"][0, 0, :B]}     # brute-force scores
+    resident = set(bf)
+    demoted_kv_differ = False
+    for j in range(steps):
+        N = T + j + 1
+        qd = q_all[j][None]
+        kd, vd = k_all[N - 1][None, None], v_all[N - 1][None, None]
+        _, _, st, drop = O.decode_step(st, N, qd, kd, vd, b, R, H)
+        P = _brute_probs(q_all, k_all, T, j)
+        bf[N - 1] = F64(0.0)
+        resident.add(N - 1)
+        for p in resident:
+            bf[p] += P[p]
+        cand = [p for p in resident if p < N - R]
+        worst = min(cand, key=lambda p: (bf[p], -p))
+        ranked = sorted(bf[p] for p in cand)
+        assert ranked[1] - ranked[0] > 1e-6, "planted scores must not nearly tie"
+        slot = N - (B + 1)
+        dpos = int(st["posq"][0, 0, slot])
+        assert dpos == worst, f"step {j}: demoted {dpos}, brute force {worst}"
+        resident.remove(worst)
+        # every resident token's stored score equals its brute-force sum
+        pos16 = st["pos16"][0, 0]
+        fr = st["free16"][0, 0]
+        for s_ in range(B + 1):
+            if s_ == fr:
+                continue
+            p = int(pos16[s_])
+            assert p in resident
+            assert abs(F64(st["acc16"][0, 0, s_]) - bf[p]) <= 1e-6 * max(1.0, bf[p]), (j, p)
+        # the demoted rows: keys exact (grid), values within scale/2 of v
+        kr = O.dequantize_rows(st["kq"][0, 0, slot:slot + 1], st["ksz"][0, 0, slot:slot + 1], G, 4)[0]
+        assert np.array_equal(kr, k_all[dpos].astype(F64))
+        vr = O.dequantize_rows(st["vq"][0, 0, slot:slot + 1], st["vsz"][0, 0, slot:slot + 1], G, 4)[0]
+        vs = np.repeat(st["vsz"][0, 0, slot, :, 0].astype(F64), G)
+        assert np.all(np.abs(vr - v_all[dpos].astype(F64)) <= 0.5 * vs * (1 + 1e-6))
+        demoted_kv_differ |= not np.array_equal(st["vq"][0, 0, slot], st["kq"][0, 0, slot])
+    assert demoted_kv_differ
+
+
+def test_new_token_score_is_its_own_probability():
+    """Right after its first step, the appended token's score is exactly the
+    probability the group's heads gave it at that step (no carried score)."""
+    T, d, G, rep, B, R = 20, 16, 8, 2, 8, 2
+    k_all, v_all, q_all = _grid_history(3, T, 3, d, G, rep)
+    acc0 = np.full((1, 1, T), 2.0, F32)
+    st = O.prefill_build(k_all[None, None, :T], v_all[None, None, :T], acc0, B, R, G, 4, T - B + 3)
+    b = np.ones((1, 1, d), F32)
+    for j in range(3):
+        N = T + j + 1
+        fr = int(st["free16"][0, 0])
+        _, _, st, _ = O.decode_step(st, N, q_all[j][None], k_all[N - 1][None, None],
+                                    v_all[N - 1][None, None], b, R, B - R)
+        assert st["pos16"][0, 0, fr] == N - 1
+        P = _brute_probs(q_all, k_all, T, j)
+        assert abs(F64(st["acc16"][0, 0, fr]) - P[N - 1]) <= 1e-6 * P[N - 1]
