@@ -67,7 +67,9 @@ typedef enum {
   MIKV_ERR_UNSUPPORTED = 3, /* d, bits or group outside the supported set   */
   MIKV_ERR_CAPACITY = 4,    /* the low-bit tier would exceed capq slots     */
   MIKV_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required      */
-  MIKV_ERR_HIP = 6          /* a HIP call or kernel launch failed           */
+  MIKV_ERR_HIP = 6,         /* a HIP call or kernel launch failed           */
+  MIKV_ERR_SCRATCH = 7      /* shape needs more than the fixed device
+                               scratch of mikv_decode_step_noalloc          */
 } mikv_status;
 
 /* Static English text for a status value (never NULL). */
@@ -310,6 +312,32 @@ mikv_status mikv_decode_step(const mikv_dims* dims, const mikv_cache* cache,
                              const uint16_t* v_new, const float* b, float* o,
                              float* p16, int32_t* demoted_pos, void* ws,
                              size_t ws_bytes, void* stream);
+
+/*
+ * mikv_decode_step for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc. Same computation, arguments, outputs and errors as
+ * mikv_decode_step, except that the per-split partial results live in a
+ * fixed device array of the library (mikv_decode_step_noalloc_limit()
+ * bytes, 16 MiB, on every device the library runs on, held until the
+ * process ends) instead of a caller workspace. No call allocates or frees
+ * memory; the first call on a device looks the array's address up once.
+ * Calls on one device share the array: calls that overlap in time on one
+ * device (two streams, two host threads) race and give undefined results;
+ * calls ordered on one stream are safe. The array needs no initial
+ * contents (each call writes what it reads).
+ * Errors: as mikv_decode_step; a shape whose partial results exceed the
+ * array (mikv_decode_attn_workspace(dims, len) > the limit) ->
+ * MIKV_ERR_SCRATCH, nothing enqueued.
+ */
+size_t mikv_decode_step_noalloc_limit(void);
+mikv_status mikv_decode_step_noalloc(const mikv_dims* dims,
+                                     const mikv_cache* cache, int32_t len,
+                                     int32_t recent, int32_t heavy,
+                                     const uint16_t* q, const uint16_t* k_new,
+                                     const uint16_t* v_new, const float* b,
+                                     float* o, float* p16,
+                                     int32_t* demoted_pos, void* stream);
 
 /*
  * CriticalKV two-stage selection per head ([gist CriticalKV] Algorithm 1;

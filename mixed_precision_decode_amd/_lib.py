@@ -16,7 +16,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmikv.so")
 
 MIKV_OK, MIKV_ERR_NULL, MIKV_ERR_SHAPE, MIKV_ERR_UNSUPPORTED = 0, 1, 2, 3
-MIKV_ERR_CAPACITY, MIKV_ERR_WORKSPACE, MIKV_ERR_HIP = 4, 5, 6
+MIKV_ERR_CAPACITY, MIKV_ERR_WORKSPACE, MIKV_ERR_HIP, MIKV_ERR_SCRATCH = 4, 5, 6, 7
 
 _vp, _sz, _i32, _i64, _f64 = C.c_void_p, C.c_size_t, C.c_int32, C.c_int64, C.c_double
 
@@ -58,6 +58,9 @@ _SIGS = {
                                          _vp, _vp, _vp, _vp, _sz, _vp, _vp, _vp]),
     "mikv_decode_step": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _i32, _i32, _vp,
                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mikv_decode_step_noalloc_limit": (_sz, []),
+    "mikv_decode_step_noalloc": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _i32, _i32,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mikv_h2o_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
     "mikv_h2o_update_select": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _i32, _i32,
                                          _vp, C.POINTER(MikvPrefillSrc), _vp, _vp, _sz, _vp]),
@@ -289,6 +292,23 @@ def mikv_decode_step(dims: Dims, cache: Cache, length: int, recent: int, heavy: 
         _ptr(o, _f32t(), (n, hq, d), "o"), _ptr(p16, _f32t(), (n, hkv, dims.cap16), "p16"),
         _ptr(demoted_pos, _i32t(), (n, hkv), "demoted_pos", optional=True),
         _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mikv_decode_step_noalloc_limit() -> int:
+    return lib().mikv_decode_step_noalloc_limit()
+
+
+def mikv_decode_step_noalloc(dims: Dims, cache: Cache, length: int, recent: int, heavy: int, q, k_new,
+                             v_new, b, o, p16, demoted_pos=None, stream=None):
+    """mikv_decode_step with the library's fixed device scratch in place of
+    a workspace (no allocation)."""
+    n, hq, hkv, d = dims.batch, dims.hq, dims.hkv, dims.d
+    _check(lib().mikv_decode_step_noalloc(
+        C.byref(dims.c()), C.byref(cache.c()), length, recent, heavy,
+        _ptr(q, "f16", (n, hq, d), "q"), _ptr(k_new, "f16", (n, hkv, d), "k_new"),
+        _ptr(v_new, "f16", (n, hkv, d), "v_new"), _ptr(b, _f32t(), (n, hkv, d), "b"),
+        _ptr(o, _f32t(), (n, hq, d), "o"), _ptr(p16, _f32t(), (n, hkv, dims.cap16), "p16"),
+        _ptr(demoted_pos, _i32t(), (n, hkv), "demoted_pos", optional=True), _stream(stream)))
 
 
 def mikv_h2o_update_select(dims: Dims, cache: Cache, length: int, recent: int, heavy: int,

@@ -64,6 +64,7 @@ const char* mikv_status_str(int s) {
     case MIKV_ERR_CAPACITY: return "low-bit tier capacity exceeded";
     case MIKV_ERR_WORKSPACE: return "workspace missing or too small";
     case MIKV_ERR_HIP: return "HIP call or kernel launch failed";
+    case MIKV_ERR_SCRATCH: return "shape needs more than the library's fixed device scratch";
     default: return "unknown status";
   }
 }
@@ -190,10 +191,16 @@ mikv_status mikv_decode_attn_timed(const mikv_dims* m, const mikv_cache* c, int3
                      split_stop);
 }
 
-mikv_status mikv_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t len, int32_t recent,
-                             int32_t heavy, const uint16_t* q, const uint16_t* k_new,
-                             const uint16_t* v_new, const float* b, float* o, float* p16,
-                             int32_t* demoted_pos, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks of a decode step; on success `plan` and `need` (workspace
+// bytes for this length) are set.
+mikv_status check_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t len, int32_t recent,
+                              int32_t heavy, const uint16_t* q, const uint16_t* k_new,
+                              const uint16_t* v_new, const float* b, const float* o,
+                              const float* p16, DecodePlan* plan, size_t* need) {
   mikv_status st = check_dims(m, true);
   if (st != MIKV_OK) return st;
   st = check_cache(c);
@@ -204,10 +211,16 @@ mikv_status mikv_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t le
   const int nq = len - m->cap16;
   if (nq < 0) return MIKV_ERR_SHAPE;
   if (nq + 1 > m->capq) return MIKV_ERR_CAPACITY;  // the demotion adds one low-bit token
-  const DecodePlan pl = decode_plan(m->batch, m->hkv, m->d, m->bits, m->group, m->hq / m->hkv,
-                                    m->cap16, nq);
-  const size_t need = decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, pl);
-  if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
+  *plan = decode_plan(m->batch, m->hkv, m->d, m->bits, m->group, m->hq / m->hkv, m->cap16, nq);
+  *need = decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, *plan);
+  return MIKV_OK;
+}
+
+// Launches of a checked decode step with workspace ws.
+mikv_status launch_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t len, int32_t recent,
+                               int32_t heavy, const uint16_t* q, const uint16_t* k_new,
+                               const uint16_t* v_new, const float* b, float* o, float* p16,
+                               int32_t* demoted_pos, const DecodePlan& pl, void* ws, void* stream) {
   DecodeArgs a;
   a.batch = m->batch; a.hq = m->hq; a.hkv = m->hkv; a.d = m->d; a.group = m->group;
   a.bits = m->bits; a.cap16 = m->cap16; a.capq = m->capq; a.len = len;
@@ -235,6 +248,40 @@ mikv_status mikv_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t le
   h.kq = c->kq; h.vq = c->vq; h.ksz = c->ksz; h.vsz = c->vsz; h.posq = c->posq;
   h.p16 = p16; h.demoted_pos = demoted_pos;
   return from_hip(launch_h2o_decode(h, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+mikv_status mikv_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t len, int32_t recent,
+                             int32_t heavy, const uint16_t* q, const uint16_t* k_new,
+                             const uint16_t* v_new, const float* b, float* o, float* p16,
+                             int32_t* demoted_pos, void* ws, size_t ws_bytes, void* stream) {
+  DecodePlan pl;
+  size_t need = 0;
+  const mikv_status st = check_decode_step(m, c, len, recent, heavy, q, k_new, v_new, b, o, p16, &pl, &need);
+  if (st != MIKV_OK) return st;
+  if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
+  return launch_decode_step(m, c, len, recent, heavy, q, k_new, v_new, b, o, p16, demoted_pos, pl, ws,
+                            stream);
+}
+
+size_t mikv_decode_step_noalloc_limit(void) { return kStaticScratchBytes; }
+
+mikv_status mikv_decode_step_noalloc(const mikv_dims* m, const mikv_cache* c, int32_t len,
+                                     int32_t recent, int32_t heavy, const uint16_t* q,
+                                     const uint16_t* k_new, const uint16_t* v_new, const float* b,
+                                     float* o, float* p16, int32_t* demoted_pos, void* stream) {
+  DecodePlan pl;
+  size_t need = 0;
+  const mikv_status st = check_decode_step(m, c, len, recent, heavy, q, k_new, v_new, b, o, p16, &pl, &need);
+  if (st != MIKV_OK) return st;
+  if (need > kStaticScratchBytes) return MIKV_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (static_scratch_ptr(&ws) != hipSuccess || !ws) return MIKV_ERR_HIP;
+  return launch_decode_step(m, c, len, recent, heavy, q, k_new, v_new, b, o, p16, demoted_pos, pl, ws,
+                            stream);
 }
 
 // ---------------------------------------------------------------- H2O

@@ -60,6 +60,10 @@ hipError_t launch_decode_attn(const DecodeArgs& a, const DecodePlan& plan, hipSt
 // largest FP16 tier the fused merge handles (slots held in registers)
 constexpr int kFusedMaxCap16 = 16 * 256;
 
+// Fixed device scratch of mikv_decode_step_noalloc (16 MiB per device).
+constexpr size_t kStaticScratchBytes = size_t{16} << 20;
+hipError_t static_scratch_ptr(void** ptr);
+
 struct H2OArgs {
   int batch, hkv, d, group, bits, cap16, capq, len, recent, heavy;
   uint16_t* k16;

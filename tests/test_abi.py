@@ -29,7 +29,7 @@ def _header_functions():
 
 def test_exports_every_declared_function(lib):
     names = _header_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L._SIGS)
@@ -37,7 +37,7 @@ def test_exports_every_declared_function(lib):
 
 def test_abi_version_and_status_text(lib):
     assert lib.mikv_abi_version() == 2
-    for s in range(7):
+    for s in range(8):
         assert len(L.mikv_status_str(s)) > 0
     assert L.mikv_status_str(99) == "unknown status"
 
@@ -131,6 +131,26 @@ def test_decode_step_validation(lib):
     assert call(length=111) == L.MIKV_ERR_CAPACITY     # demotion would need slot 100
     assert call(ws_bytes=16) == L.MIKV_ERR_WORKSPACE
     assert call(_dims(bits=8)) == L.MIKV_ERR_UNSUPPORTED
+
+
+def test_decode_step_noalloc_validation(lib):
+    """The fixed-scratch decode step checks like mikv_decode_step and
+    rejects shapes whose partial results exceed its scratch before any
+    HIP call."""
+    c = _cache()
+    good = _dims()
+    assert lib.mikv_decode_step_noalloc_limit() == 16 << 20
+    call = lambda dims=good, length=50, recent=4, heavy=6, q=FAKE: lib.mikv_decode_step_noalloc(
+        C.byref(dims.c()), C.byref(c), length, recent, heavy, q, FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert call(q=None) == L.MIKV_ERR_NULL
+    assert call(recent=5) == L.MIKV_ERR_SHAPE
+    assert call(length=10) == L.MIKV_ERR_SHAPE
+    assert call(length=111) == L.MIKV_ERR_CAPACITY
+    assert call(_dims(bits=8)) == L.MIKV_ERR_UNSUPPORTED
+    big = _dims(batch=64, hq=32, hkv=32, cap16=4097, capq=100)
+    need = lib.mikv_decode_attn_workspace(C.byref(big.c()), 4097 + 50)
+    assert need > lib.mikv_decode_step_noalloc_limit()
+    assert call(big, length=4097 + 50, recent=64, heavy=4032) == L.MIKV_ERR_SCRATCH
 
 
 def test_h2o_validation(lib):
