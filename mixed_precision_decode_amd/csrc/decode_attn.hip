@@ -25,6 +25,9 @@
 //   merge kernel  one block per (sequence, kv head): combines the split
 //                 partials of every query head of the group and turns the
 //                 FP16-tier scores into p16 (summed over the group).
+// Tiles of 2-4 query heads with groups of d/2 channels run the split step as
+// decode_tile_kernel (decode_tile.hpp): key scores on the matrix cores, one
+// lane per (token, heads) for the softmax, value sums on the vector ALUs.
 // Scores are in the log2 domain (q-hat is pre-multiplied by log2(e)/sqrt(d)).
 #include <atomic>
 #include <hip/hip_ext.h>
@@ -731,6 +734,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
   }
 }
 
+#include "decode_tile.hpp"
+
 // Grid: (unit, output chunk [+ 1]). An output block of unit x combines the
 // split partials of kMergeOut * G outputs (head, channel) of the unit,
 // kMergeTPO threads per output, each summing a strided subset of the splits,
@@ -748,6 +753,7 @@ constexpr int kMergeOut = 64;
 constexpr int kMergeTPO = kThreads / kMergeOut;
 constexpr int kMergeSlots = 16;  // FP16-tier slots per thread held in registers
 constexpr int kMergeHeads = 4;   // heads whose FP16-tier scores are loaded up front
+
 #ifndef MIKV_MERGE_MAX_BLOCKS
 #define MIKV_MERGE_MAX_BLOCKS 1024
 #endif
@@ -974,24 +980,33 @@ static int device_cus() {
 // Resident split-kernel blocks per compute unit for this instantiation, from
 // the runtime's occupancy calculator (cached per instantiation); the
 // default when it cannot answer (no device).
-template <int D, int BITS, int RT>
+template <int D, int BITS, int RT, bool TILE>
+static const void* split_kernel_ptr() {
+  if constexpr (TILE) return reinterpret_cast<const void*>(decode_tile_kernel<D, BITS, RT>);
+  else return reinterpret_cast<const void*>(decode_split_kernel<D, BITS, RT>);
+}
+template <int D, int BITS, int RT, bool TILE>
 static int occupancy_of() {
   int n = 0;
   const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &n, reinterpret_cast<const void*>(decode_split_kernel<D, BITS, RT>), kThreads, 0);
+      &n, split_kernel_ptr<D, BITS, RT, TILE>(), kThreads, 0);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
   return n;
 }
-static int split_blocks_per_cu(int d, int bits, int rt) {
-  static std::atomic<int> cache[2][2][3];
-  std::atomic<int>& c = cache[d == 128][bits == 4][rt == 1 ? 0 : (rt == 2 ? 1 : 2)];
+// Head tiles of 2-4 heads with groups of d/2 channels run decode_tile_kernel
+// (scores on the matrix cores); the other tiles decode_split_kernel.
+static inline bool use_tile_kernel(int d, int group, int rt) { return rt > 1 && group == d / 2; }
+static int split_blocks_per_cu(int d, int bits, int rt, bool tile) {
+  static std::atomic<int> cache[2][2][3][2];
+  std::atomic<int>& c = cache[d == 128][bits == 4][rt == 1 ? 0 : (rt == 2 ? 1 : 2)][tile ? 1 : 0];
   int n = c.load(std::memory_order_relaxed);
   if (n == 0) {
-#define MIKV_OCC(D_, B_, RT_) \
-  if (d == D_ && bits == B_ && rt == RT_) n = occupancy_of<D_, B_, RT_>();
+#define MIKV_OCC(D_, B_, RT_)                                                   \
+  if (d == D_ && bits == B_ && rt == RT_)                                       \
+    n = tile ? occupancy_of<D_, B_, RT_, (RT_ > 1)>() : occupancy_of<D_, B_, RT_, false>();
     MIKV_OCC(128, 4, 1) MIKV_OCC(128, 4, 2) MIKV_OCC(128, 4, 4)
     MIKV_OCC(128, 2, 1) MIKV_OCC(128, 2, 2) MIKV_OCC(128, 2, 4)
     MIKV_OCC(64, 4, 1) MIKV_OCC(64, 4, 2) MIKV_OCC(64, 4, 4)
@@ -1020,12 +1035,13 @@ DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, 
   DecodePlan pl;
   pl.RT = (rep % 4 == 0) ? 4 : (rep % 2 == 0 ? 2 : 1);
   pl.tiles = rep / pl.RT;
+  const bool tile = use_tile_kernel(d, group, pl.RT);
   const double b16 = static_cast<double>(cap16) * 4.0 * d;
   const double bq = static_cast<double>(nq) * 2.0 * (d * bits / 8 + 4 * (d / group));
   const double t16 = pl.RT == 1 ? b16 : 1.3 * cap16;
   const double tq = pl.RT == 1 ? bq : static_cast<double>(nq);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
-  long per_unit = (static_cast<long>(device_cus()) * split_blocks_per_cu(d, bits, pl.RT)) / units;
+  long per_unit = (static_cast<long>(device_cus()) * split_blocks_per_cu(d, bits, pl.RT, tile)) / units;
   // no split below ~16 KB of rows
   const long cap_splits = static_cast<long>((b16 + bq) / 16384.0) + 1;
   if (per_unit > cap_splits) per_unit = cap_splits;
@@ -1070,13 +1086,14 @@ size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int cap16, const Decod
 }
 
 // Workspace for every length up to nq_max: the partial count of any plan is
-// at most max(2, blocks-per-unit) + 1 splits per (sequence, kv head, tile).
+// at most max(4, blocks-per-unit) + 1 splits per (sequence, kv head, tile)
+// (head tiles take up to 4 splits when fewer than two blocks per unit fit).
 size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nq_max) {
   const int rep = hq / hkv;
   DecodePlan pl = decode_plan(batch, hkv, d, bits, group, rep, cap16, nq_max);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
   long per_unit = (static_cast<long>(device_cus()) * MIKV_BLOCKS_PER_CU) / units;
-  if (per_unit < 2) per_unit = 2;
+  if (per_unit < 4) per_unit = 4;
   pl.S16 = static_cast<int>(per_unit + 1);
   pl.Sq = 0;
   return decode_ws_bytes(batch, hq, hkv, d, cap16, pl);
@@ -1104,12 +1121,16 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   w += al256(nparts * pl.RT * D * sizeof(float));
   k.sc16 = reinterpret_cast<float*>(w);
   hipError_t e;
+  const bool tile = use_tile_kernel(D, a.group, RT);
+  const void* kfn = tile ? split_kernel_ptr<D, BITS, RT, (RT > 1)>() : split_kernel_ptr<D, BITS, RT, false>();
   if (a.ev_split_start || a.ev_split_stop) {
     // the events take the kernel's own start and end timestamps
     void* args[] = {&k};
-    e = hipExtLaunchKernel(reinterpret_cast<const void*>(decode_split_kernel<D, BITS, RT>),
-                           dim3(static_cast<unsigned>(nparts)), dim3(kThreads), args, 0, stream,
+    e = hipExtLaunchKernel(kfn, dim3(static_cast<unsigned>(nparts)), dim3(kThreads), args, 0, stream,
                            a.ev_split_start, a.ev_split_stop, 0);
+  } else if (tile) {
+    if constexpr (RT > 1) decode_tile_kernel<D, BITS, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
+    e = hipGetLastError();
   } else {
     decode_split_kernel<D, BITS, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
     e = hipGetLastError();

@@ -1,0 +1,488 @@
+// Head tiles (2-4 query heads sharing a kv head) of the split kernel, with the
+// key scores on the matrix cores.
+//
+// velog notes "No Token Left Behind ...", section 3.4: decode attention is a
+// batched matrix-vector product over a precision-grouped cache. With g query
+// heads per kv head the product against the keys is a small matrix product
+// (heads x tokens x channels); here it runs as v_mfma_f32_16x16x32_f16:
+//   A = q-hat, rows = the tile's heads (rows RT..15 zero), k = 32 channels;
+//   B = keys of 16 tokens, k = the same 32 channels, columns = tokens;
+//   D = scores, lane l < 16 holds the RT head scores of token l.
+// q-hat enters as two fp16 operands, hi = fp16(q-hat) and lo = fp16(q-hat -
+// hi), accumulated into the same D, so the product keeps about 22 bits of
+// q-hat (fp32 q-hat is the reading the method needs: the query stays floating
+// point). Low-bit key codes enter as exact fp16 integers. The score of a
+// low-bit token is then scale * (q . code) + zero * sum(q) per group of d/2
+// channels, so the channels of one MFMA never span two groups.
+//
+// Every (token, head) score, its exp and its running-max check are computed
+// once, on the lane that holds it. The value sums stay on the vector ALUs in
+// row layout (8 channels per lane, the token's probability times the value
+// scale read from LDS); the zero-point part sum(p * zero) is kept per head and
+// group on the score lanes. The running maximum per head is lazy: it moves
+// only when a score exceeds it by more than kTileHeadroom (log2 units), so
+// the rescaling of the sums is rare and the common path has no reduction.
+#pragma once
+
+#ifndef MIKV_TILE_NS
+#define MIKV_TILE_NS 2
+#endif
+
+typedef _Float16 tile_h8 __attribute__((ext_vector_type(8)));
+typedef float tile_f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int tile_u4 __attribute__((ext_vector_type(4)));
+
+constexpr float kTileHeadroom = 16.0f;
+constexpr int kTileG = 16;  // tokens per MFMA group
+
+// Element e of chunk c (32 channels) for lane group r: the channel it holds.
+// Chunks 0..CPG-1 cover group 0 (channels [0, d/2)), the rest group 1; lane
+// group r takes a contiguous run of 8*CPG channels of each group. Within the
+// 8 channels of a chunk the order is the one the code conversion produces.
+template <int D, int BITS, bool F16T>
+__device__ __forceinline__ constexpr int tile_chan(int c, int r, int e) {
+  constexpr int CPG = D / 64, G = D / 2;
+  int pe = e;
+  if constexpr (!F16T && BITS == 4) pe = (e < 4) ? 2 * e : 2 * (e - 4) + 1;
+  if constexpr (!F16T && BITS == 2) pe = (e % 2 == 0) ? e / 2 : 4 + e / 2;
+  return (c / CPG) * G + 8 * CPG * r + (c % CPG) * 8 + pe;
+}
+
+template <int NB>
+struct TileBytes { uint32_t w[(NB + 3) / 4]; };
+
+// NB bytes at byte offset off of a buffer resource (NB in {2, 4, 8, 16, 32}).
+template <int NB>
+__device__ __forceinline__ void tile_load(Rsrc r, uint32_t off, uint32_t* w) {
+  if constexpr (NB == 32) {
+    const Words<4> a = bload<4>(r, off), b = bload<4>(r, off + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { w[i] = a.w[i]; w[4 + i] = b.w[i]; }
+  } else if constexpr (NB == 16) {
+    const Words<4> a = bload<4>(r, off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = a.w[i];
+  } else if constexpr (NB == 8) {
+    const Words<2> a = bload<2>(r, off);
+    w[0] = a.w[0]; w[1] = a.w[1];
+  } else if constexpr (NB == 4) {
+    w[0] = bload1(r, off);
+  } else {
+    w[0] = static_cast<uint32_t>(
+        __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, kBufNT));
+  }
+}
+
+// 8 codes -> the MFMA operand (exact fp16 integers, order of tile_chan).
+template <int BITS>
+__device__ __forceinline__ tile_h8 tile_codes(uint32_t w, uint32_t magic) {
+  constexpr uint32_t kLo = 0x04010400u, kHi = 0x04030402u;
+  tile_u4 u;
+  if constexpr (BITS == 4) {  // 8 nibbles of one word
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    u[0] = __builtin_amdgcn_perm(magic, lo, kLo);
+    u[1] = __builtin_amdgcn_perm(magic, lo, kHi);
+    u[2] = __builtin_amdgcn_perm(magic, hi, kLo);
+    u[3] = __builtin_amdgcn_perm(magic, hi, kHi);
+  } else {  // 8 crumbs in the low 16 bits
+#pragma unroll
+    for (int m = 0; m < 4; ++m) u[m] = __builtin_amdgcn_perm(magic, (w >> (2 * m)) & 0x0303u, kLo);
+  }
+  return __builtin_bit_cast(tile_h8, u) - static_cast<tile_h8>(static_cast<_Float16>(1024.0f));
+}
+
+template <int D, int BITS, bool F16T>
+struct TileRegs {
+  static constexpr int CPG = D / 64;
+  static constexpr int KB = F16T ? 16 * CPG : CPG * BITS;     // key bytes per lane and group
+  static constexpr int KW = F16T ? 4 * CPG : (KB + 3) / 4;    // words per lane and group
+  static constexpr int LPTV = D / 8, VSLOTS = 64 / LPTV, VTPL = kTileG / VSLOTS;
+  static constexpr int VB = F16T ? 16 : BITS;                 // value bytes per lane and token
+  static constexpr int VW = (VB + 3) / 4;
+  uint32_t k[2][KW];
+  uint32_t ksz[2], vsz[2];
+  uint32_t v[VTPL][VW];
+};
+
+template <int D, int BITS, int RT, bool F16T>
+__device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, int g, int tile, int split,
+                                           const float* bvec, float* red, float (*sm)[RT], float* po,
+                                           float2* pml, float (*wbuf)[kTileG][2][RT]) {
+  using R_t = TileRegs<D, BITS, F16T>;
+  constexpr int NCH = D / 32, CPG = D / 64, G = D / 2;
+  constexpr int LPTV = R_t::LPTV, VSLOTS = R_t::VSLOTS, VTPL = R_t::VTPL;
+  constexpr int ROWB = F16T ? 2 * D : D * BITS / 8;  // bytes per token row
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int ai = lane % 16, ar = lane / 16;           // MFMA row / k block of this lane
+  const int vs = lane / LPTV, vj = lane % LPTV;       // value slot, 8-channel slice
+  const int vg = (8 * vj) / G;                        // value group of the slice
+
+  // ---- block range and buffer resources
+  int nt, frel = -1;
+  Rsrc rk, rv, rks, rvs;
+  int64_t scb = 0, rb16 = 0;
+  if constexpr (F16T) {
+    const int s0 = split * p.C16;
+    const int s1 = min(p.cap16, s0 + p.C16);
+    nt = max(s1 - s0, 0);
+    rb16 = static_cast<int64_t>(unit) * p.cap16;
+    frel = p.free16[unit] - s0;
+    rk = make_rsrc(p.k16 + (rb16 + s0) * D, static_cast<uint32_t>(nt) * ROWB);
+    rv = make_rsrc(p.v16 + (rb16 + s0) * D, static_cast<uint32_t>(nt) * ROWB);
+    rks = rk;  // no scales on the FP16 tier
+    rvs = rv;
+    scb = (static_cast<int64_t>(unit) * p.rep + tile * RT) * p.cap16 + s0;
+  } else {
+    const int t0 = (split - p.S16) * p.Cq;
+    const int t1 = min(p.nq, t0 + p.Cq);
+    nt = max(t1 - t0, 0);
+    const int64_t ub = static_cast<int64_t>(unit) * p.capq + t0;
+    rk = make_rsrc(p.kq + ub * ROWB, static_cast<uint32_t>(nt) * ROWB);
+    rv = make_rsrc(p.vq + ub * ROWB, static_cast<uint32_t>(nt) * ROWB);
+    rks = make_rsrc(p.ksz + ub * 2, static_cast<uint32_t>(nt) * 8);
+    rvs = make_rsrc(p.vsz + ub * 2, static_cast<uint32_t>(nt) * 8);
+  }
+
+  auto load = [&](int grp, R_t& R) {
+    const uint32_t tb = static_cast<uint32_t>(grp * kTileG);
+    const uint32_t tk = tb + ai;
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const uint32_t ch0 = gi * G + 8 * CPG * ar;
+      tile_load<R_t::KB>(rk, tk * ROWB + (F16T ? 2 * ch0 : ch0 * BITS / 8), R.k[gi]);
+    }
+    if constexpr (!F16T) {
+      const Words<2> ks = bload<2>(rks, tk * 8), vz = bload<2>(rvs, tk * 8);
+      R.ksz[0] = ks.w[0]; R.ksz[1] = ks.w[1];
+      R.vsz[0] = vz.w[0]; R.vsz[1] = vz.w[1];
+    }
+#pragma unroll
+    for (int k = 0; k < VTPL; ++k) {
+      const uint32_t tv = tb + vs + k * VSLOTS;
+      tile_load<R_t::VB>(rv, tv * ROWB + vj * R_t::VB, R.v[k]);
+    }
+  };
+  // register sets in a ring: NS - 1 groups' loads in flight while one group
+  // is computed (two sets; three or four on the low-bit tier measured no
+  // faster: the loop is bound by VALU issue, not by loads in flight)
+  constexpr int NS = F16T ? 2 : MIKV_TILE_NS;
+  R_t R[NS];
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) load(wave + 4 * i, R[i]);
+
+  // ---- q-hat as MFMA A operands (hi and lo halves), per-group sums of q-hat
+  const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+  const int hrow = g * p.rep + tile * RT + ai;  // query head of this lane's row (ai < RT)
+  tile_h8 qa_hi[NCH], qa_lo[NCH];
+  float qs_part[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int base = tile_chan<D, BITS, true>(c, ar, 0);  // first channel of the run
+    float qv[8];
+    if (ai < RT) {
+      load8(p.q + (static_cast<int64_t>(n) * p.hq + hrow) * D + base, qv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[e] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ch = tile_chan<D, BITS, F16T>(c, ar, e);
+      const float q = qv[ch - base] * __builtin_amdgcn_rcpf(bvec[ch]) * qscale;
+      const _Float16 hi = static_cast<_Float16>(q);
+      qa_hi[c][e] = hi;
+      qa_lo[c][e] = static_cast<_Float16>(q - static_cast<float>(hi));
+      qs_part[c / CPG] += q;
+    }
+  }
+  // qs[h][gi] = sum over group gi's channels of head h's q-hat (wave-uniform)
+  float qs[RT][2];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    float t = qs_part[gi];
+    t += shfl_xor_f(t, 16);
+    t += shfl_xor_f(t, 32);
+#pragma unroll
+    for (int h = 0; h < RT; ++h)
+      qs[h][gi] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), h));
+  }
+
+  // ---- online-softmax state of the wave
+  float M[RT], l[RT], zz[RT][2], a[RT][8];
+#pragma unroll
+  for (int h = 0; h < RT; ++h) {
+    M[h] = -INFINITY;
+    l[h] = 0.0f;
+    zz[h][0] = zz[h][1] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[h][e] = 0.0f;
+  }
+
+  // ---- the new token: appended by the tile-0 block that owns the free
+  // slot, and seeded into wave 0's state (max = its score, sum = 1, o = v)
+  if constexpr (F16T) {
+    if (frel >= 0 && frel < nt && wave == 0) {  // uniform
+      float x[RT];
+#pragma unroll
+      for (int h = 0; h < RT; ++h) x[h] = 0.0f;
+      if (lane < LPTV) {
+        const int c0 = 8 * lane;
+        const int64_t nb = static_cast<int64_t>(unit) * D + c0;
+        float kx[8];
+        load8(p.k_new + nb, kx);
+        uint32_t kw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = f2h(mul_rn(kx[2 * i], bvec[c0 + 2 * i]));
+          const uint32_t hi = f2h(mul_rn(kx[2 * i + 1], bvec[c0 + 2 * i + 1]));
+          kw[i] = lo | (hi << 16);
+        }
+        const uint4 vn = *reinterpret_cast<const uint4*>(p.v_new + nb);
+        if (tile == 0) {
+          *reinterpret_cast<uint4*>(p.k16 + (rb16 + p.free16[unit]) * D + c0) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+          *reinterpret_cast<uint4*>(p.v16 + (rb16 + p.free16[unit]) * D + c0) = vn;
+          if (lane == 0) p.pos16[rb16 + p.free16[unit]] = p.len - 1;
+        }
+        const uint32_t vw[4] = {vn.x, vn.y, vn.z, vn.w};
+#pragma unroll
+        for (int h = 0; h < RT; ++h) {
+          float qv[8];
+          load8(p.q + (static_cast<int64_t>(n) * p.hq + g * p.rep + tile * RT + h) * D + c0, qv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[h] += qv[2 * i] * __builtin_amdgcn_rcpf(bvec[c0 + 2 * i]) * qscale * lo_h(kw[i]);
+            x[h] += qv[2 * i + 1] * __builtin_amdgcn_rcpf(bvec[c0 + 2 * i + 1]) * qscale * hi_h(kw[i]);
+            a[h][2 * i] = lo_h(vw[i]);
+            a[h][2 * i + 1] = hi_h(vw[i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < RT; ++h) {
+        x[h] = group_sum<LPTV>(x[h]);
+        M[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x[h]), 0));
+        if (lane == 0) {
+          l[h] = 1.0f;
+          p.sc16[scb + static_cast<int64_t>(h) * p.cap16 + frel] = M[h];
+        }
+      }
+    }
+  }
+
+  const uint32_t magic = opaque(0x64646464u);
+  auto step = [&](const R_t& R, int grp) {
+    // scores on the matrix cores: one accumulator per group of d/2 channels
+    tile_f4 acc[2];
+    acc[0] = tile_f4{0.0f, 0.0f, 0.0f, 0.0f};
+    acc[1] = acc[0];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int gi = c / CPG, part = c % CPG;
+      tile_h8 bop;
+      if constexpr (F16T) {
+        tile_u4 u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = R.k[gi][4 * part + i];
+        bop = __builtin_bit_cast(tile_h8, u);
+      } else if constexpr (BITS == 4) {
+        bop = tile_codes<4>(R.k[gi][part], magic);
+      } else {
+        bop = tile_codes<2>(part ? (R.k[gi][0] >> 16) : R.k[gi][0], magic);
+      }
+      acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[c], bop, acc[gi], 0, 0, 0);
+      acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[c], bop, acc[gi], 0, 0, 0);
+    }
+    const int tok = grp * kTileG + ai;
+    bool valid = lane < kTileG && tok < nt;
+    if constexpr (F16T) valid = valid && tok != frel;
+    float x[RT];
+#pragma unroll
+    for (int h = 0; h < RT; ++h) {
+      float xv;
+      if constexpr (F16T) {
+        xv = acc[0][h] + acc[1][h];
+      } else {
+        xv = lo_h(R.ksz[0]) * acc[0][h] + lo_h(R.ksz[1]) * acc[1][h];
+        xv += hi_h(R.ksz[0]) * qs[h][0] + hi_h(R.ksz[1]) * qs[h][1];
+      }
+      x[h] = valid ? xv : -INFINITY;
+      if constexpr (F16T) {
+        if (valid) p.sc16[scb + static_cast<int64_t>(h) * p.cap16 + tok] = xv;
+      }
+    }
+    // lazy running maximum: moves only when a score exceeds it by more than
+    // the headroom (also on the first scores of the wave)
+    bool need = false;
+#pragma unroll
+    for (int h = 0; h < RT; ++h) need |= x[h] > M[h] + kTileHeadroom;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int h = 0; h < RT; ++h) {
+        const float mn = fmaxf(M[h], wave_max(x[h]));
+        if (mn > M[h]) {
+          const float f = fast_exp2(M[h] - mn);  // 0 when M was -inf
+          l[h] *= f;
+          zz[h][0] *= f;
+          zz[h][1] *= f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[h][e] *= f;
+          M[h] = mn;
+        }
+      }
+    }
+    // probabilities and the weights of the value sums
+    float w[2][RT];
+#pragma unroll
+    for (int h = 0; h < RT; ++h) {
+      const float pr = fast_exp2(x[h] - fmaxf(M[h], -FLT_MAX));
+      l[h] += pr;
+      if constexpr (F16T) {
+        w[0][h] = pr;
+        w[1][h] = pr;
+      } else {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          const float s = lo_h(R.vsz[gi]), z = hi_h(R.vsz[gi]);
+          w[gi][h] = pr * s;
+          // value codes enter as fp16 1024 + code: take 1024 * w back out here
+          zz[h][gi] += pr * z - 1024.0f * w[gi][h];
+        }
+      }
+    }
+    if (lane < kTileG) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int h = 0; h < RT; ++h) wbuf[wave][lane][gi][h] = w[gi][h];
+    }
+    __builtin_amdgcn_wave_barrier();
+    // value sums: 8 channels per lane, VTPL tokens
+#pragma unroll
+    for (int k = 0; k < VTPL; ++k) {
+      const int tl = vs + k * VSLOTS;
+      float wv[RT];
+#pragma unroll
+      for (int h = 0; h < RT; ++h) wv[h] = wbuf[wave][tl][vg][h];
+      if constexpr (F16T) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = lo_h(R.v[k][i]), hi = hi_h(R.v[k][i]);
+#pragma unroll
+          for (int h = 0; h < RT; ++h) {
+            a[h][2 * i] += wv[h] * lo;
+            a[h][2 * i + 1] += wv[h] * hi;
+          }
+        }
+      } else if constexpr (BITS == 4) {
+        const MagicPairs<4> mp(R.v[k][0], magic);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const float lo = lo_h(mp.h[kk]), hi = hi_h(mp.h[kk]);
+#pragma unroll
+          for (int h = 0; h < RT; ++h) {
+            a[h][MagicPairs<4>::chan(kk, 0)] += wv[h] * lo;
+            a[h][MagicPairs<4>::chan(kk, 1)] += wv[h] * hi;
+          }
+        }
+      } else {
+        const uint32_t cw = R.v[k][0];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t pr2 = __builtin_amdgcn_perm(magic, (cw >> (2 * m)) & 0x0303u, 0x04010400u);
+          const float lo = lo_h(pr2), hi = hi_h(pr2);  // channels m and 4 + m
+#pragma unroll
+          for (int h = 0; h < RT; ++h) {
+            a[h][m] += wv[h] * lo;
+            a[h][4 + m] += wv[h] * hi;
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  for (int grp = wave; grp * kTileG < nt || grp == wave;) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      load(grp + 4 * (NS - 1), R[(i + NS - 1) % NS]);
+      step(R[i], grp);
+      grp += 4;
+      if (grp * kTileG >= nt) break;
+    }
+  }
+
+  // ---- wave partials: sums over the score lanes, value slices over slots
+#pragma unroll
+  for (int h = 0; h < RT; ++h) {
+    l[h] = wave_sum(l[h]);
+    zz[h][0] = wave_sum(zz[h][0]);
+    zz[h][1] = wave_sum(zz[h][1]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[h][e] = sum_over_stride<LPTV>(a[h][e]);
+  }
+  if (lane < LPTV) {
+#pragma unroll
+    for (int h = 0; h < RT; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        red[(wave * RT + h) * D + 8 * lane + e] = a[h][e] + (F16T ? 0.0f : zz[h][vg]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < RT; ++h) {
+      sm[wave][h] = M[h];
+      red[4 * RT * D + wave * RT + h] = l[h];
+    }
+  }
+  __syncthreads();
+  // ---- block partial: the four waves rebased to their common maximum
+  for (int i = tid; i < RT * D; i += kThreads) {
+    const int h = i / D, c = i % D;
+    const float mx = fmaxf(fmaxf(sm[0][h], sm[1][h]), fmaxf(sm[2][h], sm[3][h]));
+    float o = 0.0f;
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+      const float f = (sm[w4][h] == -INFINITY) ? 0.0f : fast_exp2(sm[w4][h] - mx);
+      o += f * red[(w4 * RT + h) * D + c];
+    }
+    po[i] = o;
+  }
+  if (tid < RT) {
+    const int h = tid;
+    const float mx = fmaxf(fmaxf(sm[0][h], sm[1][h]), fmaxf(sm[2][h], sm[3][h]));
+    float L = 0.0f;
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4)
+      L += (sm[w4][h] == -INFINITY) ? 0.0f : fast_exp2(sm[w4][h] - mx) * red[4 * RT * D + w4 * RT + h];
+    pml[h] = make_float2(mx, L);
+  }
+}
+
+
+template <int D, int BITS, int RT>
+__global__ __launch_bounds__(kThreads, 3) void decode_tile_kernel(const DecodeK p) {
+  // block order as decode_split_kernel (split-major)
+  const int S = p.S16 + p.Sq;
+  const int ut = p.units * p.tiles;
+  const int sd = blockIdx.x / ut;
+  const int split = p.f16_first ? sd : ((sd < p.Sq) ? p.S16 + sd : sd - p.Sq);
+  const int rest = blockIdx.x % ut;
+  const int tile = rest % p.tiles;
+  const int unit = rest / p.tiles;
+  const int n = unit / p.hkv;
+  const int g = unit % p.hkv;
+  const float* bvec = p.b + static_cast<int64_t>(unit) * D;
+  const int part = (unit * p.tiles + tile) * S + split;
+  float* po = p.part_o + static_cast<int64_t>(part) * RT * D;
+  float2* pml = p.part_ml + static_cast<int64_t>(part) * RT;
+
+  __shared__ float red[4 * RT * D + 4 * RT];
+  __shared__ float sm_max[4][RT];
+  __shared__ float wbuf[4][kTileG][2][RT];
+
+  if (split < p.S16) {
+    tile_split<D, BITS, RT, true>(p, unit, n, g, tile, split, bvec, red, sm_max, po, pml, wbuf);
+  } else {
+    tile_split<D, BITS, RT, false>(p, unit, n, g, tile, split, bvec, red, sm_max, po, pml, wbuf);
+  }
+}

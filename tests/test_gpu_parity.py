@@ -323,7 +323,7 @@ def test_decode_lockstep(name, over, balanced, steps):
     ("llama3_8b_32k", dict(T=6000), 4),
     # 43 x 8 units of 4 heads: 4 output groups per merge block and no room for
     # a separate H2O block (output block 0 runs it), <128, 4, 8, true, 4>
-    ("gqa_throughput", dict(batch=43, T=300), 4),
+    ("gqa_throughput", dict(batch=43, T=400), 4),
     ("llama2_7b_layer", dict(T=700), 3),
 ])
 def test_decode_lockstep_fused(name, over, steps):
