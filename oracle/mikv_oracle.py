@@ -36,7 +36,12 @@ design notes of the repository):
   * the recent window is the R newest positions, the new token included;
   * tokens in the low-bit tier are never promoted back;
   * CriticalKV: b1 = floor(alpha*budget), b2 = budget-b1, stage-2 score
-    A_i * ||V_i W_O,h||_1 with W_O laid out [H*d, hidden].
+    A_i * ||V_i W_O,h||_1 with W_O laid out [H*d, hidden];
+  * reduced-precision importance tier (imp_bits 8 or 4): the same
+    per-token group quantizer; a new token is quantized as it is appended
+    and attended to through its codes; a token leaving the tier is
+    re-quantized for the retained tier from its codes rebuilt as an fp16
+    row (fp32 product, fp32 sum rounded to nearest even, then fp16).
 
 Parity unpinned (conventions of this repository, not fixed by the pages):
   the bit layout of packed codes, the rounding of the budget split, and the
@@ -49,7 +54,7 @@ import numpy as np
 
 __all__ = [
     "balance", "balance_keys", "quantize_rows", "pack_codes", "unpack_codes",
-    "dequantize_rows", "top_by_key", "prefill_build", "decode_attention",
+    "dequantize_rows", "dequantize_rows_f16", "top_by_key", "prefill_build", "decode_attention",
     "h2o_accumulate", "select_drop", "demote", "decode_step",
     "projected_value_l1", "criticalkv_select", "empty_state", "prefill_scores",
 ]
@@ -137,6 +142,10 @@ def quantize_rows(x: np.ndarray, group: int, bits: int):
     Key contributions 2), additional notes, and [paperlayer] section 3.2: the
     group size is half of the head dimension, to soften RoPE artifacts.
 
+    The same quantizer serves the retained tier (2 or 4 bits) and a
+    reduced-precision importance tier (8 or 4 bits, [velog notes] Key
+    contributions 3); [paperlayer] section 3.3).
+
     Per row and group of `group` contiguous channels:
       mn, mx = min, max (exact in fp16)
       s = fp16( (f32(mx) - f32(mn)) / (2^bits - 1) ),  z = mn
@@ -145,7 +154,7 @@ def quantize_rows(x: np.ndarray, group: int, bits: int):
     x: [rows, d] fp16. Returns packed codes [rows, d*bits/8] uint8 and
     sz [rows, d/group, 2] fp16 holding (scale, zero) per group.
     """
-    assert bits in (2, 4)
+    assert bits in (2, 4, 8)
     rows, d = x.shape
     assert d % group == 0 and group % (8 // bits) == 0
     qmax = F32((1 << bits) - 1)
@@ -179,6 +188,22 @@ def dequantize_rows(packed: np.ndarray, sz: np.ndarray, group: int, bits: int) -
     return (c * s + z).reshape(rows, d)
 
 
+def dequantize_rows_f16(packed: np.ndarray, sz: np.ndarray, group: int, bits: int) -> np.ndarray:
+    """fp16 rows of codes: fp16(fl32(fl32(code * scale) + zero)).
+
+    A reduced-precision importance tier keeps only codes, so a token that
+    leaves it is re-quantized for the retained tier from this fp16 row (the
+    fp16 original no longer exists). Reading of this repository: the row is
+    rebuilt in fp32 (the product is exact, the sum rounded to nearest even)
+    and rounded to fp16, the precision the quantizer takes in."""
+    rows = packed.shape[0]
+    d = packed.shape[1] * 8 // bits
+    c = unpack_codes(packed, d, bits).astype(F32).reshape(rows, d // group, group)
+    s = sz[:, :, 0].astype(F32)[:, :, None]
+    z = sz[:, :, 1].astype(F32)[:, :, None]
+    return ((c * s).astype(F32) + z).astype(F32).astype(F16).reshape(rows, d)
+
+
 # --------------------------------------------------------------------------
 # Importance ranking (H2O heavy hitters)
 # --------------------------------------------------------------------------
@@ -194,11 +219,15 @@ def top_by_key(score: np.ndarray, pos: np.ndarray, m: int) -> np.ndarray:
     return order[:m]
 
 
-def empty_state(batch, hkv, d, cap16, capq, group, bits):
-    """Zeroed cache in the layout of the C interface (see include/mikv.h)."""
+def empty_state(batch, hkv, d, cap16, capq, group, bits, imp_bits=16):
+    """Zeroed cache in the layout of the C interface (see include/mikv.h).
+
+    imp_bits = 16: the importance tier holds fp16 rows (k16, v16). imp_bits
+    in (8, 4): it holds codes and (scale, zero) like the retained tier
+    (kimp, vimp, kimpsz, vimpsz), the reduced-precision importance cache of
+    [velog notes] Key contributions 3) and [paperlayer] section 3.3."""
     cb = d * bits // 8
-    return dict(
-        k16=np.zeros((batch, hkv, cap16, d), F16), v16=np.zeros((batch, hkv, cap16, d), F16),
+    st = dict(
         pos16=np.full((batch, hkv, cap16), -1, np.int32),
         acc16=np.zeros((batch, hkv, cap16), F32),
         free16=np.zeros((batch, hkv), np.int32),
@@ -206,11 +235,68 @@ def empty_state(batch, hkv, d, cap16, capq, group, bits):
         ksz=np.zeros((batch, hkv, capq, d // group, 2), F16),
         vsz=np.zeros((batch, hkv, capq, d // group, 2), F16),
         posq=np.full((batch, hkv, capq), -1, np.int32),
-        group=group, bits=bits,
+        group=group, bits=bits, imp_bits=imp_bits,
     )
+    if imp_bits == 16:
+        st["k16"] = np.zeros((batch, hkv, cap16, d), F16)
+        st["v16"] = np.zeros((batch, hkv, cap16, d), F16)
+    else:
+        assert imp_bits in (4, 8)
+        ci = d * imp_bits // 8
+        st["kimp"] = np.zeros((batch, hkv, cap16, ci), np.uint8)
+        st["vimp"] = np.zeros((batch, hkv, cap16, ci), np.uint8)
+        st["kimpsz"] = np.zeros((batch, hkv, cap16, d // group, 2), F16)
+        st["vimpsz"] = np.zeros((batch, hkv, cap16, d // group, 2), F16)
+    return st
 
 
-def prefill_build(kb, v, acc0, B, R, group, bits, capq):
+def _shape(st):
+    n, hkv, cap16 = st["pos16"].shape
+    return n, hkv, cap16, st["kq"].shape[-1] * 8 // st["bits"]
+
+
+def _imp_bits(st):
+    return st.get("imp_bits", 16)
+
+
+def _imp_kv(st, i, g):
+    """Keys and values of the importance tier of unit (i, g), float64."""
+    ib = _imp_bits(st)
+    if ib == 16:
+        return st["k16"][i, g].astype(F64), st["v16"][i, g].astype(F64)
+    grp = st["group"]
+    return (dequantize_rows(st["kimp"][i, g], st["kimpsz"][i, g], grp, ib),
+            dequantize_rows(st["vimp"][i, g], st["vimpsz"][i, g], grp, ib))
+
+
+def _imp_put(st, i, g, slots, krows, vrows):
+    """Store fp16 rows [m, d] into importance-tier slots (quantized when the
+    tier is reduced-precision)."""
+    ib = _imp_bits(st)
+    if ib == 16:
+        st["k16"][i, g, slots] = krows
+        st["v16"][i, g, slots] = vrows
+        return
+    grp = st["group"]
+    ck, sk = quantize_rows(krows, grp, ib)
+    cv, sv = quantize_rows(vrows, grp, ib)
+    st["kimp"][i, g, slots], st["kimpsz"][i, g, slots] = ck, sk
+    st["vimp"][i, g, slots], st["vimpsz"][i, g, slots] = cv, sv
+
+
+def _imp_rows16(st, i, g, s):
+    """fp16 key and value rows of importance slot s: the stored rows, or the
+    codes rebuilt as fp16 (dequantize_rows_f16) for a reduced-precision
+    tier."""
+    ib = _imp_bits(st)
+    if ib == 16:
+        return st["k16"][i, g, s:s + 1], st["v16"][i, g, s:s + 1]
+    grp = st["group"]
+    return (dequantize_rows_f16(st["kimp"][i, g, s:s + 1], st["kimpsz"][i, g, s:s + 1], grp, ib),
+            dequantize_rows_f16(st["vimp"][i, g, s:s + 1], st["vimpsz"][i, g, s:s + 1], grp, ib))
+
+
+def prefill_build(kb, v, acc0, B, R, group, bits, capq, imp_bits=16):
     """Initial two-tier cache after the prompt.
 
     [velog notes] one-line summary and Key contributions 1): tokens an
@@ -224,11 +310,12 @@ def prefill_build(kb, v, acc0, B, R, group, bits, capq):
     ([velog notes] section 3.4).
 
     kb, v: [n, hkv, T, d] fp16 (balanced keys, values); acc0 [n, hkv, T] fp32.
+    imp_bits < 16: the important rows are stored as imp_bits codes.
     """
     n, hkv, T, d = kb.shape
     H = B - R
     assert 0 <= R <= B <= T and T - B <= capq
-    st = empty_state(n, hkv, d, B + 1, capq, group, bits)
+    st = empty_state(n, hkv, d, B + 1, capq, group, bits, imp_bits)
     pos_all = np.arange(T, dtype=np.int64)
     for i in range(n):
         for g in range(hkv):
@@ -239,8 +326,7 @@ def prefill_build(kb, v, acc0, B, R, group, bits, capq):
             keep[T - R:] = True
             kp = pos_all[keep]
             rp = pos_all[~keep]
-            st["k16"][i, g, :B] = kb[i, g, kp]
-            st["v16"][i, g, :B] = v[i, g, kp]
+            _imp_put(st, i, g, slice(0, B), kb[i, g, kp], v[i, g, kp])
             st["pos16"][i, g, :B] = kp
             st["acc16"][i, g, :B] = acc0[i, g, kp]
             st["free16"][i, g] = B
@@ -263,7 +349,9 @@ def decode_attention(state, N, q, k_new, v_new, b):
     is a batch matrix-vector product; keys and values are stored at reduced
     precision while the query and the attention map stay floating point.
     [velog notes] Key contributions 2): the query is divided by b (q-hat) and
-    the key was multiplied by b, so q-hat . k-hat reproduces q . k.
+    the key was multiplied by b, so q-hat . k-hat reproduces q . k. With a
+    reduced-precision importance tier the new token is stored as codes and
+    attended to through them, like every other importance-tier token.
     Scores use scale 1/sqrt(d); the new token attends to every cached token
     and to itself.
 
@@ -276,7 +364,7 @@ def decode_attention(state, N, q, k_new, v_new, b):
     """
     st = {kk: (vv.copy() if isinstance(vv, np.ndarray) else vv) for kk, vv in state.items()}
     group, bits = st["group"], st["bits"]
-    n, hkv, cap16, d = st["k16"].shape
+    n, hkv, cap16, d = _shape(st)
     hq = q.shape[1]
     rep = hq // hkv
     nq = N - cap16
@@ -287,14 +375,13 @@ def decode_attention(state, N, q, k_new, v_new, b):
     for i in range(n):
         for g in range(hkv):
             s = int(st["free16"][i, g])
-            st["k16"][i, g, s] = balance_keys(k_new[i, g], b[i, g])
-            st["v16"][i, g, s] = v_new[i, g]
+            _imp_put(st, i, g, slice(s, s + 1), balance_keys(k_new[i, g], b[i, g])[None],
+                     v_new[i, g][None])
             st["pos16"][i, g, s] = N - 1
             st["acc16"][i, g, s] = 0.0
-            K = np.concatenate([st["k16"][i, g].astype(F64),
-                                dequantize_rows(st["kq"][i, g, :nq], st["ksz"][i, g, :nq], group, bits)])
-            V = np.concatenate([st["v16"][i, g].astype(F64),
-                                dequantize_rows(st["vq"][i, g, :nq], st["vsz"][i, g, :nq], group, bits)])
+            Ki, Vi = _imp_kv(st, i, g)
+            K = np.concatenate([Ki, dequantize_rows(st["kq"][i, g, :nq], st["ksz"][i, g, :nq], group, bits)])
+            V = np.concatenate([Vi, dequantize_rows(st["vq"][i, g, :nq], st["vsz"][i, g, :nq], group, bits)])
             for r in range(rep):
                 h = g * rep + r
                 qh = q[i, h].astype(F64) / b[i, g].astype(F64)
@@ -363,20 +450,23 @@ def select_drop(acc, pos16, N, R, H):
 
 
 def demote(state, N, drop):
-    """Quantize each dropped FP16-tier token into low-bit slot N - cap16.
+    """Quantize each dropped importance-tier token into low-bit slot N - cap16.
 
     [velog notes] Key contributions 1): tokens leaving the important set are
-    kept as low-bit codes instead of being discarded.
+    kept as low-bit codes instead of being discarded. From a reduced-precision
+    importance tier the row re-quantized is its codes rebuilt in fp16
+    (dequantize_rows_f16).
     """
     st = {kk: (vv.copy() if isinstance(vv, np.ndarray) else vv) for kk, vv in state.items()}
     group, bits = st["group"], st["bits"]
-    n, hkv, cap16, d = st["k16"].shape
+    n, hkv, cap16, d = _shape(st)
     slot = N - cap16
     for i in range(n):
         for g in range(hkv):
             s = int(drop[i, g])
-            ck, sk = quantize_rows(st["k16"][i, g, s:s + 1], group, bits)
-            cv, sv = quantize_rows(st["v16"][i, g, s:s + 1], group, bits)
+            krow, vrow = _imp_rows16(st, i, g, s)
+            ck, sk = quantize_rows(krow, group, bits)
+            cv, sv = quantize_rows(vrow, group, bits)
             st["kq"][i, g, slot], st["ksz"][i, g, slot] = ck[0], sk[0]
             st["vq"][i, g, slot], st["vsz"][i, g, slot] = cv[0], sv[0]
             st["posq"][i, g, slot] = st["pos16"][i, g, s]

@@ -123,7 +123,7 @@ def test_quantizer_hand_vectors(case):
     assert O.unpack_codes(packed, d, case["bits"])[0].tolist() == case["codes"]
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [8, 4, 2])
 @pytest.mark.parametrize("group", [32, 64])
 def test_quantizer_roundtrip_bound(bits, group):
     """|x - dequant(quant(x))| <= scale/2 for every element (round to nearest
@@ -141,7 +141,14 @@ def test_quantizer_roundtrip_bound(bits, group):
     s = np.repeat(sz[:, :, 0].astype(F64), group, axis=1)
     err = np.abs(xr - x.astype(F64))
     slack = 1e-6 * (np.abs(x.astype(F64)) + s)
-    assert np.all(err <= 0.5 * s + slack)
+    # the stored scale is the fp16 rounding of range/qmax: when it rounds
+    # down, the group maximum lies up to qmax * (range/qmax - s) above the
+    # top code and is clamped there (noticeable at 8 bits and subnormal scales)
+    qmax = (1 << bits) - 1
+    xs64 = x.astype(F64).reshape(rows, d // group, group)
+    s_true = (xs64.max(axis=2) - xs64.min(axis=2)) / qmax
+    over = np.repeat(np.maximum(0.0, s_true - sz[:, :, 0].astype(F64)) * qmax, group, axis=1)
+    assert np.all(err <= 0.5 * s + over + slack)
     codes = O.unpack_codes(packed, d, bits)
     assert codes.min() >= 0 and codes.max() <= (1 << bits) - 1
     xs = x.reshape(rows, d // group, group)
@@ -151,7 +158,7 @@ def test_quantizer_roundtrip_bound(bits, group):
     assert np.array_equal(xr[5], np.full(d, 0.75))
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [8, 4, 2])
 def test_pack_unpack_roundtrip(bits):
     rng = np.random.default_rng(9)
     c = rng.integers(0, 1 << bits, (13, 128))
@@ -591,3 +598,97 @@ def test_new_token_score_is_its_own_probability():
         assert st["pos16"][0, 0, fr] == N - 1
         P = _brute_probs(q_all, k_all, T, j)
         assert abs(F64(st["acc16"][0, 0, fr]) - P[N - 1]) <= 1e-6 * P[N - 1]
+
+
+# ---------------------------------------------------------------- reduced-precision importance tier
+def _grid_rows(rng, rows, d, G, bits):
+    """Rows whose every group of G channels is z + s*c with integer c in
+    [0, 2^bits - 1], c = 0 and c = 2^bits - 1 present, s a power of two and z
+    a multiple of s: quantizing them at `bits` is lossless (scale s, zero z,
+    codes c), and so is rebuilding them in fp16."""
+    qmax = (1 << bits) - 1
+    step = {8: 2.0 ** -4, 4: 0.25, 2: 1.0}[bits]
+    c = rng.integers(0, qmax + 1, (rows, d // G, G))
+    c[:, :, 0] = 0
+    c[:, :, 1] = qmax
+    for r in range(rows):
+        for j in range(d // G):
+            c[r, j] = c[r, j][rng.permutation(G)]
+    z = rng.integers(-32, 33, (rows, d // G, 1)) * step
+    return (z + step * c).reshape(rows, d).astype(F16)
+
+
+@pytest.mark.parametrize("imp_bits,bits", [(8, 2), (4, 2), (8, 4)])
+def test_importance_tier_on_lossless_rows_equals_fp16_tier(imp_bits, bits):
+    """Importance tier quantized at imp_bits ([velog notes] Key contributions
+    3), [paperlayer] section 3.3) on rows that imp_bits codes hold exactly:
+    every step (attention output, probabilities, accumulated scores,
+    selections, demoted codes) equals the fp16-tier oracle's, which the pins
+    above tie to the pages. Prompt and new tokens are all grid rows; b = 1."""
+    rng = np.random.default_rng(imp_bits * 10 + bits)
+    n, hkv, rep, d, G, T, B, R, steps = 2, 2, 2, 16, 8, 30, 9, 3, 6
+    ntok = T + steps
+    k = np.stack([np.stack([_grid_rows(rng, ntok, d, G, imp_bits) for _ in range(hkv)]) for _ in range(n)])
+    v = np.stack([np.stack([_grid_rows(rng, ntok, d, G, imp_bits) for _ in range(hkv)]) for _ in range(n)])
+    q = (rng.standard_normal((steps, n, hkv * rep, d)) * 0.3).astype(F16)
+    acc0 = (rng.integers(1, 6, (n, hkv, T)) * 0.125).astype(F32)
+    b = np.ones((n, hkv, d), F32)
+    capq = T - B + steps
+    ref = O.prefill_build(k[:, :, :T], v[:, :, :T], acc0, B, R, G, bits, capq)
+    imp = O.prefill_build(k[:, :, :T], v[:, :, :T], acc0, B, R, G, bits, capq, imp_bits=imp_bits)
+    for i in range(n):
+        for g in range(hkv):
+            ki = O.dequantize_rows(imp["kimp"][i, g], imp["kimpsz"][i, g], G, imp_bits)
+            assert np.array_equal(ki[:B], ref["k16"][i, g, :B].astype(F64))
+    for j in range(steps):
+        N = T + j + 1
+        kd, vd = k[:, :, N - 1], v[:, :, N - 1]
+        o1, p1, ref, d1 = O.decode_step(ref, N, q[j], kd, vd, b, R, B - R)
+        o2, p2, imp, d2 = O.decode_step(imp, N, q[j], kd, vd, b, R, B - R)
+        assert np.max(np.abs(o1 - o2)) <= 1e-12 * np.max(np.abs(o1))
+        assert np.max(np.abs(p1 - p2)) <= 1e-12
+        assert np.array_equal(d1, d2)
+        for key in ("acc16", "pos16", "free16", "posq", "kq", "vq", "ksz", "vsz"):
+            assert np.array_equal(np.asarray(ref[key]).view(np.uint8), np.asarray(imp[key]).view(np.uint8)), key
+
+
+def test_importance_tier_new_token_and_demotion_bounds():
+    """Random rows: a token in an 8-bit importance tier is held within
+    scale/2 of its fp16 row, and once demoted its 2-bit codes hold it within
+    the retained scale/2 plus that first error (plus one fp16 rounding):
+    the demotion re-quantizes the same token's importance row, key and value
+    each from their own row."""
+    cfg = S.CONFIGS["tiny"].scaled(hq=2, hkv=1, T=64, pct=25, recent=4, bits=2)
+    q, k, v, acc0 = S.prefill_tensors(cfg, 9)
+    b, kb = O.balance(q, k)
+    st = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, 2, cfg.capq(), imp_bits=8)
+    G = cfg.G
+    for step in range(6):
+        N = cfg.T + step + 1
+        qd, kd, vd = S.decode_tensors(cfg, 9, step)
+        fr = int(st["free16"][0, 0])
+        _, _, st, drop = O.decode_step(st, N, qd, kd, vd, b, cfg.recent, cfg.H)
+        # the new token, quantized on arrival into the freed slot
+        krow = (kd[0, 0].astype(F32) * b[0, 0]).astype(F16).astype(F64)
+        ki = O.dequantize_rows(st["kimp"][0, 0, fr:fr + 1], st["kimpsz"][0, 0, fr:fr + 1], G, 8)[0]
+        ks = np.repeat(st["kimpsz"][0, 0, fr, :, 0].astype(F64), G)
+        assert np.all(np.abs(ki - krow) <= 0.5 * ks * (1 + 1e-6))
+        vi = O.dequantize_rows(st["vimp"][0, 0, fr:fr + 1], st["vimpsz"][0, 0, fr:fr + 1], G, 8)[0]
+        vsc = np.repeat(st["vimpsz"][0, 0, fr, :, 0].astype(F64), G)
+        assert np.all(np.abs(vi - vd[0, 0].astype(F64)) <= 0.5 * vsc * (1 + 1e-6))
+        # the demoted token: retained 2-bit codes around its importance row
+        slot = N - cfg.cap16
+        pos = int(st["posq"][0, 0, slot])
+        src = kb if pos < cfg.T else None
+        for name, arr in (("k", "kq"), ("v", "vq")):
+            r = O.dequantize_rows(st[arr][0, 0, slot:slot + 1], st[arr[0] + "sz"][0, 0, slot:slot + 1], G, 2)[0]
+            rs = np.repeat(st[arr[0] + "sz"][0, 0, slot, :, 0].astype(F64), G)
+            if pos < cfg.T:
+                orig = (kb if name == "k" else v)[0, 0, pos].astype(F64)
+            else:
+                kd2, vd2 = S.decode_tensors(cfg, 9, pos - cfg.T)[1:]
+                orig = ((kd2[0, 0].astype(F32) * b[0, 0]).astype(F16) if name == "k" else vd2[0, 0]).astype(F64)
+            # importance-tier error (8-bit scale over the group's range) + 2-bit
+            # rounding + one fp16 rounding of the rebuilt row
+            span = np.repeat((rs * 3.0).reshape(-1, 1), 1, axis=0)
+            assert np.all(np.abs(r - orig) <= 0.5 * rs + span / 255.0 + 1e-3 * np.abs(orig) + 1e-6), (step, name)
