@@ -87,14 +87,22 @@ def recorded_traffic(workload, key="split_traffic_bytes_per_launch"):
     return None if w is None or key not in w else float(w[key])
 
 
+def imp_row_bytes(cfg):
+    """Bytes of one importance-tier token, key and value: fp16 rows, or
+    codes plus an fp16 (scale, zero) per group for a reduced-precision tier."""
+    if cfg.imp_bits == 16:
+        return 4 * cfg.d
+    return 2 * (cfg.d * cfg.imp_bits // 8 + 4 * (cfg.d // cfg.G))
+
+
 def attn_bytes(cfg, N):
     """Algorithmic bytes of one decode-attention launch at length N (new
-    token included): FP16 tier rows read (cap16-1) plus the new row read and
-    appended, low-bit rows (codes + fp16 scale/zero per group, K and V), q, b,
-    o and p16."""
+    token included): importance-tier rows read (cap16-1), the new token read
+    (k_new, v_new) and appended, low-bit rows (codes + fp16 scale/zero per
+    group, K and V), q, b, o and p16."""
     d, G = cfg.d, cfg.G
     nq = N - cfg.cap16
-    per_unit = ((cfg.cap16 - 1) * 4 * d + 4 * d + 4 * d
+    per_unit = ((cfg.cap16 - 1) * imp_row_bytes(cfg) + 4 * d + imp_row_bytes(cfg)
                 + nq * 2 * (d * cfg.bits // 8 + 4 * (d // G))
                 + cfg.rep * d * 2 + d * 4 + cfg.rep * d * 4 + cfg.cap16 * 4)
     return per_unit * cfg.batch * cfg.hkv
@@ -107,10 +115,10 @@ def split_bytes(cfg, N):
 
 
 def h2o_bytes(cfg):
-    """acc16 read+write, p16 and pos16 read per FP16 slot; the demoted K/V
-    rows read and written as codes."""
+    """acc16 read+write, p16 and pos16 read per importance slot; the demoted
+    K/V rows read and written as codes."""
     d = cfg.d
-    per_unit = cfg.cap16 * 16 + 4 * d + 2 * (d * cfg.bits // 8 + 4 * (d // cfg.G)) + 16
+    per_unit = cfg.cap16 * 16 + imp_row_bytes(cfg) + 2 * (d * cfg.bits // 8 + 4 * (d // cfg.G)) + 16
     return per_unit * cfg.batch * cfg.hkv
 
 
@@ -420,7 +428,7 @@ def decode_run(cfg, args, log, K, W, KA, cpu_seconds):
     t0 = time.perf_counter()
     q, k, v, acc0 = S.prefill_tensors(cfg, args.seed)
     dims = L.Dims(batch=cfg.batch, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, group=cfg.G, bits=cfg.bits,
-                  cap16=cfg.cap16, capq=cfg.T - cfg.B + total)
+                  cap16=cfg.cap16, capq=cfg.T - cfg.B + total, imp_bits=cfg.imp_bits)
     cache = L.Cache(dims)
     b = torch.empty((cfg.batch, cfg.hkv, cfg.d), dtype=torch.float32, device="cuda")
     qg, kg = dev(q), dev(k)
@@ -519,11 +527,11 @@ def decode_run(cfg, args, log, K, W, KA, cpu_seconds):
     if cpu_seconds > 0:
         # one more decode step, untimed: the oracle replays it from the same
         # state (sequence 0) and compares
-        before = {kk: getattr(cache, kk)[:1].cpu().numpy() for kk in L.Cache.NAMES}
-        before["group"], before["bits"] = cfg.G, cfg.bits
+        before = {kk: getattr(cache, kk)[:1].cpu().numpy() for kk in cache.names}
+        before["group"], before["bits"], before["imp_bits"] = cfg.G, cfg.bits, cache.imp_bits
         N += 1
         step_call(s_next, N)
-        after = {kk: getattr(cache, kk)[:1].cpu().numpy() for kk in L.Cache.NAMES}
+        after = {kk: getattr(cache, kk)[:1].cpu().numpy() for kk in cache.names}
         gpu = {"o": o[:1].cpu().numpy(), "after": after}
         qn, kn, vn = (x[:1] for x in steps_np[s_next])
         cpu = cpu_baseline(cfg, before, b[:1].cpu().numpy(), N, qn, kn, vn, gpu, cpu_seconds)
@@ -537,6 +545,7 @@ def decode_run(cfg, args, log, K, W, KA, cpu_seconds):
         "ms_per_step_median": float(np.median(step_ms)), "steps": K, "warmup": W,
         "config": {"workload": cfg.name, "batch": cfg.batch, "q_heads": cfg.hq, "kv_heads": cfg.hkv,
                    "head_dim": cfg.d, "context": cfg.T, "low_bits": cfg.bits,
+                   "importance_bits": cfg.imp_bits,
                    "important_pct": cfg.pct, "recent": cfg.recent, "group": cfg.G,
                    "cache_flush_per_step": args.flush,
                    "step_launch": "hip_graph" if args.graph else "eager"},
@@ -621,7 +630,7 @@ def main():
     head = decode_run(cfg, args, log, K, W, KA, cpu_s)
     extra = []
     if not args.no_extra and not args.set:
-        for name in ("llama3_8b_32k", "gqa_throughput"):
+        for name in ("llama3_8b_32k", "gqa_throughput", "llama2_7b_imp4"):
             if name == cfg.name:
                 continue
             c2 = S.CONFIGS[name]

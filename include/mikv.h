@@ -27,7 +27,9 @@
  *     MIKV_ERR_HIP. Faults inside kernels surface at the caller's next
  *     synchronisation. No C++ exception crosses this interface.
  *   - Supported shapes: head dim d in {64, 128}; bits in {2, 4}; group in
- *     {d/2, d} (d/2 is the method's setting); hq a multiple of hkv.
+ *     {d/2, d} (d/2 is the method's setting); hq a multiple of hkv;
+ *     imp_bits in {16 (or 0), 8, 4}, 8 and 4 with group d/2 only
+ *     (MIKV_ERR_UNSUPPORTED otherwise).
  *   - Inputs must be finite; non-finite values give unspecified results.
  *
  * Two-tier cache (mikv_cache), per sequence n and kv head g:
@@ -42,6 +44,16 @@
  *     posq     [batch][hkv][capq]     int32  token position of the slot
  *   Code packing: code of channel (8/bits)*j + m sits in bits
  *   [bits*m, bits*m+bits) of byte j. Dequantized value = code*scale + zero.
+ * Reduced-precision importance tier ([velog notes] Key contributions 3);
+ * [paperlayer] section 3.3: the importance cache itself quantized, e.g.
+ * INT4 or INT8 over a 2-bit retention cache), selected by dims.imp_bits:
+ *   imp_bits 16 (or 0): the FP16 tier above (k16, v16).
+ *   imp_bits 8 or 4: k16 and v16 are unused (may be NULL) and the tier holds
+ *     kimp, vimp [batch][hkv][cap16][d*imp_bits/8] uint8 codes and
+ *     kimpsz, vimpsz [batch][hkv][cap16][d/group][2] fp16 (scale, zero),
+ *     packed like the low-bit tier; requires group == d/2. A new token is
+ *     quantized as it is appended; a demoted token is re-quantized to `bits`
+ *     from its codes rebuilt as the fp16 row fp16(code*scale + zero).
  *   Grouping pairs by precision is allowed because attention is invariant
  *   under jointly permuting KV pairs ([velog notes] section 3.4).
  *   With B = cap16 - 1 important tokens and a current length N (new token
@@ -58,7 +70,7 @@
 extern "C" {
 #endif
 
-#define MIKV_ABI_VERSION 2
+#define MIKV_ABI_VERSION 3
 
 typedef enum {
   MIKV_OK = 0,
@@ -87,6 +99,7 @@ typedef struct {
   int32_t bits;  /* low-bit code width, 4 or 2                             */
   int32_t cap16; /* FP16-tier slots per (n, g) = B + 1                     */
   int32_t capq;  /* low-bit-tier slots per (n, g)                          */
+  int32_t imp_bits; /* importance tier: 16 or 0 = fp16 rows; 8 or 4 = codes */
 } mikv_dims;
 
 typedef struct {
@@ -100,6 +113,10 @@ typedef struct {
   uint16_t* ksz;
   uint16_t* vsz;
   int32_t* posq;
+  uint8_t* kimp;    /* importance tier as codes (imp_bits 8 or 4), else NULL */
+  uint8_t* vimp;
+  uint16_t* kimpsz;
+  uint16_t* vimpsz;
 } mikv_cache;
 
 /*

@@ -22,12 +22,14 @@ _vp, _sz, _i32, _i64, _f64 = C.c_void_p, C.c_size_t, C.c_int32, C.c_int64, C.c_d
 
 
 class MikvDims(C.Structure):
-    _fields_ = [(n, _i32) for n in ("batch", "hq", "hkv", "d", "group", "bits", "cap16", "capq")]
+    _fields_ = [(n, _i32) for n in ("batch", "hq", "hkv", "d", "group", "bits", "cap16", "capq",
+                                     "imp_bits")]
 
 
 class MikvCache(C.Structure):
     _fields_ = [(n, _vp) for n in ("k16", "v16", "pos16", "acc16", "free16",
-                                   "kq", "vq", "ksz", "vsz", "posq")]
+                                   "kq", "vq", "ksz", "vsz", "posq",
+                                   "kimp", "vimp", "kimpsz", "vimpsz")]
 
 
 class MikvPrefillSrc(C.Structure):
@@ -102,6 +104,7 @@ class Dims:
     bits: int
     cap16: int
     capq: int
+    imp_bits: int = 16
 
     def c(self) -> MikvDims:
         key = tuple(int(getattr(self, f.name)) for f in dataclasses.fields(self))
@@ -215,14 +218,24 @@ def mikv_quantize_tokens(x, rows, codes, sz, group: int, bits: int, stream=None)
 
 
 class Cache:
-    """Device tensors of one two-tier cache (layout of include/mikv.h)."""
+    """Device tensors of one two-tier cache (layout of include/mikv.h). With
+    dims.imp_bits 8 or 4 the importance tier is kimp/vimp codes with
+    kimpsz/vimpsz (scale, zero), and k16/v16 are not allocated."""
 
     def __init__(self, dims: Dims, device="cuda"):
         import torch
         n, g, d, c16, cq = dims.batch, dims.hkv, dims.d, dims.cap16, dims.capq
         self.dims = dims
-        self.k16 = torch.zeros((n, g, c16, d), dtype=torch.float16, device=device)
-        self.v16 = torch.zeros_like(self.k16)
+        ib = dims.imp_bits or 16
+        self.imp_bits = ib
+        if ib == 16:
+            self.k16 = torch.zeros((n, g, c16, d), dtype=torch.float16, device=device)
+            self.v16 = torch.zeros_like(self.k16)
+        else:
+            self.kimp = torch.zeros((n, g, c16, d * ib // 8), dtype=torch.uint8, device=device)
+            self.vimp = torch.zeros_like(self.kimp)
+            self.kimpsz = torch.zeros((n, g, c16, d // dims.group, 2), dtype=torch.float16, device=device)
+            self.vimpsz = torch.zeros_like(self.kimpsz)
         self.pos16 = torch.full((n, g, c16), -1, dtype=torch.int32, device=device)
         self.acc16 = torch.zeros((n, g, c16), dtype=torch.float32, device=device)
         self.free16 = torch.zeros((n, g), dtype=torch.int32, device=device)
@@ -235,14 +248,21 @@ class Cache:
 
     def c(self) -> MikvCache:
         if getattr(self, "_c", None) is None:
-            self._c = MikvCache(*(getattr(self, f).data_ptr() for f, _ in MikvCache._fields_))
+            self._c = MikvCache(*(getattr(self, f).data_ptr() if hasattr(self, f) else None
+                                  for f, _ in MikvCache._fields_))
         return self._c
 
-    NAMES = ("k16", "v16", "pos16", "acc16", "free16", "kq", "vq", "ksz", "vsz", "posq")
+    COMMON = ("pos16", "acc16", "free16", "kq", "vq", "ksz", "vsz", "posq")
+    NAMES = ("k16", "v16") + COMMON
+    IMP_NAMES = ("kimp", "vimp", "kimpsz", "vimpsz") + COMMON
+
+    @property
+    def names(self):
+        return self.NAMES if self.imp_bits == 16 else self.IMP_NAMES
 
     def to_numpy(self) -> dict:
-        out = {k: getattr(self, k).cpu().numpy() for k in self.NAMES}
-        out["group"], out["bits"] = self.dims.group, self.dims.bits
+        out = {k: getattr(self, k).cpu().numpy() for k in self.names}
+        out["group"], out["bits"], out["imp_bits"] = self.dims.group, self.dims.bits, self.imp_bits
         return out
 
 

@@ -21,6 +21,9 @@ bool supported_dims(int d, int group, int bits) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Bits of the importance tier: 16 (fp16 rows; 0 means the same) or 8 / 4.
+int imp_of(const mikv_dims* m) { return m->imp_bits == 0 ? 16 : m->imp_bits; }
+
 mikv_status check_dims(const mikv_dims* m, bool need_tiers) {
   if (!m) return MIKV_ERR_NULL;
   if (m->batch < 1 || m->hq < 1 || m->hkv < 1 || m->d < 1) return MIKV_ERR_SHAPE;
@@ -31,22 +34,45 @@ mikv_status check_dims(const mikv_dims* m, bool need_tiers) {
     if (m->bits != 2 && m->bits != 4) return MIKV_ERR_UNSUPPORTED;
     if (!supported_dims(m->d, m->group, m->bits)) return MIKV_ERR_UNSUPPORTED;
     if (m->cap16 < 1 || m->capq < 0) return MIKV_ERR_SHAPE;
+    // a reduced-precision importance tier: 8- or 4-bit codes, groups of d/2
+    const int ib = imp_of(m);
+    if (ib != 16 && ib != 8 && ib != 4) return MIKV_ERR_UNSUPPORTED;
+    if (ib != 16 && m->group != m->d / 2) return MIKV_ERR_UNSUPPORTED;
     // the decode kernels address one (sequence, kv head) tier with 32-bit byte offsets
     if (static_cast<int64_t>(m->capq) * m->d * m->bits / 8 >= (int64_t{1} << 31) ||
-        static_cast<int64_t>(m->cap16) * m->d * 2 >= (int64_t{1} << 31))
+        static_cast<int64_t>(m->cap16) * m->d * ib / 8 >= (int64_t{1} << 31))
       return MIKV_ERR_SHAPE;
   }
   return MIKV_OK;
 }
 
-mikv_status check_cache(const mikv_cache* c) {
+mikv_status check_cache(const mikv_cache* c, int imp_bits) {
   if (!c) return MIKV_ERR_NULL;
-  if (!c->k16 || !c->v16 || !c->pos16 || !c->acc16 || !c->free16 || !c->kq || !c->vq ||
-      !c->ksz || !c->vsz || !c->posq)
+  if (!c->pos16 || !c->acc16 || !c->free16 || !c->kq || !c->vq || !c->ksz || !c->vsz || !c->posq)
     return MIKV_ERR_NULL;
-  if (!aligned16(c->k16) || !aligned16(c->v16) || !aligned16(c->kq) || !aligned16(c->vq))
-    return MIKV_ERR_SHAPE;
+  if (!aligned16(c->kq) || !aligned16(c->vq)) return MIKV_ERR_SHAPE;
+  if (imp_bits == 16) {
+    if (!c->k16 || !c->v16) return MIKV_ERR_NULL;
+    if (!aligned16(c->k16) || !aligned16(c->v16)) return MIKV_ERR_SHAPE;
+  } else {
+    if (!c->kimp || !c->vimp || !c->kimpsz || !c->vimpsz) return MIKV_ERR_NULL;
+    if (!aligned16(c->kimp) || !aligned16(c->vimp)) return MIKV_ERR_SHAPE;
+  }
   return MIKV_OK;
+}
+
+void set_imp(DecodeArgs& a, const mikv_dims* m, const mikv_cache* c) {
+  a.imp_bits = imp_of(m);
+  a.kimp = c->kimp; a.vimp = c->vimp; a.kimpsz = c->kimpsz; a.vimpsz = c->vimpsz;
+  a.h2o.imp_bits = a.imp_bits;
+  a.h2o.kimp = c->kimp; a.h2o.vimp = c->vimp;
+  a.h2o.kimpsz = reinterpret_cast<uint32_t*>(c->kimpsz);
+  a.h2o.vimpsz = reinterpret_cast<uint32_t*>(c->vimpsz);
+}
+
+void set_imp(H2OArgs& a, const mikv_dims* m, const mikv_cache* c) {
+  a.imp_bits = imp_of(m);
+  a.kimp = c->kimp; a.vimp = c->vimp; a.kimpsz = c->kimpsz; a.vimpsz = c->vimpsz;
 }
 
 mikv_status from_hip(hipError_t e) { return e == hipSuccess ? MIKV_OK : MIKV_ERR_HIP; }
@@ -141,7 +167,7 @@ size_t mikv_decode_attn_workspace(const mikv_dims* m, int32_t max_len) {
   if (check_dims(m, true) != MIKV_OK) return 0;
   const int nq = max_len - m->cap16;
   if (nq < 0) return 0;
-  return decode_ws_bound(m->batch, m->hq, m->hkv, m->d, m->bits, m->group, m->cap16, nq);
+  return decode_ws_bound(m->batch, m->hq, m->hkv, m->d, m->bits, m->group, m->cap16, nq, imp_of(m));
 }
 
 static mikv_status decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t len,
@@ -150,7 +176,7 @@ static mikv_status decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t 
                                void* stream, void* ev_start, void* ev_stop) {
   mikv_status st = check_dims(m, true);
   if (st != MIKV_OK) return st;
-  st = check_cache(c);
+  st = check_cache(c, imp_of(m));
   if (st != MIKV_OK) return st;
   if (!q || !k_new || !v_new || !b || !o || !p16) return MIKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new)) return MIKV_ERR_SHAPE;
@@ -158,7 +184,7 @@ static mikv_status decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t 
   if (nq < 0) return MIKV_ERR_SHAPE;
   if (nq > m->capq) return MIKV_ERR_CAPACITY;
   const DecodePlan pl = decode_plan(m->batch, m->hkv, m->d, m->bits, m->group, m->hq / m->hkv,
-                                    m->cap16, nq);
+                                    m->cap16, nq, imp_of(m));
   const size_t need = decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, pl);
   if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
   DecodeArgs a;
@@ -170,6 +196,7 @@ static mikv_status decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t 
   a.o = o; a.p16 = p16; a.ws = ws;
   a.fuse_h2o = false;
   a.h2o = H2OView{};
+  set_imp(a, m, c);
   a.ev_split_start = static_cast<hipEvent_t>(ev_start);
   a.ev_split_stop = static_cast<hipEvent_t>(ev_stop);
   return from_hip(launch_decode_attn(a, pl, static_cast<hipStream_t>(stream)));
@@ -203,7 +230,7 @@ mikv_status check_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t l
                               const float* p16, DecodePlan* plan, size_t* need) {
   mikv_status st = check_dims(m, true);
   if (st != MIKV_OK) return st;
-  st = check_cache(c);
+  st = check_cache(c, imp_of(m));
   if (st != MIKV_OK) return st;
   if (!q || !k_new || !v_new || !b || !o || !p16) return MIKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new)) return MIKV_ERR_SHAPE;
@@ -211,7 +238,8 @@ mikv_status check_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t l
   const int nq = len - m->cap16;
   if (nq < 0) return MIKV_ERR_SHAPE;
   if (nq + 1 > m->capq) return MIKV_ERR_CAPACITY;  // the demotion adds one low-bit token
-  *plan = decode_plan(m->batch, m->hkv, m->d, m->bits, m->group, m->hq / m->hkv, m->cap16, nq);
+  *plan = decode_plan(m->batch, m->hkv, m->d, m->bits, m->group, m->hq / m->hkv, m->cap16, nq,
+                      imp_of(m));
   *need = decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, *plan);
   return MIKV_OK;
 }
@@ -238,6 +266,7 @@ mikv_status launch_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t 
   v.ksz = reinterpret_cast<uint32_t*>(c->ksz);
   v.vsz = reinterpret_cast<uint32_t*>(c->vsz);
   v.posq = c->posq; v.demoted_pos = demoted_pos;
+  set_imp(a, m, c);
   hipError_t e = launch_decode_attn(a, pl, static_cast<hipStream_t>(stream));
   if (e != hipSuccess || a.fuse_h2o) return from_hip(e);
   // large FP16 tiers: the H2O step runs as its own launch
@@ -247,6 +276,7 @@ mikv_status launch_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t 
   h.k16 = c->k16; h.v16 = c->v16; h.pos16 = c->pos16; h.acc16 = c->acc16; h.free16 = c->free16;
   h.kq = c->kq; h.vq = c->vq; h.ksz = c->ksz; h.vsz = c->vsz; h.posq = c->posq;
   h.p16 = p16; h.demoted_pos = demoted_pos;
+  set_imp(h, m, c);
   return from_hip(launch_h2o_decode(h, static_cast<hipStream_t>(stream)));
 }
 
@@ -296,7 +326,7 @@ mikv_status mikv_h2o_update_select(const mikv_dims* m, const mikv_cache* c, int3
                                    size_t ws_bytes, void* stream) {
   mikv_status st = check_dims(m, true);
   if (st != MIKV_OK) return st;
-  st = check_cache(c);
+  st = check_cache(c, imp_of(m));
   if (st != MIKV_OK) return st;
   if ((p16 == nullptr) == (src == nullptr)) return MIKV_ERR_NULL;
   if (recent < 0 || heavy < 0 || heavy + recent != m->cap16 - 1) return MIKV_ERR_SHAPE;
@@ -305,6 +335,7 @@ mikv_status mikv_h2o_update_select(const mikv_dims* m, const mikv_cache* c, int3
   a.cap16 = m->cap16; a.capq = m->capq; a.len = len; a.recent = recent; a.heavy = heavy;
   a.k16 = c->k16; a.v16 = c->v16; a.pos16 = c->pos16; a.acc16 = c->acc16; a.free16 = c->free16;
   a.kq = c->kq; a.vq = c->vq; a.ksz = c->ksz; a.vsz = c->vsz; a.posq = c->posq;
+  set_imp(a, m, c);
   const int B = m->cap16 - 1;
   if (p16) {
     // decode: the low-bit tier grows to len - B tokens

@@ -95,7 +95,7 @@ __device__ __forceinline__ float sum_over_stride(float v) {
 // and writes (scale | zero << 16) to *sz_word.
 // ---------------------------------------------------------------------------
 template <int BITS, int NL>
-__device__ __forceinline__ uint32_t quantize8(const float (&x)[8], uint32_t* sz_word) {
+__device__ __forceinline__ void quantize8_codes(const float (&x)[8], uint32_t* sz_word, uint32_t (&code)[8]) {
   constexpr float qmax = static_cast<float>((1 << BITS) - 1);
   float mn = x[0], mx = x[0];
 #pragma unroll
@@ -111,25 +111,27 @@ __device__ __forceinline__ uint32_t quantize8(const float (&x)[8], uint32_t* sz_
   uint16_t z16 = f2h(mn);  // exact: mn is an fp16 value
   if ((z16 & 0x7FFFu) == 0) z16 = 0;
   *sz_word = static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16);
-  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) code[i] = 0;
   if (s16 != 0) {
     const float s = h2f(s16);
     const float z = h2f(z16);
     // code = rint of the IEEE quotient fl((x - z) / s), found without the
     // divide: y = (x - z) * rcp(s) is within 1.6 * 2^-23 |Q| of the exact
     // quotient Q (rcp within 1 ulp, one rounded multiply) and fl(Q) within
-    // 2^-24 |Q|, so |y - fl(Q)| <= 2^-18 for the codes' range |Q| <= 16.
-    // When y is more than 2^-16 away from its nearest half-integer, y and
-    // fl(Q) lie in the same rounding interval and rint(y) = rint(fl(Q)); a
-    // lane with any value closer than that (about 1e-5 of values) takes the
-    // IEEE divide for all of its values.
+    // 2^-24 |Q|, so |y - fl(Q)| <= 2^-22 |Q|: 2^-18 for the 2- and 4-bit
+    // codes' range |Q| <= 16, 2^-14 for 8-bit codes (|Q| <= 256).
+    // When y is farther than the margin (2^-16, or 2^-13 at 8 bits) from its
+    // nearest half-integer, y and fl(Q) lie in the same rounding interval and
+    // rint(y) = rint(fl(Q)); a lane with any value closer than that (about
+    // 1e-5 of values, 1e-4 at 8 bits) takes the IEEE divide for all of them.
     const float r = __builtin_amdgcn_rcpf(s);
     float t[8];
     bool near_half = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float y = (x[i] - z) * r;
-      near_half |= fabsf((y - floorf(y)) - 0.5f) <= 0x1p-16f;
+      near_half |= fabsf((y - floorf(y)) - 0.5f) <= (BITS == 8 ? 0x1p-13f : 0x1p-16f);
       t[i] = rintf(y);
     }
     if (near_half) {
@@ -137,12 +139,41 @@ __device__ __forceinline__ uint32_t quantize8(const float (&x)[8], uint32_t* sz_
       for (int i = 0; i < 8; ++i) t[i] = rintf((x[i] - z) / s);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float c = fminf(fmaxf(t[i], 0.0f), qmax);
-      packed |= static_cast<uint32_t>(c) << (BITS * i);
-    }
+    for (int i = 0; i < 8; ++i) code[i] = static_cast<uint32_t>(fminf(fmaxf(t[i], 0.0f), qmax));
   }
+}
+
+// Packed codes of the lane's 8 channels (BITS <= 4: the low 8*BITS bits).
+template <int BITS, int NL>
+__device__ __forceinline__ uint32_t quantize8(const float (&x)[8], uint32_t* sz_word) {
+  uint32_t code[8];
+  quantize8_codes<BITS, NL>(x, sz_word, code);
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) packed |= code[i] << (BITS * i);
   return packed;
+}
+
+// The 8 codes packed at QB bits (8, 4 or 2) into w[0..1]: byte j of the
+// 8-bit form holds channel j; the 4- and 2-bit forms use w[0] only.
+template <int QB>
+__device__ __forceinline__ void pack8(const uint32_t (&code)[8], uint32_t (&w)[2]) {
+  if constexpr (QB == 8) {
+    w[0] = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    w[1] = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+  } else {
+    w[0] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[0] |= code[i] << (QB * i);
+    w[1] = 0;
+  }
+}
+
+// Code of channel e (0..7) of a lane's QB-bit codes w[0..1].
+template <int QB>
+__device__ __forceinline__ uint32_t code_of(const uint32_t* w, int e) {
+  if constexpr (QB == 8) return (w[e / 4] >> (8 * (e % 4))) & 0xFFu;
+  else return (w[0] >> (QB * e)) & ((1u << QB) - 1u);
 }
 
 // Streaming loads with the nontemporal hint (the cache rows of a decode
@@ -168,6 +199,33 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
   x[2] = lo_h(w.y); x[3] = hi_h(w.y);
   x[4] = lo_h(w.z); x[5] = hi_h(w.z);
   x[6] = lo_h(w.w); x[7] = hi_h(w.w);
+}
+
+// Store packed codes of 8 channels: INT8 -> 8 bytes, INT4 -> one 32-bit
+// word, INT2 -> 16 bits.
+template <int BITS>
+__device__ __forceinline__ void store_codes8w(uint8_t* row_codes, int lane_in_row, const uint32_t (&w)[2]) {
+  if constexpr (BITS == 8) {
+    reinterpret_cast<uint2*>(row_codes)[lane_in_row] = make_uint2(w[0], w[1]);
+  } else if constexpr (BITS == 4) {
+    reinterpret_cast<uint32_t*>(row_codes)[lane_in_row] = w[0];
+  } else {
+    reinterpret_cast<uint16_t*>(row_codes)[lane_in_row] = static_cast<uint16_t>(w[0]);
+  }
+}
+// Load the packed codes of a lane's 8 channels (the inverse of store_codes8w).
+template <int BITS>
+__device__ __forceinline__ void load_codes8w(const uint8_t* row_codes, int lane_in_row, uint32_t (&w)[2]) {
+  if constexpr (BITS == 8) {
+    const uint2 t = reinterpret_cast<const uint2*>(row_codes)[lane_in_row];
+    w[0] = t.x; w[1] = t.y;
+  } else if constexpr (BITS == 4) {
+    w[0] = reinterpret_cast<const uint32_t*>(row_codes)[lane_in_row];
+    w[1] = 0;
+  } else {
+    w[0] = reinterpret_cast<const uint16_t*>(row_codes)[lane_in_row];
+    w[1] = 0;
+  }
 }
 
 // Store packed codes of 8 channels: INT4 -> one 32-bit word, INT2 -> 16 bits.

@@ -69,6 +69,10 @@ struct DecodeK {
   const uint8_t* vq;
   const uint32_t* ksz;
   const uint32_t* vsz;
+  uint8_t* kimp;      // importance tier as codes (reduced-precision importance cache)
+  uint8_t* vimp;
+  uint32_t* kimpsz;
+  uint32_t* vimpsz;
   float* o;
   float* p16;
   float2* part_ml;  // [units][tiles][S][RT]  (max, sum) per split and head
@@ -980,42 +984,50 @@ static int device_cus() {
 // Resident split-kernel blocks per compute unit for this instantiation, from
 // the runtime's occupancy calculator (cached per instantiation); the
 // default when it cannot answer (no device).
-template <int D, int BITS, int RT, bool TILE>
+template <int D, int BITS, int IB, int RT, bool TILE>
 static const void* split_kernel_ptr() {
-  if constexpr (TILE) return reinterpret_cast<const void*>(decode_tile_kernel<D, BITS, RT>);
+  if constexpr (TILE) return reinterpret_cast<const void*>(decode_tile_kernel<D, BITS, IB, RT>);
   else return reinterpret_cast<const void*>(decode_split_kernel<D, BITS, RT>);
 }
-template <int D, int BITS, int RT, bool TILE>
-static int occupancy_of() {
-  int n = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &n, split_kernel_ptr<D, BITS, RT, TILE>(), kThreads, 0);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  return n;
-}
-// Head tiles of 2-4 heads with groups of d/2 channels run decode_tile_kernel
-// (scores on the matrix cores); the other tiles decode_split_kernel.
-static inline bool use_tile_kernel(int d, int group, int rt) { return rt > 1 && group == d / 2; }
-static int split_blocks_per_cu(int d, int bits, int rt, bool tile) {
-  static std::atomic<int> cache[2][2][3][2];
-  std::atomic<int>& c = cache[d == 128][bits == 4][rt == 1 ? 0 : (rt == 2 ? 1 : 2)][tile ? 1 : 0];
-  int n = c.load(std::memory_order_relaxed);
+template <int D, int BITS, int IB, int RT, bool TILE>
+static int blocks_per_cu() {
+  static std::atomic<int> cache{0};
+  int n = cache.load(std::memory_order_relaxed);
   if (n == 0) {
-#define MIKV_OCC(D_, B_, RT_)                                                   \
-  if (d == D_ && bits == B_ && rt == RT_)                                       \
-    n = tile ? occupancy_of<D_, B_, RT_, (RT_ > 1)>() : occupancy_of<D_, B_, RT_, false>();
-    MIKV_OCC(128, 4, 1) MIKV_OCC(128, 4, 2) MIKV_OCC(128, 4, 4)
-    MIKV_OCC(128, 2, 1) MIKV_OCC(128, 2, 2) MIKV_OCC(128, 2, 4)
-    MIKV_OCC(64, 4, 1) MIKV_OCC(64, 4, 2) MIKV_OCC(64, 4, 4)
-    MIKV_OCC(64, 2, 1) MIKV_OCC(64, 2, 2) MIKV_OCC(64, 2, 4)
-#undef MIKV_OCC
-    if (n <= 0) return MIKV_BLOCKS_PER_CU;
-    c.store(n, std::memory_order_relaxed);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr<D, BITS, IB, RT, TILE>(), kThreads,
+                                                     0) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      return MIKV_BLOCKS_PER_CU;
+    }
+    cache.store(n, std::memory_order_relaxed);
   }
   return n < MIKV_BLOCKS_PER_CU ? n : MIKV_BLOCKS_PER_CU;
+}
+// decode_tile_kernel (scores on the matrix cores) for head tiles of 2-4
+// heads, and for every tile when the importance tier holds codes; groups of
+// d/2 channels. Otherwise decode_split_kernel.
+static inline bool use_tile_kernel(int d, int group, int rt, int ib) {
+  return group == d / 2 && (ib < 16 || rt > 1);
+}
+static int split_blocks_per_cu(int d, int bits, int ib, int rt, bool tile) {
+#define MIKV_OCC16(D_, B_, RT_)                           \
+  if (d == D_ && bits == B_ && ib == 16 && rt == RT_)     \
+    return tile ? blocks_per_cu<D_, B_, 16, RT_, (RT_ > 1)>() : blocks_per_cu<D_, B_, 16, RT_, false>();
+#define MIKV_OCCQ(D_, B_, IB_)                                                           \
+  if (d == D_ && bits == B_ && ib == IB_) {                                              \
+    if (rt == 1) return blocks_per_cu<D_, B_, IB_, 1, true>();                           \
+    if (rt == 2) return blocks_per_cu<D_, B_, IB_, 2, true>();                           \
+    return blocks_per_cu<D_, B_, IB_, 4, true>();                                        \
+  }
+  MIKV_OCC16(128, 4, 1) MIKV_OCC16(128, 4, 2) MIKV_OCC16(128, 4, 4)
+  MIKV_OCC16(128, 2, 1) MIKV_OCC16(128, 2, 2) MIKV_OCC16(128, 2, 4)
+  MIKV_OCC16(64, 4, 1) MIKV_OCC16(64, 4, 2) MIKV_OCC16(64, 4, 4)
+  MIKV_OCC16(64, 2, 1) MIKV_OCC16(64, 2, 2) MIKV_OCC16(64, 2, 4)
+  MIKV_OCCQ(128, 4, 8) MIKV_OCCQ(128, 4, 4) MIKV_OCCQ(128, 2, 8) MIKV_OCCQ(128, 2, 4)
+  MIKV_OCCQ(64, 4, 8) MIKV_OCCQ(64, 4, 4) MIKV_OCCQ(64, 2, 8) MIKV_OCCQ(64, 2, 4)
+#undef MIKV_OCC16
+#undef MIKV_OCCQ
+  return MIKV_BLOCKS_PER_CU;
 }
 
 // Split sizes. The grid is sized to one resident wave of blocks
@@ -1031,17 +1043,20 @@ static int split_blocks_per_cu(int d, int bits, int rt, bool tile) {
 // lane groups): the time of a tier is its token count, an FP16 token
 // weighted 1.3 (on the 32K GQA shape, token shares of 1:1 and 1.3:1 gave a
 // split kernel of 29.6 and 28.7 us, byte shares 34.2 us).
-DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq) {
+DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq,
+                       int imp_bits) {
   DecodePlan pl;
   pl.RT = (rep % 4 == 0) ? 4 : (rep % 2 == 0 ? 2 : 1);
   pl.tiles = rep / pl.RT;
-  const bool tile = use_tile_kernel(d, group, pl.RT);
-  const double b16 = static_cast<double>(cap16) * 4.0 * d;
+  const bool tile = use_tile_kernel(d, group, pl.RT, imp_bits);
+  const double b16 = static_cast<double>(cap16) *
+                     (imp_bits == 16 ? 4.0 * d : 2.0 * (d * imp_bits / 8 + 4 * (d / group)));
   const double bq = static_cast<double>(nq) * 2.0 * (d * bits / 8 + 4 * (d / group));
-  const double t16 = pl.RT == 1 ? b16 : 1.3 * cap16;
-  const double tq = pl.RT == 1 ? bq : static_cast<double>(nq);
+  // a code importance tier costs like the retained tier: shares by bytes
+  const double t16 = (pl.RT == 1 || imp_bits < 16) ? b16 : 1.3 * cap16;
+  const double tq = (pl.RT == 1 || imp_bits < 16) ? bq : static_cast<double>(nq);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
-  long per_unit = (static_cast<long>(device_cus()) * split_blocks_per_cu(d, bits, pl.RT, tile)) / units;
+  long per_unit = (static_cast<long>(device_cus()) * split_blocks_per_cu(d, bits, imp_bits, pl.RT, tile)) / units;
   // no split below ~16 KB of rows
   const long cap_splits = static_cast<long>((b16 + bq) / 16384.0) + 1;
   if (per_unit > cap_splits) per_unit = cap_splits;
@@ -1053,7 +1068,7 @@ DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, 
   // token costs about 1.6 low-bit tokens there (per-block timestamps, 32K
   // GQA shape: FP16-first 27.2 us against 28.1 us; GQA batch FP16-first
   // 85.5 us against 81.1 us; 4K MHA layer 43.1 against 40.8 us).
-  pl.f16_first = (pl.RT > 1 && per_unit >= 2) ? 1 : 0;
+  pl.f16_first = (pl.RT > 1 && imp_bits == 16 && per_unit >= 2) ? 1 : 0;
   if (nq > 0) {
     if (per_unit < 2) per_unit = 2;
     long s16 = static_cast<long>(per_unit * t16 / (t16 + tq) + 0.5);
@@ -1088,9 +1103,10 @@ size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int cap16, const Decod
 // Workspace for every length up to nq_max: the partial count of any plan is
 // at most max(4, blocks-per-unit) + 1 splits per (sequence, kv head, tile)
 // (head tiles take up to 4 splits when fewer than two blocks per unit fit).
-size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nq_max) {
+size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nq_max,
+                       int imp_bits) {
   const int rep = hq / hkv;
-  DecodePlan pl = decode_plan(batch, hkv, d, bits, group, rep, cap16, nq_max);
+  DecodePlan pl = decode_plan(batch, hkv, d, bits, group, rep, cap16, nq_max, imp_bits);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
   long per_unit = (static_cast<long>(device_cus()) * MIKV_BLOCKS_PER_CU) / units;
   if (per_unit < 4) per_unit = 4;
@@ -1099,7 +1115,7 @@ size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, i
   return decode_ws_bytes(batch, hq, hkv, d, cap16, pl);
 }
 
-template <int D, int BITS, int RT>
+template <int D, int BITS, int IB, int RT>
 static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
   DecodeK k;
   k.hq = a.hq; k.hkv = a.hkv; k.rep = a.hq / a.hkv; k.cap16 = a.cap16; k.capq = a.capq;
@@ -1110,6 +1126,9 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   k.kq = a.kq; k.vq = a.vq;
   k.ksz = reinterpret_cast<const uint32_t*>(a.ksz);
   k.vsz = reinterpret_cast<const uint32_t*>(a.vsz);
+  k.kimp = a.kimp; k.vimp = a.vimp;
+  k.kimpsz = reinterpret_cast<uint32_t*>(a.kimpsz);
+  k.vimpsz = reinterpret_cast<uint32_t*>(a.vimpsz);
   k.o = a.o; k.p16 = a.p16;
   const size_t units = static_cast<size_t>(a.batch) * a.hkv;
   const int S = pl.S16 + pl.Sq;
@@ -1121,18 +1140,24 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   w += al256(nparts * pl.RT * D * sizeof(float));
   k.sc16 = reinterpret_cast<float*>(w);
   hipError_t e;
-  const bool tile = use_tile_kernel(D, a.group, RT);
-  const void* kfn = tile ? split_kernel_ptr<D, BITS, RT, (RT > 1)>() : split_kernel_ptr<D, BITS, RT, false>();
+  // IB < 16 (a code importance tier): decode_tile_kernel for every tile;
+  // IB = 16: the tile kernel for head tiles of groups d/2, else the split kernel
+  constexpr bool kTileAlways = IB < 16;
+  const bool tile = kTileAlways || use_tile_kernel(D, a.group, RT, IB);
+  const void* kfn = tile ? split_kernel_ptr<D, BITS, IB, RT, (kTileAlways || RT > 1)>()
+                         : split_kernel_ptr<D, BITS, IB, RT, false>();
   if (a.ev_split_start || a.ev_split_stop) {
     // the events take the kernel's own start and end timestamps
     void* args[] = {&k};
     e = hipExtLaunchKernel(kfn, dim3(static_cast<unsigned>(nparts)), dim3(kThreads), args, 0, stream,
                            a.ev_split_start, a.ev_split_stop, 0);
   } else if (tile) {
-    if constexpr (RT > 1) decode_tile_kernel<D, BITS, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
+    if constexpr (kTileAlways || RT > 1)
+      decode_tile_kernel<D, BITS, IB, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
     e = hipGetLastError();
   } else {
-    decode_split_kernel<D, BITS, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
+    if constexpr (!kTileAlways)
+      decode_split_kernel<D, BITS, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
@@ -1170,12 +1195,15 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
 }
 
 hipError_t launch_decode_attn(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
-#define MIKV_DA(D_, B_, RT_) \
-  if (a.d == D_ && a.bits == B_ && pl.RT == RT_) return launch_da<D_, B_, RT_>(a, pl, stream);
-  MIKV_DA(128, 4, 1) MIKV_DA(128, 4, 2) MIKV_DA(128, 4, 4)
-  MIKV_DA(128, 2, 1) MIKV_DA(128, 2, 2) MIKV_DA(128, 2, 4)
-  MIKV_DA(64, 4, 1) MIKV_DA(64, 4, 2) MIKV_DA(64, 4, 4)
-  MIKV_DA(64, 2, 1) MIKV_DA(64, 2, 2) MIKV_DA(64, 2, 4)
+#define MIKV_DA(D_, B_, IB_, RT_) \
+  if (a.d == D_ && a.bits == B_ && a.imp_bits == IB_ && pl.RT == RT_) return launch_da<D_, B_, IB_, RT_>(a, pl, stream);
+#define MIKV_DA3(D_, B_, IB_) MIKV_DA(D_, B_, IB_, 1) MIKV_DA(D_, B_, IB_, 2) MIKV_DA(D_, B_, IB_, 4)
+  MIKV_DA3(128, 4, 16) MIKV_DA3(128, 2, 16) MIKV_DA3(64, 4, 16) MIKV_DA3(64, 2, 16)
+  if (a.group == a.d / 2) {
+    MIKV_DA3(128, 4, 8) MIKV_DA3(128, 4, 4) MIKV_DA3(128, 2, 8) MIKV_DA3(128, 2, 4)
+    MIKV_DA3(64, 4, 8) MIKV_DA3(64, 4, 4) MIKV_DA3(64, 2, 8) MIKV_DA3(64, 2, 4)
+  }
+#undef MIKV_DA3
 #undef MIKV_DA
   return hipErrorInvalidValue;
 }

@@ -22,6 +22,12 @@
 // group on the score lanes. The running maximum per head is lazy: it moves
 // only when a score exceeds it by more than kTileHeadroom (log2 units), so
 // the rescaling of the sums is rare and the common path has no reduction.
+//
+// The importance tier is either fp16 rows (QB = 16) or, for a reduced-
+// precision importance cache (velog notes, Key contributions 3); paperlayer
+// summary, section 3.3), codes of 8 or 4 bits read exactly like the retained
+// tier's; the new token is then quantized as it is appended and enters the
+// attention through its dequantized codes.
 #pragma once
 
 #ifndef MIKV_TILE_NS
@@ -39,12 +45,12 @@ constexpr int kTileG = 16;  // tokens per MFMA group
 // Chunks 0..CPG-1 cover group 0 (channels [0, d/2)), the rest group 1; lane
 // group r takes a contiguous run of 8*CPG channels of each group. Within the
 // 8 channels of a chunk the order is the one the code conversion produces.
-template <int D, int BITS, bool F16T>
+template <int D, int QB>
 __device__ __forceinline__ constexpr int tile_chan(int c, int r, int e) {
   constexpr int CPG = D / 64, G = D / 2;
   int pe = e;
-  if constexpr (!F16T && BITS == 4) pe = (e < 4) ? 2 * e : 2 * (e - 4) + 1;
-  if constexpr (!F16T && BITS == 2) pe = (e % 2 == 0) ? e / 2 : 4 + e / 2;
+  if constexpr (QB == 4) pe = (e < 4) ? 2 * e : 2 * (e - 4) + 1;
+  if constexpr (QB == 2) pe = (e % 2 == 0) ? e / 2 : 4 + e / 2;
   return (c / CPG) * G + 8 * CPG * r + (c % CPG) * 8 + pe;
 }
 
@@ -73,45 +79,57 @@ __device__ __forceinline__ void tile_load(Rsrc r, uint32_t off, uint32_t* w) {
   }
 }
 
-// 8 codes -> the MFMA operand (exact fp16 integers, order of tile_chan).
-template <int BITS>
-__device__ __forceinline__ tile_h8 tile_codes(uint32_t w, uint32_t magic) {
+// The 8 codes of part `part` of a lane's group words -> the MFMA operand
+// (exact fp16 integers, order of tile_chan).
+template <int QB>
+__device__ __forceinline__ tile_h8 tile_codes(const uint32_t* w, int part, uint32_t magic) {
   constexpr uint32_t kLo = 0x04010400u, kHi = 0x04030402u;
   tile_u4 u;
-  if constexpr (BITS == 4) {  // 8 nibbles of one word
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  if constexpr (QB == 8) {  // 8 bytes in two words, channel order kept
+    const uint32_t a = w[2 * part], b = w[2 * part + 1];
+    u[0] = __builtin_amdgcn_perm(magic, a, kLo);
+    u[1] = __builtin_amdgcn_perm(magic, a, kHi);
+    u[2] = __builtin_amdgcn_perm(magic, b, kLo);
+    u[3] = __builtin_amdgcn_perm(magic, b, kHi);
+  } else if constexpr (QB == 4) {  // 8 nibbles of one word
+    const uint32_t x = w[part];
+    const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
     u[0] = __builtin_amdgcn_perm(magic, lo, kLo);
     u[1] = __builtin_amdgcn_perm(magic, lo, kHi);
     u[2] = __builtin_amdgcn_perm(magic, hi, kLo);
     u[3] = __builtin_amdgcn_perm(magic, hi, kHi);
-  } else {  // 8 crumbs in the low 16 bits
+  } else {  // 8 crumbs in 16 bits
+    const uint32_t x = part ? (w[0] >> 16) : w[0];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) u[m] = __builtin_amdgcn_perm(magic, (w >> (2 * m)) & 0x0303u, kLo);
+    for (int m = 0; m < 4; ++m) u[m] = __builtin_amdgcn_perm(magic, (x >> (2 * m)) & 0x0303u, kLo);
   }
   return __builtin_bit_cast(tile_h8, u) - static_cast<tile_h8>(static_cast<_Float16>(1024.0f));
 }
 
-template <int D, int BITS, bool F16T>
+template <int D, int QB>
 struct TileRegs {
   static constexpr int CPG = D / 64;
-  static constexpr int KB = F16T ? 16 * CPG : CPG * BITS;     // key bytes per lane and group
-  static constexpr int KW = F16T ? 4 * CPG : (KB + 3) / 4;    // words per lane and group
+  static constexpr int KB = CPG * 8 * QB / 8;                 // key bytes per lane and group
+  static constexpr int KW = (KB + 3) / 4;                     // words per lane and group
   static constexpr int LPTV = D / 8, VSLOTS = 64 / LPTV, VTPL = kTileG / VSLOTS;
-  static constexpr int VB = F16T ? 16 : BITS;                 // value bytes per lane and token
+  static constexpr int VB = QB;                               // value bytes per lane and token (8 channels)
   static constexpr int VW = (VB + 3) / 4;
   uint32_t k[2][KW];
   uint32_t ksz[2], vsz[2];
   uint32_t v[VTPL][VW];
 };
 
-template <int D, int BITS, int RT, bool F16T>
+// QB: bits per value of this tier (16 = fp16 rows); IMPT: the importance
+// tier (free slot, scores for p16, the new token) rather than the retained.
+template <int D, int QB, int RT, bool IMPT>
 __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, int g, int tile, int split,
                                            const float* bvec, float* red, float (*sm)[RT], float* po,
                                            float2* pml, float (*wbuf)[kTileG][2][RT]) {
-  using R_t = TileRegs<D, BITS, F16T>;
+  using R_t = TileRegs<D, QB>;
+  constexpr bool F16T = QB == 16;
   constexpr int NCH = D / 32, CPG = D / 64, G = D / 2;
   constexpr int LPTV = R_t::LPTV, VSLOTS = R_t::VSLOTS, VTPL = R_t::VTPL;
-  constexpr int ROWB = F16T ? 2 * D : D * BITS / 8;  // bytes per token row
+  constexpr int ROWB = D * QB / 8;  // bytes per token row
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int ai = lane % 16, ar = lane / 16;           // MFMA row / k block of this lane
   const int vs = lane / LPTV, vj = lane % LPTV;       // value slot, 8-channel slice
@@ -121,16 +139,23 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
   int nt, frel = -1;
   Rsrc rk, rv, rks, rvs;
   int64_t scb = 0, rb16 = 0;
-  if constexpr (F16T) {
+  if constexpr (IMPT) {
     const int s0 = split * p.C16;
     const int s1 = min(p.cap16, s0 + p.C16);
     nt = max(s1 - s0, 0);
     rb16 = static_cast<int64_t>(unit) * p.cap16;
     frel = p.free16[unit] - s0;
-    rk = make_rsrc(p.k16 + (rb16 + s0) * D, static_cast<uint32_t>(nt) * ROWB);
-    rv = make_rsrc(p.v16 + (rb16 + s0) * D, static_cast<uint32_t>(nt) * ROWB);
-    rks = rk;  // no scales on the FP16 tier
-    rvs = rv;
+    if constexpr (F16T) {
+      rk = make_rsrc(p.k16 + (rb16 + s0) * D, static_cast<uint32_t>(nt) * ROWB);
+      rv = make_rsrc(p.v16 + (rb16 + s0) * D, static_cast<uint32_t>(nt) * ROWB);
+      rks = rk;  // no scales on an fp16 tier
+      rvs = rv;
+    } else {
+      rk = make_rsrc(p.kimp + (rb16 + s0) * ROWB, static_cast<uint32_t>(nt) * ROWB);
+      rv = make_rsrc(p.vimp + (rb16 + s0) * ROWB, static_cast<uint32_t>(nt) * ROWB);
+      rks = make_rsrc(p.kimpsz + (rb16 + s0) * 2, static_cast<uint32_t>(nt) * 8);
+      rvs = make_rsrc(p.vimpsz + (rb16 + s0) * 2, static_cast<uint32_t>(nt) * 8);
+    }
     scb = (static_cast<int64_t>(unit) * p.rep + tile * RT) * p.cap16 + s0;
   } else {
     const int t0 = (split - p.S16) * p.Cq;
@@ -149,7 +174,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       const uint32_t ch0 = gi * G + 8 * CPG * ar;
-      tile_load<R_t::KB>(rk, tk * ROWB + (F16T ? 2 * ch0 : ch0 * BITS / 8), R.k[gi]);
+      tile_load<R_t::KB>(rk, tk * ROWB + ch0 * QB / 8, R.k[gi]);
     }
     if constexpr (!F16T) {
       const Words<2> ks = bload<2>(rks, tk * 8), vz = bload<2>(rvs, tk * 8);
@@ -177,7 +202,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
   float qs_part[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int base = tile_chan<D, BITS, true>(c, ar, 0);  // first channel of the run
+    const int base = tile_chan<D, 16>(c, ar, 0);  // first channel of the run
     float qv[8];
     if (ai < RT) {
       load8(p.q + (static_cast<int64_t>(n) * p.hq + hrow) * D + base, qv);
@@ -187,7 +212,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int ch = tile_chan<D, BITS, F16T>(c, ar, e);
+      const int ch = tile_chan<D, QB>(c, ar, e);
       const float q = qv[ch - base] * __builtin_amdgcn_rcpf(bvec[ch]) * qscale;
       const _Float16 hi = static_cast<_Float16>(q);
       qa_hi[c][e] = hi;
@@ -219,8 +244,10 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
   }
 
   // ---- the new token: appended by the tile-0 block that owns the free
-  // slot, and seeded into wave 0's state (max = its score, sum = 1, o = v)
-  if constexpr (F16T) {
+  // slot, and seeded into wave 0's state (max = its score, sum = 1, o = v).
+  // A code tier stores it quantized and seeds the state with its codes
+  // rebuilt (code * scale + zero), as it will be read from then on.
+  if constexpr (IMPT) {
     if (frel >= 0 && frel < nt && wave == 0) {  // uniform
       float x[RT];
 #pragma unroll
@@ -228,32 +255,52 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
       if (lane < LPTV) {
         const int c0 = 8 * lane;
         const int64_t nb = static_cast<int64_t>(unit) * D + c0;
-        float kx[8];
+        const int64_t fs = rb16 + p.free16[unit];
+        float kx[8], vx[8];
         load8(p.k_new + nb, kx);
-        uint32_t kw[4];
+        load8(p.v_new + nb, vx);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = f2h(mul_rn(kx[2 * i], bvec[c0 + 2 * i]));
-          const uint32_t hi = f2h(mul_rn(kx[2 * i + 1], bvec[c0 + 2 * i + 1]));
-          kw[i] = lo | (hi << 16);
+        for (int e = 0; e < 8; ++e) kx[e] = h2f(f2h(mul_rn(kx[e], bvec[c0 + e])));  // fp16(k * b)
+        if constexpr (F16T) {
+          if (tile == 0) {
+            uint32_t kw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              kw[i] = static_cast<uint32_t>(f2h(kx[2 * i])) | (static_cast<uint32_t>(f2h(kx[2 * i + 1])) << 16);
+            *reinterpret_cast<uint4*>(p.k16 + fs * D + c0) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+            *reinterpret_cast<uint4*>(p.v16 + fs * D + c0) = *reinterpret_cast<const uint4*>(p.v_new + nb);
+          }
+        } else {
+          constexpr int NL = G / 8;  // lanes per quantization group
+          uint32_t kszw, vszw, kc[8], vc[8];
+          quantize8_codes<QB, NL>(kx, &kszw, kc);
+          quantize8_codes<QB, NL>(vx, &vszw, vc);
+          if (tile == 0) {
+            uint32_t kw2[2], vw2[2];
+            pack8<QB>(kc, kw2);
+            pack8<QB>(vc, vw2);
+            store_codes8w<QB>(p.kimp + fs * ROWB, lane, kw2);
+            store_codes8w<QB>(p.vimp + fs * ROWB, lane, vw2);
+            if (lane % NL == 0) {
+              p.kimpsz[fs * 2 + lane / NL] = kszw;
+              p.vimpsz[fs * 2 + lane / NL] = vszw;
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kx[e] = fmaf(static_cast<float>(kc[e]), lo_h(kszw), hi_h(kszw));
+            vx[e] = fmaf(static_cast<float>(vc[e]), lo_h(vszw), hi_h(vszw));
+          }
         }
-        const uint4 vn = *reinterpret_cast<const uint4*>(p.v_new + nb);
-        if (tile == 0) {
-          *reinterpret_cast<uint4*>(p.k16 + (rb16 + p.free16[unit]) * D + c0) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-          *reinterpret_cast<uint4*>(p.v16 + (rb16 + p.free16[unit]) * D + c0) = vn;
-          if (lane == 0) p.pos16[rb16 + p.free16[unit]] = p.len - 1;
-        }
-        const uint32_t vw[4] = {vn.x, vn.y, vn.z, vn.w};
+        if (tile == 0 && lane == 0) p.pos16[fs] = p.len - 1;
 #pragma unroll
         for (int h = 0; h < RT; ++h) {
           float qv[8];
           load8(p.q + (static_cast<int64_t>(n) * p.hq + g * p.rep + tile * RT + h) * D + c0, qv);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[h] += qv[2 * i] * __builtin_amdgcn_rcpf(bvec[c0 + 2 * i]) * qscale * lo_h(kw[i]);
-            x[h] += qv[2 * i + 1] * __builtin_amdgcn_rcpf(bvec[c0 + 2 * i + 1]) * qscale * hi_h(kw[i]);
-            a[h][2 * i] = lo_h(vw[i]);
-            a[h][2 * i + 1] = hi_h(vw[i]);
+          for (int e = 0; e < 8; ++e) {
+            x[h] += qv[e] * __builtin_amdgcn_rcpf(bvec[c0 + e]) * qscale * kx[e];
+            a[h][e] = vx[e];
           }
         }
       }
@@ -284,17 +331,15 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 #pragma unroll
         for (int i = 0; i < 4; ++i) u[i] = R.k[gi][4 * part + i];
         bop = __builtin_bit_cast(tile_h8, u);
-      } else if constexpr (BITS == 4) {
-        bop = tile_codes<4>(R.k[gi][part], magic);
       } else {
-        bop = tile_codes<2>(part ? (R.k[gi][0] >> 16) : R.k[gi][0], magic);
+        bop = tile_codes<QB>(R.k[gi], part, magic);
       }
       acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[c], bop, acc[gi], 0, 0, 0);
       acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[c], bop, acc[gi], 0, 0, 0);
     }
     const int tok = grp * kTileG + ai;
     bool valid = lane < kTileG && tok < nt;
-    if constexpr (F16T) valid = valid && tok != frel;
+    if constexpr (IMPT) valid = valid && tok != frel;
     float x[RT];
 #pragma unroll
     for (int h = 0; h < RT; ++h) {
@@ -306,7 +351,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
         xv += hi_h(R.ksz[0]) * qs[h][0] + hi_h(R.ksz[1]) * qs[h][1];
       }
       x[h] = valid ? xv : -INFINITY;
-      if constexpr (F16T) {
+      if constexpr (IMPT) {
         if (valid) p.sc16[scb + static_cast<int64_t>(h) * p.cap16 + tok] = xv;
       }
     }
@@ -373,7 +418,18 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
             a[h][2 * i + 1] += wv[h] * hi;
           }
         }
-      } else if constexpr (BITS == 4) {
+      } else if constexpr (QB == 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // channels 2i, 2i + 1
+          const uint32_t pr2 = __builtin_amdgcn_perm(magic, R.v[k][i / 2], (i % 2) ? 0x04030402u : 0x04010400u);
+          const float lo = lo_h(pr2), hi = hi_h(pr2);
+#pragma unroll
+          for (int h = 0; h < RT; ++h) {
+            a[h][2 * i] += wv[h] * lo;
+            a[h][2 * i + 1] += wv[h] * hi;
+          }
+        }
+      } else if constexpr (QB == 4) {
         const MagicPairs<4> mp(R.v[k][0], magic);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -459,7 +515,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 }
 
 
-template <int D, int BITS, int RT>
+template <int D, int BITS, int IB, int RT>
 __global__ __launch_bounds__(kThreads, 3) void decode_tile_kernel(const DecodeK p) {
   // block order as decode_split_kernel (split-major)
   const int S = p.S16 + p.Sq;
@@ -481,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_tile_kernel(const DecodeK 
   __shared__ float wbuf[4][kTileG][2][RT];
 
   if (split < p.S16) {
-    tile_split<D, BITS, RT, true>(p, unit, n, g, tile, split, bvec, red, sm_max, po, pml, wbuf);
+    tile_split<D, IB, RT, true>(p, unit, n, g, tile, split, bvec, red, sm_max, po, pml, wbuf);
   } else {
     tile_split<D, BITS, RT, false>(p, unit, n, g, tile, split, bvec, red, sm_max, po, pml, wbuf);
   }

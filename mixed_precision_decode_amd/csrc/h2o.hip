@@ -30,7 +30,7 @@ namespace mikv {
 // thread, the common case), so the select costs one memory round trip and the
 // demotion a second one.
 constexpr int kH2OSlots = 16;
-template <int D, int BITS, int NL>
+template <int D, int BITS, int NL, int IB>
 __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
   const int unit = blockIdx.x;
   const int tid = threadIdx.x;
@@ -64,8 +64,11 @@ __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
     for (int s = tid; s < a.cap16; s += 256) consider(s, accin[s], p16[s], pos16[s]);
   }
   H2OView v;
-  v.cap16 = a.cap16; v.capq = a.capq; v.len = a.len; v.recent = a.recent;
+  v.cap16 = a.cap16; v.capq = a.capq; v.len = a.len; v.recent = a.recent; v.imp_bits = IB;
   v.k16 = a.k16; v.v16 = a.v16; v.pos16 = a.pos16; v.acc16 = a.acc16; v.free16 = a.free16;
+  v.kimp = a.kimp; v.vimp = a.vimp;
+  v.kimpsz = reinterpret_cast<uint32_t*>(a.kimpsz);
+  v.vimpsz = reinterpret_cast<uint32_t*>(a.vimpsz);
   v.kq = a.kq; v.vq = a.vq;
   v.ksz = reinterpret_cast<uint32_t*>(a.ksz);
   v.vsz = reinterpret_cast<uint32_t*>(a.vsz);
@@ -161,10 +164,24 @@ __global__ __launch_bounds__(kSelThreads) void h2o_prefill_select_kernel(H2OArgs
   }
   // the free slot's rows start as zeros: decode reads them (masked), so they
   // must hold finite values
-  for (int i = tid; i < a.d / 8; i += kSelThreads) {
-    const int64_t o = (base16 + a.cap16 - 1) * a.d + 8 * i;
-    *reinterpret_cast<uint4*>(a.k16 + o) = make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(a.v16 + o) = make_uint4(0u, 0u, 0u, 0u);
+  if (a.imp_bits == 16) {
+    for (int i = tid; i < a.d / 8; i += kSelThreads) {
+      const int64_t o = (base16 + a.cap16 - 1) * a.d + 8 * i;
+      *reinterpret_cast<uint4*>(a.k16 + o) = make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(a.v16 + o) = make_uint4(0u, 0u, 0u, 0u);
+    }
+  } else {
+    // codes 0 with (scale, zero) = (0, 0): the free slot reads as zeros
+    const int cbi = a.d * a.imp_bits / 8, ng = a.d / a.group;
+    for (int i = tid; i < cbi / 4; i += kSelThreads) {
+      const int64_t o = (base16 + a.cap16 - 1) * cbi + 4 * i;
+      *reinterpret_cast<uint32_t*>(a.kimp + o) = 0u;
+      *reinterpret_cast<uint32_t*>(a.vimp + o) = 0u;
+    }
+    for (int i = tid; i < ng; i += kSelThreads) {
+      reinterpret_cast<uint32_t*>(a.kimpsz)[(base16 + a.cap16 - 1) * ng + i] = 0u;
+      reinterpret_cast<uint32_t*>(a.vimpsz)[(base16 + a.cap16 - 1) * ng + i] = 0u;
+    }
   }
 }
 
@@ -174,7 +191,7 @@ __global__ __launch_bounds__(kSelThreads) void h2o_prefill_select_kernel(H2OArgs
 // 16 blocks of 256 threads per compute unit (measured best among 1024-65536)
 constexpr int64_t kScatterBlocks = MIKV_SCATTER_BLOCKS;
 
-template <int D, int BITS, int NL>
+template <int D, int BITS, int NL, int IB>
 __global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int T,
                                                                   const int32_t* map) {
   constexpr int LPR = D / 8;
@@ -233,9 +250,26 @@ __global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int
     // R.s is the same on every lane of a row and the group reductions of
     // quantize8 stay inside a row, so the branches keep rows whole
     if (R.s >= 0) {
-      const int64_t o16 = (unit * a.cap16 + R.s) * D + lane * 8;
-      *reinterpret_cast<uint4*>(a.k16 + o16) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-      *reinterpret_cast<uint4*>(a.v16 + o16) = R.v;
+      if constexpr (IB == 16) {
+        const int64_t o16 = (unit * a.cap16 + R.s) * D + lane * 8;
+        *reinterpret_cast<uint4*>(a.k16 + o16) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+        *reinterpret_cast<uint4*>(a.v16 + o16) = R.v;
+      } else {
+        // reduced-precision importance tier: the row is stored as IB-bit codes
+        constexpr int CBI = D * IB / 8;
+        uint32_t kszw, vszw, kc[8], vc[8], kw2[2], vw2[2];
+        quantize8_codes<IB, NL>(kx, &kszw, kc);
+        quantize8_codes<IB, NL>(vx, &vszw, vc);
+        pack8<IB>(kc, kw2);
+        pack8<IB>(vc, vw2);
+        const int64_t si = unit * a.cap16 + R.s;
+        store_codes8w<IB>(a.kimp + si * CBI, lane, kw2);
+        store_codes8w<IB>(a.vimp + si * CBI, lane, vw2);
+        if (lane % NL == 0) {
+          reinterpret_cast<uint32_t*>(a.kimpsz)[si * GPT + lane / NL] = kszw;
+          reinterpret_cast<uint32_t*>(a.vimpsz)[si * GPT + lane / NL] = vszw;
+        }
+      }
     } else if (R.s != INT_MIN) {
       uint32_t kszw, vszw;
       const uint32_t kp = quantize8<BITS, NL>(kx, &kszw);
@@ -279,13 +313,13 @@ size_t h2o_ws_bytes(int batch, int hkv, int T) {
   return static_cast<size_t>(batch) * hkv * (T > 0 ? T : 1) * sizeof(int32_t);
 }
 
-template <int D, int BITS, int NL>
+template <int D, int BITS, int NL, int IB>
 static hipError_t launch_dec(const H2OArgs& a, hipStream_t stream) {
-  h2o_decode_kernel<D, BITS, NL><<<a.batch * a.hkv, 256, 0, stream>>>(a);
+  h2o_decode_kernel<D, BITS, NL, IB><<<a.batch * a.hkv, 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <int D, int BITS, int NL>
+template <int D, int BITS, int NL, int IB>
 static hipError_t launch_pre(const H2OArgs& a, hipStream_t stream) {
   const int T = a.len;
   int32_t* map = static_cast<int32_t*>(a.ws);
@@ -296,19 +330,30 @@ static hipError_t launch_pre(const H2OArgs& a, hipStream_t stream) {
   const int64_t n_rows = static_cast<int64_t>(a.batch) * a.hkv * T;
   int64_t blocks = (n_rows + RPB - 1) / RPB;
   if (blocks > kScatterBlocks) blocks = kScatterBlocks;
-  h2o_prefill_scatter_kernel<D, BITS, NL><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(a, T, map);
+  h2o_prefill_scatter_kernel<D, BITS, NL, IB><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(a, T, map);
   return hipGetLastError();
 }
 
-#define MIKV_H2O_DISPATCH(FN)                                                \
-  if (a.d == 128 && a.bits == 4 && a.group == 64) return FN<128, 4, 8>(a, stream);  \
-  if (a.d == 128 && a.bits == 4 && a.group == 128) return FN<128, 4, 16>(a, stream); \
-  if (a.d == 128 && a.bits == 2 && a.group == 64) return FN<128, 2, 8>(a, stream);  \
-  if (a.d == 128 && a.bits == 2 && a.group == 128) return FN<128, 2, 16>(a, stream); \
-  if (a.d == 64 && a.bits == 4 && a.group == 32) return FN<64, 4, 4>(a, stream);    \
-  if (a.d == 64 && a.bits == 4 && a.group == 64) return FN<64, 4, 8>(a, stream);    \
-  if (a.d == 64 && a.bits == 2 && a.group == 32) return FN<64, 2, 4>(a, stream);    \
-  if (a.d == 64 && a.bits == 2 && a.group == 64) return FN<64, 2, 8>(a, stream);    \
+#define MIKV_H2O_DISPATCH(FN)                                                          \
+  if (a.imp_bits == 16) {                                                              \
+    if (a.d == 128 && a.bits == 4 && a.group == 64) return FN<128, 4, 8, 16>(a, stream);  \
+    if (a.d == 128 && a.bits == 4 && a.group == 128) return FN<128, 4, 16, 16>(a, stream); \
+    if (a.d == 128 && a.bits == 2 && a.group == 64) return FN<128, 2, 8, 16>(a, stream);  \
+    if (a.d == 128 && a.bits == 2 && a.group == 128) return FN<128, 2, 16, 16>(a, stream); \
+    if (a.d == 64 && a.bits == 4 && a.group == 32) return FN<64, 4, 4, 16>(a, stream);    \
+    if (a.d == 64 && a.bits == 4 && a.group == 64) return FN<64, 4, 8, 16>(a, stream);    \
+    if (a.d == 64 && a.bits == 2 && a.group == 32) return FN<64, 2, 4, 16>(a, stream);    \
+    if (a.d == 64 && a.bits == 2 && a.group == 64) return FN<64, 2, 8, 16>(a, stream);    \
+  } else if (a.group == a.d / 2) {                                                     \
+    if (a.d == 128 && a.bits == 4 && a.imp_bits == 8) return FN<128, 4, 8, 8>(a, stream); \
+    if (a.d == 128 && a.bits == 4 && a.imp_bits == 4) return FN<128, 4, 8, 4>(a, stream); \
+    if (a.d == 128 && a.bits == 2 && a.imp_bits == 8) return FN<128, 2, 8, 8>(a, stream); \
+    if (a.d == 128 && a.bits == 2 && a.imp_bits == 4) return FN<128, 2, 8, 4>(a, stream); \
+    if (a.d == 64 && a.bits == 4 && a.imp_bits == 8) return FN<64, 4, 4, 8>(a, stream);   \
+    if (a.d == 64 && a.bits == 4 && a.imp_bits == 4) return FN<64, 4, 4, 4>(a, stream);   \
+    if (a.d == 64 && a.bits == 2 && a.imp_bits == 8) return FN<64, 2, 4, 8>(a, stream);   \
+    if (a.d == 64 && a.bits == 2 && a.imp_bits == 4) return FN<64, 2, 4, 4>(a, stream);   \
+  }                                                                                    \
   return hipErrorInvalidValue;
 
 hipError_t launch_h2o_decode(const H2OArgs& a, hipStream_t stream) { MIKV_H2O_DISPATCH(launch_dec) }

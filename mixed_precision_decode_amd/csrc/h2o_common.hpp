@@ -11,8 +11,13 @@ namespace mikv {
 
 struct H2OView {
   int cap16, capq, len, recent;
+  int imp_bits;       // 16: fp16 importance tier (k16, v16); 8 or 4: codes
   uint16_t* k16;
   uint16_t* v16;
+  uint8_t* kimp;      // importance tier as codes (IB < 16)
+  uint8_t* vimp;
+  uint32_t* kimpsz;   // (scale | zero << 16) per group
+  uint32_t* vimpsz;
   int32_t* pos16;
   float* acc16;
   int32_t* free16;
@@ -41,7 +46,21 @@ struct Worst {
 // Block-wide (256 threads): pick the worst candidate and quantize its key and
 // value rows into low-bit slot len - cap16 of the unit; free16 becomes the
 // dropped slot. `fr` is the slot the new token occupies (its position is
-// len - 1).
+// len - 1). v.imp_bits = 16: the rows are the slot's fp16 rows; 8 or 4: the
+// importance tier holds codes, and the row quantized is the slot's codes
+// rebuilt in fp16, fp16(code * scale + zero) (the product is exact in fp32,
+// so the fused multiply-add rounds once, like the sum of the exact product).
+template <int IB, int D, int NL>
+__device__ __forceinline__ void imp_row16(const H2OView& v, bool is_v, int64_t slot, int lane, float (&x)[8]) {
+  constexpr int CBI = D * IB / 8, GPT = D / (8 * NL);
+  uint32_t cw[2];
+  load_codes8w<IB>((is_v ? v.vimp : v.kimp) + slot * CBI, lane, cw);
+  const uint32_t szw = (is_v ? v.vimpsz : v.kimpsz)[slot * GPT + lane / NL];
+  const float s = lo_h(szw), z = hi_h(szw);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = h2f(f2h(fmaf(static_cast<float>(code_of<IB>(cw, e)), s, z)));
+}
+
 template <int D, int BITS, int NL>
 __device__ void h2o_select_demote(Worst w, const H2OView& v, int unit, int fr) {
   __shared__ float s_acc[4];
@@ -76,9 +95,15 @@ __device__ void h2o_select_demote(Worst w, const H2OView& v, int unit, int fr) {
   if (tid < 2 * LPR) {
     const int lane = tid % LPR;
     const bool is_v = tid >= LPR;
-    const uint16_t* src = (is_v ? v.v16 : v.k16) + (base16 + drop) * D + lane * 8;
     float x[8];
-    load8(src, x);
+    if (v.imp_bits == 16) {
+      const uint16_t* src = (is_v ? v.v16 : v.k16) + (base16 + drop) * D + lane * 8;
+      load8(src, x);
+    } else if (v.imp_bits == 8) {
+      imp_row16<8, D, NL>(v, is_v, base16 + drop, lane, x);
+    } else {
+      imp_row16<4, D, NL>(v, is_v, base16 + drop, lane, x);
+    }
     uint32_t szw;
     const uint32_t packed = quantize8<BITS, NL>(x, &szw);
     store_codes8<BITS>((is_v ? v.vq : v.kq) + qslot * CB, lane, packed);

@@ -26,13 +26,16 @@ struct DecodePlan {
   int tiles;       // rep / RT
   int f16_first;   // 1: FP16-tier splits take the first block indices (else the low-bit splits do)
 };
-DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq);
+DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq,
+                       int imp_bits);
 size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int cap16, const DecodePlan& plan);
 // workspace that serves every length up to nq_max low-bit tokens
-size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nq_max);
+size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nq_max,
+                       int imp_bits);
 
 struct DecodeArgs {
   int batch, hq, hkv, d, group, bits, cap16, capq, len;
+  int imp_bits;  // 16: fp16 importance tier (k16, v16); 8 or 4: codes (kimp, vimp)
   const uint16_t* q;
   const uint16_t* k_new;
   const uint16_t* v_new;
@@ -45,6 +48,10 @@ struct DecodeArgs {
   const uint8_t* vq;
   const uint16_t* ksz;
   const uint16_t* vsz;
+  uint8_t* kimp;
+  uint8_t* vimp;
+  uint16_t* kimpsz;
+  uint16_t* vimpsz;
   float* o;
   float* p16;
   void* ws;
@@ -66,6 +73,11 @@ hipError_t static_scratch_ptr(void** ptr);
 
 struct H2OArgs {
   int batch, hkv, d, group, bits, cap16, capq, len, recent, heavy;
+  int imp_bits;  // 16: fp16 importance tier; 8 or 4: codes (kimp, vimp)
+  uint8_t* kimp;
+  uint8_t* vimp;
+  uint16_t* kimpsz;
+  uint16_t* vimpsz;
   uint16_t* k16;
   uint16_t* v16;
   int32_t* pos16;

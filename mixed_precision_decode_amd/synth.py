@@ -13,7 +13,10 @@ weight is used):
   * a Llama-3-8B-shaped GQA layer (32 query / 8 kv heads) at 32K context;
   * a GQA throughput batch;
   * the CriticalKV 32K-context, batch-1 setting (gist.science summary of
-    arXiv 2502.03805, experiments / efficiency).
+    arXiv 2502.03805, experiments / efficiency);
+  * the reduced-precision importance cache of Table 3 on the velog notes
+    page (20% importance at INT4 or INT8, 2-bit retention), on the
+    Llama-2-7B layer shape.
 
 Value model. q, k, v are N(0,1) draws cast to fp16 with round-to-nearest-even.
 Query/key outliers follow the observations on the velog notes page
@@ -62,6 +65,7 @@ class DecodeConfig:
     pairs: int        # outlier channel pairs per kv head
     factor: float     # outlier magnitude multiplier
     group: int = 0    # channels per quantization group (0: d/2)
+    imp_bits: int = 16  # importance tier: 16 = fp16 rows, 8 or 4 = codes
 
     @property
     def rep(self) -> int:
@@ -117,6 +121,14 @@ CONFIGS = {
                                   bits=2, pct=10, recent=64, steps=64, pairs=2, factor=20.0),
     "gqa_throughput": DecodeConfig("gqa_throughput", batch=64, hq=32, hkv=8, d=128, T=2048,
                                    bits=4, pct=20, recent=64, steps=100, pairs=2, factor=20.0),
+    # reduced-precision importance cache: 20% importance at INT4 or INT8 over a
+    # 2-bit retention cache (the setting of Table 3 on the velog notes page)
+    "llama2_7b_imp4": DecodeConfig("llama2_7b_imp4", batch=8, hq=32, hkv=32, d=128, T=4096,
+                                   bits=2, pct=20, recent=64, steps=128, pairs=2, factor=20.0,
+                                   imp_bits=4),
+    "llama2_7b_imp8": DecodeConfig("llama2_7b_imp8", batch=8, hq=32, hkv=32, d=128, T=4096,
+                                   bits=2, pct=20, recent=64, steps=128, pairs=2, factor=20.0,
+                                   imp_bits=8),
 }
 
 CKV_CONFIGS = {

@@ -36,7 +36,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.mikv_abi_version() == 2
+    assert lib.mikv_abi_version() == 3
     for s in range(8):
         assert len(L.mikv_status_str(s)) > 0
     assert L.mikv_status_str(99) == "unknown status"
@@ -131,6 +131,32 @@ def test_decode_step_validation(lib):
     assert call(length=111) == L.MIKV_ERR_CAPACITY     # demotion would need slot 100
     assert call(ws_bytes=16) == L.MIKV_ERR_WORKSPACE
     assert call(_dims(bits=8)) == L.MIKV_ERR_UNSUPPORTED
+
+
+def test_importance_codes_validation(lib):
+    """imp_bits: 16 or 0 = fp16 importance tier, 8 or 4 = codes (with groups
+    of d/2 and the kimp/vimp/kimpsz/vimpsz pointers); anything else is
+    refused before a launch."""
+    c = _cache()
+    need = lib.mikv_decode_attn_workspace(C.byref(_dims(imp_bits=8).c()), 80)
+    assert need > 0
+    call = lambda dims, cache=c: lib.mikv_decode_attn(
+        C.byref(dims.c()), C.byref(cache), 50, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None)
+    assert call(_dims(imp_bits=6)) == L.MIKV_ERR_UNSUPPORTED
+    assert call(_dims(imp_bits=2)) == L.MIKV_ERR_UNSUPPORTED
+    assert call(_dims(imp_bits=8, group=128)) == L.MIKV_ERR_UNSUPPORTED
+    # codes tier without its pointers; an fp16 tier may leave them NULL
+    no_imp = L.MikvCache(*([FAKE] * 10 + [0] * 4))
+    assert call(_dims(imp_bits=8), no_imp) == L.MIKV_ERR_NULL
+    no16 = L.MikvCache(*([0, 0] + [FAKE] * 12))
+    assert call(_dims(imp_bits=16), no16) == L.MIKV_ERR_NULL
+    step = lambda dims, cache: lib.mikv_decode_step(
+        C.byref(dims.c()), C.byref(cache), 50, 4, 6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, None)
+    assert step(_dims(imp_bits=4), no_imp) == L.MIKV_ERR_NULL
+    assert step(_dims(imp_bits=4), no16) == L.MIKV_ERR_WORKSPACE  # checks pass up to the workspace
+    h2o = lambda dims, cache: lib.mikv_h2o_update_select(
+        C.byref(dims.c()), C.byref(cache), 50, 4, 6, FAKE, None, None, None, 0, None)
+    assert h2o(_dims(imp_bits=8), no_imp) == L.MIKV_ERR_NULL
 
 
 def test_decode_step_noalloc_validation(lib):

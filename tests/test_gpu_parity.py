@@ -48,7 +48,7 @@ def assert_close(gpu, ref, what, floor=0.0):
 
 def dims_of(cfg, capq=None):
     return L.Dims(batch=cfg.batch, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, group=cfg.G, bits=cfg.bits,
-                  cap16=cfg.cap16, capq=cfg.capq() if capq is None else capq)
+                  cap16=cfg.cap16, capq=cfg.capq() if capq is None else capq, imp_bits=cfg.imp_bits)
 
 
 # ---------------------------------------------------------------- quantize
@@ -143,10 +143,13 @@ def _state_equal(gpu, ref):
     for key in ("pos16", "free16", "posq"):
         assert np.array_equal(gpu[key], ref[key]), key
     assert np.array_equal(gpu["acc16"].view(np.uint32), ref["acc16"].view(np.uint32))
-    for key in ("k16", "v16", "ksz", "vsz"):
-        assert np.array_equal(bits16(gpu[key]), bits16(ref[key])), key
-    for key in ("kq", "vq"):
-        assert np.array_equal(gpu[key], ref[key]), key
+    # fp16 importance rows or importance codes, whichever the cache holds
+    for key in ("k16", "v16", "ksz", "vsz", "kimpsz", "vimpsz"):
+        if key in ref:
+            assert np.array_equal(bits16(gpu[key]), bits16(ref[key])), key
+    for key in ("kq", "vq", "kimp", "vimp"):
+        if key in ref:
+            assert np.array_equal(gpu[key], ref[key]), key
 
 
 @pytest.mark.parametrize("name,over,balanced", [
@@ -169,7 +172,7 @@ def test_prefill_build_parity(name, over, balanced):
         _, kb = O.balance(q, k)
     else:
         kb = k
-    ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq())
+    ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq(), imp_bits=cfg.imp_bits)
     _state_equal(cache.to_numpy(), ref)
 
 
@@ -180,8 +183,8 @@ def _units_state(cache, units):
     head each (the oracle treats every unit independently)."""
     ns = torch.tensor([u[0] for u in units], device="cuda")
     gs = torch.tensor([u[1] for u in units], device="cuda")
-    out = {k: getattr(cache, k)[ns, gs].unsqueeze(1).cpu().numpy() for k in L.Cache.NAMES}
-    out["group"], out["bits"] = cache.dims.group, cache.dims.bits
+    out = {k: getattr(cache, k)[ns, gs].unsqueeze(1).cpu().numpy() for k in cache.names}
+    out["group"], out["bits"], out["imp_bits"] = cache.dims.group, cache.dims.bits, cache.imp_bits
     return out
 
 
@@ -206,8 +209,9 @@ def _check_step(cfg, N, step, before, after, qd, kd, vd, bh, og, gp16, gdpos, mi
     ro, rp16, _, rst = O.decode_attention(before, N, qd, kd, vd, bh)
     if mid is not None:
         # separate calls: the attention call alone appends the new token
-        for key in ("k16", "v16"):
-            assert np.array_equal(bits16(mid[key]), bits16(rst[key])), key
+        for key in ("k16", "v16", "kimp", "vimp", "kimpsz", "vimpsz"):
+            if key in rst:
+                assert np.array_equal(np.asarray(mid[key]).view(np.uint8), np.asarray(rst[key]).view(np.uint8)), key
         assert np.array_equal(mid["pos16"], rst["pos16"])
     assert_close(og, ro, f"o step {step}")
     # probabilities below 2^-126 flush to 0 in fp32, fp64 keeps them
@@ -247,7 +251,7 @@ def _lockstep(cfg, seed, steps, balanced=True, check_every=1, fused=False, sampl
     bh = host(b)
     if gpu_scores:
         kb = O.balance(q, k)[1] if balanced else k
-        ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq())
+        ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq(), imp_bits=cfg.imp_bits)
         _state_equal(cache.to_numpy(), ref)
         print(f"  prefill build on the device's prompt scores matches the oracle", flush=True)
     del q, k, v
@@ -350,6 +354,60 @@ def test_prompt_scores_to_decode(name, over, steps):
     full = name == "llama2_7b_layer" and not over
     _lockstep(cfg, 1000 + list(S.CONFIGS).index(name), steps, fused=True, gpu_scores=True,
               check_every=steps if full else 1, sample=8 if full else 0)
+
+
+# ---------------------------------------------------------------- reduced-precision importance tier
+@pytest.mark.parametrize("name,over", [
+    ("tiny", dict(imp_bits=8, bits=2)), ("tiny", dict(imp_bits=4, bits=2)),
+    ("tiny", dict(imp_bits=8, bits=4, hq=4, hkv=2)), ("tiny", dict(imp_bits=4, bits=4, batch=64, T=700)),
+    ("gqa_throughput", dict(batch=2, T=700, imp_bits=8, bits=2)),
+    ("llama2_7b_layer", dict(batch=1, hq=4, hkv=4, T=900, imp_bits=4, bits=2)),
+])
+def test_prefill_build_importance_codes(name, over):
+    """Prefill build with the importance tier stored as 8- or 4-bit codes:
+    bit-exact against the oracle (importance and retained codes, scales,
+    positions, scores)."""
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"prefill (importance codes) {name} {over}", flush=True)
+    dims, cache, b, (q, k, v, acc0) = _prefill_gpu(cfg, 6, True)
+    _, kb = O.balance(q, k)
+    ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq(), imp_bits=cfg.imp_bits)
+    _state_equal(cache.to_numpy(), ref)
+
+
+@pytest.mark.parametrize("name,over,steps,fused", [
+    ("tiny", dict(imp_bits=8, bits=2), 12, False),
+    ("tiny", dict(imp_bits=4, bits=2), 12, True),
+    ("tiny", dict(imp_bits=8, bits=4, hq=4, hkv=2), 8, True),      # two-head tiles
+    ("tiny", dict(imp_bits=4, bits=2, hq=8, hkv=2), 8, False),     # four-head tiles
+    ("tiny", dict(imp_bits=8, bits=2, hq=8, hkv=1), 4, True),      # two tiles of four heads
+    ("tiny", dict(imp_bits=4, bits=4, recent=0), 6, True),
+    ("tiny", dict(imp_bits=8, bits=2, pct=0, recent=0), 4, True),  # B = 0: only the new token
+    ("gqa_throughput", dict(batch=3, T=600, imp_bits=8, bits=2), 4, True),
+    ("llama3_8b_32k", dict(hq=8, hkv=2, T=4100, imp_bits=4, bits=2), 3, True),
+    ("llama2_7b_layer", dict(batch=2, hq=3, hkv=3, T=1500, imp_bits=4, bits=2), 3, False),
+])
+def test_decode_lockstep_importance_codes(name, over, steps, fused):
+    """Decode steps with an 8- or 4-bit importance tier against the oracle,
+    every step: the new token quantized on append (exact codes), attention
+    over both code tiers (tolerance), scores, selection and the demoted
+    token re-quantized from its importance codes (exact)."""
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"lockstep (importance codes) {name} {over} steps={steps} fused={fused}", flush=True)
+    _lockstep(cfg, 17, steps, fused=fused)
+
+
+@pytest.mark.parametrize("name", ["llama2_7b_imp4", "llama2_7b_imp8"])
+def test_decode_importance_codes_full_size(name):
+    """The reduced-precision importance workloads at full size (8 x 32 heads,
+    4096 tokens, 20% importance at INT4 / INT8, INT2 retention) through
+    mikv_decode_step: 24 steps, all units at the first and last, 8 units at
+    the others."""
+    cfg = S.CONFIGS[name]
+    print(f"full-size lockstep {name}", flush=True)
+    _, checked, sampled = _lockstep(cfg, 1000 + list(S.CONFIGS).index(name), 24, check_every=23,
+                                    fused=True, sample=8)
+    assert checked + sampled == 24
 
 
 @pytest.mark.parametrize("name,check_every", [("llama2_7b_layer", 16), ("llama3_8b_32k", 8),

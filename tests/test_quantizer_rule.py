@@ -8,13 +8,15 @@ import numpy as np
 def test_divide_free_code_rule_matches_ieee_division():
     """The HIP quantizer finds rint(fl((x - z) / s)) as rint((x - z) * r) with
     r a reciprocal of s within 1 ulp, and falls back to the IEEE divide when
-    the product is within 2^-16 of a half-integer. Check that rule in float32
+    the product is within 2^-16 (2^-13 for 8-bit codes) of a half-integer.
+    Check that rule in float32
     over random fp16 groups (the oracle's step-3 setting, scale from the
     group's range) with r = the rounded reciprocal and its neighbours one ulp
     away: wherever the margin test passes, the code equals the divide's."""
     rng = np.random.default_rng(20260)
     checked = 0
-    for bits in (4, 2):
+    for bits in (8, 4, 2):
+        margin = np.float32(2.0 ** -13 if bits == 8 else 2.0 ** -16)
         qmax = np.float32((1 << bits) - 1)
         for scale in (1.0, 20.0, 1e-3):
             x = (rng.standard_normal((4000, 64)) * scale).astype(np.float16).astype(np.float32)
@@ -27,7 +29,7 @@ def test_divide_free_code_rule_matches_ieee_division():
             r0 = (np.float32(1.0) / s).astype(np.float32)
             for r in (r0, np.nextafter(r0, np.float32(np.inf)), np.nextafter(r0, np.float32(0))):
                 y = (a * r).astype(np.float32)
-                far = np.abs((y - np.floor(y)) - np.float32(0.5)) > np.float32(2.0 ** -16)
+                far = np.abs((y - np.floor(y)) - np.float32(0.5)) > margin
                 assert np.array_equal(np.rint(y)[far], ref[far])
                 checked += int(far.sum())
     assert checked > 1_000_000
