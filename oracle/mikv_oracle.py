@@ -57,6 +57,7 @@ __all__ = [
     "dequantize_rows", "dequantize_rows_f16", "top_by_key", "prefill_build", "decode_attention",
     "h2o_accumulate", "select_drop", "demote", "decode_step",
     "projected_value_l1", "criticalkv_select", "empty_state", "prefill_scores",
+    "output_perturbation",
 ]
 
 F16, F32, F64 = np.float16, np.float32, np.float64
@@ -540,3 +541,46 @@ def criticalkv_select(A, V, W_O, budget, alpha, norms=None, score2=None):
         sel2 = rest[top_by_key(score2[h, rest], rest, b2)]
         idx[h] = np.sort(np.concatenate([pos[s1[h]], sel2]))
     return idx, score2, s1
+
+
+# --------------------------------------------------------------------------
+# Output-perturbation diagnostic
+# --------------------------------------------------------------------------
+def output_perturbation(q, K, V, W_O, keep=None, o_hat=None):
+    """L = ||o - o_hat||_1 per head, in head space and after W_O,h (float64).
+
+    [gist CriticalKV] theoretical framework: the perturbation of replacing
+    the full cache by a selected part is the L1 distance between the
+    attention outputs, and its bound involves the attention weights and the
+    value states projected by W_O. Reading of this repository: o is the
+    head's softmax attention over all T tokens (scale 1/sqrt(d)); o_hat is
+    either the attention over the kept tokens `keep[h]` with the softmax
+    renormalized over them (an eviction: H2O, CriticalKV) or a given output
+    (a compressed cache such as MiKV's mixed precision); the projected
+    perturbation is ||(o - o_hat) W_O,h||_1 with W_O,h = rows h*d..h*d+d-1
+    of W_O [H*d, hidden].
+
+    q [H, d], K, V [H, T, d] (fp16 values), W_O [H*d, hidden]; keep: list of
+    index arrays or None; o_hat [H, d] or None. Returns (o [H, d],
+    o_hat [H, d], L_head [H], L_proj [H]).
+    """
+    H, T, d = K.shape
+    assert (keep is None) != (o_hat is None)
+    o = np.zeros((H, d), F64)
+    oh = np.zeros((H, d), F64)
+    L_head = np.zeros(H, F64)
+    L_proj = np.zeros(H, F64)
+    for h in range(H):
+        s = (K[h].astype(F64) @ q[h].astype(F64)) / np.sqrt(F64(d))
+        e = np.exp(s - s.max())
+        o[h] = (e / e.sum()) @ V[h].astype(F64)
+        if keep is not None:
+            sel = np.asarray(keep[h])
+            es = np.exp(s[sel] - s[sel].max())
+            oh[h] = (es / es.sum()) @ V[h, sel].astype(F64)
+        else:
+            oh[h] = np.asarray(o_hat[h], F64)
+        delta = o[h] - oh[h]
+        L_head[h] = np.abs(delta).sum()
+        L_proj[h] = np.abs(delta @ W_O[h * d:(h + 1) * d].astype(F64)).sum()
+    return o, oh, L_head, L_proj

@@ -692,3 +692,95 @@ def test_importance_tier_new_token_and_demotion_bounds():
             # rounding + one fp16 rounding of the rebuilt row
             span = np.repeat((rs * 3.0).reshape(-1, 1), 1, axis=0)
             assert np.all(np.abs(r - orig) <= 0.5 * rs + span / 255.0 + 1e-3 * np.abs(orig) + 1e-6), (step, name)
+
+
+# ---------------------------------------------------------------- output perturbation
+def _pert_inputs(seed, H=3, T=40, d=8, hidden=12):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((H, d)).astype(F16)
+    K = rng.standard_normal((H, T, d)).astype(F16)
+    V = rng.standard_normal((H, T, d)).astype(F16)
+    W = (rng.standard_normal((H * d, hidden)) * 0.3).astype(F16)
+    return q, K, V, W
+
+
+def test_perturbation_keep_all_and_single_token():
+    """Keeping every token leaves the output unchanged (L = 0); keeping one
+    token i makes the renormalised output exactly V_i, and o is the
+    textbook attention (float64 SDPA)."""
+    q, K, V, W = _pert_inputs(1)
+    H, T, d = K.shape
+    o, oh, Lh, Lp = O.output_perturbation(q, K, V, W, keep=[np.arange(T)] * H)
+    assert np.all(Lh == 0) and np.all(Lp == 0)
+    for h in range(H):
+        assert np.max(np.abs(o[h] - _sdpa(q[h].astype(F64), K[h].astype(F64), V[h].astype(F64)))) <= 1e-12
+    keep = [np.array([h * 5 + 2]) for h in range(H)]
+    o, oh, Lh, Lp = O.output_perturbation(q, K, V, W, keep=keep)
+    for h in range(H):
+        i = keep[h][0]
+        assert np.array_equal(oh[h], V[h, i].astype(F64))
+        assert abs(Lh[h] - np.abs(o[h] - V[h, i].astype(F64)).sum()) <= 1e-12
+
+
+def test_perturbation_projection_uses_the_heads_rows():
+    """W_O made of per-head blocks c_h * I: the projected perturbation of head
+    h is c_h times its head-space perturbation (a wrong row offset picks
+    another head's c)."""
+    q, K, V, _ = _pert_inputs(2, H=4, d=8)
+    H, T, d = K.shape
+    c = np.array([0.5, 2.0, 3.0, 0.25])
+    W = np.zeros((H * d, H * d), F16)
+    for h in range(H):
+        W[h * d:(h + 1) * d, h * d:(h + 1) * d] = np.eye(d) * c[h]
+    rng = np.random.default_rng(0)
+    keep = [np.sort(rng.choice(T, 7, replace=False)) for _ in range(H)]
+    _, _, Lh, Lp = O.output_perturbation(q, K, V, W, keep=keep)
+    assert np.allclose(Lp, c * Lh, rtol=1e-12, atol=0)
+    assert np.all(Lh > 0)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_perturbation_within_its_attention_value_bound(seed):
+    """The bound that ties the perturbation to A and V W_O: with u_i = V_i W_O,h,
+    A the softmax weights and Z = sum of A over the kept set S,
+      o - o_hat = sum_{i not in S} A_i u_i - (1/Z - 1) sum_{i in S} A_i u_i,
+    so ||o - o_hat||_1 <= sum_{i not in S} A_i ||u_i||_1 + (1/Z - 1) sum_{i in S} A_i ||u_i||_1
+    (triangle inequality; gist CriticalKV, theoretical framework). Also
+    identical value rows give no perturbation whatever is kept."""
+    q, K, V, W = _pert_inputs(10 + seed)
+    H, T, d = K.shape
+    rng = np.random.default_rng(seed)
+    keep = [np.sort(rng.choice(T, int(rng.integers(1, T)), replace=False)) for _ in range(H)]
+    _, _, _, Lp = O.output_perturbation(q, K, V, W, keep=keep)
+    for h in range(H):
+        s = (K[h].astype(F64) @ q[h].astype(F64)) / np.sqrt(d)
+        A = np.exp(s - s.max())
+        A /= A.sum()
+        un = np.abs(V[h].astype(F64) @ W[h * d:(h + 1) * d].astype(F64)).sum(axis=1)
+        S_ = np.zeros(T, bool)
+        S_[keep[h]] = True
+        Z = A[S_].sum()
+        theta = (A[~S_] * un[~S_]).sum() + (1 / Z - 1) * (A[S_] * un[S_]).sum()
+        assert Lp[h] <= theta * (1 + 1e-12)
+    Vc = np.repeat(V[:, :1], T, axis=1)
+    _, _, Lh, Lp = O.output_perturbation(q, K, Vc, W, keep=keep)
+    assert np.all(Lh <= 1e-12) and np.all(Lp <= 1e-12)
+
+
+def test_perturbation_of_a_given_output():
+    """With o_hat given (a compressed cache's output) L is its distance to
+    the full attention, e.g. 0 for the full attention itself."""
+    q, K, V, W = _pert_inputs(3)
+    o, _, _, _ = O.output_perturbation(q, K, V, W, keep=[np.arange(K.shape[1])] * K.shape[0])
+    _, oh, Lh, Lp = O.output_perturbation(q, K, V, W, o_hat=o)
+    assert np.array_equal(oh, o) and np.all(Lh == 0) and np.all(Lp == 0)
+    _, _, Lh2, _ = O.output_perturbation(q, K, V, W, o_hat=o + 0.5)
+    assert np.allclose(Lh2, 0.5 * K.shape[2], rtol=1e-12)
+    # the projection is taken before the absolute value: an offset (+t, -t,
+    # 0, ...) against an all-ones output column cancels exactly
+    H, _, d = K.shape
+    off = np.zeros((H, d))
+    off[:, 0], off[:, 1] = 0.25, -0.25
+    ones = np.ones((H * d, 1), F16)
+    _, _, Lh3, Lp3 = O.output_perturbation(q, K, V, ones, o_hat=o + off)
+    assert np.allclose(Lh3, 0.5, rtol=1e-12) and np.all(Lp3 <= 1e-12)
