@@ -331,6 +331,39 @@ mikv_status mikv_decode_step(const mikv_dims* dims, const mikv_cache* cache,
                              size_t ws_bytes, void* stream);
 
 /*
+ * Output-perturbation diagnostic ([gist CriticalKV] theoretical framework:
+ * replacing the full cache by a selected part perturbs the attention output
+ * by L = ||o - o_hat||_1, bounded through the attention weights and the
+ * value states projected by W_O). Per head h, with scale 1/sqrt(d):
+ *   o[h]     = softmax over all T tokens of K[h] . q[h], weighting V[h];
+ *   o_hat[h] = the same over the kept tokens keep[h][0..n_keep) with the
+ *              softmax renormalised over them (an eviction), or, when keep
+ *              is NULL, the caller's o_hat[h] (e.g. the output of
+ *              mikv_decode_attn on a mixed-precision cache of these tokens);
+ *   delta = o - o_hat; L_head[h] = ||delta||_1;
+ *   L_proj[h] = ||delta . W_O[h*d .. h*d+d-1][:]||_1 (the head's share of
+ *              the layer output, W_O laid out [H*d][hidden]).
+ * q [H][d], K, V [H][T][d] fp16, W_O [H*d][hidden] fp16, keep [H][n_keep]
+ * int32 (indices in [0, T), each at most once; others are ignored) or NULL,
+ * o_hat [H][d] fp32 or NULL: exactly one of keep and o_hat (inputs).
+ * o [H][d] fp32 or NULL, delta [H][d] fp32 or NULL, L_head [H], L_proj [H]
+ * fp32 (outputs). fp32 accumulation.
+ * ws: mikv_perturbation_workspace(H, T, d, hidden) bytes (any contents).
+ * Errors: keep and o_hat both or neither given, a required pointer NULL ->
+ * MIKV_ERR_NULL; d not 64 or 128 -> MIKV_ERR_UNSUPPORTED; H, T, hidden < 1,
+ * n_keep outside [1, T], q/K/V not 16-byte aligned, T*d*2 >= 2^31 ->
+ * MIKV_ERR_SHAPE; workspace too small -> MIKV_ERR_WORKSPACE.
+ */
+size_t mikv_perturbation_workspace(int32_t H, int32_t T, int32_t d, int32_t hidden);
+mikv_status mikv_output_perturbation(const uint16_t* q, const uint16_t* K,
+                                     const uint16_t* V, const uint16_t* W_O,
+                                     const int32_t* keep, int32_t n_keep,
+                                     const float* o_hat, int32_t H, int32_t T,
+                                     int32_t d, int32_t hidden, float* o,
+                                     float* delta, float* L_head, float* L_proj,
+                                     void* ws, size_t ws_bytes, void* stream);
+
+/*
  * mikv_decode_step for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, and harnesses that forbid
  * hipMalloc. Same computation, arguments, outputs and errors as

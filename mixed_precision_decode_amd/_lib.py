@@ -66,6 +66,9 @@ _SIGS = {
     "mikv_h2o_workspace": (_sz, [C.POINTER(MikvDims), _i32]),
     "mikv_h2o_update_select": (C.c_int, [C.POINTER(MikvDims), C.POINTER(MikvCache), _i32, _i32, _i32,
                                          _vp, C.POINTER(MikvPrefillSrc), _vp, _vp, _sz, _vp]),
+    "mikv_perturbation_workspace": (_sz, [_i32, _i32, _i32, _i32]),
+    "mikv_output_perturbation": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                           _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mikv_criticalkv_workspace": (_sz, [_i32, _i32, _i32, _i32]),
     "mikv_criticalkv_select": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f64, _vp, _vp,
                                          _vp, _sz, _vp]),
@@ -361,4 +364,25 @@ def mikv_criticalkv_select(A, V, W_O, budget: int, alpha: float, idx, score2=Non
         _ptr(W_O, "f16", (H * d, hidden), "W_O"), H, T, d, hidden, budget, float(alpha),
         _ptr(idx, _i32t(), (H, budget), "idx"),
         _ptr(score2, _f32t(), (H, T), "score2", optional=True),
+        _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def mikv_perturbation_workspace(H: int, T: int, d: int, hidden: int) -> int:
+    return lib().mikv_perturbation_workspace(H, T, d, hidden)
+
+
+def mikv_output_perturbation(q, K, V, W_O, L_head, L_proj, ws, keep=None, o_hat=None, o=None, delta=None,
+                             stream=None):
+    """L_head / L_proj [H] receive ||o - o_hat||_1 in head space and after
+    W_O,h; keep [H, n_keep] int32 (kept token indices) or o_hat [H, d]."""
+    H, T, d = K.shape
+    hidden = W_O.shape[1]
+    n_keep = 0 if keep is None else keep.shape[1]
+    _check(lib().mikv_output_perturbation(
+        _ptr(q, "f16", (H, d), "q"), _ptr(K, "f16", (H, T, d), "K"), _ptr(V, "f16", (H, T, d), "V"),
+        _ptr(W_O, "f16", (H * d, hidden), "W_O"),
+        _ptr(keep, _i32t(), (H, n_keep), "keep", optional=True), n_keep,
+        _ptr(o_hat, _f32t(), (H, d), "o_hat", optional=True), H, T, d, hidden,
+        _ptr(o, _f32t(), (H, d), "o", optional=True), _ptr(delta, _f32t(), (H, d), "delta", optional=True),
+        _ptr(L_head, _f32t(), (H,), "L_head"), _ptr(L_proj, _f32t(), (H,), "L_proj"),
         _ptr(ws, name="ws"), ws.numel() * ws.element_size(), _stream(stream)))

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmikv.so")
 
 SOURCES = ["api.cpp", "quantize.hip", "balance.hip", "decode_attn.hip", "h2o.hip", "criticalkv.hip",
-           "prefill_scores.hip", "read_probe.hip", "static_scratch.hip"]
+           "prefill_scores.hip", "read_probe.hip", "static_scratch.hip", "perturbation.hip"]
 
 
 def hipcc() -> str:

@@ -357,6 +357,31 @@ mikv_status mikv_h2o_update_select(const mikv_dims* m, const mikv_cache* c, int3
   return from_hip(launch_h2o_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+// ---------------------------------------------------------------- output perturbation
+size_t mikv_perturbation_workspace(int32_t H, int32_t T, int32_t d, int32_t hidden) {
+  if (H < 1 || T < 1 || (d != 64 && d != 128) || hidden < 1) return 0;
+  return perturbation_ws_bytes(H, T, d, hidden);
+}
+
+mikv_status mikv_output_perturbation(const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                                     const uint16_t* W_O, const int32_t* keep, int32_t n_keep,
+                                     const float* o_hat, int32_t H, int32_t T, int32_t d, int32_t hidden,
+                                     float* o, float* delta, float* L_head, float* L_proj, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  if (!q || !K || !V || !W_O || !L_head || !L_proj) return MIKV_ERR_NULL;
+  if ((keep == nullptr) == (o_hat == nullptr)) return MIKV_ERR_NULL;
+  if (H < 1 || T < 1 || hidden < 1) return MIKV_ERR_SHAPE;
+  if (d != 64 && d != 128) return MIKV_ERR_UNSUPPORTED;
+  if (keep && (n_keep < 1 || n_keep > T)) return MIKV_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(K) || !aligned16(V)) return MIKV_ERR_SHAPE;
+  // one head's rows are addressed with 32-bit byte offsets
+  if (static_cast<int64_t>(T) * d * 2 >= (int64_t{1} << 31)) return MIKV_ERR_SHAPE;
+  const size_t need = perturbation_ws_bytes(H, T, d, hidden);
+  if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
+  return from_hip(launch_perturbation(q, K, V, W_O, keep, n_keep, o_hat, H, T, d, hidden, o, delta, L_head,
+                                      L_proj, ws, static_cast<hipStream_t>(stream)));
+}
+
 // ---------------------------------------------------------------- CriticalKV
 size_t mikv_criticalkv_workspace(int32_t H, int32_t T, int32_t d, int32_t hidden) {
   if (H < 1 || T < 1 || d != 128 || hidden < 128 || hidden % 128 != 0) return 0;

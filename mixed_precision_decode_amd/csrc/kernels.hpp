@@ -109,6 +109,14 @@ hipError_t launch_prefill_scores(int batch, int hq, int hkv, int d, int T, const
 // Streaming-read probe (measurement): reads `bytes` (a multiple of 16) of p.
 hipError_t launch_read_probe(const void* p, size_t bytes, int blocks, uint32_t* sink, hipStream_t stream);
 
+// Output-perturbation diagnostic.
+int perturbation_splits(int H, int T);
+size_t perturbation_ws_bytes(int H, int T, int d, int hidden);
+hipError_t launch_perturbation(const uint16_t* q, const uint16_t* K, const uint16_t* V, const uint16_t* W,
+                               const int32_t* keep, int n_keep, const float* o_hat, int H, int T, int d,
+                               int hidden, float* o, float* delta_out, float* L_head, float* L_proj,
+                               void* ws, hipStream_t stream);
+
 size_t criticalkv_ws_bytes(int H, int T, int d, int hidden);
 hipError_t launch_criticalkv(const float* A, const uint16_t* V, const uint16_t* W, int H, int T,
                              int d, int hidden, int b1, int b2, int32_t* idx, float* score2,

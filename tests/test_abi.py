@@ -29,7 +29,7 @@ def _header_functions():
 
 def test_exports_every_declared_function(lib):
     names = _header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L._SIGS)
@@ -157,6 +157,23 @@ def test_importance_codes_validation(lib):
     h2o = lambda dims, cache: lib.mikv_h2o_update_select(
         C.byref(dims.c()), C.byref(cache), 50, 4, 6, FAKE, None, None, None, 0, None)
     assert h2o(_dims(imp_bits=8), no_imp) == L.MIKV_ERR_NULL
+
+
+def test_perturbation_validation(lib):
+    need = lib.mikv_perturbation_workspace(4, 100, 128, 256)
+    assert need > 0 and lib.mikv_perturbation_workspace(4, 100, 96, 256) == 0
+    call = lambda keep=FAKE, n_keep=5, o_hat=None, H=4, T=100, d=128, hidden=256, ws_bytes=need, q=FAKE: \
+        lib.mikv_output_perturbation(q, FAKE, FAKE, FAKE, keep, n_keep, o_hat, H, T, d, hidden, None, None,
+                                     FAKE, FAKE, FAKE, ws_bytes, None)
+    assert call(q=None) == L.MIKV_ERR_NULL
+    assert call(keep=None) == L.MIKV_ERR_NULL            # neither keep nor o_hat
+    assert call(o_hat=FAKE) == L.MIKV_ERR_NULL           # both
+    assert call(d=96) == L.MIKV_ERR_UNSUPPORTED
+    assert call(n_keep=0) == L.MIKV_ERR_SHAPE
+    assert call(n_keep=101) == L.MIKV_ERR_SHAPE
+    assert call(T=0) == L.MIKV_ERR_SHAPE
+    assert call(T=(1 << 23)) == L.MIKV_ERR_SHAPE         # T*d*2 >= 2^31
+    assert call(ws_bytes=8) == L.MIKV_ERR_WORKSPACE
 
 
 def test_decode_step_noalloc_validation(lib):
