@@ -41,7 +41,15 @@ design notes of the repository):
     per-token group quantizer; a new token is quantized as it is appended
     and attended to through its codes; a token leaving the tier is
     re-quantized for the retained tier from its codes rebuilt as an fp16
-    row (fp32 product, fp32 sum rounded to nearest even, then fp16).
+    row (fp32 product, fp32 sum rounded to nearest even, then fp16);
+  * per-channel key quantization (key_tile = 64): each retained key channel
+    gets its own (scale, zero) over a tile of 64 tokens, by the same
+    quantizer rule run along tokens; values stay per token. Demoted pairs
+    wait in an fp16 buffer until 64 have gathered, then the buffer becomes
+    one tile (keys per channel, values per token); buffered pairs are
+    attended to in fp16. At prefill the retained tokens fill tiles in
+    ascending position and the last (T-B) mod 64 of them start the buffer.
+    The importance tier stays fp16 in this mode.
 
 Parity unpinned (conventions of this repository, not fixed by the pages):
   the bit layout of packed codes, the rounding of the budget split, and the
@@ -57,7 +65,7 @@ __all__ = [
     "dequantize_rows", "dequantize_rows_f16", "top_by_key", "prefill_build", "decode_attention",
     "h2o_accumulate", "select_drop", "demote", "decode_step",
     "projected_value_l1", "criticalkv_select", "empty_state", "prefill_scores",
-    "output_perturbation",
+    "output_perturbation", "KEY_TILE", "quantize_channels", "dequantize_channels", "retained_counts",
 ]
 
 F16, F32, F64 = np.float16, np.float32, np.float64
@@ -206,6 +214,75 @@ def dequantize_rows_f16(packed: np.ndarray, sz: np.ndarray, group: int, bits: in
 
 
 # --------------------------------------------------------------------------
+# Per-channel key quantization over token tiles
+# --------------------------------------------------------------------------
+KEY_TILE = 64
+
+
+def quantize_channels(x: np.ndarray, bits: int):
+    """Per-channel asymmetric quantization of a tile of keys.
+
+    [velog notes] Alternative approach (per-channel quantization) and its
+    appendix C summary; [paperlayer] appendix C: keys may instead be
+    quantized per channel, which isolates outlier channels, with groups of
+    64 along the tokens. The rule is the per-token quantizer's (quantize_rows)
+    applied to each channel's column of the tile: every channel c gets
+    s_c = fp16((max - min) / (2^bits - 1)) and z_c = min over the t tokens.
+
+    x: [t, d] fp16 (one tile). Returns packed codes [t, d*bits/8] in the
+    per-token byte layout (token-major, channels packed within a row) and
+    sz [d, 2] fp16 holding (scale, zero) per channel.
+    """
+    t, d = x.shape
+    packed_c, sz = quantize_rows(np.ascontiguousarray(x.T), t, bits)   # rows = channels
+    codes = unpack_codes(packed_c, t, bits).T                            # [t, d]
+    return pack_codes(np.ascontiguousarray(codes), bits), sz[:, 0, :].copy()
+
+
+def dequantize_channels(packed: np.ndarray, sz: np.ndarray, bits: int) -> np.ndarray:
+    """code * scale_c + zero_c of a tile, float64 [t, d]."""
+    d = sz.shape[0]
+    c = unpack_codes(packed, d, bits).astype(F64)
+    return c * sz[:, 0].astype(F64)[None, :] + sz[:, 1].astype(F64)[None, :]
+
+
+def retained_counts(st, D):
+    """(tokens in full tiles, tokens in the buffer) of a per-channel cache
+    whose retained tier has taken D tokens; (D, 0) for per-token keys."""
+    kt = st.get("key_tile", 0)
+    if not kt:
+        return D, 0
+    return kt * (D // kt), D % kt
+
+
+def _put_tile(st, i, g, j, krows, vrows, pos):
+    """Quantize a full tile of retained pairs into tile j: keys per channel,
+    values per token (group d/2 like every value row)."""
+    kt, bits, group = st["key_tile"], st["bits"], st["group"]
+    sl = slice(j * kt, (j + 1) * kt)
+    st["kq"][i, g, sl], st["kcsz"][i, g, j] = quantize_channels(krows, bits)
+    st["vq"][i, g, sl], st["vsz"][i, g, sl] = quantize_rows(vrows, group, bits)
+    st["posq"][i, g, sl] = pos
+
+
+def _retained_kv(st, i, g, D):
+    """Keys and values (float64) of the retained tokens of unit (i, g), in
+    the order they left the importance tier: the low-bit slots, then (per-
+    channel keys) the buffered pairs."""
+    group, bits = st["group"], st["bits"]
+    nq, nb = retained_counts(st, D)
+    if not st.get("key_tile", 0):
+        return (dequantize_rows(st["kq"][i, g, :nq], st["ksz"][i, g, :nq], group, bits),
+                dequantize_rows(st["vq"][i, g, :nq], st["vsz"][i, g, :nq], group, bits))
+    kt = st["key_tile"]
+    K = [dequantize_channels(st["kq"][i, g, j * kt:(j + 1) * kt], st["kcsz"][i, g, j], bits)
+         for j in range(nq // kt)]
+    K.append(st["kbuf"][i, g, :nb].astype(F64))
+    V = dequantize_rows(st["vq"][i, g, :nq], st["vsz"][i, g, :nq], group, bits)
+    return np.concatenate(K), np.concatenate([V, st["vbuf"][i, g, :nb].astype(F64)])
+
+
+# --------------------------------------------------------------------------
 # Importance ranking (H2O heavy hitters)
 # --------------------------------------------------------------------------
 def top_by_key(score: np.ndarray, pos: np.ndarray, m: int) -> np.ndarray:
@@ -220,24 +297,37 @@ def top_by_key(score: np.ndarray, pos: np.ndarray, m: int) -> np.ndarray:
     return order[:m]
 
 
-def empty_state(batch, hkv, d, cap16, capq, group, bits, imp_bits=16):
+def empty_state(batch, hkv, d, cap16, capq, group, bits, imp_bits=16, key_tile=0):
     """Zeroed cache in the layout of the C interface (see include/mikv.h).
 
     imp_bits = 16: the importance tier holds fp16 rows (k16, v16). imp_bits
     in (8, 4): it holds codes and (scale, zero) like the retained tier
     (kimp, vimp, kimpsz, vimpsz), the reduced-precision importance cache of
-    [velog notes] Key contributions 3) and [paperlayer] section 3.3."""
+    [velog notes] Key contributions 3) and [paperlayer] section 3.3.
+
+    key_tile = 64: retained keys are quantized per channel over tiles of 64
+    tokens (kcsz [n, hkv, capq/64, d, 2] in place of ksz), with an fp16
+    buffer (kbuf, vbuf [n, hkv, 64, d], posbuf) for pairs that wait for a
+    tile to fill ([velog notes] appendix C summary: a temporary buffer,
+    kept apart from the important pairs)."""
     cb = d * bits // 8
     st = dict(
         pos16=np.full((batch, hkv, cap16), -1, np.int32),
         acc16=np.zeros((batch, hkv, cap16), F32),
         free16=np.zeros((batch, hkv), np.int32),
         kq=np.zeros((batch, hkv, capq, cb), np.uint8), vq=np.zeros((batch, hkv, capq, cb), np.uint8),
-        ksz=np.zeros((batch, hkv, capq, d // group, 2), F16),
         vsz=np.zeros((batch, hkv, capq, d // group, 2), F16),
         posq=np.full((batch, hkv, capq), -1, np.int32),
-        group=group, bits=bits, imp_bits=imp_bits,
+        group=group, bits=bits, imp_bits=imp_bits, key_tile=key_tile,
     )
+    if key_tile:
+        assert key_tile == KEY_TILE and capq % key_tile == 0 and imp_bits == 16
+        st["kcsz"] = np.zeros((batch, hkv, capq // key_tile, d, 2), F16)
+        st["kbuf"] = np.zeros((batch, hkv, key_tile, d), F16)
+        st["vbuf"] = np.zeros((batch, hkv, key_tile, d), F16)
+        st["posbuf"] = np.full((batch, hkv, key_tile), -1, np.int32)
+    else:
+        st["ksz"] = np.zeros((batch, hkv, capq, d // group, 2), F16)
     if imp_bits == 16:
         st["k16"] = np.zeros((batch, hkv, cap16, d), F16)
         st["v16"] = np.zeros((batch, hkv, cap16, d), F16)
@@ -297,7 +387,7 @@ def _imp_rows16(st, i, g, s):
             dequantize_rows_f16(st["vimp"][i, g, s:s + 1], st["vimpsz"][i, g, s:s + 1], grp, ib))
 
 
-def prefill_build(kb, v, acc0, B, R, group, bits, capq, imp_bits=16):
+def prefill_build(kb, v, acc0, B, R, group, bits, capq, imp_bits=16, key_tile=0):
     """Initial two-tier cache after the prompt.
 
     [velog notes] one-line summary and Key contributions 1): tokens an
@@ -312,11 +402,13 @@ def prefill_build(kb, v, acc0, B, R, group, bits, capq, imp_bits=16):
 
     kb, v: [n, hkv, T, d] fp16 (balanced keys, values); acc0 [n, hkv, T] fp32.
     imp_bits < 16: the important rows are stored as imp_bits codes.
+    key_tile = 64: the retained tokens fill per-channel key tiles in
+    ascending position; the last (T-B) mod 64 of them go to the buffer.
     """
     n, hkv, T, d = kb.shape
     H = B - R
     assert 0 <= R <= B <= T and T - B <= capq
-    st = empty_state(n, hkv, d, B + 1, capq, group, bits, imp_bits)
+    st = empty_state(n, hkv, d, B + 1, capq, group, bits, imp_bits, key_tile)
     pos_all = np.arange(T, dtype=np.int64)
     for i in range(n):
         for g in range(hkv):
@@ -331,6 +423,15 @@ def prefill_build(kb, v, acc0, B, R, group, bits, capq, imp_bits=16):
             st["pos16"][i, g, :B] = kp
             st["acc16"][i, g, :B] = acc0[i, g, kp]
             st["free16"][i, g] = B
+            if key_tile:
+                nq, nb = retained_counts(st, len(rp))
+                for j in range(nq // key_tile):
+                    tp = rp[j * key_tile:(j + 1) * key_tile]
+                    _put_tile(st, i, g, j, kb[i, g, tp], v[i, g, tp], tp)
+                st["kbuf"][i, g, :nb] = kb[i, g, rp[nq:]]
+                st["vbuf"][i, g, :nb] = v[i, g, rp[nq:]]
+                st["posbuf"][i, g, :nb] = rp[nq:]
+                continue
             ck, sk = quantize_rows(kb[i, g, rp], group, bits)
             cv, sv = quantize_rows(v[i, g, rp], group, bits)
             m = len(rp)
@@ -354,14 +455,15 @@ def decode_attention(state, N, q, k_new, v_new, b):
     reduced-precision importance tier the new token is stored as codes and
     attended to through them, like every other importance-tier token.
     Scores use scale 1/sqrt(d); the new token attends to every cached token
-    and to itself.
+    and to itself. With per-channel keys the retained tokens are the full
+    tiles (keys code * scale_c + zero_c) and the buffered fp16 pairs.
 
-    state: cache dict (see empty_state) before the step; the low-bit tier
+    state: cache dict (see empty_state) before the step; the retained tier
     holds N - cap16 tokens and slot free16 of the FP16 tier is free.
     q [n, hq, d], k_new/v_new [n, hkv, d] fp16; b [n, hkv, d] fp32.
     Returns (o [n,hq,d] f64, p16 [n,hkv,cap16] f64 summed over the group's
-    query heads, pq [n,hkv,N-cap16] f64 likewise for the low-bit tier,
-    appended state).
+    query heads, pq [n,hkv,N-cap16] f64 likewise for the retained tokens in
+    the order they were demoted, appended state).
     """
     st = {kk: (vv.copy() if isinstance(vv, np.ndarray) else vv) for kk, vv in state.items()}
     group, bits = st["group"], st["bits"]
@@ -381,8 +483,9 @@ def decode_attention(state, N, q, k_new, v_new, b):
             st["pos16"][i, g, s] = N - 1
             st["acc16"][i, g, s] = 0.0
             Ki, Vi = _imp_kv(st, i, g)
-            K = np.concatenate([Ki, dequantize_rows(st["kq"][i, g, :nq], st["ksz"][i, g, :nq], group, bits)])
-            V = np.concatenate([Vi, dequantize_rows(st["vq"][i, g, :nq], st["vsz"][i, g, :nq], group, bits)])
+            Kr, Vr = _retained_kv(st, i, g, nq)
+            K = np.concatenate([Ki, Kr])
+            V = np.concatenate([Vi, Vr])
             for r in range(rep):
                 h = g * rep + r
                 qh = q[i, h].astype(F64) / b[i, g].astype(F64)
@@ -456,16 +559,28 @@ def demote(state, N, drop):
     [velog notes] Key contributions 1): tokens leaving the important set are
     kept as low-bit codes instead of being discarded. From a reduced-precision
     importance tier the row re-quantized is its codes rebuilt in fp16
-    (dequantize_rows_f16).
+    (dequantize_rows_f16). With per-channel keys the pair goes to buffer row
+    (N - cap16) mod 64 instead; the pair that fills the buffer turns it into
+    tile (N - cap16) // 64 ([velog notes] appendix C summary: pairs wait in
+    a temporary buffer until enough have gathered, then are quantized).
     """
     st = {kk: (vv.copy() if isinstance(vv, np.ndarray) else vv) for kk, vv in state.items()}
     group, bits = st["group"], st["bits"]
     n, hkv, cap16, d = _shape(st)
     slot = N - cap16
+    kt = st.get("key_tile", 0)
     for i in range(n):
         for g in range(hkv):
             s = int(drop[i, g])
             krow, vrow = _imp_rows16(st, i, g, s)
+            if kt:
+                r = slot % kt
+                st["kbuf"][i, g, r], st["vbuf"][i, g, r] = krow[0], vrow[0]
+                st["posbuf"][i, g, r] = st["pos16"][i, g, s]
+                if r == kt - 1:
+                    _put_tile(st, i, g, slot // kt, st["kbuf"][i, g], st["vbuf"][i, g], st["posbuf"][i, g])
+                st["free16"][i, g] = s
+                continue
             ck, sk = quantize_rows(krow, group, bits)
             cv, sv = quantize_rows(vrow, group, bits)
             st["kq"][i, g, slot], st["ksz"][i, g, slot] = ck[0], sk[0]

@@ -784,3 +784,199 @@ def test_perturbation_of_a_given_output():
     ones = np.ones((H * d, 1), F16)
     _, _, Lh3, Lp3 = O.output_perturbation(q, K, V, ones, o_hat=o + off)
     assert np.allclose(Lh3, 0.5, rtol=1e-12) and np.all(Lp3 <= 1e-12)
+
+
+# ------------------------------------------------ per-channel key quantization
+def _channel_grid_tile(rng, t, d, bits):
+    """A tile whose every channel c is z_c + s_c * code with integer codes in
+    [0, 2^bits - 1], 0 and 2^bits - 1 both present, s_c a power of two that
+    differs widely between channels (outlier channels have large s_c) and z_c
+    a multiple of s_c. Returns (x fp16, codes, s, z)."""
+    qmax = (1 << bits) - 1
+    e = rng.integers(-6, 4, d)
+    e[[1, d // 2 + 3]] = 6                    # two outlier channels
+    s = 2.0 ** e
+    z = rng.integers(-8, 9, d) * s
+    c = rng.integers(0, qmax + 1, (t, d))
+    for ch in range(d):
+        r0, r1 = rng.choice(t, 2, replace=False)
+        c[r0, ch], c[r1, ch] = 0, qmax
+    x = z[None, :] + c * s[None, :]
+    assert np.array_equal(x.astype(F16).astype(F64), x)
+    return x.astype(F16), c, s, z
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("d", [16, 128])
+def test_channel_quantizer_lossless_grid(bits, d):
+    """[velog notes] appendix C summary and [paperlayer] appendix C: keys
+    quantized per channel over groups of 64 tokens. A tile built from known
+    per-channel (scale, zero, codes) comes back exactly: each channel gets its
+    own scale and zero (a per-token group, or channels mixed up, would not:
+    the scales differ by up to 2^12 between channels)."""
+    rng = np.random.default_rng(100 + bits + d)
+    x, c, s, z = _channel_grid_tile(rng, O.KEY_TILE, d, bits)
+    packed, sz = O.quantize_channels(x, bits)
+    assert packed.shape == (O.KEY_TILE, d * bits // 8) and sz.shape == (d, 2)
+    assert np.array_equal(O.unpack_codes(packed, d, bits), c)
+    assert np.array_equal(sz[:, 0].astype(F64), s) and np.array_equal(sz[:, 1].astype(F64), z)
+    assert np.array_equal(O.dequantize_channels(packed, sz, bits), x.astype(F64))
+    # the per-token rule on the same tile is lossy: the pin tells them apart
+    pt, szt = O.quantize_rows(x, d // 2, bits)
+    assert not np.array_equal(O.dequantize_rows(pt, szt, d // 2, bits), x.astype(F64))
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_channel_quantizer_bound_and_outlier_isolation(bits):
+    """Random tile with two outlier channels (x20, the synthetic outlier
+    factor): every element is within s_c/2 of its channel's grid (plus the
+    clamp term when the fp16 scale rounds down), and on the ordinary channels
+    the per-channel error stays far below the per-token (group d/2) error,
+    the isolation of outliers the appendix C summary credits it with."""
+    rng = np.random.default_rng(7 + bits)
+    t, d = O.KEY_TILE, 128
+    x = rng.standard_normal((t, d))
+    out = [5, 77]
+    x[:, out] *= 20
+    x = x.astype(F16)
+    packed, sz = O.quantize_channels(x, bits)
+    xr = O.dequantize_channels(packed, sz, bits)
+    qmax = (1 << bits) - 1
+    x64 = x.astype(F64)
+    s = sz[:, 0].astype(F64)
+    s_true = (x64.max(axis=0) - x64.min(axis=0)) / qmax
+    bound = 0.5 * s + qmax * np.maximum(0.0, s_true - s) + 1e-6 * (np.abs(x64).max(axis=0) + s)
+    err = np.abs(xr - x64)
+    assert np.all(err <= bound[None, :])
+    assert np.array_equal(O.unpack_codes(packed, d, bits)[x64.argmin(axis=0), np.arange(d)], np.zeros(d))
+    pt, szt = O.quantize_rows(x, d // 2, bits)
+    err_tok = np.abs(O.dequantize_rows(pt, szt, d // 2, bits) - x64)
+    ordinary = np.setdiff1d(np.arange(d), out)
+    assert err[:, ordinary].max() < 0.25 * err_tok[:, ordinary].max()
+
+
+def _two_level_keys(rng, n, hkv, ntok, d, G, bits):
+    """Keys whose every group j of G channels takes, in every token, only the
+    values z_j and z_j + qmax * s_j (s_j a power of two): both the per-token
+    group quantizer and the per-channel tile quantizer hold them exactly,
+    whichever tokens share a tile (one level present: scale 0, zero = that
+    level; both: scale s_j, codes 0 and qmax)."""
+    qmax = (1 << bits) - 1
+    s = 2.0 ** rng.integers(-4, 2, (n, hkv, 1, d // G, 1))
+    z = rng.integers(-4, 5, (n, hkv, 1, d // G, 1)) * s
+    hi = rng.random((n, hkv, ntok, d // G, G)) < 0.5
+    return (z + hi * qmax * s).reshape(n, hkv, ntok, d).astype(F16)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_key_tiles_on_lossless_keys_equal_per_token_cache(bits):
+    """Per-channel key tiles with the fp16 buffer, on keys both quantizers hold
+    exactly and values on the per-token grid: every decode step (output,
+    probabilities, accumulated scores, selections) is bit-identical to the
+    per-token cache's, which the pins above tie to the pages; the retained
+    positions in tile order then buffer order are the per-token cache's slot
+    order (demotion order), and the tiles' value codes are its rows. The
+    prompt leaves 130 = 2*64 + 2 retained tokens, so the buffer starts with
+    two pairs and fills (one tile flushed) at the 62nd step."""
+    rng = np.random.default_rng(40 + bits)
+    n, hkv, rep, d, G, T, B, R, steps = 1, 2, 2, 16, 8, 150, 20, 4, 70
+    ntok = T + steps
+    k = _two_level_keys(rng, n, hkv, ntok, d, G, bits)
+    v = np.stack([np.stack([_grid_rows(rng, ntok, d, G, bits) for _ in range(hkv)]) for _ in range(n)])
+    q = (rng.standard_normal((steps, n, hkv * rep, d)) * 0.3).astype(F16)
+    acc0 = (rng.integers(1, 6, (n, hkv, T)) * 0.125).astype(F32)
+    b = np.ones((n, hkv, d), F32)
+    capq = 256
+    ref = O.prefill_build(k[:, :, :T], v[:, :, :T], acc0, B, R, G, bits, capq)
+    kt = O.prefill_build(k[:, :, :T], v[:, :, :T], acc0, B, R, G, bits, capq, key_tile=O.KEY_TILE)
+    flushed = False
+    for j in range(steps):
+        N = T + j + 1
+        kd, vd = k[:, :, N - 1], v[:, :, N - 1]
+        o1, p1, ref, d1 = O.decode_step(ref, N, q[j], kd, vd, b, R, B - R)
+        o2, p2, kt, d2 = O.decode_step(kt, N, q[j], kd, vd, b, R, B - R)
+        assert np.array_equal(o1, o2) and np.array_equal(p1, p2)
+        assert np.array_equal(d1, d2)
+        for key in ("acc16", "pos16", "free16"):
+            assert np.array_equal(ref[key], kt[key]), key
+        D = N - B                                  # retained after this step
+        nq, nb = O.retained_counts(kt, D)
+        assert nq + nb == D and nb == (T - B + j + 1) % 64
+        flushed |= nq == 192
+        for i in range(n):
+            for g in range(hkv):
+                order = np.concatenate([kt["posq"][i, g, :nq], kt["posbuf"][i, g, :nb]])
+                assert np.array_equal(order, ref["posq"][i, g, :D])
+                assert np.array_equal(kt["vq"][i, g, :nq], ref["vq"][i, g, :nq])
+                assert np.array_equal(kt["vsz"][i, g, :nq].view(np.uint16), ref["vsz"][i, g, :nq].view(np.uint16))
+    assert flushed
+
+
+def test_key_tiles_hold_the_history_rows():
+    """Random balanced keys (outlier channels) through prefill and 75 decode
+    steps with per-channel tiles: after every step the importance tier, the
+    tiles and the buffer partition positions 0..N-1; the retained positions
+    in tile then buffer order are the prompt's retained positions ascending
+    followed by the decode steps' dropped positions in the order dropped;
+    every tile is the per-channel quantization of its 64 positions' balanced
+    keys (values per token) taken from the token history, and the buffer
+    holds those rows in fp16. The step's attention output is softmax
+    attention over exactly those keys and values (scaled-dot-product
+    attention in float64)."""
+    cfg = S.CONFIGS["tiny"].scaled(hq=2, hkv=1, T=120, pct=20, recent=4, bits=4)
+    q, k, v, acc0 = S.prefill_tensors(cfg, 31)
+    b, kb = O.balance(q, k)
+    steps, KT, d = 75, O.KEY_TILE, cfg.d
+    capq = 192
+    st = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, capq, key_tile=KT)
+    hist_k = [kb[0, 0, t] for t in range(cfg.T)]
+    hist_v = [v[0, 0, t] for t in range(cfg.T)]
+    keep = set(st["pos16"][0, 0, :cfg.B].tolist())
+    order = [t for t in range(cfg.T) if t not in keep]
+    for j in range(steps):
+        N = cfg.T + j + 1
+        qd, kd, vd = S.decode_tensors(cfg, 31, j)
+        hist_k.append(O.balance_keys(kd[0, 0], b[0, 0]))
+        hist_v.append(vd[0, 0])
+        before = st
+        o, _, st, drop = O.decode_step(st, N, qd, kd, vd, b, cfg.recent, cfg.H)
+        # the attention of this step, from the cache before it and the history
+        nq, nb = O.retained_counts(before, N - cfg.B - 1)
+        Kl, Vl = [], []
+        held = np.arange(cfg.cap16) != before["free16"][0, 0]      # the free slot is stale
+        for t in list(before["pos16"][0, 0][held]) + [N - 1]:
+            Kl.append(hist_k[t].astype(F64))
+            Vl.append(hist_v[t].astype(F64))
+        for tj in range(nq // KT):
+            tp = before["posq"][0, 0, tj * KT:(tj + 1) * KT]
+            pk, szk = O.quantize_channels(np.stack([hist_k[t] for t in tp]), cfg.bits)
+            Kl.extend(O.dequantize_channels(pk, szk, cfg.bits))
+            pv, szv = O.quantize_rows(np.stack([hist_v[t] for t in tp]), cfg.G, cfg.bits)
+            Vl.extend(O.dequantize_rows(pv, szv, cfg.G, cfg.bits))
+        for t in before["posbuf"][0, 0, :nb]:
+            Kl.append(hist_k[t].astype(F64))
+            Vl.append(hist_v[t].astype(F64))
+        assert len(Kl) == N
+        for h in range(cfg.hq):
+            qh = qd[0, h].astype(F64) / b[0, 0].astype(F64)
+            ref = _sdpa(qh, np.stack(Kl), np.stack(Vl))
+            assert np.max(np.abs(o[0, h] - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+        order.append(int(before["pos16"][0, 0, drop[0, 0]]) if drop[0, 0] != before["free16"][0, 0]
+                     else N - 1)
+        D = N - cfg.B
+        nq, nb = O.retained_counts(st, D)
+        got = np.concatenate([st["posq"][0, 0, :nq], st["posbuf"][0, 0, :nb]])
+        assert np.array_equal(got, np.array(order))
+        imp = st["pos16"][0, 0][np.arange(cfg.cap16) != st["free16"][0, 0]]
+        assert np.array_equal(np.sort(np.concatenate([imp, got])), np.arange(N))
+        for tj in range(nq // KT):
+            tp = st["posq"][0, 0, tj * KT:(tj + 1) * KT]
+            pk, szk = O.quantize_channels(np.stack([hist_k[t] for t in tp]), cfg.bits)
+            assert np.array_equal(st["kq"][0, 0, tj * KT:(tj + 1) * KT], pk)
+            assert np.array_equal(st["kcsz"][0, 0, tj].view(np.uint16), szk.view(np.uint16))
+            pv, szv = O.quantize_rows(np.stack([hist_v[t] for t in tp]), cfg.G, cfg.bits)
+            assert np.array_equal(st["vq"][0, 0, tj * KT:(tj + 1) * KT], pv)
+        for r, t in enumerate(st["posbuf"][0, 0, :nb]):
+            assert np.array_equal(st["kbuf"][0, 0, r].view(np.uint16), hist_k[t].view(np.uint16))
+            assert np.array_equal(st["vbuf"][0, 0, r].view(np.uint16), hist_v[t].view(np.uint16))
+    assert O.retained_counts(st, cfg.T + steps - cfg.B)[0] >= 2 * KT
