@@ -96,15 +96,28 @@ def imp_row_bytes(cfg):
     return 2 * (cfg.d * cfg.imp_bits // 8 + 4 * (cfg.d // cfg.G))
 
 
+def retained_bytes(cfg, nr):
+    """Bytes of nr retained tokens, keys and values. Per-token keys: codes
+    plus an fp16 (scale, zero) per group, K and V. Per-channel key tiles:
+    the whole tiles' key codes plus an fp16 (scale, zero) per channel and
+    tile, value codes with their per-token groups, and the buffered pairs as
+    fp16 rows."""
+    d, G = cfg.d, cfg.G
+    cb, vsz = d * cfg.bits // 8, 4 * (d // G)
+    if not cfg.key_tile:
+        return nr * 2 * (cb + vsz)
+    nq, nb = nr // cfg.key_tile * cfg.key_tile, nr % cfg.key_tile
+    return nq * (2 * cb + vsz) + (nq // cfg.key_tile) * 4 * d + nb * 4 * d
+
+
 def attn_bytes(cfg, N):
     """Algorithmic bytes of one decode-attention launch at length N (new
     token included): importance-tier rows read (cap16-1), the new token read
-    (k_new, v_new) and appended, low-bit rows (codes + fp16 scale/zero per
-    group, K and V), q, b, o and p16."""
-    d, G = cfg.d, cfg.G
-    nq = N - cfg.cap16
+    (k_new, v_new) and appended, the retained tokens (retained_bytes), q, b,
+    o and p16."""
+    d = cfg.d
     per_unit = ((cfg.cap16 - 1) * imp_row_bytes(cfg) + 4 * d + imp_row_bytes(cfg)
-                + nq * 2 * (d * cfg.bits // 8 + 4 * (d // G))
+                + retained_bytes(cfg, N - cfg.cap16)
                 + cfg.rep * d * 2 + d * 4 + cfg.rep * d * 4 + cfg.cap16 * 4)
     return per_unit * cfg.batch * cfg.hkv
 
@@ -117,9 +130,15 @@ def split_bytes(cfg, N):
 
 def h2o_bytes(cfg):
     """acc16 read+write, p16 and pos16 read per importance slot; the demoted
-    K/V rows read and written as codes."""
+    K/V rows read and written as codes (per-channel key tiles: written to the
+    buffer as fp16 rows, and one step in 64 the buffer read and written back
+    as a tile, counted here as its 1/64 share)."""
     d = cfg.d
-    per_unit = cfg.cap16 * 16 + imp_row_bytes(cfg) + 2 * (d * cfg.bits // 8 + 4 * (d // cfg.G)) + 16
+    if cfg.key_tile:
+        tile = cfg.key_tile * 4 * d + retained_bytes(cfg, cfg.key_tile)
+        per_unit = cfg.cap16 * 16 + 8 * d + 16 + tile / cfg.key_tile
+    else:
+        per_unit = cfg.cap16 * 16 + imp_row_bytes(cfg) + 2 * (d * cfg.bits // 8 + 4 * (d // cfg.G)) + 16
     return per_unit * cfg.batch * cfg.hkv
 
 
@@ -171,8 +190,14 @@ def cpu_baseline(cfg, before, b_np, N, q_np, k_np, v_np, gpu, budget_s):
     dem = O.demote(mid, N, drop_dev)
     slot = N - cfg.cap16
     raw = lambda a: np.ascontiguousarray(np.asarray(a)[:, :, slot]).view(np.uint8)
-    codes_ok = all(np.array_equal(raw(gpu["after"][key]), raw(dem[key]))
-                   for key in ("kq", "vq", "ksz", "vsz", "posq"))
+    if cfg.key_tile:
+        # the demoted pair's buffer row, and the tile when it filled the buffer
+        full = lambda a: np.ascontiguousarray(np.asarray(a)).view(np.uint8)
+        codes_ok = all(np.array_equal(full(gpu["after"][key]), full(dem[key]))
+                       for key in ("kbuf", "vbuf", "posbuf", "kq", "vq", "kcsz", "vsz", "posq"))
+    else:
+        codes_ok = all(np.array_equal(raw(gpu["after"][key]), raw(dem[key]))
+                       for key in ("kq", "vq", "ksz", "vsz", "posq"))
     parity = {"units": f"sequence 0, {cfg.hkv} kv heads, step N={N}",
               "o_max_err_rel": o_err, "acc_max_err_rel": acc_err, "tolerance": tol,
               "selection_on_device_scores_exact": sel_ok, "demoted_codes_exact": bool(codes_ok),
@@ -541,7 +566,8 @@ def decode_run(cfg, args, log, K, W, KA, cpu_seconds):
     t0 = time.perf_counter()
     q, k, v, acc0 = S.prefill_tensors(cfg, args.seed)
     dims = L.Dims(batch=cfg.batch, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, group=cfg.G, bits=cfg.bits,
-                  cap16=cfg.cap16, capq=cfg.T - cfg.B + total, imp_bits=cfg.imp_bits)
+                  cap16=cfg.cap16, capq=cfg.scaled(steps=total).capq(), imp_bits=cfg.imp_bits,
+                  key_tile=cfg.key_tile)
     cache = L.Cache(dims)
     b = torch.empty((cfg.batch, cfg.hkv, cfg.d), dtype=torch.float32, device="cuda")
     qg, kg = dev(q), dev(k)
@@ -642,6 +668,7 @@ def decode_run(cfg, args, log, K, W, KA, cpu_seconds):
         # state (sequence 0) and compares
         before = {kk: getattr(cache, kk)[:1].cpu().numpy() for kk in cache.names}
         before["group"], before["bits"], before["imp_bits"] = cfg.G, cfg.bits, cache.imp_bits
+        before["key_tile"] = cache.key_tile
         N += 1
         step_call(s_next, N)
         after = {kk: getattr(cache, kk)[:1].cpu().numpy() for kk in cache.names}
@@ -658,7 +685,7 @@ def decode_run(cfg, args, log, K, W, KA, cpu_seconds):
         "ms_per_step_median": float(np.median(step_ms)), "steps": K, "warmup": W,
         "config": {"workload": cfg.name, "batch": cfg.batch, "q_heads": cfg.hq, "kv_heads": cfg.hkv,
                    "head_dim": cfg.d, "context": cfg.T, "low_bits": cfg.bits,
-                   "importance_bits": cfg.imp_bits,
+                   "importance_bits": cfg.imp_bits, "key_tile": cfg.key_tile,
                    "important_pct": cfg.pct, "recent": cfg.recent, "group": cfg.G,
                    "cache_flush_per_step": args.flush,
                    "step_launch": "hip_graph" if args.graph else "eager"},
@@ -747,7 +774,7 @@ def main():
     head = decode_run(cfg, args, log, K, W, KA, cpu_s)
     extra = []
     if not args.no_extra and not args.set:
-        for name in ("llama3_8b_32k", "gqa_throughput", "llama2_7b_imp4"):
+        for name in ("llama3_8b_32k", "gqa_throughput", "llama2_7b_imp4", "llama2_7b_kchan"):
             if name == cfg.name:
                 continue
             c2 = S.CONFIGS[name]

@@ -56,6 +56,23 @@
  *     from its codes rebuilt as the fp16 row fp16(code*scale + zero).
  *   Grouping pairs by precision is allowed because attention is invariant
  *   under jointly permuting KV pairs ([velog notes] section 3.4).
+ * Per-channel key quantization ([velog notes] the per-channel alternative
+ * and its appendix C summary; [paperlayer] appendix C: retained keys
+ * quantized per channel with groups of 64 tokens, which needs a buffer
+ * for pairs until enough have gathered), selected by dims.key_tile = 64
+ * (requires imp_bits 16 and capq a multiple of 64):
+ *   kq      [batch][hkv][capq][d*bits/8] uint8: tiles of 64 consecutive
+ *           slots, packed token-major as above; ksz is unused (may be NULL)
+ *   kcsz    [batch][hkv][capq/64][d][2] fp16 (scale, zero) per tile and
+ *           channel: the per-token rule run along the tile's 64 tokens
+ *   vq, vsz values per token, as above
+ *   kbuf, vbuf [batch][hkv][64][d] fp16, posbuf [batch][hkv][64] int32:
+ *           pairs that left the importance tier and wait for a tile.
+ *   A cache whose retained tier has taken D tokens holds 64*floor(D/64) of
+ *   them in tiles (slots 0..) and the other D mod 64 in buffer rows
+ *   0..D mod 64 - 1, both in the order they were demoted; buffered pairs
+ *   are attended to in fp16. The demotion that fills the buffer turns it
+ *   into the next tile (keys per channel, values per token).
  *   With B = cap16 - 1 important tokens and a current length N (new token
  *   included), the low-bit tier holds N - 1 - B tokens when a decode step
  *   starts and N - B after it.
@@ -70,7 +87,7 @@
 extern "C" {
 #endif
 
-#define MIKV_ABI_VERSION 3
+#define MIKV_ABI_VERSION 4
 
 typedef enum {
   MIKV_OK = 0,
@@ -100,6 +117,8 @@ typedef struct {
   int32_t cap16; /* FP16-tier slots per (n, g) = B + 1                     */
   int32_t capq;  /* low-bit-tier slots per (n, g)                          */
   int32_t imp_bits; /* importance tier: 16 or 0 = fp16 rows; 8 or 4 = codes */
+  int32_t key_tile; /* 0: per-token keys; 64: per-channel keys over tiles of
+                       64 tokens with an fp16 token buffer (see above)     */
 } mikv_dims;
 
 typedef struct {
@@ -117,6 +136,10 @@ typedef struct {
   uint8_t* vimp;
   uint16_t* kimpsz;
   uint16_t* vimpsz;
+  uint16_t* kcsz;   /* per-channel key tiles (key_tile 64), else NULL     */
+  uint16_t* kbuf;
+  uint16_t* vbuf;
+  int32_t* posbuf;
 } mikv_cache;
 
 /*
@@ -174,6 +197,9 @@ mikv_status mikv_quantize_tokens(const uint16_t* x, const int32_t* rows,
  *      enter outputs that are specified to a tolerance.
  *   3. p16[n][g][slot] = sum over the query heads of group g of p at that
  *      FP16 slot (input of the H2O accumulation).
+ *      Per-channel key tiles: the len - cap16 retained tokens are the
+ *      whole tiles (k~[c] = code*scale[c] + zero[c] of the tile) and the
+ *      (len - cap16) mod 64 buffered pairs (k~ = kbuf, v~ = vbuf in fp16).
  * Precondition: the low-bit tier holds len - cap16 tokens (slots
  * 0..len-cap16-1); every FP16 slot other than free16 is occupied. The free
  * slot's stale K/V rows are read and masked, so they must hold finite fp16
@@ -188,7 +214,10 @@ mikv_status mikv_quantize_tokens(const uint16_t* x, const int32_t* rows,
  * Errors: len - cap16 < 0 -> MIKV_ERR_SHAPE; len - cap16 > capq ->
  * MIKV_ERR_CAPACITY; a per-(sequence, kv head) tier of 2^31 bytes or more
  * (capq*d*bits/8 or cap16*2*d) -> MIKV_ERR_SHAPE (the kernels address a tier
- * with 32-bit offsets).
+ * with 32-bit offsets); key_tile not 0 or 64, or 64 with imp_bits 8 or 4
+ * -> MIKV_ERR_UNSUPPORTED; key_tile 64 with capq not a multiple of 64 ->
+ * MIKV_ERR_SHAPE; key_tile 64 with kcsz, kbuf, vbuf or posbuf NULL ->
+ * MIKV_ERR_NULL, kbuf or vbuf not 16-byte aligned -> MIKV_ERR_SHAPE.
  */
 size_t mikv_decode_attn_workspace(const mikv_dims* dims, int32_t max_len);
 mikv_status mikv_decode_attn(const mikv_dims* dims, const mikv_cache* cache,
@@ -289,12 +318,17 @@ typedef struct {
  *   mikv_quantize_tokens, keys and values) into low-bit slot len - cap16,
  *   its position copied to posq, and free16 set to its slot.
  *   demoted_pos[n][g] (optional) receives its position.
+ *   Per-channel key tiles: the candidate's fp16 key and value rows go to
+ *   buffer row (len - cap16) mod 64 (position to posbuf); when that is row
+ *   63 the buffer becomes tile (len - cap16) / 64.
  * Prefill mode (p16 == NULL, src != NULL, len == src->T):
  *   important = positions >= T - recent plus the top-`heavy` positions of
  *   [0, T - recent) by (acc0 desc, position asc); they fill FP16 slots
  *   0..B-1 in ascending position with acc16 = acc0, free16 = B (its K/V
  *   rows zeroed, pos16 = -1, acc16 = 0); the other T - B positions are
- *   quantized into low-bit slots 0..T-B-1 in ascending position.
+ *   quantized into low-bit slots 0..T-B-1 in ascending position
+ *   (per-channel key tiles: the first 64*floor((T-B)/64) of them fill
+ *   tiles, the last (T-B) mod 64 go to the buffer as fp16).
  *   demoted_pos is ignored.
  * ws: mikv_h2o_workspace(dims, max_T) bytes (any contents; decode mode
  * needs none and accepts ws == NULL).

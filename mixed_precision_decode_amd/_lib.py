@@ -23,13 +23,14 @@ _vp, _sz, _i32, _i64, _f64 = C.c_void_p, C.c_size_t, C.c_int32, C.c_int64, C.c_d
 
 class MikvDims(C.Structure):
     _fields_ = [(n, _i32) for n in ("batch", "hq", "hkv", "d", "group", "bits", "cap16", "capq",
-                                     "imp_bits")]
+                                     "imp_bits", "key_tile")]
 
 
 class MikvCache(C.Structure):
     _fields_ = [(n, _vp) for n in ("k16", "v16", "pos16", "acc16", "free16",
                                    "kq", "vq", "ksz", "vsz", "posq",
-                                   "kimp", "vimp", "kimpsz", "vimpsz")]
+                                   "kimp", "vimp", "kimpsz", "vimpsz",
+                                   "kcsz", "kbuf", "vbuf", "posbuf")]
 
 
 class MikvPrefillSrc(C.Structure):
@@ -108,6 +109,7 @@ class Dims:
     cap16: int
     capq: int
     imp_bits: int = 16
+    key_tile: int = 0
 
     def c(self) -> MikvDims:
         key = tuple(int(getattr(self, f.name)) for f in dataclasses.fields(self))
@@ -223,7 +225,9 @@ def mikv_quantize_tokens(x, rows, codes, sz, group: int, bits: int, stream=None)
 class Cache:
     """Device tensors of one two-tier cache (layout of include/mikv.h). With
     dims.imp_bits 8 or 4 the importance tier is kimp/vimp codes with
-    kimpsz/vimpsz (scale, zero), and k16/v16 are not allocated."""
+    kimpsz/vimpsz (scale, zero), and k16/v16 are not allocated. With
+    dims.key_tile 64 the retained keys are per-channel tiles (kcsz in place
+    of ksz) with the fp16 buffer kbuf/vbuf/posbuf."""
 
     def __init__(self, dims: Dims, device="cuda"):
         import torch
@@ -245,9 +249,17 @@ class Cache:
         cb = d * dims.bits // 8
         self.kq = torch.zeros((n, g, cq, cb), dtype=torch.uint8, device=device)
         self.vq = torch.zeros_like(self.kq)
-        self.ksz = torch.zeros((n, g, cq, d // dims.group, 2), dtype=torch.float16, device=device)
-        self.vsz = torch.zeros_like(self.ksz)
+        self.vsz = torch.zeros((n, g, cq, d // dims.group, 2), dtype=torch.float16, device=device)
         self.posq = torch.full((n, g, cq), -1, dtype=torch.int32, device=device)
+        self.key_tile = dims.key_tile
+        if dims.key_tile:
+            kt = dims.key_tile
+            self.kcsz = torch.zeros((n, g, cq // kt, d, 2), dtype=torch.float16, device=device)
+            self.kbuf = torch.zeros((n, g, kt, d), dtype=torch.float16, device=device)
+            self.vbuf = torch.zeros_like(self.kbuf)
+            self.posbuf = torch.full((n, g, kt), -1, dtype=torch.int32, device=device)
+        else:
+            self.ksz = torch.zeros_like(self.vsz)
 
     def c(self) -> MikvCache:
         if getattr(self, "_c", None) is None:
@@ -259,13 +271,19 @@ class Cache:
     NAMES = ("k16", "v16") + COMMON
     IMP_NAMES = ("kimp", "vimp", "kimpsz", "vimpsz") + COMMON
 
+    KT_NAMES = ("k16", "v16", "pos16", "acc16", "free16", "kq", "vq", "vsz", "posq",
+                "kcsz", "kbuf", "vbuf", "posbuf")
+
     @property
     def names(self):
+        if self.key_tile:
+            return self.KT_NAMES
         return self.NAMES if self.imp_bits == 16 else self.IMP_NAMES
 
     def to_numpy(self) -> dict:
         out = {k: getattr(self, k).cpu().numpy() for k in self.names}
         out["group"], out["bits"], out["imp_bits"] = self.dims.group, self.dims.bits, self.imp_bits
+        out["key_tile"] = self.key_tile
         return out
 
 

@@ -38,6 +38,10 @@ mikv_status check_dims(const mikv_dims* m, bool need_tiers) {
     const int ib = imp_of(m);
     if (ib != 16 && ib != 8 && ib != 4) return MIKV_ERR_UNSUPPORTED;
     if (ib != 16 && m->group != m->d / 2) return MIKV_ERR_UNSUPPORTED;
+    // per-channel key tiles of 64 tokens: fp16 importance tier, whole tiles of slots
+    if (m->key_tile != 0 && m->key_tile != kKeyTile) return MIKV_ERR_UNSUPPORTED;
+    if (m->key_tile && ib != 16) return MIKV_ERR_UNSUPPORTED;
+    if (m->key_tile && m->capq % kKeyTile != 0) return MIKV_ERR_SHAPE;
     // the decode kernels address one (sequence, kv head) tier with 32-bit byte offsets
     if (static_cast<int64_t>(m->capq) * m->d * m->bits / 8 >= (int64_t{1} << 31) ||
         static_cast<int64_t>(m->cap16) * m->d * ib / 8 >= (int64_t{1} << 31))
@@ -46,11 +50,18 @@ mikv_status check_dims(const mikv_dims* m, bool need_tiers) {
   return MIKV_OK;
 }
 
-mikv_status check_cache(const mikv_cache* c, int imp_bits) {
+mikv_status check_cache(const mikv_cache* c, const mikv_dims* m) {
+  const int imp_bits = imp_of(m);
   if (!c) return MIKV_ERR_NULL;
-  if (!c->pos16 || !c->acc16 || !c->free16 || !c->kq || !c->vq || !c->ksz || !c->vsz || !c->posq)
+  if (!c->pos16 || !c->acc16 || !c->free16 || !c->kq || !c->vq || !c->vsz || !c->posq)
     return MIKV_ERR_NULL;
   if (!aligned16(c->kq) || !aligned16(c->vq)) return MIKV_ERR_SHAPE;
+  if (m->key_tile) {
+    if (!c->kcsz || !c->kbuf || !c->vbuf || !c->posbuf) return MIKV_ERR_NULL;
+    if (!aligned16(c->kbuf) || !aligned16(c->vbuf)) return MIKV_ERR_SHAPE;
+  } else if (!c->ksz) {
+    return MIKV_ERR_NULL;
+  }
   if (imp_bits == 16) {
     if (!c->k16 || !c->v16) return MIKV_ERR_NULL;
     if (!aligned16(c->k16) || !aligned16(c->v16)) return MIKV_ERR_SHAPE;
@@ -62,6 +73,11 @@ mikv_status check_cache(const mikv_cache* c, int imp_bits) {
 }
 
 void set_imp(DecodeArgs& a, const mikv_dims* m, const mikv_cache* c) {
+  a.key_tile = m->key_tile;
+  a.kcsz = c->kcsz; a.kbuf = c->kbuf; a.vbuf = c->vbuf;
+  a.h2o.key_tile = m->key_tile;
+  a.h2o.kcsz = reinterpret_cast<uint32_t*>(c->kcsz);
+  a.h2o.kbuf = c->kbuf; a.h2o.vbuf = c->vbuf; a.h2o.posbuf = c->posbuf;
   a.imp_bits = imp_of(m);
   a.kimp = c->kimp; a.vimp = c->vimp; a.kimpsz = c->kimpsz; a.vimpsz = c->vimpsz;
   a.h2o.imp_bits = a.imp_bits;
@@ -71,6 +87,8 @@ void set_imp(DecodeArgs& a, const mikv_dims* m, const mikv_cache* c) {
 }
 
 void set_imp(H2OArgs& a, const mikv_dims* m, const mikv_cache* c) {
+  a.key_tile = m->key_tile;
+  a.kcsz = c->kcsz; a.kbuf = c->kbuf; a.vbuf = c->vbuf; a.posbuf = c->posbuf;
   a.imp_bits = imp_of(m);
   a.kimp = c->kimp; a.vimp = c->vimp; a.kimpsz = c->kimpsz; a.vimpsz = c->vimpsz;
 }
@@ -167,7 +185,8 @@ size_t mikv_decode_attn_workspace(const mikv_dims* m, int32_t max_len) {
   if (check_dims(m, true) != MIKV_OK) return 0;
   const int nq = max_len - m->cap16;
   if (nq < 0) return 0;
-  return decode_ws_bound(m->batch, m->hq, m->hkv, m->d, m->bits, m->group, m->cap16, nq, imp_of(m));
+  return decode_ws_bound(m->batch, m->hq, m->hkv, m->d, m->bits, m->group, m->cap16, nq, imp_of(m),
+                         m->key_tile);
 }
 
 static mikv_status decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t len,
@@ -176,7 +195,7 @@ static mikv_status decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t 
                                void* stream, void* ev_start, void* ev_stop) {
   mikv_status st = check_dims(m, true);
   if (st != MIKV_OK) return st;
-  st = check_cache(c, imp_of(m));
+  st = check_cache(c, m);
   if (st != MIKV_OK) return st;
   if (!q || !k_new || !v_new || !b || !o || !p16) return MIKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new)) return MIKV_ERR_SHAPE;
@@ -184,7 +203,7 @@ static mikv_status decode_attn(const mikv_dims* m, const mikv_cache* c, int32_t 
   if (nq < 0) return MIKV_ERR_SHAPE;
   if (nq > m->capq) return MIKV_ERR_CAPACITY;
   const DecodePlan pl = decode_plan(m->batch, m->hkv, m->d, m->bits, m->group, m->hq / m->hkv,
-                                    m->cap16, nq, imp_of(m));
+                                    m->cap16, nq, imp_of(m), m->key_tile);
   const size_t need = decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, pl);
   if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
   DecodeArgs a;
@@ -230,7 +249,7 @@ mikv_status check_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t l
                               const float* p16, DecodePlan* plan, size_t* need) {
   mikv_status st = check_dims(m, true);
   if (st != MIKV_OK) return st;
-  st = check_cache(c, imp_of(m));
+  st = check_cache(c, m);
   if (st != MIKV_OK) return st;
   if (!q || !k_new || !v_new || !b || !o || !p16) return MIKV_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new)) return MIKV_ERR_SHAPE;
@@ -239,7 +258,7 @@ mikv_status check_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t l
   if (nq < 0) return MIKV_ERR_SHAPE;
   if (nq + 1 > m->capq) return MIKV_ERR_CAPACITY;  // the demotion adds one low-bit token
   *plan = decode_plan(m->batch, m->hkv, m->d, m->bits, m->group, m->hq / m->hkv, m->cap16, nq,
-                      imp_of(m));
+                      imp_of(m), m->key_tile);
   *need = decode_ws_bytes(m->batch, m->hq, m->hkv, m->d, m->cap16, *plan);
   return MIKV_OK;
 }
@@ -256,9 +275,11 @@ mikv_status launch_decode_step(const mikv_dims* m, const mikv_cache* c, int32_t 
   a.k16 = c->k16; a.v16 = c->v16; a.pos16 = c->pos16; a.free16 = c->free16;
   a.kq = c->kq; a.vq = c->vq; a.ksz = c->ksz; a.vsz = c->vsz;
   a.o = o; a.p16 = p16; a.ws = ws;
-  a.fuse_h2o = m->cap16 <= kFusedMaxCap16;
+  // per-channel key tiles: the H2O step (buffer and tile flush) is its own launch
+  a.fuse_h2o = m->key_tile == 0 && m->cap16 <= kFusedMaxCap16;
   a.ev_split_start = nullptr;
   a.ev_split_stop = nullptr;
+  a.h2o = H2OView{};
   H2OView& v = a.h2o;
   v.cap16 = m->cap16; v.capq = m->capq; v.len = len; v.recent = recent;
   v.k16 = c->k16; v.v16 = c->v16; v.pos16 = c->pos16; v.acc16 = c->acc16; v.free16 = c->free16;
@@ -326,7 +347,7 @@ mikv_status mikv_h2o_update_select(const mikv_dims* m, const mikv_cache* c, int3
                                    size_t ws_bytes, void* stream) {
   mikv_status st = check_dims(m, true);
   if (st != MIKV_OK) return st;
-  st = check_cache(c, imp_of(m));
+  st = check_cache(c, m);
   if (st != MIKV_OK) return st;
   if ((p16 == nullptr) == (src == nullptr)) return MIKV_ERR_NULL;
   if (recent < 0 || heavy < 0 || heavy + recent != m->cap16 - 1) return MIKV_ERR_SHAPE;

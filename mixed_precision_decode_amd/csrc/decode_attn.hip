@@ -25,6 +25,12 @@
 //   merge kernel  one block per (sequence, kv head): combines the split
 //                 partials of every query head of the group and turns the
 //                 FP16-tier scores into p16 (summed over the group).
+// Per-channel key tiles (velog notes, the per-channel alternative and its
+// appendix C summary): the low-bit tier holds whole tiles of 64 tokens, each
+// key channel with its own (scale, zero) per tile; a block first builds a
+// table of q-hat * scale and sum(q-hat * zero) per tile and head in LDS, and
+// a key score is then table . code + that sum. The fp16 buffer of pairs
+// waiting for a tile is one more split, streamed like the FP16 tier.
 // Tiles of 2-4 query heads with groups of d/2 channels run the split step as
 // decode_tile_kernel (decode_tile.hpp): key scores on the matrix cores, one
 // lane per (token, heads) for the softmax, value sums on the vector ALUs.
@@ -57,6 +63,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct DecodeK {
   int hq, hkv, rep, cap16, capq, nq, len, group, units;
   int S16, Sq, C16, Cq, tiles, f16_first;
+  int Sb, nb;         // per-channel key tiles: buffer splits (0 or 1) and buffered pairs
+  const uint32_t* kcsz;  // [units][capq/64][D] (scale | zero << 16) per tile and channel
+  const uint16_t* kbuf;  // [units][64][D] fp16 buffered pairs
+  const uint16_t* vbuf;
   const uint16_t* q;
   const uint16_t* k_new;
   const uint16_t* v_new;
@@ -321,7 +331,12 @@ struct MagicPairs {
 // float q-hat of 2-4 heads is held too
 constexpr int lowbit_cpl(int d, int rt) { return (rt == 1 ? 32 : 16) < d ? (rt == 1 ? 32 : 16) : d; }
 
-template <int D, int BITS, int RT>
+// LDS of the per-tile key table: q-hat * scale [tiles][RT][D] and
+// sum(q-hat * zero) [tiles][RT]; a low-bit split spans at most this many tiles.
+constexpr int kKtLdsBytes = 24576;
+constexpr int kt_max_tiles(int d, int rt) { return kKtLdsBytes / (4 * rt * (d + 1)); }
+
+template <int D, int BITS, int RT, bool KT>
 __device__ __forceinline__ void lowbit_split(const DecodeK& p, int unit, int n, int g, int tile, int split,
                                              const float* bvec, float* red, float (*sm)[RT], float* sM,
                                              float* po, float2* pml) {
@@ -330,7 +345,7 @@ __device__ __forceinline__ void lowbit_split(const DecodeK& p, int unit, int n, 
   constexpr int NB = CPL * BITS / 8, NW = NB / 4;  // code bytes / words per lane and token
   constexpr int CB = D * BITS / 8;                 // code bytes per token
   constexpr int CPW = 32 / BITS;                   // channels per code word
-  constexpr bool kIntDot = (RT == 1);
+  constexpr bool kIntDot = (RT == 1) && !KT;
   static_assert(NB % 4 == 0 && NW >= 1 && NW <= 4, "lane code slice must be 1, 2 or 4 words");
   const int tid = threadIdx.x;
   const int lane = tid % LPT, tslot = tid / LPT, c0 = lane * CPL;
@@ -344,7 +359,8 @@ __device__ __forceinline__ void lowbit_split(const DecodeK& p, int unit, int n, 
   const uint32_t sbytes = static_cast<uint32_t>(nt) * gpt * 4;
   const Rsrc rk = make_rsrc(p.kq + ub * CB, rbytes);
   const Rsrc rv = make_rsrc(p.vq + ub * CB, rbytes);
-  const Rsrc rks = make_rsrc(p.ksz + ub * gpt, sbytes);
+  // per-channel key tiles have no per-token key (scale, zero)
+  const Rsrc rks = make_rsrc(KT ? p.vsz + ub * gpt : p.ksz + ub * gpt, KT ? 0u : sbytes);
   const Rsrc rvs = make_rsrc(p.vsz + ub * gpt, sbytes);
   // byte offsets of this lane's slice of token 0 of its slot
   const uint32_t cof = static_cast<uint32_t>(tslot * CB + lane * NB);
@@ -356,21 +372,63 @@ __device__ __forceinline__ void lowbit_split(const DecodeK& p, int unit, int n, 
     for (int j = 0; j < TPT; ++j) {
       const uint32_t t = static_cast<uint32_t>(base + j * SLOTS);
       R.k[j] = bload<NW>(rk, cof + t * CB);
-      R.ks[j] = bload1(rks, sof + t * gpt * 4);
+      if constexpr (!KT) R.ks[j] = bload1(rks, sof + t * gpt * 4);
+      else R.ks[j] = 0u;
       R.v[j] = bload<NW>(rv, cof + t * CB);
       R.vs[j] = bload1(rvs, sof + t * gpt * 4);
     }
   };
   Regs A, B;
   load(0, A);
-  float qh[RT][CPL];
-  load_qhat<D, RT, CPL>(p, n, g, tile, c0, bvec, qh);
+  float qh[RT][KT ? 1 : CPL];
   float qsum[RT];
+  // per-channel key tiles: table of q-hat * scale and sum(q-hat * zero) of
+  // the block's tiles (the range starts on a tile and holds whole tiles);
+  // wave w builds tiles w, w + 4, ..., lane l channels l, l + 64
+  __shared__ float kt_qs[KT ? kt_max_tiles(D, RT) * RT * D : 1];
+  __shared__ float kt_qz[KT ? kt_max_tiles(D, RT) * RT : 1];
+  const int ntl = nt / kKeyTile;
+  if constexpr (KT) {
+    constexpr int CPX = D / kWave;
+    const int wave = tid / kWave, wl = tid % kWave;
+    const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+    float qx[RT][CPX];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    qsum[r] = 0.0f;
+    for (int r = 0; r < RT; ++r) {
+      const int h = g * p.rep + tile * RT + r;
+      const uint16_t* qp = p.q + (static_cast<int64_t>(n) * p.hq + h) * D;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) qsum[r] += qh[r][i];
+      for (int e = 0; e < CPX; ++e) {
+        const int c = wl + e * kWave;
+        qx[r][e] = h2f(qp[c]) * __builtin_amdgcn_rcpf(bvec[c]) * qscale;
+      }
+    }
+    const uint32_t* zs = p.kcsz + (static_cast<int64_t>(unit) * (p.capq / kKeyTile) + t0 / kKeyTile) * D;
+    for (int tl = wave; tl < ntl; tl += kThreads / kWave) {
+      uint32_t w[CPX];
+#pragma unroll
+      for (int e = 0; e < CPX; ++e) w[e] = zs[static_cast<int64_t>(tl) * D + wl + e * kWave];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        float zsum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < CPX; ++e) {
+          kt_qs[(tl * RT + r) * D + wl + e * kWave] = qx[r][e] * lo_h(w[e]);
+          zsum += qx[r][e] * hi_h(w[e]);
+        }
+        zsum = wave_sum(zsum);
+        if (wl == 0) kt_qz[tl * RT + r] = zsum;
+      }
+    }
+    __syncthreads();
+  } else {
+    load_qhat<D, RT, CPL>(p, n, g, tile, c0, bvec, qh);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      qsum[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) qsum[r] += qh[r][i];
+    }
   }
   // Integer form of q-hat (single head): q_int = rint(q-hat * 2^F) with F
   // chosen per lane so |q_int| < 2^22, biased by 2^23 into [0, 2^24) and
@@ -422,7 +480,21 @@ __device__ __forceinline__ void lowbit_split(const DecodeK& p, int unit, int n, 
     for (int j = 0; j < TPT; ++j) {
       const bool valid = base + j * SLOTS + tslot < nt;
       const float s = lo_h(R.ks[j]), z = hi_h(R.ks[j]);
-      if constexpr (kIntDot) {
+      if constexpr (KT) {
+        // the token's tile (clamped for masked tokens past the range)
+        const int tl = min((base + j * SLOTS + tslot) / kKeyTile, ntl - 1);
+        float cf[CPL];
+        unpack_codes<BITS, CPL>(R.k[j].w, cf);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const float* qs = kt_qs + (tl * RT + r) * D + c0;
+          float dot = 0.0f;
+#pragma unroll
+          for (int i = 0; i < CPL; ++i) dot += qs[i] * cf[i];
+          const float v = group_sum<LPT>(dot) + kt_qz[tl * RT + r];
+          sc[j][r] = valid ? v : -INFINITY;
+        }
+      } else if constexpr (kIntDot) {
         uint32_t acc[6] = {0u, 0u, 0u, 0u, 0u, 0u}, csum = 0u;
 #pragma unroll
         for (int i = 0; i < NQW; ++i) {
@@ -520,7 +592,10 @@ __device__ __forceinline__ void lowbit_split(const DecodeK& p, int unit, int n, 
 #endif
 constexpr int fp16_cpl(int rt) { return rt == 1 ? MIKV_FP16_CPL1 : 8; }
 
-template <int D, int RT>
+// With per-channel key tiles (KT) the split after the low-bit splits streams
+// the fp16 buffer of pairs that wait for a tile: the same arithmetic, with no
+// FP16-tier scores to keep and no new token.
+template <int D, int RT, bool KT>
 __device__ __forceinline__ void fp16_split(const DecodeK& p, int unit, int n, int g, int tile, int split,
                                            const float* bvec, float* red, float (*sm)[RT], float* sM,
                                            float* po, float2* pml) {
@@ -530,14 +605,16 @@ __device__ __forceinline__ void fp16_split(const DecodeK& p, int unit, int n, in
   constexpr int NV = CPL / 8;  // 16-byte loads per row and lane
   const int tid = threadIdx.x;
   const int lane = tid % LPT, tslot = tid / LPT, c0 = lane * CPL;
-  const int s0 = split * p.C16;
-  const int s1 = min(p.cap16, s0 + p.C16);
+  const bool buf = KT && split >= p.S16 + p.Sq;
+  const int s0 = buf ? 0 : split * p.C16;
+  const int s1 = buf ? p.nb : min(p.cap16, s0 + p.C16);
   const int ns = max(s1 - s0, 0);
-  const int fr = p.free16[unit];
+  const int fr = buf ? -1 : p.free16[unit];
   const int64_t rb = static_cast<int64_t>(unit) * p.cap16;
   const uint32_t rbytes = static_cast<uint32_t>(ns) * D * 2;
-  const Rsrc rk = make_rsrc(p.k16 + (rb + s0) * D, rbytes);
-  const Rsrc rv = make_rsrc(p.v16 + (rb + s0) * D, rbytes);
+  const int64_t bb = static_cast<int64_t>(unit) * kKeyTile * D;
+  const Rsrc rk = make_rsrc(buf ? p.kbuf + bb : p.k16 + (rb + s0) * D, rbytes);
+  const Rsrc rv = make_rsrc(buf ? p.vbuf + bb : p.v16 + (rb + s0) * D, rbytes);
   // scores of this tile's heads for the block's slots, [RT][cap16] rows
   const int64_t scb = (static_cast<int64_t>(unit) * p.rep + tile * RT) * p.cap16 + s0;
   const uint32_t cof = static_cast<uint32_t>((tslot * D + c0) * 2);
@@ -637,7 +714,7 @@ __device__ __forceinline__ void fp16_split(const DecodeK& p, int unit, int n, in
         }
         dot = group_sum<LPT>(dot);
         sc[j][r] = valid ? dot : -INFINITY;
-        if (lane == 0 && valid) p.sc16[scb + static_cast<int64_t>(r) * p.cap16 + t] = dot;
+        if (lane == 0 && valid && !buf) p.sc16[scb + static_cast<int64_t>(r) * p.cap16 + t] = dot;
       }
     }
 #pragma unroll
@@ -704,7 +781,7 @@ __device__ __forceinline__ void fp16_split(const DecodeK& p, int unit, int n, in
   write_partial<D, RT, LPT, CPL>(st, red, sm, sM, po, pml);
 }
 
-template <int D, int BITS, int RT>
+template <int D, int BITS, int RT, bool KT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p) {
   // Split-major block order. Blocks are dispatched to the 8 XCDs in turn
   // (block i to XCD i mod 8), so with the split index outermost every XCD
@@ -712,10 +789,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
   // FP16 and low-bit splits, instead of XCDs that hold only one tier's
   // splits and finish at different times. The tier whose blocks take
   // longer is dispatched first: a compute unit's older waves win issue.
-  const int S = p.S16 + p.Sq;
+  const int S = p.S16 + p.Sq + p.Sb;
   const int ut = p.units * p.tiles;
   const int sd = blockIdx.x / ut;
-  const int split = p.f16_first ? sd : ((sd < p.Sq) ? p.S16 + sd : sd - p.Sq);
+  // the buffer split (per-channel key tiles) comes last
+  const int split = (sd >= p.S16 + p.Sq || p.f16_first) ? sd : ((sd < p.Sq) ? p.S16 + sd : sd - p.Sq);
   const int rest = blockIdx.x % ut;
   const int tile = rest % p.tiles;
   const int unit = rest / p.tiles;
@@ -731,10 +809,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
   __shared__ float sm_max[4][RT];
   __shared__ float sm_M[RT];
 
-  if (split < p.S16) {
-    fp16_split<D, RT>(p, unit, n, g, tile, split, bvec, red, sm_max, sm_M, po, pml);
+  if (split < p.S16 || (KT && split >= p.S16 + p.Sq)) {
+    fp16_split<D, RT, KT>(p, unit, n, g, tile, split, bvec, red, sm_max, sm_M, po, pml);
   } else {
-    lowbit_split<D, BITS, RT>(p, unit, n, g, tile, split, bvec, red, sm_max, sm_M, po, pml);
+    lowbit_split<D, BITS, RT, KT>(p, unit, n, g, tile, split, bvec, red, sm_max, sm_M, po, pml);
   }
 }
 
@@ -770,7 +848,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
   const int chunk = blockIdx.y;
   const int n = unit / p.hkv, g = unit % p.hkv;
   const int tid = threadIdx.x;
-  const int S = p.S16 + p.Sq;
+  const int S = p.S16 + p.Sq + p.Sb;
   const int rep = p.rep;
   const int cap16 = p.cap16;
   float* sM = reinterpret_cast<float*>(sml + rep * S);
@@ -984,17 +1062,17 @@ static int device_cus() {
 // Resident split-kernel blocks per compute unit for this instantiation, from
 // the runtime's occupancy calculator (cached per instantiation); the
 // default when it cannot answer (no device).
-template <int D, int BITS, int IB, int RT, bool TILE>
+template <int D, int BITS, int IB, int RT, bool TILE, bool KT = false>
 static const void* split_kernel_ptr() {
   if constexpr (TILE) return reinterpret_cast<const void*>(decode_tile_kernel<D, BITS, IB, RT>);
-  else return reinterpret_cast<const void*>(decode_split_kernel<D, BITS, RT>);
+  else return reinterpret_cast<const void*>(decode_split_kernel<D, BITS, RT, KT>);
 }
-template <int D, int BITS, int IB, int RT, bool TILE>
+template <int D, int BITS, int IB, int RT, bool TILE, bool KT = false>
 static int blocks_per_cu() {
   static std::atomic<int> cache{0};
   int n = cache.load(std::memory_order_relaxed);
   if (n == 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr<D, BITS, IB, RT, TILE>(), kThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr<D, BITS, IB, RT, TILE, KT>(), kThreads,
                                                      0) != hipSuccess || n <= 0) {
       (void)hipGetLastError();
       return MIKV_BLOCKS_PER_CU;
@@ -1006,10 +1084,18 @@ static int blocks_per_cu() {
 // decode_tile_kernel (scores on the matrix cores) for head tiles of 2-4
 // heads, and for every tile when the importance tier holds codes; groups of
 // d/2 channels. Otherwise decode_split_kernel.
-static inline bool use_tile_kernel(int d, int group, int rt, int ib) {
-  return group == d / 2 && (ib < 16 || rt > 1);
+static inline bool use_tile_kernel(int d, int group, int rt, int ib, int key_tile) {
+  return key_tile == 0 && group == d / 2 && (ib < 16 || rt > 1);
 }
-static int split_blocks_per_cu(int d, int bits, int ib, int rt, bool tile) {
+static int split_blocks_per_cu(int d, int bits, int ib, int rt, bool tile, int key_tile) {
+#define MIKV_OCCK(D_, B_)                                      \
+  if (key_tile && d == D_ && bits == B_) {                     \
+    if (rt == 1) return blocks_per_cu<D_, B_, 16, 1, false, true>(); \
+    if (rt == 2) return blocks_per_cu<D_, B_, 16, 2, false, true>(); \
+    return blocks_per_cu<D_, B_, 16, 4, false, true>();        \
+  }
+  MIKV_OCCK(128, 4) MIKV_OCCK(128, 2) MIKV_OCCK(64, 4) MIKV_OCCK(64, 2)
+#undef MIKV_OCCK
 #define MIKV_OCC16(D_, B_, RT_)                           \
   if (d == D_ && bits == B_ && ib == 16 && rt == RT_)     \
     return tile ? blocks_per_cu<D_, B_, 16, RT_, (RT_ > 1)>() : blocks_per_cu<D_, B_, 16, RT_, false>();
@@ -1043,12 +1129,21 @@ static int split_blocks_per_cu(int d, int bits, int ib, int rt, bool tile) {
 // lane groups): the time of a tier is its token count, an FP16 token
 // weighted 1.3 (on the 32K GQA shape, token shares of 1:1 and 1.3:1 gave a
 // split kernel of 29.6 and 28.7 us, byte shares 34.2 us).
-DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq,
-                       int imp_bits) {
+//
+// Per-channel key tiles: the low-bit splits hold whole tiles of 64 tokens
+// (at most kt_max_tiles, the LDS table of a block), and the buffered pairs,
+// if any, are one more split (Sb = 1) whose bytes count with the FP16 tier.
+DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nr,
+                       int imp_bits, int key_tile) {
   DecodePlan pl;
   pl.RT = (rep % 4 == 0) ? 4 : (rep % 2 == 0 ? 2 : 1);
   pl.tiles = rep / pl.RT;
-  const bool tile = use_tile_kernel(d, group, pl.RT, imp_bits);
+  pl.key_tile = key_tile;
+  const int nq = key_tile ? nr / kKeyTile * kKeyTile : nr;
+  pl.nq = nq;
+  pl.nb = nr - nq;
+  pl.Sb = pl.nb > 0 ? 1 : 0;
+  const bool tile = use_tile_kernel(d, group, pl.RT, imp_bits, key_tile);
   const double b16 = static_cast<double>(cap16) *
                      (imp_bits == 16 ? 4.0 * d : 2.0 * (d * imp_bits / 8 + 4 * (d / group)));
   const double bq = static_cast<double>(nq) * 2.0 * (d * bits / 8 + 4 * (d / group));
@@ -1056,7 +1151,8 @@ DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, 
   const double t16 = (pl.RT == 1 || imp_bits < 16) ? b16 : 1.3 * cap16;
   const double tq = (pl.RT == 1 || imp_bits < 16) ? bq : static_cast<double>(nq);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
-  long per_unit = (static_cast<long>(device_cus()) * split_blocks_per_cu(d, bits, imp_bits, pl.RT, tile)) / units;
+  long per_unit =
+      (static_cast<long>(device_cus()) * split_blocks_per_cu(d, bits, imp_bits, pl.RT, tile, key_tile)) / units;
   // no split below ~16 KB of rows
   const long cap_splits = static_cast<long>((b16 + bq) / 16384.0) + 1;
   if (per_unit > cap_splits) per_unit = cap_splits;
@@ -1086,6 +1182,15 @@ DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, 
   pl.C16 = cdiv(cap16, pl.S16);
   pl.S16 = cdiv(cap16, pl.C16);
   pl.Cq = nq > 0 ? cdiv(nq, pl.Sq) : 0;
+  if (nq > 0 && key_tile) {
+    // whole tiles per split, within the block's LDS table
+    const int mt = (d == 128) ? (pl.RT == 1 ? kt_max_tiles(128, 1) : pl.RT == 2 ? kt_max_tiles(128, 2)
+                                                                                : kt_max_tiles(128, 4))
+                              : (pl.RT == 1 ? kt_max_tiles(64, 1) : pl.RT == 2 ? kt_max_tiles(64, 2)
+                                                                               : kt_max_tiles(64, 4));
+    pl.Cq = cdiv(pl.Cq, kKeyTile) * kKeyTile;
+    if (pl.Cq > mt * kKeyTile) pl.Cq = mt * kKeyTile;
+  }
   if (nq > 0) pl.Sq = cdiv(nq, pl.Cq);
   return pl;
 }
@@ -1095,31 +1200,39 @@ static inline size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(2
 size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int cap16, const DecodePlan& pl) {
   const size_t units = static_cast<size_t>(batch) * hkv;
   const size_t rep = hq / hkv;
-  const size_t nparts = units * pl.tiles * (pl.S16 + pl.Sq);
+  const size_t nparts = units * pl.tiles * (pl.S16 + pl.Sq + pl.Sb);
   return al256(nparts * pl.RT * sizeof(float2)) + al256(nparts * pl.RT * d * sizeof(float)) +
          al256(units * rep * cap16 * sizeof(float));
 }
 
-// Workspace for every length up to nq_max: the partial count of any plan is
+// Workspace for every length up to nr_max: the partial count of any plan is
 // at most max(4, blocks-per-unit) + 1 splits per (sequence, kv head, tile)
-// (head tiles take up to 4 splits when fewer than two blocks per unit fit).
-size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nq_max,
-                       int imp_bits) {
+// (head tiles take up to 4 splits when fewer than two blocks per unit fit),
+// plus the buffer split of per-channel key tiles, plus the low-bit splits that
+// the LDS table of per-channel key tiles may add (one per kt_max_tiles tiles).
+size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nr_max,
+                       int imp_bits, int key_tile) {
   const int rep = hq / hkv;
-  DecodePlan pl = decode_plan(batch, hkv, d, bits, group, rep, cap16, nq_max, imp_bits);
+  DecodePlan pl = decode_plan(batch, hkv, d, bits, group, rep, cap16, nr_max, imp_bits, key_tile);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
   long per_unit = (static_cast<long>(device_cus()) * MIKV_BLOCKS_PER_CU) / units;
   if (per_unit < 4) per_unit = 4;
-  pl.S16 = static_cast<int>(per_unit + 1);
+  long extra = 0;
+  if (key_tile) extra = 1 + cdiv(nr_max, kt_max_tiles(d, 4) * kKeyTile);
+  pl.S16 = static_cast<int>(per_unit + 1 + extra);
   pl.Sq = 0;
+  pl.Sb = 0;
   return decode_ws_bytes(batch, hq, hkv, d, cap16, pl);
 }
 
-template <int D, int BITS, int IB, int RT>
+template <int D, int BITS, int IB, int RT, bool KT>
 static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
   DecodeK k;
   k.hq = a.hq; k.hkv = a.hkv; k.rep = a.hq / a.hkv; k.cap16 = a.cap16; k.capq = a.capq;
-  k.nq = a.len - a.cap16; k.len = a.len; k.group = a.group; k.units = a.batch * a.hkv;
+  k.nq = pl.nq; k.len = a.len; k.group = a.group; k.units = a.batch * a.hkv;
+  k.Sb = pl.Sb; k.nb = pl.nb;
+  k.kcsz = reinterpret_cast<const uint32_t*>(a.kcsz);
+  k.kbuf = a.kbuf; k.vbuf = a.vbuf;
   k.S16 = pl.S16; k.Sq = pl.Sq; k.C16 = pl.C16; k.Cq = pl.Cq; k.tiles = pl.tiles; k.f16_first = pl.f16_first;
   k.q = a.q; k.k_new = a.k_new; k.v_new = a.v_new; k.b = a.b;
   k.k16 = a.k16; k.v16 = a.v16; k.pos16 = a.pos16; k.free16 = a.free16;
@@ -1131,7 +1244,7 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   k.vimpsz = reinterpret_cast<uint32_t*>(a.vimpsz);
   k.o = a.o; k.p16 = a.p16;
   const size_t units = static_cast<size_t>(a.batch) * a.hkv;
-  const int S = pl.S16 + pl.Sq;
+  const int S = pl.S16 + pl.Sq + pl.Sb;
   const size_t nparts = units * pl.tiles * S;
   char* w = static_cast<char*>(a.ws);
   k.part_ml = reinterpret_cast<float2*>(w);
@@ -1143,26 +1256,26 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
   // IB < 16 (a code importance tier): decode_tile_kernel for every tile;
   // IB = 16: the tile kernel for head tiles of groups d/2, else the split kernel
   constexpr bool kTileAlways = IB < 16;
-  const bool tile = kTileAlways || use_tile_kernel(D, a.group, RT, IB);
+  const bool tile = !KT && (kTileAlways || use_tile_kernel(D, a.group, RT, IB, 0));
   const void* kfn = tile ? split_kernel_ptr<D, BITS, IB, RT, (kTileAlways || RT > 1)>()
-                         : split_kernel_ptr<D, BITS, IB, RT, false>();
+                         : split_kernel_ptr<D, BITS, IB, RT, false, KT>();
   if (a.ev_split_start || a.ev_split_stop) {
     // the events take the kernel's own start and end timestamps
     void* args[] = {&k};
     e = hipExtLaunchKernel(kfn, dim3(static_cast<unsigned>(nparts)), dim3(kThreads), args, 0, stream,
                            a.ev_split_start, a.ev_split_stop, 0);
   } else if (tile) {
-    if constexpr (kTileAlways || RT > 1)
+    if constexpr (!KT && (kTileAlways || RT > 1))
       decode_tile_kernel<D, BITS, IB, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
     e = hipGetLastError();
   } else {
     if constexpr (!kTileAlways)
-      decode_split_kernel<D, BITS, RT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
+      decode_split_kernel<D, BITS, RT, KT><<<static_cast<unsigned>(nparts), kThreads, 0, stream>>>(k);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
   const size_t lds = static_cast<size_t>(k.rep) * S * sizeof(float2) + 2 * k.rep * sizeof(float);
-  const bool fuse = a.fuse_h2o && a.cap16 <= kFusedMaxCap16;
+  const bool fuse = !KT && a.fuse_h2o && a.cap16 <= kFusedMaxCap16;
   H2OView hv = a.h2o;
   if (!a.fuse_h2o) hv.len = a.len, hv.recent = 0;
   // Output groups of 64 per merge block: with few splits one block takes all
@@ -1187,16 +1300,28 @@ static hipError_t launch_da(const DecodeArgs& a, const DecodePlan& pl, hipStream
     else MIKV_MERGE_G(NL_, F_, 8);            \
   } while (0)
   if (!fuse) MIKV_MERGE(D / 16, false);
-  else if (a.group == D / 2) MIKV_MERGE(D / 16, true);
-  else MIKV_MERGE(D / 8, true);
+  else if constexpr (!KT) {
+    if (a.group == D / 2) MIKV_MERGE(D / 16, true);
+    else MIKV_MERGE(D / 8, true);
+  }
 #undef MIKV_MERGE
 #undef MIKV_MERGE_G
   return hipGetLastError();
 }
 
 hipError_t launch_decode_attn(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
+  if (pl.key_tile) {
+    if (a.imp_bits != 16) return hipErrorInvalidValue;
+#define MIKV_DAK(D_, B_, RT_) \
+    if (a.d == D_ && a.bits == B_ && pl.RT == RT_) return launch_da<D_, B_, 16, RT_, true>(a, pl, stream);
+#define MIKV_DAK3(D_, B_) MIKV_DAK(D_, B_, 1) MIKV_DAK(D_, B_, 2) MIKV_DAK(D_, B_, 4)
+    MIKV_DAK3(128, 4) MIKV_DAK3(128, 2) MIKV_DAK3(64, 4) MIKV_DAK3(64, 2)
+#undef MIKV_DAK3
+#undef MIKV_DAK
+    return hipErrorInvalidValue;
+  }
 #define MIKV_DA(D_, B_, IB_, RT_) \
-  if (a.d == D_ && a.bits == B_ && a.imp_bits == IB_ && pl.RT == RT_) return launch_da<D_, B_, IB_, RT_>(a, pl, stream);
+  if (a.d == D_ && a.bits == B_ && a.imp_bits == IB_ && pl.RT == RT_) return launch_da<D_, B_, IB_, RT_, false>(a, pl, stream);
 #define MIKV_DA3(D_, B_, IB_) MIKV_DA(D_, B_, IB_, 1) MIKV_DA(D_, B_, IB_, 2) MIKV_DA(D_, B_, IB_, 4)
   MIKV_DA3(128, 4, 16) MIKV_DA3(128, 2, 16) MIKV_DA3(64, 4, 16) MIKV_DA3(64, 2, 16)
   if (a.group == a.d / 2) {

@@ -518,7 +518,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 template <int D, int BITS, int IB, int RT>
 __global__ __launch_bounds__(kThreads, 3) void decode_tile_kernel(const DecodeK p) {
   // block order as decode_split_kernel (split-major)
-  const int S = p.S16 + p.Sq;
+  const int S = p.S16 + p.Sq + p.Sb;
   const int ut = p.units * p.tiles;
   const int sd = blockIdx.x / ut;
   const int split = p.f16_first ? sd : ((sd < p.Sq) ? p.S16 + sd : sd - p.Sq);

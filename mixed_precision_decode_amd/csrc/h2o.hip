@@ -30,7 +30,25 @@ namespace mikv {
 // thread, the common case), so the select costs one memory round trip and the
 // demotion a second one.
 constexpr int kH2OSlots = 16;
-template <int D, int BITS, int NL, int IB>
+// The cache views of the H2O args as the shared select/demote code takes them.
+static __device__ __forceinline__ H2OView h2o_view(const H2OArgs& a, int IB) {
+  H2OView v;
+  v.cap16 = a.cap16; v.capq = a.capq; v.len = a.len; v.recent = a.recent; v.imp_bits = IB;
+  v.k16 = a.k16; v.v16 = a.v16; v.pos16 = a.pos16; v.acc16 = a.acc16; v.free16 = a.free16;
+  v.kimp = a.kimp; v.vimp = a.vimp;
+  v.kimpsz = reinterpret_cast<uint32_t*>(a.kimpsz);
+  v.vimpsz = reinterpret_cast<uint32_t*>(a.vimpsz);
+  v.kq = a.kq; v.vq = a.vq;
+  v.ksz = reinterpret_cast<uint32_t*>(a.ksz);
+  v.vsz = reinterpret_cast<uint32_t*>(a.vsz);
+  v.posq = a.posq; v.demoted_pos = a.demoted_pos;
+  v.key_tile = a.key_tile;
+  v.kcsz = reinterpret_cast<uint32_t*>(a.kcsz);
+  v.kbuf = a.kbuf; v.vbuf = a.vbuf; v.posbuf = a.posbuf;
+  return v;
+}
+
+template <int D, int BITS, int NL, int IB, bool KT>
 __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
   const int unit = blockIdx.x;
   const int tid = threadIdx.x;
@@ -63,17 +81,7 @@ __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
   } else {
     for (int s = tid; s < a.cap16; s += 256) consider(s, accin[s], p16[s], pos16[s]);
   }
-  H2OView v;
-  v.cap16 = a.cap16; v.capq = a.capq; v.len = a.len; v.recent = a.recent; v.imp_bits = IB;
-  v.k16 = a.k16; v.v16 = a.v16; v.pos16 = a.pos16; v.acc16 = a.acc16; v.free16 = a.free16;
-  v.kimp = a.kimp; v.vimp = a.vimp;
-  v.kimpsz = reinterpret_cast<uint32_t*>(a.kimpsz);
-  v.vimpsz = reinterpret_cast<uint32_t*>(a.vimpsz);
-  v.kq = a.kq; v.vq = a.vq;
-  v.ksz = reinterpret_cast<uint32_t*>(a.ksz);
-  v.vsz = reinterpret_cast<uint32_t*>(a.vsz);
-  v.posq = a.posq; v.demoted_pos = a.demoted_pos;
-  h2o_select_demote<D, BITS, NL>(w, v, unit, fr);
+  h2o_select_demote<D, BITS, NL, KT>(w, h2o_view(a, IB), unit, fr);
 }
 
 // ------------------------------------------------------------------ prefill
@@ -104,6 +112,8 @@ __global__ __launch_bounds__(kSelThreads) void h2o_prefill_select_kernel(H2OArgs
   const int64_t base16 = static_cast<int64_t>(unit) * a.cap16;
   const int64_t baseq = static_cast<int64_t>(unit) * a.capq;
   int32_t* umap = map + static_cast<int64_t>(unit) * T;
+  // per-channel key tiles: retained ranks from nq0 on start the buffer
+  const int nq0 = a.key_tile ? (T - (a.cap16 - 1)) / kKeyTile * kKeyTile : INT_MAX;
   for (int p0 = 0; p0 < T; p0 += kSelThreads * kSelRun) {
     const int base = p0 + tid * kSelRun;
     float av[kSelRun];
@@ -150,7 +160,10 @@ __global__ __launch_bounds__(kSelThreads) void h2o_prefill_select_kernel(H2OArgs
           // positions before p that were not kept
           const int slot = p - krank;
           const bool ok = slot < a.capq;
-          if (ok) a.posq[baseq + slot] = p;
+          if (ok) {
+            if (slot < nq0) a.posq[baseq + slot] = p;
+            else a.posbuf[static_cast<int64_t>(unit) * kKeyTile + (slot - nq0)] = p;
+          }
           umap[p] = ok ? -1 - slot : INT_MIN;
         }
       }
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(kSelThreads) void h2o_prefill_select_kernel(H2OArgs
 // 16 blocks of 256 threads per compute unit (measured best among 1024-65536)
 constexpr int64_t kScatterBlocks = MIKV_SCATTER_BLOCKS;
 
-template <int D, int BITS, int NL, int IB>
+template <int D, int BITS, int NL, int IB, bool KT>
 __global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int T,
                                                                   const int32_t* map) {
   constexpr int LPR = D / 8;
@@ -270,6 +283,23 @@ __global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int
           reinterpret_cast<uint32_t*>(a.vimpsz)[si * GPT + lane / NL] = vszw;
         }
       }
+    } else if (KT && R.s != INT_MIN) {
+      // per-channel key tiles: values per token into the tile slots (the
+      // keys follow per tile in h2o_key_tile_kernel); the last (T - B) mod 64
+      // retained pairs go to the buffer as fp16
+      const int slot = -1 - R.s;
+      const int nq0 = (T - (a.cap16 - 1)) / kKeyTile * kKeyTile;
+      if (slot < nq0) {
+        uint32_t vszw;
+        const uint32_t vp = quantize8<BITS, NL>(vx, &vszw);
+        const int64_t qs = unit * a.capq + slot;
+        store_codes8<BITS>(a.vq + qs * CB, lane, vp);
+        if (lane % NL == 0) reinterpret_cast<uint32_t*>(a.vsz)[qs * GPT + lane / NL] = vszw;
+      } else {
+        const int64_t ob = (unit * kKeyTile + (slot - nq0)) * D + lane * 8;
+        *reinterpret_cast<uint4*>(a.kbuf + ob) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+        *reinterpret_cast<uint4*>(a.vbuf + ob) = R.v;
+      }
     } else if (R.s != INT_MIN) {
       uint32_t kszw, vszw;
       const uint32_t kp = quantize8<BITS, NL>(kx, &kszw);
@@ -309,17 +339,56 @@ __global__ __launch_bounds__(256) void h2o_prefill_scatter_kernel(H2OArgs a, int
   }
 }
 
+// Prefill key tiles: one block per (sequence, kv head, tile of 64 retained
+// positions). The balanced key rows of the tile's positions (posq, written by
+// the select kernel) are gathered into LDS and quantized per channel.
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void h2o_key_tile_kernel(H2OArgs a, int T, int tiles) {
+  __shared__ uint16_t s_x[kKeyTile * D];
+  __shared__ uint8_t s_c[kKeyTile * D];
+  __shared__ int s_pos[kKeyTile];
+  constexpr int LPR = D / 8, CB = D * BITS / 8;
+  const int unit = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int tid = threadIdx.x;
+  const int64_t q0 = static_cast<int64_t>(unit) * a.capq + static_cast<int64_t>(tile) * kKeyTile;
+  // positions are clamped into the prompt, so that a selection error could
+  // only give a wrong result, never a read outside src_k
+  if (tid < kKeyTile) s_pos[tid] = min(max(a.posq[q0 + tid], 0), T - 1);
+  __syncthreads();
+  const float* bvec = a.src_b ? a.src_b + static_cast<int64_t>(unit) * D : nullptr;
+  for (int i = tid; i < kKeyTile * LPR; i += 256) {
+    const int t = i / LPR, lane = i % LPR;
+    const int64_t r = static_cast<int64_t>(unit) * T + s_pos[t];
+    uint4 w = *reinterpret_cast<const uint4*>(a.src_k + r * D + lane * 8);
+    if (bvec) {
+      uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = h2f(f2h(mul_rn(lo_h(ww[j]), bvec[lane * 8 + 2 * j])));
+        const float hi = h2f(f2h(mul_rn(hi_h(ww[j]), bvec[lane * 8 + 2 * j + 1])));
+        ww[j] = static_cast<uint32_t>(f2h(lo)) | (static_cast<uint32_t>(f2h(hi)) << 16);
+      }
+      w = make_uint4(ww[0], ww[1], ww[2], ww[3]);
+    }
+    *reinterpret_cast<uint4*>(s_x + t * D + lane * 8) = w;
+  }
+  __syncthreads();
+  quantize_key_tile<D, BITS>(s_x, s_c, a.kq + q0 * CB,
+                             reinterpret_cast<uint32_t*>(a.kcsz) +
+                                 (static_cast<int64_t>(unit) * (a.capq / kKeyTile) + tile) * D);
+}
+
 size_t h2o_ws_bytes(int batch, int hkv, int T) {
   return static_cast<size_t>(batch) * hkv * (T > 0 ? T : 1) * sizeof(int32_t);
 }
 
-template <int D, int BITS, int NL, int IB>
+template <int D, int BITS, int NL, int IB, bool KT>
 static hipError_t launch_dec(const H2OArgs& a, hipStream_t stream) {
-  h2o_decode_kernel<D, BITS, NL, IB><<<a.batch * a.hkv, 256, 0, stream>>>(a);
+  h2o_decode_kernel<D, BITS, NL, IB, KT><<<a.batch * a.hkv, 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
-template <int D, int BITS, int NL, int IB>
+template <int D, int BITS, int NL, int IB, bool KT>
 static hipError_t launch_pre(const H2OArgs& a, hipStream_t stream) {
   const int T = a.len;
   int32_t* map = static_cast<int32_t*>(a.ws);
@@ -330,29 +399,48 @@ static hipError_t launch_pre(const H2OArgs& a, hipStream_t stream) {
   const int64_t n_rows = static_cast<int64_t>(a.batch) * a.hkv * T;
   int64_t blocks = (n_rows + RPB - 1) / RPB;
   if (blocks > kScatterBlocks) blocks = kScatterBlocks;
-  h2o_prefill_scatter_kernel<D, BITS, NL, IB><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(a, T, map);
-  return hipGetLastError();
+  h2o_prefill_scatter_kernel<D, BITS, NL, IB, KT><<<static_cast<unsigned>(blocks), 256, 0, stream>>>(a, T, map);
+  e = hipGetLastError();
+  if constexpr (KT) {
+    const int tiles = (T - (a.cap16 - 1)) / kKeyTile;
+    if (e == hipSuccess && tiles > 0)
+      h2o_key_tile_kernel<D, BITS><<<static_cast<unsigned>(a.batch * a.hkv * tiles), 256, 0, stream>>>(a, T, tiles);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 #define MIKV_H2O_DISPATCH(FN)                                                          \
+  if (a.key_tile) {                                                                    \
+    if (a.imp_bits != 16) return hipErrorInvalidValue;                                 \
+    if (a.d == 128 && a.bits == 4 && a.group == 64) return FN<128, 4, 8, 16, true>(a, stream);  \
+    if (a.d == 128 && a.bits == 4 && a.group == 128) return FN<128, 4, 16, 16, true>(a, stream); \
+    if (a.d == 128 && a.bits == 2 && a.group == 64) return FN<128, 2, 8, 16, true>(a, stream);  \
+    if (a.d == 128 && a.bits == 2 && a.group == 128) return FN<128, 2, 16, 16, true>(a, stream); \
+    if (a.d == 64 && a.bits == 4 && a.group == 32) return FN<64, 4, 4, 16, true>(a, stream);    \
+    if (a.d == 64 && a.bits == 4 && a.group == 64) return FN<64, 4, 8, 16, true>(a, stream);    \
+    if (a.d == 64 && a.bits == 2 && a.group == 32) return FN<64, 2, 4, 16, true>(a, stream);    \
+    if (a.d == 64 && a.bits == 2 && a.group == 64) return FN<64, 2, 8, 16, true>(a, stream);    \
+    return hipErrorInvalidValue;                                                       \
+  }                                                                                    \
   if (a.imp_bits == 16) {                                                              \
-    if (a.d == 128 && a.bits == 4 && a.group == 64) return FN<128, 4, 8, 16>(a, stream);  \
-    if (a.d == 128 && a.bits == 4 && a.group == 128) return FN<128, 4, 16, 16>(a, stream); \
-    if (a.d == 128 && a.bits == 2 && a.group == 64) return FN<128, 2, 8, 16>(a, stream);  \
-    if (a.d == 128 && a.bits == 2 && a.group == 128) return FN<128, 2, 16, 16>(a, stream); \
-    if (a.d == 64 && a.bits == 4 && a.group == 32) return FN<64, 4, 4, 16>(a, stream);    \
-    if (a.d == 64 && a.bits == 4 && a.group == 64) return FN<64, 4, 8, 16>(a, stream);    \
-    if (a.d == 64 && a.bits == 2 && a.group == 32) return FN<64, 2, 4, 16>(a, stream);    \
-    if (a.d == 64 && a.bits == 2 && a.group == 64) return FN<64, 2, 8, 16>(a, stream);    \
+    if (a.d == 128 && a.bits == 4 && a.group == 64) return FN<128, 4, 8, 16, false>(a, stream);  \
+    if (a.d == 128 && a.bits == 4 && a.group == 128) return FN<128, 4, 16, 16, false>(a, stream); \
+    if (a.d == 128 && a.bits == 2 && a.group == 64) return FN<128, 2, 8, 16, false>(a, stream);  \
+    if (a.d == 128 && a.bits == 2 && a.group == 128) return FN<128, 2, 16, 16, false>(a, stream); \
+    if (a.d == 64 && a.bits == 4 && a.group == 32) return FN<64, 4, 4, 16, false>(a, stream);    \
+    if (a.d == 64 && a.bits == 4 && a.group == 64) return FN<64, 4, 8, 16, false>(a, stream);    \
+    if (a.d == 64 && a.bits == 2 && a.group == 32) return FN<64, 2, 4, 16, false>(a, stream);    \
+    if (a.d == 64 && a.bits == 2 && a.group == 64) return FN<64, 2, 8, 16, false>(a, stream);    \
   } else if (a.group == a.d / 2) {                                                     \
-    if (a.d == 128 && a.bits == 4 && a.imp_bits == 8) return FN<128, 4, 8, 8>(a, stream); \
-    if (a.d == 128 && a.bits == 4 && a.imp_bits == 4) return FN<128, 4, 8, 4>(a, stream); \
-    if (a.d == 128 && a.bits == 2 && a.imp_bits == 8) return FN<128, 2, 8, 8>(a, stream); \
-    if (a.d == 128 && a.bits == 2 && a.imp_bits == 4) return FN<128, 2, 8, 4>(a, stream); \
-    if (a.d == 64 && a.bits == 4 && a.imp_bits == 8) return FN<64, 4, 4, 8>(a, stream);   \
-    if (a.d == 64 && a.bits == 4 && a.imp_bits == 4) return FN<64, 4, 4, 4>(a, stream);   \
-    if (a.d == 64 && a.bits == 2 && a.imp_bits == 8) return FN<64, 2, 4, 8>(a, stream);   \
-    if (a.d == 64 && a.bits == 2 && a.imp_bits == 4) return FN<64, 2, 4, 4>(a, stream);   \
+    if (a.d == 128 && a.bits == 4 && a.imp_bits == 8) return FN<128, 4, 8, 8, false>(a, stream); \
+    if (a.d == 128 && a.bits == 4 && a.imp_bits == 4) return FN<128, 4, 8, 4, false>(a, stream); \
+    if (a.d == 128 && a.bits == 2 && a.imp_bits == 8) return FN<128, 2, 8, 8, false>(a, stream); \
+    if (a.d == 128 && a.bits == 2 && a.imp_bits == 4) return FN<128, 2, 8, 4, false>(a, stream); \
+    if (a.d == 64 && a.bits == 4 && a.imp_bits == 8) return FN<64, 4, 4, 8, false>(a, stream);   \
+    if (a.d == 64 && a.bits == 4 && a.imp_bits == 4) return FN<64, 4, 4, 4, false>(a, stream);   \
+    if (a.d == 64 && a.bits == 2 && a.imp_bits == 8) return FN<64, 2, 4, 8, false>(a, stream);   \
+    if (a.d == 64 && a.bits == 2 && a.imp_bits == 4) return FN<64, 2, 4, 4, false>(a, stream);   \
   }                                                                                    \
   return hipErrorInvalidValue;
 

@@ -27,7 +27,72 @@ struct H2OView {
   uint32_t* vsz;
   int32_t* posq;
   int32_t* demoted_pos;
+  // per-channel key tiles (key_tile = 64): kq rows hold tiles of 64 tokens
+  // whose (scale | zero << 16) words are kcsz [tile][d]; demoted pairs wait
+  // in kbuf / vbuf [64][d] fp16 (positions posbuf) until a tile fills
+  int key_tile;
+  uint32_t* kcsz;
+  uint16_t* kbuf;
+  uint16_t* vbuf;
+  int32_t* posbuf;
 };
+
+constexpr int kKeyTile = 64;
+
+// Per-channel quantization of one tile of keys (velog notes "No Token Left
+// Behind ...", the per-channel alternative and its appendix C summary;
+// paperlayer summary of arXiv 2402.18096, appendix C: per-channel key
+// quantization with groups of 64 along the tokens). xs: LDS [64][D] fp16
+// rows of the tile, token-major; cl: LDS [64][D] bytes of scratch. Channel c
+// is one quantization group of 64 values, held as 8 tokens by each of 8
+// consecutive lanes, so quantize8_codes applies the per-token rule (same
+// fixed fp32 sequence) along the tokens. The codes are packed token-major
+// like per-token rows into kq_tile [64][D*BITS/8]; (scale | zero << 16) of
+// channel c goes to kcsz_tile[c]. All 256 threads of the block call it.
+template <int D, int BITS>
+__device__ __forceinline__ void quantize_key_tile(const uint16_t* xs, uint8_t* cl, uint8_t* kq_tile,
+                                                  uint32_t* kcsz_tile) {
+  const int tid = threadIdx.x;
+  const int l8 = tid % 8;  // tokens 8*l8 .. 8*l8 + 7 of the lane's channel
+  static_assert(D % 32 == 0, "32 channels per pass");
+  for (int c = tid / 8; c < D; c += 32) {  // the same trip count on every lane
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = h2f(xs[(8 * l8 + e) * D + c]);
+    uint32_t szw, code[8];
+    quantize8_codes<BITS, 8>(x, &szw, code);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cl[(8 * l8 + e) * D + c] = static_cast<uint8_t>(code[e]);
+    if (l8 == 0) kcsz_tile[c] = szw;
+  }
+  __syncthreads();
+  constexpr int CPW = 32 / BITS, WPR = D / CPW, CB = D * BITS / 8;
+  for (int i = tid; i < kKeyTile * WPR; i += 256) {
+    const int t = i / WPR, w = i % WPR;
+    uint32_t word = 0;
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) word |= static_cast<uint32_t>(cl[t * D + w * CPW + m]) << (BITS * m);
+    reinterpret_cast<uint32_t*>(kq_tile + static_cast<int64_t>(t) * CB)[w] = word;
+  }
+}
+
+// Per-token quantization of 64 value rows into the low-bit slots of a tile:
+// rows t < 63 from vsrc [63][D] (global), row 63 from vlast; LPR = D/8 lanes
+// per row, groups of NL lanes.
+template <int D, int BITS, int NL>
+__device__ __forceinline__ void quantize_value_tile(const uint16_t* vsrc, const uint16_t* vlast, uint8_t* vq_tile,
+                                                    uint32_t* vsz_tile) {
+  constexpr int LPR = D / 8, RPP = 256 / LPR, CB = D * BITS / 8, GPT = D / (8 * NL);
+  const int tid = threadIdx.x, lane = tid % LPR;
+  for (int t = tid / LPR; t < kKeyTile; t += RPP) {  // rows stay whole within a pass
+    float x[8];
+    load8((t < kKeyTile - 1 ? vsrc + static_cast<int64_t>(t) * D : vlast) + lane * 8, x);
+    uint32_t szw;
+    const uint32_t packed = quantize8<BITS, NL>(x, &szw);
+    store_codes8<BITS>(vq_tile + static_cast<int64_t>(t) * CB, lane, packed);
+    if (lane % NL == 0) vsz_tile[t * GPT + lane / NL] = szw;
+  }
+}
 
 // Running "worst candidate" of a thread: smallest accumulated score, latest
 // position among equal scores (the one a top-H re-select by (acc desc,
@@ -61,7 +126,45 @@ __device__ __forceinline__ void imp_row16(const H2OView& v, bool is_v, int64_t s
   for (int e = 0; e < 8; ++e) x[e] = h2f(f2h(fmaf(static_cast<float>(code_of<IB>(cw, e)), s, z)));
 }
 
+// Per-channel key tiles: the dropped pair goes to buffer row r = (len -
+// cap16) mod 64 as fp16; when r is the last row the buffer becomes tile
+// (len - cap16) / 64 (keys per channel, values per token, posq from posbuf),
+// its last row taken from the importance slot itself.
 template <int D, int BITS, int NL>
+__device__ __forceinline__ void demote_to_buffer(const H2OView& v, int unit, int drop, int pos) {
+  __shared__ uint16_t s_x[kKeyTile * D];
+  __shared__ uint8_t s_c[kKeyTile * D];
+  constexpr int LPR = D / 8;
+  const int tid = threadIdx.x;
+  const int D0 = v.len - v.cap16;  // retained tokens before this demotion
+  const int r = D0 % kKeyTile, tile = D0 / kKeyTile;
+  const int64_t base16 = static_cast<int64_t>(unit) * v.cap16;
+  const int64_t bb = static_cast<int64_t>(unit) * kKeyTile;
+  const uint16_t* krow = v.k16 + (base16 + drop) * D;
+  const uint16_t* vrow = v.v16 + (base16 + drop) * D;
+  if (tid < 2 * LPR) {
+    const bool is_v = tid >= LPR;
+    const int lane = tid % LPR;
+    const uint4 x = *reinterpret_cast<const uint4*>((is_v ? vrow : krow) + lane * 8);
+    *reinterpret_cast<uint4*>((is_v ? v.vbuf : v.kbuf) + (bb + r) * D + lane * 8) = x;
+  }
+  if (tid == 0) v.posbuf[bb + r] = pos;
+  if (r != kKeyTile - 1) return;  // uniform
+  for (int i = tid; i < kKeyTile * LPR; i += 256) {
+    const int t = i / LPR, lane = i % LPR;
+    const uint16_t* src = (t < kKeyTile - 1) ? v.kbuf + (bb + t) * D : krow;
+    *reinterpret_cast<uint4*>(s_x + t * D + lane * 8) = *reinterpret_cast<const uint4*>(src + lane * 8);
+  }
+  __syncthreads();
+  constexpr int CB = D * BITS / 8, GPT = D / (8 * NL);
+  const int64_t q0 = static_cast<int64_t>(unit) * v.capq + static_cast<int64_t>(tile) * kKeyTile;
+  quantize_key_tile<D, BITS>(s_x, s_c, v.kq + q0 * CB,
+                             v.kcsz + (static_cast<int64_t>(unit) * (v.capq / kKeyTile) + tile) * D);
+  quantize_value_tile<D, BITS, NL>(v.vbuf + bb * D, vrow, v.vq + q0 * CB, v.vsz + q0 * GPT);
+  for (int t = tid; t < kKeyTile; t += 256) v.posq[q0 + t] = (t < kKeyTile - 1) ? v.posbuf[bb + t] : pos;
+}
+
+template <int D, int BITS, int NL, bool KT = false>
 __device__ void h2o_select_demote(Worst w, const H2OView& v, int unit, int fr) {
   __shared__ float s_acc[4];
   __shared__ int s_pos[4];
@@ -86,6 +189,16 @@ __device__ void h2o_select_demote(Worst w, const H2OView& v, int unit, int fr) {
   __syncthreads();
   const int drop = s_drop;
   if (drop < 0) return;  // unreachable when heavy + recent == cap16 - 1
+  if constexpr (KT) {
+    const int64_t b16 = static_cast<int64_t>(unit) * v.cap16;
+    const int pos = (drop == fr) ? v.len - 1 : v.pos16[b16 + drop];
+    if (tid == 0) {
+      v.free16[unit] = drop;
+      if (v.demoted_pos) v.demoted_pos[unit] = pos;
+    }
+    demote_to_buffer<D, BITS, NL>(v, unit, drop, pos);
+    return;
+  }
   constexpr int LPR = D / 8;
   constexpr int CB = D * BITS / 8;
   constexpr int GPT = D / (8 * NL);

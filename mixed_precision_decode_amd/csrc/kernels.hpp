@@ -25,13 +25,17 @@ struct DecodePlan {
   int RT;          // query heads per block
   int tiles;       // rep / RT
   int f16_first;   // 1: FP16-tier splits take the first block indices (else the low-bit splits do)
+  int nq;          // low-bit tokens attended (per-channel key tiles: whole tiles only)
+  int nb, Sb;      // per-channel key tiles: buffered fp16 pairs and their splits (0 or 1)
+  int key_tile;    // 0: per-token keys; 64: per-channel key tiles
 };
-DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nq,
-                       int imp_bits);
+// nr = retained tokens when the step starts (len - cap16)
+DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, int cap16, int nr,
+                       int imp_bits, int key_tile);
 size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int cap16, const DecodePlan& plan);
-// workspace that serves every length up to nq_max low-bit tokens
-size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nq_max,
-                       int imp_bits);
+// workspace that serves every length up to nr_max retained tokens
+size_t decode_ws_bound(int batch, int hq, int hkv, int d, int bits, int group, int cap16, int nr_max,
+                       int imp_bits, int key_tile);
 
 struct DecodeArgs {
   int batch, hq, hkv, d, group, bits, cap16, capq, len;
@@ -55,6 +59,11 @@ struct DecodeArgs {
   float* o;
   float* p16;
   void* ws;
+  // per-channel key tiles (key_tile = 64)
+  int key_tile;
+  const uint16_t* kcsz;
+  const uint16_t* kbuf;
+  const uint16_t* vbuf;
   // fused decode step: the merge kernel also runs the H2O update, re-select
   // and demotion (fuse_h2o = true; h2o holds the cache views it writes)
   bool fuse_h2o;
@@ -90,6 +99,12 @@ struct H2OArgs {
   int32_t* posq;
   const float* p16;
   int32_t* demoted_pos;
+  // per-channel key tiles (key_tile = 64; 0 = per-token keys)
+  int key_tile;
+  uint16_t* kcsz;
+  uint16_t* kbuf;
+  uint16_t* vbuf;
+  int32_t* posbuf;
   // prefill
   const uint16_t* src_k;
   const uint16_t* src_v;

@@ -66,6 +66,7 @@ class DecodeConfig:
     factor: float     # outlier magnitude multiplier
     group: int = 0    # channels per quantization group (0: d/2)
     imp_bits: int = 16  # importance tier: 16 = fp16 rows, 8 or 4 = codes
+    key_tile: int = 0   # 0: per-token keys; 64: per-channel key tiles + token buffer
 
     @property
     def rep(self) -> int:
@@ -90,7 +91,10 @@ class DecodeConfig:
 
     def capq(self, steps: int | None = None) -> int:
         s = self.steps if steps is None else steps
-        return self.T - self.B + s
+        c = self.T - self.B + s
+        if self.key_tile:  # whole tiles
+            c = -(-c // self.key_tile) * self.key_tile
+        return c
 
     def scaled(self, **kw) -> "DecodeConfig":
         return dataclasses.replace(self, **kw)
@@ -129,6 +133,12 @@ CONFIGS = {
     "llama2_7b_imp8": DecodeConfig("llama2_7b_imp8", batch=8, hq=32, hkv=32, d=128, T=4096,
                                    bits=2, pct=20, recent=64, steps=128, pairs=2, factor=20.0,
                                    imp_bits=8),
+    # per-channel key quantization over 64-token tiles with the fp16 token
+    # buffer, 20% importance (the setting of appendix C on the paperlayer
+    # page), on the Llama-2-7B layer shape
+    "llama2_7b_kchan": DecodeConfig("llama2_7b_kchan", batch=8, hq=32, hkv=32, d=128, T=4096,
+                                    bits=4, pct=20, recent=64, steps=128, pairs=2, factor=20.0,
+                                    key_tile=64),
 }
 
 CKV_CONFIGS = {

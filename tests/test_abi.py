@@ -36,7 +36,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.mikv_abi_version() == 3
+    assert lib.mikv_abi_version() == 4
     for s in range(8):
         assert len(L.mikv_status_str(s)) > 0
     assert L.mikv_status_str(99) == "unknown status"
@@ -157,6 +157,47 @@ def test_importance_codes_validation(lib):
     h2o = lambda dims, cache: lib.mikv_h2o_update_select(
         C.byref(dims.c()), C.byref(cache), 50, 4, 6, FAKE, None, None, None, 0, None)
     assert h2o(_dims(imp_bits=8), no_imp) == L.MIKV_ERR_NULL
+
+
+def test_key_tile_validation(lib):
+    """key_tile: 0 = per-token keys, 64 = per-channel key tiles (fp16
+    importance tier, capq a whole number of tiles, the kcsz/kbuf/vbuf/posbuf
+    pointers; ksz may then be NULL); anything else is refused before a
+    launch."""
+    kt = _dims(key_tile=64, capq=128)
+    need = lib.mikv_decode_attn_workspace(C.byref(kt.c()), 80)
+    assert need > 0
+    full = L.MikvCache(*([FAKE] * 18))
+    call = lambda dims, cache=full: lib.mikv_decode_attn(
+        C.byref(dims.c()), C.byref(cache), 50, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None)
+    assert call(_dims(key_tile=32, capq=128)) == L.MIKV_ERR_UNSUPPORTED
+    assert call(_dims(key_tile=1, capq=128)) == L.MIKV_ERR_UNSUPPORTED
+    assert call(_dims(key_tile=64, capq=100)) == L.MIKV_ERR_SHAPE
+    assert call(_dims(key_tile=64, capq=128, imp_bits=8)) == L.MIKV_ERR_UNSUPPORTED
+    no_kt = L.MikvCache(*([FAKE] * 14 + [0] * 4))
+    assert call(kt, no_kt) == L.MIKV_ERR_NULL
+    for i in range(4):  # each of kcsz, kbuf, vbuf, posbuf
+        ptrs = [FAKE] * 18
+        ptrs[14 + i] = 0
+        assert call(kt, L.MikvCache(*ptrs)) == L.MIKV_ERR_NULL, i
+    mis = [FAKE] * 18
+    mis[15] = FAKE + 4  # kbuf not 16-byte aligned
+    assert call(kt, L.MikvCache(*mis)) == L.MIKV_ERR_SHAPE
+    # per-channel keys need no per-token key scales: a NULL ksz passes the
+    # cache checks (the call then stops at the missing workspace)
+    no_ksz = [FAKE] * 18
+    no_ksz[7] = 0
+    assert lib.mikv_decode_attn(C.byref(kt.c()), C.byref(L.MikvCache(*no_ksz)), 50, FAKE, FAKE, FAKE, FAKE,
+                                FAKE, FAKE, None, need, None) == L.MIKV_ERR_WORKSPACE
+    assert call(_dims(capq=128), L.MikvCache(*no_ksz)) == L.MIKV_ERR_NULL  # per-token keys need ksz
+    step = lambda dims, cache: lib.mikv_decode_step(
+        C.byref(dims.c()), C.byref(cache), 50, 4, 6, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16, None)
+    assert step(kt, no_kt) == L.MIKV_ERR_NULL
+    assert step(kt, full) == L.MIKV_ERR_WORKSPACE
+    h2o = lambda dims, cache: lib.mikv_h2o_update_select(
+        C.byref(dims.c()), C.byref(cache), 50, 4, 6, FAKE, None, None, None, 0, None)
+    assert h2o(kt, no_kt) == L.MIKV_ERR_NULL
+    assert h2o(_dims(key_tile=64, capq=96), full) == L.MIKV_ERR_SHAPE
 
 
 def test_perturbation_validation(lib):

@@ -48,7 +48,8 @@ def assert_close(gpu, ref, what, floor=0.0):
 
 def dims_of(cfg, capq=None):
     return L.Dims(batch=cfg.batch, hq=cfg.hq, hkv=cfg.hkv, d=cfg.d, group=cfg.G, bits=cfg.bits,
-                  cap16=cfg.cap16, capq=cfg.capq() if capq is None else capq, imp_bits=cfg.imp_bits)
+                  cap16=cfg.cap16, capq=cfg.capq() if capq is None else capq, imp_bits=cfg.imp_bits,
+                  key_tile=cfg.key_tile)
 
 
 # ---------------------------------------------------------------- quantize
@@ -143,10 +144,13 @@ def _state_equal(gpu, ref):
     for key in ("pos16", "free16", "posq"):
         assert np.array_equal(gpu[key], ref[key]), key
     assert np.array_equal(gpu["acc16"].view(np.uint32), ref["acc16"].view(np.uint32))
-    # fp16 importance rows or importance codes, whichever the cache holds
-    for key in ("k16", "v16", "ksz", "vsz", "kimpsz", "vimpsz"):
+    # fp16 importance rows or importance codes, whichever the cache holds;
+    # per-channel key tiles and the fp16 buffer
+    for key in ("k16", "v16", "ksz", "vsz", "kimpsz", "vimpsz", "kcsz", "kbuf", "vbuf"):
         if key in ref:
             assert np.array_equal(bits16(gpu[key]), bits16(ref[key])), key
+    if "posbuf" in ref:
+        assert np.array_equal(gpu["posbuf"], ref["posbuf"]), "posbuf"
     for key in ("kq", "vq", "kimp", "vimp"):
         if key in ref:
             assert np.array_equal(gpu[key], ref[key]), key
@@ -172,7 +176,8 @@ def test_prefill_build_parity(name, over, balanced):
         _, kb = O.balance(q, k)
     else:
         kb = k
-    ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq(), imp_bits=cfg.imp_bits)
+    ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq(), imp_bits=cfg.imp_bits,
+                           key_tile=cfg.key_tile)
     _state_equal(cache.to_numpy(), ref)
 
 
@@ -185,6 +190,7 @@ def _units_state(cache, units):
     gs = torch.tensor([u[1] for u in units], device="cuda")
     out = {k: getattr(cache, k)[ns, gs].unsqueeze(1).cpu().numpy() for k in cache.names}
     out["group"], out["bits"], out["imp_bits"] = cache.dims.group, cache.dims.bits, cache.imp_bits
+    out["key_tile"] = cache.key_tile
     return out
 
 
@@ -251,7 +257,8 @@ def _lockstep(cfg, seed, steps, balanced=True, check_every=1, fused=False, sampl
     bh = host(b)
     if gpu_scores:
         kb = O.balance(q, k)[1] if balanced else k
-        ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq(), imp_bits=cfg.imp_bits)
+        ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq(), imp_bits=cfg.imp_bits,
+                           key_tile=cfg.key_tile)
         _state_equal(cache.to_numpy(), ref)
         print(f"  prefill build on the device's prompt scores matches the oracle", flush=True)
     del q, k, v
@@ -371,7 +378,8 @@ def test_prefill_build_importance_codes(name, over):
     print(f"prefill (importance codes) {name} {over}", flush=True)
     dims, cache, b, (q, k, v, acc0) = _prefill_gpu(cfg, 6, True)
     _, kb = O.balance(q, k)
-    ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq(), imp_bits=cfg.imp_bits)
+    ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq(), imp_bits=cfg.imp_bits,
+                           key_tile=cfg.key_tile)
     _state_equal(cache.to_numpy(), ref)
 
 
@@ -408,6 +416,62 @@ def test_decode_importance_codes_full_size(name):
     _, checked, sampled = _lockstep(cfg, 1000 + list(S.CONFIGS).index(name), 24, check_every=23,
                                     fused=True, sample=8)
     assert checked + sampled == 24
+
+
+# ---------------------------------------------------------------- per-channel key tiles
+@pytest.mark.parametrize("name,over,balanced", [
+    ("tiny", dict(key_tile=64), True),                            # 205 retained: 3 tiles + 13 buffered
+    ("tiny", dict(key_tile=64), False),
+    ("tiny", dict(key_tile=64, pct=0, recent=0), True),           # all 256 retained: 4 tiles, no buffer
+    ("tiny", dict(key_tile=64, T=40, recent=4), True),            # 32 retained: buffer only
+    ("tiny", dict(key_tile=64, bits=2, T=512, pct=25, recent=8, group=64), True),
+    ("gqa_throughput", dict(key_tile=64, batch=2, T=700), True),
+    ("llama2_7b_kchan", dict(batch=2, T=1000), True),
+    ("llama3_8b_32k", dict(key_tile=64, hq=8, hkv=2, T=3000), True),
+])
+def test_prefill_build_key_tiles(name, over, balanced):
+    """Prefill build with per-channel key tiles: tiles (codes and per-channel
+    scale and zero), per-token value codes, buffered fp16 pairs and every
+    position bit-exact against the oracle."""
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"prefill (key tiles) {name} {over} balanced={balanced}", flush=True)
+    dims, cache, b, (q, k, v, acc0) = _prefill_gpu(cfg, 8, balanced)
+    kb = O.balance(q, k)[1] if balanced else k
+    ref = O.prefill_build(kb, v, acc0, cfg.B, cfg.recent, cfg.G, cfg.bits, cfg.capq(), key_tile=64)
+    _state_equal(cache.to_numpy(), ref)
+
+
+@pytest.mark.parametrize("name,over,steps,fused", [
+    ("tiny", dict(key_tile=64), 80, False),                        # a tile flushed at step 51
+    ("tiny", dict(key_tile=64, hq=8, hkv=2), 70, True),            # four-head tiles
+    ("tiny", dict(key_tile=64, hq=4, hkv=2, bits=2), 70, True),    # two-head tiles
+    ("tiny", dict(key_tile=64, T=40, recent=4), 100, True),        # first tile formed while decoding
+    ("tiny", dict(key_tile=64, pct=0, recent=0), 70, False),       # B = 0
+    ("tiny", dict(key_tile=64, batch=3, hq=6, hkv=3, group=64, bits=2), 66, True),
+    ("gqa_throughput", dict(key_tile=64, batch=3, T=700), 70, True),
+    ("llama3_8b_32k", dict(key_tile=64, hq=8, hkv=2, T=3000), 66, True),
+    ("llama2_7b_kchan", dict(batch=2, hq=4, hkv=4, T=1000), 66, False),
+])
+def test_decode_lockstep_key_tiles(name, over, steps, fused):
+    """Decode with per-channel key tiles against the oracle at every step:
+    attention over the FP16 tier, the tiles and the buffered pairs
+    (tolerance), scores and selection, the demoted pair in its buffer row and
+    every flush of a full buffer into a tile (exact)."""
+    cfg = S.CONFIGS[name].scaled(**over, steps=steps)   # capq holds every step
+    print(f"lockstep (key tiles) {name} {over} steps={steps} fused={fused}", flush=True)
+    _lockstep(cfg, 19, steps, fused=fused)
+
+
+def test_decode_key_tiles_full_size():
+    """The per-channel key-tile workload at full size (8 x 32 heads, 4096
+    tokens, 20% importance, INT4) through mikv_decode_step over all 128
+    steps: all units every 32nd step and at the last (those include flushes
+    of every unit's buffer), 8 units at the others."""
+    cfg = S.CONFIGS["llama2_7b_kchan"]
+    print(f"full-size lockstep {cfg.name}", flush=True)
+    _, checked, sampled = _lockstep(cfg, 1000 + list(S.CONFIGS).index(cfg.name), cfg.steps, check_every=32,
+                                    fused=True, sample=8)
+    assert checked + sampled == cfg.steps
 
 
 @pytest.mark.parametrize("name,check_every", [("llama2_7b_layer", 16), ("llama3_8b_32k", 8),
