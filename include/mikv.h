@@ -385,8 +385,9 @@ mikv_status mikv_decode_step(const mikv_dims* dims, const mikv_cache* cache,
  * ws: mikv_perturbation_workspace(H, T, d, hidden) bytes (any contents).
  * Errors: keep and o_hat both or neither given, a required pointer NULL ->
  * MIKV_ERR_NULL; d not 64 or 128 -> MIKV_ERR_UNSUPPORTED; H, T, hidden < 1,
- * n_keep outside [1, T], q/K/V not 16-byte aligned, T*d*2 >= 2^31 ->
- * MIKV_ERR_SHAPE; workspace too small -> MIKV_ERR_WORKSPACE.
+ * n_keep outside [1, T], q/K/V not 16-byte aligned, T*d*2 >= 2^31,
+ * hidden*d*2 >= 2^31 - 1024 -> MIKV_ERR_SHAPE; workspace too small ->
+ * MIKV_ERR_WORKSPACE.
  */
 size_t mikv_perturbation_workspace(int32_t H, int32_t T, int32_t d, int32_t hidden);
 mikv_status mikv_output_perturbation(const uint16_t* q, const uint16_t* K,

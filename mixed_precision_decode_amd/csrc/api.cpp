@@ -395,8 +395,9 @@ mikv_status mikv_output_perturbation(const uint16_t* q, const uint16_t* K, const
   if (d != 64 && d != 128) return MIKV_ERR_UNSUPPORTED;
   if (keep && (n_keep < 1 || n_keep > T)) return MIKV_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(K) || !aligned16(V)) return MIKV_ERR_SHAPE;
-  // one head's rows are addressed with 32-bit byte offsets
+  // one head's rows (of K and V, and of W_O) are addressed with 32-bit byte offsets
   if (static_cast<int64_t>(T) * d * 2 >= (int64_t{1} << 31)) return MIKV_ERR_SHAPE;
+  if (static_cast<int64_t>(hidden) * d * 2 + 1024 >= (int64_t{1} << 31)) return MIKV_ERR_SHAPE;
   const size_t need = perturbation_ws_bytes(H, T, d, hidden);
   if (!ws || ws_bytes < need) return MIKV_ERR_WORKSPACE;
   return from_hip(launch_perturbation(q, K, V, W_O, keep, n_keep, o_hat, H, T, d, hidden, o, delta, L_head,

@@ -11,14 +11,16 @@
 // cache, e.g. MiKV's mixed-precision decode attention).
 //
 // Kernels (HBM-bound streaming):
-//   pert_mask_kernel   kept-token mask per head from the kept index lists;
-//   pert_attn_kernel   one block per (split, head): streams K and V rows of
-//                      its token range once, keeping two online softmaxes
-//                      (all tokens, kept tokens); writes split partials;
-//   pert_merge_kernel  one block per head: o, o_hat, delta = o - o_hat,
-//                      ||delta||_1;
-//   pert_proj_kernel   one block per (256 output columns, head):
-//                      |delta . W_O,h[:, j]| summed over its columns;
+//   pert_attn_kernel   one block per (split, head): marks its range's kept
+//                      tokens in an LDS bitmap from the head's kept index
+//                      list, then streams K and V rows of the range once,
+//                      keeping two online softmaxes (all tokens, kept
+//                      tokens); writes split partials;
+//   pert_out_kernel    one block per (512 output columns, head): combines
+//                      the head's partials into o, o_hat and delta = o -
+//                      o_hat (column block 0 writes them and ||delta||_1),
+//                      then |delta . W_O,h[:, j]| summed over its columns,
+//                      W_O read in 16-byte rows by 4 row groups;
 //   pert_sum_kernel    the column blocks' sums per head.
 #include <hip/hip_runtime.h>
 
@@ -33,7 +35,8 @@ namespace {
 
 constexpr int kPT = 256;                  // threads per block
 constexpr float kPLog2e = 1.4426950408889634f;
-constexpr int kProjCols = 256;            // output columns per projection block
+constexpr int kProjCols = 512;            // output columns per projection block (64 x 8)
+constexpr int kMaxChunk = 65536;          // tokens per split at most (LDS bitmap of 8 KB)
 
 typedef __amdgpu_buffer_rsrc_t PRsrc;
 __device__ __forceinline__ PRsrc pert_rsrc(const void* base, uint32_t bytes) {
@@ -68,25 +71,12 @@ struct PState {
   }
 };
 
-__global__ __launch_bounds__(kPT) void pert_mask_kernel(const int32_t* __restrict__ keep, int n_keep, int T,
-                                                         uint8_t* __restrict__ mask) {
-  const int h = blockIdx.x;
-  uint8_t* m = mask + static_cast<int64_t>(h) * T;
-  for (int t = threadIdx.x; t < T; t += kPT) m[t] = 0;
-  __syncthreads();
-  const int32_t* kp = keep + static_cast<int64_t>(h) * n_keep;
-  for (int i = threadIdx.x; i < n_keep; i += kPT) {
-    const int t = kp[i];
-    if (t >= 0 && t < T) m[t] = 1;  // indices outside [0, T) are ignored
-  }
-}
-
 // Partials: part_ml [H][S][2] (max, sum) and part_o [H][S][2][D] (o sums),
 // index 0 = all tokens, 1 = kept tokens.
 template <int D>
 __global__ __launch_bounds__(kPT) void pert_attn_kernel(const uint16_t* __restrict__ q, const uint16_t* K,
-                                                         const uint16_t* V, const uint8_t* __restrict__ mask,
-                                                         int T, int chunk, float2* __restrict__ part_ml,
+                                                         const uint16_t* V, const int32_t* __restrict__ keep,
+                                                         int n_keep, int T, int chunk, float2* __restrict__ part_ml,
                                                          float* __restrict__ part_o) {
   constexpr int LPT = D / 8, SLOTS = kPT / LPT;
   const int split = blockIdx.x, h = blockIdx.y, S = gridDim.x;
@@ -97,7 +87,19 @@ __global__ __launch_bounds__(kPT) void pert_attn_kernel(const uint16_t* __restri
   const int64_t rowb = (static_cast<int64_t>(h) * T + t0) * D;
   const PRsrc rk = pert_rsrc(K + rowb, static_cast<uint32_t>(nt) * D * 2);
   const PRsrc rv = pert_rsrc(V + rowb, static_cast<uint32_t>(nt) * D * 2);
-  const uint8_t* mk = mask ? mask + static_cast<int64_t>(h) * T + t0 : nullptr;
+  // kept tokens of the range as a bitmap (indices outside [0, T) ignored)
+  __shared__ uint32_t kept_bits[kMaxChunk / 32];
+  if (keep) {  // uniform
+    const int nw = (nt + 31) / 32;
+    for (int i = tid; i < nw; i += kPT) kept_bits[i] = 0u;
+    __syncthreads();
+    const int32_t* kp = keep + static_cast<int64_t>(h) * n_keep;
+    for (int i = tid; i < n_keep; i += kPT) {
+      const int t = kp[i] - t0;
+      if (t >= 0 && t < nt) atomicOr(&kept_bits[t / 32], 1u << (t % 32));
+    }
+    __syncthreads();
+  }
   float qh[8];
   load8(q + static_cast<int64_t>(h) * D + lane * 8, qh);
   const float qs = kPLog2e / sqrtf(static_cast<float>(D));
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kPT) void pert_attn_kernel(const uint16_t* __restri
     }
     s = group_sum<LPT>(s);
     all.add(s, v);
-    if (mk && mk[t]) kept.add(s, v);
+    if (keep && ((kept_bits[t / 32] >> (t % 32)) & 1u)) kept.add(s, v);
   }
   // combine the slots: per state, max over slots, rescale, sum
   __shared__ float sm[2][SLOTS];
@@ -157,65 +159,136 @@ __global__ __launch_bounds__(kPT) void pert_attn_kernel(const uint16_t* __restri
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(D) void pert_merge_kernel(const float2* __restrict__ part_ml,
+// o, o_hat and delta of head h for its D channels (every block of the head
+// recomputes them from the split partials, which stay in L2), then the
+// projection of delta onto the block's 512 columns of W_O,h: 64 column
+// groups of 8 x 4 row groups of D/4 rows, 16-byte loads (hidden a multiple
+// of 8); the row groups' column sums are added before |.|.
+template <int D, bool VEC>
+__global__ __launch_bounds__(kPT) void pert_out_kernel(const float2* __restrict__ part_ml,
                                                         const float* __restrict__ part_o, int S,
-                                                        const float* __restrict__ o_hat, float* __restrict__ o_out,
-                                                        float* __restrict__ delta, float* __restrict__ L_head) {
-  const int h = blockIdx.x, c = threadIdx.x;
-  float res[2];
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    if (w == 1 && o_hat) {
-      res[1] = o_hat[static_cast<int64_t>(h) * D + c];
-      continue;
-    }
-    float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, part_ml[(static_cast<int64_t>(h) * S + s) * 2 + w].x);
-    float L = 0.0f, o = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float2 ml = part_ml[(static_cast<int64_t>(h) * S + s) * 2 + w];
-      if (ml.x == -INFINITY) continue;
-      const float f = __builtin_amdgcn_exp2f(ml.x - mx);
-      L += f * ml.y;
-      o += f * part_o[((static_cast<int64_t>(h) * S + s) * 2 + w) * D + c];
-    }
-    res[w] = o / L;
-  }
-  const float dl = res[0] - res[1];
-  if (o_out) o_out[static_cast<int64_t>(h) * D + c] = res[0];
-  delta[static_cast<int64_t>(h) * D + c] = dl;
-  __shared__ float red[D];
-  red[c] = fabsf(dl);
-  __syncthreads();
-  for (int k = D / 2; k > 0; k /= 2) {
-    if (c < k) red[c] += red[c + k];
-    __syncthreads();
-  }
-  if (c == 0) L_head[h] = red[0];
-}
-
-__global__ __launch_bounds__(kPT) void pert_proj_kernel(const float* __restrict__ delta,
-                                                         const uint16_t* __restrict__ W, int D, int hidden,
-                                                         float* __restrict__ part) {
+                                                        const float* __restrict__ o_hat, const uint16_t* W,
+                                                        int hidden, float* __restrict__ o_out,
+                                                        float* __restrict__ delta, float* __restrict__ L_head,
+                                                        float* __restrict__ part) {
   const int chunk = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  __shared__ float dl[128];
-  __shared__ float red[kPT];
-  if (tid < D) dl[tid] = delta[static_cast<int64_t>(h) * D + tid];
-  __syncthreads();
-  const int j = chunk * kProjCols + tid;
-  float acc = 0.0f;
-  if (j < hidden) {
-    const uint16_t* w = W + static_cast<int64_t>(h) * D * hidden + j;
-    for (int c = 0; c < D; ++c) acc += dl[c] * h2f(w[static_cast<int64_t>(c) * hidden]);
+  __shared__ float sM[2], sIL[2];
+  __shared__ float dl[D];
+  __shared__ float red[kPT][8];
+  // (1) per state: max and reciprocal sum over the splits, one wave each
+  {
+    const int wave = tid / kWave, ln = tid % kWave;
+    if (wave < 2 && !(wave == 1 && o_hat)) {
+      const float2* ml = part_ml + static_cast<int64_t>(h) * S * 2 + wave;
+      float mx = -INFINITY;
+      for (int s = ln; s < S; s += kWave) mx = fmaxf(mx, ml[2 * s].x);
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
+      float L = 0.0f;
+      for (int s = ln; s < S; s += kWave) {
+        const float2 v = ml[2 * s];
+        if (v.x != -INFINITY) L += __builtin_amdgcn_exp2f(v.x - mx) * v.y;
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) L += shfl_xor_f(L, m);
+      if (ln == 0) {
+        sM[wave] = mx;
+        sIL[wave] = 1.0f / L;
+      }
+    }
   }
-  red[tid] = fabsf(acc);
   __syncthreads();
-  for (int k = kPT / 2; k > 0; k /= 2) {
-    if (tid < k) red[tid] += red[tid + k];
-    __syncthreads();
+  // (2) o and o_hat per channel: thread (w, c) for w = tid / D
+  if (tid < 2 * D) {
+    const int w = tid / D, c = tid % D;
+    float res;
+    if (w == 1 && o_hat) {
+      res = o_hat[static_cast<int64_t>(h) * D + c];
+    } else {
+      const float mx = sM[w];
+      const float2* ml = part_ml + static_cast<int64_t>(h) * S * 2 + w;
+      const float* po = part_o + (static_cast<int64_t>(h) * S * 2 + w) * D + c;
+      float o = 0.0f;
+#pragma unroll 8
+      for (int s = 0; s < S; ++s) {
+        const float2 v = ml[2 * s];
+        const float x = po[static_cast<int64_t>(s) * 2 * D];
+        if (v.x != -INFINITY) o += __builtin_amdgcn_exp2f(v.x - mx) * x;
+      }
+      res = o * sIL[w];
+    }
+    red[tid][0] = res;
   }
-  if (tid == 0) part[static_cast<int64_t>(h) * gridDim.x + chunk] = red[0];
+  __syncthreads();
+  if (tid < D) {
+    const float o = red[tid][0], oh = red[D + tid][0];
+    const float d = o - oh;
+    dl[tid] = d;
+    if (chunk == 0) {
+      if (o_out) o_out[static_cast<int64_t>(h) * D + tid] = o;
+      delta[static_cast<int64_t>(h) * D + tid] = d;
+    }
+  }
+  __syncthreads();
+  if (chunk == 0 && tid < kWave) {
+    float a = 0.0f;
+    for (int c = tid; c < D; c += kWave) a += fabsf(dl[c]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) a += shfl_xor_f(a, m);
+    if (tid == 0) L_head[h] = a;
+  }
+  // (3) projection: column group cg (8 columns), row group rg (D/4 rows)
+  constexpr int RPG = D / 4;
+  const int cg = tid % 64, rg = tid / 64;
+  const int j0 = chunk * kProjCols + cg * 8;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  const uint16_t* wh = W + static_cast<int64_t>(h) * D * hidden;
+  if constexpr (VEC) {
+    // a column group lies wholly inside or outside [0, hidden) (hidden is a
+    // multiple of 8); groups outside add nothing (their addresses would be
+    // the next row's columns)
+    if (j0 < hidden) {
+    const PRsrc rw = pert_rsrc(wh, static_cast<uint32_t>(D) * hidden * 2);
+    uint4 wv[RPG];
+#pragma unroll
+    for (int r = 0; r < RPG; ++r)
+      wv[r] = pert_load16(rw, static_cast<uint32_t>((rg * RPG + r) * hidden + j0) * 2);
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+      const float dv = dl[rg * RPG + r];
+      const uint32_t ww[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += dv * lo_h(ww[i]);
+        acc[2 * i + 1] += dv * hi_h(ww[i]);
+      }
+    }
+    }
+  } else {
+    for (int r = 0; r < RPG; ++r) {
+      const float dv = dl[rg * RPG + r];
+      const uint16_t* wr = wh + static_cast<int64_t>(rg * RPG + r) * hidden;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (j0 + e < hidden) acc[e] += dv * h2f(wr[j0 + e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[tid][e] = acc[e];
+  __syncthreads();
+  float colabs = 0.0f;
+  if (tid < 64) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      colabs += fabsf(red[tid][e] + red[64 + tid][e] + red[128 + tid][e] + red[192 + tid][e]);
+  }
+  if (tid < kWave) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) colabs += shfl_xor_f(colabs, m);
+    if (tid == 0) part[static_cast<int64_t>(h) * gridDim.x + chunk] = colabs;
+  }
 }
 
 __global__ __launch_bounds__(kWave) void pert_sum_kernel(const float* __restrict__ part, int nchunk,
@@ -236,15 +309,16 @@ int perturbation_splits(int H, int T) {
   int s = (1024 + H - 1) / H;   // about 1024 blocks in all
   const int per = (T + 255) / 256;  // at least 256 tokens per split
   if (s > per) s = per;
+  const int fit = (T + kMaxChunk - 1) / kMaxChunk;  // the kept bitmap of a split fits LDS
+  if (s < fit) s = fit;
   return s < 1 ? 1 : s;
 }
 
 size_t perturbation_ws_bytes(int H, int T, int d, int hidden) {
   const size_t S = perturbation_splits(H, T);
   const size_t nchunk = (hidden + kProjCols - 1) / kProjCols;
-  return al256(static_cast<size_t>(H) * T) + al256(H * S * 2 * sizeof(float2)) +
-         al256(H * S * 2 * d * sizeof(float)) + al256(static_cast<size_t>(H) * d * sizeof(float)) +
-         al256(H * nchunk * sizeof(float));
+  return al256(H * S * 2 * sizeof(float2)) + al256(H * S * 2 * d * sizeof(float)) +
+         al256(static_cast<size_t>(H) * d * sizeof(float)) + al256(H * nchunk * sizeof(float));
 }
 
 hipError_t launch_perturbation(const uint16_t* q, const uint16_t* K, const uint16_t* V, const uint16_t* W,
@@ -255,8 +329,6 @@ hipError_t launch_perturbation(const uint16_t* q, const uint16_t* K, const uint1
   const int chunk = (T + S - 1) / S;
   const int nchunk = (hidden + kProjCols - 1) / kProjCols;
   char* w = static_cast<char*>(ws);
-  uint8_t* mask = reinterpret_cast<uint8_t*>(w);
-  w += al256(static_cast<size_t>(H) * T);
   float2* part_ml = reinterpret_cast<float2*>(w);
   w += al256(static_cast<size_t>(H) * S * 2 * sizeof(float2));
   float* part_o = reinterpret_cast<float*>(w);
@@ -264,24 +336,21 @@ hipError_t launch_perturbation(const uint16_t* q, const uint16_t* K, const uint1
   float* delta = delta_out ? delta_out : reinterpret_cast<float*>(w);
   w += al256(static_cast<size_t>(H) * d * sizeof(float));
   float* part = reinterpret_cast<float*>(w);
-  if (keep) {
-    pert_mask_kernel<<<H, kPT, 0, stream>>>(keep, n_keep, T, mask);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const dim3 grid(static_cast<unsigned>(S), static_cast<unsigned>(H));
+  const dim3 ogrid(static_cast<unsigned>(nchunk), static_cast<unsigned>(H));
+  const float* oh = keep ? nullptr : o_hat;
+  // 16-byte rows of W_O: hidden a multiple of 8 and W_O 16-byte aligned
+  const bool vec = hidden % 8 == 0 && (reinterpret_cast<uintptr_t>(W) & 15u) == 0;
   if (d == 128) {
-    pert_attn_kernel<128><<<grid, kPT, 0, stream>>>(q, K, V, keep ? mask : nullptr, T, chunk, part_ml, part_o);
-    pert_merge_kernel<128><<<H, 128, 0, stream>>>(part_ml, part_o, S, keep ? nullptr : o_hat, o, delta, L_head);
+    pert_attn_kernel<128><<<grid, kPT, 0, stream>>>(q, K, V, keep, n_keep, T, chunk, part_ml, part_o);
+    if (vec) pert_out_kernel<128, true><<<ogrid, kPT, 0, stream>>>(part_ml, part_o, S, oh, W, hidden, o, delta, L_head, part);
+    else pert_out_kernel<128, false><<<ogrid, kPT, 0, stream>>>(part_ml, part_o, S, oh, W, hidden, o, delta, L_head, part);
   } else {
-    pert_attn_kernel<64><<<grid, kPT, 0, stream>>>(q, K, V, keep ? mask : nullptr, T, chunk, part_ml, part_o);
-    pert_merge_kernel<64><<<H, 64, 0, stream>>>(part_ml, part_o, S, keep ? nullptr : o_hat, o, delta, L_head);
+    pert_attn_kernel<64><<<grid, kPT, 0, stream>>>(q, K, V, keep, n_keep, T, chunk, part_ml, part_o);
+    if (vec) pert_out_kernel<64, true><<<ogrid, kPT, 0, stream>>>(part_ml, part_o, S, oh, W, hidden, o, delta, L_head, part);
+    else pert_out_kernel<64, false><<<ogrid, kPT, 0, stream>>>(part_ml, part_o, S, oh, W, hidden, o, delta, L_head, part);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  pert_proj_kernel<<<dim3(static_cast<unsigned>(nchunk), static_cast<unsigned>(H)), kPT, 0, stream>>>(
-      delta, W, d, hidden, part);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   pert_sum_kernel<<<H, kWave, 0, stream>>>(part, nchunk, L_proj);
   return hipGetLastError();

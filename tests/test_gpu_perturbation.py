@@ -67,6 +67,33 @@ def test_perturbation_random_subsets(H, T, d, hidden):
     _check(q, K, V, W, o_hat=ro + rng.standard_normal(ro.shape) * 0.01, what="o_hat")
 
 
+def test_perturbation_unaligned_w_and_unsorted_keep():
+    """W_O at a 2-byte offset (the row-by-row projection path) against the
+    16-byte-row path on the same values, and kept indices in any order with
+    out-of-range entries (which are ignored) against the sorted set."""
+    rng = np.random.default_rng(77)
+    H, T, d, hidden = 4, 700, 128, 520
+    q = (rng.standard_normal((H, d)) * 1.5).astype(F16)
+    K = rng.standard_normal((H, T, d)).astype(F16)
+    V = rng.standard_normal((H, T, d)).astype(F16)
+    W = (rng.standard_normal((H * d, hidden)) / np.sqrt(hidden)).astype(F16)
+    keep = np.stack([np.sort(rng.choice(T, 150, replace=False)) for _ in range(H)])
+    Lh, Lp, _, _ = _check(q, K, V, W, keep=keep, what="aligned W")
+    # the same W_O one element into a larger buffer: 2-byte aligned
+    buf = torch.zeros(H * d * hidden + 1, dtype=torch.float16, device="cuda")
+    buf[1:] = torch.from_numpy(W.reshape(-1)).cuda()
+    Wu = buf[1:].view(H * d, hidden)
+    assert Wu.data_ptr() % 16 != 0
+    Lh2 = torch.empty(H, dtype=torch.float32, device="cuda")
+    Lp2 = torch.empty(H, dtype=torch.float32, device="cuda")
+    ws = torch.empty(L.mikv_perturbation_workspace(H, T, d, hidden), dtype=torch.uint8, device="cuda")
+    shuffled = np.stack([np.concatenate([rng.permutation(k), [-3, T, T + 7]]) for k in keep]).astype(np.int32)
+    L.mikv_output_perturbation(dev(q), dev(K), dev(V), Wu, Lh2, Lp2, ws, keep=dev(shuffled))
+    torch.cuda.synchronize()
+    assert np.allclose(Lh2.cpu().numpy(), Lh, rtol=1e-5)
+    assert np.allclose(Lp2.cpu().numpy(), Lp, rtol=1e-4)
+
+
 def test_perturbation_of_selections_h2o_criticalkv_mikv():
     """One Llama-2-shaped layer (8 heads of 128, 2048 prompt tokens, one new
     token, 20% budget): the kept sets of H2O (recent window + heavy hitters
