@@ -95,7 +95,7 @@ __device__ __forceinline__ float sum_over_stride(float v) {
 // and writes (scale | zero << 16) to *sz_word.
 // ---------------------------------------------------------------------------
 template <int BITS, int NL>
-__device__ __forceinline__ void quantize8_codes(const float (&x)[8], uint32_t* sz_word, uint32_t (&code)[8]) {
+__device__ __forceinline__ void quantize8_values(const float (&x)[8], uint32_t* sz_word, float (&t)[8]) {
   constexpr float qmax = static_cast<float>((1 << BITS) - 1);
   float mn = x[0], mx = x[0];
 #pragma unroll
@@ -112,7 +112,7 @@ __device__ __forceinline__ void quantize8_codes(const float (&x)[8], uint32_t* s
   if ((z16 & 0x7FFFu) == 0) z16 = 0;
   *sz_word = static_cast<uint32_t>(s16) | (static_cast<uint32_t>(z16) << 16);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) code[i] = 0;
+  for (int i = 0; i < 8; ++i) t[i] = 0.0f;
   if (s16 != 0) {
     const float s = h2f(s16);
     const float z = h2f(z16);
@@ -122,36 +122,65 @@ __device__ __forceinline__ void quantize8_codes(const float (&x)[8], uint32_t* s
     // 2^-24 |Q|, so |y - fl(Q)| <= 2^-22 |Q|: 2^-18 for the 2- and 4-bit
     // codes' range |Q| <= 16, 2^-14 for 8-bit codes (|Q| <= 256).
     // When y is farther than the margin (2^-16, or 2^-13 at 8 bits) from its
-    // nearest half-integer, y and fl(Q) lie in the same rounding interval and
-    // rint(y) = rint(fl(Q)); a lane with any value closer than that (about
-    // 1e-5 of values, 1e-4 at 8 bits) takes the IEEE divide for all of them.
+    // nearest half-integer, y and fl(Q) lie in the same rounding interval
+    // and rint(y) = rint(fl(Q)). The distance is taken as |fma(x - z, r,
+    // -rint(y))|, the exact product's distance from rint(y) rounded once: it
+    // differs from |y - rint(y)| by at most half an ulp of y (2^-20 at
+    // |y| <= 16, 2^-16 at |y| <= 256), which the margins leave room for. A
+    // lane whose largest distance reaches 1/2 - margin (about 1e-5 of
+    // values, 1e-4 at 8 bits) takes the IEEE divide for all its values.
+    constexpr float kFar = 0.5f - (BITS == 8 ? 0x1p-13f : 0x1p-16f);
     const float r = __builtin_amdgcn_rcpf(s);
-    float t[8];
-    bool near_half = false;
+    float dist = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float y = (x[i] - z) * r;
-      near_half |= fabsf((y - floorf(y)) - 0.5f) <= (BITS == 8 ? 0x1p-13f : 0x1p-16f);
-      t[i] = rintf(y);
+      const float a = x[i] - z;  // exact: fp16 values
+      t[i] = rintf(a * r);
+      dist = fmaxf(dist, fabsf(fmaf(a, r, -t[i])));
     }
-    if (near_half) {
+    if (dist >= kFar) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) t[i] = rintf((x[i] - z) / s);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = static_cast<uint32_t>(fminf(fmaxf(t[i], 0.0f), qmax));
+    for (int i = 0; i < 8; ++i) t[i] = __builtin_amdgcn_fmed3f(t[i], 0.0f, qmax);
   }
 }
 
+template <int BITS, int NL>
+__device__ __forceinline__ void quantize8_codes(const float (&x)[8], uint32_t* sz_word, uint32_t (&code)[8]) {
+  float t[8];
+  quantize8_values<BITS, NL>(x, sz_word, t);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) code[i] = static_cast<uint32_t>(t[i]);
+}
+
 // Packed codes of the lane's 8 channels (BITS <= 4: the low 8*BITS bits).
+// Each code goes into a byte with one v_cvt_pk_u8_f32; the bytes are then
+// merged: INT4 even channels' bytes | odd channels' bytes << 4; INT2 four
+// words of two bytes (channels m and 4 + m) shifted by 2m.
 template <int BITS, int NL>
 __device__ __forceinline__ uint32_t quantize8(const float (&x)[8], uint32_t* sz_word) {
-  uint32_t code[8];
-  quantize8_codes<BITS, NL>(x, sz_word, code);
-  uint32_t packed = 0;
+  static_assert(BITS == 4 || BITS == 2, "4- or 2-bit codes");
+  float t[8];
+  quantize8_values<BITS, NL>(x, sz_word, t);
+  if constexpr (BITS == 4) {
+    uint32_t a = 0u, b = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) packed |= code[i] << (BITS * i);
-  return packed;
+    for (int k = 0; k < 4; ++k) {
+      a = __builtin_amdgcn_cvt_pk_u8_f32(t[2 * k], k, a);
+      b = __builtin_amdgcn_cvt_pk_u8_f32(t[2 * k + 1], k, b);
+    }
+    return a | (b << 4);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      w[m] = __builtin_amdgcn_cvt_pk_u8_f32(t[m], 0, 0u);
+      w[m] = __builtin_amdgcn_cvt_pk_u8_f32(t[4 + m], 1, w[m]);
+    }
+    return w[0] | (w[1] << 2) | (w[2] << 4) | (w[3] << 6);
+  }
 }
 
 // The 8 codes packed at QB bits (8, 4 or 2) into w[0..1]: byte j of the

@@ -8,8 +8,10 @@ import numpy as np
 def test_divide_free_code_rule_matches_ieee_division():
     """The HIP quantizer finds rint(fl((x - z) / s)) as rint((x - z) * r) with
     r a reciprocal of s within 1 ulp, and falls back to the IEEE divide when
-    the product is within 2^-16 (2^-13 for 8-bit codes) of a half-integer.
-    Check that rule in float32
+    the product is within 2^-16 (2^-13 for 8-bit codes) of a half-integer,
+    tested as |fma(x - z, r, -rint(y))| >= 1/2 - margin (the exact product's
+    distance from the code, rounded once to float32). Check that rule in
+    float32
     over random fp16 groups (the oracle's step-3 setting, scale from the
     group's range) with r = the rounded reciprocal and its neighbours one ulp
     away: wherever the margin test passes, the code equals the divide's."""
@@ -29,7 +31,10 @@ def test_divide_free_code_rule_matches_ieee_division():
             r0 = (np.float32(1.0) / s).astype(np.float32)
             for r in (r0, np.nextafter(r0, np.float32(np.inf)), np.nextafter(r0, np.float32(0))):
                 y = (a * r).astype(np.float32)
-                far = np.abs((y - np.floor(y)) - np.float32(0.5)) > margin
-                assert np.array_equal(np.rint(y)[far], ref[far])
+                t = np.rint(y)
+                # fma: the float64 product of two float32 values is exact
+                d = (a.astype(np.float64) * r.astype(np.float64) - t).astype(np.float32)
+                far = np.abs(d) < np.float32(0.5) - margin
+                assert np.array_equal(t[far], ref[far])
                 checked += int(far.sum())
     assert checked > 1_000_000
