@@ -54,6 +54,26 @@ __device__ __forceinline__ constexpr int tile_chan(int c, int r, int e) {
   return (c / CPG) * G + 8 * CPG * r + (c % CPG) * 8 + pe;
 }
 
+// Sum over the wave's four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48),
+// every lane ending with its column's total: two cross-row swaps on the vector
+// ALU (v_permlane32_swap, v_permlane16_swap) instead of LDS-routed shuffles.
+__device__ __forceinline__ float row_sum4(float v) {
+  int x = __builtin_bit_cast(int, v);
+  const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);  // rows (0,1,0,1) | (2,3,2,3)
+  v = __builtin_bit_cast(float, static_cast<int>(a[0])) + __builtin_bit_cast(float, static_cast<int>(a[1]));
+  x = __builtin_bit_cast(int, v);
+  const auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);  // rows (0,0,2,2) | (1,1,3,3)
+  return __builtin_bit_cast(float, static_cast<int>(b[0])) + __builtin_bit_cast(float, static_cast<int>(b[1]));
+}
+
+// Sum over the lanes of the wave that share lane % S (S in {8, 16}).
+template <int S>
+__device__ __forceinline__ float slot_sum(float v) {
+  static_assert(S == 8 || S == 16, "value slices of 8 channels: 8 or 16 lanes per row");
+  if constexpr (S == 8) v += dpp<0x128>(v);  // row_ror:8 -> lane ^ 8 within the row
+  return row_sum4(v);
+}
+
 template <int NB>
 struct TileBytes { uint32_t w[(NB + 3) / 4]; };
 
@@ -187,6 +207,20 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
       tile_load<R_t::VB>(rv, tv * ROWB + vj * R_t::VB, R.v[k]);
     }
   };
+  // ---- q and b first, every lane unconditionally (lanes of rows >= RT read
+  // the last live row and zero it below): their wait then covers neither the
+  // first groups' loads issued after them nor a branch per chunk
+  const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+  const int hrow = g * p.rep + tile * RT + min(ai, RT - 1);  // query head of this lane's row
+  float qv[NCH][8], bv[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int base = tile_chan<D, 16>(c, ar, 0);  // first channel of the run
+    load8(p.q + (static_cast<int64_t>(n) * p.hq + hrow) * D + base, qv[c]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bv[c][e] = bvec[base + e];
+  }
+
   // register sets in a ring: NS - 1 groups' loads in flight while one group
   // is computed (two sets; three or four on the low-bit tier measured no
   // faster: the loop is bound by VALU issue, not by loads in flight)
@@ -196,24 +230,16 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
   for (int i = 0; i < NS - 1; ++i) load(wave + 4 * i, R[i]);
 
   // ---- q-hat as MFMA A operands (hi and lo halves), per-group sums of q-hat
-  const float qscale = kLog2e / sqrtf(static_cast<float>(D));
-  const int hrow = g * p.rep + tile * RT + ai;  // query head of this lane's row (ai < RT)
   tile_h8 qa_hi[NCH], qa_lo[NCH];
   float qs_part[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    const int base = tile_chan<D, 16>(c, ar, 0);  // first channel of the run
-    float qv[8];
-    if (ai < RT) {
-      load8(p.q + (static_cast<int64_t>(n) * p.hq + hrow) * D + base, qv);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[e] = 0.0f;
-    }
+    const int base = tile_chan<D, 16>(c, ar, 0);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int ch = tile_chan<D, QB>(c, ar, e);
-      const float q = qv[ch - base] * __builtin_amdgcn_rcpf(bvec[ch]) * qscale;
+      const float qe = qv[c][ch - base] * __builtin_amdgcn_rcpf(bv[c][ch - base]) * qscale;
+      const float q = ai < RT ? qe : 0.0f;
       const _Float16 hi = static_cast<_Float16>(q);
       qa_hi[c][e] = hi;
       qa_lo[c][e] = static_cast<_Float16>(q - static_cast<float>(hi));
@@ -224,9 +250,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
   float qs[RT][2];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
-    float t = qs_part[gi];
-    t += shfl_xor_f(t, 16);
-    t += shfl_xor_f(t, 32);
+    const float t = row_sum4(qs_part[gi]);
 #pragma unroll
     for (int h = 0; h < RT; ++h)
       qs[h][gi] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), h));
@@ -256,11 +280,17 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
         const int c0 = 8 * lane;
         const int64_t nb = static_cast<int64_t>(unit) * D + c0;
         const int64_t fs = rb16 + p.free16[unit];
-        float kx[8], vx[8];
+        // every input of the seed in flight at once
+        float kx[8], vx[8], b8[8], qn[RT][8];
         load8(p.k_new + nb, kx);
         load8(p.v_new + nb, vx);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kx[e] = h2f(f2h(mul_rn(kx[e], bvec[c0 + e])));  // fp16(k * b)
+        for (int e = 0; e < 8; ++e) b8[e] = bvec[c0 + e];
+#pragma unroll
+        for (int h = 0; h < RT; ++h)
+          load8(p.q + (static_cast<int64_t>(n) * p.hq + g * p.rep + tile * RT + h) * D + c0, qn[h]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kx[e] = h2f(f2h(mul_rn(kx[e], b8[e])));  // fp16(k * b)
         if constexpr (F16T) {
           if (tile == 0) {
             uint32_t kw[4];
@@ -295,11 +325,9 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
         if (tile == 0 && lane == 0) p.pos16[fs] = p.len - 1;
 #pragma unroll
         for (int h = 0; h < RT; ++h) {
-          float qv[8];
-          load8(p.q + (static_cast<int64_t>(n) * p.hq + g * p.rep + tile * RT + h) * D + c0, qv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            x[h] += qv[e] * __builtin_amdgcn_rcpf(bvec[c0 + e]) * qscale * kx[e];
+            x[h] += qn[h][e] * __builtin_amdgcn_rcpf(b8[e]) * qscale * kx[e];
             a[h][e] = vx[e];
           }
         }
@@ -363,7 +391,9 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
       for (int h = 0; h < RT; ++h) {
-        const float mn = fmaxf(M[h], wave_max(x[h]));
+        // scores live on lanes 0..15 (-inf elsewhere): a row maximum, made uniform
+        const float rm = group_max<16>(x[h]);
+        const float mn = fmaxf(M[h], __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rm), 0)));
         if (mn > M[h]) {
           const float f = fast_exp2(M[h] - mn);  // 0 when M was -inf
           l[h] *= f;
@@ -467,14 +497,15 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     }
   }
 
-  // ---- wave partials: sums over the score lanes, value slices over slots
+  // ---- wave partials: l and the zero-point sums over the 16 score lanes (zero
+  // on the others; lanes 0..15 end with the totals), value slices over slots
 #pragma unroll
   for (int h = 0; h < RT; ++h) {
-    l[h] = wave_sum(l[h]);
-    zz[h][0] = wave_sum(zz[h][0]);
-    zz[h][1] = wave_sum(zz[h][1]);
+    l[h] = group_sum<16>(l[h]);
+    zz[h][0] = group_sum<16>(zz[h][0]);
+    zz[h][1] = group_sum<16>(zz[h][1]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a[h][e] = sum_over_stride<LPTV>(a[h][e]);
+    for (int e = 0; e < 8; ++e) a[h][e] = slot_sum<LPTV>(a[h][e]);
   }
   if (lane < LPTV) {
 #pragma unroll
