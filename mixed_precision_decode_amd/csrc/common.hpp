@@ -69,21 +69,40 @@ __device__ __forceinline__ float group_min(float v) {
   return v;
 }
 
-__device__ __forceinline__ float shfl_xor_f(float v, int m) {
-  return __builtin_bit_cast(float, __shfl_xor(__builtin_bit_cast(int, v), m));
+// Cross-row steps of a wave reduction on gfx950 (v_permlane32_swap,
+// v_permlane16_swap: vector ALU, no LDS). The pair holds, in some order, the
+// values of lanes l and l ^ 32 (l ^ 16), so a commutative combine of its two
+// halves needs no per-row select and every lane ends with the same result.
+struct LanePair { uint32_t a, b; };
+__device__ __forceinline__ LanePair pair_xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return {static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1])};
+}
+__device__ __forceinline__ LanePair pair_xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return {static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1])};
+}
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Sum / max over the wave's four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float rows_sum(float v) {
+  LanePair x = pair_xor32(f2u(v));
+  v = u2f(x.a) + u2f(x.b);
+  x = pair_xor16(f2u(v));
+  return u2f(x.a) + u2f(x.b);
+}
+__device__ __forceinline__ float rows_max(float v) {
+  LanePair x = pair_xor32(f2u(v));
+  v = fmaxf(u2f(x.a), u2f(x.b));
+  x = pair_xor16(f2u(v));
+  return fmaxf(u2f(x.a), u2f(x.b));
 }
 
-// Sum over lanes that share (lane % S) within the wave, S a power of two <= 16.
-template <int S>
-__device__ __forceinline__ float sum_over_stride(float v) {
-  if constexpr (S <= 1) v += shfl_xor_f(v, 1);
-  if constexpr (S <= 2) v += shfl_xor_f(v, 2);
-  if constexpr (S <= 4) v += shfl_xor_f(v, 4);
-  if constexpr (S <= 8) v += shfl_xor_f(v, 8);
-  if constexpr (S <= 16) v += shfl_xor_f(v, 16);
-  v += shfl_xor_f(v, 32);
-  return v;
-}
+// Sum / max over the whole wave (all 64 lanes active); every lane ends with
+// the result.
+__device__ __forceinline__ float wave_sum(float v) { return rows_sum(group_sum<16>(v)); }
+__device__ __forceinline__ float wave_max(float v) { return rows_max(group_max<16>(v)); }
 
 // ---------------------------------------------------------------------------
 // Per-token asymmetric quantization of one group held by NL lanes, 8

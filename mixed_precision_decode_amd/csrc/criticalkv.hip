@@ -268,11 +268,9 @@ __global__ __launch_bounds__(256) void ckv_project_kernel(const float* __restric
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float v = rsum[mi][r];
-      v += shfl_xor_f(v, 1);
-      v += shfl_xor_f(v, 2);
-      v += shfl_xor_f(v, 4);
-      v += shfl_xor_f(v, 8);
-      v += shfl_xor_f(v, 16);
+      v = group_sum<16>(v);  // DPP within the row
+      const LanePair x = pair_xor16(f2u(v));  // rows 0+1 and 2+3
+      v = u2f(x.a) + u2f(x.b);
       rsum[mi][r] = v;
     }
   if (lane % 32 == 0) {

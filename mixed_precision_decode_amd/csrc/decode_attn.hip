@@ -150,21 +150,7 @@ __device__ __forceinline__ float fold_slots(float v) {
   if constexpr (LPT <= 2) v += dpp<0x122>(v);
   if constexpr (LPT <= 4) v += dpp<0x124>(v);
   if constexpr (LPT <= 8) v += dpp<0x128>(v);
-  v += shfl_xor_f(v, 16);
-  v += shfl_xor_f(v, 32);
-  return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
-  return v;
+  return rows_sum(v);
 }
 
 // Online-softmax state of one thread for RT heads and CPL channels.

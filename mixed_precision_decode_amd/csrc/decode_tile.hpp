@@ -54,24 +54,12 @@ __device__ __forceinline__ constexpr int tile_chan(int c, int r, int e) {
   return (c / CPG) * G + 8 * CPG * r + (c % CPG) * 8 + pe;
 }
 
-// Sum over the wave's four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48),
-// every lane ending with its column's total: two cross-row swaps on the vector
-// ALU (v_permlane32_swap, v_permlane16_swap) instead of LDS-routed shuffles.
-__device__ __forceinline__ float row_sum4(float v) {
-  int x = __builtin_bit_cast(int, v);
-  const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);  // rows (0,1,0,1) | (2,3,2,3)
-  v = __builtin_bit_cast(float, static_cast<int>(a[0])) + __builtin_bit_cast(float, static_cast<int>(a[1]));
-  x = __builtin_bit_cast(int, v);
-  const auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);  // rows (0,0,2,2) | (1,1,3,3)
-  return __builtin_bit_cast(float, static_cast<int>(b[0])) + __builtin_bit_cast(float, static_cast<int>(b[1]));
-}
-
 // Sum over the lanes of the wave that share lane % S (S in {8, 16}).
 template <int S>
 __device__ __forceinline__ float slot_sum(float v) {
   static_assert(S == 8 || S == 16, "value slices of 8 channels: 8 or 16 lanes per row");
   if constexpr (S == 8) v += dpp<0x128>(v);  // row_ror:8 -> lane ^ 8 within the row
-  return row_sum4(v);
+  return rows_sum(v);
 }
 
 template <int NB>
@@ -250,7 +238,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
   float qs[RT][2];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
-    const float t = row_sum4(qs_part[gi]);
+    const float t = rows_sum(qs_part[gi]);
 #pragma unroll
     for (int h = 0; h < RT; ++h)
       qs[h][gi] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), h));

@@ -171,12 +171,28 @@ __device__ void h2o_select_demote(Worst w, const H2OView& v, int unit, int fr) {
   __shared__ int s_slot[4];
   __shared__ int s_drop;
   const int tid = threadIdx.x;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float oa = shfl_xor_f(w.a, m);
-    const int op = __shfl_xor(w.pos, m);
-    const int os = __shfl_xor(w.slot, m);
-    w.merge(oa, op, os);
+  // wave argmin: within each row by DPP (quad swaps, then the half-row and
+  // row mirrors), across rows by the permlane swaps; merge keeps the minimum
+  // of a total order, so each pair combines in either order
+  w.merge(dpp<0xB1>(w.a), dppi<0xB1>(w.pos), dppi<0xB1>(w.slot));
+  w.merge(dpp<0x4E>(w.a), dppi<0x4E>(w.pos), dppi<0x4E>(w.slot));
+  w.merge(dpp<0x141>(w.a), dppi<0x141>(w.pos), dppi<0x141>(w.slot));
+  w.merge(dpp<0x140>(w.a), dppi<0x140>(w.pos), dppi<0x140>(w.slot));
+  {
+    const LanePair a = pair_xor32(f2u(w.a)), p = pair_xor32(static_cast<uint32_t>(w.pos)),
+                   s = pair_xor32(static_cast<uint32_t>(w.slot));
+    Worst x;
+    x.merge(u2f(a.a), static_cast<int>(p.a), static_cast<int>(s.a));
+    x.merge(u2f(a.b), static_cast<int>(p.b), static_cast<int>(s.b));
+    w = x;
+  }
+  {
+    const LanePair a = pair_xor16(f2u(w.a)), p = pair_xor16(static_cast<uint32_t>(w.pos)),
+                   s = pair_xor16(static_cast<uint32_t>(w.slot));
+    Worst x;
+    x.merge(u2f(a.a), static_cast<int>(p.a), static_cast<int>(s.a));
+    x.merge(u2f(a.b), static_cast<int>(p.b), static_cast<int>(s.b));
+    w = x;
   }
   if (tid % kWave == 0) { s_acc[tid / kWave] = w.a; s_pos[tid / kWave] = w.pos; s_slot[tid / kWave] = w.slot; }
   __syncthreads();

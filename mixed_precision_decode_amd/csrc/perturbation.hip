@@ -182,15 +182,13 @@ __global__ __launch_bounds__(kPT) void pert_out_kernel(const float2* __restrict_
       const float2* ml = part_ml + static_cast<int64_t>(h) * S * 2 + wave;
       float mx = -INFINITY;
       for (int s = ln; s < S; s += kWave) mx = fmaxf(mx, ml[2 * s].x);
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
+      mx = wave_max(mx);
       float L = 0.0f;
       for (int s = ln; s < S; s += kWave) {
         const float2 v = ml[2 * s];
         if (v.x != -INFINITY) L += __builtin_amdgcn_exp2f(v.x - mx) * v.y;
       }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) L += shfl_xor_f(L, m);
+      L = wave_sum(L);
       if (ln == 0) {
         sM[wave] = mx;
         sIL[wave] = 1.0f / L;
@@ -233,8 +231,7 @@ __global__ __launch_bounds__(kPT) void pert_out_kernel(const float2* __restrict_
   if (chunk == 0 && tid < kWave) {
     float a = 0.0f;
     for (int c = tid; c < D; c += kWave) a += fabsf(dl[c]);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) a += shfl_xor_f(a, m);
+    a = wave_sum(a);
     if (tid == 0) L_head[h] = a;
   }
   // (3) projection: column group cg (8 columns), row group rg (D/4 rows)
@@ -285,8 +282,7 @@ __global__ __launch_bounds__(kPT) void pert_out_kernel(const float2* __restrict_
       colabs += fabsf(red[tid][e] + red[64 + tid][e] + red[128 + tid][e] + red[192 + tid][e]);
   }
   if (tid < kWave) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) colabs += shfl_xor_f(colabs, m);
+    colabs = wave_sum(colabs);
     if (tid == 0) part[static_cast<int64_t>(h) * gridDim.x + chunk] = colabs;
   }
 }
@@ -296,8 +292,7 @@ __global__ __launch_bounds__(kWave) void pert_sum_kernel(const float* __restrict
   const int h = blockIdx.x;
   float s = 0.0f;
   for (int i = threadIdx.x; i < nchunk; i += kWave) s += part[static_cast<int64_t>(h) * nchunk + i];
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  s = wave_sum(s);
   if (threadIdx.x == 0) L_proj[h] = s;
 }
 

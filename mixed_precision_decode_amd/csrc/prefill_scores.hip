@@ -193,9 +193,12 @@ __global__ __launch_bounds__(kPsThreads, kPsMinWaves) void ps_rowstat_kernel(con
 #pragma unroll
   for (int u = 0; u < kPsTilesPerWave; ++u) {
     // lanes l and l + 32 hold the two halves of column i's key rows
-    const float mo = shfl_xor_f(m[u], 32), lo = shfl_xor_f(l[u], 32);
-    const float M = fmaxf(m[u], mo);  // finite: key t = i is in lane l or l + 32
-    const float L = l[u] * ps_exp2(m[u] - M) + lo * ps_exp2(mo - M);  // >= 1
+    // (the pairs hold lanes l and l ^ 32 in the same order for m and l; the
+    // combine is symmetric in the two)
+    const LanePair pm = pair_xor32(f2u(m[u])), pl = pair_xor32(f2u(l[u]));
+    const float ma = u2f(pm.a), mb = u2f(pm.b);
+    const float M = fmaxf(ma, mb);  // finite: key t = i is in lane l or l + 32
+    const float L = u2f(pl.a) * ps_exp2(ma - M) + u2f(pl.b) * ps_exp2(mb - M);  // >= 1
     // log2-sum-exp of the row: p[i][t] = exp2(s[i][t] * c - lse[i])
     if (lane < 32 && iq[u] < T) lse[static_cast<int64_t>(nhi) * T + iq[u]] = M + __builtin_amdgcn_logf(L);
   }
@@ -292,11 +295,9 @@ __global__ __launch_bounds__(kPsThreads, kPsMinWaves) void ps_colsum_kernel(cons
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float v = col[u][r];
-      v += shfl_xor_f(v, 1);
-      v += shfl_xor_f(v, 2);
-      v += shfl_xor_f(v, 4);
-      v += shfl_xor_f(v, 8);
-      v += shfl_xor_f(v, 16);
+      v = group_sum<16>(v);  // DPP within the row
+      const LanePair x = pair_xor16(f2u(v));  // rows 0+1 and 2+3
+      v = u2f(x.a) + u2f(x.b);
       col[u][r] = v;
     }
   if (lane % 32 == 0) {
