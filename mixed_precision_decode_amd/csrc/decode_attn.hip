@@ -281,7 +281,8 @@ __device__ __forceinline__ uint32_t bload1(Rsrc r, uint32_t off) {
 
 // fp16 pairs (1024 + code_a, 1024 + code_b) from one word of packed codes:
 // each code is isolated in a byte, and v_perm puts it under a 0x64 byte, the
-// fp16 1024 + code exactly. Pair k of the word's CPW channels covers:
+// fp16 1024 + code exactly (with magic = 0 under a zero byte instead: the
+// fp16 subnormal code * 2^-24, also exact). Pair k of the word's CPW channels covers:
 //   INT4 (channels at bits 4c): k = 0,1 even channels (4k, 4k+2), k = 2,3 odd
 //        channels (4(k-2)+1, 4(k-2)+3);
 //   INT2 (channels at bits 2c): pair 2m+q holds (8q+m, 8q+4+m).

@@ -11,9 +11,10 @@
 // q-hat enters as two fp16 operands, hi = fp16(q-hat) and lo = fp16(q-hat -
 // hi), accumulated into the same D, so the product keeps about 22 bits of
 // q-hat (fp32 q-hat is the reading the method needs: the query stays floating
-// point). Low-bit key codes enter as exact fp16 integers. The score of a
-// low-bit token is then scale * (q . code) + zero * sum(q) per group of d/2
-// channels, so the channels of one MFMA never span two groups.
+// point). Low-bit key codes enter as exact fp16 integers (1024 + code, less
+// 1024; the matrix cores do not take fp16 subnormal operands exactly). The
+// score of a low-bit token is then scale * (q . code) + zero * sum(q) per
+// group of d/2 channels, so the channels of one MFMA never span two groups.
 //
 // Every (token, head) score, its exp and its running-max check are computed
 // once, on the lane that holds it. The value sums stay on the vector ALUs in
@@ -40,6 +41,7 @@ typedef unsigned int tile_u4 __attribute__((ext_vector_type(4)));
 
 constexpr float kTileHeadroom = 16.0f;
 constexpr int kTileG = 16;  // tokens per MFMA group
+constexpr float kTileCodeUnit = 0x1p24f;  // value codes sum as fp16 subnormals, code * 2^-24
 
 // Element e of chunk c (32 channels) for lane group r: the channel it holds.
 // Chunks 0..CPG-1 cover group 0 (channels [0, d/2)), the rest group 1; lane
@@ -316,7 +318,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             x[h] += qn[h][e] * __builtin_amdgcn_rcpf(b8[e]) * qscale * kx[e];
-            a[h][e] = vx[e];
+            a[h][e] = F16T ? vx[e] : vx[e] * (1.0f / kTileCodeUnit);  // code tiers sum in code units
           }
         }
       }
@@ -332,7 +334,10 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     }
   }
 
-  const uint32_t magic = opaque(0x64646464u);
+  // key codes under a 0x64 byte (fp16 1024 + code) for the MFMA; value codes
+  // under a zero byte, the fp16 subnormals code * 2^-24, which v_fma_mix takes
+  // exactly: the value sums carry no 1024 offset to cancel later
+  const uint32_t kmagic = opaque(0x64646464u), magic = opaque(0u);
   auto step = [&](const R_t& R, int grp) {
     // scores on the matrix cores: one accumulator per group of d/2 channels
     tile_f4 acc[2];
@@ -348,7 +353,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
         for (int i = 0; i < 4; ++i) u[i] = R.k[gi][4 * part + i];
         bop = __builtin_bit_cast(tile_h8, u);
       } else {
-        bop = tile_codes<QB>(R.k[gi], part, magic);
+        bop = tile_codes<QB>(R.k[gi], part, kmagic);
       }
       acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[c], bop, acc[gi], 0, 0, 0);
       acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[c], bop, acc[gi], 0, 0, 0);
@@ -407,8 +412,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
         for (int gi = 0; gi < 2; ++gi) {
           const float s = lo_h(R.vsz[gi]), z = hi_h(R.vsz[gi]);
           w[gi][h] = pr * s;
-          // value codes enter as fp16 1024 + code: take 1024 * w back out here
-          zz[h][gi] += pr * z - 1024.0f * w[gi][h];
+          zz[h][gi] += pr * z;
         }
       }
     }
@@ -500,7 +504,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     for (int h = 0; h < RT; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        red[(wave * RT + h) * D + 8 * lane + e] = a[h][e] + (F16T ? 0.0f : zz[h][vg]);
+        red[(wave * RT + h) * D + 8 * lane + e] = F16T ? a[h][e] : a[h][e] * kTileCodeUnit + zz[h][vg];
   }
   if (lane == 0) {
 #pragma unroll
