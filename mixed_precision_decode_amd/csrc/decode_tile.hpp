@@ -538,8 +538,19 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 }
 
 
+#include "decode_tile_mv.hpp"
+
+// Value sums on the matrix cores (tile_split_mv) for 2-bit retained codes of
+// 2-4 heads: measured faster there (32K GQA layer, 4 heads: split kernel
+// 22.4 -> 20.2 us). With 4-bit codes the path needs 233 registers (two waves
+// per SIMD, which the fp16-tier blocks of the same launch then share) and the
+// GQA batch went 53.3 -> 60.8 us; with one head 15 of the 16 MFMA rows idle
+// and the importance-tier layer went 31.9 -> 35.0 us. Those keep tile_split.
+template <int D, int BITS, int RT>
+constexpr bool tile_mv() { return D == 128 && BITS == 2 && RT >= 2; }
+
 template <int D, int BITS, int IB, int RT>
-__global__ __launch_bounds__(kThreads, 3) void decode_tile_kernel(const DecodeK p) {
+__global__ __launch_bounds__(kThreads, (tile_mv<D, BITS, RT>() ? 2 : 3)) void decode_tile_kernel(const DecodeK p) {
   // block order as decode_split_kernel (split-major)
   const int S = p.S16 + p.Sq + p.Sb;
   const int ut = p.units * p.tiles;
@@ -558,9 +569,13 @@ __global__ __launch_bounds__(kThreads, 3) void decode_tile_kernel(const DecodeK 
   __shared__ float red[4 * RT * D + 4 * RT];
   __shared__ float sm_max[4][RT];
   __shared__ float wbuf[4][kTileG][2][RT];
+  constexpr bool kMv = tile_mv<D, BITS, RT>();  // value sums on the matrix cores
+  __shared__ __attribute__((aligned(16))) unsigned char mvbuf[kMv ? 4 * MvStage<(BITS == 2 ? 2 : 4)>::BYTES : 16];
 
   if (split < p.S16) {
     tile_split<D, IB, RT, true>(p, unit, n, g, tile, split, bvec, red, sm_max, po, pml, wbuf);
+  } else if constexpr (kMv) {
+    tile_split_mv<BITS, RT>(p, unit, n, g, tile, split, bvec, red, sm_max, po, pml, mvbuf);
   } else {
     tile_split<D, BITS, RT, false>(p, unit, n, g, tile, split, bvec, red, sm_max, po, pml, wbuf);
   }
