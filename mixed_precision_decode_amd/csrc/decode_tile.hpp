@@ -542,10 +542,12 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 
 // Value sums on the matrix cores (tile_split_mv) for 2-bit retained codes of
 // 2-4 heads: measured faster there (32K GQA layer, 4 heads: split kernel
-// 22.4 -> 20.2 us). With 4-bit codes the path needs 233 registers (two waves
-// per SIMD, which the fp16-tier blocks of the same launch then share) and the
-// GQA batch went 53.3 -> 60.8 us; with one head 15 of the 16 MFMA rows idle
-// and the importance-tier layer went 31.9 -> 35.0 us. Those keep tile_split.
+// 22.4 -> 19.8-20.3 us). With 4-bit codes the path measured slower on the GQA
+// batch (57.7-58.4 us at 168-170 registers against 53.5 us here: per-wave
+// stamps show each 64-token step waiting on its MFMA chains and LDS round
+// trips at two or three waves per SIMD); with one head 15 of the 16 MFMA rows
+// idle and the importance-tier layer went 31.9 -> 35.0 us. Those keep
+// tile_split.
 template <int D, int BITS, int RT>
 constexpr bool tile_mv() { return D == 128 && BITS == 2 && RT >= 2; }
 

@@ -140,13 +140,14 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
   uint32_t kr[4][2][KW];  // keys of the 4 groups (tile_split layout)
   uint32_t vr[VW];        // this lane's token row of value codes
   uint32_t ksz[2], vsz[2];
+  auto load_key_group = [&](int s, int r) {
+    const uint32_t tk = static_cast<uint32_t>((wave + 4 * (4 * s + r)) * kTileG + ai);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) tile_load<KB>(rk, tk * ROWB + (gi * G + 8 * CPG * ar) * QB / 8, kr[r][gi]);
+  };
   auto load_keys = [&](int s) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t tk = static_cast<uint32_t>((wave + 4 * (4 * s + r)) * kTileG + ai);
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi) tile_load<KB>(rk, tk * ROWB + (gi * G + 8 * CPG * ar) * QB / 8, kr[r][gi]);
-    }
+    for (int r = 0; r < 4; ++r) load_key_group(s, r);
   };
   auto load_vals = [&](int s) {
     const uint32_t tv = lane_tok(s);
@@ -165,7 +166,6 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
   };
   load_vals(0);
   load_keys(0);
-  load_sz(0);
 
   // ---- q-hat as MFMA A operands, per-group sums of q-hat (as tile_split)
   tile_h8 qa_hi[NCH], qa_lo[NCH];
@@ -209,11 +209,24 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
   const uint32_t kmagic = opaque(0x64646464u);
   const int kb = lane / 16, li = lane % 16;
   // this lane as a source of the W reads: row of its group for read r, half H
+  // (one lane base; every (group, hi/lo, H, r) is a constant offset from it,
+  // which the reads carry in their offset field: perm(4 r + i) - perm(i) is
+  // 4 r for 2-bit codes and r for 4-bit codes)
+  unsigned char* const wbase = wst + (16 * kb + mv_perm<QB>(li / 4)) * 8;
   auto w_src = [&](int gi, int hl, int H, int r) -> unsigned char* {
-    return wst + (((gi * 2 + hl) * 64) + 16 * kb + 8 * H + mv_perm<QB>(4 * r + li / 4)) * 8;
+    return wbase + ((gi * 2 + hl) * 64 + 8 * H + (QB == 4 ? r : 4 * r)) * 8;
   };
+  // this lane as a source of the 2-bit code reads: row 16 kb + 8 H + i of
+  // chunk 2 kp + h (lane = 16 kb + 2 i + h), again a base plus constants
+  const unsigned char* const cbase = vst + (16 * kb + li / 2) * PITCH + 8 * (li % 2);
 
   for (int s = 0; s < nss; ++s) {
+    // this superstep's scales, loaded here rather than one superstep ahead: a
+    // prefetched copy is a loaded value carried around the loop, and the
+    // compiler moved it between registers at the loop edge behind a wait for
+    // every load in flight; issued first, their own wait at the softmax does
+    // not cover the prefetches issued after them
+    load_sz(s);
     // (1) value code rows into LDS (row = lane), then the next superstep's
     // rows into the same registers
     if constexpr (QB == 4) {
@@ -226,40 +239,45 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
         *reinterpret_cast<uint4*>(vst + lane * PITCH + 16 * i) =
             make_uint4(vr[4 * i], vr[4 * i + 1], vr[4 * i + 2], vr[4 * i + 3]);
     }
-    if (s + 1 < nss) load_vals(s + 1);
+    load_vals(s + 1);  // unconditional: past the range the loads return zeros, and exact wait counts need them
 
-    // (2) key scores of the 4 groups on the matrix cores
-    tile_f4 acc[4][2];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      acc[r][0] = tile_f4{0.0f, 0.0f, 0.0f, 0.0f};
-      acc[r][1] = acc[r][0];
+    // (2) key scores of the 4 groups on the matrix cores, two groups at a time,
+    // each group's key registers refilled for the next superstep once used;
+    // (3) lane t = 16 r + i takes token i of group r: row 0 (lanes 0..15) of
+    // groups 2 q and 2 q + 1 paired by v_permlane16_swap, the pairs by
+    // v_permlane32_swap
+    auto group_scores = [&](int r, tile_f4 (&a)[2]) {
+      a[0] = tile_f4{0.0f, 0.0f, 0.0f, 0.0f};
+      a[1] = a[0];
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int gi = c / CPG, part = c % CPG;
         const tile_h8 bop = tile_codes<QB>(kr[r][gi], part, kmagic);
-        acc[r][gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[c], bop, acc[r][gi], 0, 0, 0);
-        acc[r][gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[c], bop, acc[r][gi], 0, 0, 0);
+        a[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[c], bop, a[gi], 0, 0, 0);
+        a[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[c], bop, a[gi], 0, 0, 0);
       }
+      load_key_group(s + 1, r);
+    };
+    uint32_t pair[2][2][RT];  // [group pair][channel group][head]
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      tile_f4 a0[2], a1[2];
+      group_scores(2 * q2, a0);
+      group_scores(2 * q2 + 1, a1);
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int h = 0; h < RT; ++h) {
+          const auto t = __builtin_amdgcn_permlane16_swap(f2u(a0[gi][h]), f2u(a1[gi][h]), false, false);
+          pair[q2][gi][h] = static_cast<uint32_t>(t[0]);
+        }
     }
-    if (s + 1 < nss) load_keys(s + 1);
-
-    // (3) lane t = 16 r + i takes token i of group r: rows 0 of the four
-    // groups' tiles gathered by two row swaps
     float x[2][RT];
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
       for (int h = 0; h < RT; ++h) {
-        const LanePair p01 = [&] {
-          const auto t = __builtin_amdgcn_permlane16_swap(f2u(acc[0][gi][h]), f2u(acc[1][gi][h]), false, false);
-          return LanePair{static_cast<uint32_t>(t[0]), static_cast<uint32_t>(t[1])};
-        }();
-        const LanePair p23 = [&] {
-          const auto t = __builtin_amdgcn_permlane16_swap(f2u(acc[2][gi][h]), f2u(acc[3][gi][h]), false, false);
-          return LanePair{static_cast<uint32_t>(t[0]), static_cast<uint32_t>(t[1])};
-        }();
-        const auto t = __builtin_amdgcn_permlane32_swap(p01.a, p23.a, false, false);
+        const auto t = __builtin_amdgcn_permlane32_swap(pair[0][gi][h], pair[1][gi][h], false, false);
         x[gi][h] = u2f(static_cast<uint32_t>(t[0]));
       }
 
@@ -268,7 +286,6 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
     const bool valid = tok < nt;
     const float sk0 = lo_h(ksz[0]), sk1 = lo_h(ksz[1]), zk0 = hi_h(ksz[0]), zk1 = hi_h(ksz[1]);
     const float sv0 = lo_h(vsz[0]), sv1 = lo_h(vsz[1]), zv0 = hi_h(vsz[0]), zv1 = hi_h(vsz[1]);
-    if (s + 1 < nss) load_sz(s + 1);
     const float yoff = fmaxf(__builtin_amdgcn_logf(fmaxf(sv0, sv1)), kMvScaleFloor);
     float xs[RT], y[RT];
     bool need = false;
@@ -290,7 +307,7 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
           zz[h][1] *= f;
 #pragma unroll
           for (int t = 0; t < 8; ++t) Dv[t][h] *= f;
-          M[h] = mn;
+          M[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mn)));  // uniform
         }
       }
     }
@@ -321,32 +338,38 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
         *reinterpret_cast<uint2*>(wst + ((gi * 2 + hl) * 64 + lane) * 8) = make_uint2(wh[gi][hl][0], wh[gi][hl][1]);
     __builtin_amdgcn_wave_barrier();
 
-    // (5) W back in A-row layout (row m = head, k-slot e = token 8H + perm(e))
-    tile_h8 aw[2][2][2];  // [group][H][hi/lo]
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-      for (int H = 0; H < 2; ++H)
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) {
-          // the results are taken as whole 32-bit words: unpacking them element by
-          // element into an fp16 vector compiled into element 0 repeated
-          const mv_u2 a = __builtin_bit_cast(mv_u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(MV_LDS(mv_v4s, w_src(gi, hl, H, 0))));
-          const mv_u2 b = __builtin_bit_cast(mv_u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(MV_LDS(mv_v4s, w_src(gi, hl, H, 1))));
-          aw[gi][H][hl] = __builtin_bit_cast(tile_h8, tile_u4{a[0], a[1], b[0], b[1]});
-        }
+    // (5) W back in A-row layout (row m = head, k-slot e = token 8H + perm(e)),
+    // each (group, H) pair read right before its MFMAs; the results are taken
+    // as whole 32-bit words: unpacking them element by element into an fp16
+    // vector compiled into element 0 repeated
+    auto read_w = [&](int gi, int H, tile_h8& whi, tile_h8& wlo) {
+      const mv_u2 a = __builtin_bit_cast(mv_u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(MV_LDS(mv_v4s, w_src(gi, 0, H, 0))));
+      const mv_u2 b = __builtin_bit_cast(mv_u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(MV_LDS(mv_v4s, w_src(gi, 0, H, 1))));
+      const mv_u2 c = __builtin_bit_cast(mv_u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(MV_LDS(mv_v4s, w_src(gi, 1, H, 0))));
+      const mv_u2 d = __builtin_bit_cast(mv_u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(MV_LDS(mv_v4s, w_src(gi, 1, H, 1))));
+      whi = __builtin_bit_cast(tile_h8, tile_u4{a[0], a[1], b[0], b[1]});
+      wlo = __builtin_bit_cast(tile_h8, tile_u4{c[0], c[1], d[0], d[1]});
+    };
 
     // (6) value tiles: codes transposed out of LDS, W x codes on the matrix cores
     if constexpr (QB == 4) {
 #pragma unroll
-      for (int vt = 0; vt < 8; ++vt) {
-        const mv_v2i cw = __builtin_amdgcn_ds_read_tr4_b64_v2i32(MV_LDS(mv_v2i, vst + lane * PITCH + 8 * vt));
-        const int gi = vt / 4;
+      for (int gi = 0; gi < 2; ++gi) {
+        mv_v2i cw[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          cw[v] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(MV_LDS(mv_v2i, vst + lane * PITCH + 8 * (4 * gi + v)));
 #pragma unroll
         for (int H = 0; H < 2; ++H) {
-          const tile_h8 bop = mv_codes<4>(static_cast<uint32_t>(cw[H]), 0u, 0, kmagic);
-          Dv[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[gi][H][0], bop, Dv[vt], 0, 0, 0);
-          Dv[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[gi][H][1], bop, Dv[vt], 0, 0, 0);
+          tile_h8 whi, wlo;
+          read_w(gi, H, whi, wlo);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int vt = 4 * gi + v;
+            const tile_h8 bop = mv_codes<4>(static_cast<uint32_t>(cw[v][H]), 0u, 0, kmagic);
+            Dv[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(whi, bop, Dv[vt], 0, 0, 0);
+            Dv[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo, bop, Dv[vt], 0, 0, 0);
+          }
         }
       }
     } else {
@@ -354,15 +377,16 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
       for (int H = 0; H < 2; ++H)
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
-          // source: row 16 kb + 8 H + i of chunk 2 kp + h (lane = 16 kb + 2 i + h)
-          const unsigned char* src = vst + (16 * kb + 8 * H + li / 2) * PITCH + 8 * (2 * kp + li % 2);
+          const unsigned char* src = cbase + 8 * H * PITCH + 16 * kp;
           const mv_v2i cw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(MV_LDS(mv_v2i, src));
+          tile_h8 whi, wlo;
+          read_w(kp, H, whi, wlo);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const tile_h8 bop = mv_codes<2>(static_cast<uint32_t>(cw[0]), static_cast<uint32_t>(cw[1]), c, kmagic);
             const int vt = 4 * kp + c;
-            Dv[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[kp][H][0], bop, Dv[vt], 0, 0, 0);
-            Dv[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[kp][H][1], bop, Dv[vt], 0, 0, 0);
+            Dv[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(whi, bop, Dv[vt], 0, 0, 0);
+            Dv[vt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo, bop, Dv[vt], 0, 0, 0);
           }
         }
     }
