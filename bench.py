@@ -55,6 +55,8 @@ HBM_PEAK_GBPS = 8000.0
 # sources compiled into the decode-attention kernels; the HBM traffic recorded
 # under profiles/ is reported only while their hash matches the recorded one
 KERNEL_SOURCES = ("mixed_precision_decode_amd/csrc/decode_attn.hip",
+                  "mixed_precision_decode_amd/csrc/decode_tile.hpp",
+                  "mixed_precision_decode_amd/csrc/decode_tile_mv.hpp",
                   "mixed_precision_decode_amd/csrc/common.hpp",
                   "mixed_precision_decode_amd/csrc/kernels.hpp",
                   "mixed_precision_decode_amd/csrc/h2o_common.hpp")
