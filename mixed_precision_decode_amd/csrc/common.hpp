@@ -99,6 +99,25 @@ __device__ __forceinline__ float rows_max(float v) {
   return fmaxf(u2f(x.a), u2f(x.b));
 }
 
+// DPP move of v under control CTRL into the rows set in ROWMASK; other rows,
+// and lanes whose source is out of the row when BC is set, read 0.
+template <int CTRL, int ROWMASK, bool BC>
+__device__ __forceinline__ int dpp_rows(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, BC); }
+
+// Inclusive prefix sum of an int over the wave's 64 lanes (all active): a
+// Hillis-Steele scan inside each 16-lane row (DPP row_shr 1, 2, 4, 8, lanes
+// before the row start reading 0), then row_bcast:15 adds the end of rows 0
+// and 2 to rows 1 and 3, and row_bcast:31 the end of row 1 to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_rows<0x111, 0xF, true>(v);
+  v += dpp_rows<0x112, 0xF, true>(v);
+  v += dpp_rows<0x114, 0xF, true>(v);
+  v += dpp_rows<0x118, 0xF, true>(v);
+  v += dpp_rows<0x142, 0xA, false>(v);
+  v += dpp_rows<0x143, 0xC, false>(v);
+  return v;
+}
+
 // Sum / max over the whole wave (all 64 lanes active); every lane ends with
 // the result.
 __device__ __forceinline__ float wave_sum(float v) { return rows_sum(group_sum<16>(v)); }

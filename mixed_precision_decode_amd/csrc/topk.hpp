@@ -29,12 +29,7 @@ __device__ __forceinline__ int block_scan_add(int v, int* total) {
   constexpr int NWV = NT / kWave;
   __shared__ int s_w[NWV];
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const int incl = wave_incl_scan(v);
   if (lane == kWave - 1) s_w[w] = incl;
   __syncthreads();
   int off = 0, tot = 0;
@@ -113,12 +108,7 @@ __device__ void block_radix_topm(int n, int m, KeyFn keyfn, uint32_t* tau, int* 
 #pragma unroll
       for (int j = 0; j < 4; ++j) { c[j] = static_cast<int>(hist[0][255 - 4 * tid - j]); sum += c[j]; }
       // inclusive scan of lane sums across the wave
-      int incl = sum;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (tid >= off) incl += o;
-      }
+      const int incl = wave_incl_scan(sum);
       const int excl = incl - sum;
       const bool hit = excl < nd && incl >= nd;
       if (hit) {
