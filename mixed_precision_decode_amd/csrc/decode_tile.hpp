@@ -11,10 +11,14 @@
 // q-hat enters as two fp16 operands, hi = fp16(q-hat) and lo = fp16(q-hat -
 // hi), accumulated into the same D, so the product keeps about 22 bits of
 // q-hat (fp32 q-hat is the reading the method needs: the query stays floating
-// point). Low-bit key codes enter as exact fp16 integers (1024 + code, less
-// 1024; the matrix cores do not take fp16 subnormal operands exactly). The
-// score of a low-bit token is then scale * (q . code) + zero * sum(q) per
-// group of d/2 channels, so the channels of one MFMA never span two groups.
+// point). Low-bit key codes enter as the exact fp16 values 1 + code * step
+// (tile_codes; the matrix cores do not take fp16 subnormal operands exactly,
+// so the code cannot simply sit in the low mantissa bits). Per group of d/2
+// channels the product is then sum(q) + step * (q . code), where sum(q) is
+// what the matrix cores form against B = 1 (taken once, at the start). The
+// score of a low-bit token, scale * (q . code) + zero * sum(q), becomes
+// (scale / step) * product + (zero - scale / step) * sum(q): two per-token
+// coefficients, so the channels of one MFMA never span two groups.
 //
 // Every (token, head) score, its exp and its running-max check are computed
 // once, on the lane that holds it. The value sums stay on the vector ALUs in
@@ -89,8 +93,21 @@ __device__ __forceinline__ void tile_load(Rsrc r, uint32_t off, uint32_t* w) {
   }
 }
 
+// Codes as matrix-core operands. 2- and 4-bit codes become the exact fp16
+// values 1 + code * kCodeStep: the code goes to the top of the mantissa under
+// the exponent of 1.0 (2-bit: bits 8-9, a byte 0x3C | code over a zero byte;
+// 4-bit: bits 4-7, the nibble over a 0x3C byte), so building an operand takes
+// byte moves and masks only, and a product with it is sum(A) + step * (A .
+// code), sum(A) being taken back out by the caller. 8-bit codes fill the
+// whole low mantissa byte under 1024 (magic byte 0x64) and one packed
+// subtraction per operand gives the integers.
+template <int QB>
+constexpr float kCodeStep = QB == 2 ? 0.25f : (QB == 4 ? 0x1p-6f : 1.0f);
+template <int QB>
+constexpr uint32_t kCodeMagic = QB == 8 ? 0x64646464u : 0x3C3C3C3Cu;
+
 // The 8 codes of part `part` of a lane's group words -> the MFMA operand
-// (exact fp16 integers, order of tile_chan).
+// (order of tile_chan); magic = kCodeMagic<QB>, kept in a register.
 template <int QB>
 __device__ __forceinline__ tile_h8 tile_codes(const uint32_t* w, int part, uint32_t magic) {
   constexpr uint32_t kLo = 0x04010400u, kHi = 0x04030402u;
@@ -101,19 +118,53 @@ __device__ __forceinline__ tile_h8 tile_codes(const uint32_t* w, int part, uint3
     u[1] = __builtin_amdgcn_perm(magic, a, kHi);
     u[2] = __builtin_amdgcn_perm(magic, b, kLo);
     u[3] = __builtin_amdgcn_perm(magic, b, kHi);
-  } else if constexpr (QB == 4) {  // 8 nibbles of one word
+    return __builtin_bit_cast(tile_h8, u) - static_cast<tile_h8>(static_cast<_Float16>(1024.0f));
+  } else if constexpr (QB == 4) {  // 8 nibbles of one word, each moved to the top of its byte
     const uint32_t x = w[part];
-    const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lo = (x << 4) & 0xF0F0F0F0u, hi = x & 0xF0F0F0F0u;
     u[0] = __builtin_amdgcn_perm(magic, lo, kLo);
     u[1] = __builtin_amdgcn_perm(magic, lo, kHi);
     u[2] = __builtin_amdgcn_perm(magic, hi, kLo);
     u[3] = __builtin_amdgcn_perm(magic, hi, kHi);
-  } else {  // 8 crumbs in 16 bits
-    const uint32_t x = part ? (w[0] >> 16) : w[0];
+  } else {  // 8 crumbs in half `part` of the word: crumb m of its two bytes
+    // as 0x3C | code (one v_and_or_b32, magic in a register), each over a
+    // zero byte: [0, y.b(2 part), 0, y.b(2 part + 1)]
+    const uint32_t x = w[0];
+    const uint32_t sel = part ? 0x03040204u : 0x01040004u;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) u[m] = __builtin_amdgcn_perm(magic, (x >> (2 * m)) & 0x0303u, kLo);
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t y = ((x >> (2 * m)) & 0x03030303u) | magic;
+      u[m] = __builtin_amdgcn_perm(0u, y, sel);
+    }
   }
-  return __builtin_bit_cast(tile_h8, u) - static_cast<tile_h8>(static_cast<_Float16>(1024.0f));
+  return __builtin_bit_cast(tile_h8, u);
+}
+
+// Per-head sums of q-hat over the two channel groups as the matrix cores
+// form them (B = 1; the result's lane 0 holds rows 0..3 = the heads), made
+// wave-uniform.
+template <int NCH, int RT>
+__device__ __forceinline__ void tile_qsums(const tile_h8 (&qa_hi)[NCH], const tile_h8 (&qa_lo)[NCH],
+                                           float (&qs)[RT][2]) {
+  constexpr int CPG = NCH / 2;
+  const tile_h8 ones = static_cast<tile_h8>(static_cast<_Float16>(1.0f));
+  tile_f4 s[2];
+  s[0] = tile_f4{0.0f, 0.0f, 0.0f, 0.0f};
+  s[1] = s[0];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    s[c / CPG] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[c], ones, s[c / CPG], 0, 0, 0);
+    s[c / CPG] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[c], ones, s[c / CPG], 0, 0, 0);
+  }
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int h = 0; h < RT; ++h) {
+      // copied to a scalar first: __builtin_bit_cast of a vector element
+      // compiles into element 0 whatever the index
+      const float v = s[gi][h];
+      qs[h][gi] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    }
 }
 
 template <int D, int QB>
@@ -221,7 +272,6 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 
   // ---- q-hat as MFMA A operands (hi and lo halves), per-group sums of q-hat
   tile_h8 qa_hi[NCH], qa_lo[NCH];
-  float qs_part[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int base = tile_chan<D, 16>(c, ar, 0);
@@ -233,18 +283,11 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
       const _Float16 hi = static_cast<_Float16>(q);
       qa_hi[c][e] = hi;
       qa_lo[c][e] = static_cast<_Float16>(q - static_cast<float>(hi));
-      qs_part[c / CPG] += q;
     }
   }
   // qs[h][gi] = sum over group gi's channels of head h's q-hat (wave-uniform)
   float qs[RT][2];
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const float t = rows_sum(qs_part[gi]);
-#pragma unroll
-    for (int h = 0; h < RT; ++h)
-      qs[h][gi] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), h));
-  }
+  if constexpr (!F16T) tile_qsums<NCH, RT>(qa_hi, qa_lo, qs);
 
   // ---- online-softmax state of the wave
   float M[RT], l[RT], zz[RT][2], a[RT][8];
@@ -334,10 +377,10 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     }
   }
 
-  // key codes under a 0x64 byte (fp16 1024 + code) for the MFMA; value codes
-  // under a zero byte, the fp16 subnormals code * 2^-24, which v_fma_mix takes
-  // exactly: the value sums carry no 1024 offset to cancel later
-  const uint32_t kmagic = opaque(0x64646464u), magic = opaque(0u);
+  // key codes as 1 + code * step for the MFMA (tile_codes); value codes under
+  // a zero byte, the fp16 subnormals code * 2^-24, which v_fma_mix takes
+  // exactly: the value sums carry no offset to cancel later
+  const uint32_t kmagic = opaque(kCodeMagic<QB>), magic = opaque(0u);
   auto step = [&](const R_t& R, int grp) {
     // scores on the matrix cores: one accumulator per group of d/2 channels
     tile_f4 acc[2];
@@ -361,6 +404,16 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     const int tok = grp * kTileG + ai;
     bool valid = lane < kTileG && tok < nt;
     if constexpr (IMPT) valid = valid && tok != frel;
+    // the token's coefficients: scale / step on the product, zero - scale /
+    // step on sum(q-hat) (for 8-bit codes, scale and zero)
+    float ka[2], kz[2];
+    if constexpr (!F16T) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        ka[gi] = lo_h(R.ksz[gi]) * (1.0f / kCodeStep<QB>);
+        kz[gi] = hi_h(R.ksz[gi]) - (QB == 8 ? 0.0f : ka[gi]);
+      }
+    }
     float x[RT];
 #pragma unroll
     for (int h = 0; h < RT; ++h) {
@@ -368,8 +421,8 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
       if constexpr (F16T) {
         xv = acc[0][h] + acc[1][h];
       } else {
-        xv = lo_h(R.ksz[0]) * acc[0][h] + lo_h(R.ksz[1]) * acc[1][h];
-        xv += hi_h(R.ksz[0]) * qs[h][0] + hi_h(R.ksz[1]) * qs[h][1];
+        xv = ka[0] * acc[0][h] + ka[1] * acc[1][h];
+        xv += kz[0] * qs[h][0] + kz[1] * qs[h][1];
       }
       x[h] = valid ? xv : -INFINITY;
       if constexpr (IMPT) {

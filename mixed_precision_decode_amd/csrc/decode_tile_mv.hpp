@@ -16,7 +16,10 @@
 //    head) with every lane busy.
 //  - Value product O[h][c] = sum_t W[h][t] * code[t][c] with W = p * value
 //    scale: k = tokens, B = codes (column = channel), A = W as fp16 hi and lo
-//    rows (about 22 bits of W). A lane of B holds one channel across 8 tokens,
+//    rows (about 22 bits of W). The codes enter as 1 + code * step, like the
+//    keys' (tile_codes), and a second product against B = 1 sums W as the
+//    matrix cores see it, so sum_t W * code = (O - that sum) / step holds
+//    with no assumption on how they treat small W. A lane of B holds one channel across 8 tokens,
 //    which the token-major cache does not give by loads. Each lane writes its
 //    token's code row into LDS and a transposing read returns the channel
 //    view: ds_read_b64_tr_b4 (lane j of a 16-lane group gets nibble j of the 16
@@ -60,27 +63,30 @@ typedef unsigned int mv_u2 __attribute__((ext_vector_type(2)));
 #define MV_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 // 8 codes (one per token) in 8 bytes' crumb c (2-bit) or in a word's nibbles
-// (4-bit) -> B operand, exact fp16 integers in k-slot order.
+// (4-bit) -> B operand, 1 + code * kCodeStep<QB> in k-slot order; magic =
+// kCodeMagic<QB> (the encoding of tile_codes).
 template <int QB>
-__device__ __forceinline__ tile_h8 mv_codes(uint32_t w0, uint32_t w1, int c, uint32_t kmagic) {
-  constexpr uint32_t kLo = 0x04010400u, kHi = 0x04030402u;
+__device__ __forceinline__ tile_h8 mv_codes(uint32_t w0, uint32_t w1, int c, uint32_t magic) {
   tile_u4 u;
-  if constexpr (QB == 4) {  // w0: 8 nibbles = tokens 0..7
-    const uint32_t lo = w0 & 0x0F0F0F0Fu, hi = (w0 >> 4) & 0x0F0F0F0Fu;
-    u[0] = __builtin_amdgcn_perm(kmagic, lo, kLo);
-    u[1] = __builtin_amdgcn_perm(kmagic, lo, kHi);
-    u[2] = __builtin_amdgcn_perm(kmagic, hi, kLo);
-    u[3] = __builtin_amdgcn_perm(kmagic, hi, kHi);
-  } else {  // bytes of w0, w1 = tokens 0..7; crumb c of each
-    const uint32_t y0 = (w0 >> (2 * c)) & 0x03030303u, y1 = (w1 >> (2 * c)) & 0x03030303u;
-    u[0] = __builtin_amdgcn_perm(kmagic, y0, kLo);
-    u[1] = __builtin_amdgcn_perm(kmagic, y0, kHi);
-    u[2] = __builtin_amdgcn_perm(kmagic, y1, kLo);
-    u[3] = __builtin_amdgcn_perm(kmagic, y1, kHi);
+  if constexpr (QB == 4) {  // w0: 8 nibbles = tokens 0..7, each moved to the top of its byte
+    constexpr uint32_t kLo = 0x04010400u, kHi = 0x04030402u;
+    const uint32_t lo = (w0 << 4) & 0xF0F0F0F0u, hi = w0 & 0xF0F0F0F0u;
+    u[0] = __builtin_amdgcn_perm(magic, lo, kLo);
+    u[1] = __builtin_amdgcn_perm(magic, lo, kHi);
+    u[2] = __builtin_amdgcn_perm(magic, hi, kLo);
+    u[3] = __builtin_amdgcn_perm(magic, hi, kHi);
+  } else {  // bytes of w0, w1 = tokens 0..7; crumb c of each as 0x3C | code over a zero byte
+    constexpr uint32_t kB01 = 0x01040004u, kB23 = 0x03040204u;
+    const uint32_t y0 = ((w0 >> (2 * c)) & 0x03030303u) | magic;
+    const uint32_t y1 = ((w1 >> (2 * c)) & 0x03030303u) | magic;
+    u[0] = __builtin_amdgcn_perm(0u, y0, kB01);
+    u[1] = __builtin_amdgcn_perm(0u, y0, kB23);
+    u[2] = __builtin_amdgcn_perm(0u, y1, kB01);
+    u[3] = __builtin_amdgcn_perm(0u, y1, kB23);
   }
   (void)w1;
   (void)c;
-  return __builtin_bit_cast(tile_h8, u) - static_cast<tile_h8>(static_cast<_Float16>(1024.0f));
+  return __builtin_bit_cast(tile_h8, u);
 }
 
 // Channel of column n of value tile vt (8 tiles of 16 channels).
@@ -169,7 +175,6 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
 
   // ---- q-hat as MFMA A operands, per-group sums of q-hat (as tile_split)
   tile_h8 qa_hi[NCH], qa_lo[NCH];
-  float qs_part[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int base = tile_chan<D, 16>(c, ar, 0);
@@ -181,22 +186,15 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
       const _Float16 hi = static_cast<_Float16>(q);
       qa_hi[c][e] = hi;
       qa_lo[c][e] = static_cast<_Float16>(q - static_cast<float>(hi));
-      qs_part[c / CPG] += q;
     }
   }
   float qs[RT][2];
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
-    const float t = rows_sum(qs_part[gi]);
-#pragma unroll
-    for (int h = 0; h < RT; ++h)
-      qs[h][gi] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), h));
-  }
+  tile_qsums<NCH, RT>(qa_hi, qa_lo, qs);
 
   // ---- state: per head the reference M (uniform); per lane the normaliser
   // and zero-point sums; value tiles (lanes 0..15 = heads 0..3 x 16 channels)
   float M[RT], l[RT], zz[RT][2];
-  tile_f4 Dv[8];
+  tile_f4 Dv[8], Dw[2];  // value tiles; W summed against B = 1 per channel group
 #pragma unroll
   for (int h = 0; h < RT; ++h) {
     M[h] = -INFINITY;
@@ -205,8 +203,11 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
   }
 #pragma unroll
   for (int t = 0; t < 8; ++t) Dv[t] = tile_f4{0.0f, 0.0f, 0.0f, 0.0f};
+  Dw[0] = Dv[0];
+  Dw[1] = Dv[0];
+  const tile_h8 ones = static_cast<tile_h8>(static_cast<_Float16>(1.0f));
 
-  const uint32_t kmagic = opaque(0x64646464u);
+  const uint32_t kmagic = opaque(kCodeMagic<QB>);
   const int kb = lane / 16, li = lane % 16;
   // this lane as a source of the W reads: row of its group for read r, half H
   // (one lane base; every (group, hi/lo, H, r) is a constant offset from it,
@@ -284,14 +285,16 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
     // (4) scores, the lazy reference, probabilities and weights
     const int tok = static_cast<int>(lane_tok(s));
     const bool valid = tok < nt;
-    const float sk0 = lo_h(ksz[0]), sk1 = lo_h(ksz[1]), zk0 = hi_h(ksz[0]), zk1 = hi_h(ksz[1]);
+    // key coefficients as in tile_split: scale / step, zero - scale / step
+    const float ka0 = lo_h(ksz[0]) * (1.0f / kCodeStep<QB>), ka1 = lo_h(ksz[1]) * (1.0f / kCodeStep<QB>);
+    const float kz0 = hi_h(ksz[0]) - ka0, kz1 = hi_h(ksz[1]) - ka1;
     const float sv0 = lo_h(vsz[0]), sv1 = lo_h(vsz[1]), zv0 = hi_h(vsz[0]), zv1 = hi_h(vsz[1]);
     const float yoff = fmaxf(__builtin_amdgcn_logf(fmaxf(sv0, sv1)), kMvScaleFloor);
     float xs[RT], y[RT];
     bool need = false;
 #pragma unroll
     for (int h = 0; h < RT; ++h) {
-      const float xv = sk0 * x[0][h] + sk1 * x[1][h] + zk0 * qs[h][0] + zk1 * qs[h][1];
+      const float xv = ka0 * x[0][h] + ka1 * x[1][h] + kz0 * qs[h][0] + kz1 * qs[h][1];
       xs[h] = valid ? xv : -INFINITY;
       y[h] = xs[h] + yoff;
       need |= y[h] > M[h] + kMvHeadroom;
@@ -307,6 +310,8 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
           zz[h][1] *= f;
 #pragma unroll
           for (int t = 0; t < 8; ++t) Dv[t][h] *= f;
+          Dw[0][h] *= f;
+          Dw[1][h] *= f;
           M[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mn)));  // uniform
         }
       }
@@ -363,6 +368,8 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
         for (int H = 0; H < 2; ++H) {
           tile_h8 whi, wlo;
           read_w(gi, H, whi, wlo);
+          Dw[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(whi, ones, Dw[gi], 0, 0, 0);
+          Dw[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo, ones, Dw[gi], 0, 0, 0);
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const int vt = 4 * gi + v;
@@ -381,6 +388,8 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
           const mv_v2i cw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(MV_LDS(mv_v2i, src));
           tile_h8 whi, wlo;
           read_w(kp, H, whi, wlo);
+          Dw[kp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(whi, ones, Dw[kp], 0, 0, 0);
+          Dw[kp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wlo, ones, Dw[kp], 0, 0, 0);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const tile_h8 bop = mv_codes<2>(static_cast<uint32_t>(cw[0]), static_cast<uint32_t>(cw[1]), c, kmagic);
@@ -394,7 +403,8 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
   }
 
   // ---- wave partials: normaliser and zero-point sums over all lanes; value
-  // tiles are already summed over the wave's tokens (lanes 0..15)
+  // tiles and W sums are already summed over the wave's tokens (lanes 0..15;
+  // every column of Dw holds the same sum), sum_t W * code = (Dv - Dw) / step
 #pragma unroll
   for (int h = 0; h < RT; ++h) {
     l[h] = wave_sum(l[h]);
@@ -406,7 +416,8 @@ __device__ __forceinline__ void tile_split_mv(const DecodeK& p, int unit, int n,
     for (int vt = 0; vt < 8; ++vt) {
       const int ch = mv_chan<QB>(vt, lane);
 #pragma unroll
-      for (int h = 0; h < RT; ++h) red[(wave * RT + h) * D + ch] = Dv[vt][h] + zz[h][ch / G];
+      for (int h = 0; h < RT; ++h)
+        red[(wave * RT + h) * D + ch] = (Dv[vt][h] - Dw[ch / G][h]) * (1.0f / kCodeStep<QB>) + zz[h][ch / G];
     }
   }
   if (lane == 0) {
