@@ -1056,17 +1056,18 @@ static const void* split_kernel_ptr() {
 }
 template <int D, int BITS, int IB, int RT, bool TILE, bool KT = false>
 static int blocks_per_cu() {
+  constexpr int kCap = (TILE && tile_mv<D, BITS, RT>()) ? kMvBlocksPerCU : MIKV_BLOCKS_PER_CU;
   static std::atomic<int> cache{0};
   int n = cache.load(std::memory_order_relaxed);
   if (n == 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, split_kernel_ptr<D, BITS, IB, RT, TILE, KT>(), kThreads,
                                                      0) != hipSuccess || n <= 0) {
       (void)hipGetLastError();
-      return MIKV_BLOCKS_PER_CU;
+      return kCap;
     }
     cache.store(n, std::memory_order_relaxed);
   }
-  return n < MIKV_BLOCKS_PER_CU ? n : MIKV_BLOCKS_PER_CU;
+  return n < kCap ? n : kCap;
 }
 // decode_tile_kernel (scores on the matrix cores) for head tiles of 2-4
 // heads, and for every tile when the importance tier holds codes; groups of
@@ -1115,7 +1116,11 @@ static int split_blocks_per_cu(int d, int bits, int ib, int rt, bool tile, int k
 // value sum; the low-bit unpacking roughly matches the FP16 tier's wider
 // lane groups): the time of a tier is its token count, an FP16 token
 // weighted 1.3 (on the 32K GQA shape, token shares of 1:1 and 1.3:1 gave a
-// split kernel of 29.6 and 28.7 us, byte shares 34.2 us).
+// split kernel of 29.6 and 28.7 us, byte shares 34.2 us), and 1.6 where the
+// low-bit tier's value sums run on the matrix cores, which makes its tokens
+// cheaper (same shape: 17.4-17.5 us at 1.3, 17.1 us at 1.6, 17.1-17.2 at 2.0
+// and 2.6; splits rounded to whole 256-token steps, which makes the FP16
+// splits longer: 19.0 us).
 //
 // Per-channel key tiles: the low-bit splits hold whole tiles of 64 tokens
 // (at most kt_max_tiles, the LDS table of a block), and the buffered pairs,
@@ -1135,7 +1140,8 @@ DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, 
                      (imp_bits == 16 ? 4.0 * d : 2.0 * (d * imp_bits / 8 + 4 * (d / group)));
   const double bq = static_cast<double>(nq) * 2.0 * (d * bits / 8 + 4 * (d / group));
   // a code importance tier costs like the retained tier: shares by bytes
-  const double t16 = (pl.RT == 1 || imp_bits < 16) ? b16 : 1.3 * cap16;
+  const double w16 = (tile && tile_mv_of(d, bits, pl.RT)) ? 1.6 : 1.3;
+  const double t16 = (pl.RT == 1 || imp_bits < 16) ? b16 : w16 * cap16;
   const double tq = (pl.RT == 1 || imp_bits < 16) ? bq : static_cast<double>(nq);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;
   long per_unit =

@@ -167,6 +167,34 @@ __device__ __forceinline__ void tile_qsums(const tile_h8 (&qa_hi)[NCH], const ti
     }
 }
 
+// q and b of the tile's A operand: lane (row ai, lane group ar) takes the
+// 8-channel runs tile_chan<D, 16>(c, ar, 0) of the tile's query head ai.
+// Only lanes of live rows (ai < RT) fetch: the others read at the end of the
+// buffers, which a raw buffer load returns as zeros without a memory access
+// (their q-hat is set to 0 afterwards). Every block of the kv head reads the
+// same q and b, so these loads keep the default cache policy.
+template <int D, int RT>
+__device__ __forceinline__ void tile_load_qb(const DecodeK& p, int n, int g, int tile, const float* bvec, int ai,
+                                             int ar, float (&qv)[D / 32][8], float (&bv)[D / 32][8]) {
+  const Rsrc rq = make_rsrc(p.q + (static_cast<int64_t>(n) * p.hq + g * p.rep + tile * RT) * D, RT * D * 2);
+  const Rsrc rb = make_rsrc(bvec, D * 4);
+  const bool live = ai < RT;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const int base = tile_chan<D, 16>(c, ar, 0);
+    const auto qw = __builtin_amdgcn_raw_buffer_load_b128(rq, live ? (ai * D + base) * 2 : RT * D * 2, 0, 0);
+    const auto b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, live ? base * 4 : D * 4, 0, 0);
+    const auto b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, live ? base * 4 + 16 : D * 4, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qv[c][2 * i] = lo_h(qw[i]);
+      qv[c][2 * i + 1] = hi_h(qw[i]);
+      bv[c][i] = u2f(b0[i]);
+      bv[c][4 + i] = u2f(b1[i]);
+    }
+  }
+}
+
 template <int D, int QB>
 struct TileRegs {
   static constexpr int CPG = D / 64;
@@ -248,19 +276,12 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
       tile_load<R_t::VB>(rv, tv * ROWB + vj * R_t::VB, R.v[k]);
     }
   };
-  // ---- q and b first, every lane unconditionally (lanes of rows >= RT read
-  // the last live row and zero it below): their wait then covers neither the
-  // first groups' loads issued after them nor a branch per chunk
+  // ---- q and b first, every lane (rows >= RT read zeros and are zeroed
+  // below): their wait then covers neither the first groups' loads issued
+  // after them nor a branch per chunk
   const float qscale = kLog2e / sqrtf(static_cast<float>(D));
-  const int hrow = g * p.rep + tile * RT + min(ai, RT - 1);  // query head of this lane's row
   float qv[NCH][8], bv[NCH][8];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int base = tile_chan<D, 16>(c, ar, 0);  // first channel of the run
-    load8(p.q + (static_cast<int64_t>(n) * p.hq + hrow) * D + base, qv[c]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bv[c][e] = bvec[base + e];
-  }
+  tile_load_qb<D, RT>(p, n, g, tile, bvec, ai, ar, qv, bv);
 
   // register sets in a ring: NS - 1 groups' loads in flight while one group
   // is computed (two sets; three or four on the low-bit tier measured no
@@ -601,8 +622,15 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 // trips at two or three waves per SIMD); with one head 15 of the 16 MFMA rows
 // idle and the importance-tier layer went 31.9 -> 35.0 us. Those keep
 // tile_split.
+__host__ __device__ constexpr bool tile_mv_of(int d, int bits, int rt) { return d == 128 && bits == 2 && rt >= 2; }
 template <int D, int BITS, int RT>
-constexpr bool tile_mv() { return D == 128 && BITS == 2 && RT >= 2; }
+constexpr bool tile_mv() { return tile_mv_of(D, BITS, RT); }
+// These kernels run two blocks per compute unit (two waves per SIMD), although
+// three fit their 166 registers: on the 32K GQA layer the split kernel took
+// 17.4-17.5 us with two against 19.6-19.8 us with three (and 20.7 us with
+// one); fewer waves per SIMD start their loops sooner and take a larger share
+// of issue each.
+constexpr int kMvBlocksPerCU = 2;
 
 template <int D, int BITS, int IB, int RT>
 __global__ __launch_bounds__(kThreads, (tile_mv<D, BITS, RT>() ? 2 : 3)) void decode_tile_kernel(const DecodeK p) {
