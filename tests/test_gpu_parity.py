@@ -114,12 +114,15 @@ def test_balance_parity(name, over):
 
 
 # ---------------------------------------------------------------- prefill build
-def _prefill_gpu(cfg, seed, balanced=True, capq=None, gpu_scores=False):
+def _prefill_gpu(cfg, seed, balanced=True, capq=None, gpu_scores=False, edit=None):
     """Balancer and prefill build on the device. gpu_scores: the heavy-hitter
     scores acc0 come from the prompt through mikv_prefill_scores (the method's
     own chain) instead of the drawn stand-in; the returned acc0 is then the
-    device's, which both sides consume."""
+    device's, which both sides consume. edit: (q, k, v) -> (q, k, v), applied
+    to the drawn prompt before anything uses it."""
     q, k, v, acc0 = S.prefill_tensors(cfg, seed)
+    if edit is not None:
+        q, k, v = edit(q, k, v)
     dims = dims_of(cfg, capq)
     cache = L.Cache(dims)
     if balanced:
@@ -245,7 +248,7 @@ def _check_step(cfg, N, step, before, after, qd, kd, vd, bh, og, gp16, gdpos, mi
     assert np.array_equal(gdpos, np.take_along_axis(rst["pos16"], drop[..., None], 2)[..., 0])
 
 
-def _lockstep(cfg, seed, steps, balanced=True, check_every=1, fused=False, sample=0, gpu_scores=False):
+def _lockstep(cfg, seed, steps, balanced=True, check_every=1, fused=False, sample=0, gpu_scores=False, edit=None):
     """steps decode steps on the device; every check_every-th step (and the
     last) is compared with the oracle over all units, and with sample > 0
     every other step is compared over `sample` units (a different set each
@@ -253,7 +256,7 @@ def _lockstep(cfg, seed, steps, balanced=True, check_every=1, fused=False, sampl
     configuration); else mikv_decode_attn then mikv_h2o_update_select.
     gpu_scores: the prompt's heavy-hitter scores come from
     mikv_prefill_scores, and the prefill build on them is checked first."""
-    dims, cache, b, (q, k, v, acc0) = _prefill_gpu(cfg, seed, balanced, gpu_scores=gpu_scores)
+    dims, cache, b, (q, k, v, acc0) = _prefill_gpu(cfg, seed, balanced, gpu_scores=gpu_scores, edit=edit)
     bh = host(b)
     if gpu_scores:
         kb = O.balance(q, k)[1] if balanced else k
@@ -325,6 +328,43 @@ def test_decode_lockstep(name, over, balanced, steps):
     cfg = S.CONFIGS[name].scaled(**over)
     print(f"lockstep {name} {over} balanced={balanced} steps={steps}", flush=True)
     _lockstep(cfg, 11, steps, balanced)
+
+
+def _edge_rows(q, k, v):
+    """Prompt rows at the edges of the code encodings: constant rows (scale
+    0; a key row stays constant through the per-channel balancer only when it
+    is zero), rows scaled into fp16's subnormal range (subnormal scales), wide
+    value rows, and every other query head scaled down so that the low fp16
+    parts of its q-hat are subnormals."""
+    f32 = np.float32
+    q, k, v = q.copy(), k.copy(), v.copy()
+    k[:, :, 1::7] = k[:, :, 1::7, :1]
+    k[:, :, 6::17] = 0
+    v[:, :, 2::7] = v[:, :, 2::7, :1]
+    k[:, :, 3::11] = (k[:, :, 3::11].astype(f32) * f32(1e-5)).astype(np.float16)
+    v[:, :, 4::11] = (v[:, :, 4::11].astype(f32) * f32(1e-5)).astype(np.float16)
+    v[:, :, 5::13] = (v[:, :, 5::13].astype(f32) * f32(64.0)).astype(np.float16)
+    q[:, ::2] = (q[:, ::2].astype(f32) * f32(1e-2)).astype(np.float16)
+    return q, k, v
+
+
+@pytest.mark.parametrize("name,over,steps,balanced", [
+    ("llama3_8b_32k", dict(hq=8, hkv=2, T=1500), 3, True),    # 2-bit codes, value sums on the matrix cores
+    ("llama3_8b_32k", dict(hq=8, hkv=2, T=1500), 2, False),   # constant key rows kept constant
+    ("llama3_8b_32k", dict(hq=8, hkv=4, T=1200), 3, True),    # the same with two-head tiles
+    ("gqa_throughput", dict(batch=2, T=600), 3, True),        # 4-bit codes, vector value sums
+    ("gqa_throughput", dict(batch=2, T=600), 2, False),
+    ("tiny", dict(hq=4, hkv=1), 4, True),                     # head dim 64
+    ("llama2_7b_layer", dict(batch=1, hq=2, hkv=2, T=700), 2, True),  # single-head tiles
+])
+def test_decode_lockstep_edge_rows(name, over, steps, balanced):
+    """Lockstep decode (the fused step) over a prompt with constant,
+    subnormal-scale and wide rows and small query heads: the codes enter the
+    matrix cores as 1 + code * step and the constant part is taken back out
+    through sums the matrix cores form themselves, which these rows stress."""
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"edge-row lockstep {name} {over} steps={steps} balanced={balanced}", flush=True)
+    _lockstep(cfg, 23, steps, balanced, fused=True, edit=_edge_rows)
 
 
 @pytest.mark.parametrize("name,over,steps", [
