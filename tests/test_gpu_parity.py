@@ -641,6 +641,43 @@ def test_graph_replay_matches_eager():
             assert np.array_equal(np.asarray(c1[key]).view(np.uint8), np.asarray(c2[key]).view(np.uint8)), key
 
 
+# ---------------------------------------------------------------- determinism
+@pytest.mark.parametrize("name,over,steps", [
+    ("llama3_8b_32k", dict(hq=8, hkv=2, T=6000), 3),   # head tiles, value sums on the matrix cores
+    ("gqa_throughput", dict(batch=8, T=1500), 3),       # head tiles, 4-bit codes
+    ("llama2_7b_layer", dict(batch=2, T=2000), 3),      # single-head splits
+])
+def test_runs_bit_identical(name, over, steps):
+    """Two runs from the same prompt, prompt scores from mikv_prefill_scores
+    included, give bit-identical prompt scores, outputs, probabilities and
+    caches at every step: every reduction on the path has a fixed order."""
+    cfg = S.CONFIGS[name].scaled(**over)
+    print(f"determinism {name} {over} steps={steps}", flush=True)
+    runs = []
+    for _ in range(2):
+        dims, cache, b, (_, _, _, acc0) = _prefill_gpu(cfg, 31, True, gpu_scores=True)
+        o = torch.zeros((cfg.batch, cfg.hq, cfg.d), dtype=torch.float32, device="cuda")
+        p16 = torch.zeros((cfg.batch, cfg.hkv, cfg.cap16), dtype=torch.float32, device="cuda")
+        dpos = torch.zeros((cfg.batch, cfg.hkv), dtype=torch.int32, device="cuda")
+        ws = torch.zeros(L.mikv_decode_attn_workspace(dims, cfg.T + steps), dtype=torch.uint8, device="cuda")
+        trace = [np.asarray(acc0).copy()]
+        for step in range(steps):
+            qd, kd, vd = S.decode_tensors(cfg, 31, step)
+            L.mikv_decode_step(dims, cache, cfg.T + step + 1, cfg.recent, cfg.H, dev(qd), dev(kd), dev(vd), b,
+                               o, p16, ws, demoted_pos=dpos)
+            trace.append((host(o).copy(), host(p16).copy(), host(dpos).copy(), cache.to_numpy()))
+        runs.append(trace)
+    a, b2 = runs
+    assert np.array_equal(a[0].view(np.uint32), b2[0].view(np.uint32)), "prompt scores"
+    for step, ((o1, p1, d1, c1), (o2, p2, d2, c2)) in enumerate(zip(a[1:], b2[1:])):
+        assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), f"o step {step}"
+        assert np.array_equal(p1.view(np.uint32), p2.view(np.uint32)), f"p16 step {step}"
+        assert np.array_equal(d1, d2), f"demoted positions step {step}"
+        for key in L.Cache.NAMES:
+            assert np.array_equal(np.asarray(c1[key]).view(np.uint8), np.asarray(c2[key]).view(np.uint8)), \
+                f"{key} step {step}"
+
+
 # ---------------------------------------------------------------- fused decode step
 @pytest.mark.parametrize("name,over,steps", [
     ("tiny", {}, 8), ("tiny", dict(hq=8, hkv=2, bits=2), 6), ("tiny", dict(recent=0), 4),
