@@ -72,6 +72,16 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+def split_kernel_name(cfg):
+    """The kernel of the split step for this cache, as the library picks it:
+    tiles of 2-4 query heads (an even group) and caches whose importance tier
+    holds codes run decode_tile_kernel when quantization groups are d/2 and
+    keys are quantized per token; everything else runs decode_split_kernel."""
+    rt = 4 if cfg.rep % 4 == 0 else (2 if cfg.rep % 2 == 0 else 1)
+    tile = cfg.key_tile == 0 and cfg.G == cfg.d // 2 and (cfg.imp_bits < 16 or rt > 1)
+    return "decode_tile_kernel" if tile else "decode_split_kernel"
+
+
 def recorded_traffic(workload, key="split_traffic_bytes_per_launch"):
     """HBM bytes per launch of the split kernel (key
     split_traffic_bytes_per_launch) or per decode-attention call, split +
@@ -694,10 +704,10 @@ def decode_run(cfg, args, log, K, W, KA, cpu_seconds):
         "roofline": {"bound": "hbm", "achieved": k_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": k_gbps / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic(cfg.name) if traffic_ok else None,
-                     "launches_timed": KA, "statistic": "median", "kernel": "decode_split_kernel",
+                     "launches_timed": KA, "statistic": "median", "kernel": split_kernel_name(cfg),
                      "kernel_us": split_us, "bytes_per_launch": kbytes,
                      "timing": "hipExtLaunchKernel start/stop events of the kernel itself"},
-        "attn_call": {"kernels": "decode_split_kernel + decode_merge_kernel (one mikv_decode_attn call)",
+        "attn_call": {"kernels": f"{split_kernel_name(cfg)} + decode_merge_kernel (one mikv_decode_attn call)",
                       "us": call_us, "bytes": abytes, "GBps": a_gbps, "frac": a_gbps / HBM_PEAK_GBPS,
                       "launches_timed": KA, "statistic": "median",
                       "traffic": recorded_traffic(cfg.name, "call_traffic_bytes") if traffic_ok else None,
