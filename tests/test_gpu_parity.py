@@ -435,6 +435,9 @@ def test_prefill_build_importance_codes(name, over):
     ("gqa_throughput", dict(batch=3, T=600, imp_bits=8, bits=2), 4, True),
     ("llama3_8b_32k", dict(hq=8, hkv=2, T=4100, imp_bits=4, bits=2), 3, True),
     ("llama2_7b_layer", dict(batch=2, hq=3, hkv=3, T=1500, imp_bits=4, bits=2), 3, False),
+    ("tiny", dict(imp_bits=4, bits=2, hq=3, hkv=1, batch=2, T=333), 6, True),  # three single-head tiles, ragged
+    ("tiny", dict(imp_bits=4, bits=2, pct=0, recent=0), 4, False),             # B = 0: only the new token
+    ("llama2_7b_layer", dict(batch=2, hq=2, hkv=2, T=2100, imp_bits=4, bits=4), 3, True),
 ])
 def test_decode_lockstep_importance_codes(name, over, steps, fused):
     """Decode steps with an 8- or 4-bit importance tier against the oracle,
