@@ -1116,11 +1116,12 @@ static int split_blocks_per_cu(int d, int bits, int ib, int rt, bool tile, int k
 // value sum; the low-bit unpacking roughly matches the FP16 tier's wider
 // lane groups): the time of a tier is its token count, an FP16 token
 // weighted 1.3 (on the 32K GQA shape, token shares of 1:1 and 1.3:1 gave a
-// split kernel of 29.6 and 28.7 us, byte shares 34.2 us), and 1.6 where the
-// low-bit tier's value sums run on the matrix cores, which makes its tokens
-// cheaper (same shape: 17.4-17.5 us at 1.3, 17.1 us at 1.6, 17.1-17.2 at 2.0
-// and 2.6; splits rounded to whole 256-token steps, which makes the FP16
-// splits longer: 19.0 us).
+// split kernel of 29.6 and 28.7 us, byte shares 34.2 us; on the GQA batch
+// 1.1-1.5 all give 48.8-49.1 us), and 2.4 where the low-bit tier's value
+// sums run on the matrix cores, which makes its tokens cheaper (32K GQA
+// shape: 17.8 us at 1.2, 17.4-17.5 at 1.6, 16.8-17.1 at 2.0-3.0; splits
+// rounded to whole 256-token steps, which makes the FP16 splits longer:
+// 19.0 us).
 //
 // Per-channel key tiles: the low-bit splits hold whole tiles of 64 tokens
 // (at most kt_max_tiles, the LDS table of a block), and the buffered pairs,
@@ -1140,7 +1141,7 @@ DecodePlan decode_plan(int batch, int hkv, int d, int bits, int group, int rep, 
                      (imp_bits == 16 ? 4.0 * d : 2.0 * (d * imp_bits / 8 + 4 * (d / group)));
   const double bq = static_cast<double>(nq) * 2.0 * (d * bits / 8 + 4 * (d / group));
   // a code importance tier costs like the retained tier: shares by bytes
-  const double w16 = (tile && tile_mv_of(d, bits, pl.RT)) ? 1.6 : 1.3;
+  const double w16 = (tile && tile_mv_of(d, bits, pl.RT)) ? 2.4 : 1.3;
   const double t16 = (pl.RT == 1 || imp_bits < 16) ? b16 : w16 * cap16;
   const double tq = (pl.RT == 1 || imp_bits < 16) ? bq : static_cast<double>(nq);
   const long units = static_cast<long>(batch) * hkv * pl.tiles;

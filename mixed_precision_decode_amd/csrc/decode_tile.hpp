@@ -5,9 +5,10 @@
 // batched matrix-vector product over a precision-grouped cache. With g query
 // heads per kv head the product against the keys is a small matrix product
 // (heads x tokens x channels); here it runs as v_mfma_f32_16x16x32_f16:
-//   A = q-hat, rows = the tile's heads (rows RT..15 zero), k = 32 channels;
+//   A = q-hat, head h in row 4h (the other rows zero), k = 32 channels;
 //   B = keys of 16 tokens, k = the same 32 channels, columns = tokens;
-//   D = scores, lane l < 16 holds the RT head scores of token l.
+//   D = scores: register 0 of lane 16h + t holds head h's score of token t,
+//   so with 4 heads each lane of the wave carries one (token, head) score.
 // q-hat enters as two fp16 operands, hi = fp16(q-hat) and lo = fp16(q-hat -
 // hi), accumulated into the same D, so the product keeps about 22 bits of
 // q-hat (fp32 q-hat is the reading the method needs: the query stays floating
@@ -167,22 +168,52 @@ __device__ __forceinline__ void tile_qsums(const tile_h8 (&qa_hi)[NCH], const ti
     }
 }
 
+// The same sums with head h in A row 4h (tile_split's layout): D row 4h is
+// register 0 of lane group h, so each lane gets the sums of its own head
+// (zero on lane groups >= RT).
+template <int NCH>
+__device__ __forceinline__ void tile_qsums_lane(const tile_h8 (&qa_hi)[NCH], const tile_h8 (&qa_lo)[NCH],
+                                                float (&qs)[2]) {
+  constexpr int CPG = NCH / 2;
+  const tile_h8 ones = static_cast<tile_h8>(static_cast<_Float16>(1.0f));
+  tile_f4 s[2];
+  s[0] = tile_f4{0.0f, 0.0f, 0.0f, 0.0f};
+  s[1] = s[0];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    s[c / CPG] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_hi[c], ones, s[c / CPG], 0, 0, 0);
+    s[c / CPG] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[c], ones, s[c / CPG], 0, 0, 0);
+  }
+  qs[0] = s[0][0];
+  qs[1] = s[1][0];
+}
+
+// A-operand row ai of the tile's query heads: head ai (rows RT..15 zero),
+// or with SPREAD head ai / 4 in rows 0, 4, 8, 12 (the others zero), which
+// puts head h's scores in register 0 of lane group h. -1: a zero row.
+template <int RT, bool SPREAD>
+__device__ __forceinline__ int tile_row_head(int ai) {
+  if constexpr (SPREAD) return (ai % 4 == 0 && ai / 4 < RT) ? ai / 4 : -1;
+  else return ai < RT ? ai : -1;
+}
+
 // q and b of the tile's A operand: lane (row ai, lane group ar) takes the
-// 8-channel runs tile_chan<D, 16>(c, ar, 0) of the tile's query head ai.
-// Only lanes of live rows (ai < RT) fetch: the others read at the end of the
+// 8-channel runs tile_chan<D, 16>(c, ar, 0) of the query head of row ai.
+// Only lanes of live rows fetch: the others read at the end of the
 // buffers, which a raw buffer load returns as zeros without a memory access
 // (their q-hat is set to 0 afterwards). Every block of the kv head reads the
 // same q and b, so these loads keep the default cache policy.
-template <int D, int RT>
+template <int D, int RT, bool SPREAD = false>
 __device__ __forceinline__ void tile_load_qb(const DecodeK& p, int n, int g, int tile, const float* bvec, int ai,
                                              int ar, float (&qv)[D / 32][8], float (&bv)[D / 32][8]) {
   const Rsrc rq = make_rsrc(p.q + (static_cast<int64_t>(n) * p.hq + g * p.rep + tile * RT) * D, RT * D * 2);
   const Rsrc rb = make_rsrc(bvec, D * 4);
-  const bool live = ai < RT;
+  const int hr = tile_row_head<RT, SPREAD>(ai);
+  const bool live = hr >= 0;
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
     const int base = tile_chan<D, 16>(c, ar, 0);
-    const auto qw = __builtin_amdgcn_raw_buffer_load_b128(rq, live ? (ai * D + base) * 2 : RT * D * 2, 0, 0);
+    const auto qw = __builtin_amdgcn_raw_buffer_load_b128(rq, live ? (hr * D + base) * 2 : RT * D * 2, 0, 0);
     const auto b0 = __builtin_amdgcn_raw_buffer_load_b128(rb, live ? base * 4 : D * 4, 0, 0);
     const auto b1 = __builtin_amdgcn_raw_buffer_load_b128(rb, live ? base * 4 + 16 : D * 4, 0, 0);
 #pragma unroll
@@ -281,7 +312,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
   // after them nor a branch per chunk
   const float qscale = kLog2e / sqrtf(static_cast<float>(D));
   float qv[NCH][8], bv[NCH][8];
-  tile_load_qb<D, RT>(p, n, g, tile, bvec, ai, ar, qv, bv);
+  tile_load_qb<D, RT, true>(p, n, g, tile, bvec, ai, ar, qv, bv);
 
   // register sets in a ring: NS - 1 groups' loads in flight while one group
   // is computed (two sets; three or four on the low-bit tier measured no
@@ -300,26 +331,28 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     for (int e = 0; e < 8; ++e) {
       const int ch = tile_chan<D, QB>(c, ar, e);
       const float qe = qv[c][ch - base] * __builtin_amdgcn_rcpf(bv[c][ch - base]) * qscale;
-      const float q = ai < RT ? qe : 0.0f;
+      const float q = tile_row_head<RT, true>(ai) >= 0 ? qe : 0.0f;
       const _Float16 hi = static_cast<_Float16>(q);
       qa_hi[c][e] = hi;
       qa_lo[c][e] = static_cast<_Float16>(q - static_cast<float>(hi));
     }
   }
-  // qs[h][gi] = sum over group gi's channels of head h's q-hat (wave-uniform)
-  float qs[RT][2];
-  if constexpr (!F16T) tile_qsums<NCH, RT>(qa_hi, qa_lo, qs);
+  // head h sits in A row 4h, so lane 16 h + t holds head h's score of token
+  // t (register 0 of the accumulators); lane groups >= RT hold none
+  const int hl = lane / 16;
+  // qs[gi] = sum over group gi's channels of the lane's head's q-hat
+  float qs[2] = {0.0f, 0.0f};
+  if constexpr (!F16T) tile_qsums_lane<NCH>(qa_hi, qa_lo, qs);
 
-  // ---- online-softmax state of the wave
-  float M[RT], l[RT], zz[RT][2], a[RT][8];
+  // ---- online-softmax state of the wave: running maximum, sum and
+  // zero-point sums of the lane's head (uniform over its lane group, the
+  // sums partial per lane), value sums of every head in row layout
+  float M = -INFINITY, l = 0.0f, zz[2] = {0.0f, 0.0f};
+  float a[RT][8];
 #pragma unroll
-  for (int h = 0; h < RT; ++h) {
-    M[h] = -INFINITY;
-    l[h] = 0.0f;
-    zz[h][0] = zz[h][1] = 0.0f;
+  for (int h = 0; h < RT; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[h][e] = 0.0f;
-  }
 
   // ---- the new token: appended by the tile-0 block that owns the free
   // slot, and seeded into wave 0's state (max = its score, sum = 1, o = v).
@@ -389,11 +422,12 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 #pragma unroll
       for (int h = 0; h < RT; ++h) {
         x[h] = group_sum<LPTV>(x[h]);
-        M[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x[h]), 0));
-        if (lane == 0) {
-          l[h] = 1.0f;
-          p.sc16[scb + static_cast<int64_t>(h) * p.cap16 + frel] = M[h];
+        const float xu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x[h]), 0));
+        if (hl == h) {
+          M = xu;
+          if (lane % 16 == 0) l = 1.0f;
         }
+        if (lane == 0) p.sc16[scb + static_cast<int64_t>(h) * p.cap16 + frel] = xu;
       }
     }
   }
@@ -423,7 +457,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
       acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa_lo[c], bop, acc[gi], 0, 0, 0);
     }
     const int tok = grp * kTileG + ai;
-    bool valid = lane < kTileG && tok < nt;
+    bool valid = hl < RT && tok < nt;
     if constexpr (IMPT) valid = valid && tok != frel;
     // the token's coefficients: scale / step on the product, zero - scale /
     // step on sum(q-hat) (for 8-bit codes, scale and zero)
@@ -435,66 +469,52 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
         kz[gi] = hi_h(R.ksz[gi]) - (QB == 8 ? 0.0f : ka[gi]);
       }
     }
-    float x[RT];
-#pragma unroll
-    for (int h = 0; h < RT; ++h) {
-      float xv;
-      if constexpr (F16T) {
-        xv = acc[0][h] + acc[1][h];
-      } else {
-        xv = ka[0] * acc[0][h] + ka[1] * acc[1][h];
-        xv += kz[0] * qs[h][0] + kz[1] * qs[h][1];
-      }
-      x[h] = valid ? xv : -INFINITY;
-      if constexpr (IMPT) {
-        if (valid) p.sc16[scb + static_cast<int64_t>(h) * p.cap16 + tok] = xv;
-      }
+    float xv;
+    if constexpr (F16T) {
+      xv = acc[0][0] + acc[1][0];
+    } else {
+      xv = ka[0] * acc[0][0] + ka[1] * acc[1][0];
+      xv += kz[0] * qs[0] + kz[1] * qs[1];
+    }
+    const float x = valid ? xv : -INFINITY;
+    if constexpr (IMPT) {
+      if (valid) p.sc16[scb + static_cast<int64_t>(hl) * p.cap16 + tok] = xv;
     }
     // lazy running maximum: moves only when a score exceeds it by more than
     // the headroom (also on the first scores of the wave)
-    bool need = false;
-#pragma unroll
-    for (int h = 0; h < RT; ++h) need |= x[h] > M[h] + kTileHeadroom;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    if (__builtin_amdgcn_ballot_w64(x > M + kTileHeadroom) != 0) {
+      // the row maximum of each lane group is its head's (-inf on groups >= RT)
+      const float mn = fmaxf(M, group_max<16>(x));
+      const float f = mn > M ? fast_exp2(M - mn) : 1.0f;  // 0 when M was -inf
+      l *= f;
+      zz[0] *= f;
+      zz[1] *= f;
+      M = mn;
 #pragma unroll
       for (int h = 0; h < RT; ++h) {
-        // scores live on lanes 0..15 (-inf elsewhere): a row maximum, made uniform
-        const float rm = group_max<16>(x[h]);
-        const float mn = fmaxf(M[h], __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rm), 0)));
-        if (mn > M[h]) {
-          const float f = fast_exp2(M[h] - mn);  // 0 when M was -inf
-          l[h] *= f;
-          zz[h][0] *= f;
-          zz[h][1] *= f;
+        const float fh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), 16 * h));
 #pragma unroll
-          for (int e = 0; e < 8; ++e) a[h][e] *= f;
-          M[h] = mn;
-        }
+        for (int e = 0; e < 8; ++e) a[h][e] *= fh;
       }
     }
-    // probabilities and the weights of the value sums
-    float w[2][RT];
+    // the probability and the weights of the value sums
+    const float pr = fast_exp2(x - fmaxf(M, -FLT_MAX));
+    l += pr;
+    float w[2];
+    if constexpr (F16T) {
+      w[0] = pr;
+      w[1] = pr;
+    } else {
 #pragma unroll
-    for (int h = 0; h < RT; ++h) {
-      const float pr = fast_exp2(x[h] - fmaxf(M[h], -FLT_MAX));
-      l[h] += pr;
-      if constexpr (F16T) {
-        w[0][h] = pr;
-        w[1][h] = pr;
-      } else {
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          const float s = lo_h(R.vsz[gi]), z = hi_h(R.vsz[gi]);
-          w[gi][h] = pr * s;
-          zz[h][gi] += pr * z;
-        }
+      for (int gi = 0; gi < 2; ++gi) {
+        const float s = lo_h(R.vsz[gi]), z = hi_h(R.vsz[gi]);
+        w[gi] = pr * s;
+        zz[gi] += pr * z;
       }
     }
-    if (lane < kTileG) {
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-        for (int h = 0; h < RT; ++h) wbuf[wave][lane][gi][h] = w[gi][h];
+    if (hl < RT) {
+      wbuf[wave][ai][0][hl] = w[0];
+      wbuf[wave][ai][1][hl] = w[1];
     }
     __builtin_amdgcn_wave_barrier();
     // value sums: 8 channels per lane, VTPL tokens
@@ -563,13 +583,18 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     }
   }
 
-  // ---- wave partials: l and the zero-point sums over the 16 score lanes (zero
-  // on the others; lanes 0..15 end with the totals), value slices over slots
+  // ---- wave partials: l and the zero-point sums over each head's 16 score
+  // lanes (every lane of the group ends with its head's totals), value
+  // slices over slots
+  l = group_sum<16>(l);
+  zz[0] = group_sum<16>(zz[0]);
+  zz[1] = group_sum<16>(zz[1]);
+  float zh[RT][2];
 #pragma unroll
   for (int h = 0; h < RT; ++h) {
-    l[h] = group_sum<16>(l[h]);
-    zz[h][0] = group_sum<16>(zz[h][0]);
-    zz[h][1] = group_sum<16>(zz[h][1]);
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+      zh[h][gi] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, zz[gi]), 16 * h));
 #pragma unroll
     for (int e = 0; e < 8; ++e) a[h][e] = slot_sum<LPTV>(a[h][e]);
   }
@@ -578,14 +603,11 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     for (int h = 0; h < RT; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        red[(wave * RT + h) * D + 8 * lane + e] = F16T ? a[h][e] : a[h][e] * kTileCodeUnit + zz[h][vg];
+        red[(wave * RT + h) * D + 8 * lane + e] = F16T ? a[h][e] : a[h][e] * kTileCodeUnit + zh[h][vg];
   }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < RT; ++h) {
-      sm[wave][h] = M[h];
-      red[4 * RT * D + wave * RT + h] = l[h];
-    }
+  if (lane % 16 == 0 && hl < RT) {
+    sm[wave][hl] = M;
+    red[4 * RT * D + wave * RT + hl] = l;
   }
   __syncthreads();
   // ---- block partial: the four waves rebased to their common maximum

@@ -9,8 +9,9 @@
 // v_mfma_f32_16x16x32_f16.
 //
 // A wave takes 64 tokens at a time: four 16-token groups of its share.
-//  - Key scores as in tile_split (A = q-hat hi and lo rows, B = the codes of 16
-//    tokens); the four groups' score tiles, held by lanes 0..15, are then moved
+//  - Key scores as in tile_split, but with the tile's heads in A rows
+//    0..RT-1 (A = q-hat hi and lo rows, B = the codes of 16 tokens); the four
+//    groups' score tiles, held by lanes 0..15, are then moved
 //    so that lane t holds token t's scores of every head (v_permlane16_swap,
 //    v_permlane32_swap), and the softmax bookkeeping runs once per (token,
 //    head) with every lane busy.
