@@ -786,7 +786,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(const DecodeK p)
   const int unit = rest / p.tiles;
   const int n = unit / p.hkv;
   const int g = unit % p.hkv;
-  const int tid = threadIdx.x;
   const float* bvec = p.b + static_cast<int64_t>(unit) * D;
   const int part = (unit * p.tiles + tile) * S + split;
   float* po = p.part_o + static_cast<int64_t>(part) * RT * D;

@@ -48,6 +48,23 @@ constexpr float kTileHeadroom = 16.0f;
 constexpr int kTileG = 16;  // tokens per MFMA group
 constexpr float kTileCodeUnit = 0x1p24f;  // value codes sum as fp16 subnormals, code * 2^-24
 
+// Value codes enter the value sums as fp16 subnormals: a code masked in
+// place inside a 16-bit half, so each half reads as code * 2^(p - 24) for the
+// code's bit position p (p + bits <= 10 keeps the exponent field zero). One
+// AND gives the codes of two channels (two tokens for 2-bit codes). The
+// factor that turns channel e's sum back into code units:
+//   4-bit (channel c at bits 4c of a token's word): even channels sit at bit
+//     0 of a half, odd ones at bit 4;
+//   2-bit (channel c at bits 2c of a token's 16 bits): channels 0..4 at bits
+//     2c, channels 5..7, shifted down by 10, at bits 2(c - 5);
+//   8-bit: every code at bit 0.
+template <int QB>
+__device__ __forceinline__ constexpr float tile_val_unit(int e) {
+  if constexpr (QB == 4) return (e % 2) ? 0x1p20f : 0x1p24f;
+  else if constexpr (QB == 2) return 0x1p24f / static_cast<float>(1 << (2 * (e < 5 ? e : e - 5)));
+  else return kTileCodeUnit;
+}
+
 // Element e of chunk c (32 channels) for lane group r: the channel it holds.
 // Chunks 0..CPG-1 cover group 0 (channels [0, d/2)), the rest group 1; lane
 // group r takes a contiguous run of 8*CPG channels of each group. Within the
@@ -415,7 +432,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             x[h] += qn[h][e] * __builtin_amdgcn_rcpf(b8[e]) * qscale * kx[e];
-            a[h][e] = F16T ? vx[e] : vx[e] * (1.0f / kTileCodeUnit);  // code tiers sum in code units
+            a[h][e] = F16T ? vx[e] : vx[e] / tile_val_unit<QB>(e);  // code tiers sum in code units
           }
         }
       }
@@ -517,55 +534,57 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
       wbuf[wave][ai][1][hl] = w[1];
     }
     __builtin_amdgcn_wave_barrier();
-    // value sums: 8 channels per lane, VTPL tokens
+    // value sums: 8 channels per lane, VTPL tokens taken in pairs
+    static_assert(VTPL % 2 == 0, "2-bit values pair the lane's tokens");
+    // channel e += w * (the low or high half of word m)
+    auto acc2 = [&](int e, const float (&w)[RT], uint32_t m, bool hi) {
+      const float v = hi ? hi_h(m) : lo_h(m);
 #pragma unroll
-    for (int k = 0; k < VTPL; ++k) {
-      const int tl = vs + k * VSLOTS;
-      float wv[RT];
+      for (int h = 0; h < RT; ++h) a[h][e] += w[h] * v;
+    };
 #pragma unroll
-      for (int h = 0; h < RT; ++h) wv[h] = wbuf[wave][tl][vg][h];
-      if constexpr (F16T) {
+    for (int k = 0; k < VTPL; k += 2) {
+      float wv[2][RT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float lo = lo_h(R.v[k][i]), hi = hi_h(R.v[k][i]);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-          for (int h = 0; h < RT; ++h) {
-            a[h][2 * i] += wv[h] * lo;
-            a[h][2 * i + 1] += wv[h] * hi;
-          }
-        }
-      } else if constexpr (QB == 8) {
+        for (int h = 0; h < RT; ++h) wv[j][h] = wbuf[wave][vs + (k + j) * VSLOTS][vg][h];
+      if constexpr (QB == 2) {
+        // tokens k and k + 1 in the low and high halves: each AND gives one
+        // channel of both tokens
+        const uint32_t x = R.v[k][0] | (R.v[k + 1][0] << 16), t = x >> 10;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {  // channels 2i, 2i + 1
-          const uint32_t pr2 = __builtin_amdgcn_perm(magic, R.v[k][i / 2], (i % 2) ? 0x04030402u : 0x04010400u);
-          const float lo = lo_h(pr2), hi = hi_h(pr2);
-#pragma unroll
-          for (int h = 0; h < RT; ++h) {
-            a[h][2 * i] += wv[h] * lo;
-            a[h][2 * i + 1] += wv[h] * hi;
-          }
-        }
-      } else if constexpr (QB == 4) {
-        const MagicPairs<4> mp(R.v[k][0], magic);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const float lo = lo_h(mp.h[kk]), hi = hi_h(mp.h[kk]);
-#pragma unroll
-          for (int h = 0; h < RT; ++h) {
-            a[h][MagicPairs<4>::chan(kk, 0)] += wv[h] * lo;
-            a[h][MagicPairs<4>::chan(kk, 1)] += wv[h] * hi;
-          }
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t m = e < 5 ? (x & (0x00030003u << (2 * e))) : (t & (0x00030003u << (2 * (e - 5))));
+          acc2(e, wv[0], m, false);
+          acc2(e, wv[1], m, true);
         }
       } else {
-        const uint32_t cw = R.v[k][0];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t pr2 = __builtin_amdgcn_perm(magic, (cw >> (2 * m)) & 0x0303u, 0x04010400u);
-          const float lo = lo_h(pr2), hi = hi_h(pr2);  // channels m and 4 + m
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t* vw = R.v[k + j];
+          if constexpr (F16T) {
 #pragma unroll
-          for (int h = 0; h < RT; ++h) {
-            a[h][m] += wv[h] * lo;
-            a[h][4 + m] += wv[h] * hi;
+            for (int i = 0; i < 4; ++i) {
+              acc2(2 * i, wv[j], vw[i], false);
+              acc2(2 * i + 1, wv[j], vw[i], true);
+            }
+          } else if constexpr (QB == 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {  // channels 2i, 2i + 1
+              const uint32_t pr2 = __builtin_amdgcn_perm(magic, vw[i / 2], (i % 2) ? 0x04030402u : 0x04010400u);
+              acc2(2 * i, wv[j], pr2, false);
+              acc2(2 * i + 1, wv[j], pr2, true);
+            }
+          } else {
+            // halves (c, c + 4): channels 0/4 and 1/5 in place, 2/6 and 3/7 after >> 8
+            const uint32_t x = vw[0], t = x >> 8;
+            const uint32_t m0 = x & 0x000F000Fu, m1 = x & 0x00F000F0u;
+            const uint32_t m2 = t & 0x000F000Fu, m3 = t & 0x00F000F0u;
+            acc2(0, wv[j], m0, false); acc2(4, wv[j], m0, true);
+            acc2(1, wv[j], m1, false); acc2(5, wv[j], m1, true);
+            acc2(2, wv[j], m2, false); acc2(6, wv[j], m2, true);
+            acc2(3, wv[j], m3, false); acc2(7, wv[j], m3, true);
           }
         }
       }
@@ -603,7 +622,7 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     for (int h = 0; h < RT; ++h)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        red[(wave * RT + h) * D + 8 * lane + e] = F16T ? a[h][e] : a[h][e] * kTileCodeUnit + zh[h][vg];
+        red[(wave * RT + h) * D + 8 * lane + e] = F16T ? a[h][e] : a[h][e] * tile_val_unit<QB>(e) + zh[h][vg];
   }
   if (lane % 16 == 0 && hl < RT) {
     sm[wave][hl] = M;
