@@ -449,9 +449,10 @@ __device__ __forceinline__ void tile_split(const DecodeK& p, int unit, int n, in
     }
   }
 
-  // key codes as 1 + code * step for the MFMA (tile_codes); value codes under
-  // a zero byte, the fp16 subnormals code * 2^-24, which v_fma_mix takes
-  // exactly: the value sums carry no offset to cancel later
+  // key codes as 1 + code * step for the MFMA (tile_codes); value codes as
+  // fp16 subnormals (masked in place, or for 8-bit codes a byte under a zero
+  // byte), which v_fma_mix takes exactly: the value sums carry no offset to
+  // cancel later
   const uint32_t kmagic = opaque(kCodeMagic<QB>), magic = opaque(0u);
   auto step = [&](const R_t& R, int grp) {
     // scores on the matrix cores: one accumulator per group of d/2 channels
