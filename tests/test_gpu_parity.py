@@ -317,6 +317,8 @@ def _lockstep(cfg, seed, steps, balanced=True, check_every=1, fused=False, sampl
     ("gqa_throughput", dict(batch=3, T=600), True, 5),
     ("llama3_8b_32k", dict(hq=8, hkv=2, T=4100), True, 4),
     ("llama3_8b_32k", dict(hq=8, hkv=4, T=3000), True, 3),   # two-head tiles of 2-bit codes
+    ("gqa_throughput", dict(batch=2, hq=8, hkv=4, T=900), True, 3),  # two-head tiles of 4-bit codes
+    ("tiny", dict(hq=6, hkv=1, T=300), True, 4),                      # three two-head tiles, ragged
     ("llama2_7b_layer", dict(batch=2, hq=3, hkv=3, T=1500), True, 4),
     # one (sequence, head) unit per 1024-thread block, whole units per block
     ("tiny", dict(batch=256), True, 6),
