@@ -1015,7 +1015,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const DecodeK p,
         }
       }
     }
-    if constexpr (FUSE) h2o_select_demote<D, BITS, NL>(w, hv, unit, fr);
+    if constexpr (FUSE) h2o_select_demote<D, BITS, NL>(w, hv, unit);
   } else {
     for (int sl = tid; sl < cap16; sl += kThreads) p16[sl] = prob(sl);
   }

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void h2o_decode_kernel(H2OArgs a) {
   } else {
     for (int s = tid; s < a.cap16; s += 256) consider(s, accin[s], p16[s], pos16[s]);
   }
-  h2o_select_demote<D, BITS, NL, KT>(w, h2o_view(a, IB), unit, fr);
+  h2o_select_demote<D, BITS, NL, KT>(w, h2o_view(a, IB), unit);
 }
 
 // ------------------------------------------------------------------ prefill

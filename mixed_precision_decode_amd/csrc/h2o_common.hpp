@@ -110,8 +110,9 @@ struct Worst {
 
 // Block-wide (256 threads): pick the worst candidate and quantize its key and
 // value rows into low-bit slot len - cap16 of the unit; free16 becomes the
-// dropped slot. `fr` is the slot the new token occupies (its position is
-// len - 1). v.imp_bits = 16: the rows are the slot's fp16 rows; 8 or 4: the
+// dropped slot. Each candidate enters w with its token position (len - 1
+// for the slot the new token occupies), which the dropped slot's records
+// take. v.imp_bits = 16: the rows are the slot's fp16 rows; 8 or 4: the
 // importance tier holds codes, and the row quantized is the slot's codes
 // rebuilt in fp16, fp16(code * scale + zero) (the product is exact in fp32,
 // so the fused multiply-add rounds once, like the sum of the exact product).
@@ -165,11 +166,11 @@ __device__ __forceinline__ void demote_to_buffer(const H2OView& v, int unit, int
 }
 
 template <int D, int BITS, int NL, bool KT = false>
-__device__ void h2o_select_demote(Worst w, const H2OView& v, int unit, int fr) {
+__device__ void h2o_select_demote(Worst w, const H2OView& v, int unit) {
   __shared__ float s_acc[4];
   __shared__ int s_pos[4];
   __shared__ int s_slot[4];
-  __shared__ int s_drop;
+  __shared__ int s_drop, s_dpos;
   const int tid = threadIdx.x;
   // wave argmin: within each row by DPP (quad swaps, then the half-row and
   // row mirrors), across rows by the permlane swaps; merge keeps the minimum
@@ -201,13 +202,15 @@ __device__ void h2o_select_demote(Worst w, const H2OView& v, int unit, int fr) {
     b.a = s_acc[0]; b.pos = s_pos[0]; b.slot = s_slot[0];
     for (int i = 1; i < 4; ++i) b.merge(s_acc[i], s_pos[i], s_slot[i]);
     s_drop = b.slot;
+    s_dpos = b.pos;
   }
   __syncthreads();
   const int drop = s_drop;
   if (drop < 0) return;  // unreachable when heavy + recent == cap16 - 1
+  // the dropped token's position, as the candidates were ranked with it (the
+  // new token's, len - 1, for the free slot): no second read of pos16
+  const int pos = s_dpos;
   if constexpr (KT) {
-    const int64_t b16 = static_cast<int64_t>(unit) * v.cap16;
-    const int pos = (drop == fr) ? v.len - 1 : v.pos16[b16 + drop];
     if (tid == 0) {
       v.free16[unit] = drop;
       if (v.demoted_pos) v.demoted_pos[unit] = pos;
@@ -239,7 +242,6 @@ __device__ void h2o_select_demote(Worst w, const H2OView& v, int unit, int fr) {
     if (lane % NL == 0) (is_v ? v.vsz : v.ksz)[qslot * GPT + lane / NL] = szw;
   }
   if (tid == 0) {
-    const int pos = (drop == fr) ? v.len - 1 : v.pos16[base16 + drop];
     v.posq[qslot] = pos;
     v.free16[unit] = drop;
     if (v.demoted_pos) v.demoted_pos[unit] = pos;
