@@ -1115,12 +1115,12 @@ static int split_blocks_per_cu(int d, int bits, int ib, int rt, bool tile, int k
 // value sum; the low-bit unpacking roughly matches the FP16 tier's wider
 // lane groups): the time of a tier is its token count, an FP16 token
 // weighted 1.3 (on the 32K GQA shape, token shares of 1:1 and 1.3:1 gave a
-// split kernel of 29.6 and 28.7 us, byte shares 34.2 us; on the GQA batch
-// 1.1-1.5 all give 48.8-49.1 us), and 2.4 where the low-bit tier's value
-// sums run on the matrix cores, which makes its tokens cheaper (32K GQA
-// shape: 17.8 us at 1.2, 17.4-17.5 at 1.6, 16.8-17.1 at 2.0-3.0; splits
-// rounded to whole 256-token steps, which makes the FP16 splits longer:
-// 19.0 us).
+// split kernel of 29.6 and 28.7 us, byte shares 34.2 us; the GQA batch, one
+// split per tier and unit, takes the same plan at any weight), and 2.4 where
+// the low-bit tier's value sums run on the matrix cores, which makes its
+// tokens cheaper (32K GQA shape: 17.8 us at 1.2, 17.4-17.5 at 1.6, 16.8-17.1
+// at 2.0-3.0; splits rounded to whole 256-token steps, which makes the FP16
+// splits longer: 19.0 us).
 //
 // Per-channel key tiles: the low-bit splits hold whole tiles of 64 tokens
 // (at most kt_max_tiles, the LDS table of a block), and the buffered pairs,
